@@ -1,0 +1,124 @@
+"""The per-step tile schedule, written out plainly (integer algorithm).
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+The HPC-Ops blog (§Attention Backend: Dynamic Load-Balanced Scheduling)
+says the scheduler runs every decode step, cuts every KV sequence into
+uniform 64-token tiles, and hands tiles to the persistent grid's workers
+according to the actual work; the German retelling (§Warum ist dynamisches
+Scheduling entscheidend für Attention?) adds that tiles go to compute units
+in proportion to each sequence's actual length in the current generation
+step.  The pages fix neither the partition rule nor the work-list format.
+The reading used here (and, independently, by the C++ planner):
+
+  1. units u = b * H_kv + h (batch-major); n_u = ceil(L_b / 64) tiles; one
+     tile costs one, the last partial tile included;
+  2. P = exclusive prefix sum of n_u, T = P[U];
+  3. worker w owns global tiles [s_w, s_{w+1}) with s_w = floor(w * T / W);
+  4. for w = 0..W-1 and, inside, increasing u, every unit whose tile range
+     meets worker w's range gives one entry (u, t0, t1) of unit-local tile
+     indices; worker_ptr[w + 1] is the running entry count;
+  5. S_u = number of entries of unit u.  S_u = 1: slot -1 (the worker
+     writes the final output).  S_u >= 2: the units with S >= 2, in
+     increasing u, take consecutive blocks of partial slots; the k-th entry
+     of u in entry order gets slot base_u + k.  Units with S_u != 1 are
+     listed for the merge as (u, S_u, base_u), base_u = 0 when S_u = 0.
+
+Serialised as int32 words:
+  header[16] = {1, B, H_kv, W, T, E, n_partials, n_combine, 64, 0, ..., 0}
+  worker_ptr[W + 1], entries[E][4] = (u, t0, t1, slot), combine[n_combine][3].
+
+Pinned by ``tests/test_oracle_plan.py``: an independent quota-filling
+construction, the coverage / balance / contiguity / slot-bijection
+invariants, exhaustive small cases, and a hand-worked schedule stored
+under ``tests/golden/``.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+PAGE = 64
+HEADER_WORDS = 16
+PLAN_VERSION = 1
+
+
+def plan_size_words(batch: int, num_kv_heads: int, n_workers: int) -> int:
+    """Upper bound on the plan's int32 word count (E <= W + U - 1, n_combine <= U)."""
+    U = batch * num_kv_heads
+    return HEADER_WORDS + (n_workers + 1) + 4 * (n_workers + U) + 3 * U
+
+
+def build_plan(seq_lens, num_kv_heads: int, n_workers: int) -> np.ndarray:
+    lens = [int(x) for x in seq_lens]
+    B, H, W = len(lens), int(num_kv_heads), int(n_workers)
+    if W < 1 or H < 1 or any(L < 0 for L in lens):
+        raise ValueError("invalid plan arguments")
+    U = B * H
+    n = [(lens[u // H] + PAGE - 1) // PAGE for u in range(U)]
+    P = [0]
+    for u in range(U):
+        P.append(P[-1] + n[u])
+    T = P[U]
+    s = [(w * T) // W for w in range(W + 1)]
+
+    entries = []          # [u, t0, t1]
+    worker_ptr = [0]
+    for w in range(W):
+        for u in range(U):
+            lo = max(s[w], P[u])
+            hi = min(s[w + 1], P[u + 1])
+            if lo < hi:
+                entries.append([u, lo - P[u], hi - P[u]])
+        worker_ptr.append(len(entries))
+
+    S = [0] * U
+    for e in entries:
+        S[e[0]] += 1
+    base = [0] * U
+    running = 0
+    for u in range(U):
+        if S[u] >= 2:
+            base[u] = running
+            running += S[u]
+    n_partials = running
+
+    seen = [0] * U
+    slots = []
+    for e in entries:
+        u = e[0]
+        if S[u] == 1:
+            slots.append(-1)
+        else:
+            slots.append(base[u] + seen[u])
+        seen[u] += 1
+
+    combine = [[u, S[u], base[u]] for u in range(U) if S[u] != 1]
+
+    header = [PLAN_VERSION, B, H, W, T, len(entries), n_partials, len(combine), PAGE]
+    header += [0] * (HEADER_WORDS - len(header))
+    words = list(header) + worker_ptr
+    for e, slot in zip(entries, slots):
+        words += [e[0], e[1], e[2], slot]
+    for c in combine:
+        words += c
+    return np.asarray(words, dtype=np.int32)
+
+
+def parse_plan(words) -> dict:
+    w = np.asarray(words, dtype=np.int64)
+    hdr = w[:HEADER_WORDS]
+    W, E, C = int(hdr[3]), int(hdr[5]), int(hdr[7])
+    o = HEADER_WORDS
+    worker_ptr = w[o:o + W + 1]
+    o += W + 1
+    entries = w[o:o + 4 * E].reshape(E, 4)
+    o += 4 * E
+    combine = w[o:o + 3 * C].reshape(C, 3)
+    o += 3 * C
+    return {
+        "version": int(hdr[0]), "batch": int(hdr[1]), "num_kv_heads": int(hdr[2]),
+        "n_workers": W, "n_tiles": int(hdr[4]), "n_entries": E, "n_partials": int(hdr[6]),
+        "n_combine": C, "tile": int(hdr[8]), "worker_ptr": worker_ptr, "entries": entries,
+        "combine": combine, "n_words": o,
+    }
