@@ -1,0 +1,227 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark on one MI355X.
+
+A step is the whole hot path for one batch: the per-step host schedule
+(C++ planner), the plan upload, the persistent decode kernel and the
+log-sum-exp merge kernel.  Default workload: the skewed batch of one
+131072-token sequence and 31 sequences of 4096 tokens, 8 query heads over one
+KV head, head dim 128, bf16 KV in 64-token pages, shuffled block table
+("vLLM x HPC-Ops ...", §Attention Decode under Mixed-Length Batches).
+
+Inputs are resident in HBM before timing starts.  The KV cache is replicated
+into several copies that successive steps rotate through, so that no step
+finds its KV in the 256 MB Infinity Cache left behind by the previous one.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+METRIC = "decode-attn µs/step & achieved HBM TB/s on 1×128K+31×4K mixed batch"
+HBM_PEAK_GBPS = 8000.0
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=4, help="workload number (1-5); 4 = 1x128K+31x4K")
+    ap.add_argument("--n-workers", type=int, default=0, help="persistent workgroups (0: one per CU)")
+    ap.add_argument("--copies", type=int, default=0, help="rotating KV copies (0: enough for >= 1 GiB)")
+    ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
+    ap.add_argument("--probe", action="store_true", help="also measure the HBM streaming-read ceiling")
+    return ap.parse_args()
+
+
+def cpu_baseline(inp, alg_bytes: int):
+    """The float64 oracle on the host cores, over the same workload (median of repeated runs)."""
+    from oracle import decode_attention
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:   # threadpoolctl missing: report the affinity size
+        threads = len(os.sched_getaffinity(0))
+    args = (inp.q_bits(), inp.k_bits(), inp.v_bits(), inp.block_table.numpy(), inp.seq_lens.numpy())
+    kw = dict(num_q_heads=inp.num_q_heads, num_kv_heads=inp.num_kv_heads, kv_format=inp.kv_dtype,
+              sm_scale=inp.sm_scale, k_scale=inp.k_scale, v_scale=inp.v_scale)
+    times = []
+    t_start = time.perf_counter()
+    while len(times) < 3 or (time.perf_counter() - t_start < 10.0 and len(times) < 30):
+        t0 = time.perf_counter()
+        decode_attention(*args, **kw)
+        times.append(time.perf_counter() - t0)
+    med = statistics.median(times)
+    return {"value": alg_bytes / med / 1e12, "unit": "TB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"whole workload, {len(times)} runs of the float64 oracle, median {med:.3f} s/step",
+            "s_per_step": med}
+
+
+def main() -> int:
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the decode path has no "
+              "multi-GPU mode in this build", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import load_balanced_paged_step_amd as hd
+    from workloads import WORKLOADS, workload_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+    cus = props.multi_processor_count
+    W = args.n_workers or cus
+    wl = WORKLOADS[args.workload]
+
+    log(f"building inputs for workload {args.workload} ({wl.name})")
+    inp = workload_inputs(args.workload)
+    kv_bytes_total = inp.k_cache.numel() * inp.k_cache.element_size() * 2
+    copies = args.copies or max(1, min(16, math.ceil((1 << 30) / kv_bytes_total)))
+    alg_bytes = inp.algorithmic_bytes()
+    log(f"device {props.name}, {cus} CUs; W={W}; KV {kv_bytes_total / 1e6:.1f} MB x {copies} copies; "
+        f"algorithmic bytes/step {alg_bytes}")
+
+    q = inp.q.to(dev)
+    bt = inp.block_table.to(dev)
+    sl = inp.seq_lens.to(dev)
+    k0 = inp.k_cache.to(dev)
+    v0 = inp.v_cache.to(dev)
+    ks = [k0] + [k0.clone() for _ in range(copies - 1)]
+    vs = [v0] + [v0.clone() for _ in range(copies - 1)]
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+    step = hd.DecodeStep(inp.num_q_heads, inp.num_kv_heads, inp.batch, W, device=dev)
+    lens_host = inp.seq_lens.numpy()
+    scales = dict(sm_scale=inp.sm_scale, k_scale=inp.k_scale, v_scale=inp.v_scale)
+
+    def one_step(i: int) -> None:
+        step.plan(lens_host)
+        step.attend(q, ks[i % copies], vs[i % copies], bt, sl, out, lse, **scales)
+
+    log(f"warmup {args.warmup} steps")
+    for i in range(args.warmup):
+        one_step(i)
+    torch.cuda.synchronize()
+
+    # host planner cost alone (part of every step; overlaps the previous step's kernels)
+    t0 = time.perf_counter()
+    for _ in range(200):
+        hd.hpc_decode_plan(lens_host, inp.num_kv_heads, W)
+    plan_us = (time.perf_counter() - t0) / 200 * 1e6
+
+    log(f"timed region: {args.steps} steps")
+    s = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    hd.hpc_decode_profile_start(args.steps)
+    torch.cuda.synchronize()
+    ev0.record(s)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        one_step(i)
+    ev1.record(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    decode_ms, combine_ms, n_calls = hd.hpc_decode_profile_stop()
+    ev_ms = ev0.elapsed_time(ev1)
+    ms_per_step = max(wall * 1e3, ev_ms) / args.steps
+    decode_us = decode_ms / max(n_calls, 1) * 1e3
+    combine_us = combine_ms / max(n_calls, 1) * 1e3
+    log(f"{ms_per_step * 1e3:.2f} us/step (host {wall * 1e3 / args.steps * 1e3:.2f}, events "
+        f"{ev_ms / args.steps * 1e3:.2f}); decode kernel {decode_us:.2f} us, merge {combine_us:.2f} us")
+
+    # clean region: the same steps without profiling events, for the step time alone
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        one_step(i)
+    torch.cuda.synchronize()
+    clean_us = (time.perf_counter() - t0) / args.steps * 1e6
+    log(f"without profiling events: {clean_us:.2f} us/step")
+
+    step_tbps = alg_bytes / (ms_per_step * 1e-3) / 1e12
+    achieved_gbps = alg_bytes / (decode_us * 1e-6) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(step_tbps, 4),
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_step": round(ms_per_step * 1e3, 3),
+        "us_per_step_no_events": round(clean_us, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": inp.kv_dtype if inp.kv_dtype == "bf16" else "fp8-e4m3 KV, bf16 MFMA",
+        "data": "synthetic (seeded N(0,1) Q/K/V, shuffled block table)",
+        "config": {
+            "workload": wl.name, "batch": inp.batch, "kv_lens": _lens_summary(lens_host),
+            "num_q_heads": inp.num_q_heads, "num_kv_heads": inp.num_kv_heads, "head_dim": 128,
+            "page_size": 64, "kv_dtype": inp.kv_dtype, "n_workers": W, "kv_copies": copies,
+            "algorithmic_bytes": alg_bytes, "parallelism": "single GPU",
+        },
+        "kernels": {"decode_us": round(decode_us, 3), "merge_us": round(combine_us, 3),
+                    "plan_host_us": round(plan_us, 2), "timed_calls": n_calls},
+        "roofline": {"bound": "hbm", "achieved": round(achieved_gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "decode_kernel", "bytes_per_launch": alg_bytes},
+    }
+
+    if args.probe:
+        nbytes = 1 << 30
+        buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        buf.fill_(1)
+        sink = torch.empty(4096, dtype=torch.float32, device=dev)
+        best = 0.0
+        for nwg in (cus * 4, cus * 8, cus * 16):
+            for _ in range(3):
+                hd.hpc_probe_read(buf, sink, nwg)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(10):
+                hd.hpc_probe_read(buf, sink, nwg)
+            e1.record()
+            torch.cuda.synchronize()
+            gbps = nbytes * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+            best = max(best, gbps)
+            log(f"read probe, {nwg} workgroups: {gbps:.0f} GB/s")
+        result["probe"] = {"read_GBps": round(best, 1), "bytes": nbytes}
+
+    if args.cpu_baseline == "on":
+        log("timing the float64 oracle on the host (cpu_baseline)")
+        result["cpu_baseline"] = cpu_baseline(inp, alg_bytes)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def _lens_summary(lens) -> str:
+    from collections import Counter
+    c = Counter(int(x) for x in lens)
+    if len(c) > 6:
+        return f"{len(lens)} seqs, {int(min(lens))}..{int(max(lens))} (sum {int(sum(lens))})"
+    return " + ".join(f"{n}x{L}" for L, n in sorted(c.items(), key=lambda kv: -kv[0]))
+
+
+if __name__ == "__main__":
+    sys.exit(main())

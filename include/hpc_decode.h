@@ -1,0 +1,181 @@
+/*
+ * hpc_decode.h — C ABI of the load-balanced paged GQA decode-attention library
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What it computes.  One decode step of attention over a paged KV cache: for
+ * every sequence b and query head hq (KV head h = hq / G, G = Hq / H_kv)
+ *
+ *     out[b, hq] = softmax_t(sm_scale * <q[b, hq], k_scale * K_t>) . (v_scale * V_t)
+ *     lse[b, hq] = ln sum_t exp(sm_scale * <q[b, hq], k_scale * K_t>)
+ *
+ * over the L_b cached tokens t of sequence b, with K_t / V_t read from page
+ * block_table[b, t / 64], row t % 64.  An empty sequence gives out = 0 and
+ * lse = -inf.  The schedule follows the per-step load-balanced decode
+ * scheduler of "vLLM x HPC-Ops: High-Performance Attention and MoE Backends
+ * from Tencent Hunyuan", §Attention Backend: Dynamic Load-Balanced
+ * Scheduling: every sequence's KV is cut into uniform 64-token tiles, the
+ * tiles are spread evenly over a persistent grid, and a sequence split over
+ * several workers is merged from its partial (o, lse) results by log-sum-exp
+ * (the merge itself is not described on the pages; log-sum-exp is the
+ * reading used here).  Head shape: 64 query heads over 8 KV heads, head dim
+ * 128 ("vLLM und Tencent Hunyuan streamen zwei HPC-Backends ...",
+ * §Zwei neue HPC-Backends im vLLM-Ökosystem); page size 64 and the
+ * fp8_e4m3 cache come from §Using HPC-Ops Backends in vLLM.
+ *
+ * Conventions for every entry point
+ *  - Status codes are returned, never thrown; 0 is success, negatives are
+ *    the HPC_ERR_* values below.  Every condition checkable on the host is
+ *    checked before any HIP call, and nothing is launched on failure.
+ *  - Every buffer belongs to the caller.  The library allocates no device
+ *    memory, keeps no state between calls (apart from the optional
+ *    profiling window below) and never synchronises the stream.
+ *  - "device" pointers must be device memory usable on the current HIP
+ *    device; "host" pointers are ordinary CPU memory.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *  - Calls are thread-safe except the profiling window, which is global.
+ */
+#ifndef HPC_DECODE_H
+#define HPC_DECODE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------- */
+#define HPC_OK                 0
+#define HPC_ERR_NULL          -1   /* a required pointer is NULL                     */
+#define HPC_ERR_INVALID       -2   /* a size / count / length is out of range        */
+#define HPC_ERR_UNSUPPORTED   -3   /* head_dim != 128, page != 64, G > 16, dtype ... */
+#define HPC_ERR_PLAN_MISMATCH -4   /* plan header disagrees with the call            */
+#define HPC_ERR_TOO_SMALL     -5   /* plan buffer or workspace too small             */
+#define HPC_ERR_HIP           -6   /* a HIP runtime call or kernel launch failed     */
+
+/* ---- KV-cache element types --------------------------------------------- */
+#define HPC_KV_BF16      0   /* bfloat16                                            */
+#define HPC_KV_FP8_E4M3  1   /* OCP FP8 E4M3FN (torch.float8_e4m3fn), x = code*scale */
+
+#define HPC_DECODE_HEAD_DIM   128
+#define HPC_DECODE_PAGE       64   /* tokens per page = tokens per scheduling tile */
+#define HPC_DECODE_MAX_GROUP  16   /* query heads per KV head supported            */
+#define HPC_PLAN_HEADER_WORDS 16
+#define HPC_PLAN_VERSION      1
+
+/* Shapes and scales of one decode step. */
+typedef struct hpc_decode_params {
+    int32_t num_q_heads;        /* Hq; a multiple of num_kv_heads, Hq / H_kv <= 16   */
+    int32_t num_kv_heads;       /* H_kv >= 1                                         */
+    int32_t head_dim;           /* must be 128                                       */
+    int32_t page_size;          /* must be 64                                        */
+    int32_t max_pages_per_seq;  /* row stride of block_table, in int32 elements      */
+    int32_t num_pages;          /* physical pages in k_cache and v_cache (>= 1)      */
+    int32_t kv_dtype;           /* HPC_KV_BF16 or HPC_KV_FP8_E4M3                    */
+    float   sm_scale;           /* softmax scale, normally 1/sqrt(head_dim)          */
+    float   k_scale;            /* per-tensor dequantisation scale of K (1 for bf16) */
+    float   v_scale;            /* per-tensor dequantisation scale of V (1 for bf16) */
+} hpc_decode_params;
+
+/*
+ * Upper bound, in int32 words, of the plan for this batch shape:
+ * 16 + (W + 1) + 4 (W + U) + 3 U with U = batch * num_kv_heads, W = n_workers
+ * (a work list holds at most W + U - 1 entries and at most U merge records).
+ * Returns a negative status for batch < 0, num_kv_heads < 1 or n_workers < 1.
+ */
+int64_t hpc_decode_plan_size(int32_t batch, int32_t num_kv_heads, int32_t n_workers);
+
+/*
+ * Per-step scheduler (§Attention Backend: Dynamic Load-Balanced Scheduling;
+ * the German page, §Warum ist dynamisches Scheduling entscheidend für
+ * Attention?, adds that tiles follow each sequence's length in the current
+ * step).  Pure host code; no HIP call.
+ *
+ * seq_lens   host int32[batch], KV lengths of this step (>= 0).
+ * plan       host int32[plan_capacity] output.
+ *
+ * Units u = b * num_kv_heads + h each hold n_u = ceil(L_b / 64) tiles; with
+ * T = sum n_u, worker w (0 <= w < n_workers) owns tiles
+ * [floor(w T / W), floor((w + 1) T / W)) of the unit-major tile list, cut
+ * at unit boundaries into entries.  Layout (int32 words):
+ *   header[16]      {version=1, batch, H_kv, W, T, E, n_partials, n_combine, 64, 0...}
+ *   worker_ptr[W+1] worker w's entries are [worker_ptr[w], worker_ptr[w+1])
+ *   entries[E][4]   (unit, t0, t1, slot): tiles [t0, t1) of the unit; slot -1
+ *                   means this entry is the unit's only one and writes out/lse
+ *                   directly, otherwise it writes partial number `slot`
+ *   combine[n_combine][3]  (unit, S_u, base_u) for every unit with S_u != 1
+ *                   entries: S_u >= 2 partials in slots [base_u, base_u + S_u),
+ *                   or S_u = 0 for an empty sequence
+ * Errors: NULL pointers, batch < 0, H_kv < 1, W < 1, a negative length, or
+ * T >= 2^31 -> HPC_ERR_NULL / HPC_ERR_INVALID; capacity below the words the
+ * plan needs -> HPC_ERR_TOO_SMALL.  On error `plan` is left unspecified.
+ */
+int hpc_decode_plan(const int32_t* seq_lens, int32_t batch, int32_t num_kv_heads,
+                    int32_t n_workers, int32_t* plan, int64_t plan_capacity);
+
+/* Words actually used by a plan written by hpc_decode_plan (from its header),
+ * or a negative status for a NULL pointer or a malformed header. */
+int64_t hpc_decode_plan_words(const int32_t* plan);
+
+/*
+ * Device workspace, in bytes, that hpc_decode_attn needs for this plan:
+ * n_partials * G * 128 fp32 partial outputs followed (256-byte aligned) by
+ * n_partials * G fp32 partial log-sum-exps.  0 when no sequence is split.
+ */
+int64_t hpc_decode_workspace_size(const int32_t* plan, int32_t num_q_heads,
+                                  int32_t num_kv_heads);
+
+/*
+ * One decode step on `stream`: the persistent decode kernel (grid = the
+ * plan's W workgroups, each walking its entries), then, when the plan has
+ * merge records, the log-sum-exp merge kernel.
+ *
+ * q            device bf16 [batch][Hq][128], contiguous
+ * k_cache      device bf16 or fp8 [num_pages][H_kv][64][128], contiguous
+ * v_cache      same layout and type as k_cache
+ * block_table  device int32 [batch][max_pages_per_seq]; entries of tiles the
+ *              plan covers must lie in [0, num_pages) (others are never read;
+ *              an id outside that range is read as a page of zeros)
+ * seq_lens     device int32 [batch]; must equal the lengths the plan was made from
+ * plan_host    host copy of the plan (sizes the grids without a device sync)
+ * plan_dev     device copy of the same words
+ * workspace    device, >= hpc_decode_workspace_size bytes (may be NULL if that is 0)
+ * out          device bf16 [batch][Hq][128]
+ * lse          device fp32 [batch][Hq], natural log
+ * The host checks the plan against the call (version, H_kv, entry bounds
+ * against max_pages_per_seq) before launching.  All device buffers must
+ * stay valid until the stream work completes; plan_host only until return.
+ */
+int hpc_decode_attn(const hpc_decode_params* params, const void* q, const void* k_cache,
+                    const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                    const int32_t* plan_host, const int32_t* plan_dev, void* workspace,
+                    int64_t workspace_bytes, void* out, float* lse, void* stream);
+
+/*
+ * The host-side checks of hpc_decode_attn alone, with the same arguments
+ * (no stream): returns the status hpc_decode_attn would return before
+ * launching anything.  Never calls HIP and never dereferences device pointers.
+ */
+int hpc_decode_check(const hpc_decode_params* params, const void* q, const void* k_cache,
+                     const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                     const int32_t* plan_host, const int32_t* plan_dev, const void* workspace,
+                     int64_t workspace_bytes, const void* out, const float* lse);
+
+/* Human-readable name of a status code (static storage). */
+const char* hpc_status_string(int status);
+
+/*
+ * Optional profiling window (measurement only; global state, not
+ * thread-safe).  Between start and stop every hpc_decode_attn call brackets
+ * its decode-kernel launch and its merge-kernel launch with HIP events on
+ * the call's stream (at most `capacity` calls are recorded).  stop
+ * synchronises those events and returns the summed durations in ms and the
+ * number of calls recorded.  Returns HPC_ERR_HIP on event failures.
+ */
+int hpc_decode_profile_start(int32_t capacity);
+int hpc_decode_profile_stop(double* decode_ms, double* combine_ms, int32_t* n_calls);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HPC_DECODE_H */

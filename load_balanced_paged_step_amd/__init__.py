@@ -1,0 +1,278 @@
+"""Load-balanced paged GQA decode attention for AMD Instinct MI355X (gfx950).
+
+Python binding of the C ABI in ``include/hpc_decode.h`` / ``include/hpc_probe.h``.
+Each function here only checks and marshals arguments (torch tensors ->
+device pointers, the current HIP stream) and calls the function of the same
+name in ``libhpc_decode.so``; the schedule, the attention and the merge all
+run in that library's C++ planner and HIP kernels.  PyTorch supplies device
+memory and streams only.
+
+Method: "vLLM x HPC-Ops: High-Performance Attention and MoE Backends from
+Tencent Hunyuan", §Attention Backend: Dynamic Load-Balanced Scheduling.
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import torch
+
+from . import _lib
+from ._lib import (HPC_OK, HPC_ERR_NULL, HPC_ERR_INVALID, HPC_ERR_UNSUPPORTED, HPC_ERR_PLAN_MISMATCH,
+                   HPC_ERR_TOO_SMALL, HPC_ERR_HIP, HPC_KV_BF16, HPC_KV_FP8_E4M3, HEAD_DIM, PAGE,
+                   MAX_GROUP, PLAN_HEADER_WORDS, HpcDecodeError, hpc_decode_params, lib)
+
+__all__ = [
+    "hpc_decode_plan_size", "hpc_decode_plan", "hpc_decode_plan_words", "hpc_decode_workspace_size",
+    "hpc_decode_check", "hpc_decode_attn", "hpc_status_string", "hpc_decode_profile_start",
+    "hpc_decode_profile_stop", "hpc_probe_read", "hpc_probe_copy", "DecodeStep", "HpcDecodeError",
+    "kv_dtype_code", "make_params", "HPC_KV_BF16", "HPC_KV_FP8_E4M3",
+]
+
+_I32P = ctypes.POINTER(ctypes.c_int32)
+
+
+def _host_i32(x) -> np.ndarray:
+    """A C-contiguous int32 numpy view of host data (numpy array or CPU tensor)."""
+    if isinstance(x, torch.Tensor):
+        if x.device.type != "cpu":
+            raise ValueError("expected a host (CPU) tensor")
+        x = x.numpy()
+    a = np.ascontiguousarray(x, dtype=np.int32)
+    return a
+
+
+def _i32p(a: np.ndarray):
+    return a.ctypes.data_as(_I32P)
+
+
+def _dev_ptr(t, name: str, dtype=None, allow_none: bool = False):
+    if t is None:
+        if allow_none:
+            return None
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device (cuda) tensor")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def kv_dtype_code(dtype: torch.dtype) -> int:
+    if dtype == torch.bfloat16:
+        return HPC_KV_BF16
+    if dtype == torch.float8_e4m3fn:
+        return HPC_KV_FP8_E4M3
+    raise ValueError(f"unsupported KV-cache dtype {dtype}")
+
+
+def make_params(num_q_heads, num_kv_heads, max_pages_per_seq, num_pages, kv_dtype, sm_scale,
+                k_scale=1.0, v_scale=1.0, head_dim=HEAD_DIM, page_size=PAGE) -> hpc_decode_params:
+    code = kv_dtype if isinstance(kv_dtype, int) else kv_dtype_code(kv_dtype)
+    return hpc_decode_params(int(num_q_heads), int(num_kv_heads), int(head_dim), int(page_size),
+                             int(max_pages_per_seq), int(num_pages), code, float(sm_scale),
+                             float(k_scale), float(v_scale))
+
+
+# ---------------------------------------------------------------- planner ---
+
+def hpc_decode_plan_size(batch: int, num_kv_heads: int, n_workers: int) -> int:
+    return _lib.check(lib().hpc_decode_plan_size(batch, num_kv_heads, n_workers), "hpc_decode_plan_size")
+
+
+def hpc_decode_plan(seq_lens, num_kv_heads: int, n_workers: int, out=None) -> np.ndarray:
+    """Per-step schedule of host lengths ``seq_lens``; returns the used int32 words.
+
+    ``out`` may be a preallocated host int32 buffer (numpy array or a pinned
+    CPU tensor) of at least ``hpc_decode_plan_size`` words; the result is
+    then a view of it.
+    """
+    lens = _host_i32(seq_lens).reshape(-1)
+    cap = hpc_decode_plan_size(lens.shape[0], num_kv_heads, n_workers)
+    if out is None:
+        buf = np.empty(cap, dtype=np.int32)
+    else:
+        buf = out.numpy() if isinstance(out, torch.Tensor) else out
+        if buf.dtype != np.int32 or not buf.flags.c_contiguous:
+            raise ValueError("plan buffer must be a contiguous int32 host buffer")
+    _lib.check(lib().hpc_decode_plan(_i32p(lens), lens.shape[0], num_kv_heads, n_workers, _i32p(buf),
+                                     buf.shape[0]), "hpc_decode_plan")
+    return buf[:hpc_decode_plan_words(buf)]
+
+
+def hpc_decode_plan_words(plan) -> int:
+    a = _host_i32(plan) if not isinstance(plan, np.ndarray) else plan
+    return _lib.check(lib().hpc_decode_plan_words(_i32p(a)), "hpc_decode_plan_words")
+
+
+def hpc_decode_workspace_size(plan, num_q_heads: int, num_kv_heads: int) -> int:
+    a = _host_i32(plan) if not isinstance(plan, np.ndarray) else plan
+    return _lib.check(lib().hpc_decode_workspace_size(_i32p(a), num_q_heads, num_kv_heads),
+                      "hpc_decode_workspace_size")
+
+
+def hpc_status_string(status: int) -> str:
+    return lib().hpc_status_string(int(status)).decode()
+
+
+# ----------------------------------------------------------- decode step ---
+
+def _attn_args(q, k_cache, v_cache, block_table, seq_lens, plan_host, plan_dev, workspace, out, lse,
+               num_kv_heads, sm_scale, k_scale, v_scale):
+    if k_cache.dtype != v_cache.dtype:
+        raise ValueError("k_cache and v_cache must have the same dtype")
+    if q.dim() != 3 or k_cache.dim() != 4 or block_table.dim() != 2:
+        raise ValueError("expected q [B,Hq,128], caches [pages,H_kv,64,128], block_table [B,max_pages]")
+    params = make_params(q.shape[1], num_kv_heads, block_table.shape[1], k_cache.shape[0], k_cache.dtype,
+                         sm_scale, k_scale, v_scale, head_dim=q.shape[2], page_size=k_cache.shape[2])
+    ph = plan_host if isinstance(plan_host, np.ndarray) else _host_i32(plan_host)
+    if int(ph[1]) != q.shape[0] or block_table.shape[0] != q.shape[0] or seq_lens.shape[0] != q.shape[0]:
+        raise ValueError("batch sizes of q, block_table, seq_lens and the plan differ")
+    if k_cache.shape[1] != num_kv_heads or tuple(k_cache.shape) != tuple(v_cache.shape):
+        raise ValueError("cache shapes disagree with num_kv_heads")
+    if tuple(out.shape) != tuple(q.shape) or tuple(lse.shape) != tuple(q.shape[:2]):
+        raise ValueError("out must match q's shape and lse must be [B, Hq]")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    args = (ctypes.byref(params),
+            _dev_ptr(q, "q", torch.bfloat16),
+            _dev_ptr(k_cache, "k_cache", (torch.bfloat16, torch.float8_e4m3fn)),
+            _dev_ptr(v_cache, "v_cache", (torch.bfloat16, torch.float8_e4m3fn)),
+            _dev_ptr(block_table, "block_table", torch.int32),
+            _dev_ptr(seq_lens, "seq_lens", torch.int32),
+            _i32p(ph),
+            _dev_ptr(plan_dev, "plan_dev", torch.int32),
+            _dev_ptr(workspace, "workspace", allow_none=True),
+            ctypes.c_int64(ws_bytes),
+            _dev_ptr(out, "out", torch.bfloat16),
+            _dev_ptr(lse, "lse", torch.float32))
+    return args, ph
+
+
+def hpc_decode_check(q, k_cache, v_cache, block_table, seq_lens, plan_host, plan_dev, workspace, out,
+                     lse, *, num_kv_heads, sm_scale, k_scale=1.0, v_scale=1.0) -> int:
+    """Status that hpc_decode_attn would return for these arguments (no launch)."""
+    args, _ = _attn_args(q, k_cache, v_cache, block_table, seq_lens, plan_host, plan_dev, workspace, out,
+                         lse, num_kv_heads, sm_scale, k_scale, v_scale)
+    return lib().hpc_decode_check(*args)
+
+
+def hpc_decode_attn(q, k_cache, v_cache, block_table, seq_lens, plan_host, plan_dev, workspace, out,
+                    lse, *, num_kv_heads, sm_scale, k_scale=1.0, v_scale=1.0, stream=None) -> None:
+    """One decode step on ``stream`` (default: torch's current stream); see hpc_decode.h."""
+    args, _ = _attn_args(q, k_cache, v_cache, block_table, seq_lens, plan_host, plan_dev, workspace, out,
+                         lse, num_kv_heads, sm_scale, k_scale, v_scale)
+    _lib.check(lib().hpc_decode_attn(*args, _stream_handle(stream)), "hpc_decode_attn")
+
+
+# ------------------------------------------------------------- profiling ---
+
+def hpc_decode_profile_start(capacity: int) -> None:
+    _lib.check(lib().hpc_decode_profile_start(capacity), "hpc_decode_profile_start")
+
+
+def hpc_decode_profile_stop():
+    """(summed decode-kernel ms, summed merge-kernel ms, calls recorded)."""
+    d, c, n = ctypes.c_double(), ctypes.c_double(), ctypes.c_int32()
+    _lib.check(lib().hpc_decode_profile_stop(ctypes.byref(d), ctypes.byref(c), ctypes.byref(n)),
+               "hpc_decode_profile_stop")
+    return d.value, c.value, n.value
+
+
+def hpc_probe_read(buf: torch.Tensor, sink: torch.Tensor, n_workgroups: int, stream=None) -> None:
+    nbytes = buf.numel() * buf.element_size()
+    if sink.numel() < n_workgroups or sink.dtype != torch.float32:
+        raise ValueError("sink must hold n_workgroups float32 values")
+    _lib.check(lib().hpc_probe_read(_dev_ptr(buf, "buf"), nbytes, _dev_ptr(sink, "sink"), n_workgroups,
+                                    _stream_handle(stream)), "hpc_probe_read")
+
+
+def hpc_probe_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("dst smaller than src")
+    _lib.check(lib().hpc_probe_copy(_dev_ptr(src, "src"), _dev_ptr(dst, "dst"), nbytes,
+                                    _stream_handle(stream)), "hpc_probe_copy")
+
+
+# ------------------------------------------------------ per-step driver ---
+
+class DecodeStep:
+    """Buffers for repeated decode steps: plan, upload, attend.
+
+    Holds two pinned host plan buffers (the host plans step n+1 while step
+    n's upload may still be queued; an event guards reuse), one device plan
+    buffer and a workspace that grows on demand.  All work is queued on one
+    stream, so device buffers need no further synchronisation.
+    """
+
+    def __init__(self, num_q_heads: int, num_kv_heads: int, max_batch: int, n_workers: int,
+                 device="cuda", stream=None):
+        self.num_q_heads, self.num_kv_heads = int(num_q_heads), int(num_kv_heads)
+        self.n_workers = int(n_workers)
+        self.device = torch.device(device)
+        self.stream = stream
+        cap = hpc_decode_plan_size(max_batch, num_kv_heads, n_workers)
+        self.max_batch = int(max_batch)
+        self._host = [torch.empty(cap, dtype=torch.int32, pin_memory=True) for _ in range(2)]
+        self._host_ready = [None, None]
+        self._flip = 0
+        self.plan_dev = torch.empty(cap, dtype=torch.int32, device=self.device)
+        self.workspace = torch.empty(0, dtype=torch.uint8, device=self.device)
+        self.plan_host = None
+
+    def _stream(self):
+        return self.stream if self.stream is not None else torch.cuda.current_stream(self.device)
+
+    def plan(self, seq_lens_host) -> np.ndarray:
+        """Schedule this step's lengths and queue the plan's upload; returns the host plan."""
+        lens = _host_i32(seq_lens_host).reshape(-1)
+        if lens.shape[0] > self.max_batch:
+            raise ValueError("batch larger than max_batch")
+        i = self._flip
+        self._flip ^= 1
+        if self._host_ready[i] is not None:
+            self._host_ready[i].synchronize()     # its previous upload has left the buffer
+        words = hpc_decode_plan(lens, self.num_kv_heads, self.n_workers, out=self._host[i])
+        n = words.shape[0]
+        s = self._stream()
+        with torch.cuda.stream(s):
+            self.plan_dev[:n].copy_(self._host[i][:n], non_blocking=True)
+            ev = torch.cuda.Event()
+            ev.record(s)
+        self._host_ready[i] = ev
+        need = hpc_decode_workspace_size(words, self.num_q_heads, self.num_kv_heads)
+        if need > self.workspace.numel():
+            self.workspace = torch.empty(max(need, 2 * self.workspace.numel()), dtype=torch.uint8,
+                                         device=self.device)
+        self.plan_host = words
+        return words
+
+    def attend(self, q, k_cache, v_cache, block_table, seq_lens_dev, out=None, lse=None, *,
+               sm_scale, k_scale=1.0, v_scale=1.0):
+        if self.plan_host is None:
+            raise RuntimeError("call plan() before attend()")
+        if out is None:
+            out = torch.empty_like(q)
+        if lse is None:
+            lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+        ws = self.workspace if self.workspace.numel() else None
+        hpc_decode_attn(q, k_cache, v_cache, block_table, seq_lens_dev, self.plan_host, self.plan_dev, ws,
+                        out, lse, num_kv_heads=self.num_kv_heads, sm_scale=sm_scale, k_scale=k_scale,
+                        v_scale=v_scale, stream=self._stream())
+        return out, lse
+
+    def __call__(self, seq_lens_host, q, k_cache, v_cache, block_table, seq_lens_dev, out=None, lse=None,
+                 **scales):
+        self.plan(seq_lens_host)
+        return self.attend(q, k_cache, v_cache, block_table, seq_lens_dev, out, lse, **scales)

@@ -1,0 +1,198 @@
+// C ABI entry point of the decode step: host-side validation, then the
+// decode and merge launches on the caller's stream (see hpc_decode.h).
+// Every check below runs before the first HIP call.
+
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdint>
+#include <mutex>
+#include <vector>
+
+#include "hpc_decode.h"
+#include "internal.h"
+
+namespace {
+
+struct ProfileWindow {
+    std::mutex mu;
+    bool active = false;
+    int32_t capacity = 0;
+    int32_t used = 0;
+    std::vector<hipEvent_t> ev;   // 3 per call: before decode, after decode, after merge
+    std::vector<uint8_t> has_combine;
+};
+ProfileWindow g_prof;
+
+void destroy_events() {
+    for (hipEvent_t e : g_prof.ev)
+        if (e) (void)hipEventDestroy(e);
+    g_prof.ev.clear();
+    g_prof.has_combine.clear();
+}
+
+}  // namespace
+
+extern "C" int hpc_decode_check(const hpc_decode_params* p, const void* q, const void* k_cache,
+                                const void* v_cache, const int32_t* block_table,
+                                const int32_t* seq_lens, const int32_t* plan_host,
+                                const int32_t* plan_dev, const void* workspace,
+                                int64_t workspace_bytes, const void* out, const float* lse) {
+    if (!p || !q || !k_cache || !v_cache || !block_table || !seq_lens || !plan_host || !plan_dev ||
+        !out || !lse)
+        return HPC_ERR_NULL;
+    if (p->head_dim != HPC_DECODE_HEAD_DIM || p->page_size != HPC_DECODE_PAGE) return HPC_ERR_UNSUPPORTED;
+    if (p->kv_dtype != HPC_KV_BF16 && p->kv_dtype != HPC_KV_FP8_E4M3) return HPC_ERR_UNSUPPORTED;
+    if (p->num_kv_heads < 1 || p->num_q_heads < p->num_kv_heads || p->num_q_heads % p->num_kv_heads != 0)
+        return HPC_ERR_INVALID;
+    const int32_t G = p->num_q_heads / p->num_kv_heads;
+    if (G > HPC_DECODE_MAX_GROUP) return HPC_ERR_UNSUPPORTED;
+    if (p->max_pages_per_seq < 1 || p->num_pages < 1) return HPC_ERR_INVALID;
+    if (!std::isfinite(p->sm_scale) || !std::isfinite(p->k_scale) || !std::isfinite(p->v_scale))
+        return HPC_ERR_INVALID;
+
+    // plan header against the call
+    const int32_t* hdr = plan_host;
+    if (hdr[0] != HPC_PLAN_VERSION || hdr[8] != HPC_DECODE_PAGE) return HPC_ERR_PLAN_MISMATCH;
+    const int32_t B = hdr[1], Hkv = hdr[2], W = hdr[3], E = hdr[5], P = hdr[6], C = hdr[7];
+    if (Hkv != p->num_kv_heads || B < 0 || W < 1 || E < 0 || P < 0 || C < 0) return HPC_ERR_PLAN_MISMATCH;
+    const int64_t U = static_cast<int64_t>(B) * Hkv;
+    const int32_t* worker_ptr = plan_host + HPC_PLAN_HEADER_WORDS;
+    const int32_t* entries = worker_ptr + (W + 1);
+    const int32_t* combine = entries + 4 * static_cast<int64_t>(E);
+    if (worker_ptr[0] != 0 || worker_ptr[W] != E) return HPC_ERR_PLAN_MISMATCH;
+    for (int32_t w = 0; w < W; ++w)
+        if (worker_ptr[w + 1] < worker_ptr[w]) return HPC_ERR_PLAN_MISMATCH;
+    for (int64_t e = 0; e < E; ++e) {
+        const int32_t u = entries[4 * e], t0 = entries[4 * e + 1], t1 = entries[4 * e + 2],
+                      slot = entries[4 * e + 3];
+        if (u < 0 || u >= U || t0 < 0 || t1 <= t0 || slot < -1 || slot >= P) return HPC_ERR_PLAN_MISMATCH;
+        if (t1 > p->max_pages_per_seq) return HPC_ERR_INVALID;   // a length beyond the block table
+    }
+    for (int64_t c = 0; c < C; ++c) {
+        const int32_t u = combine[3 * c], S = combine[3 * c + 1], base = combine[3 * c + 2];
+        if (u < 0 || u >= U || S < 0 || S == 1 || base < 0 || static_cast<int64_t>(base) + S > P)
+            return HPC_ERR_PLAN_MISMATCH;
+    }
+    const int64_t need = hpc_decode_workspace_size(plan_host, p->num_q_heads, p->num_kv_heads);
+    if (need < 0) return static_cast<int>(need);
+    if (need > 0 && (workspace == nullptr)) return HPC_ERR_NULL;
+    if (workspace_bytes < need) return HPC_ERR_TOO_SMALL;
+    return HPC_OK;
+}
+
+extern "C" int hpc_decode_attn(const hpc_decode_params* p, const void* q, const void* k_cache,
+                               const void* v_cache, const int32_t* block_table,
+                               const int32_t* seq_lens, const int32_t* plan_host,
+                               const int32_t* plan_dev, void* workspace, int64_t workspace_bytes,
+                               void* out, float* lse, void* stream) {
+    const int status = hpc_decode_check(p, q, k_cache, v_cache, block_table, seq_lens, plan_host,
+                                        plan_dev, workspace, workspace_bytes, out, lse);
+    if (status != HPC_OK) return status;
+    const int32_t G = p->num_q_heads / p->num_kv_heads;
+    const int32_t Hkv = plan_host[2], W = plan_host[3], E = plan_host[5], P = plan_host[6],
+                  C = plan_host[7];
+
+    float* o_part = static_cast<float*>(workspace);
+    const int64_t o_bytes = static_cast<int64_t>(P) * G * HPC_DECODE_HEAD_DIM * 4;
+    float* lse_part = P > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + (o_bytes + 255) / 256 * 256)
+                            : nullptr;
+
+    const int64_t e_off = HPC_PLAN_HEADER_WORDS + (W + 1);
+    hpcd::DecodeArgs da{};
+    da.q = q;
+    da.k = k_cache;
+    da.v = v_cache;
+    da.block_table = block_table;
+    da.seq_lens = seq_lens;
+    da.worker_ptr = plan_dev + HPC_PLAN_HEADER_WORDS;
+    da.entries = plan_dev + e_off;
+    da.out = out;
+    da.lse = lse;
+    da.o_part = o_part;
+    da.lse_part = lse_part;
+    da.num_kv_heads = Hkv;
+    da.group = G;
+    da.max_pages_per_seq = p->max_pages_per_seq;
+    da.num_pages = p->num_pages;
+    da.qk_scale_log2 = static_cast<float>(static_cast<double>(p->sm_scale) * p->k_scale * 1.4426950408889634);
+    da.v_scale = p->v_scale;
+
+    hpcd::CombineArgs ca{};
+    ca.combine = plan_dev + e_off + 4 * static_cast<int64_t>(E);
+    ca.o_part = o_part;
+    ca.lse_part = lse_part;
+    ca.out = out;
+    ca.lse = lse;
+    ca.num_kv_heads = Hkv;
+    ca.group = G;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+    int prof_idx = -1;
+    {
+        std::lock_guard<std::mutex> lk(g_prof.mu);
+        if (g_prof.active && g_prof.used < g_prof.capacity) {
+            prof_idx = g_prof.used++;
+            for (int i = 0; i < 3; ++i) ev[i] = g_prof.ev[3 * prof_idx + i];
+            g_prof.has_combine[prof_idx] = C > 0;
+        }
+    }
+    if (prof_idx >= 0 && hipEventRecord(ev[0], s) != hipSuccess) return HPC_ERR_HIP;
+    if (E > 0 && hpcd::launch_decode(da, p->kv_dtype, W, stream) != 0) return HPC_ERR_HIP;
+    if (prof_idx >= 0 && hipEventRecord(ev[1], s) != hipSuccess) return HPC_ERR_HIP;
+    if (C > 0 && hpcd::launch_combine(ca, C, stream) != 0) return HPC_ERR_HIP;
+    if (prof_idx >= 0 && hipEventRecord(ev[2], s) != hipSuccess) return HPC_ERR_HIP;
+    return HPC_OK;
+}
+
+extern "C" int hpc_decode_profile_start(int32_t capacity) {
+    if (capacity < 1) return HPC_ERR_INVALID;
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    destroy_events();
+    g_prof.ev.assign(3 * static_cast<std::size_t>(capacity), nullptr);
+    g_prof.has_combine.assign(static_cast<std::size_t>(capacity), 0);
+    for (hipEvent_t& e : g_prof.ev) {
+        if (hipEventCreate(&e) != hipSuccess) {
+            e = nullptr;
+            destroy_events();
+            g_prof.active = false;
+            return HPC_ERR_HIP;
+        }
+    }
+    g_prof.capacity = capacity;
+    g_prof.used = 0;
+    g_prof.active = true;
+    return HPC_OK;
+}
+
+extern "C" int hpc_decode_profile_stop(double* decode_ms, double* combine_ms, int32_t* n_calls) {
+    if (!decode_ms || !combine_ms || !n_calls) return HPC_ERR_NULL;
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    double dsum = 0.0, csum = 0.0;
+    int rc = HPC_OK;
+    for (int32_t i = 0; i < g_prof.used; ++i) {
+        float a = 0.f, b = 0.f;
+        if (hipEventSynchronize(g_prof.ev[3 * i + 2]) != hipSuccess ||
+            hipEventElapsedTime(&a, g_prof.ev[3 * i], g_prof.ev[3 * i + 1]) != hipSuccess) {
+            rc = HPC_ERR_HIP;
+            break;
+        }
+        dsum += a;
+        if (g_prof.has_combine[i]) {
+            if (hipEventElapsedTime(&b, g_prof.ev[3 * i + 1], g_prof.ev[3 * i + 2]) != hipSuccess) {
+                rc = HPC_ERR_HIP;
+                break;
+            }
+            csum += b;
+        }
+    }
+    *decode_ms = dsum;
+    *combine_ms = csum;
+    *n_calls = g_prof.used;
+    destroy_events();
+    g_prof.active = false;
+    g_prof.used = 0;
+    g_prof.capacity = 0;
+    return rc;
+}

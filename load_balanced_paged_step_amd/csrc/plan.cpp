@@ -1,0 +1,156 @@
+// Per-step tile scheduler and plan bookkeeping (host only, no HIP).
+//
+// Schedule: "vLLM x HPC-Ops: High-Performance Attention and MoE Backends from
+// Tencent Hunyuan", §Attention Backend: Dynamic Load-Balanced Scheduling —
+// every KV sequence is cut into uniform 64-token tiles and tiles are given to
+// the persistent grid's workers by actual work, recomputed each decode step.
+// The partition used is contiguous equal shares floor(w*T/W) of the
+// unit-major tile list; the word layout is documented in hpc_decode.h.
+//
+// Implementation: one forward sweep.  Worker ranges are increasing and
+// contiguous, so a single cursor over the units (advanced past units that end
+// at or before the range start) finds every (worker, unit) overlap in
+// O(W + U) steps.
+
+#include "hpc_decode.h"
+
+#include <cstddef>
+#include <cstdint>
+#include <vector>
+
+namespace {
+
+constexpr int64_t kPage = HPC_DECODE_PAGE;
+
+struct Entry {
+    int32_t unit, t0, t1, slot;
+};
+
+}  // namespace
+
+extern "C" int64_t hpc_decode_plan_size(int32_t batch, int32_t num_kv_heads, int32_t n_workers) {
+    if (batch < 0 || num_kv_heads < 1 || n_workers < 1) return HPC_ERR_INVALID;
+    const int64_t U = static_cast<int64_t>(batch) * num_kv_heads;
+    const int64_t W = n_workers;
+    return HPC_PLAN_HEADER_WORDS + (W + 1) + 4 * (W + U) + 3 * U;
+}
+
+extern "C" int hpc_decode_plan(const int32_t* seq_lens, int32_t batch, int32_t num_kv_heads,
+                               int32_t n_workers, int32_t* plan, int64_t plan_capacity) {
+    if (plan == nullptr || (batch > 0 && seq_lens == nullptr)) return HPC_ERR_NULL;
+    if (batch < 0 || num_kv_heads < 1 || n_workers < 1) return HPC_ERR_INVALID;
+
+    const int64_t H = num_kv_heads;
+    const int64_t U = static_cast<int64_t>(batch) * H;
+    const int64_t W = n_workers;
+
+    // tile offset of every unit: start[u] = sum of n over units before u
+    std::vector<int64_t> start(static_cast<std::size_t>(U) + 1);
+    start[0] = 0;
+    for (int64_t b = 0; b < batch; ++b) {
+        const int32_t L = seq_lens[b];
+        if (L < 0) return HPC_ERR_INVALID;
+        const int64_t tiles = (static_cast<int64_t>(L) + kPage - 1) / kPage;
+        for (int64_t h = 0; h < H; ++h) {
+            const int64_t u = b * H + h;
+            start[u + 1] = start[u] + tiles;
+        }
+    }
+    const int64_t T = start[U];
+    if (T > INT32_MAX - 1) return HPC_ERR_INVALID;
+
+    std::vector<Entry> entries;
+    entries.reserve(static_cast<std::size_t>(W + U));
+    std::vector<int32_t> worker_ptr(static_cast<std::size_t>(W) + 1);
+    int64_t cursor = 0;  // first unit that may still own tiles
+    for (int64_t w = 0; w < W; ++w) {
+        worker_ptr[w] = static_cast<int32_t>(entries.size());
+        int64_t lo = (w * T) / W;
+        const int64_t hi = ((w + 1) * T) / W;
+        while (lo < hi) {
+            while (start[cursor + 1] <= lo) ++cursor;
+            const int64_t end = hi < start[cursor + 1] ? hi : start[cursor + 1];
+            entries.push_back({static_cast<int32_t>(cursor), static_cast<int32_t>(lo - start[cursor]),
+                               static_cast<int32_t>(end - start[cursor]), -1});
+            lo = end;
+        }
+    }
+    worker_ptr[W] = static_cast<int32_t>(entries.size());
+
+    // entries per unit, then partial slot blocks for units split over >= 2 workers
+    std::vector<int32_t> parts(static_cast<std::size_t>(U), 0);
+    for (const Entry& e : entries) ++parts[e.unit];
+    std::vector<int32_t> first_slot(static_cast<std::size_t>(U), 0);
+    int64_t n_partials = 0;
+    int64_t n_combine = 0;
+    for (int64_t u = 0; u < U; ++u) {
+        if (parts[u] >= 2) {
+            first_slot[u] = static_cast<int32_t>(n_partials);
+            n_partials += parts[u];
+        }
+        if (parts[u] != 1) ++n_combine;
+    }
+    std::vector<int32_t> next_slot(first_slot);
+    for (Entry& e : entries)
+        e.slot = parts[e.unit] >= 2 ? next_slot[e.unit]++ : -1;
+
+    const int64_t E = static_cast<int64_t>(entries.size());
+    const int64_t words = HPC_PLAN_HEADER_WORDS + (W + 1) + 4 * E + 3 * n_combine;
+    if (plan_capacity < words) return HPC_ERR_TOO_SMALL;
+
+    int32_t* p = plan;
+    const int32_t header[HPC_PLAN_HEADER_WORDS] = {
+        HPC_PLAN_VERSION, batch, num_kv_heads, n_workers, static_cast<int32_t>(T),
+        static_cast<int32_t>(E), static_cast<int32_t>(n_partials), static_cast<int32_t>(n_combine),
+        HPC_DECODE_PAGE, 0, 0, 0, 0, 0, 0, 0};
+    for (int i = 0; i < HPC_PLAN_HEADER_WORDS; ++i) *p++ = header[i];
+    for (int64_t w = 0; w <= W; ++w) *p++ = worker_ptr[w];
+    for (const Entry& e : entries) {
+        *p++ = e.unit;
+        *p++ = e.t0;
+        *p++ = e.t1;
+        *p++ = e.slot;
+    }
+    for (int64_t u = 0; u < U; ++u) {
+        if (parts[u] == 1) continue;
+        *p++ = static_cast<int32_t>(u);
+        *p++ = parts[u];
+        *p++ = parts[u] >= 2 ? first_slot[u] : 0;
+    }
+    return HPC_OK;
+}
+
+extern "C" int64_t hpc_decode_plan_words(const int32_t* plan) {
+    if (plan == nullptr) return HPC_ERR_NULL;
+    if (plan[0] != HPC_PLAN_VERSION || plan[8] != HPC_DECODE_PAGE) return HPC_ERR_PLAN_MISMATCH;
+    const int64_t W = plan[3], E = plan[5], C = plan[7];
+    if (W < 1 || E < 0 || C < 0) return HPC_ERR_PLAN_MISMATCH;
+    return HPC_PLAN_HEADER_WORDS + (W + 1) + 4 * E + 3 * C;
+}
+
+extern "C" int64_t hpc_decode_workspace_size(const int32_t* plan, int32_t num_q_heads,
+                                             int32_t num_kv_heads) {
+    if (plan == nullptr) return HPC_ERR_NULL;
+    if (plan[0] != HPC_PLAN_VERSION) return HPC_ERR_PLAN_MISMATCH;
+    if (num_kv_heads < 1 || num_q_heads < num_kv_heads || num_q_heads % num_kv_heads != 0)
+        return HPC_ERR_INVALID;
+    const int64_t G = num_q_heads / num_kv_heads;
+    const int64_t P = plan[6];
+    if (P <= 0) return 0;
+    const int64_t o_bytes = P * G * HPC_DECODE_HEAD_DIM * 4;
+    const int64_t lse_off = (o_bytes + 255) / 256 * 256;
+    return lse_off + P * G * 4;
+}
+
+extern "C" const char* hpc_status_string(int status) {
+    switch (status) {
+        case HPC_OK: return "ok";
+        case HPC_ERR_NULL: return "null pointer argument";
+        case HPC_ERR_INVALID: return "invalid size, count or length";
+        case HPC_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+        case HPC_ERR_PLAN_MISMATCH: return "plan does not match the call";
+        case HPC_ERR_TOO_SMALL: return "plan buffer or workspace too small";
+        case HPC_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}

@@ -1,0 +1,57 @@
+// Measurement helpers (see hpc_probe.h): HBM streaming-read probe and a
+// plain 16-byte copy.  Grid-stride loops; every access is within
+// [0, bytes) of the caller's buffers.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hpc_decode.h"
+#include "hpc_probe.h"
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void read_probe_kernel(const u32x4* __restrict__ buf, int64_t n16,
+                                                         float* __restrict__ sink) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+    uint32_t x = 0;
+#pragma unroll 8
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n16; i += stride) {
+        const u32x4 a = __builtin_nontemporal_load(buf + i);
+        x ^= a[0] ^ a[1] ^ a[2] ^ a[3];
+    }
+    for (int off = 32; off >= 1; off >>= 1) x ^= __shfl_xor(x, off);
+    __shared__ uint32_t s[4];
+    if ((threadIdx.x & 63) == 0) s[threadIdx.x >> 6] = x;
+    __syncthreads();
+    if (threadIdx.x == 0) sink[blockIdx.x] = static_cast<float>((s[0] ^ s[1] ^ s[2] ^ s[3]) & 0xffffu);
+}
+
+__global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                   int64_t n16) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+}
+
+}  // namespace
+
+extern "C" int hpc_probe_read(const void* buf, int64_t bytes, float* sink, int32_t n_workgroups, void* stream) {
+    if (!buf || !sink) return HPC_ERR_NULL;
+    if (bytes <= 0 || bytes % 16 != 0 || n_workgroups < 1) return HPC_ERR_INVALID;
+    hipLaunchKernelGGL(read_probe_kernel, dim3(n_workgroups), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const u32x4*>(buf), bytes / 16, sink);
+    return hipGetLastError() == hipSuccess ? HPC_OK : HPC_ERR_HIP;
+}
+
+extern "C" int hpc_probe_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+    if (!src || !dst) return HPC_ERR_NULL;
+    if (bytes <= 0 || bytes % 16 != 0) return HPC_ERR_INVALID;
+    const int64_t n16 = bytes / 16;
+    int64_t blocks = (n16 + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    hipLaunchKernelGGL(copy_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const u32x4*>(src),
+                       static_cast<u32x4*>(dst), n16);
+    return hipGetLastError() == hipSuccess ? HPC_OK : HPC_ERR_HIP;
+}

@@ -1,0 +1,66 @@
+"""Shared helpers for the GPU parity tests: run the HIP path through the C ABI
+and the float64 oracle on the same seeded inputs, and compare."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import load_balanced_paged_step_amd as hd
+from oracle import decode_attention, cache_bits_to_f64
+
+# max-abs output tolerance as a fraction of max|V| (V dequantised), per KV type
+OUT_TOL = {"bf16": 1e-2, "fp8_e4m3": 3e-2}
+# absolute log-sum-exp tolerance (natural log)
+LSE_TOL = {"bf16": 1e-3, "fp8_e4m3": 1e-2}
+
+
+def announce(msg: str) -> None:
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+def to_device(inp, device="cuda"):
+    return dict(q=inp.q.to(device), k=inp.k_cache.to(device), v=inp.v_cache.to(device),
+                bt=inp.block_table.to(device), sl=inp.seq_lens.to(device))
+
+
+def run_hip(inp, n_workers: int, dev=None, return_step=False):
+    """One decode step through DecodeStep (C++ planner, upload, HIP kernels)."""
+    if dev is None:
+        dev = to_device(inp)
+    step = hd.DecodeStep(inp.num_q_heads, inp.num_kv_heads, inp.batch, n_workers)
+    step.plan(inp.seq_lens)
+    out, lse = step.attend(dev["q"], dev["k"], dev["v"], dev["bt"], dev["sl"], sm_scale=inp.sm_scale,
+                           k_scale=inp.k_scale, v_scale=inp.v_scale)
+    torch.cuda.synchronize()
+    res = (out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64))
+    return (res + (step,)) if return_step else res
+
+
+def run_oracle(inp):
+    return decode_attention(inp.q_bits(), inp.k_bits(), inp.v_bits(), inp.block_table.numpy(),
+                            inp.seq_lens.numpy(), num_q_heads=inp.num_q_heads,
+                            num_kv_heads=inp.num_kv_heads, kv_format=inp.kv_dtype,
+                            sm_scale=inp.sm_scale, k_scale=inp.k_scale, v_scale=inp.v_scale)
+
+
+def max_abs_v(inp) -> float:
+    v = cache_bits_to_f64(inp.v_bits(), inp.kv_dtype) * inp.v_scale
+    v = v[np.isfinite(v)]
+    return float(np.abs(v).max()) if v.size else 1.0
+
+
+def compare(inp, got, ref, what=""):
+    """Assert the HIP result is within tolerance of the oracle; returns error stats."""
+    out, lse = got
+    ref_out, ref_lse = ref
+    tol = OUT_TOL[inp.kv_dtype] * max_abs_v(inp)
+    assert np.all(np.isfinite(out)), f"{what}: non-finite output"
+    err = np.abs(out - ref_out)
+    max_err = float(err.max()) if err.size else 0.0
+    assert max_err <= tol, f"{what}: max|out-ref| = {max_err:.3e} > {tol:.3e}"
+    neg = np.isneginf(ref_lse)
+    assert np.array_equal(np.isneginf(lse), neg), f"{what}: -inf pattern of lse differs"
+    lse_err = float(np.abs(lse[~neg] - ref_lse[~neg]).max()) if (~neg).any() else 0.0
+    assert lse_err <= LSE_TOL[inp.kv_dtype], f"{what}: max|lse-ref| = {lse_err:.3e}"
+    assert np.all(out[neg.nonzero()] == 0), f"{what}: empty sequences must give zeros"
+    return {"max_err": max_err, "tol": tol, "lse_err": lse_err}

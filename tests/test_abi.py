@@ -1,0 +1,188 @@
+"""C-ABI tests that need no GPU: the library loads, exports every declared
+symbol, its C++ planner equals the oracle's schedule word for word, and every
+host-checkable error is reported before anything is launched."""
+import ctypes
+import glob
+import os
+import re
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+import load_balanced_paged_step_amd as hd
+from load_balanced_paged_step_amd import _lib
+from oracle.plan import build_plan, plan_size_words
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s*(hpc_[A-Za-z0-9_]+)\s*\(",
+                             text, flags=re.M):
+            names.add(m.group(1))
+    return sorted(names)
+
+
+def test_library_exports_every_declared_function():
+    names = _declared_functions()
+    assert "hpc_decode_plan" in names and "hpc_decode_attn" in names and len(names) >= 10
+    lib = _lib.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in _lib.SIGNATURES, f"{n} has no ctypes signature"
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        assert hd.hpc_status_string(code) != "unknown status"
+    assert hd.hpc_status_string(-99) == "unknown status"
+
+
+def _cpp_plan(lens, H, W):
+    return hd.hpc_decode_plan(np.asarray(lens, dtype=np.int32), H, W)
+
+
+@pytest.mark.parametrize("lens,H,W", [
+    ([37, 64, 130, 200], 1, 4), ([0, 100, 10], 2, 4), ([65], 1, 5), ([1, 0, 128], 1, 1),
+    ([131072] + [4096] * 31, 1, 256), ([131072] + [4096] * 31, 1, 1024), ([512] * 64, 1, 256),
+    ([1024] * 8, 1, 256), ([0, 0, 0], 8, 7), ([5000] * 3, 8, 700),
+])
+def test_cpp_plan_equals_oracle(lens, H, W):
+    got = _cpp_plan(lens, H, W)
+    ref = build_plan(lens, H, W)
+    assert got.dtype == np.int32 and np.array_equal(got, ref)
+    assert hd.hpc_decode_plan_size(len(lens), H, W) == plan_size_words(len(lens), H, W)
+
+
+def test_cpp_plan_exhaustive_small():
+    for L in range(0, 131):
+        for H in (1, 2):
+            for W in range(1, 10):
+                assert np.array_equal(_cpp_plan([L], H, W), build_plan([L], H, W))
+    vals = [0, 1, 63, 64, 65, 128, 129]
+    for a in vals:
+        for b in vals:
+            for W in (1, 2, 3, 5, 8):
+                assert np.array_equal(_cpp_plan([a, b], 2, W), build_plan([a, b], 2, W))
+
+
+@settings(max_examples=300, deadline=None)
+@given(lens=st.lists(st.integers(0, 70000), min_size=0, max_size=48), H=st.integers(1, 8),
+       W=st.integers(1, 1500))
+def test_cpp_plan_random(lens, H, W):
+    assert np.array_equal(_cpp_plan(lens, H, W), build_plan(lens, H, W))
+
+
+def test_workspace_size():
+    plan = _cpp_plan([131072] + [4096] * 31, 1, 256)
+    P = int(plan[6])
+    o = P * 8 * 128 * 4
+    assert hd.hpc_decode_workspace_size(plan, 8, 1) == (o + 255) // 256 * 256 + P * 8 * 4
+    assert hd.hpc_decode_workspace_size(_cpp_plan([64], 1, 1), 8, 1) == 0
+
+
+def test_plan_errors():
+    lib = _lib.lib()
+    buf = np.zeros(1000, dtype=np.int32)
+    lens = np.array([10, 20], dtype=np.int32)
+    p = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    assert lib.hpc_decode_plan(p(lens), 2, 1, 0, p(buf), 1000) == hd.HPC_ERR_INVALID
+    assert lib.hpc_decode_plan(p(lens), 2, 0, 4, p(buf), 1000) == hd.HPC_ERR_INVALID
+    assert lib.hpc_decode_plan(p(lens), -1, 1, 4, p(buf), 1000) == hd.HPC_ERR_INVALID
+    assert lib.hpc_decode_plan(None, 2, 1, 4, p(buf), 1000) == hd.HPC_ERR_NULL
+    assert lib.hpc_decode_plan(p(lens), 2, 1, 4, None, 1000) == hd.HPC_ERR_NULL
+    assert lib.hpc_decode_plan(p(lens), 2, 1, 4, p(buf), 10) == hd.HPC_ERR_TOO_SMALL
+    neg = np.array([10, -1], dtype=np.int32)
+    assert lib.hpc_decode_plan(p(neg), 2, 1, 4, p(buf), 1000) == hd.HPC_ERR_INVALID
+    huge = np.full(40000, 2 ** 31 - 1, dtype=np.int32)        # T >= 2^31 tiles
+    big = np.zeros(hd.hpc_decode_plan_size(40000, 1, 4), dtype=np.int32)
+    assert lib.hpc_decode_plan(p(huge), 40000, 1, 4, p(big), big.shape[0]) == hd.HPC_ERR_INVALID
+    with pytest.raises(hd.HpcDecodeError):
+        hd.hpc_decode_plan([1, 2], 1, 0)
+    assert lib.hpc_decode_plan_size(-1, 1, 1) < 0 and lib.hpc_decode_plan_size(1, 1, 0) < 0
+
+
+class _Fake:
+    """Host-side stand-ins for device buffers: hpc_decode_check never dereferences them."""
+
+    def __init__(self, lens=(37, 200), H=1, Hq=8, W=4):
+        self.lens = np.asarray(lens, dtype=np.int32)
+        self.plan = _cpp_plan(self.lens, H, W).copy()
+        self.params = hd.make_params(Hq, H, 4, 8, hd.HPC_KV_BF16, 1 / np.sqrt(128))
+        self.ws = hd.hpc_decode_workspace_size(self.plan, Hq, H)
+        self.ptr = ctypes.c_void_p(0x1000)
+
+    def check(self, **over):
+        lib = _lib.lib()
+        a = dict(p=ctypes.byref(self.params), q=self.ptr, k=self.ptr, v=self.ptr, bt=self.ptr,
+                 sl=self.ptr, ph=self.plan.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                 pd=self.ptr, ws=self.ptr, wsb=self.ws, out=self.ptr, lse=self.ptr)
+        a.update(over)
+        return lib.hpc_decode_check(a["p"], a["q"], a["k"], a["v"], a["bt"], a["sl"], a["ph"], a["pd"],
+                                    a["ws"], a["wsb"], a["out"], a["lse"])
+
+
+def test_check_accepts_a_consistent_call():
+    assert _Fake().check() == hd.HPC_OK
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "bt", "sl", "ph", "pd", "out", "lse", "p"])
+def test_check_null_pointers(field):
+    assert _Fake().check(**{field: None}) == hd.HPC_ERR_NULL
+
+
+def test_check_null_workspace_only_when_needed():
+    f = _Fake()
+    assert f.ws > 0 and f.check(ws=None) == hd.HPC_ERR_NULL
+    g = _Fake(lens=(64,), W=1)
+    assert g.ws == 0 and g.check(ws=None, wsb=0) == hd.HPC_OK
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("head_dim", 64, hd.HPC_ERR_UNSUPPORTED), ("page_size", 16, hd.HPC_ERR_UNSUPPORTED),
+    ("kv_dtype", 7, hd.HPC_ERR_UNSUPPORTED),
+    ("num_q_heads", 0, hd.HPC_ERR_INVALID), ("num_kv_heads", 0, hd.HPC_ERR_INVALID),
+    ("max_pages_per_seq", 0, hd.HPC_ERR_INVALID), ("num_pages", 0, hd.HPC_ERR_INVALID),
+    ("sm_scale", float("nan"), hd.HPC_ERR_INVALID), ("v_scale", float("inf"), hd.HPC_ERR_INVALID),
+])
+def test_check_bad_params(field, value, code):
+    f = _Fake()
+    setattr(f.params, field, value)
+    assert f.check() == code
+
+
+def test_check_heads_not_a_multiple():
+    f = _Fake(H=2, Hq=16)
+    f.params.num_q_heads = 9
+    assert f.check() == hd.HPC_ERR_INVALID
+
+
+def test_check_group_too_large():
+    f = _Fake(Hq=32)
+    assert f.check() == hd.HPC_ERR_UNSUPPORTED
+
+
+def test_check_plan_mismatches():
+    f = _Fake()
+    assert f.check(wsb=f.ws - 1) == hd.HPC_ERR_TOO_SMALL
+    f.params.max_pages_per_seq = 3            # the 200-token sequence needs 4 pages
+    assert f.check() == hd.HPC_ERR_INVALID
+    g = _Fake(H=2, Hq=16)
+    g.params.num_kv_heads = 1
+    g.params.num_q_heads = 8
+    assert g.check() == hd.HPC_ERR_PLAN_MISMATCH
+    for word, bad in [(0, 2), (8, 32), (16, 1)]:
+        h = _Fake()
+        h.plan[word] = bad
+        assert h.check() == hd.HPC_ERR_PLAN_MISMATCH
+    k = _Fake()
+    e0 = 16 + int(k.plan[3]) + 1
+    k.plan[e0 + 2] = k.plan[e0 + 1]            # empty tile range
+    assert k.check() == hd.HPC_ERR_PLAN_MISMATCH
+    m = _Fake()
+    m.plan[e0 + 3] = int(m.plan[6])            # slot beyond n_partials
+    assert m.check() == hd.HPC_ERR_PLAN_MISMATCH
