@@ -322,12 +322,17 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
 }
 
 // Merge of split units: one workgroup per (merge record, query head of the
-// group).  Thread t handles dims 4*(t & 31) .. +3 over partials i = t>>5 (mod 8),
-// then the eight partial sums meet in LDS.
+// group), 1024 threads = 32 partial lanes x 32 dim quads.  Lane pl folds the
+// partials i = pl, pl + 32, ... into a running (max, weighted sum, weight)
+// triple, issuing up to eight partials' loads before using any of them; the
+// 32 triples then meet in LDS and are merged once more by log-sum-exp.
+constexpr int kMergeLanes = kCombineThreads / 32;
+constexpr int kMergeUnroll = 8;
+
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a) {
-    __shared__ f32x4 s_acc[8][32];
-    __shared__ float s_w[8];
-    __shared__ float s_max[kCombineThreads / 64];
+    __shared__ f32x4 s_acc[kMergeLanes][32];
+    __shared__ float s_m[kMergeLanes];
+    __shared__ float s_w[kMergeLanes];
 
     const int G = a.group;
     const int c = blockIdx.x / G;
@@ -350,48 +355,70 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
         return;
     }
 
-    float M = -INFINITY;
-    for (int i = t; i < S; i += kCombineThreads)
-        M = fmaxf(M, a.lse_part[static_cast<int64_t>(base + i) * G + n]);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    if ((t & 63) == 0) s_max[t >> 6] = M;
-    __syncthreads();
-    M = s_max[0];
-#pragma unroll
-    for (int w = 1; w < kCombineThreads / 64; ++w) M = fmaxf(M, s_max[w]);
-    const float M_use = (M == -INFINITY) ? 0.f : M;
-
+    float m = -INFINITY;          // running max of the folded lse values (log2 units)
+    float w = 0.f;                // running sum of 2^(lse - m)
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    float wsum = 0.f;
-    for (int i = pl; i < S; i += 8) {
-        const int64_t p = static_cast<int64_t>(base + i) * G + n;
-        const float wgt = __builtin_amdgcn_exp2f((a.lse_part[p] - M_use) * kLog2e);
-        const f32x4 o = *reinterpret_cast<const f32x4*>(a.o_part + p * kHeadDim + 4 * dq);
-        acc += wgt * o;
-        wsum += wgt;
+    for (int i0 = pl; i0 < S; i0 += kMergeLanes * kMergeUnroll) {
+        float l[kMergeUnroll];
+        f32x4 o[kMergeUnroll];
+#pragma unroll
+        for (int k = 0; k < kMergeUnroll; ++k) {
+            const int i = i0 + k * kMergeLanes;
+            const int64_t p = static_cast<int64_t>(base + (i < S ? i : 0)) * G + n;
+            l[k] = (i < S) ? a.lse_part[p] * kLog2e : -INFINITY;
+            o[k] = *reinterpret_cast<const f32x4*>(a.o_part + p * kHeadDim + 4 * dq);
+        }
+        float mk = m;
+#pragma unroll
+        for (int k = 0; k < kMergeUnroll; ++k) mk = fmaxf(mk, l[k]);
+        const float m_use = (mk == -INFINITY) ? 0.f : mk;
+        const float f = __builtin_amdgcn_exp2f(m - m_use);
+        acc *= f;
+        w *= f;
+#pragma unroll
+        for (int k = 0; k < kMergeUnroll; ++k) {
+            const float e = __builtin_amdgcn_exp2f(l[k] - m_use);
+            acc += e * o[k];
+            w += e;
+        }
+        m = mk;
     }
     s_acc[pl][dq] = acc;
-    if (dq == 0) s_w[pl] = wsum;
+    if (dq == 0) {
+        s_m[pl] = m;
+        s_w[pl] = w;
+    }
     __syncthreads();
     if (pl == 0) {
-        f32x4 r = s_acc[0][dq];
-        float ws = s_w[0];
+        float M = -INFINITY;
 #pragma unroll
-        for (int j = 1; j < 8; ++j) {
-            r += s_acc[j][dq];
-            ws += s_w[j];
+        for (int j = 0; j < kMergeLanes; ++j) M = fmaxf(M, s_m[j]);
+        const float M_use = (M == -INFINITY) ? 0.f : M;
+        f32x4 r = f32x4{0.f, 0.f, 0.f, 0.f};
+        float ws = 0.f;
+#pragma unroll 8
+        for (int j = 0; j < kMergeLanes; ++j) {
+            const float e = __builtin_amdgcn_exp2f(s_m[j] - M_use);
+            r += e * s_acc[j][dq];
+            ws += e * s_w[j];
         }
         const float inv = ws > 0.f ? 1.f / ws : 0.f;
-        bf16x4 ov = bf16x4{static_cast<__bf16>(r[0] * inv), static_cast<__bf16>(r[1] * inv),
-                           static_cast<__bf16>(r[2] * inv), static_cast<__bf16>(r[3] * inv)};
+        const bf16x4 ov = bf16x4{static_cast<__bf16>(r[0] * inv), static_cast<__bf16>(r[1] * inv),
+                                 static_cast<__bf16>(r[2] * inv), static_cast<__bf16>(r[3] * inv)};
         *reinterpret_cast<bf16x4*>(out + 4 * dq) = ov;
-        if (dq == 0) a.lse[row] = ws > 0.f ? M + __logf(ws) : -INFINITY;
+        if (dq == 0) a.lse[row] = ws > 0.f ? (M + __log2f(ws)) * kLn2 : -INFINITY;
     }
 }
 
-constexpr int kPrefetchBf16 = 4;
-constexpr int kPrefetchFp8 = 4;
+// tiles in flight per wave (register ring depth)
+#ifndef HPC_DECODE_PREFETCH_BF16
+#define HPC_DECODE_PREFETCH_BF16 4
+#endif
+#ifndef HPC_DECODE_PREFETCH_FP8
+#define HPC_DECODE_PREFETCH_FP8 4
+#endif
+constexpr int kPrefetchBf16 = HPC_DECODE_PREFETCH_BF16;
+constexpr int kPrefetchFp8 = HPC_DECODE_PREFETCH_FP8;
 
 }  // namespace
 

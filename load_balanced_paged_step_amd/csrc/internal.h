@@ -10,7 +10,7 @@ constexpr int kHeadDim = 128;
 constexpr int kPage = 64;
 constexpr int kWaves = 4;                 // waves per decode workgroup
 constexpr int kDecodeThreads = 64 * kWaves;
-constexpr int kCombineThreads = 256;
+constexpr int kCombineThreads = 1024;
 
 struct DecodeArgs {
     const void* q;               // bf16 [B][Hq][128]
