@@ -1,9 +1,13 @@
 #!/usr/bin/env python3
 """Decode-step benchmark on one MI355X.
 
-A step is the whole hot path for one batch: the per-step host schedule
-(C++ planner), the plan upload, the persistent decode kernel and the
-log-sum-exp merge kernel.  Default workload: the skewed batch of one
+A step is the whole hot path for one batch: the per-step schedule (64-token
+tiles spread evenly over the persistent grid), the decode kernel, and the
+log-sum-exp merge of split sequences.  With --schedule device (default) the
+schedule is derived inside the single decode kernel from the lengths on the
+GPU and the merge is fused into it; with --schedule host the C++ planner runs
+on the host every step, the plan is uploaded, and a merge kernel follows the
+decode kernel.  Default workload: the skewed batch of one
 131072-token sequence and 31 sequences of 4096 tokens, 8 query heads over one
 KV head, head dim 128, bf16 KV in 64-token pages, shuffled block table
 ("vLLM x HPC-Ops ...", §Attention Decode under Mixed-Length Batches).
@@ -43,6 +47,9 @@ def parse_args():
     ap.add_argument("--copies", type=int, default=0, help="rotating KV copies (0: enough for >= 1 GiB)")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--probe", action="store_true", help="also measure the HBM streaming-read ceiling")
+    ap.add_argument("--schedule", choices=["device", "host"], default="device",
+                    help="device: kernels derive the per-step schedule from the lengths on the GPU; "
+                         "host: C++ planner on the host + plan upload every step")
     return ap.parse_args()
 
 
@@ -109,13 +116,22 @@ def main() -> int:
     vs = [v0] + [v0.clone() for _ in range(copies - 1)]
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
-    step = hd.DecodeStep(inp.num_q_heads, inp.num_kv_heads, inp.batch, W, device=dev)
     lens_host = inp.seq_lens.numpy()
     scales = dict(sm_scale=inp.sm_scale, k_scale=inp.k_scale, v_scale=inp.v_scale)
+    if args.schedule == "device":
+        ws = torch.zeros(hd.hpc_decode_step_workspace_size(inp.batch, inp.num_q_heads, inp.num_kv_heads, W),
+                         dtype=torch.uint8, device=dev)
+        launchers = [hd.StepLauncher(q, ks[c], vs[c], bt, sl, out, lse, num_kv_heads=inp.num_kv_heads,
+                                     n_workers=W, workspace=ws, **scales) for c in range(copies)]
 
-    def one_step(i: int) -> None:
-        step.plan(lens_host)
-        step.attend(q, ks[i % copies], vs[i % copies], bt, sl, out, lse, **scales)
+        def one_step(i: int) -> None:
+            launchers[i % copies]()
+    else:
+        step = hd.DecodeStep(inp.num_q_heads, inp.num_kv_heads, inp.batch, W, device=dev)
+
+        def one_step(i: int) -> None:
+            step.plan(lens_host)
+            step.attend(q, ks[i % copies], vs[i % copies], bt, sl, out, lse, **scales)
 
     log(f"warmup {args.warmup} steps")
     for i in range(args.warmup):
@@ -176,7 +192,7 @@ def main() -> int:
             "workload": wl.name, "batch": inp.batch, "kv_lens": _lens_summary(lens_host),
             "num_q_heads": inp.num_q_heads, "num_kv_heads": inp.num_kv_heads, "head_dim": 128,
             "page_size": 64, "kv_dtype": inp.kv_dtype, "n_workers": W, "kv_copies": copies,
-            "algorithmic_bytes": alg_bytes, "parallelism": "single GPU",
+            "algorithmic_bytes": alg_bytes, "schedule": args.schedule, "parallelism": "single GPU",
         },
         "kernels": {"decode_us": round(decode_us, 3), "merge_us": round(combine_us, 3),
                     "plan_host_us": round(plan_us, 2), "timed_calls": n_calls},

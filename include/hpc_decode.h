@@ -160,12 +160,65 @@ int hpc_decode_check(const hpc_decode_params* params, const void* q, const void*
                      const int32_t* plan_host, const int32_t* plan_dev, const void* workspace,
                      int64_t workspace_bytes, const void* out, const float* lse);
 
+/*
+ * Device-scheduled decode step (no host plan).  The same per-step schedule
+ * as hpc_decode_plan (§Attention Backend: Dynamic Load-Balanced Scheduling)
+ * is derived inside the decode kernel from the device copy of the lengths:
+ * every workgroup scans the tile counts of the batch in LDS and finds its
+ * own tile range, entries and partial slots in closed form.  The first
+ * worker of each split sequence also writes that sequence's merge record
+ * into the workspace, and the merge kernel launched after it combines the
+ * partials by log-sum-exp; empty sequences are written by the decode kernel.
+ * Nothing crosses from the host per step except the two launches, so the
+ * call can be captured in a HIP graph.
+ *
+ * batch        sequences in q / block_table / seq_lens (1 .. 4096)
+ * n_workers    persistent workgroups W (the plan's W)
+ * seq_lens     device int32 [batch]; lengths are clamped to
+ *              [0, max_pages_per_seq * 64] so no read leaves the block table
+ * workspace    device, >= hpc_decode_step_workspace_size(batch, Hq, H_kv, W);
+ *              calls that may run concurrently (other streams) need
+ *              separate workspaces
+ * Other arguments as for hpc_decode_attn.  Errors as hpc_decode_attn, plus
+ * HPC_ERR_UNSUPPORTED for batch > 4096 and HPC_ERR_INVALID when
+ * batch * max_pages_per_seq * H_kv does not fit in int32.
+ */
+int hpc_decode_step(const hpc_decode_params* params, int32_t batch, int32_t n_workers, const void* q,
+                    const void* k_cache, const void* v_cache, const int32_t* block_table,
+                    const int32_t* seq_lens, void* workspace, int64_t workspace_bytes, void* out,
+                    float* lse, void* stream);
+
+/* The host-side checks of hpc_decode_step alone (never calls HIP). */
+int hpc_decode_step_check(const hpc_decode_params* params, int32_t batch, int32_t n_workers,
+                          const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_table, const int32_t* seq_lens, const void* workspace,
+                          int64_t workspace_bytes, const void* out, const float* lse);
+
+/* Workspace bytes hpc_decode_step needs for any lengths: room for
+ * P = W + batch * H_kv partials (a bound on the split entries of any
+ * schedule): fp32 outputs [P][G][128], then (256-byte aligned) fp32 lse
+ * [P][G], then (aligned) int32 merge records [W][3]. */
+int64_t hpc_decode_step_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                       int32_t n_workers);
+
+/*
+ * The device-derived schedule written out on `stream` into device `plan`
+ * (int32 words, capacity >= hpc_decode_plan_size) in exactly the layout of
+ * hpc_decode_plan, so the two can be compared word for word.  One
+ * workgroup; limits: batch <= 2048, n_workers <= 2048, batch * H_kv <= 4096
+ * (else HPC_ERR_UNSUPPORTED).  Lengths are clamped as in hpc_decode_step.
+ */
+int hpc_decode_plan_device(const int32_t* seq_lens, int32_t batch, int32_t num_kv_heads,
+                           int32_t n_workers, int32_t max_pages_per_seq, int32_t* plan,
+                           int64_t plan_capacity, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* hpc_status_string(int status);
 
 /*
  * Optional profiling window (measurement only; global state, not
- * thread-safe).  Between start and stop every hpc_decode_attn call brackets
+ * thread-safe).  Between start and stop every hpc_decode_attn or
+ * hpc_decode_step call brackets
  * its decode-kernel launch and its merge-kernel launch with HIP events on
  * the call's stream (at most `capacity` calls are recorded).  stop
  * synchronises those events and returns the summed durations in ms and the

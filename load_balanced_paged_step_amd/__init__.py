@@ -26,7 +26,9 @@ from ._lib import (HPC_OK, HPC_ERR_NULL, HPC_ERR_INVALID, HPC_ERR_UNSUPPORTED, H
 __all__ = [
     "hpc_decode_plan_size", "hpc_decode_plan", "hpc_decode_plan_words", "hpc_decode_workspace_size",
     "hpc_decode_check", "hpc_decode_attn", "hpc_status_string", "hpc_decode_profile_start",
-    "hpc_decode_profile_stop", "hpc_probe_read", "hpc_probe_copy", "DecodeStep", "HpcDecodeError",
+    "hpc_decode_profile_stop", "hpc_probe_read", "hpc_probe_copy", "hpc_decode_step",
+    "hpc_decode_step_check", "hpc_decode_step_workspace_size", "hpc_decode_plan_device", "StepLauncher",
+    "DecodeStep", "HpcDecodeError",
     "kv_dtype_code", "make_params", "HPC_KV_BF16", "HPC_KV_FP8_E4M3",
 ]
 
@@ -173,6 +175,98 @@ def hpc_decode_attn(q, k_cache, v_cache, block_table, seq_lens, plan_host, plan_
     args, _ = _attn_args(q, k_cache, v_cache, block_table, seq_lens, plan_host, plan_dev, workspace, out,
                          lse, num_kv_heads, sm_scale, k_scale, v_scale)
     _lib.check(lib().hpc_decode_attn(*args, _stream_handle(stream)), "hpc_decode_attn")
+
+
+# -------------------------------------------- device-scheduled decode step ---
+
+def hpc_decode_step_workspace_size(batch: int, num_q_heads: int, num_kv_heads: int, n_workers: int) -> int:
+    return _lib.check(lib().hpc_decode_step_workspace_size(batch, num_q_heads, num_kv_heads, n_workers),
+                      "hpc_decode_step_workspace_size")
+
+
+def _step_args(q, k_cache, v_cache, block_table, seq_lens, workspace, out, lse, num_kv_heads, n_workers,
+               sm_scale, k_scale, v_scale):
+    if k_cache.dtype != v_cache.dtype or tuple(k_cache.shape) != tuple(v_cache.shape):
+        raise ValueError("k_cache and v_cache must have the same dtype and shape")
+    if q.dim() != 3 or k_cache.dim() != 4 or block_table.dim() != 2 or k_cache.shape[1] != num_kv_heads:
+        raise ValueError("expected q [B,Hq,128], caches [pages,H_kv,64,128], block_table [B,max_pages]")
+    B = q.shape[0]
+    if block_table.shape[0] != B or seq_lens.shape[0] != B:
+        raise ValueError("batch sizes of q, block_table and seq_lens differ")
+    if tuple(out.shape) != tuple(q.shape) or tuple(lse.shape) != tuple(q.shape[:2]):
+        raise ValueError("out must match q's shape and lse must be [B, Hq]")
+    params = make_params(q.shape[1], num_kv_heads, block_table.shape[1], k_cache.shape[0], k_cache.dtype,
+                         sm_scale, k_scale, v_scale, head_dim=q.shape[2], page_size=k_cache.shape[2])
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return (params,
+            (ctypes.c_int32(B), ctypes.c_int32(n_workers),
+             _dev_ptr(q, "q", torch.bfloat16),
+             _dev_ptr(k_cache, "k_cache", (torch.bfloat16, torch.float8_e4m3fn)),
+             _dev_ptr(v_cache, "v_cache", (torch.bfloat16, torch.float8_e4m3fn)),
+             _dev_ptr(block_table, "block_table", torch.int32),
+             _dev_ptr(seq_lens, "seq_lens", torch.int32),
+             _dev_ptr(workspace, "workspace", allow_none=True),
+             ctypes.c_int64(ws_bytes),
+             _dev_ptr(out, "out", torch.bfloat16),
+             _dev_ptr(lse, "lse", torch.float32)))
+
+
+def hpc_decode_step_check(q, k_cache, v_cache, block_table, seq_lens, workspace, out, lse, *, num_kv_heads,
+                          n_workers, sm_scale, k_scale=1.0, v_scale=1.0) -> int:
+    params, args = _step_args(q, k_cache, v_cache, block_table, seq_lens, workspace, out, lse, num_kv_heads,
+                              n_workers, sm_scale, k_scale, v_scale)
+    return lib().hpc_decode_step_check(ctypes.byref(params), *args)
+
+
+def hpc_decode_step(q, k_cache, v_cache, block_table, seq_lens, workspace, out, lse, *, num_kv_heads,
+                    n_workers, sm_scale, k_scale=1.0, v_scale=1.0, stream=None) -> None:
+    """One decode step with the schedule derived on the device from ``seq_lens``."""
+    params, args = _step_args(q, k_cache, v_cache, block_table, seq_lens, workspace, out, lse, num_kv_heads,
+                              n_workers, sm_scale, k_scale, v_scale)
+    _lib.check(lib().hpc_decode_step(ctypes.byref(params), *args, _stream_handle(stream)), "hpc_decode_step")
+
+
+def hpc_decode_plan_device(seq_lens: torch.Tensor, num_kv_heads: int, n_workers: int, max_pages_per_seq: int,
+                           plan: torch.Tensor = None, stream=None) -> torch.Tensor:
+    """The device-derived schedule as plan words (device int32 tensor, host-plan layout)."""
+    B = int(seq_lens.shape[0])
+    cap = hpc_decode_plan_size(B, num_kv_heads, n_workers)
+    if plan is None:
+        plan = torch.zeros(cap, dtype=torch.int32, device=seq_lens.device)
+    _lib.check(lib().hpc_decode_plan_device(_dev_ptr(seq_lens, "seq_lens", torch.int32), B, num_kv_heads,
+                                            n_workers, max_pages_per_seq, _dev_ptr(plan, "plan", torch.int32),
+                                            plan.numel(), _stream_handle(stream)), "hpc_decode_plan_device")
+    return plan
+
+
+class StepLauncher:
+    """A device-scheduled decode step with its arguments marshalled once.
+
+
+    Calling it issues exactly one ``hpc_decode_step`` on the stream given at
+    construction (default: the current stream then); the tensors must stay
+    alive and unchanged in shape for the launcher's lifetime.  Lengths are
+    read from ``seq_lens`` on the device at every call.
+    """
+
+    def __init__(self, q, k_cache, v_cache, block_table, seq_lens, out, lse, *, num_kv_heads, n_workers,
+                 sm_scale, k_scale=1.0, v_scale=1.0, workspace=None, stream=None):
+        need = hpc_decode_step_workspace_size(q.shape[0], q.shape[1], num_kv_heads, n_workers)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        self._keep = (q, k_cache, v_cache, block_table, seq_lens, out, lse, workspace)
+        self.params, args = _step_args(q, k_cache, v_cache, block_table, seq_lens, workspace, out, lse,
+                                       num_kv_heads, n_workers, sm_scale, k_scale, v_scale)
+        self.workspace = workspace
+        self._args = (ctypes.byref(self.params),) + args + (_stream_handle(stream),)
+        status = lib().hpc_decode_step_check(*self._args[:-1])
+        _lib.check(status, "StepLauncher")
+        self._fn = lib().hpc_decode_step
+
+    def __call__(self) -> None:
+        status = self._fn(*self._args)
+        if status:
+            _lib.check(status, "hpc_decode_step")
 
 
 # ------------------------------------------------------------- profiling ---

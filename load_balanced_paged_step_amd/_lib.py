@@ -60,6 +60,14 @@ SIGNATURES = {
                                         _VP, _VP]),
     "hpc_decode_attn": (ctypes.c_int, [_PP, _VP, _VP, _VP, _VP, _VP, _I32P, _VP, _VP, ctypes.c_int64,
                                        _VP, _VP, _VP]),
+    "hpc_decode_step": (ctypes.c_int, [_PP, ctypes.c_int32, ctypes.c_int32, _VP, _VP, _VP, _VP, _VP, _VP,
+                                       ctypes.c_int64, _VP, _VP, _VP]),
+    "hpc_decode_step_check": (ctypes.c_int, [_PP, ctypes.c_int32, ctypes.c_int32, _VP, _VP, _VP, _VP, _VP,
+                                             _VP, ctypes.c_int64, _VP, _VP]),
+    "hpc_decode_step_workspace_size": (ctypes.c_int64, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                        ctypes.c_int32]),
+    "hpc_decode_plan_device": (ctypes.c_int, [_VP, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                              ctypes.c_int32, _VP, ctypes.c_int64, _VP]),
     "hpc_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "hpc_decode_profile_start": (ctypes.c_int, [ctypes.c_int32]),
     "hpc_decode_profile_stop": (ctypes.c_int, [_F64P, _F64P, _I32P]),

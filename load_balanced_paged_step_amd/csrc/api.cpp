@@ -24,6 +24,16 @@ struct ProfileWindow {
 };
 ProfileWindow g_prof;
 
+// events for one profiled call, or -1 outside a profiling window
+int claim_profile_events(hipEvent_t ev[3], bool has_combine) {
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    if (!g_prof.active || g_prof.used >= g_prof.capacity) return -1;
+    const int idx = g_prof.used++;
+    for (int i = 0; i < 3; ++i) ev[i] = g_prof.ev[3 * static_cast<std::size_t>(idx) + i];
+    g_prof.has_combine[idx] = has_combine ? 1 : 0;
+    return idx;
+}
+
 void destroy_events() {
     for (hipEvent_t e : g_prof.ev)
         if (e) (void)hipEventDestroy(e);
@@ -111,6 +121,8 @@ extern "C" int hpc_decode_attn(const hpc_decode_params* p, const void* q, const 
     da.lse = lse;
     da.o_part = o_part;
     da.lse_part = lse_part;
+    da.batch = plan_host[1];
+    da.max_partials = P;
     da.num_kv_heads = Hkv;
     da.group = G;
     da.max_pages_per_seq = p->max_pages_per_seq;
@@ -126,24 +138,148 @@ extern "C" int hpc_decode_attn(const hpc_decode_params* p, const void* q, const 
     ca.lse = lse;
     ca.num_kv_heads = Hkv;
     ca.group = G;
+    ca.max_partials = P;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
-    int prof_idx = -1;
-    {
-        std::lock_guard<std::mutex> lk(g_prof.mu);
-        if (g_prof.active && g_prof.used < g_prof.capacity) {
-            prof_idx = g_prof.used++;
-            for (int i = 0; i < 3; ++i) ev[i] = g_prof.ev[3 * prof_idx + i];
-            g_prof.has_combine[prof_idx] = C > 0;
-        }
-    }
+    const int prof_idx = claim_profile_events(ev, C > 0);
     if (prof_idx >= 0 && hipEventRecord(ev[0], s) != hipSuccess) return HPC_ERR_HIP;
-    if (E > 0 && hpcd::launch_decode(da, p->kv_dtype, W, stream) != 0) return HPC_ERR_HIP;
+    if (E > 0 && hpcd::launch_decode(da, p->kv_dtype, W, false, stream) != 0) return HPC_ERR_HIP;
     if (prof_idx >= 0 && hipEventRecord(ev[1], s) != hipSuccess) return HPC_ERR_HIP;
     if (C > 0 && hpcd::launch_combine(ca, C, stream) != 0) return HPC_ERR_HIP;
     if (prof_idx >= 0 && hipEventRecord(ev[2], s) != hipSuccess) return HPC_ERR_HIP;
     return HPC_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Device-scheduled step: the kernels derive the schedule from seq_lens.
+
+namespace {
+
+int64_t step_partials_bound(int32_t batch, int32_t num_kv_heads, int32_t n_workers) {
+    return static_cast<int64_t>(n_workers) + static_cast<int64_t>(batch) * num_kv_heads;
+}
+
+int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
+
+// device-scheduled workspace: partial outputs, partial lse, per-worker merge records
+struct StepLayout {
+    int64_t o_off, lse_off, rec_off, total;
+};
+
+StepLayout step_layout(int64_t partials, int64_t G, int64_t n_workers) {
+    StepLayout L{};
+    L.o_off = 0;
+    L.lse_off = align256(partials * G * HPC_DECODE_HEAD_DIM * 4);
+    L.rec_off = align256(L.lse_off + partials * G * 4);
+    L.total = L.rec_off + 3 * n_workers * 4;
+    return L;
+}
+
+}  // namespace
+
+extern "C" int64_t hpc_decode_step_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                                  int32_t n_workers) {
+    if (batch < 0 || n_workers < 1 || num_kv_heads < 1 || num_q_heads < num_kv_heads ||
+        num_q_heads % num_kv_heads != 0)
+        return HPC_ERR_INVALID;
+    return step_layout(step_partials_bound(batch, num_kv_heads, n_workers), num_q_heads / num_kv_heads, n_workers)
+        .total;
+}
+
+extern "C" int hpc_decode_step_check(const hpc_decode_params* p, int32_t batch, int32_t n_workers, const void* q,
+                                     const void* k_cache, const void* v_cache, const int32_t* block_table,
+                                     const int32_t* seq_lens, const void* workspace, int64_t workspace_bytes,
+                                     const void* out, const float* lse) {
+    if (!p || !q || !k_cache || !v_cache || !block_table || !seq_lens || !out || !lse) return HPC_ERR_NULL;
+    if (p->head_dim != HPC_DECODE_HEAD_DIM || p->page_size != HPC_DECODE_PAGE) return HPC_ERR_UNSUPPORTED;
+    if (p->kv_dtype != HPC_KV_BF16 && p->kv_dtype != HPC_KV_FP8_E4M3) return HPC_ERR_UNSUPPORTED;
+    if (p->num_kv_heads < 1 || p->num_q_heads < p->num_kv_heads || p->num_q_heads % p->num_kv_heads != 0)
+        return HPC_ERR_INVALID;
+    if (p->num_q_heads / p->num_kv_heads > HPC_DECODE_MAX_GROUP) return HPC_ERR_UNSUPPORTED;
+    if (p->max_pages_per_seq < 1 || p->num_pages < 1) return HPC_ERR_INVALID;
+    if (!std::isfinite(p->sm_scale) || !std::isfinite(p->k_scale) || !std::isfinite(p->v_scale))
+        return HPC_ERR_INVALID;
+    if (batch < 1 || n_workers < 1) return HPC_ERR_INVALID;
+    if (batch > hpcd::kDeviceSchedMaxBatch) return HPC_ERR_UNSUPPORTED;
+    // every tile index the kernels form must fit in int32
+    if (static_cast<int64_t>(batch) * p->max_pages_per_seq * p->num_kv_heads >= INT32_MAX) return HPC_ERR_INVALID;
+    const int64_t need = hpc_decode_step_workspace_size(batch, p->num_q_heads, p->num_kv_heads, n_workers);
+    if (need < 0) return static_cast<int>(need);
+    if (need > 0 && workspace == nullptr) return HPC_ERR_NULL;
+    if (workspace_bytes < need) return HPC_ERR_TOO_SMALL;
+    return HPC_OK;
+}
+
+extern "C" int hpc_decode_step(const hpc_decode_params* p, int32_t batch, int32_t n_workers, const void* q,
+                               const void* k_cache, const void* v_cache, const int32_t* block_table,
+                               const int32_t* seq_lens, void* workspace, int64_t workspace_bytes, void* out,
+                               float* lse, void* stream) {
+    const int status = hpc_decode_step_check(p, batch, n_workers, q, k_cache, v_cache, block_table, seq_lens,
+                                             workspace, workspace_bytes, out, lse);
+    if (status != HPC_OK) return status;
+    const int32_t G = p->num_q_heads / p->num_kv_heads;
+    const int64_t P = step_partials_bound(batch, p->num_kv_heads, n_workers);
+    const StepLayout L = step_layout(P, G, n_workers);
+    char* ws = static_cast<char*>(workspace);
+    float* o_part = reinterpret_cast<float*>(ws + L.o_off);
+    float* lse_part = reinterpret_cast<float*>(ws + L.lse_off);
+    int32_t* records = reinterpret_cast<int32_t*>(ws + L.rec_off);
+
+    hpcd::DecodeArgs da{};
+    da.q = q;
+    da.k = k_cache;
+    da.v = v_cache;
+    da.block_table = block_table;
+    da.seq_lens = seq_lens;
+    da.out = out;
+    da.lse = lse;
+    da.o_part = o_part;
+    da.lse_part = lse_part;
+    da.merge_records = records;
+    da.batch = batch;
+    da.max_partials = static_cast<int32_t>(P);
+    da.num_kv_heads = p->num_kv_heads;
+    da.group = G;
+    da.max_pages_per_seq = p->max_pages_per_seq;
+    da.num_pages = p->num_pages;
+    da.qk_scale_log2 = static_cast<float>(static_cast<double>(p->sm_scale) * p->k_scale * 1.4426950408889634);
+    da.v_scale = p->v_scale;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+    hpcd::CombineArgs ca{};
+    ca.combine = records;
+    ca.o_part = o_part;
+    ca.lse_part = lse_part;
+    ca.out = out;
+    ca.lse = lse;
+    ca.num_kv_heads = p->num_kv_heads;
+    ca.group = G;
+    ca.max_partials = static_cast<int32_t>(P);
+
+    const int prof_idx = claim_profile_events(ev, true);
+    if (prof_idx >= 0 && hipEventRecord(ev[0], s) != hipSuccess) return HPC_ERR_HIP;
+    if (hpcd::launch_decode(da, p->kv_dtype, n_workers, true, stream) != 0) return HPC_ERR_HIP;
+    if (prof_idx >= 0 && hipEventRecord(ev[1], s) != hipSuccess) return HPC_ERR_HIP;
+    if (hpcd::launch_combine(ca, n_workers, stream) != 0) return HPC_ERR_HIP;
+    if (prof_idx >= 0 && hipEventRecord(ev[2], s) != hipSuccess) return HPC_ERR_HIP;
+    return HPC_OK;
+}
+
+extern "C" int hpc_decode_plan_device(const int32_t* seq_lens, int32_t batch, int32_t num_kv_heads,
+                                      int32_t n_workers, int32_t max_pages_per_seq, int32_t* plan,
+                                      int64_t plan_capacity, void* stream) {
+    if (!seq_lens || !plan) return HPC_ERR_NULL;
+    if (batch < 1 || num_kv_heads < 1 || n_workers < 1 || max_pages_per_seq < 1) return HPC_ERR_INVALID;
+    if (batch > hpcd::kPlanDeviceMaxBatch || n_workers > hpcd::kPlanDeviceMaxWorkers ||
+        static_cast<int64_t>(batch) * num_kv_heads > hpcd::kPlanDeviceMaxUnits)
+        return HPC_ERR_UNSUPPORTED;
+    if (static_cast<int64_t>(batch) * max_pages_per_seq * num_kv_heads >= INT32_MAX) return HPC_ERR_INVALID;
+    if (plan_capacity < hpc_decode_plan_size(batch, num_kv_heads, n_workers)) return HPC_ERR_TOO_SMALL;
+    return hpcd::launch_plan_device(seq_lens, batch, num_kv_heads, n_workers, max_pages_per_seq, plan, stream) == 0
+               ? HPC_OK
+               : HPC_ERR_HIP;
 }
 
 extern "C" int hpc_decode_profile_start(int32_t capacity) {

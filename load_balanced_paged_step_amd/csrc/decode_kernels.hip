@@ -1,34 +1,37 @@
-// Persistent paged GQA decode attention and the log-sum-exp merge, for
-// CDNA4 (gfx950).
+// Persistent paged GQA decode attention, the log-sum-exp merge, and the
+// on-device form of the per-step schedule, for CDNA4 (gfx950).
 //
 // Method: "vLLM x HPC-Ops: High-Performance Attention and MoE Backends from
 // Tencent Hunyuan", §Attention Backend: Dynamic Load-Balanced Scheduling —
-// 64-token KV tiles spread evenly over a persistent grid; a sequence split
-// over several workers is merged afterwards (log-sum-exp, the reading used
-// here; the pages do not describe the merge).  Head shape (8 query heads per
-// KV head, head dim 128): "vLLM und Tencent Hunyuan streamen zwei
-// HPC-Backends ...", §Zwei neue HPC-Backends im vLLM-Ökosystem.  The pages'
-// own kernels target Hopper; nothing of their design is assumed here.
+// 64-token KV tiles spread evenly over a persistent grid, recomputed every
+// decode step; a sequence split over several workers is merged afterwards
+// (log-sum-exp, the reading used here; the pages do not describe the merge).
+// Head shape (8 query heads per KV head, head dim 128): "vLLM und Tencent
+// Hunyuan streamen zwei HPC-Backends ...", §Zwei neue HPC-Backends im
+// vLLM-Ökosystem.  The pages' kernels target Hopper; none of their design is
+// assumed here.
 //
-// Decode kernel (one workgroup = one worker of the plan, 4 waves):
-//  * every wave takes a fixed 16-token slice (rows 16*wave .. 16*wave+15) of
-//    every 64-token tile of the worker's entries and keeps its own online
-//    softmax state; the four states are merged through LDS at the end of
-//    each entry, so a workgroup emits one result per entry;
-//  * K and V rows are read straight from HBM into VGPRs with buffer loads
-//    whose range is the valid part of the page: rows past the sequence end
-//    (and tiles past the entry end, used to keep the prefetch ring
-//    branch-free) come back as zeros without touching memory;
-//  * S = K Q^T on MFMA 16x16x32 bf16 (rows = 16 tokens, columns = the G <= 16
-//    query heads of the group, zero-padded); P V on MFMA 16x16x16 bf16 as
-//    O^T = V^T P^T, with V^T operands built in registers by byte permutes
-//    (each lane holds 4 token rows x 8 dims), so the softmax state and the
-//    accumulator share one lane<->head layout and no LDS is needed per tile;
+// Decode kernel (one workgroup = one worker, 4 waves):
+//  * the worker's tiles come either from the host plan's entries or from the
+//    schedule derived on the device from the lengths (device_schedule.h);
+//    both walk the same tile sequence;
+//  * every wave owns a fixed 16-token slice (rows 16*wave .. +15) of every
+//    64-token tile and keeps its own online-softmax state; at the end of an
+//    entry the four states meet in LDS and one result per entry is written;
+//  * a ring of PF tile slots is kept in flight across entry boundaries: each
+//    slot holds its K/V rows, and for the first tile of an entry also that
+//    entry's Q, so changing sequence never drains the load pipeline;
+//  * K, V and Q are read with buffer loads whose range is the valid part of
+//    the page (rows past a sequence's end, padding heads and ring slots past
+//    the worker's last tile read as zeros without touching memory); K/V use
+//    the nontemporal cache policy, since every byte is read exactly once;
+//  * S = K Q^T on MFMA 16x16x32 bf16 (16 tokens x up to 16 heads, padded);
+//    P V on MFMA 16x16x16 bf16 as O^T = V^T P^T, V^T operands built in
+//    registers by byte permutes (each lane holds 4 token rows x 8 dims);
 //  * fp8 tiles are widened to bf16 exactly (every E4M3FN value is a bf16
-//    value) with the hardware convert; k_scale folds into the score scale,
-//    v_scale into the output.
+//    value); k_scale folds into the score scale, v_scale into the output.
 // Lane layout: lane = n + 16 g (n = lane & 15, g = lane >> 4).
-//   QK:  A = K rows [token n][dims 32g+8kk .. +8], B = Q^T [head n][same dims],
+//   QK:  A = K rows [token n][dims 32kk+8g .. +8], B = Q^T [head n][same dims],
 //        D[token 4g+i][head n] in register i.
 //   PV:  A = V^T [dim 8n+nb][tokens 4g .. 4g+3], B = P^T [tokens 4g+i][head n],
 //        D[dim 8(4g+i)+nb][head n] in register i of accumulator nb.
@@ -36,6 +39,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "device_schedule.h"
 #include "hpc_decode.h"
 #include "internal.h"
 
@@ -44,7 +48,6 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -52,8 +55,12 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw (untyped) buffer, gfx9 family
-constexpr uint32_t kSelLo = 0x05040100u;        // v_perm: low halves of (a, b) -> {a.lo, b.lo}
-constexpr uint32_t kSelHi = 0x07060302u;        // v_perm: high halves -> {a.hi, b.hi}
+#ifndef HPC_DECODE_KV_POLICY
+#define HPC_DECODE_KV_POLICY 2
+#endif
+constexpr int kPolicyStream = HPC_DECODE_KV_POLICY;   // K/V buffer-load cache policy (2: nontemporal)
+constexpr uint32_t kSelLo = 0x05040100u;       // v_perm: low halves of (a, b) -> {a.lo, b.lo}
+constexpr uint32_t kSelHi = 0x07060302u;       // v_perm: high halves -> {a.hi, b.hi}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
@@ -65,6 +72,8 @@ __device__ __forceinline__ To bitcast(const From& x) {
     static_assert(sizeof(To) == sizeof(From), "size mismatch");
     return __builtin_bit_cast(To, x);
 }
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 // two E4M3FN codes (16-bit half HI of x) -> two bf16, exact
 template <bool HI>
@@ -85,16 +94,18 @@ struct KvTile;
 template <>
 struct KvTile<HPC_KV_BF16> {
     static constexpr uint32_t kRow = kHeadDim * 2;   // bytes per token row
-    u32x4 k[4];   // K row 16*wave+n, dims 32g .. 32g+31
+    u32x4 k[4];   // K row 16*wave+n, dims 32kk+8g .. +8 (one 64-byte run per row per load)
     u32x4 v[4];   // V rows 16*wave+4g+i, dims 8n .. 8n+7
     __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
                                          int wave, int n, int g) {
-        const uint32_t ko = (16 * wave + n) * kRow + 64 * g;
+        const uint32_t ko = (16 * wave + n) * kRow + 16 * g;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) k[kk] = __builtin_amdgcn_raw_buffer_load_b128(rk, ko + 16 * kk, 0, 0);
+        for (int kk = 0; kk < 4; ++kk)
+            k[kk] = __builtin_amdgcn_raw_buffer_load_b128(rk, ko + 64 * kk, 0, kPolicyStream);
         const uint32_t vo = (16 * wave + 4 * g) * kRow + 16 * n;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, vo + i * kRow, 0, 0);
+        for (int i = 0; i < 4; ++i)
+            v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, vo + i * kRow, 0, kPolicyStream);
     }
     __device__ __forceinline__ bf16x8 k_op(int kk) const { return bitcast<bf16x8>(k[kk]); }
     __device__ __forceinline__ u32x4 v_row(int i) const { return v[i]; }
@@ -103,49 +114,102 @@ struct KvTile<HPC_KV_BF16> {
 template <>
 struct KvTile<HPC_KV_FP8_E4M3> {
     static constexpr uint32_t kRow = kHeadDim;       // bytes per token row
-    u32x4 k[2];   // K row 16*wave+n, dims 32g .. 32g+31 (fp8)
+    u32x2 k[4];   // K row 16*wave+n, dims 32kk+8g .. +8 (fp8)
     u32x2 v[4];   // V rows 16*wave+4g+i, dims 8n .. 8n+7 (fp8)
     __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
                                          int wave, int n, int g) {
-        const uint32_t ko = (16 * wave + n) * kRow + 32 * g;
-        k[0] = __builtin_amdgcn_raw_buffer_load_b128(rk, ko, 0, 0);
-        k[1] = __builtin_amdgcn_raw_buffer_load_b128(rk, ko + 16, 0, 0);
+        const uint32_t ko = (16 * wave + n) * kRow + 8 * g;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            k[kk] = __builtin_amdgcn_raw_buffer_load_b64(rk, ko + 32 * kk, 0, kPolicyStream);
         const uint32_t vo = (16 * wave + 4 * g) * kRow + 8 * n;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b64(rv, vo + i * kRow, 0, 0);
+        for (int i = 0; i < 4; ++i)
+            v[i] = __builtin_amdgcn_raw_buffer_load_b64(rv, vo + i * kRow, 0, kPolicyStream);
     }
-    __device__ __forceinline__ bf16x8 k_op(int kk) const {
-        const u32x4& src = k[kk >> 1];
-        const int d = 2 * (kk & 1);
-        return bitcast<bf16x8>(fp8x8_to_bf16x8(src[d], src[d + 1]));
-    }
+    __device__ __forceinline__ bf16x8 k_op(int kk) const { return bitcast<bf16x8>(fp8x8_to_bf16x8(k[kk][0], k[kk][1])); }
     __device__ __forceinline__ u32x4 v_row(int i) const { return fp8x8_to_bf16x8(v[i][0], v[i][1]); }
 };
 
+// One slot of the prefetch ring.  Everything but the register arrays is
+// wave-uniform.
 template <int KV>
 struct TileSlot {
-    KvTile<KV> data;
-    int valid;    // valid token rows of the tile (0..64); 0 for a padding slot
+    KvTile<KV> kv;
+    u32x4 q[4];   // Q^T operand of the entry, loaded only for an entry's first tile
+    int real;     // holds a tile of this worker
+    int valid;    // valid token rows (0..64)
+    int first, last;
+    int row;      // b * Hq + h * G: first query head row of the entry
+    int part;     // output target of the entry (see TileRef::part)
 };
 
-// Scalars of the decode launch; the pointers are separate __restrict__
-// kernel arguments so the plan words, block table and lengths are known not
-// to be written by the kernel and load through the scalar unit.
+// Host-planned tile source: walks this worker's entries in the plan words.
+struct HostWalker {
+    const int32_t* entries;
+    const int32_t* seq_lens;
+    int H, e, e_end;
+    int b, h, t, tb, L, part;
+    bool have, at_entry_start;
+
+    __device__ __forceinline__ void load_entry() {
+        have = e < e_end;
+        if (!have) return;
+        const int u = entries[4 * e + 0];
+        b = u / H;
+        h = u - b * H;
+        t = entries[4 * e + 1];
+        tb = entries[4 * e + 2];
+        part = entries[4 * e + 3];
+        L = seq_lens[b];
+        at_entry_start = true;
+        ++e;
+    }
+    __device__ __forceinline__ void init(const int32_t* worker_ptr, const int32_t* ent, const int32_t* lens,
+                                         int num_kv_heads, int w) {
+        entries = ent;
+        seq_lens = lens;
+        H = num_kv_heads;
+        e = worker_ptr[w];
+        e_end = worker_ptr[w + 1];
+        load_entry();
+    }
+    __device__ __forceinline__ bool next(TileRef& r) {
+        if (!have) return false;
+        r.b = b;
+        r.h = h;
+        r.t = t;
+        r.L = L;
+        r.first = at_entry_start;
+        r.last = (t == tb - 1);
+        r.part = part;
+        at_entry_start = false;
+        if (++t == tb) load_entry();
+        return true;
+    }
+};
+
+// Scalars of the decode launch; pointers are separate __restrict__ kernel
+// arguments so plan words, block table and lengths are known read-only and
+// load through the scalar unit.
 struct DecodeScalars {
-    int32_t num_kv_heads, group, max_pages_per_seq, num_pages;
+    int32_t batch, num_kv_heads, group, max_pages_per_seq, num_pages;
+    int32_t max_partials;   // partial slots the workspace holds
     float qk_scale_log2, v_scale;
 };
 
-template <int KV, int PF>
+template <int KV, int PF, bool DEV>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     const __bf16* __restrict__ q, const char* __restrict__ kcache, const char* __restrict__ vcache,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ worker_ptr, const int32_t* __restrict__ entries,
     __bf16* __restrict__ out, float* __restrict__ lse, float* __restrict__ o_part,
-    float* __restrict__ lse_part, DecodeScalars a) {
+    float* __restrict__ lse_part, int32_t* __restrict__ merge_records, DecodeScalars a) {
     __shared__ float s_acc[kWaves][4][8][64];
     __shared__ float s_m[kWaves][64];
     __shared__ float s_l[kWaves][64];
+    __shared__ int32_t s_tmp[2 * kWaves];
+    extern __shared__ int32_t s_dyn[];   // device schedule: len[B], tile prefix[B + 1]
 
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
@@ -154,119 +218,131 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     const int G = a.group;
     const int Hkv = a.num_kv_heads;
     const int Hq = G * Hkv;
+    const int w = blockIdx.x;
     constexpr uint32_t kRow = KvTile<KV>::kRow;
     constexpr uint64_t kBlock = static_cast<uint64_t>(kPage) * kRow;   // one (page, head) block
 
-    const int e_begin = worker_ptr[blockIdx.x];
-    const int e_end = worker_ptr[blockIdx.x + 1];
-
-    for (int e = e_begin; e < e_end; ++e) {
-        const int u = entries[4 * e + 0];
-        const int t0 = entries[4 * e + 1];
-        const int t1 = entries[4 * e + 2];
-        const int slot = entries[4 * e + 3];
-        const int b = u / Hkv;
-        const int h = u - b * Hkv;
-        const int L = seq_lens[b];
-        const int32_t* bt = block_table + static_cast<int64_t>(b) * a.max_pages_per_seq;
-        const char* kbase = kcache;
-        const char* vbase = vcache;
-
-        // Q^T operand: head n, dims 32g + 8kk .. +8 (zero for padding heads)
-        bf16x8 qop[4];
-        if (n < G) {
-            const u32x4* qp = reinterpret_cast<const u32x4*>(
-                q + (static_cast<int64_t>(b) * Hq + h * G + n) * kHeadDim + 32 * g);
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) qop[kk] = bitcast<bf16x8>(qp[kk]);
-        } else {
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) qop[kk] = bitcast<bf16x8>(u32x4{0u, 0u, 0u, 0u});
+    // ---- this worker's tile source ----
+    Sched sched;
+    DeviceWalker dwalk;
+    HostWalker hwalk;
+    int64_t w_begin = 0, w_end = 0;
+    if constexpr (DEV) {
+        build_prefix<kDecodeThreads>(seq_lens, a.batch, a.max_pages_per_seq, s_dyn, s_dyn + a.batch, s_tmp);
+        sched.len = s_dyn;
+        sched.pb = s_dyn + a.batch;
+        sched.B = a.batch;
+        sched.H = Hkv;
+        sched.W = gridDim.x;
+        sched.T = static_cast<int64_t>(Hkv) * s_dyn[2 * a.batch];
+        // empty sequences get out = 0, lse = -inf from worker u mod W
+        for (int u = w; u < a.batch * Hkv; u += gridDim.x) {
+            const int b = u / Hkv;
+            if (sched.len[b] != 0) continue;
+            const int row = b * Hq + (u - b * Hkv) * G;
+            const int t = threadIdx.x;
+            if (t < G * 16)
+                *reinterpret_cast<u32x4*>(out + static_cast<int64_t>(row + (t >> 4)) * kHeadDim + 8 * (t & 15)) =
+                    u32x4{0u, 0u, 0u, 0u};
+            if (t < G) lse[row + t] = -INFINITY;
         }
-
-        auto issue = [&](TileSlot<KV>& s, int t) {
-            int valid = 0;
-            const char* kp = kbase;
-            const char* vp = vbase;
-            if (t < t1) {
-                const int page = bt[t];
-                if (static_cast<unsigned>(page) < static_cast<unsigned>(a.num_pages)) {
-                    const int rem = L - t * kPage;
-                    valid = rem < 0 ? 0 : (rem > kPage ? kPage : rem);
-                    const uint64_t off = (static_cast<uint64_t>(page) * Hkv + h) * kBlock;
-                    kp += off;
-                    vp += off;
-                }
-            }
-            // the clamp above may be selected as a VALU op; the value is wave-uniform,
-            // and the buffer descriptor must live in SGPRs
-            valid = __builtin_amdgcn_readfirstlane(valid);
-            s.valid = valid;
-            s.data.load(make_rsrc(kp, valid * kRow), make_rsrc(vp, valid * kRow), wave, n, g);
-        };
-
-        float m = -INFINITY;   // running max (log2 domain), uniform over g
-        float l = 0.f;         // this lane's share of the running sum
-        f32x4 acc[8];
-#pragma unroll
-        for (int nb = 0; nb < 8; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-        auto consume = [&](const TileSlot<KV>& s) {
-            f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s.data.k_op(kk), qop[kk], sc, 0, 0, 0);
-            const int r0 = 16 * wave + 4 * g;
-            float mt = -INFINITY;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                sc[i] = (r0 + i < s.valid) ? sc[i] * a.qk_scale_log2 : -INFINITY;
-                mt = fmaxf(mt, sc[i]);
-            }
-            mt = fmaxf(mt, __shfl_xor(mt, 16));
-            mt = fmaxf(mt, __shfl_xor(mt, 32));
-            const float m_new = fmaxf(m, mt);
-            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m - m_use);
-            float p[4];
-            float psum = 0.f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                p[i] = __builtin_amdgcn_exp2f(sc[i] - m_use);
-                psum += p[i];
-            }
-            l = l * alpha + psum;
-            m = m_new;
-            const bf16x4 pop = bf16x4{static_cast<__bf16>(p[0]), static_cast<__bf16>(p[1]),
-                                      static_cast<__bf16>(p[2]), static_cast<__bf16>(p[3])};
-            u32x4 rows[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) rows[i] = s.data.v_row(i);
-#pragma unroll
-            for (int nb = 0; nb < 8; ++nb) {
-                const int d = nb >> 1;
-                const uint32_t sel = (nb & 1) ? kSelHi : kSelLo;
-                const u32x2 vt = u32x2{__builtin_amdgcn_perm(rows[1][d], rows[0][d], sel),
-                                       __builtin_amdgcn_perm(rows[3][d], rows[2][d], sel)};
-                acc[nb] = acc[nb] * alpha;
-                acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(bitcast<bf16x4>(vt), pop, acc[nb], 0, 0, 0);
-            }
-        };
-
-        TileSlot<KV> ring[PF];
-#pragma unroll
-        for (int j = 0; j < PF; ++j) issue(ring[j], t0 + j);
-        for (int t = t0; t < t1; t += PF) {
-#pragma unroll
-            for (int j = 0; j < PF; ++j) {
-                if (t + j < t1) {
-                    consume(ring[j]);
-                    issue(ring[j], t + j + PF);
-                }
-            }
+        w_begin = sched.range_begin(w);
+        w_end = sched.range_begin(w + 1);
+        if (w_begin == w_end) {                    // uniform: an empty worker
+            if (threadIdx.x == 0) merge_records[3 * w] = -1;
+            return;
         }
+        dwalk.init(sched, w_begin, w_end);
+    } else {
+        hwalk.init(worker_ptr, entries, seq_lens, Hkv, w);
+        if (!hwalk.have) return;
+    }
 
-        // ---- merge the four waves' states for this entry ----
+    auto issue = [&](TileSlot<KV>& s) {
+        TileRef r;
+        bool ok;
+        if constexpr (DEV) ok = dwalk.next(r);
+        else ok = hwalk.next(r);
+        int valid = 0, page = 0, h = 0, row = 0, part = -1, first = 0, last = 0;
+        if (ok) {
+            const int b = uniform(r.b);
+            const int t = uniform(r.t);
+            h = uniform(r.h);
+            page = block_table[static_cast<int64_t>(b) * a.max_pages_per_seq + t];
+            const int rem = uniform(r.L) - t * kPage;
+            valid = rem < 0 ? 0 : (rem > kPage ? kPage : rem);
+            if (static_cast<unsigned>(page) >= static_cast<unsigned>(a.num_pages)) {
+                valid = 0;
+                page = 0;
+            }
+            row = b * Hq + h * G;
+            first = r.first;
+            last = r.last;
+            part = r.part;
+        }
+        s.real = uniform(ok ? 1 : 0);
+        s.valid = uniform(valid);
+        s.first = uniform(first);
+        s.last = uniform(last);
+        s.row = uniform(row);
+        s.part = uniform(part);
+        const uint64_t off = (static_cast<uint64_t>(uniform(page)) * Hkv + uniform(h)) * kBlock;
+        const uint32_t kv_bytes = static_cast<uint32_t>(s.valid) * kRow;
+        s.kv.load(make_rsrc(kcache + off, kv_bytes), make_rsrc(vcache + off, kv_bytes), wave, n, g);
+        // Q^T operand of a new entry: head n, dims 32kk + 8g .. +8; heads >= G read as zero
+        const __amdgpu_buffer_rsrc_t rq =
+            make_rsrc(q + static_cast<int64_t>(s.row) * kHeadDim, s.first ? G * kHeadDim * 2 : 0);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            s.q[kk] = __builtin_amdgcn_raw_buffer_load_b128(rq, n * kHeadDim * 2 + 64 * kk + 16 * g, 0, 0);
+    };
+
+    TileSlot<KV> ring[PF];
+#pragma unroll
+    for (int j = 0; j < PF; ++j) issue(ring[j]);
+
+    // device schedule: partial slots of this worker's (at most two) split
+    // entries, and the merge record of the split unit this worker starts
+    // (its first worker writes it; no worker starts two), read by the merge
+    // kernel after this kernel completes
+    int slot_first = -1, slot_last = -1;
+    if constexpr (DEV) {
+        int b0, h0, t0, bl, hl, tl;
+        sched.locate(w_begin, b0, h0, t0);
+        sched.locate(w_end - 1, bl, hl, tl);
+        int base_f, base_l;
+        split_bases_wave(sched, b0 * Hkv + h0, bl * Hkv + hl, base_f, base_l);
+        const int rank_f = sched.rank_in_unit(w, b0, h0, t0);
+        slot_first = uniform(base_f + rank_f);
+        slot_last = uniform(base_l);
+        const bool single = (b0 == bl && h0 == hl);
+        const int S_f = sched.parts(b0, h0);
+        const int S_l = sched.parts(bl, hl);
+        int ru = -1, rS = 0, rbase = 0;
+        if (S_f >= 2 && rank_f == 0) {
+            ru = b0 * Hkv + h0;
+            rS = S_f;
+            rbase = base_f;
+        } else if (!single && S_l >= 2) {
+            ru = bl * Hkv + hl;
+            rS = S_l;
+            rbase = base_l;
+        }
+        if (threadIdx.x == 0) {
+            merge_records[3 * w + 0] = ru;
+            merge_records[3 * w + 1] = rS;
+            merge_records[3 * w + 2] = rbase;
+        }
+    }
+
+    float m = -INFINITY;   // running max (log2 domain), uniform over g
+    float l = 0.f;         // this lane's share of the running sum
+    f32x4 acc[8];
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 qop[4];
+
+    auto flush = [&](int row, int part) {
         l += __shfl_xor(l, 16);
         l += __shfl_xor(l, 32);
         s_m[wave][lane] = m;
@@ -276,15 +352,14 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
 #pragma unroll
             for (int nb = 0; nb < 8; ++nb) s_acc[wave][i][nb][lane] = acc[nb][i];
         __syncthreads();
-
-        float ms[kWaves], wsum = 0.f, M = -INFINITY;
+        float ms[kWaves], M = -INFINITY;
 #pragma unroll
         for (int s = 0; s < kWaves; ++s) {
             ms[s] = s_m[s][lane];
             M = fmaxf(M, ms[s]);
         }
         const float M_use = (M == -INFINITY) ? 0.f : M;
-        float wt[kWaves];
+        float wt[kWaves], wsum = 0.f;
 #pragma unroll
         for (int s = 0; s < kWaves; ++s) {
             wt[s] = __builtin_amdgcn_exp2f(ms[s] - M_use);
@@ -298,19 +373,19 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
             for (int s = 0; s < kWaves; ++s) x += wt[s] * s_acc[s][wave][nb][lane];
             o[nb] = x;
         }
+        int slot = part;
+        if constexpr (DEV) slot = (part == kPartFirst) ? slot_first : (part == kPartLast ? slot_last : part);
         if (n < G) {
             const float inv = (wsum > 0.f) ? a.v_scale / wsum : 0.f;
             const float lse_val = (wsum > 0.f) ? (M + __log2f(wsum)) * kLn2 : -INFINITY;
-            const int hq = h * G + n;
             const int dim0 = 32 * g + 8 * wave;   // this wave merges register i = wave
             if (slot < 0) {
                 bf16x8 ov;
 #pragma unroll
                 for (int nb = 0; nb < 8; ++nb) ov[nb] = static_cast<__bf16>(o[nb] * inv);
-                *reinterpret_cast<bf16x8*>(out +
-                                           (static_cast<int64_t>(b) * Hq + hq) * kHeadDim + dim0) = ov;
-                if (wave == 0 && g == 0) lse[static_cast<int64_t>(b) * Hq + hq] = lse_val;
-            } else {
+                *reinterpret_cast<bf16x8*>(out + static_cast<int64_t>(row + n) * kHeadDim + dim0) = ov;
+                if (wave == 0 && g == 0) lse[row + n] = lse_val;
+            } else if (slot < a.max_partials) {   // a slot is always in range; the test keeps stray writes out
                 float* dst = o_part + (static_cast<int64_t>(slot) * G + n) * kHeadDim + dim0;
                 *reinterpret_cast<f32x4*>(dst) = f32x4{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
                 *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv};
@@ -318,14 +393,82 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
             }
         }
         __syncthreads();
+        m = -INFINITY;
+        l = 0.f;
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    };
+
+    auto consume = [&](const TileSlot<KV>& s) {
+        if (s.first) {
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) qop[kk] = bitcast<bf16x8>(s.q[kk]);
+        }
+        f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s.kv.k_op(kk), qop[kk], sc, 0, 0, 0);
+        const int r0 = 16 * wave + 4 * g;
+        float mt = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            sc[i] = (r0 + i < s.valid) ? sc[i] * a.qk_scale_log2 : -INFINITY;
+            mt = fmaxf(mt, sc[i]);
+        }
+        mt = fmaxf(mt, __shfl_xor(mt, 16));
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        const float m_new = fmaxf(m, mt);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m - m_use);
+        float p[4];
+        float psum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            p[i] = __builtin_amdgcn_exp2f(sc[i] - m_use);
+            psum += p[i];
+        }
+        l = l * alpha + psum;
+        m = m_new;
+        const bf16x4 pop = bf16x4{static_cast<__bf16>(p[0]), static_cast<__bf16>(p[1]),
+                                  static_cast<__bf16>(p[2]), static_cast<__bf16>(p[3])};
+        u32x4 rows[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rows[i] = s.kv.v_row(i);
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) {
+            const int d = nb >> 1;
+            const uint32_t sel = (nb & 1) ? kSelHi : kSelLo;
+            const u32x2 vt = u32x2{__builtin_amdgcn_perm(rows[1][d], rows[0][d], sel),
+                                   __builtin_amdgcn_perm(rows[3][d], rows[2][d], sel)};
+            acc[nb] = acc[nb] * alpha;
+            acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(bitcast<bf16x4>(vt), pop, acc[nb], 0, 0, 0);
+        }
+        if (s.last) flush(s.row, s.part);
+    };
+
+    // Leaving the loop the moment a slot is empty keeps every path that
+    // reaches the back edge with all PF slots re-issued, so the compiler's
+    // load-counter waits let the other PF - 1 tiles stay in flight.
+    for (;;) {
+#pragma unroll
+        for (int j = 0; j < PF; ++j) {
+            if (!ring[j].real) goto done;
+            consume(ring[j]);
+            issue(ring[j]);
+        }
     }
+done:
+    return;
 }
 
-// Merge of split units: one workgroup per (merge record, query head of the
-// group), 1024 threads = 32 partial lanes x 32 dim quads.  Lane pl folds the
-// partials i = pl, pl + 32, ... into a running (max, weighted sum, weight)
-// triple, issuing up to eight partials' loads before using any of them; the
-// 32 triples then meet in LDS and are merged once more by log-sum-exp.
+// Merge of split units: one workgroup per (merge
+// record, query head of the group), 1024 threads = 32 partial lanes x 32
+// dim quads.  Lane pl folds partials i = pl, pl + 32, ... into a running
+// (max, weighted sum, weight) triple, issuing up to eight partials' loads
+// before using any of them; the 32 triples then meet in LDS and are merged
+// once more by log-sum-exp.  The records are the host plan's merge list, or,
+// for the device-scheduled step, one record per worker written by the decode
+// kernel (u = -1: nothing to merge; empty sequences were written there too).
 constexpr int kMergeLanes = kCombineThreads / 32;
 constexpr int kMergeUnroll = 8;
 
@@ -335,12 +478,13 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
     __shared__ float s_w[kMergeLanes];
 
     const int G = a.group;
+    const int Hkv = a.num_kv_heads;
     const int c = blockIdx.x / G;
     const int n = blockIdx.x - c * G;
     const int u = a.combine[3 * c + 0];
     const int S = a.combine[3 * c + 1];
     const int base = a.combine[3 * c + 2];
-    const int Hkv = a.num_kv_heads;
+    if (u < 0) return;   // per-worker records: this worker starts no split unit
     const int b = u / Hkv;
     const int h = u - b * Hkv;
     const int64_t row = static_cast<int64_t>(b) * (G * Hkv) + h * G + n;
@@ -354,30 +498,35 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
         if (t == 0) a.lse[row] = -INFINITY;
         return;
     }
+    if (static_cast<int64_t>(base) + S > a.max_partials) {   // never for a consistent schedule: report NaN
+        if (pl == 0) *reinterpret_cast<u32x2*>(out + 4 * dq) = u32x2{0x7fc07fc0u, 0x7fc07fc0u};
+        if (t == 0) a.lse[row] = __builtin_nanf("");
+        return;
+    }
 
     float m = -INFINITY;          // running max of the folded lse values (log2 units)
     float w = 0.f;                // running sum of 2^(lse - m)
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int i0 = pl; i0 < S; i0 += kMergeLanes * kMergeUnroll) {
-        float l[kMergeUnroll];
+        float lv[kMergeUnroll];
         f32x4 o[kMergeUnroll];
 #pragma unroll
         for (int k = 0; k < kMergeUnroll; ++k) {
             const int i = i0 + k * kMergeLanes;
             const int64_t p = static_cast<int64_t>(base + (i < S ? i : 0)) * G + n;
-            l[k] = (i < S) ? a.lse_part[p] * kLog2e : -INFINITY;
+            lv[k] = (i < S) ? a.lse_part[p] * kLog2e : -INFINITY;
             o[k] = *reinterpret_cast<const f32x4*>(a.o_part + p * kHeadDim + 4 * dq);
         }
         float mk = m;
 #pragma unroll
-        for (int k = 0; k < kMergeUnroll; ++k) mk = fmaxf(mk, l[k]);
+        for (int k = 0; k < kMergeUnroll; ++k) mk = fmaxf(mk, lv[k]);
         const float m_use = (mk == -INFINITY) ? 0.f : mk;
         const float f = __builtin_amdgcn_exp2f(m - m_use);
         acc *= f;
         w *= f;
 #pragma unroll
         for (int k = 0; k < kMergeUnroll; ++k) {
-            const float e = __builtin_amdgcn_exp2f(l[k] - m_use);
+            const float e = __builtin_amdgcn_exp2f(lv[k] - m_use);
             acc += e * o[k];
             w += e;
         }
@@ -410,9 +559,123 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
     }
 }
 
+// Block-wide exclusive scan of arr[0..count) in LDS (kPlanThreads threads);
+// returns the total.  s_tmp needs kPlanThreads / 64 ints.
+__device__ int block_scan_inplace(int32_t* arr, int count, int32_t* s_tmp) {
+    const int t = threadIdx.x;
+    const int per = (count + kPlanThreads - 1) / kPlanThreads;
+    const int lo = t * per;
+    const int hi = min(count, lo + per);
+    int sum = 0;
+    for (int i = lo; i < hi; ++i) sum += arr[i];
+    const int incl = wave_inclusive_sum(sum);
+    __syncthreads();
+    if ((t & 63) == 63) s_tmp[t >> 6] = incl;
+    __syncthreads();
+    int run = incl - sum;
+    for (int w = 0; w < (t >> 6); ++w) run += s_tmp[w];
+    for (int i = lo; i < hi; ++i) {
+        const int x = arr[i];
+        arr[i] = run;
+        run += x;
+    }
+    int total = 0;
+    for (int w = 0; w < kPlanThreads / 64; ++w) total += s_tmp[w];
+    __syncthreads();
+    return total;
+}
+
+// The device schedule written out in the host plan's word layout, by one
+// workgroup, so it can be compared word for word with the host planner.
+__global__ __launch_bounds__(kPlanThreads) void plan_device_kernel(const int32_t* __restrict__ seq_lens, int B,
+                                                                   int H, int W, int max_pages,
+                                                                   int32_t* __restrict__ plan) {
+    extern __shared__ int32_t s_dyn[];
+    __shared__ int32_t s_tmp[kPlanThreads / 64];
+    const int U = B * H;
+    int32_t* s_len = s_dyn;               // [B]
+    int32_t* s_pb = s_len + B;            // [B + 1]
+    int32_t* s_cnt = s_pb + B + 1;        // [W]   entries per worker -> worker_ptr
+    int32_t* s_base = s_cnt + W;          // [U]   split slots per unit -> base
+    int32_t* s_cidx = s_base + U;         // [U]   merge record flag -> record index
+    build_prefix<kPlanThreads>(seq_lens, B, max_pages, s_len, s_pb, s_tmp);
+    Sched sched;
+    sched.len = s_len;
+    sched.pb = s_pb;
+    sched.B = B;
+    sched.H = H;
+    sched.W = W;
+    sched.T = static_cast<int64_t>(H) * s_pb[B];
+    const int t = threadIdx.x;
+
+    for (int w = t; w < W; w += kPlanThreads) {
+        DeviceWalker dw;
+        dw.init(sched, sched.range_begin(w), sched.range_begin(w + 1));
+        TileRef r;
+        int cnt = 0;
+        while (dw.next(r)) cnt += r.first ? 1 : 0;
+        s_cnt[w] = cnt;
+    }
+    for (int u = t; u < U; u += kPlanThreads) {
+        const int b = u / H;
+        const int S = sched.parts(b, u - b * H);
+        s_base[u] = S >= 2 ? S : 0;
+        s_cidx[u] = S != 1 ? 1 : 0;
+    }
+    __syncthreads();
+    const int E = block_scan_inplace(s_cnt, W, s_tmp);
+    const int P = block_scan_inplace(s_base, U, s_tmp);
+    const int C = block_scan_inplace(s_cidx, U, s_tmp);
+
+    int32_t* wp = plan + HPC_PLAN_HEADER_WORDS;
+    int32_t* ent = wp + W + 1;
+    int32_t* comb = ent + 4 * E;
+    if (t < HPC_PLAN_HEADER_WORDS) {
+        const int32_t hdr[9] = {HPC_PLAN_VERSION, B, H, W, static_cast<int32_t>(sched.T), E, P, C, HPC_DECODE_PAGE};
+        plan[t] = t < 9 ? hdr[t] : 0;
+    }
+    if (t == 0) wp[W] = E;
+    for (int w = t; w < W; w += kPlanThreads) {
+        wp[w] = s_cnt[w];
+        const int64_t beg = sched.range_begin(w), end = sched.range_begin(w + 1);
+        if (beg == end) continue;
+        int b0, h0, t0;
+        sched.locate(beg, b0, h0, t0);
+        const int k0 = sched.rank_in_unit(w, b0, h0, t0);
+        DeviceWalker dw;
+        dw.init(sched, beg, end);
+        TileRef r;
+        int e = s_cnt[w] - 1;
+        int ta = 0;
+        while (dw.next(r)) {
+            if (r.first) {
+                ++e;
+                ta = r.t;
+            }
+            if (r.last) {
+                const int u = r.b * H + r.h;
+                const int slot = r.part == kPartFirst ? s_base[u] + k0 : (r.part == kPartLast ? s_base[u] : -1);
+                ent[4 * e + 0] = u;
+                ent[4 * e + 1] = ta;
+                ent[4 * e + 2] = r.t + 1;
+                ent[4 * e + 3] = slot;
+            }
+        }
+    }
+    for (int u = t; u < U; u += kPlanThreads) {
+        const int b = u / H;
+        const int S = sched.parts(b, u - b * H);
+        if (S == 1) continue;
+        const int i = s_cidx[u];
+        comb[3 * i + 0] = u;
+        comb[3 * i + 1] = S;
+        comb[3 * i + 2] = S >= 2 ? s_base[u] : 0;
+    }
+}
+
 // tiles in flight per wave (register ring depth)
 #ifndef HPC_DECODE_PREFETCH_BF16
-#define HPC_DECODE_PREFETCH_BF16 4
+#define HPC_DECODE_PREFETCH_BF16 2
 #endif
 #ifndef HPC_DECODE_PREFETCH_FP8
 #define HPC_DECODE_PREFETCH_FP8 4
@@ -420,29 +683,43 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
 constexpr int kPrefetchBf16 = HPC_DECODE_PREFETCH_BF16;
 constexpr int kPrefetchFp8 = HPC_DECODE_PREFETCH_FP8;
 
+template <int KV, int PF, bool DEV>
+void launch_decode_t(const DecodeArgs& a, int n_workers, size_t lds, hipStream_t s) {
+    const DecodeScalars sc{a.batch,        a.num_kv_heads,  a.group,  a.max_pages_per_seq, a.num_pages,
+                           a.max_partials, a.qk_scale_log2, a.v_scale};
+    hipLaunchKernelGGL((decode_kernel<KV, PF, DEV>), dim3(n_workers), dim3(kDecodeThreads), lds, s,
+                       static_cast<const __bf16*>(a.q), static_cast<const char*>(a.k),
+                       static_cast<const char*>(a.v), a.block_table, a.seq_lens, a.worker_ptr, a.entries,
+                       static_cast<__bf16*>(a.out), a.lse, a.o_part, a.lse_part, a.merge_records, sc);
+}
+
 }  // namespace
 
-int launch_decode(const DecodeArgs& a, int kv_dtype, int n_workers, void* stream) {
+int launch_decode(const DecodeArgs& a, int kv_dtype, int n_workers, bool device_sched, void* stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const DecodeScalars sc{a.num_kv_heads, a.group, a.max_pages_per_seq, a.num_pages, a.qk_scale_log2, a.v_scale};
-    const __bf16* q = static_cast<const __bf16*>(a.q);
-    const char* k = static_cast<const char*>(a.k);
-    const char* v = static_cast<const char*>(a.v);
-    __bf16* out = static_cast<__bf16*>(a.out);
-    if (kv_dtype == HPC_KV_BF16)
-        hipLaunchKernelGGL((decode_kernel<HPC_KV_BF16, kPrefetchBf16>), dim3(n_workers), dim3(kDecodeThreads), 0, s,
-                           q, k, v, a.block_table, a.seq_lens, a.worker_ptr, a.entries, out, a.lse, a.o_part,
-                           a.lse_part, sc);
-    else
-        hipLaunchKernelGGL((decode_kernel<HPC_KV_FP8_E4M3, kPrefetchFp8>), dim3(n_workers), dim3(kDecodeThreads), 0, s,
-                           q, k, v, a.block_table, a.seq_lens, a.worker_ptr, a.entries, out, a.lse, a.o_part,
-                           a.lse_part, sc);
+    const size_t lds = device_sched ? (2 * static_cast<size_t>(a.batch) + 1) * sizeof(int32_t) : 0;
+    if (kv_dtype == HPC_KV_BF16) {
+        if (device_sched) launch_decode_t<HPC_KV_BF16, kPrefetchBf16, true>(a, n_workers, lds, s);
+        else launch_decode_t<HPC_KV_BF16, kPrefetchBf16, false>(a, n_workers, lds, s);
+    } else {
+        if (device_sched) launch_decode_t<HPC_KV_FP8_E4M3, kPrefetchFp8, true>(a, n_workers, lds, s);
+        else launch_decode_t<HPC_KV_FP8_E4M3, kPrefetchFp8, false>(a, n_workers, lds, s);
+    }
     return static_cast<int>(hipGetLastError());
 }
 
-int launch_combine(const CombineArgs& a, int n_combine, void* stream) {
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    hipLaunchKernelGGL(combine_kernel, dim3(n_combine * a.group), dim3(kCombineThreads), 0, s, a);
+int launch_combine(const CombineArgs& a, int n_records, void* stream) {
+    hipLaunchKernelGGL(combine_kernel, dim3(n_records * a.group), dim3(kCombineThreads), 0,
+                       static_cast<hipStream_t>(stream), a);
+    return static_cast<int>(hipGetLastError());
+}
+
+int launch_plan_device(const int32_t* seq_lens, int batch, int num_kv_heads, int n_workers, int max_pages_per_seq,
+                       int32_t* plan, void* stream) {
+    const int U = batch * num_kv_heads;
+    const size_t lds = (static_cast<size_t>(2 * batch + 1) + n_workers + 2 * static_cast<size_t>(U)) * sizeof(int32_t);
+    hipLaunchKernelGGL(plan_device_kernel, dim3(1), dim3(kPlanThreads), lds, static_cast<hipStream_t>(stream),
+                       seq_lens, batch, num_kv_heads, n_workers, max_pages_per_seq, plan);
     return static_cast<int>(hipGetLastError());
 }
 

@@ -11,6 +11,15 @@ constexpr int kPage = 64;
 constexpr int kWaves = 4;                 // waves per decode workgroup
 constexpr int kDecodeThreads = 64 * kWaves;
 constexpr int kCombineThreads = 1024;
+constexpr int kPlanThreads = 1024;
+
+// Limits of the device-scheduled path: the lengths (and their tile prefix)
+// live in LDS of every workgroup.
+constexpr int kDeviceSchedMaxBatch = 4096;
+// Limits of the plan-materialising kernel (one workgroup, everything in LDS).
+constexpr int kPlanDeviceMaxBatch = 2048;
+constexpr int kPlanDeviceMaxWorkers = 2048;
+constexpr int kPlanDeviceMaxUnits = 4096;
 
 struct DecodeArgs {
     const void* q;               // bf16 [B][Hq][128]
@@ -18,32 +27,40 @@ struct DecodeArgs {
     const void* v;
     const int32_t* block_table;  // [B][max_pages_per_seq]
     const int32_t* seq_lens;     // [B]
-    const int32_t* worker_ptr;   // plan words (device)
-    const int32_t* entries;      // plan words (device), 4 per entry
+    const int32_t* worker_ptr;   // host plan words (device copy); unused when scheduled on device
+    const int32_t* entries;      // host plan words (device copy), 4 per entry
     void* out;                   // bf16 [B][Hq][128]
     float* lse;                  // [B][Hq]
     float* o_part;               // [n_partials][G][128]
     float* lse_part;             // [n_partials][G]
+    int32_t* merge_records;      // device schedule: [W][3] (unit or -1, partials, first slot)
+    int32_t batch;
     int32_t num_kv_heads;
     int32_t group;               // G = Hq / H_kv, 1..16
     int32_t max_pages_per_seq;
     int32_t num_pages;
+    int32_t max_partials;        // partial slots in the workspace
     float qk_scale_log2;         // sm_scale * k_scale * log2(e)
     float v_scale;
 };
 
 struct CombineArgs {
-    const int32_t* combine;      // plan words (device), 3 per record
+    const int32_t* combine;      // merge records, 3 per record (host plan list, or one per worker)
     const float* o_part;
     const float* lse_part;
     void* out;
     float* lse;
     int32_t num_kv_heads;
     int32_t group;
+    int32_t max_partials;        // partial slots in the workspace
 };
 
-// Both return the hipError_t of the launch as int (0 = success).
-int launch_decode(const DecodeArgs& a, int kv_dtype, int n_workers, void* stream);
-int launch_combine(const CombineArgs& a, int n_combine, void* stream);
+// All return the hipError_t of the launch as int (0 = success).
+// device_sched: the decode kernel derives the schedule from seq_lens itself
+// and writes one merge record per worker for the merge kernel.
+int launch_decode(const DecodeArgs& a, int kv_dtype, int n_workers, bool device_sched, void* stream);
+int launch_combine(const CombineArgs& a, int n_records, void* stream);
+int launch_plan_device(const int32_t* seq_lens, int batch, int num_kv_heads, int n_workers,
+                       int max_pages_per_seq, int32_t* plan, void* stream);
 
 }  // namespace hpcd

@@ -186,3 +186,39 @@ def test_check_plan_mismatches():
     m = _Fake()
     m.plan[e0 + 3] = int(m.plan[6])            # slot beyond n_partials
     assert m.check() == hd.HPC_ERR_PLAN_MISMATCH
+
+
+def test_step_check_errors():
+    lib = _lib.lib()
+    ptr = ctypes.c_void_p(0x1000)
+    params = hd.make_params(8, 1, 4, 8, hd.HPC_KV_BF16, 1 / np.sqrt(128))
+    need = hd.hpc_decode_step_workspace_size(2, 8, 1, 16)
+    P = 16 + 2
+    al = lambda x: (x + 255) // 256 * 256
+    assert need == al(al(P * 8 * 128 * 4) + P * 8 * 4) + 3 * 16 * 4
+
+    def chk(batch=2, W=16, ws=ptr, wsb=need, **over):
+        a = dict(q=ptr, k=ptr, v=ptr, bt=ptr, sl=ptr, out=ptr, lse=ptr)
+        a.update(over)
+        return lib.hpc_decode_step_check(ctypes.byref(params), batch, W, a["q"], a["k"], a["v"], a["bt"],
+                                         a["sl"], ws, wsb, a["out"], a["lse"])
+    assert chk() == hd.HPC_OK
+    assert chk(sl=None) == hd.HPC_ERR_NULL and chk(ws=None) == hd.HPC_ERR_NULL
+    assert chk(wsb=need - 1) == hd.HPC_ERR_TOO_SMALL
+    assert chk(batch=0) == hd.HPC_ERR_INVALID and chk(W=0) == hd.HPC_ERR_INVALID
+    assert chk(batch=5000, wsb=1 << 40) == hd.HPC_ERR_UNSUPPORTED
+    params.max_pages_per_seq = 1 << 20
+    assert chk(batch=4096, wsb=1 << 40) == hd.HPC_ERR_INVALID       # tile indices beyond int32
+    params.max_pages_per_seq = 4
+    params.head_dim = 64
+    assert chk() == hd.HPC_ERR_UNSUPPORTED
+
+
+def test_plan_device_argument_errors():
+    lib = _lib.lib()
+    ptr = ctypes.c_void_p(0x1000)
+    cap = hd.hpc_decode_plan_size(4, 1, 8)
+    assert lib.hpc_decode_plan_device(None, 4, 1, 8, 4, ptr, cap, None) == hd.HPC_ERR_NULL
+    assert lib.hpc_decode_plan_device(ptr, 4, 1, 8, 4, ptr, cap - 1, None) == hd.HPC_ERR_TOO_SMALL
+    assert lib.hpc_decode_plan_device(ptr, 4, 1, 0, 4, ptr, cap, None) == hd.HPC_ERR_INVALID
+    assert lib.hpc_decode_plan_device(ptr, 4096, 1, 8, 4, ptr, 1 << 30, None) == hd.HPC_ERR_UNSUPPORTED

@@ -1,0 +1,156 @@
+"""The schedule derived on the GPU (hpc_decode_plan_device / hpc_decode_step)
+against the host planner and the oracle.
+
+* plan words materialised on the device equal the oracle's schedule word for
+  word (every tile covered once, same entries, slots and merge records);
+* a device-scheduled step matches the host-planned step: bitwise for every
+  sequence that one worker finishes alone (same schedule, same arithmetic),
+  and to fp32 rounding for split sequences, whose merge runs in the decode
+  kernel (groups of 16 partials folded in order) instead of the separate
+  merge kernel (32 lanes reduced in LDS); both match the float64 oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import load_balanced_paged_step_amd as hd
+from oracle import build_plan
+from workloads import make_inputs, workload_inputs
+
+from decode_harness import announce, compare, run_hip, run_oracle, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    hd.lib()
+
+
+def _device_plan(lens, H, W, max_pages=None):
+    lens = np.asarray(lens, dtype=np.int32)
+    mp = max_pages or max(1, int((lens.max() + 63) // 64) if lens.size else 1)
+    sl = torch.from_numpy(lens).cuda()
+    plan = hd.hpc_decode_plan_device(sl, H, W, mp)
+    torch.cuda.synchronize()
+    words = plan.cpu().numpy()
+    return words[:hd.hpc_decode_plan_words(words)]
+
+
+@pytest.mark.parametrize("lens,H,W", [
+    ([37, 64, 130, 200], 1, 4), ([0, 100, 10], 2, 4), ([65], 1, 5), ([1, 0, 128], 1, 1),
+    ([131072] + [4096] * 31, 1, 256), ([131072] + [4096] * 31, 1, 1024), ([512] * 64, 1, 256),
+    ([1024] * 8, 1, 256), ([0, 0, 0], 8, 7), ([5000] * 3, 8, 700), ([1] * 300, 2, 37),
+])
+def test_device_plan_equals_oracle(lens, H, W):
+    announce(f"device plan lens[:4]={lens[:4]} B={len(lens)} H={H} W={W}")
+    assert np.array_equal(_device_plan(lens, H, W), build_plan(lens, H, W))
+
+
+def test_device_plan_random_batches():
+    rng = np.random.default_rng(123)
+    for i in range(60):
+        B = int(rng.integers(1, 64))
+        H = int(rng.integers(1, 9))
+        W = int(rng.integers(1, 1500))
+        lens = rng.integers(0, 20000, size=B)
+        lens[rng.random(B) < 0.2] = 0
+        announce(f"device plan random #{i} B={B} H={H} W={W}")
+        assert np.array_equal(_device_plan(lens, H, W), build_plan(lens, H, W)), (lens.tolist(), H, W)
+
+
+def test_device_plan_of_fp8_workload():
+    inp = workload_inputs(5)
+    lens = inp.seq_lens.numpy()
+    for W in (256, 1024):
+        announce(f"device plan workload 5 W={W}")
+        assert np.array_equal(_device_plan(lens, 8, W), build_plan(lens, 8, W))
+
+
+def assert_same_as_host_planned(inp, W, a, b):
+    plan = build_plan(inp.seq_lens.numpy(), inp.num_kv_heads, W)
+    hdr_W, E = int(plan[3]), int(plan[5])
+    ents = plan[16 + hdr_W + 1:16 + hdr_W + 1 + 4 * E].reshape(E, 4)
+    G = inp.num_q_heads // inp.num_kv_heads
+    single = np.zeros(inp.batch * inp.num_kv_heads, dtype=bool)
+    single[ents[ents[:, 3] < 0, 0]] = True
+    rows = np.repeat(single, G).reshape(inp.batch, inp.num_q_heads)
+    assert np.array_equal(a[0][rows], b[0][rows]) and np.array_equal(a[1][rows], b[1][rows])
+    np.testing.assert_allclose(a[0], b[0], rtol=2.0 ** -7, atol=1e-6)
+    fin = np.isfinite(b[1])
+    assert np.array_equal(fin, np.isfinite(a[1]))
+    np.testing.assert_allclose(a[1][fin], b[1][fin], rtol=0, atol=4e-6)
+
+
+def run_step(inp, W, dev=None):
+    if dev is None:
+        dev = to_device(inp)
+    out = torch.empty_like(dev["q"])
+    lse = torch.empty(dev["q"].shape[:2], dtype=torch.float32, device="cuda")
+    launch = hd.StepLauncher(dev["q"], dev["k"], dev["v"], dev["bt"], dev["sl"], out, lse,
+                             num_kv_heads=inp.num_kv_heads, n_workers=W, sm_scale=inp.sm_scale,
+                             k_scale=inp.k_scale, v_scale=inp.v_scale)
+    launch()
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("cfg,W", [(1, 3), (1, 256), (2, 256), (3, 256), (4, 256), (4, 1024), (5, 256)])
+def test_step_equals_host_planned(cfg, W):
+    inp = workload_inputs(cfg, poison=True)
+    dev = to_device(inp)
+    announce(f"device step vs host plan, workload {cfg}, W={W}")
+    a = run_step(inp, W, dev)
+    b = run_hip(inp, W, dev)
+    assert_same_as_host_planned(inp, W, a, b)
+    compare(inp, a, run_oracle(inp), f"device step workload {cfg} W={W}")
+
+
+@pytest.mark.parametrize("lens,hq,hkv,W", [
+    ([0, 0, 0], 8, 1, 4), ([0, 37, 0, 1], 8, 1, 3), ([1] * 9, 8, 1, 4),
+    ([63, 64, 65, 127, 128, 129], 8, 1, 5), ([500, 30], 16, 1, 6), ([300, 1000, 7], 12, 3, 11),
+    ([4000, 17], 64, 8, 64), ([2] * 700, 8, 1, 256),
+])
+def test_step_edge_shapes(lens, hq, hkv, W):
+    inp = make_inputs(lens, hq, hkv, "bf16", seed=len(lens) + hq, poison=True)
+    announce(f"device step edge lens[:4]={lens[:4]} B={len(lens)} hq={hq} hkv={hkv} W={W}")
+    dev = to_device(inp)
+    a = run_step(inp, W, dev)
+    b = run_hip(inp, W, dev)
+    assert_same_as_host_planned(inp, W, a, b)
+    compare(inp, a, run_oracle(inp), "device step edge")
+
+
+def test_step_clamps_lengths_to_the_block_table():
+    """Device lengths beyond max_pages * 64 are clamped, never read past the table."""
+    inp = make_inputs([100, 200], 8, 1, "bf16", seed=11, max_pages_per_seq=4)
+    dev = to_device(inp)
+    dev["sl"] = torch.tensor([100, 10_000], dtype=torch.int32, device="cuda")
+    announce("device step with an over-long length")
+    a = run_step(inp, 8, dev)
+    inp.seq_lens = torch.tensor([100, 256], dtype=torch.int32)      # what the clamp leaves
+    compare(inp, a, run_oracle(inp), "clamped")
+
+
+def test_repeated_device_steps_with_changing_splits():
+    """One workspace reused across steps whose lengths change which sequences
+    are split (and which are empty): no merge record of an earlier step
+    leaks into a later one."""
+    base = make_inputs([7000, 300, 65, 4000], 16, 2, "bf16", seed=17, max_pages_per_seq=130)
+    dev = to_device(base)
+    out = torch.empty_like(dev["q"])
+    lse = torch.empty(dev["q"].shape[:2], dtype=torch.float32, device="cuda")
+    sl = dev["sl"]
+    launch = hd.StepLauncher(dev["q"], dev["k"], dev["v"], dev["bt"], sl, out, lse, num_kv_heads=2,
+                             n_workers=64, sm_scale=base.sm_scale)
+    for i, lens in enumerate(([7000, 300, 65, 4000], [7001, 0, 66, 4100], [8000, 1, 64, 8300],
+                              [100, 200, 300, 400], [0, 0, 0, 0], [7000, 300, 65, 4000])):
+        announce(f"repeated device step {i} lens={lens}")
+        sl.copy_(torch.tensor(lens, dtype=torch.int32))
+        launch()
+        torch.cuda.synchronize()
+        base.seq_lens = torch.tensor(lens, dtype=torch.int32)
+        got = (out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64))
+        compare(base, got, run_oracle(base), f"step {i}")
