@@ -165,14 +165,17 @@ int hpc_decode_check(const hpc_decode_params* params, const void* q, const void*
  * as hpc_decode_plan (§Attention Backend: Dynamic Load-Balanced Scheduling)
  * is derived inside the decode kernel from the device copy of the lengths:
  * every workgroup scans the tile counts of the batch in LDS and finds its
- * own tile range, entries and partial slots in closed form.  The first
- * worker of each split sequence also writes that sequence's merge record
- * into the workspace, and the merge kernel launched after it combines the
- * partials by log-sum-exp; empty sequences are written by the decode kernel.
+ * own tile range and entries.  A split entry writes its partial result to a
+ * worker-indexed slot; the worker holding a sequence's first tile writes that
+ * sequence's merge record (how many workers share it, which is the first),
+ * and the merge kernel launched after it combines the partials by
+ * log-sum-exp.  Empty sequences are written by the decode kernel.  Every
+ * record is rewritten at every call.
  * Nothing crosses from the host per step except the two launches, so the
  * call can be captured in a HIP graph.
  *
- * batch        sequences in q / block_table / seq_lens (1 .. 4096)
+ * batch        sequences in q / block_table / seq_lens (1 .. 2048, and
+ *              batch * H_kv <= 4096)
  * n_workers    persistent workgroups W (the plan's W)
  * seq_lens     device int32 [batch]; lengths are clamped to
  *              [0, max_pages_per_seq * 64] so no read leaves the block table
@@ -180,7 +183,7 @@ int hpc_decode_check(const hpc_decode_params* params, const void* q, const void*
  *              calls that may run concurrently (other streams) need
  *              separate workspaces
  * Other arguments as for hpc_decode_attn.  Errors as hpc_decode_attn, plus
- * HPC_ERR_UNSUPPORTED for batch > 4096 and HPC_ERR_INVALID when
+ * HPC_ERR_UNSUPPORTED beyond those limits and HPC_ERR_INVALID when
  * batch * max_pages_per_seq * H_kv does not fit in int32.
  */
 int hpc_decode_step(const hpc_decode_params* params, int32_t batch, int32_t n_workers, const void* q,
@@ -194,10 +197,11 @@ int hpc_decode_step_check(const hpc_decode_params* params, int32_t batch, int32_
                           const int32_t* block_table, const int32_t* seq_lens, const void* workspace,
                           int64_t workspace_bytes, const void* out, const float* lse);
 
-/* Workspace bytes hpc_decode_step needs for any lengths: room for
- * P = W + batch * H_kv partials (a bound on the split entries of any
- * schedule): fp32 outputs [P][G][128], then (256-byte aligned) fp32 lse
- * [P][G], then (aligned) int32 merge records [W][3]. */
+/* Workspace bytes hpc_decode_step needs for any lengths: P = 2 W partial
+ * slots (a worker's first and last entries are the only ones that can be
+ * split, and they use slots 2w and 2w + 1): fp32 outputs [P][G][128], then
+ * (256-byte aligned) fp32 lse [P][G], then (aligned) int32 merge records
+ * [batch * H_kv][6]. */
 int64_t hpc_decode_step_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                        int32_t n_workers);
 

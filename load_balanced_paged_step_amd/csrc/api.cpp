@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <mutex>
@@ -146,7 +147,7 @@ extern "C" int hpc_decode_attn(const hpc_decode_params* p, const void* q, const 
     if (prof_idx >= 0 && hipEventRecord(ev[0], s) != hipSuccess) return HPC_ERR_HIP;
     if (E > 0 && hpcd::launch_decode(da, p->kv_dtype, W, false, stream) != 0) return HPC_ERR_HIP;
     if (prof_idx >= 0 && hipEventRecord(ev[1], s) != hipSuccess) return HPC_ERR_HIP;
-    if (C > 0 && hpcd::launch_combine(ca, C, stream) != 0) return HPC_ERR_HIP;
+    if (C > 0 && hpcd::launch_combine(ca, C, false, stream) != 0) return HPC_ERR_HIP;
     if (prof_idx >= 0 && hipEventRecord(ev[2], s) != hipSuccess) return HPC_ERR_HIP;
     return HPC_OK;
 }
@@ -156,23 +157,25 @@ extern "C" int hpc_decode_attn(const hpc_decode_params* p, const void* q, const 
 
 namespace {
 
-int64_t step_partials_bound(int32_t batch, int32_t num_kv_heads, int32_t n_workers) {
-    return static_cast<int64_t>(n_workers) + static_cast<int64_t>(batch) * num_kv_heads;
+// partial slots of the device-scheduled step: two per worker (its first and
+// its last entry are the only ones that can be split)
+int64_t step_partials_bound(int32_t /*batch*/, int32_t /*num_kv_heads*/, int32_t n_workers) {
+    return 2 * static_cast<int64_t>(n_workers);
 }
 
 int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 
-// device-scheduled workspace: partial outputs, partial lse, per-worker merge records
+// device-scheduled workspace: partial outputs, partial lse, per-unit merge records
 struct StepLayout {
     int64_t o_off, lse_off, rec_off, total;
 };
 
-StepLayout step_layout(int64_t partials, int64_t G, int64_t n_workers) {
+StepLayout step_layout(int64_t partials, int64_t G, int64_t units) {
     StepLayout L{};
     L.o_off = 0;
     L.lse_off = align256(partials * G * HPC_DECODE_HEAD_DIM * 4);
     L.rec_off = align256(L.lse_off + partials * G * 4);
-    L.total = L.rec_off + 3 * n_workers * 4;
+    L.total = L.rec_off + 6 * units * 4;
     return L;
 }
 
@@ -183,7 +186,8 @@ extern "C" int64_t hpc_decode_step_workspace_size(int32_t batch, int32_t num_q_h
     if (batch < 0 || n_workers < 1 || num_kv_heads < 1 || num_q_heads < num_kv_heads ||
         num_q_heads % num_kv_heads != 0)
         return HPC_ERR_INVALID;
-    return step_layout(step_partials_bound(batch, num_kv_heads, n_workers), num_q_heads / num_kv_heads, n_workers)
+    return step_layout(step_partials_bound(batch, num_kv_heads, n_workers), num_q_heads / num_kv_heads,
+                       static_cast<int64_t>(batch) * num_kv_heads)
         .total;
 }
 
@@ -201,7 +205,9 @@ extern "C" int hpc_decode_step_check(const hpc_decode_params* p, int32_t batch, 
     if (!std::isfinite(p->sm_scale) || !std::isfinite(p->k_scale) || !std::isfinite(p->v_scale))
         return HPC_ERR_INVALID;
     if (batch < 1 || n_workers < 1) return HPC_ERR_INVALID;
-    if (batch > hpcd::kDeviceSchedMaxBatch) return HPC_ERR_UNSUPPORTED;
+    if (batch > hpcd::kDeviceSchedMaxBatch ||
+        static_cast<int64_t>(batch) * p->num_kv_heads > hpcd::kDeviceSchedMaxUnits)
+        return HPC_ERR_UNSUPPORTED;
     // every tile index the kernels form must fit in int32
     if (static_cast<int64_t>(batch) * p->max_pages_per_seq * p->num_kv_heads >= INT32_MAX) return HPC_ERR_INVALID;
     const int64_t need = hpc_decode_step_workspace_size(batch, p->num_q_heads, p->num_kv_heads, n_workers);
@@ -220,7 +226,7 @@ extern "C" int hpc_decode_step(const hpc_decode_params* p, int32_t batch, int32_
     if (status != HPC_OK) return status;
     const int32_t G = p->num_q_heads / p->num_kv_heads;
     const int64_t P = step_partials_bound(batch, p->num_kv_heads, n_workers);
-    const StepLayout L = step_layout(P, G, n_workers);
+    const StepLayout L = step_layout(P, G, static_cast<int64_t>(batch) * p->num_kv_heads);
     char* ws = static_cast<char*>(workspace);
     float* o_part = reinterpret_cast<float*>(ws + L.o_off);
     float* lse_part = reinterpret_cast<float*>(ws + L.lse_off);
@@ -258,11 +264,15 @@ extern "C" int hpc_decode_step(const hpc_decode_params* p, int32_t batch, int32_
     ca.group = G;
     ca.max_partials = static_cast<int32_t>(P);
 
-    const int prof_idx = claim_profile_events(ev, true);
+    ca.n_workers = n_workers;
+    const int64_t units = static_cast<int64_t>(batch) * p->num_kv_heads;
+    const bool any_split = n_workers > 1;
+
+    const int prof_idx = claim_profile_events(ev, any_split);
     if (prof_idx >= 0 && hipEventRecord(ev[0], s) != hipSuccess) return HPC_ERR_HIP;
     if (hpcd::launch_decode(da, p->kv_dtype, n_workers, true, stream) != 0) return HPC_ERR_HIP;
     if (prof_idx >= 0 && hipEventRecord(ev[1], s) != hipSuccess) return HPC_ERR_HIP;
-    if (hpcd::launch_combine(ca, n_workers, stream) != 0) return HPC_ERR_HIP;
+    if (any_split && hpcd::launch_combine(ca, static_cast<int>(units), true, stream) != 0) return HPC_ERR_HIP;
     if (prof_idx >= 0 && hipEventRecord(ev[2], s) != hipSuccess) return HPC_ERR_HIP;
     return HPC_OK;
 }

@@ -61,6 +61,9 @@ constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw (untyped) buffer, gfx9 fam
 constexpr int kPolicyStream = HPC_DECODE_KV_POLICY;   // K/V buffer-load cache policy (2: nontemporal)
 constexpr uint32_t kSelLo = 0x05040100u;       // v_perm: low halves of (a, b) -> {a.lo, b.lo}
 constexpr uint32_t kSelHi = 0x07060302u;       // v_perm: high halves -> {a.hi, b.hi}
+// device-scheduled merge record of a unit: {workers sharing it (0: empty),
+// its first worker, that worker's partial slot, first tile P_u, total tiles T, -}
+constexpr int kRecordWords = 6;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
@@ -142,6 +145,10 @@ struct TileSlot {
     int first, last;
     int row;      // b * Hq + h * G: first query head row of the entry
     int part;     // output target of the entry (see TileRef::part)
+    int page;     // physical page of the tile
+    int head;     // kv head of the tile
+    int rec_parts;  // device schedule: >= 0 when this entry writes its unit's merge record
+    int rec_slot;   // partial slot of this entry (for that record)
 };
 
 // Host-planned tile source: walks this worker's entries in the plan words.
@@ -228,65 +235,65 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     HostWalker hwalk;
     int64_t w_begin = 0, w_end = 0;
     if constexpr (DEV) {
-        build_prefix<kDecodeThreads>(seq_lens, a.batch, a.max_pages_per_seq, s_dyn, s_dyn + a.batch, s_tmp);
+        build_prefix(seq_lens, a.batch, a.max_pages_per_seq, s_dyn, s_dyn + a.batch);
         sched.len = s_dyn;
         sched.pb = s_dyn + a.batch;
         sched.B = a.batch;
         sched.H = Hkv;
         sched.W = gridDim.x;
         sched.T = static_cast<int64_t>(Hkv) * s_dyn[2 * a.batch];
-        // empty sequences get out = 0, lse = -inf from worker u mod W
-        for (int u = w; u < a.batch * Hkv; u += gridDim.x) {
-            const int b = u / Hkv;
-            if (sched.len[b] != 0) continue;
-            const int row = b * Hq + (u - b * Hkv) * G;
-            const int t = threadIdx.x;
-            if (t < G * 16)
-                *reinterpret_cast<u32x4*>(out + static_cast<int64_t>(row + (t >> 4)) * kHeadDim + 8 * (t & 15)) =
-                    u32x4{0u, 0u, 0u, 0u};
-            if (t < G) lse[row + t] = -INFINITY;
-        }
         w_begin = sched.range_begin(w);
         w_end = sched.range_begin(w + 1);
-        if (w_begin == w_end) {                    // uniform: an empty worker
-            if (threadIdx.x == 0) merge_records[3 * w] = -1;
-            return;
-        }
-        dwalk.init(sched, w_begin, w_end);
+        if (w_begin < w_end) dwalk.init(sched, w, w_begin, w_end, true);
+        else dwalk.remaining = 0;                  // an empty worker: only bookkeeping below
     } else {
         hwalk.init(worker_ptr, entries, seq_lens, Hkv, w);
         if (!hwalk.have) return;
     }
 
-    auto issue = [&](TileSlot<KV>& s) {
+    // Filling a ring slot: `plan_tile` takes the next tile of the worker and
+    // reads its page id; `load_tile` issues the K/V (and, for an entry's
+    // first tile, Q) loads.  The first PF slots are planned together so their
+    // page-id reads are in flight at once.
+    auto plan_tile = [&](TileSlot<KV>& s) {
         TileRef r;
         bool ok;
         if constexpr (DEV) ok = dwalk.next(r);
         else ok = hwalk.next(r);
-        int valid = 0, page = 0, h = 0, row = 0, part = -1, first = 0, last = 0;
+        int page = 0, h = 0, row = 0, part = -1, first = 0, last = 0, rem = 0, rparts = -1, rslot = -1;
         if (ok) {
             const int b = uniform(r.b);
             const int t = uniform(r.t);
             h = uniform(r.h);
             page = block_table[static_cast<int64_t>(b) * a.max_pages_per_seq + t];
-            const int rem = uniform(r.L) - t * kPage;
-            valid = rem < 0 ? 0 : (rem > kPage ? kPage : rem);
-            if (static_cast<unsigned>(page) >= static_cast<unsigned>(a.num_pages)) {
-                valid = 0;
-                page = 0;
-            }
+            rem = uniform(r.L) - t * kPage;
             row = b * Hq + h * G;
             first = r.first;
             last = r.last;
             part = r.part;
+            if constexpr (DEV) {
+                rparts = r.rec_parts;
+                rslot = r.rec_first_slot;
+            }
         }
         s.real = uniform(ok ? 1 : 0);
-        s.valid = uniform(valid);
+        s.valid = uniform(rem < 0 ? 0 : (rem > kPage ? kPage : rem));
+        s.page = page;
+        s.head = uniform(h);
         s.first = uniform(first);
         s.last = uniform(last);
         s.row = uniform(row);
         s.part = uniform(part);
-        const uint64_t off = (static_cast<uint64_t>(uniform(page)) * Hkv + uniform(h)) * kBlock;
+        s.rec_parts = uniform(rparts);
+        s.rec_slot = uniform(rslot);
+    };
+    auto load_tile = [&](TileSlot<KV>& s) {
+        int page = uniform(s.page);
+        if (static_cast<unsigned>(page) >= static_cast<unsigned>(a.num_pages)) {
+            s.valid = 0;
+            page = 0;
+        }
+        const uint64_t off = (static_cast<uint64_t>(page) * Hkv + s.head) * kBlock;
         const uint32_t kv_bytes = static_cast<uint32_t>(s.valid) * kRow;
         s.kv.load(make_rsrc(kcache + off, kv_bytes), make_rsrc(vcache + off, kv_bytes), wave, n, g);
         // Q^T operand of a new entry: head n, dims 32kk + 8g .. +8; heads >= G read as zero
@@ -296,43 +303,34 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
         for (int kk = 0; kk < 4; ++kk)
             s.q[kk] = __builtin_amdgcn_raw_buffer_load_b128(rq, n * kHeadDim * 2 + 64 * kk + 16 * g, 0, 0);
     };
+    auto issue = [&](TileSlot<KV>& s) {
+        plan_tile(s);
+        load_tile(s);
+    };
 
     TileSlot<KV> ring[PF];
 #pragma unroll
-    for (int j = 0; j < PF; ++j) issue(ring[j]);
+    for (int j = 0; j < PF; ++j) plan_tile(ring[j]);
+#pragma unroll
+    for (int j = 0; j < PF; ++j) load_tile(ring[j]);
 
-    // device schedule: partial slots of this worker's (at most two) split
-    // entries, and the merge record of the split unit this worker starts
-    // (its first worker writes it; no worker starts two), read by the merge
-    // kernel after this kernel completes
-    int slot_first = -1, slot_last = -1;
+    // Device schedule, while the first tiles are in flight: empty sequences
+    // get out = 0, lse = -inf and a merge record saying so, from worker
+    // u mod W (every other unit's record is written by the worker holding
+    // its first tile, so all records are rewritten every step).
     if constexpr (DEV) {
-        int b0, h0, t0, bl, hl, tl;
-        sched.locate(w_begin, b0, h0, t0);
-        sched.locate(w_end - 1, bl, hl, tl);
-        int base_f, base_l;
-        split_bases_wave(sched, b0 * Hkv + h0, bl * Hkv + hl, base_f, base_l);
-        const int rank_f = sched.rank_in_unit(w, b0, h0, t0);
-        slot_first = uniform(base_f + rank_f);
-        slot_last = uniform(base_l);
-        const bool single = (b0 == bl && h0 == hl);
-        const int S_f = sched.parts(b0, h0);
-        const int S_l = sched.parts(bl, hl);
-        int ru = -1, rS = 0, rbase = 0;
-        if (S_f >= 2 && rank_f == 0) {
-            ru = b0 * Hkv + h0;
-            rS = S_f;
-            rbase = base_f;
-        } else if (!single && S_l >= 2) {
-            ru = bl * Hkv + hl;
-            rS = S_l;
-            rbase = base_l;
+        const int U = a.batch * Hkv;
+        for (int u = w + static_cast<int>(gridDim.x) * threadIdx.x; u < U;
+             u += static_cast<int>(gridDim.x) * kDecodeThreads) {
+            const int b = u / Hkv;
+            if (sched.len[b] != 0) continue;
+            const int64_t row = static_cast<int64_t>(b) * Hq + (u - b * Hkv) * G;
+            for (int i = 0; i < G * 16; ++i)
+                *reinterpret_cast<u32x4*>(out + (row + (i >> 4)) * kHeadDim + 8 * (i & 15)) = u32x4{0u, 0u, 0u, 0u};
+            for (int i = 0; i < G; ++i) lse[row + i] = -INFINITY;
+            merge_records[kRecordWords * u] = 0;
         }
-        if (threadIdx.x == 0) {
-            merge_records[3 * w + 0] = ru;
-            merge_records[3 * w + 1] = rS;
-            merge_records[3 * w + 2] = rbase;
-        }
+        if (w_begin == w_end) return;
     }
 
     float m = -INFINITY;   // running max (log2 domain), uniform over g
@@ -342,7 +340,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     for (int nb = 0; nb < 8; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     bf16x8 qop[4];
 
-    auto flush = [&](int row, int part) {
+    auto flush = [&](const TileSlot<KV>& ts) {
+        const int row = ts.row;
+        const int part = ts.part;
         l += __shfl_xor(l, 16);
         l += __shfl_xor(l, 32);
         s_m[wave][lane] = m;
@@ -373,8 +373,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
             for (int s = 0; s < kWaves; ++s) x += wt[s] * s_acc[s][wave][nb][lane];
             o[nb] = x;
         }
-        int slot = part;
-        if constexpr (DEV) slot = (part == kPartFirst) ? slot_first : (part == kPartLast ? slot_last : part);
+        const int slot = part;
         if (n < G) {
             const float inv = (wsum > 0.f) ? a.v_scale / wsum : 0.f;
             const float lse_val = (wsum > 0.f) ? (M + __log2f(wsum)) * kLn2 : -INFINITY;
@@ -390,6 +389,18 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
                 *reinterpret_cast<f32x4*>(dst) = f32x4{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
                 *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv};
                 if (wave == 0 && g == 0) lse_part[static_cast<int64_t>(slot) * G + n] = lse_val;
+            }
+        }
+        if constexpr (DEV) {
+            if (ts.rec_parts >= 0 && threadIdx.x == 0) {   // this worker holds the unit's first tile
+                const int u = row / G;
+                const int bu = u / Hkv;
+                int32_t* rec = merge_records + kRecordWords * u;
+                rec[0] = ts.rec_parts;
+                rec[1] = w;
+                rec[2] = ts.rec_slot;
+                rec[3] = static_cast<int32_t>(sched.unit_start(bu, u - bu * Hkv));
+                rec[4] = static_cast<int32_t>(sched.T);
             }
         }
         __syncthreads();
@@ -443,7 +454,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
             acc[nb] = acc[nb] * alpha;
             acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(bitcast<bf16x4>(vt), pop, acc[nb], 0, 0, 0);
         }
-        if (s.last) flush(s.row, s.part);
+        if (s.last) flush(s);
     };
 
     // Leaving the loop the moment a slot is empty keeps every path that
@@ -467,11 +478,13 @@ done:
 // (max, weighted sum, weight) triple, issuing up to eight partials' loads
 // before using any of them; the 32 triples then meet in LDS and are merged
 // once more by log-sum-exp.  The records are the host plan's merge list, or,
-// for the device-scheduled step, one record per worker written by the decode
-// kernel (u = -1: nothing to merge; empty sequences were written there too).
+// for the device-scheduled step, the list the decode kernel wrote (a count,
+// then one record per split unit in unit order; the grid covers the largest
+// possible count and surplus blocks exit).
 constexpr int kMergeLanes = kCombineThreads / 32;
 constexpr int kMergeUnroll = 8;
 
+template <bool DEV>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a) {
     __shared__ f32x4 s_acc[kMergeLanes][32];
     __shared__ float s_m[kMergeLanes];
@@ -481,10 +494,32 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
     const int Hkv = a.num_kv_heads;
     const int c = blockIdx.x / G;
     const int n = blockIdx.x - c * G;
-    const int u = a.combine[3 * c + 0];
-    const int S = a.combine[3 * c + 1];
-    const int base = a.combine[3 * c + 2];
-    if (u < 0) return;   // per-worker records: this worker starts no split unit
+    int u, S, base = 0;
+    int w_first = 0, first_slot = 0, W = a.n_workers;
+    int64_t Pu = 0, T = 1;
+    if constexpr (DEV) {
+        const int32_t* rec = a.combine + kRecordWords * c;
+        u = c;
+        S = rec[0];
+        if (S <= 1) return;   // empty (written by the decode kernel) or written directly
+        w_first = rec[1];
+        first_slot = rec[2];
+        Pu = rec[3];
+        T = rec[4];
+    } else {
+        const int32_t* rec = a.combine + 3 * c;
+        u = rec[0];
+        S = rec[1];
+        base = rec[2];
+    }
+    // partial slot of the k-th worker of the unit
+    auto slot_of = [&](int k) -> int {
+        if constexpr (!DEV) return base + k;
+        if (k == 0) return first_slot;
+        // later workers start inside the unit, so it is their first entry (slot 2w)
+        if (static_cast<int64_t>(W) <= T) return 2 * (w_first + k);
+        return 2 * static_cast<int>(div_floor((Pu + k + 1) * W - 1, T));   // one tile per worker
+    };
     const int b = u / Hkv;
     const int h = u - b * Hkv;
     const int64_t row = static_cast<int64_t>(b) * (G * Hkv) + h * G + n;
@@ -498,7 +533,8 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
         if (t == 0) a.lse[row] = -INFINITY;
         return;
     }
-    if (static_cast<int64_t>(base) + S > a.max_partials) {   // never for a consistent schedule: report NaN
+    if (static_cast<int64_t>(slot_of(0)) >= a.max_partials || static_cast<int64_t>(slot_of(S - 1)) >= a.max_partials ||
+        (!DEV && static_cast<int64_t>(base) + S > a.max_partials)) {   // never for a consistent schedule: NaN
         if (pl == 0) *reinterpret_cast<u32x2*>(out + 4 * dq) = u32x2{0x7fc07fc0u, 0x7fc07fc0u};
         if (t == 0) a.lse[row] = __builtin_nanf("");
         return;
@@ -513,7 +549,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
 #pragma unroll
         for (int k = 0; k < kMergeUnroll; ++k) {
             const int i = i0 + k * kMergeLanes;
-            const int64_t p = static_cast<int64_t>(base + (i < S ? i : 0)) * G + n;
+            const int64_t p = static_cast<int64_t>(slot_of(i < S ? i : 0)) * G + n;
             lv[k] = (i < S) ? a.lse_part[p] * kLog2e : -INFINITY;
             o[k] = *reinterpret_cast<const f32x4*>(a.o_part + p * kHeadDim + 4 * dq);
         }
@@ -559,32 +595,6 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
     }
 }
 
-// Block-wide exclusive scan of arr[0..count) in LDS (kPlanThreads threads);
-// returns the total.  s_tmp needs kPlanThreads / 64 ints.
-__device__ int block_scan_inplace(int32_t* arr, int count, int32_t* s_tmp) {
-    const int t = threadIdx.x;
-    const int per = (count + kPlanThreads - 1) / kPlanThreads;
-    const int lo = t * per;
-    const int hi = min(count, lo + per);
-    int sum = 0;
-    for (int i = lo; i < hi; ++i) sum += arr[i];
-    const int incl = wave_inclusive_sum(sum);
-    __syncthreads();
-    if ((t & 63) == 63) s_tmp[t >> 6] = incl;
-    __syncthreads();
-    int run = incl - sum;
-    for (int w = 0; w < (t >> 6); ++w) run += s_tmp[w];
-    for (int i = lo; i < hi; ++i) {
-        const int x = arr[i];
-        arr[i] = run;
-        run += x;
-    }
-    int total = 0;
-    for (int w = 0; w < kPlanThreads / 64; ++w) total += s_tmp[w];
-    __syncthreads();
-    return total;
-}
-
 // The device schedule written out in the host plan's word layout, by one
 // workgroup, so it can be compared word for word with the host planner.
 __global__ __launch_bounds__(kPlanThreads) void plan_device_kernel(const int32_t* __restrict__ seq_lens, int B,
@@ -598,7 +608,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_device_kernel(const int32_t
     int32_t* s_cnt = s_pb + B + 1;        // [W]   entries per worker -> worker_ptr
     int32_t* s_base = s_cnt + W;          // [U]   split slots per unit -> base
     int32_t* s_cidx = s_base + U;         // [U]   merge record flag -> record index
-    build_prefix<kPlanThreads>(seq_lens, B, max_pages, s_len, s_pb, s_tmp);
+    build_prefix(seq_lens, B, max_pages, s_len, s_pb);
     Sched sched;
     sched.len = s_len;
     sched.pb = s_pb;
@@ -610,7 +620,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_device_kernel(const int32_t
 
     for (int w = t; w < W; w += kPlanThreads) {
         DeviceWalker dw;
-        dw.init(sched, sched.range_begin(w), sched.range_begin(w + 1));
+        dw.init(sched, w, sched.range_begin(w), sched.range_begin(w + 1), false);
         TileRef r;
         int cnt = 0;
         while (dw.next(r)) cnt += r.first ? 1 : 0;
@@ -623,9 +633,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_device_kernel(const int32_t
         s_cidx[u] = S != 1 ? 1 : 0;
     }
     __syncthreads();
-    const int E = block_scan_inplace(s_cnt, W, s_tmp);
-    const int P = block_scan_inplace(s_base, U, s_tmp);
-    const int C = block_scan_inplace(s_cidx, U, s_tmp);
+    const int E = block_scan_inplace<kPlanThreads>(s_cnt, W, s_tmp);
+    const int P = block_scan_inplace<kPlanThreads>(s_base, U, s_tmp);
+    const int C = block_scan_inplace<kPlanThreads>(s_cidx, U, s_tmp);
 
     int32_t* wp = plan + HPC_PLAN_HEADER_WORDS;
     int32_t* ent = wp + W + 1;
@@ -643,7 +653,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_device_kernel(const int32_t
         sched.locate(beg, b0, h0, t0);
         const int k0 = sched.rank_in_unit(w, b0, h0, t0);
         DeviceWalker dw;
-        dw.init(sched, beg, end);
+        dw.init(sched, w, beg, end, false);
         TileRef r;
         int e = s_cnt[w] - 1;
         int ta = 0;
@@ -654,7 +664,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_device_kernel(const int32_t
             }
             if (r.last) {
                 const int u = r.b * H + r.h;
-                const int slot = r.part == kPartFirst ? s_base[u] + k0 : (r.part == kPartLast ? s_base[u] : -1);
+                // the walker numbers split entries by worker (2w first, 2w + 1 last);
+                // the plan numbers them by unit: base_u + rank of the worker in the unit
+                const int slot = r.part < 0 ? -1 : (r.part == 2 * w ? s_base[u] + k0 : s_base[u]);
                 ent[4 * e + 0] = u;
                 ent[4 * e + 1] = ta;
                 ent[4 * e + 2] = r.t + 1;
@@ -708,9 +720,12 @@ int launch_decode(const DecodeArgs& a, int kv_dtype, int n_workers, bool device_
     return static_cast<int>(hipGetLastError());
 }
 
-int launch_combine(const CombineArgs& a, int n_records, void* stream) {
-    hipLaunchKernelGGL(combine_kernel, dim3(n_records * a.group), dim3(kCombineThreads), 0,
-                       static_cast<hipStream_t>(stream), a);
+int launch_combine(const CombineArgs& a, int n_records, bool device_sched, void* stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (device_sched)
+        hipLaunchKernelGGL(combine_kernel<true>, dim3(n_records * a.group), dim3(kCombineThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL(combine_kernel<false>, dim3(n_records * a.group), dim3(kCombineThreads), 0, s, a);
     return static_cast<int>(hipGetLastError());
 }
 

@@ -18,9 +18,22 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+extern "C" __device__ int __ockl_wfred_add_i32(int);
+extern "C" __device__ int __ockl_wfscan_add_i32(int, bool);
+
 namespace hpcd {
 
 __device__ __forceinline__ int tiles_of(int L) { return (L + 63) >> 6; }
+
+// floor(x / y) for 0 <= x < 2^62, 1 <= y < 2^31: a double-precision quotient
+// (off by at most one here) corrected with exact integer products; far
+// cheaper than the generic 64-bit integer division.
+__device__ __forceinline__ int64_t div_floor(int64_t x, int64_t y) {
+    int64_t q = static_cast<int64_t>(static_cast<double>(x) / static_cast<double>(y));
+    if (q * y > x) --q;
+    else if ((q + 1) * y <= x) ++q;
+    return q;
+}
 
 __device__ __forceinline__ int wave_inclusive_sum(int x) {
     const int lane = threadIdx.x & 63;
@@ -32,40 +45,32 @@ __device__ __forceinline__ int wave_inclusive_sum(int x) {
     return x;
 }
 
-__device__ __forceinline__ int wave_sum(int x) {
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d);
-    return x;
-}
+__device__ __forceinline__ int wave_sum(int x) { return __ockl_wfred_add_i32(x); }
 
 // Lengths (clamped to [0, max_pages * 64]) into s_len[B] and the exclusive
-// prefix of tile counts into s_pb[B + 1].  Every thread of the block calls
-// it; s_tmp needs NT / 64 ints.  Ends with a barrier.
-template <int NT>
+// prefix of tile counts into s_pb[B + 1], built by the first wave alone
+// (wave-wide scans, 64 sequences at a time); every thread of the block calls
+// it and it ends with the block's only barrier.
 __device__ void build_prefix(const int32_t* __restrict__ seq_lens, int B, int max_pages, int32_t* s_len,
-                             int32_t* s_pb, int32_t* s_tmp) {
-    const int t = threadIdx.x;
-    const int per = (B + NT - 1) / NT;
-    const int lo = t * per;
-    const int hi = min(B, lo + per);
-    const int cap = max_pages * 64;
-    int sum = 0;
-    for (int b = lo; b < hi; ++b) {
-        int L = seq_lens[b];
-        L = L < 0 ? 0 : (L > cap ? cap : L);
-        s_len[b] = L;
-        sum += tiles_of(L);
+                             int32_t* s_pb) {
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        const int cap = max_pages * 64;
+        int carry = 0;
+        for (int b0 = 0; b0 < B; b0 += 64) {
+            const int b = b0 + lane;
+            int L = b < B ? seq_lens[b] : 0;
+            L = L < 0 ? 0 : (L > cap ? cap : L);
+            const int n = tiles_of(L);
+            const int incl = __ockl_wfscan_add_i32(n, true);
+            if (b < B) {
+                s_len[b] = L;
+                s_pb[b] = carry + incl - n;
+            }
+            carry += __shfl(incl, 63);
+        }
+        if (lane == 0) s_pb[B] = carry;
     }
-    const int incl = wave_inclusive_sum(sum);
-    if ((t & 63) == 63) s_tmp[t >> 6] = incl;
-    __syncthreads();
-    int run = incl - sum;
-    for (int w = 0; w < (t >> 6); ++w) run += s_tmp[w];
-    for (int b = lo; b < hi; ++b) {
-        s_pb[b] = run;
-        run += tiles_of(s_len[b]);
-    }
-    if (t == NT - 1) s_pb[B] = run;
     __syncthreads();
 }
 
@@ -79,9 +84,9 @@ struct Sched {
     __device__ __forceinline__ int64_t unit_start(int b, int h) const {
         return static_cast<int64_t>(H) * pb[b] + static_cast<int64_t>(h) * tiles(b);
     }
-    __device__ __forceinline__ int64_t range_begin(int w) const { return (static_cast<int64_t>(w) * T) / W; }
+    __device__ __forceinline__ int64_t range_begin(int w) const { return div_floor(static_cast<int64_t>(w) * T, W); }
     __device__ __forceinline__ int owner(int64_t j) const {    // valid for W <= T
-        return static_cast<int>(((j + 1) * W - 1) / T);
+        return static_cast<int>(div_floor((j + 1) * W - 1, T));
     }
     // number of workers that share unit (b, h)
     __device__ __forceinline__ int parts(int b, int h) const {
@@ -91,7 +96,16 @@ struct Sched {
         const int64_t a = unit_start(b, h);
         return owner(a + n - 1) - owner(a) + 1;
     }
-    // (b, h, t) of global tile j, 0 <= j < T
+    // (b, h, t) of global tile j, 0 <= j < T: b is the last sequence whose
+    // tiles start at or before j (such a sequence has tiles).
+    __device__ __forceinline__ void split_tile(int64_t j, int b_, int& b, int& h, int& t) const {
+        b = b_;
+        const int n = tiles(b);
+        const int r = static_cast<int>(j - static_cast<int64_t>(H) * pb[b]);   // < H * n < 2^31
+        h = r / n;
+        t = r - h * n;
+    }
+    // per-thread form: binary search over the non-decreasing prefix
     __device__ __forceinline__ void locate(int64_t j, int& b, int& h, int& t) const {
         int lo = 0, hi = B;
         while (hi - lo > 1) {
@@ -99,11 +113,20 @@ struct Sched {
             if (static_cast<int64_t>(H) * pb[mid] <= j) lo = mid;
             else hi = mid;
         }
-        b = lo;
-        const int n = tiles(b);
-        const int64_t r = j - static_cast<int64_t>(H) * pb[b];
-        h = static_cast<int>(r / n);
-        t = static_cast<int>(r - static_cast<int64_t>(h) * n);
+        split_tile(j, lo, b, h, t);
+    }
+    // wave-uniform j, whole wave active: the lanes test 64 sequences at once
+    // and count the ones that start at or before j
+    __device__ __forceinline__ void locate_uniform(int64_t j, int& b, int& h, int& t) const {
+        int count = 0;
+        for (int b0 = 0; b0 < B; b0 += 64) {
+            const int bb = b0 + (threadIdx.x & 63);
+            const bool le = bb < B && static_cast<int64_t>(H) * pb[bb] <= j;
+            const int c = __popcll(__ballot(le));
+            count += c;
+            if (c < 64) break;
+        }
+        split_tile(j, __builtin_amdgcn_readfirstlane(count - 1), b, h, t);
     }
     // k such that worker w (whose range starts at tile `t_first` of unit
     // (b, h)) is the k-th worker of that unit
@@ -113,50 +136,31 @@ struct Sched {
     }
 };
 
-// base_u of two units at once: sum over u' < u of S_u' for split units.
-// Wave-level (every wave computes it for itself; no barrier).
-__device__ __forceinline__ void split_bases_wave(const Sched& s, int u1, int u2, int& base1, int& base2) {
-    int a1 = 0, a2 = 0;
-    const int umax = max(u1, u2);
-    for (int u = threadIdx.x & 63; u < umax; u += 64) {
-        const int b = u / s.H;
-        const int S = s.parts(b, u - b * s.H);
-        const int c = S >= 2 ? S : 0;
-        if (u < u1) a1 += c;
-        if (u < u2) a2 += c;
-    }
-    base1 = wave_sum(a1);
-    base2 = wave_sum(a2);
-}
-
-// Block-wide form of the same (NT threads, all must call); s_tmp needs
-// 2 * NT / 64 ints.
+// Block-wide exclusive scan of arr[0..count) in LDS (NT threads, all must
+// call); returns the total.  s_tmp needs NT / 64 ints.
 template <int NT>
-__device__ void split_bases(const Sched& s, int u1, int u2, int& base1, int& base2, int32_t* s_tmp) {
-    int a1 = 0, a2 = 0;
-    const int umax = max(u1, u2);
-    for (int u = threadIdx.x; u < umax; u += NT) {
-        const int b = u / s.H;
-        const int S = s.parts(b, u - b * s.H);
-        const int c = S >= 2 ? S : 0;
-        if (u < u1) a1 += c;
-        if (u < u2) a2 += c;
-    }
-    a1 = wave_sum(a1);
-    a2 = wave_sum(a2);
-    __syncthreads();   // s_tmp may still be read by an earlier caller
-    if ((threadIdx.x & 63) == 0) {
-        s_tmp[2 * (threadIdx.x >> 6)] = a1;
-        s_tmp[2 * (threadIdx.x >> 6) + 1] = a2;
-    }
+__device__ int block_scan_inplace(int32_t* arr, int count, int32_t* s_tmp) {
+    const int t = threadIdx.x;
+    const int per = (count + NT - 1) / NT;
+    const int lo = t * per;
+    const int hi = min(count, lo + per);
+    int sum = 0;
+    for (int i = lo; i < hi; ++i) sum += arr[i];
+    const int incl = __ockl_wfscan_add_i32(sum, true);
+    __syncthreads();   // s_tmp may still be read by an earlier call
+    if ((t & 63) == 63) s_tmp[t >> 6] = incl;
     __syncthreads();
-    base1 = 0;
-    base2 = 0;
-#pragma unroll
-    for (int w = 0; w < NT / 64; ++w) {
-        base1 += s_tmp[2 * w];
-        base2 += s_tmp[2 * w + 1];
+    int run = incl - sum;
+    for (int w = 0; w < (t >> 6); ++w) run += s_tmp[w];
+    for (int i = lo; i < hi; ++i) {
+        const int x = arr[i];
+        arr[i] = run;
+        run += x;
     }
+    int total = 0;
+    for (int w = 0; w < NT / 64; ++w) total += s_tmp[w];
+    __syncthreads();
+    return total;
 }
 
 // Walks one worker's tiles in order, entry by entry.  Device-scheduled form:
@@ -166,31 +170,54 @@ struct TileRef {
     int b, h, t;       // sequence, kv head, tile of the unit
     int L;             // sequence length
     bool first, last;  // first / last tile of its entry
-    int part;          // -1: direct output; >= 0: partial slot; kPartFirst / kPartLast: resolved later
+    int part;          // -1: direct output; >= 0: partial slot
+    int rec_parts;     // device schedule, entry starting at the unit's first tile: workers sharing
+                       // the unit (its merge record is written by this worker); else -1
+    int rec_first_slot;  // partial slot of this worker's entry of that unit (when rec_parts >= 2)
 };
 
-constexpr int kPartFirst = -2;   // the worker's first entry, split
-constexpr int kPartLast = -3;    // the worker's last entry, split
-
+// Device-scheduled walker.  Partial slots are worker-indexed: a split entry
+// is either the worker's first entry (slot 2w) or its last (slot 2w + 1) —
+// only those two can extend past the worker's range.  The worker holding a
+// unit's first tile reports, at that entry, how many workers share the unit,
+// for the unit's merge record.
 struct DeviceWalker {
     const Sched* s;
-    int b, h, t, n;          // next tile to hand out
+    int w;                   // this worker
+    int b, h, t, n;          // next tile to hand out; n = tiles of sequence b
+    int L;                   // length of sequence b
     int64_t remaining;       // tiles of the worker not yet handed out
     bool at_start;           // the next tile is the worker's first
-    int cur_part;            // part code of the entry holding the next tile
+    int cur_part, cur_rec_parts, cur_rec_slot;   // of the entry holding the next tile
 
-    __device__ __forceinline__ void init(const Sched& sched, int64_t begin, int64_t end) {
+    __device__ __forceinline__ void start_entry(bool worker_first) {
+        const bool split = (t > 0) || (static_cast<int64_t>(n - t) > remaining);
+        cur_part = split ? 2 * w + (worker_first ? 0 : 1) : -1;
+        cur_rec_parts = -1;
+        cur_rec_slot = cur_part;
+        if (t == 0) {   // this worker owns the unit's first tile
+            if (!split) cur_rec_parts = 1;
+            else if (static_cast<int64_t>(s->W) > s->T) cur_rec_parts = n;
+            else cur_rec_parts = s->owner(s->unit_start(b, h) + n - 1) - w + 1;
+        }
+    }
+
+    // wave_uniform: begin is the same in every lane and the whole wave is active
+    __device__ __forceinline__ void init(const Sched& sched, int worker, int64_t begin, int64_t end,
+                                         bool wave_uniform) {
         s = &sched;
+        w = worker;
         remaining = end - begin;
         at_start = true;
         if (remaining > 0) {
-            sched.locate(begin, b, h, t);
-            n = sched.tiles(b);
-            const bool split = (t > 0) || (static_cast<int64_t>(n - t) > remaining);
-            cur_part = split ? kPartFirst : -1;
+            if (wave_uniform) sched.locate_uniform(begin, b, h, t);
+            else sched.locate(begin, b, h, t);
+            L = sched.len[b];
+            n = tiles_of(L);
+            start_entry(true);
         } else {
-            b = h = t = n = 0;
-            cur_part = -1;
+            b = h = t = n = L = 0;
+            cur_part = cur_rec_parts = cur_rec_slot = -1;
         }
     }
 
@@ -199,10 +226,12 @@ struct DeviceWalker {
         r.b = b;
         r.h = h;
         r.t = t;
-        r.L = s->len[b];
+        r.L = L;
         r.first = (t == 0) || at_start;
         r.last = (t == n - 1) || (remaining == 1);
         r.part = cur_part;
+        r.rec_parts = cur_rec_parts;
+        r.rec_first_slot = cur_rec_slot;
         at_start = false;
         --remaining;
         ++t;
@@ -211,12 +240,11 @@ struct DeviceWalker {
             ++h;
             if (h == s->H) {
                 h = 0;
-                do { ++b; } while (s->tiles(b) == 0);
+                do { ++b; } while (s->len[b] == 0);
+                L = s->len[b];
+                n = tiles_of(L);
             }
-            n = s->tiles(b);
-            // an entry after the first starts at tile 0; it is split only if
-            // the worker's range ends inside it (then it is the last entry)
-            cur_part = (static_cast<int64_t>(n) > remaining) ? kPartLast : -1;
+            start_entry(false);
         }
         return true;
     }

@@ -13,9 +13,10 @@ constexpr int kDecodeThreads = 64 * kWaves;
 constexpr int kCombineThreads = 1024;
 constexpr int kPlanThreads = 1024;
 
-// Limits of the device-scheduled path: the lengths (and their tile prefix)
-// live in LDS of every workgroup.
-constexpr int kDeviceSchedMaxBatch = 4096;
+// Limits of the device-scheduled path: the lengths, their tile prefix and
+// the per-unit split tables live in LDS of every workgroup.
+constexpr int kDeviceSchedMaxBatch = 2048;
+constexpr int kDeviceSchedMaxUnits = 4096;
 // Limits of the plan-materialising kernel (one workgroup, everything in LDS).
 constexpr int kPlanDeviceMaxBatch = 2048;
 constexpr int kPlanDeviceMaxWorkers = 2048;
@@ -33,7 +34,7 @@ struct DecodeArgs {
     float* lse;                  // [B][Hq]
     float* o_part;               // [n_partials][G][128]
     float* lse_part;             // [n_partials][G]
-    int32_t* merge_records;      // device schedule: [W][3] (unit or -1, partials, first slot)
+    int32_t* merge_records;      // device schedule: [units][6] merge records (see decode_kernels.hip)
     int32_t batch;
     int32_t num_kv_heads;
     int32_t group;               // G = Hq / H_kv, 1..16
@@ -45,7 +46,8 @@ struct DecodeArgs {
 };
 
 struct CombineArgs {
-    const int32_t* combine;      // merge records, 3 per record (host plan list, or one per worker)
+    const int32_t* combine;      // merge records: host plan list (3 words each) or per-unit device records
+    int32_t n_workers;           // W (device records)
     const float* o_part;
     const float* lse_part;
     void* out;
@@ -57,9 +59,9 @@ struct CombineArgs {
 
 // All return the hipError_t of the launch as int (0 = success).
 // device_sched: the decode kernel derives the schedule from seq_lens itself
-// and writes one merge record per worker for the merge kernel.
+// and writes one merge record per unit for the merge kernel.
 int launch_decode(const DecodeArgs& a, int kv_dtype, int n_workers, bool device_sched, void* stream);
-int launch_combine(const CombineArgs& a, int n_records, void* stream);
+int launch_combine(const CombineArgs& a, int n_records, bool device_sched, void* stream);
 int launch_plan_device(const int32_t* seq_lens, int batch, int num_kv_heads, int n_workers,
                        int max_pages_per_seq, int32_t* plan, void* stream);
 

@@ -193,9 +193,9 @@ def test_step_check_errors():
     ptr = ctypes.c_void_p(0x1000)
     params = hd.make_params(8, 1, 4, 8, hd.HPC_KV_BF16, 1 / np.sqrt(128))
     need = hd.hpc_decode_step_workspace_size(2, 8, 1, 16)
-    P = 16 + 2
+    P = 2 * 16            # two partial slots per worker
     al = lambda x: (x + 255) // 256 * 256
-    assert need == al(al(P * 8 * 128 * 4) + P * 8 * 4) + 3 * 16 * 4
+    assert need == al(al(P * 8 * 128 * 4) + P * 8 * 4) + 6 * 2 * 4
 
     def chk(batch=2, W=16, ws=ptr, wsb=need, **over):
         a = dict(q=ptr, k=ptr, v=ptr, bt=ptr, sl=ptr, out=ptr, lse=ptr)
@@ -208,7 +208,7 @@ def test_step_check_errors():
     assert chk(batch=0) == hd.HPC_ERR_INVALID and chk(W=0) == hd.HPC_ERR_INVALID
     assert chk(batch=5000, wsb=1 << 40) == hd.HPC_ERR_UNSUPPORTED
     params.max_pages_per_seq = 1 << 20
-    assert chk(batch=4096, wsb=1 << 40) == hd.HPC_ERR_INVALID       # tile indices beyond int32
+    assert chk(batch=2048, wsb=1 << 40) == hd.HPC_ERR_INVALID       # tile indices beyond int32
     params.max_pages_per_seq = 4
     params.head_dim = 64
     assert chk() == hd.HPC_ERR_UNSUPPORTED
