@@ -4,10 +4,10 @@
 A step is the whole hot path for one batch: the per-step schedule (64-token
 tiles spread evenly over the persistent grid), the decode kernel, and the
 log-sum-exp merge of split sequences.  With --schedule device (default) the
-schedule is derived inside the single decode kernel from the lengths on the
-GPU and the merge is fused into it; with --schedule host the C++ planner runs
-on the host every step, the plan is uploaded, and a merge kernel follows the
-decode kernel.  Default workload: the skewed batch of one
+decode kernel derives the schedule from the lengths on the GPU and writes one
+merge record per (sequence, KV head) for the merge kernel that follows; with
+--schedule host the C++ planner runs on the host every step, the plan is
+uploaded, and the decode and merge kernels read it.  Default workload: the skewed batch of one
 131072-token sequence and 31 sequences of 4096 tokens, 8 query heads over one
 KV head, head dim 128, bf16 KV in 64-token pages, shuffled block table
 ("vLLM x HPC-Ops ...", §Attention Decode under Mixed-Length Batches).
@@ -31,6 +31,33 @@ import time
 
 METRIC = "decode-attn µs/step & achieved HBM TB/s on 1×128K+31×4K mixed batch"
 HBM_PEAK_GBPS = 8000.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_traffic_skewed-1x128k+31x4k.json")
+KERNEL_SOURCES = ("load_balanced_paged_step_amd/csrc/decode_kernels.hip",
+                  "load_balanced_paged_step_amd/csrc/device_schedule.h")
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload_name: str, schedule: str, n_workers: int):
+    """HBM bytes per decode launch from the committed counter summary, or None
+    when it was taken for another configuration or an older kernel."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if (t.get("kernel_source_sha256") != kernel_source_hash() or t.get("workload") != workload_name
+            or t.get("schedule") != schedule or t.get("n_workers") != n_workers):
+        return None
+    return t.get("hbm_bytes_per_launch")
 
 
 def log(msg: str) -> None:
@@ -47,6 +74,8 @@ def parse_args():
     ap.add_argument("--copies", type=int, default=0, help="rotating KV copies (0: enough for >= 1 GiB)")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--probe", action="store_true", help="also measure the HBM streaming-read ceiling")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run the plain copy kernel over MIB MiB (hardware-counter calibration) and exit")
     ap.add_argument("--schedule", choices=["device", "host"], default="device",
                     help="device: kernels derive the per-step schedule from the lengths on the GPU; "
                          "host: C++ planner on the host + plan upload every step")
@@ -92,6 +121,15 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
+    if args.calibrate_copy:
+        nbytes = args.calibrate_copy << 20
+        src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            hd.hpc_probe_copy(src, dst)
+        torch.cuda.synchronize()
+        log(f"copied {nbytes} bytes x 3 with the probe copy kernel")
+        return 0
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     props = torch.cuda.get_device_properties(dev)
@@ -197,8 +235,10 @@ def main() -> int:
         "kernels": {"decode_us": round(decode_us, 3), "merge_us": round(combine_us, 3),
                     "plan_host_us": round(plan_us, 2), "timed_calls": n_calls},
         "roofline": {"bound": "hbm", "achieved": round(achieved_gbps, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "kernel": "decode_kernel", "bytes_per_launch": alg_bytes},
+                     "unit": "GB/s", "frac": round(achieved_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic(wl.name, args.schedule, W),
+                     "kernel": "decode_kernel", "bytes_per_launch": alg_bytes,
+                     "kernel_us_hip_events": round(decode_us, 3)},
     }
 
     if args.probe:
@@ -207,7 +247,7 @@ def main() -> int:
         buf.fill_(1)
         sink = torch.empty(4096, dtype=torch.float32, device=dev)
         best = 0.0
-        for nwg in (cus * 4, cus * 8, cus * 16):
+        for nwg in (cus * 2, cus * 4, cus * 16):
             for _ in range(3):
                 hd.hpc_probe_read(buf, sink, nwg)
             torch.cuda.synchronize()

@@ -220,13 +220,14 @@ int hpc_decode_plan_device(const int32_t* seq_lens, int32_t batch, int32_t num_k
 const char* hpc_status_string(int status);
 
 /*
- * Optional profiling window (measurement only; global state, not
- * thread-safe).  Between start and stop every hpc_decode_attn or
- * hpc_decode_step call brackets
- * its decode-kernel launch and its merge-kernel launch with HIP events on
- * the call's stream (at most `capacity` calls are recorded).  stop
- * synchronises those events and returns the summed durations in ms and the
- * number of calls recorded.  Returns HPC_ERR_HIP on event failures.
+ * Optional profiling window (measurement only; global state guarded by a
+ * lock).  Between start and stop every hpc_decode_attn or hpc_decode_step
+ * call launches its decode kernel and its merge kernel with a pair of HIP
+ * events that the dispatch itself stamps at the kernel's start and end (the
+ * kernel's own execution time, not the queue gaps around it; at most
+ * `capacity` calls are recorded).  stop synchronises those events and
+ * returns the summed kernel durations in ms and the number of calls
+ * recorded.  Returns HPC_ERR_HIP on event failures.
  */
 int hpc_decode_profile_start(int32_t capacity);
 int hpc_decode_profile_stop(double* decode_ms, double* combine_ms, int32_t* n_calls);

@@ -20,18 +20,18 @@ struct ProfileWindow {
     bool active = false;
     int32_t capacity = 0;
     int32_t used = 0;
-    std::vector<hipEvent_t> ev;   // 3 per call: before decode, after decode, after merge
-    std::vector<uint8_t> has_combine;
+    std::vector<hipEvent_t> ev;   // 4 per call: decode start / end, merge start / end (kernel timestamps)
+    std::vector<uint8_t> launched;  // per call: bit 0 decode kernel, bit 1 merge kernel
 };
 ProfileWindow g_prof;
 
 // events for one profiled call, or -1 outside a profiling window
-int claim_profile_events(hipEvent_t ev[3], bool has_combine) {
+int claim_profile_events(hipEvent_t ev[4], bool has_decode, bool has_combine) {
     std::lock_guard<std::mutex> lk(g_prof.mu);
     if (!g_prof.active || g_prof.used >= g_prof.capacity) return -1;
     const int idx = g_prof.used++;
-    for (int i = 0; i < 3; ++i) ev[i] = g_prof.ev[3 * static_cast<std::size_t>(idx) + i];
-    g_prof.has_combine[idx] = has_combine ? 1 : 0;
+    for (int i = 0; i < 4; ++i) ev[i] = g_prof.ev[4 * static_cast<std::size_t>(idx) + i];
+    g_prof.launched[idx] = static_cast<uint8_t>((has_decode ? 1 : 0) | (has_combine ? 2 : 0));
     return idx;
 }
 
@@ -39,7 +39,7 @@ void destroy_events() {
     for (hipEvent_t e : g_prof.ev)
         if (e) (void)hipEventDestroy(e);
     g_prof.ev.clear();
-    g_prof.has_combine.clear();
+    g_prof.launched.clear();
 }
 
 }  // namespace
@@ -141,14 +141,10 @@ extern "C" int hpc_decode_attn(const hpc_decode_params* p, const void* q, const 
     ca.group = G;
     ca.max_partials = P;
 
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
-    const int prof_idx = claim_profile_events(ev, C > 0);
-    if (prof_idx >= 0 && hipEventRecord(ev[0], s) != hipSuccess) return HPC_ERR_HIP;
-    if (E > 0 && hpcd::launch_decode(da, p->kv_dtype, W, false, stream) != 0) return HPC_ERR_HIP;
-    if (prof_idx >= 0 && hipEventRecord(ev[1], s) != hipSuccess) return HPC_ERR_HIP;
-    if (C > 0 && hpcd::launch_combine(ca, C, false, stream) != 0) return HPC_ERR_HIP;
-    if (prof_idx >= 0 && hipEventRecord(ev[2], s) != hipSuccess) return HPC_ERR_HIP;
+    hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
+    claim_profile_events(ev, E > 0, C > 0);
+    if (E > 0 && hpcd::launch_decode(da, p->kv_dtype, W, false, stream, ev[0], ev[1]) != 0) return HPC_ERR_HIP;
+    if (C > 0 && hpcd::launch_combine(ca, C, false, stream, ev[2], ev[3]) != 0) return HPC_ERR_HIP;
     return HPC_OK;
 }
 
@@ -252,8 +248,7 @@ extern "C" int hpc_decode_step(const hpc_decode_params* p, int32_t batch, int32_
     da.qk_scale_log2 = static_cast<float>(static_cast<double>(p->sm_scale) * p->k_scale * 1.4426950408889634);
     da.v_scale = p->v_scale;
 
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+    hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
     hpcd::CombineArgs ca{};
     ca.combine = records;
     ca.o_part = o_part;
@@ -268,12 +263,10 @@ extern "C" int hpc_decode_step(const hpc_decode_params* p, int32_t batch, int32_
     const int64_t units = static_cast<int64_t>(batch) * p->num_kv_heads;
     const bool any_split = n_workers > 1;
 
-    const int prof_idx = claim_profile_events(ev, any_split);
-    if (prof_idx >= 0 && hipEventRecord(ev[0], s) != hipSuccess) return HPC_ERR_HIP;
-    if (hpcd::launch_decode(da, p->kv_dtype, n_workers, true, stream) != 0) return HPC_ERR_HIP;
-    if (prof_idx >= 0 && hipEventRecord(ev[1], s) != hipSuccess) return HPC_ERR_HIP;
-    if (any_split && hpcd::launch_combine(ca, static_cast<int>(units), true, stream) != 0) return HPC_ERR_HIP;
-    if (prof_idx >= 0 && hipEventRecord(ev[2], s) != hipSuccess) return HPC_ERR_HIP;
+    claim_profile_events(ev, true, any_split);
+    if (hpcd::launch_decode(da, p->kv_dtype, n_workers, true, stream, ev[0], ev[1]) != 0) return HPC_ERR_HIP;
+    if (any_split && hpcd::launch_combine(ca, static_cast<int>(units), true, stream, ev[2], ev[3]) != 0)
+        return HPC_ERR_HIP;
     return HPC_OK;
 }
 
@@ -296,8 +289,8 @@ extern "C" int hpc_decode_profile_start(int32_t capacity) {
     if (capacity < 1) return HPC_ERR_INVALID;
     std::lock_guard<std::mutex> lk(g_prof.mu);
     destroy_events();
-    g_prof.ev.assign(3 * static_cast<std::size_t>(capacity), nullptr);
-    g_prof.has_combine.assign(static_cast<std::size_t>(capacity), 0);
+    g_prof.ev.assign(4 * static_cast<std::size_t>(capacity), nullptr);
+    g_prof.launched.assign(static_cast<std::size_t>(capacity), 0);
     for (hipEvent_t& e : g_prof.ev) {
         if (hipEventCreate(&e) != hipSuccess) {
             e = nullptr;
@@ -319,14 +312,17 @@ extern "C" int hpc_decode_profile_stop(double* decode_ms, double* combine_ms, in
     int rc = HPC_OK;
     for (int32_t i = 0; i < g_prof.used; ++i) {
         float a = 0.f, b = 0.f;
-        if (hipEventSynchronize(g_prof.ev[3 * i + 2]) != hipSuccess ||
-            hipEventElapsedTime(&a, g_prof.ev[3 * i], g_prof.ev[3 * i + 1]) != hipSuccess) {
-            rc = HPC_ERR_HIP;
-            break;
+        if (g_prof.launched[i] & 1) {
+            if (hipEventSynchronize(g_prof.ev[4 * i + 1]) != hipSuccess ||
+                hipEventElapsedTime(&a, g_prof.ev[4 * i], g_prof.ev[4 * i + 1]) != hipSuccess) {
+                rc = HPC_ERR_HIP;
+                break;
+            }
+            dsum += a;
         }
-        dsum += a;
-        if (g_prof.has_combine[i]) {
-            if (hipEventElapsedTime(&b, g_prof.ev[3 * i + 1], g_prof.ev[3 * i + 2]) != hipSuccess) {
+        if (g_prof.launched[i] & 2) {
+            if (hipEventSynchronize(g_prof.ev[4 * i + 3]) != hipSuccess ||
+                hipEventElapsedTime(&b, g_prof.ev[4 * i + 2], g_prof.ev[4 * i + 3]) != hipSuccess) {
                 rc = HPC_ERR_HIP;
                 break;
             }

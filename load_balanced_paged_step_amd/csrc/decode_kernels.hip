@@ -36,8 +36,11 @@
 //   PV:  A = V^T [dim 8n+nb][tokens 4g .. 4g+3], B = P^T [tokens 4g+i][head n],
 //        D[dim 8(4g+i)+nb][head n] in register i of accumulator nb.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <cstdint>
 
 #include "device_schedule.h"
 #include "hpc_decode.h"
@@ -696,36 +699,43 @@ constexpr int kPrefetchBf16 = HPC_DECODE_PREFETCH_BF16;
 constexpr int kPrefetchFp8 = HPC_DECODE_PREFETCH_FP8;
 
 template <int KV, int PF, bool DEV>
-void launch_decode_t(const DecodeArgs& a, int n_workers, size_t lds, hipStream_t s) {
+void launch_decode_t(const DecodeArgs& a, int n_workers, size_t lds, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     const DecodeScalars sc{a.batch,        a.num_kv_heads,  a.group,  a.max_pages_per_seq, a.num_pages,
                            a.max_partials, a.qk_scale_log2, a.v_scale};
-    hipLaunchKernelGGL((decode_kernel<KV, PF, DEV>), dim3(n_workers), dim3(kDecodeThreads), lds, s,
-                       static_cast<const __bf16*>(a.q), static_cast<const char*>(a.k),
-                       static_cast<const char*>(a.v), a.block_table, a.seq_lens, a.worker_ptr, a.entries,
-                       static_cast<__bf16*>(a.out), a.lse, a.o_part, a.lse_part, a.merge_records, sc);
+    hipExtLaunchKernelGGL((decode_kernel<KV, PF, DEV>), dim3(n_workers), dim3(kDecodeThreads),
+                          static_cast<std::uint32_t>(lds), s, e0, e1, 0u,
+                          static_cast<const __bf16*>(a.q), static_cast<const char*>(a.k),
+                          static_cast<const char*>(a.v), a.block_table, a.seq_lens, a.worker_ptr, a.entries,
+                          static_cast<__bf16*>(a.out), a.lse, a.o_part, a.lse_part, a.merge_records, sc);
 }
 
 }  // namespace
 
-int launch_decode(const DecodeArgs& a, int kv_dtype, int n_workers, bool device_sched, void* stream) {
+int launch_decode(const DecodeArgs& a, int kv_dtype, int n_workers, bool device_sched, void* stream,
+                  void* ev_start, void* ev_stop) {
     hipStream_t s = static_cast<hipStream_t>(stream);
+    hipEvent_t e0 = static_cast<hipEvent_t>(ev_start), e1 = static_cast<hipEvent_t>(ev_stop);
     const size_t lds = device_sched ? (2 * static_cast<size_t>(a.batch) + 1) * sizeof(int32_t) : 0;
     if (kv_dtype == HPC_KV_BF16) {
-        if (device_sched) launch_decode_t<HPC_KV_BF16, kPrefetchBf16, true>(a, n_workers, lds, s);
-        else launch_decode_t<HPC_KV_BF16, kPrefetchBf16, false>(a, n_workers, lds, s);
+        if (device_sched) launch_decode_t<HPC_KV_BF16, kPrefetchBf16, true>(a, n_workers, lds, s, e0, e1);
+        else launch_decode_t<HPC_KV_BF16, kPrefetchBf16, false>(a, n_workers, lds, s, e0, e1);
     } else {
-        if (device_sched) launch_decode_t<HPC_KV_FP8_E4M3, kPrefetchFp8, true>(a, n_workers, lds, s);
-        else launch_decode_t<HPC_KV_FP8_E4M3, kPrefetchFp8, false>(a, n_workers, lds, s);
+        if (device_sched) launch_decode_t<HPC_KV_FP8_E4M3, kPrefetchFp8, true>(a, n_workers, lds, s, e0, e1);
+        else launch_decode_t<HPC_KV_FP8_E4M3, kPrefetchFp8, false>(a, n_workers, lds, s, e0, e1);
     }
     return static_cast<int>(hipGetLastError());
 }
 
-int launch_combine(const CombineArgs& a, int n_records, bool device_sched, void* stream) {
+int launch_combine(const CombineArgs& a, int n_records, bool device_sched, void* stream, void* ev_start,
+                   void* ev_stop) {
     hipStream_t s = static_cast<hipStream_t>(stream);
+    hipEvent_t e0 = static_cast<hipEvent_t>(ev_start), e1 = static_cast<hipEvent_t>(ev_stop);
     if (device_sched)
-        hipLaunchKernelGGL(combine_kernel<true>, dim3(n_records * a.group), dim3(kCombineThreads), 0, s, a);
+        hipExtLaunchKernelGGL(combine_kernel<true>, dim3(n_records * a.group), dim3(kCombineThreads), 0u, s, e0, e1,
+                              0u, a);
     else
-        hipLaunchKernelGGL(combine_kernel<false>, dim3(n_records * a.group), dim3(kCombineThreads), 0, s, a);
+        hipExtLaunchKernelGGL(combine_kernel<false>, dim3(n_records * a.group), dim3(kCombineThreads), 0u, s, e0,
+                              e1, 0u, a);
     return static_cast<int>(hipGetLastError());
 }
 

@@ -60,8 +60,12 @@ struct CombineArgs {
 // All return the hipError_t of the launch as int (0 = success).
 // device_sched: the decode kernel derives the schedule from seq_lens itself
 // and writes one merge record per unit for the merge kernel.
-int launch_decode(const DecodeArgs& a, int kv_dtype, int n_workers, bool device_sched, void* stream);
-int launch_combine(const CombineArgs& a, int n_records, bool device_sched, void* stream);
+// ev_start / ev_stop (hipEvent_t or null): events that the launch itself
+// stamps when the kernel starts and ends, i.e. the kernel's own duration.
+int launch_decode(const DecodeArgs& a, int kv_dtype, int n_workers, bool device_sched, void* stream,
+                  void* ev_start = nullptr, void* ev_stop = nullptr);
+int launch_combine(const CombineArgs& a, int n_records, bool device_sched, void* stream,
+                   void* ev_start = nullptr, void* ev_stop = nullptr);
 int launch_plan_device(const int32_t* seq_lens, int batch, int num_kv_heads, int n_workers,
                        int max_pages_per_seq, int32_t* plan, void* stream);
 

@@ -1,6 +1,6 @@
-// Measurement helpers (see hpc_probe.h): HBM streaming-read probe and a
-// plain 16-byte copy.  Grid-stride loops; every access is within
-// [0, bytes) of the caller's buffers.
+// Measurement helpers (declared in hpc_probe.h): HBM streaming-read probe
+// and a plain 16-byte copy.  Every access is within [0, bytes) of the
+// caller's buffers.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -12,13 +12,29 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+constexpr int kProbeUnroll = 8;   // 16-byte loads in flight per thread
+
+// Workgroup g streams the contiguous chunk [g * per, (g + 1) * per) of 16-byte
+// words (per a multiple of 256 * kProbeUnroll, so every unrolled load stays
+// inside the chunk), with nontemporal loads, 4 KiB per wave in flight; the
+// words past grid * per are read grid-stride.  Contiguous per-workgroup
+// chunks with deep unrolling read faster than a plain grid-stride loop.
 __global__ __launch_bounds__(256) void read_probe_kernel(const u32x4* __restrict__ buf, int64_t n16,
                                                          float* __restrict__ sink) {
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+    constexpr int64_t step = 256 * kProbeUnroll;
+    const int64_t per = n16 / gridDim.x / step * step;
+    const int64_t beg = per * blockIdx.x;
     uint32_t x = 0;
-#pragma unroll 8
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n16; i += stride) {
-        const u32x4 a = __builtin_nontemporal_load(buf + i);
+    for (int64_t i = beg + threadIdx.x; i < beg + per; i += step) {
+        u32x4 v[kProbeUnroll];
+#pragma unroll
+        for (int k = 0; k < kProbeUnroll; ++k) v[k] = __builtin_nontemporal_load(buf + i + k * 256);
+#pragma unroll
+        for (int k = 0; k < kProbeUnroll; ++k) x ^= v[k][0] ^ v[k][1] ^ v[k][2] ^ v[k][3];
+    }
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+    for (int64_t i = per * gridDim.x + static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n16; i += stride) {
+        const u32x4 a = buf[i];
         x ^= a[0] ^ a[1] ^ a[2] ^ a[3];
     }
     for (int off = 32; off >= 1; off >>= 1) x ^= __shfl_xor(x, off);
