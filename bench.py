@@ -76,6 +76,9 @@ def parse_args():
     ap.add_argument("--probe", action="store_true", help="also measure the HBM streaming-read ceiling")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run the plain copy kernel over MIB MiB (hardware-counter calibration) and exit")
+    ap.add_argument("--skew-sweep", action="store_true",
+                    help="instead of the bench line: time the balanced schedule against static split-KV "
+                         "schedules on batches from uniform 64x512 to 1x128K+31x4K, print one JSON line")
     ap.add_argument("--schedule", choices=["device", "host"], default="device",
                     help="device: kernels derive the per-step schedule from the lengths on the GPU; "
                          "host: C++ planner on the host + plan upload every step")
@@ -135,6 +138,9 @@ def main() -> int:
     props = torch.cuda.get_device_properties(dev)
     cus = props.multi_processor_count
     W = args.n_workers or cus
+    if args.skew_sweep:
+        print(json.dumps(skew_sweep(dev, W, cus, args.steps, args.warmup)), flush=True)
+        return 0
     wl = WORKLOADS[args.workload]
 
     log(f"building inputs for workload {args.workload} ({wl.name})")
@@ -267,6 +273,88 @@ def main() -> int:
         result["cpu_baseline"] = cpu_baseline(inp, alg_bytes)
     print(json.dumps(result), flush=True)
     return 0
+
+
+SKEW_BATCHES = (
+    ("64x512", [512] * 64),
+    ("32x4K", [4096] * 32),
+    ("1x8K+31x4K", [8192] + [4096] * 31),
+    ("1x16K+31x4K", [16384] + [4096] * 31),
+    ("1x32K+31x4K", [32768] + [4096] * 31),
+    ("1x64K+31x4K", [65536] + [4096] * 31),
+    ("1x128K+31x4K", [131072] + [4096] * 31),
+)
+STATIC_SPLITS = (1, 2, 4, 8, 16, 32, 64, 128)
+
+
+def skew_sweep(dev, W: int, cus: int, steps: int, warmup: int) -> dict:
+    """Balanced (device-scheduled) step against static split-KV plans with S
+    splits per sequence, on batches from uniform to one long sequence among
+    short ones (8 query heads over one KV head, bf16).  Times are the summed
+    decode + merge kernel durations per step (dispatch-stamped events), KV
+    rotated over >= 1 GiB of copies; ratio = static / balanced."""
+    import torch
+
+    import load_balanced_paged_step_amd as hd
+    from workloads import make_inputs
+
+    steps = min(steps, 50)
+    rows = []
+    for name, lens in SKEW_BATCHES:
+        inp = make_inputs(lens, 8, 1, "bf16", seed=4)
+        kv_bytes = inp.k_cache.numel() * inp.k_cache.element_size() * 2
+        copies = max(1, min(64, math.ceil((1 << 30) / kv_bytes)))
+        q, bt, sl = inp.q.to(dev), inp.block_table.to(dev), inp.seq_lens.to(dev)
+        ks = [inp.k_cache.to(dev) for _ in range(copies)]
+        vs = [inp.v_cache.to(dev) for _ in range(copies)]
+        out = torch.empty_like(q)
+        lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+        scales = dict(sm_scale=inp.sm_scale, k_scale=inp.k_scale, v_scale=inp.v_scale)
+
+        def kernel_us(one_step) -> float:
+            for i in range(warmup):
+                one_step(i)
+            torch.cuda.synchronize()
+            hd.hpc_decode_profile_start(steps)
+            for i in range(steps):
+                one_step(i)
+            torch.cuda.synchronize()
+            d_ms, c_ms, n = hd.hpc_decode_profile_stop()
+            return (d_ms + c_ms) / max(n, 1) * 1e3
+
+        ws = torch.zeros(hd.hpc_decode_step_workspace_size(inp.batch, 8, 1, W), dtype=torch.uint8, device=dev)
+        launchers = [hd.StepLauncher(q, ks[c], vs[c], bt, sl, out, lse, num_kv_heads=1, n_workers=W,
+                                     workspace=ws, **scales) for c in range(copies)]
+        balanced = kernel_us(lambda i: launchers[i % copies]())
+        lens_np = inp.seq_lens.numpy()
+        rule_S = hd.hpc_decode_static_splits(lens_np, 1, cus)
+        static = {}
+        for S in sorted(set(STATIC_SPLITS) | {rule_S}):
+            plan = hd.hpc_decode_plan_static(lens_np, 1, S)
+            plan_dev = torch.from_numpy(plan.copy()).to(dev)
+            nb = hd.hpc_decode_workspace_size(plan, 8, 1)
+            sws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev) if nb > 0 else None
+
+            def one(i, plan=plan, plan_dev=plan_dev, sws=sws):
+                hd.hpc_decode_attn(q, ks[i % copies], vs[i % copies], bt, sl, plan, plan_dev, sws, out, lse,
+                                   num_kv_heads=1, **scales)
+            static[S] = kernel_us(one)
+        best_S = min(static, key=static.get)
+        row = {"batch": name, "balanced_us": round(balanced, 2),
+               "static_us": {str(S): round(t, 2) for S, t in static.items()},
+               "rule_splits": rule_S, "ratio_rule": round(static[rule_S] / balanced, 3),
+               "best_splits": best_S, "ratio_best": round(static[best_S] / balanced, 3)}
+        log(f"skew sweep {name}: balanced {balanced:.1f} us; static S={rule_S} (rule) "
+            f"{static[rule_S]:.1f} us = {row['ratio_rule']}x; best static S={best_S} {static[best_S]:.1f} us "
+            f"= {row['ratio_best']}x")
+        rows.append(row)
+        del ks, vs, launchers
+        torch.cuda.empty_cache()
+    return {"metric": "static split-KV / balanced schedule kernel time, uniform -> skewed batches",
+            "unit": "ratio", "higher_is_better": True, "n_workers": W, "steps": steps, "warmup": warmup,
+            "heads": "8 q / 1 kv, head dim 128, bf16 KV, page 64",
+            "static_rule": "smallest power of two S with units x S >= CUs, S <= 128 and <= the longest unit's tiles",
+            "rows": rows}
 
 
 def _lens_summary(lens) -> str:

@@ -112,6 +112,36 @@ int64_t hpc_decode_plan_size(int32_t batch, int32_t num_kv_heads, int32_t n_work
 int hpc_decode_plan(const int32_t* seq_lens, int32_t batch, int32_t num_kv_heads,
                     int32_t n_workers, int32_t* plan, int64_t plan_capacity);
 
+/*
+ * Static split-KV schedule in the same word layout, for comparison with the
+ * balanced one (the pages measure their scheduler against a static split-KV
+ * schedule, §Attention Decode under Mixed-Length Batches, without defining
+ * it; this is the common form).  Pure host code; no HIP call.
+ *
+ * Every unit with n_u >= 1 tiles is cut into shares of c_u = ceil(n_u /
+ * splits) tiles, [k c_u, min((k + 1) c_u, n_u)); every non-empty share is
+ * one worker holding one entry, in (unit, share) order, so W = number of
+ * shares (at least 1: an all-empty batch keeps one idle worker).  Slots and
+ * merge records follow the same rule as hpc_decode_plan.  The plan runs
+ * through hpc_decode_attn like any other.
+ * hpc_decode_plan_static_size: a word bound for (batch, num_kv_heads,
+ * splits), or a negative status for batch < 0, H_kv < 1 or splits < 1.
+ * Errors of hpc_decode_plan_static as for hpc_decode_plan (splits < 1 ->
+ * HPC_ERR_INVALID).
+ */
+int64_t hpc_decode_plan_static_size(int32_t batch, int32_t num_kv_heads, int32_t splits);
+int hpc_decode_plan_static(const int32_t* seq_lens, int32_t batch, int32_t num_kv_heads,
+                           int32_t splits, int32_t* plan, int64_t plan_capacity);
+
+/* Split count of the static split-KV baseline for a batch: the smallest
+ * power of two S with batch * num_kv_heads * S >= n_cus (one share per
+ * compute unit at least), capped at max_splits and at the largest unit's
+ * tile count (the pages leave the static heuristic open; this is the rule
+ * used here).  Negative status for NULL lengths, batch < 0, H_kv < 1,
+ * n_cus < 1, max_splits < 1 or a negative length. */
+int32_t hpc_decode_static_splits(const int32_t* seq_lens, int32_t batch, int32_t num_kv_heads, int32_t n_cus,
+                                 int32_t max_splits);
+
 /* Words actually used by a plan written by hpc_decode_plan (from its header),
  * or a negative status for a NULL pointer or a malformed header. */
 int64_t hpc_decode_plan_words(const int32_t* plan);

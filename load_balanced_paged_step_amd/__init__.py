@@ -24,7 +24,9 @@ from ._lib import (HPC_OK, HPC_ERR_NULL, HPC_ERR_INVALID, HPC_ERR_UNSUPPORTED, H
                    MAX_GROUP, PLAN_HEADER_WORDS, HpcDecodeError, hpc_decode_params, lib)
 
 __all__ = [
-    "hpc_decode_plan_size", "hpc_decode_plan", "hpc_decode_plan_words", "hpc_decode_workspace_size",
+    "hpc_decode_plan_size", "hpc_decode_plan", "hpc_decode_plan_static_size", "hpc_decode_plan_static",
+    "hpc_decode_static_splits",
+    "hpc_decode_plan_words", "hpc_decode_workspace_size",
     "hpc_decode_check", "hpc_decode_attn", "hpc_status_string", "hpc_decode_profile_start",
     "hpc_decode_profile_stop", "hpc_probe_read", "hpc_probe_copy", "hpc_decode_step",
     "hpc_decode_step_check", "hpc_decode_step_workspace_size", "hpc_decode_plan_device", "StepLauncher",
@@ -111,6 +113,29 @@ def hpc_decode_plan(seq_lens, num_kv_heads: int, n_workers: int, out=None) -> np
     _lib.check(lib().hpc_decode_plan(_i32p(lens), lens.shape[0], num_kv_heads, n_workers, _i32p(buf),
                                      buf.shape[0]), "hpc_decode_plan")
     return buf[:hpc_decode_plan_words(buf)]
+
+
+def hpc_decode_plan_static_size(batch: int, num_kv_heads: int, splits: int) -> int:
+    return _lib.check(lib().hpc_decode_plan_static_size(batch, num_kv_heads, splits),
+                      "hpc_decode_plan_static_size")
+
+
+def hpc_decode_plan_static(seq_lens, num_kv_heads: int, splits: int) -> np.ndarray:
+    """Static split-KV schedule (every unit cut into ``splits`` equal shares of
+    its own tiles, one worker per share), in the plan word layout."""
+    lens = _host_i32(seq_lens).reshape(-1)
+    cap = hpc_decode_plan_static_size(lens.shape[0], num_kv_heads, splits)
+    buf = np.empty(cap, dtype=np.int32)
+    _lib.check(lib().hpc_decode_plan_static(_i32p(lens), lens.shape[0], num_kv_heads, splits, _i32p(buf),
+                                            buf.shape[0]), "hpc_decode_plan_static")
+    return buf[:hpc_decode_plan_words(buf)]
+
+
+def hpc_decode_static_splits(seq_lens, num_kv_heads: int, n_cus: int, max_splits: int = 128) -> int:
+    """Split count the static split-KV baseline uses for this batch."""
+    lens = _host_i32(seq_lens).reshape(-1)
+    return _lib.check(lib().hpc_decode_static_splits(_i32p(lens), lens.shape[0], num_kv_heads, n_cus, max_splits),
+                      "hpc_decode_static_splits")
 
 
 def hpc_decode_plan_words(plan) -> int:

@@ -54,6 +54,11 @@ SIGNATURES = {
     "hpc_decode_plan_size": (ctypes.c_int64, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]),
     "hpc_decode_plan": (ctypes.c_int, [_I32P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _I32P,
                                        ctypes.c_int64]),
+    "hpc_decode_plan_static_size": (ctypes.c_int64, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]),
+    "hpc_decode_plan_static": (ctypes.c_int, [_I32P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _I32P,
+                                              ctypes.c_int64]),
+    "hpc_decode_static_splits": (ctypes.c_int32, [_I32P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                  ctypes.c_int32]),
     "hpc_decode_plan_words": (ctypes.c_int64, [_I32P]),
     "hpc_decode_workspace_size": (ctypes.c_int64, [_I32P, ctypes.c_int32, ctypes.c_int32]),
     "hpc_decode_check": (ctypes.c_int, [_PP, _VP, _VP, _VP, _VP, _VP, _I32P, _VP, _VP, ctypes.c_int64,

@@ -120,6 +120,100 @@ extern "C" int hpc_decode_plan(const int32_t* seq_lens, int32_t batch, int32_t n
     return HPC_OK;
 }
 
+// Static split-KV baseline in the same word layout (the schedule the balanced
+// scheduler is measured against in §Attention Decode under Mixed-Length
+// Batches).  Every unit is cut into `splits` equal shares of its own tiles;
+// each non-empty share is one worker with one entry.
+extern "C" int64_t hpc_decode_plan_static_size(int32_t batch, int32_t num_kv_heads, int32_t splits) {
+    if (batch < 0 || num_kv_heads < 1 || splits < 1) return HPC_ERR_INVALID;
+    const int64_t U = static_cast<int64_t>(batch) * num_kv_heads;
+    const int64_t W = U * splits > 1 ? U * splits : 1;
+    return HPC_PLAN_HEADER_WORDS + (W + 1) + 4 * W + 3 * U;
+}
+
+extern "C" int hpc_decode_plan_static(const int32_t* seq_lens, int32_t batch, int32_t num_kv_heads,
+                                      int32_t splits, int32_t* plan, int64_t plan_capacity) {
+    if (plan == nullptr || (batch > 0 && seq_lens == nullptr)) return HPC_ERR_NULL;
+    if (batch < 0 || num_kv_heads < 1 || splits < 1) return HPC_ERR_INVALID;
+    const int64_t H = num_kv_heads;
+    const int64_t U = static_cast<int64_t>(batch) * H;
+
+    std::vector<Entry> entries;
+    std::vector<int32_t> parts(static_cast<std::size_t>(U), 0);
+    int64_t T = 0;
+    for (int64_t b = 0; b < batch; ++b) {
+        const int32_t L = seq_lens[b];
+        if (L < 0) return HPC_ERR_INVALID;
+        const int64_t n = (static_cast<int64_t>(L) + kPage - 1) / kPage;
+        T += n * H;
+        if (n == 0) continue;
+        const int64_t chunk = (n + splits - 1) / splits;
+        const int32_t k_count = static_cast<int32_t>((n + chunk - 1) / chunk);
+        for (int64_t h = 0; h < H; ++h) {
+            const int64_t u = b * H + h;
+            parts[u] = k_count;
+            for (int64_t t0 = 0; t0 < n; t0 += chunk)
+                entries.push_back({static_cast<int32_t>(u), static_cast<int32_t>(t0),
+                                   static_cast<int32_t>(t0 + chunk < n ? t0 + chunk : n), -1});
+        }
+    }
+    if (T > INT32_MAX - 1) return HPC_ERR_INVALID;
+
+    const int64_t E = static_cast<int64_t>(entries.size());
+    const int64_t W = E > 0 ? E : 1;
+    if (W > INT32_MAX - 1) return HPC_ERR_INVALID;
+    std::vector<int32_t> first_slot(static_cast<std::size_t>(U), 0);
+    int64_t n_partials = 0, n_combine = 0;
+    for (int64_t u = 0; u < U; ++u) {
+        if (parts[u] >= 2) {
+            first_slot[u] = static_cast<int32_t>(n_partials);
+            n_partials += parts[u];
+        }
+        if (parts[u] != 1) ++n_combine;
+    }
+    std::vector<int32_t> next_slot(first_slot);
+    for (Entry& e : entries) e.slot = parts[e.unit] >= 2 ? next_slot[e.unit]++ : -1;
+
+    const int64_t words = HPC_PLAN_HEADER_WORDS + (W + 1) + 4 * E + 3 * n_combine;
+    if (plan_capacity < words) return HPC_ERR_TOO_SMALL;
+    int32_t* p = plan;
+    const int32_t header[HPC_PLAN_HEADER_WORDS] = {
+        HPC_PLAN_VERSION, batch, num_kv_heads, static_cast<int32_t>(W), static_cast<int32_t>(T),
+        static_cast<int32_t>(E), static_cast<int32_t>(n_partials), static_cast<int32_t>(n_combine),
+        HPC_DECODE_PAGE, 0, 0, 0, 0, 0, 0, 0};
+    for (int i = 0; i < HPC_PLAN_HEADER_WORDS; ++i) *p++ = header[i];
+    for (int64_t w = 0; w <= W; ++w) *p++ = static_cast<int32_t>(w < E ? w : E);
+    for (const Entry& e : entries) {
+        *p++ = e.unit;
+        *p++ = e.t0;
+        *p++ = e.t1;
+        *p++ = e.slot;
+    }
+    for (int64_t u = 0; u < U; ++u) {
+        if (parts[u] == 1) continue;
+        *p++ = static_cast<int32_t>(u);
+        *p++ = parts[u];
+        *p++ = parts[u] >= 2 ? first_slot[u] : 0;
+    }
+    return HPC_OK;
+}
+
+extern "C" int32_t hpc_decode_static_splits(const int32_t* seq_lens, int32_t batch, int32_t num_kv_heads,
+                                            int32_t n_cus, int32_t max_splits) {
+    if (batch > 0 && seq_lens == nullptr) return HPC_ERR_NULL;
+    if (batch < 0 || num_kv_heads < 1 || n_cus < 1 || max_splits < 1) return HPC_ERR_INVALID;
+    int64_t n_max = 1;
+    for (int32_t b = 0; b < batch; ++b) {
+        if (seq_lens[b] < 0) return HPC_ERR_INVALID;
+        const int64_t n = (static_cast<int64_t>(seq_lens[b]) + kPage - 1) / kPage;
+        if (n > n_max) n_max = n;
+    }
+    const int64_t U = static_cast<int64_t>(batch) * num_kv_heads;
+    int64_t S = 1;
+    while (U * S < n_cus && 2 * S <= max_splits && 2 * S <= n_max) S *= 2;
+    return static_cast<int32_t>(S);
+}
+
 extern "C" int64_t hpc_decode_plan_words(const int32_t* plan) {
     if (plan == nullptr) return HPC_ERR_NULL;
     if (plan[0] != HPC_PLAN_VERSION || plan[8] != HPC_DECODE_PAGE) return HPC_ERR_PLAN_MISMATCH;

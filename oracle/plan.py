@@ -122,3 +122,83 @@ def parse_plan(words) -> dict:
         "n_combine": C, "tile": int(hdr[8]), "worker_ptr": worker_ptr, "entries": entries,
         "combine": combine, "n_words": o,
     }
+
+
+# ---------------------------------------------------------------------------
+# Static split-KV baseline (the schedule the pages compare against).
+#
+# The HPC-Ops blog (§Attention Backend: Dynamic Load-Balanced Scheduling and
+# §Attention Decode under Mixed-Length Batches) measures the balanced
+# scheduler against a static split-KV schedule without defining it.  The
+# reading used here is the common one: every unit is cut into the same number
+# S of splits, each split taking an equal share of that unit's own tiles, and
+# every non-empty split is launched as its own worker.  A batch with one long
+# sequence therefore gets splits of very different sizes.
+#
+#   c_u = ceil(n_u / S) tiles per split of unit u (n_u >= 1);
+#   split k of u covers tiles [k c_u, min((k + 1) c_u, n_u)), for k with k c_u < n_u;
+#   workers are the non-empty splits in (u, k) order, one entry each;
+#   slots and the merge list follow the same rule as the balanced plan.
+#
+# The words use the balanced plan's layout; W (header word 3) is the number of
+# non-empty splits, at least 1 (an all-empty batch keeps one idle worker).
+
+def static_split_count(seq_lens, num_kv_heads: int, n_cus: int, max_splits: int = 128) -> int:
+    """The split count a static split-KV launch picks here: the smallest power
+    of two S with U * S >= n_cus (enough splits to give every compute unit one),
+    at most max_splits and at most the largest unit's tile count."""
+    lens = [int(x) for x in seq_lens]
+    U = len(lens) * int(num_kv_heads)
+    n_max = max([(L + PAGE - 1) // PAGE for L in lens] + [1])
+    S = 1
+    while U * S < n_cus and 2 * S <= max_splits and 2 * S <= n_max:
+        S *= 2
+    return S
+
+
+def build_static_plan(seq_lens, num_kv_heads: int, splits: int) -> np.ndarray:
+    lens = [int(x) for x in seq_lens]
+    B, H, S_req = len(lens), int(num_kv_heads), int(splits)
+    if S_req < 1 or H < 1 or any(L < 0 for L in lens):
+        raise ValueError("invalid plan arguments")
+    U = B * H
+    n = [(lens[u // H] + PAGE - 1) // PAGE for u in range(U)]
+    T = sum(n)
+
+    entries = []
+    for u in range(U):
+        if n[u] == 0:
+            continue
+        c = (n[u] + S_req - 1) // S_req
+        k = 0
+        while k * c < n[u]:
+            entries.append([u, k * c, min((k + 1) * c, n[u])])
+            k += 1
+    W = max(1, len(entries))
+    worker_ptr = list(range(len(entries) + 1)) + [len(entries)] * (W - len(entries))
+
+    S = [0] * U
+    for e in entries:
+        S[e[0]] += 1
+    base = [0] * U
+    running = 0
+    for u in range(U):
+        if S[u] >= 2:
+            base[u] = running
+            running += S[u]
+    seen = [0] * U
+    slots = []
+    for e in entries:
+        u = e[0]
+        slots.append(-1 if S[u] == 1 else base[u] + seen[u])
+        seen[u] += 1
+    combine = [[u, S[u], base[u]] for u in range(U) if S[u] != 1]
+
+    header = [PLAN_VERSION, B, H, W, T, len(entries), running, len(combine), PAGE]
+    header += [0] * (HEADER_WORDS - len(header))
+    words = list(header) + worker_ptr
+    for e, slot in zip(entries, slots):
+        words += [e[0], e[1], e[2], slot]
+    for c in combine:
+        words += c
+    return np.asarray(words, dtype=np.int32)

@@ -64,3 +64,21 @@ def compare(inp, got, ref, what=""):
     assert lse_err <= LSE_TOL[inp.kv_dtype], f"{what}: max|lse-ref| = {lse_err:.3e}"
     assert np.all(out[neg.nonzero()] == 0), f"{what}: empty sequences must give zeros"
     return {"max_err": max_err, "tol": tol, "lse_err": lse_err}
+
+
+def run_hip_plan(inp, plan_words, dev=None):
+    """One decode step through hpc_decode_attn with a given host plan (any
+    schedule in the plan word layout), uploaded once."""
+    if dev is None:
+        dev = to_device(inp)
+    plan_host = np.ascontiguousarray(plan_words, dtype=np.int32)
+    plan_dev = torch.from_numpy(plan_host).cuda()
+    ws_bytes = hd.hpc_decode_workspace_size(plan_host, inp.num_q_heads, inp.num_kv_heads)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda") if ws_bytes > 0 else None
+    out = torch.empty_like(dev["q"])
+    lse = torch.empty(dev["q"].shape[:2], dtype=torch.float32, device="cuda")
+    hd.hpc_decode_attn(dev["q"], dev["k"], dev["v"], dev["bt"], dev["sl"], plan_host, plan_dev, ws, out, lse,
+                       num_kv_heads=inp.num_kv_heads, sm_scale=inp.sm_scale, k_scale=inp.k_scale,
+                       v_scale=inp.v_scale)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)

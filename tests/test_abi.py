@@ -12,7 +12,7 @@ from hypothesis import given, settings, strategies as st
 
 import load_balanced_paged_step_amd as hd
 from load_balanced_paged_step_amd import _lib
-from oracle.plan import build_plan, plan_size_words
+from oracle.plan import build_plan, build_static_plan, plan_size_words, static_split_count
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -75,6 +75,47 @@ def test_cpp_plan_exhaustive_small():
        W=st.integers(1, 1500))
 def test_cpp_plan_random(lens, H, W):
     assert np.array_equal(_cpp_plan(lens, H, W), build_plan(lens, H, W))
+
+
+@pytest.mark.parametrize("lens,H,S", [
+    ([37, 64, 130, 200], 1, 2), ([0, 320], 2, 3), ([130], 1, 4), ([0, 0], 1, 8), ([1, 0, 128], 1, 1),
+    ([131072] + [4096] * 31, 1, 8), ([131072] + [4096] * 31, 1, 128), ([512] * 64, 1, 4), ([5000] * 3, 8, 7),
+])
+def test_cpp_static_plan_equals_oracle(lens, H, S):
+    got = hd.hpc_decode_plan_static(np.asarray(lens, dtype=np.int32), H, S)
+    assert np.array_equal(got, build_static_plan(lens, H, S))
+    assert hd.hpc_decode_plan_static_size(len(lens), H, S) >= got.shape[0]
+
+
+@settings(max_examples=200, deadline=None)
+@given(lens=st.lists(st.integers(0, 70000), min_size=0, max_size=40), H=st.integers(1, 8),
+       S=st.integers(1, 200))
+def test_cpp_static_plan_random(lens, H, S):
+    got = hd.hpc_decode_plan_static(np.asarray(lens, dtype=np.int32), H, S)
+    assert np.array_equal(got, build_static_plan(lens, H, S))
+
+
+@settings(max_examples=200, deadline=None)
+@given(lens=st.lists(st.integers(0, 300000), min_size=0, max_size=64), H=st.integers(1, 8),
+       cus=st.integers(1, 1024), cap=st.integers(1, 256))
+def test_cpp_static_splits_equal_oracle(lens, H, cus, cap):
+    assert hd.hpc_decode_static_splits(np.asarray(lens, dtype=np.int32), H, cus, cap) == \
+        static_split_count(lens, H, cus, cap)
+
+
+def test_static_plan_errors():
+    lib = hd.lib()
+    buf = np.zeros(64, dtype=np.int32)
+    lens = np.asarray([100, 200], dtype=np.int32)
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    assert lib.hpc_decode_plan_static(lens.ctypes.data_as(i32p), 2, 1, 0, buf.ctypes.data_as(i32p), 64) == _lib.HPC_ERR_INVALID
+    assert lib.hpc_decode_plan_static(lens.ctypes.data_as(i32p), 2, 0, 2, buf.ctypes.data_as(i32p), 64) == _lib.HPC_ERR_INVALID
+    assert lib.hpc_decode_plan_static(None, 2, 1, 2, buf.ctypes.data_as(i32p), 64) == _lib.HPC_ERR_NULL
+    assert lib.hpc_decode_plan_static(lens.ctypes.data_as(i32p), 2, 1, 2, buf.ctypes.data_as(i32p), 8) == _lib.HPC_ERR_TOO_SMALL
+    bad = np.asarray([100, -1], dtype=np.int32)
+    assert lib.hpc_decode_plan_static(bad.ctypes.data_as(i32p), 2, 1, 2, buf.ctypes.data_as(i32p), 64) == _lib.HPC_ERR_INVALID
+    assert lib.hpc_decode_plan_static_size(-1, 1, 1) == _lib.HPC_ERR_INVALID
+    assert lib.hpc_decode_plan_static_size(1, 1, 0) == _lib.HPC_ERR_INVALID
 
 
 def test_workspace_size():
