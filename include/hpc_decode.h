@@ -206,7 +206,7 @@ int hpc_decode_check(const hpc_decode_params* params, const void* q, const void*
  *
  * batch        sequences in q / block_table / seq_lens (1 .. 2048, and
  *              batch * H_kv <= 4096)
- * n_workers    persistent workgroups W (the plan's W)
+ * n_workers    persistent workgroups W (the plan's W), 1 .. 65536
  * seq_lens     device int32 [batch]; lengths are clamped to
  *              [0, max_pages_per_seq * 64] so no read leaves the block table
  * workspace    device, >= hpc_decode_step_workspace_size(batch, Hq, H_kv, W);

@@ -201,7 +201,7 @@ extern "C" int hpc_decode_step_check(const hpc_decode_params* p, int32_t batch, 
     if (!std::isfinite(p->sm_scale) || !std::isfinite(p->k_scale) || !std::isfinite(p->v_scale))
         return HPC_ERR_INVALID;
     if (batch < 1 || n_workers < 1) return HPC_ERR_INVALID;
-    if (batch > hpcd::kDeviceSchedMaxBatch ||
+    if (batch > hpcd::kDeviceSchedMaxBatch || n_workers > hpcd::kDeviceSchedMaxWorkers ||
         static_cast<int64_t>(batch) * p->num_kv_heads > hpcd::kDeviceSchedMaxUnits)
         return HPC_ERR_UNSUPPORTED;
     // every tile index the kernels form must fit in int32

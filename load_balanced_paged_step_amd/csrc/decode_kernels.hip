@@ -137,21 +137,28 @@ struct KvTile<HPC_KV_FP8_E4M3> {
     __device__ __forceinline__ u32x4 v_row(int i) const { return fp8x8_to_bf16x8(v[i][0], v[i][1]); }
 };
 
-// One slot of the prefetch ring.  Everything but the register arrays is
-// wave-uniform.
+// Where a tile comes from and where its entry's result goes; all wave-uniform
+// (scalar registers, packed to keep a deep ring within the SGPR budget).
+struct TileInfo {
+    int bits;     // valid token rows (0..64) | first << 7 | last << 8 | real << 9 | kv head << 10
+    int row;      // b * Hq + h * G: first query head row of the entry
+    int part;     // output target of the entry (see TileRef::part)
+    int page;     // physical page of the tile (its scalar load may still be in flight)
+    int rec_parts;  // device schedule: >= 0 when this entry writes its unit's merge record
+    int rec_slot;   // partial slot of this entry (for that record)
+    __device__ __forceinline__ int valid() const { return bits & 127; }
+    __device__ __forceinline__ bool first() const { return (bits >> 7) & 1; }
+    __device__ __forceinline__ bool last() const { return (bits >> 8) & 1; }
+    __device__ __forceinline__ bool real() const { return (bits >> 9) & 1; }
+    __device__ __forceinline__ int head() const { return bits >> 10; }
+};
+
+// One slot of the prefetch ring: a tile's K/V rows in flight or arrived.
 template <int KV>
 struct TileSlot {
     KvTile<KV> kv;
     u32x4 q[4];   // Q^T operand of the entry, loaded only for an entry's first tile
-    int real;     // holds a tile of this worker
-    int valid;    // valid token rows (0..64)
-    int first, last;
-    int row;      // b * Hq + h * G: first query head row of the entry
-    int part;     // output target of the entry (see TileRef::part)
-    int page;     // physical page of the tile
-    int head;     // kv head of the tile
-    int rec_parts;  // device schedule: >= 0 when this entry writes its unit's merge record
-    int rec_slot;   // partial slot of this entry (for that record)
+    TileInfo info;
 };
 
 // Host-planned tile source: walks this worker's entries in the plan words.
@@ -208,7 +215,7 @@ struct DecodeScalars {
     float qk_scale_log2, v_scale;
 };
 
-template <int KV, int PF, bool DEV>
+template <int KV, int PF, bool DEV, bool AHEAD>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     const __bf16* __restrict__ q, const char* __restrict__ kcache, const char* __restrict__ vcache,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
@@ -244,7 +251,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
         sched.B = a.batch;
         sched.H = Hkv;
         sched.W = gridDim.x;
-        sched.T = static_cast<int64_t>(Hkv) * s_dyn[2 * a.batch];
+        sched.set_tiles(static_cast<int64_t>(Hkv) * s_dyn[2 * a.batch]);
         w_begin = sched.range_begin(w);
         w_end = sched.range_begin(w + 1);
         if (w_begin < w_end) dwalk.init(sched, w, w_begin, w_end, true);
@@ -255,10 +262,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     }
 
     // Filling a ring slot: `plan_tile` takes the next tile of the worker and
-    // reads its page id; `load_tile` issues the K/V (and, for an entry's
-    // first tile, Q) loads.  The first PF slots are planned together so their
-    // page-id reads are in flight at once.
-    auto plan_tile = [&](TileSlot<KV>& s) {
+    // starts the scalar load of its page id; `load_tile` issues the K/V (and,
+    // for an entry's first tile, Q) loads.  With AHEAD, every slot's
+    // following tile is planned one full ring turn before it is loaded, so
+    // the page-id load never delays the K/V loads (this pays for fp8 tiles;
+    // bf16 tiles measured faster with the page-id load in between, which
+    // keeps fewer requests in flight).
+    auto plan_tile = [&](TileInfo& s) {
         TileRef r;
         bool ok;
         if constexpr (DEV) ok = dwalk.next(r);
@@ -279,43 +289,42 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
                 rslot = r.rec_first_slot;
             }
         }
-        s.real = uniform(ok ? 1 : 0);
-        s.valid = uniform(rem < 0 ? 0 : (rem > kPage ? kPage : rem));
+        const int valid = rem < 0 ? 0 : (rem > kPage ? kPage : rem);
+        s.bits = uniform(valid | (first ? 1 << 7 : 0) | (last ? 1 << 8 : 0) | (ok ? 1 << 9 : 0) | (h << 10));
         s.page = page;
-        s.head = uniform(h);
-        s.first = uniform(first);
-        s.last = uniform(last);
         s.row = uniform(row);
         s.part = uniform(part);
         s.rec_parts = uniform(rparts);
         s.rec_slot = uniform(rslot);
     };
-    auto load_tile = [&](TileSlot<KV>& s) {
-        int page = uniform(s.page);
+    auto load_tile = [&](TileSlot<KV>& s, const TileInfo& info) {
+        s.info = info;
+        int page = uniform(info.page);
         if (static_cast<unsigned>(page) >= static_cast<unsigned>(a.num_pages)) {
-            s.valid = 0;
+            s.info.bits &= ~127;
             page = 0;
         }
-        const uint64_t off = (static_cast<uint64_t>(page) * Hkv + s.head) * kBlock;
-        const uint32_t kv_bytes = static_cast<uint32_t>(s.valid) * kRow;
+        const uint64_t off = (static_cast<uint64_t>(page) * Hkv + info.head()) * kBlock;
+        const uint32_t kv_bytes = static_cast<uint32_t>(s.info.valid()) * kRow;
         s.kv.load(make_rsrc(kcache + off, kv_bytes), make_rsrc(vcache + off, kv_bytes), wave, n, g);
         // Q^T operand of a new entry: head n, dims 32kk + 8g .. +8; heads >= G read as zero
         const __amdgpu_buffer_rsrc_t rq =
-            make_rsrc(q + static_cast<int64_t>(s.row) * kHeadDim, s.first ? G * kHeadDim * 2 : 0);
+            make_rsrc(q + static_cast<int64_t>(info.row) * kHeadDim, info.first() ? G * kHeadDim * 2 : 0);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
             s.q[kk] = __builtin_amdgcn_raw_buffer_load_b128(rq, n * kHeadDim * 2 + 64 * kk + 16 * g, 0, 0);
     };
-    auto issue = [&](TileSlot<KV>& s) {
-        plan_tile(s);
-        load_tile(s);
-    };
 
     TileSlot<KV> ring[PF];
+    TileInfo ahead[PF];   // the tile each slot loads next
 #pragma unroll
-    for (int j = 0; j < PF; ++j) plan_tile(ring[j]);
+    for (int j = 0; j < PF; ++j) plan_tile(ahead[j]);
 #pragma unroll
-    for (int j = 0; j < PF; ++j) load_tile(ring[j]);
+    for (int j = 0; j < PF; ++j) load_tile(ring[j], ahead[j]);
+    if constexpr (AHEAD) {
+#pragma unroll
+        for (int j = 0; j < PF; ++j) plan_tile(ahead[j]);
+    }
 
     // Device schedule, while the first tiles are in flight: empty sequences
     // get out = 0, lse = -inf and a merge record saying so, from worker
@@ -343,7 +352,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     for (int nb = 0; nb < 8; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     bf16x8 qop[4];
 
-    auto flush = [&](const TileSlot<KV>& ts) {
+    auto flush = [&](const TileInfo& ts) {
         const int row = ts.row;
         const int part = ts.part;
         l += __shfl_xor(l, 16);
@@ -414,7 +423,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     };
 
     auto consume = [&](const TileSlot<KV>& s) {
-        if (s.first) {
+        if (s.info.first()) {
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) qop[kk] = bitcast<bf16x8>(s.q[kk]);
         }
@@ -426,7 +435,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
         float mt = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            sc[i] = (r0 + i < s.valid) ? sc[i] * a.qk_scale_log2 : -INFINITY;
+            sc[i] = (r0 + i < s.info.valid()) ? sc[i] * a.qk_scale_log2 : -INFINITY;
             mt = fmaxf(mt, sc[i]);
         }
         mt = fmaxf(mt, __shfl_xor(mt, 16));
@@ -457,7 +466,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
             acc[nb] = acc[nb] * alpha;
             acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(bitcast<bf16x4>(vt), pop, acc[nb], 0, 0, 0);
         }
-        if (s.last) flush(s);
+        if (s.info.last()) flush(s.info);
     };
 
     // Leaving the loop the moment a slot is empty keeps every path that
@@ -466,9 +475,15 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     for (;;) {
 #pragma unroll
         for (int j = 0; j < PF; ++j) {
-            if (!ring[j].real) goto done;
+            if (!ring[j].info.real()) goto done;
             consume(ring[j]);
-            issue(ring[j]);
+            if constexpr (AHEAD) {
+                load_tile(ring[j], ahead[j]);
+                plan_tile(ahead[j]);
+            } else {
+                plan_tile(ahead[j]);
+                load_tile(ring[j], ahead[j]);
+            }
         }
     }
 done:
@@ -521,7 +536,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
         if (k == 0) return first_slot;
         // later workers start inside the unit, so it is their first entry (slot 2w)
         if (static_cast<int64_t>(W) <= T) return 2 * (w_first + k);
-        return 2 * static_cast<int>(div_floor((Pu + k + 1) * W - 1, T));   // one tile per worker
+        return 2 * small_quot((Pu + k + 1) * W - 1, T);   // one tile per worker
     };
     const int b = u / Hkv;
     const int h = u - b * Hkv;
@@ -618,7 +633,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_device_kernel(const int32_t
     sched.B = B;
     sched.H = H;
     sched.W = W;
-    sched.T = static_cast<int64_t>(H) * s_pb[B];
+    sched.set_tiles(static_cast<int64_t>(H) * s_pb[B]);
     const int t = threadIdx.x;
 
     for (int w = t; w < W; w += kPlanThreads) {
@@ -700,9 +715,10 @@ constexpr int kPrefetchFp8 = HPC_DECODE_PREFETCH_FP8;
 
 template <int KV, int PF, bool DEV>
 void launch_decode_t(const DecodeArgs& a, int n_workers, size_t lds, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+    constexpr bool kAhead = KV == HPC_KV_FP8_E4M3;
     const DecodeScalars sc{a.batch,        a.num_kv_heads,  a.group,  a.max_pages_per_seq, a.num_pages,
                            a.max_partials, a.qk_scale_log2, a.v_scale};
-    hipExtLaunchKernelGGL((decode_kernel<KV, PF, DEV>), dim3(n_workers), dim3(kDecodeThreads),
+    hipExtLaunchKernelGGL((decode_kernel<KV, PF, DEV, kAhead>), dim3(n_workers), dim3(kDecodeThreads),
                           static_cast<std::uint32_t>(lds), s, e0, e1, 0u,
                           static_cast<const __bf16*>(a.q), static_cast<const char*>(a.k),
                           static_cast<const char*>(a.v), a.block_table, a.seq_lens, a.worker_ptr, a.entries,

@@ -25,13 +25,15 @@ namespace hpcd {
 
 __device__ __forceinline__ int tiles_of(int L) { return (L + 63) >> 6; }
 
-// floor(x / y) for 0 <= x < 2^62, 1 <= y < 2^31: a double-precision quotient
-// (off by at most one here) corrected with exact integer products; far
-// cheaper than the generic 64-bit integer division.
-__device__ __forceinline__ int64_t div_floor(int64_t x, int64_t y) {
-    int64_t q = static_cast<int64_t>(static_cast<double>(x) / static_cast<double>(y));
-    if (q * y > x) --q;
-    else if ((q + 1) * y <= x) ++q;
+// floor(x / y) for 0 <= x < 2^62, 1 <= y < 2^31 when the quotient is below
+// 2^20: a single-precision estimate (conversions, reciprocal and product
+// leave a relative error below 2^-21, so the estimate is off by at most one)
+// corrected with exact integer products.  Much shorter than a 64-bit integer
+// or double division.
+__device__ __forceinline__ int small_quot(int64_t x, int64_t y) {
+    int q = static_cast<int>(static_cast<float>(x) * __builtin_amdgcn_rcpf(static_cast<float>(y)));
+    if (static_cast<int64_t>(q) * y > x) --q;
+    else if (static_cast<int64_t>(q + 1) * y <= x) ++q;
     return q;
 }
 
@@ -77,16 +79,27 @@ __device__ void build_prefix(const int32_t* __restrict__ seq_lens, int B, int ma
 struct Sched {
     const int32_t* len;   // LDS [B]
     const int32_t* pb;    // LDS [B + 1]
-    int B, H, W;
-    int64_t T;
+    int B, H, W;          // W <= 65536
+    int64_t T;            // < 2^31
+    int64_t qT, rT;       // T = qT W + rT
+
+    __device__ __forceinline__ void set_tiles(int64_t tiles) {
+        T = tiles;
+        const uint32_t t32 = static_cast<uint32_t>(tiles);
+        qT = t32 / static_cast<uint32_t>(W);
+        rT = tiles - qT * W;
+    }
 
     __device__ __forceinline__ int tiles(int b) const { return tiles_of(len[b]); }
     __device__ __forceinline__ int64_t unit_start(int b, int h) const {
         return static_cast<int64_t>(H) * pb[b] + static_cast<int64_t>(h) * tiles(b);
     }
-    __device__ __forceinline__ int64_t range_begin(int w) const { return div_floor(static_cast<int64_t>(w) * T, W); }
-    __device__ __forceinline__ int owner(int64_t j) const {    // valid for W <= T
-        return static_cast<int>(div_floor((j + 1) * W - 1, T));
+    // floor(w T / W) = w qT + floor(w rT / W), with w rT < W^2
+    __device__ __forceinline__ int64_t range_begin(int w) const {
+        return static_cast<int64_t>(w) * qT + small_quot(static_cast<int64_t>(w) * rT, W);
+    }
+    __device__ __forceinline__ int owner(int64_t j) const {    // valid for W <= T (quotient < W)
+        return small_quot((j + 1) * W - 1, T);
     }
     // number of workers that share unit (b, h)
     __device__ __forceinline__ int parts(int b, int h) const {

@@ -17,6 +17,7 @@ constexpr int kPlanThreads = 1024;
 // the per-unit split tables live in LDS of every workgroup.
 constexpr int kDeviceSchedMaxBatch = 2048;
 constexpr int kDeviceSchedMaxUnits = 4096;
+constexpr int kDeviceSchedMaxWorkers = 65536;   // keeps every schedule quotient below 2^20
 // Limits of the plan-materialising kernel (one workgroup, everything in LDS).
 constexpr int kPlanDeviceMaxBatch = 2048;
 constexpr int kPlanDeviceMaxWorkers = 2048;

@@ -248,6 +248,7 @@ def test_step_check_errors():
     assert chk(wsb=need - 1) == hd.HPC_ERR_TOO_SMALL
     assert chk(batch=0) == hd.HPC_ERR_INVALID and chk(W=0) == hd.HPC_ERR_INVALID
     assert chk(batch=5000, wsb=1 << 40) == hd.HPC_ERR_UNSUPPORTED
+    assert chk(W=65537, wsb=1 << 40) == hd.HPC_ERR_UNSUPPORTED
     params.max_pages_per_seq = 1 << 20
     assert chk(batch=2048, wsb=1 << 40) == hd.HPC_ERR_INVALID       # tile indices beyond int32
     params.max_pages_per_seq = 4

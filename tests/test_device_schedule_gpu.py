@@ -49,6 +49,18 @@ def test_device_plan_equals_oracle(lens, H, W):
     assert np.array_equal(_device_plan(lens, H, W), build_plan(lens, H, W))
 
 
+@pytest.mark.parametrize("lens,H,W", [
+    ([2 ** 28 - 1, 5, 2 ** 27 + 13, 0] * 4, 8, 2047),     # T near 2^29 tiles: large w T / W quotients
+    ([2 ** 28] * 16, 8, 2048),
+    ([64 * 2047 - 1, 1, 1, 1], 1, 2048),                     # W just above T
+    ([100] * 5, 3, 2048),                                    # W far above T: one tile per worker
+    ([64 * 4096 + 1] * 3, 2, 1999),
+])
+def test_device_plan_extreme_quotients(lens, H, W):
+    announce(f"device plan extreme B={len(lens)} H={H} W={W}")
+    assert np.array_equal(_device_plan(lens, H, W), build_plan(lens, H, W))
+
+
 def test_device_plan_random_batches():
     rng = np.random.default_rng(123)
     for i in range(60):
