@@ -213,7 +213,18 @@ struct DecodeScalars {
     int32_t batch, num_kv_heads, group, max_pages_per_seq, num_pages;
     int32_t max_partials;   // partial slots the workspace holds
     float qk_scale_log2, v_scale;
+    int32_t n_workers;      // the grid size (passed so no hidden argument is read)
 };
+
+// Passes kernel arguments through one empty scalar-register asm, so that
+// they are fetched together at the first use of any of them instead of one
+// dependent fetch each where they are first used.  The asm is not volatile
+// and touches no memory, so later loads stay known as unclobbered (and keep
+// going through the scalar unit).
+template <typename A, typename B, typename C, typename D>
+__device__ __forceinline__ void fetch_args(A& a, B& b, C& c, D& d) {
+    asm("" : "+s"(a), "+s"(b), "+s"(c), "+s"(d));
+}
 
 template <int KV, int PF, bool DEV, bool AHEAD>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
@@ -228,6 +239,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     __shared__ int32_t s_tmp[2 * kWaves];
     extern __shared__ int32_t s_dyn[];   // device schedule: len[B], tile prefix[B + 1]
 
+    fetch_args(seq_lens, a.batch, a.max_pages_per_seq, a.n_workers);
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int n = lane & 15;
@@ -250,7 +262,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
         sched.pb = s_dyn + a.batch;
         sched.B = a.batch;
         sched.H = Hkv;
-        sched.W = gridDim.x;
+        sched.W = a.n_workers;
         sched.set_tiles(static_cast<int64_t>(Hkv) * s_dyn[2 * a.batch]);
         w_begin = sched.range_begin(w);
         w_end = sched.range_begin(w + 1);
@@ -332,8 +344,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     // its first tile, so all records are rewritten every step).
     if constexpr (DEV) {
         const int U = a.batch * Hkv;
-        for (int u = w + static_cast<int>(gridDim.x) * threadIdx.x; u < U;
-             u += static_cast<int>(gridDim.x) * kDecodeThreads) {
+        for (int u = w + a.n_workers * static_cast<int>(threadIdx.x); u < U;
+             u += a.n_workers * kDecodeThreads) {
             const int b = u / Hkv;
             if (sched.len[b] != 0) continue;
             const int64_t row = static_cast<int64_t>(b) * Hq + (u - b * Hkv) * G;
@@ -490,28 +502,33 @@ done:
     return;
 }
 
-// Merge of split units: one workgroup per (merge
-// record, query head of the group), 1024 threads = 32 partial lanes x 32
-// dim quads.  Lane pl folds partials i = pl, pl + 32, ... into a running
-// (max, weighted sum, weight) triple, issuing up to eight partials' loads
-// before using any of them; the 32 triples then meet in LDS and are merged
-// once more by log-sum-exp.  The records are the host plan's merge list, or,
-// for the device-scheduled step, the list the decode kernel wrote (a count,
-// then one record per split unit in unit order; the grid covers the largest
-// possible count and surplus blocks exit).
-constexpr int kMergeLanes = kCombineThreads / 32;
+// Merge of split units: kMergeSplit workgroups per (merge record, query head
+// of the group), each merging 32 of the 128 dims, so that a unit shared by
+// many workers is read by several compute units at once.  256 threads = 32
+// partial lanes x 8 dim quads.  Lane pl folds partials i = pl, pl + 32, ...
+// into a running (max, weighted sum, weight) triple, issuing up to eight
+// partials' loads before using any of them; the 32 triples are then merged by
+// log-sum-exp, 8 per wave with lane shuffles and the 4 wave results in LDS.  The records are the host plan's
+// merge list, or, for the device-scheduled step, one record per unit written
+// by the decode kernel.
+constexpr int kMergeSplit = 4;                          // workgroups per (record, head)
+constexpr int kMergeQuads = kHeadDim / 4 / kMergeSplit;  // dim quads per workgroup (8)
+constexpr int kMergeLanes = kCombineThreads / kMergeQuads;
 constexpr int kMergeUnroll = 8;
 
 template <bool DEV>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a) {
-    __shared__ f32x4 s_acc[kMergeLanes][32];
-    __shared__ float s_m[kMergeLanes];
-    __shared__ float s_w[kMergeLanes];
+    __shared__ f32x4 s_acc[kCombineThreads / 64][kMergeQuads];
+    __shared__ float s_m[kCombineThreads / 64];
+    __shared__ float s_w[kCombineThreads / 64];
 
+    fetch_args(a.combine, a.o_part, a.lse_part, a.group);
     const int G = a.group;
     const int Hkv = a.num_kv_heads;
-    const int c = blockIdx.x / G;
-    const int n = blockIdx.x - c * G;
+    const int qd = blockIdx.x % kMergeSplit;
+    const int cn = blockIdx.x / kMergeSplit;
+    const int c = cn / G;
+    const int n = cn - c * G;
     int u, S, base = 0;
     int w_first = 0, first_slot = 0, W = a.n_workers;
     int64_t Pu = 0, T = 1;
@@ -542,19 +559,20 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
     const int h = u - b * Hkv;
     const int64_t row = static_cast<int64_t>(b) * (G * Hkv) + h * G + n;
     const int t = threadIdx.x;
-    const int dq = t & 31;
-    const int pl = t >> 5;
+    const int dq = t % kMergeQuads;
+    const int pl = t / kMergeQuads;
+    const int dim0 = 4 * (kMergeQuads * qd + dq);
     __bf16* out = static_cast<__bf16*>(a.out) + row * kHeadDim;
 
     if (S == 0) {   // empty sequence: out = 0, lse = -inf
-        if (pl == 0) *reinterpret_cast<u32x2*>(out + 4 * dq) = u32x2{0u, 0u};
-        if (t == 0) a.lse[row] = -INFINITY;
+        if (pl == 0) *reinterpret_cast<u32x2*>(out + dim0) = u32x2{0u, 0u};
+        if (t == 0 && qd == 0) a.lse[row] = -INFINITY;
         return;
     }
     if (static_cast<int64_t>(slot_of(0)) >= a.max_partials || static_cast<int64_t>(slot_of(S - 1)) >= a.max_partials ||
         (!DEV && static_cast<int64_t>(base) + S > a.max_partials)) {   // never for a consistent schedule: NaN
-        if (pl == 0) *reinterpret_cast<u32x2*>(out + 4 * dq) = u32x2{0x7fc07fc0u, 0x7fc07fc0u};
-        if (t == 0) a.lse[row] = __builtin_nanf("");
+        if (pl == 0) *reinterpret_cast<u32x2*>(out + dim0) = u32x2{0x7fc07fc0u, 0x7fc07fc0u};
+        if (t == 0 && qd == 0) a.lse[row] = __builtin_nanf("");
         return;
     }
 
@@ -569,7 +587,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
             const int i = i0 + k * kMergeLanes;
             const int64_t p = static_cast<int64_t>(slot_of(i < S ? i : 0)) * G + n;
             lv[k] = (i < S) ? a.lse_part[p] * kLog2e : -INFINITY;
-            o[k] = *reinterpret_cast<const f32x4*>(a.o_part + p * kHeadDim + 4 * dq);
+            o[k] = *reinterpret_cast<const f32x4*>(a.o_part + p * kHeadDim + dim0);
         }
         float mk = m;
 #pragma unroll
@@ -586,21 +604,41 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
         }
         m = mk;
     }
-    s_acc[pl][dq] = acc;
-    if (dq == 0) {
-        s_m[pl] = m;
-        s_w[pl] = w;
+    // fold the 8 partial lanes of each wave with shuffles (lanes differing in
+    // bits 3..5 hold the same dims), then the 4 waves through LDS
+#pragma unroll
+    for (int off = kMergeQuads; off < 64; off <<= 1) {
+        const float m2 = __shfl_xor(m, off);
+        const float w2 = __shfl_xor(w, off);
+        f32x4 a2;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a2[i] = __shfl_xor(acc[i], off);
+        const float M = fmaxf(m, m2);
+        const float M_use = (M == -INFINITY) ? 0.f : M;
+        const float f1 = __builtin_amdgcn_exp2f(m - M_use);
+        const float f2 = __builtin_amdgcn_exp2f(m2 - M_use);
+        acc = acc * f1 + a2 * f2;
+        w = w * f1 + w2 * f2;
+        m = M;
+    }
+    const int wave = t >> 6;
+    if ((t & 63) < kMergeQuads) {
+        s_acc[wave][dq] = acc;
+        if (dq == 0) {
+            s_m[wave] = m;
+            s_w[wave] = w;
+        }
     }
     __syncthreads();
-    if (pl == 0) {
+    if (t < kMergeQuads) {
         float M = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < kMergeLanes; ++j) M = fmaxf(M, s_m[j]);
+        for (int j = 0; j < kCombineThreads / 64; ++j) M = fmaxf(M, s_m[j]);
         const float M_use = (M == -INFINITY) ? 0.f : M;
         f32x4 r = f32x4{0.f, 0.f, 0.f, 0.f};
         float ws = 0.f;
-#pragma unroll 8
-        for (int j = 0; j < kMergeLanes; ++j) {
+#pragma unroll
+        for (int j = 0; j < kCombineThreads / 64; ++j) {
             const float e = __builtin_amdgcn_exp2f(s_m[j] - M_use);
             r += e * s_acc[j][dq];
             ws += e * s_w[j];
@@ -608,8 +646,8 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
         const float inv = ws > 0.f ? 1.f / ws : 0.f;
         const bf16x4 ov = bf16x4{static_cast<__bf16>(r[0] * inv), static_cast<__bf16>(r[1] * inv),
                                  static_cast<__bf16>(r[2] * inv), static_cast<__bf16>(r[3] * inv)};
-        *reinterpret_cast<bf16x4*>(out + 4 * dq) = ov;
-        if (dq == 0) a.lse[row] = ws > 0.f ? (M + __log2f(ws)) * kLn2 : -INFINITY;
+        *reinterpret_cast<bf16x4*>(out + dim0) = ov;
+        if (dq == 0 && qd == 0) a.lse[row] = ws > 0.f ? (M + __log2f(ws)) * kLn2 : -INFINITY;
     }
 }
 
@@ -716,8 +754,8 @@ constexpr int kPrefetchFp8 = HPC_DECODE_PREFETCH_FP8;
 template <int KV, int PF, bool DEV>
 void launch_decode_t(const DecodeArgs& a, int n_workers, size_t lds, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     constexpr bool kAhead = KV == HPC_KV_FP8_E4M3;
-    const DecodeScalars sc{a.batch,        a.num_kv_heads,  a.group,  a.max_pages_per_seq, a.num_pages,
-                           a.max_partials, a.qk_scale_log2, a.v_scale};
+    const DecodeScalars sc{a.batch,        a.num_kv_heads,  a.group,   a.max_pages_per_seq, a.num_pages,
+                           a.max_partials, a.qk_scale_log2, a.v_scale, n_workers};
     hipExtLaunchKernelGGL((decode_kernel<KV, PF, DEV, kAhead>), dim3(n_workers), dim3(kDecodeThreads),
                           static_cast<std::uint32_t>(lds), s, e0, e1, 0u,
                           static_cast<const __bf16*>(a.q), static_cast<const char*>(a.k),
@@ -747,10 +785,10 @@ int launch_combine(const CombineArgs& a, int n_records, bool device_sched, void*
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipEvent_t e0 = static_cast<hipEvent_t>(ev_start), e1 = static_cast<hipEvent_t>(ev_stop);
     if (device_sched)
-        hipExtLaunchKernelGGL(combine_kernel<true>, dim3(n_records * a.group), dim3(kCombineThreads), 0u, s, e0, e1,
+        hipExtLaunchKernelGGL(combine_kernel<true>, dim3(n_records * a.group * kMergeSplit), dim3(kCombineThreads), 0u, s, e0, e1,
                               0u, a);
     else
-        hipExtLaunchKernelGGL(combine_kernel<false>, dim3(n_records * a.group), dim3(kCombineThreads), 0u, s, e0,
+        hipExtLaunchKernelGGL(combine_kernel<false>, dim3(n_records * a.group * kMergeSplit), dim3(kCombineThreads), 0u, s, e0,
                               e1, 0u, a);
     return static_cast<int>(hipGetLastError());
 }

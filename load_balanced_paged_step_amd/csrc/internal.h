@@ -10,7 +10,7 @@ constexpr int kHeadDim = 128;
 constexpr int kPage = 64;
 constexpr int kWaves = 4;                 // waves per decode workgroup
 constexpr int kDecodeThreads = 64 * kWaves;
-constexpr int kCombineThreads = 1024;
+constexpr int kCombineThreads = 256;
 constexpr int kPlanThreads = 1024;
 
 // Limits of the device-scheduled path: the lengths, their tile prefix and
