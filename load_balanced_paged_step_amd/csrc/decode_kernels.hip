@@ -144,8 +144,6 @@ struct TileInfo {
     int row;      // b * Hq + h * G: first query head row of the entry
     int part;     // output target of the entry (see TileRef::part)
     int page;     // physical page of the tile (its scalar load may still be in flight)
-    int rec_parts;  // device schedule: >= 0 when this entry writes its unit's merge record
-    int rec_slot;   // partial slot of this entry (for that record)
     __device__ __forceinline__ int valid() const { return bits & 127; }
     __device__ __forceinline__ bool first() const { return (bits >> 7) & 1; }
     __device__ __forceinline__ bool last() const { return (bits >> 8) & 1; }
@@ -277,15 +275,14 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     // starts the scalar load of its page id; `load_tile` issues the K/V (and,
     // for an entry's first tile, Q) loads.  With AHEAD, every slot's
     // following tile is planned one full ring turn before it is loaded, so
-    // the page-id load never delays the K/V loads (this pays for fp8 tiles;
-    // bf16 tiles measured faster with the page-id load in between, which
-    // keeps fewer requests in flight).
+    // the page-id load never delays the K/V loads (measured no faster:
+    // off by default).
     auto plan_tile = [&](TileInfo& s) {
         TileRef r;
         bool ok;
         if constexpr (DEV) ok = dwalk.next(r);
         else ok = hwalk.next(r);
-        int page = 0, h = 0, row = 0, part = -1, first = 0, last = 0, rem = 0, rparts = -1, rslot = -1;
+        int page = 0, h = 0, row = 0, part = -1, first = 0, last = 0, rem = 0;
         if (ok) {
             const int b = uniform(r.b);
             const int t = uniform(r.t);
@@ -296,18 +293,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
             first = r.first;
             last = r.last;
             part = r.part;
-            if constexpr (DEV) {
-                rparts = r.rec_parts;
-                rslot = r.rec_first_slot;
-            }
         }
         const int valid = rem < 0 ? 0 : (rem > kPage ? kPage : rem);
         s.bits = uniform(valid | (first ? 1 << 7 : 0) | (last ? 1 << 8 : 0) | (ok ? 1 << 9 : 0) | (h << 10));
         s.page = page;
         s.row = uniform(row);
         s.part = uniform(part);
-        s.rec_parts = uniform(rparts);
-        s.rec_slot = uniform(rslot);
     };
     auto load_tile = [&](TileSlot<KV>& s, const TileInfo& info) {
         s.info = info;
@@ -416,15 +407,19 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
             }
         }
         if constexpr (DEV) {
-            if (ts.rec_parts >= 0 && threadIdx.x == 0) {   // this worker holds the unit's first tile
+            if (threadIdx.x == 0) {
                 const int u = row / G;
                 const int bu = u / Hkv;
-                int32_t* rec = merge_records + kRecordWords * u;
-                rec[0] = ts.rec_parts;
-                rec[1] = w;
-                rec[2] = ts.rec_slot;
-                rec[3] = static_cast<int32_t>(sched.unit_start(bu, u - bu * Hkv));
-                rec[4] = static_cast<int32_t>(sched.T);
+                const int hu = u - bu * Hkv;
+                const int64_t pu = sched.unit_start(bu, hu);
+                if (pu >= w_begin && pu < w_end) {   // this worker holds the unit's first tile
+                    int32_t* rec = merge_records + kRecordWords * u;
+                    rec[0] = sched.parts(bu, hu);
+                    rec[1] = w;
+                    rec[2] = part;
+                    rec[3] = static_cast<int32_t>(pu);
+                    rec[4] = static_cast<int32_t>(sched.T);
+                }
             }
         }
         __syncthreads();
@@ -746,14 +741,21 @@ __global__ __launch_bounds__(kPlanThreads) void plan_device_kernel(const int32_t
 #define HPC_DECODE_PREFETCH_BF16 2
 #endif
 #ifndef HPC_DECODE_PREFETCH_FP8
-#define HPC_DECODE_PREFETCH_FP8 4
+#define HPC_DECODE_PREFETCH_FP8 2
+#endif
+// fp8 tiles: plan every slot's next tile one ring turn ahead (see load_tile).
+// Off: with it, or with more than two slots, the compiler's load-counter
+// waits at the loop head drain the whole ring once per turn, which measured
+// slower than a clean two-slot ring.
+#ifndef HPC_DECODE_AHEAD_FP8
+#define HPC_DECODE_AHEAD_FP8 0
 #endif
 constexpr int kPrefetchBf16 = HPC_DECODE_PREFETCH_BF16;
 constexpr int kPrefetchFp8 = HPC_DECODE_PREFETCH_FP8;
 
 template <int KV, int PF, bool DEV>
 void launch_decode_t(const DecodeArgs& a, int n_workers, size_t lds, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-    constexpr bool kAhead = KV == HPC_KV_FP8_E4M3;
+    constexpr bool kAhead = KV == HPC_KV_FP8_E4M3 ? HPC_DECODE_AHEAD_FP8 != 0 : false;
     const DecodeScalars sc{a.batch,        a.num_kv_heads,  a.group,   a.max_pages_per_seq, a.num_pages,
                            a.max_partials, a.qk_scale_log2, a.v_scale, n_workers};
     hipExtLaunchKernelGGL((decode_kernel<KV, PF, DEV, kAhead>), dim3(n_workers), dim3(kDecodeThreads),

@@ -184,16 +184,11 @@ struct TileRef {
     int L;             // sequence length
     bool first, last;  // first / last tile of its entry
     int part;          // -1: direct output; >= 0: partial slot
-    int rec_parts;     // device schedule, entry starting at the unit's first tile: workers sharing
-                       // the unit (its merge record is written by this worker); else -1
-    int rec_first_slot;  // partial slot of this worker's entry of that unit (when rec_parts >= 2)
 };
 
 // Device-scheduled walker.  Partial slots are worker-indexed: a split entry
 // is either the worker's first entry (slot 2w) or its last (slot 2w + 1) —
-// only those two can extend past the worker's range.  The worker holding a
-// unit's first tile reports, at that entry, how many workers share the unit,
-// for the unit's merge record.
+// only those two can extend past the worker's range.
 struct DeviceWalker {
     const Sched* s;
     int w;                   // this worker
@@ -201,18 +196,11 @@ struct DeviceWalker {
     int L;                   // length of sequence b
     int64_t remaining;       // tiles of the worker not yet handed out
     bool at_start;           // the next tile is the worker's first
-    int cur_part, cur_rec_parts, cur_rec_slot;   // of the entry holding the next tile
+    int cur_part;            // of the entry holding the next tile
 
     __device__ __forceinline__ void start_entry(bool worker_first) {
         const bool split = (t > 0) || (static_cast<int64_t>(n - t) > remaining);
         cur_part = split ? 2 * w + (worker_first ? 0 : 1) : -1;
-        cur_rec_parts = -1;
-        cur_rec_slot = cur_part;
-        if (t == 0) {   // this worker owns the unit's first tile
-            if (!split) cur_rec_parts = 1;
-            else if (static_cast<int64_t>(s->W) > s->T) cur_rec_parts = n;
-            else cur_rec_parts = s->owner(s->unit_start(b, h) + n - 1) - w + 1;
-        }
     }
 
     // wave_uniform: begin is the same in every lane and the whole wave is active
@@ -230,7 +218,7 @@ struct DeviceWalker {
             start_entry(true);
         } else {
             b = h = t = n = L = 0;
-            cur_part = cur_rec_parts = cur_rec_slot = -1;
+            cur_part = -1;
         }
     }
 
@@ -243,8 +231,6 @@ struct DeviceWalker {
         r.first = (t == 0) || at_start;
         r.last = (t == n - 1) || (remaining == 1);
         r.part = cur_part;
-        r.rec_parts = cur_rec_parts;
-        r.rec_first_slot = cur_rec_slot;
         at_start = false;
         --remaining;
         ++t;
