@@ -307,15 +307,17 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
             s.info.bits &= ~127;
             page = 0;
         }
-        const uint64_t off = (static_cast<uint64_t>(page) * Hkv + info.head()) * kBlock;
-        const uint32_t kv_bytes = static_cast<uint32_t>(s.info.valid()) * kRow;
-        s.kv.load(make_rsrc(kcache + off, kv_bytes), make_rsrc(vcache + off, kv_bytes), wave, n, g);
-        // Q^T operand of a new entry: head n, dims 32kk + 8g .. +8; heads >= G read as zero
+        // Q^T operand of a new entry: head n, dims 32kk + 8g .. +8; heads >= G read
+        // as zero, and so does all of it for a tile that does not start an entry.
+        // Issued before the K/V loads, so that it has landed whenever they have.
         const __amdgpu_buffer_rsrc_t rq =
             make_rsrc(q + static_cast<int64_t>(info.row) * kHeadDim, info.first() ? G * kHeadDim * 2 : 0);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
             s.q[kk] = __builtin_amdgcn_raw_buffer_load_b128(rq, n * kHeadDim * 2 + 64 * kk + 16 * g, 0, 0);
+        const uint64_t off = (static_cast<uint64_t>(page) * Hkv + info.head()) * kBlock;
+        const uint32_t kv_bytes = static_cast<uint32_t>(s.info.valid()) * kRow;
+        s.kv.load(make_rsrc(kcache + off, kv_bytes), make_rsrc(vcache + off, kv_bytes), wave, n, g);
     };
 
     TileSlot<KV> ring[PF];
@@ -430,9 +432,15 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     };
 
     auto consume = [&](const TileSlot<KV>& s) {
-        if (s.info.first()) {
+        // the slot's Q registers are read on every tile (a select, not a
+        // branch): a load whose result went unread could have its register
+        // reused while still in flight, which forces a wait for every load
+        const bool fq = s.info.first();
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) qop[kk] = bitcast<bf16x8>(s.q[kk]);
+        for (int kk = 0; kk < 4; ++kk) {
+            const u32x4 prev = bitcast<u32x4>(qop[kk]);
+            qop[kk] = bitcast<bf16x8>(u32x4{fq ? s.q[kk][0] : prev[0], fq ? s.q[kk][1] : prev[1],
+                                            fq ? s.q[kk][2] : prev[2], fq ? s.q[kk][3] : prev[3]});
         }
         f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll

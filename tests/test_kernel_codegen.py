@@ -1,0 +1,58 @@
+"""Code-generation guards for the decode kernel (CPU only: hipcc cross-compiles
+for gfx950 and the AMD assembly of this repository's own kernel is read).
+
+The decode kernel keeps a ring of tiles in flight: when a slot is consumed,
+only that slot's loads may be waited for.  Small register-allocation changes
+can make the compiler insert a wait for *all* outstanding loads at the loop
+head (it then copies in-flight load destinations), which drains the ring once
+per turn and costs a large part of the bandwidth.  This test fails if any
+decode kernel's main loop waits with fewer than one tile of loads still
+outstanding before its first score MFMA.
+"""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from load_balanced_paged_step_amd import build as B
+
+LOADS_PER_TILE = 12   # 4 K + 4 V + 4 Q buffer loads per wave and tile
+
+
+def _asm(tmp_path) -> str:
+    try:
+        hipcc = B._hipcc()
+    except RuntimeError:
+        pytest.skip("hipcc not available")
+    out = tmp_path / "decode_kernels.s"
+    cmd = [hipcc, "-x", "hip", *B.DEVICE, *B.COMMON, "-S", "--offload-device-only",
+           os.path.join(B.HERE, "csrc", "decode_kernels.hip"), "-o", str(out)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    return out.read_text()
+
+
+def _kernels(asm: str):
+    for m in re.finditer(r"^(_ZN4hpcd\w*decode_kernel\w*):", asm, re.M):
+        end = asm.find("s_endpgm", m.end())
+        yield m.group(1), asm[m.end():end]
+
+
+def test_ring_waits_leave_a_tile_in_flight(tmp_path):
+    asm = _asm(tmp_path)
+    kernels = list(_kernels(asm))
+    assert len(kernels) == 4, [k for k, _ in kernels]   # bf16 / fp8 x host plan / device schedule
+    bad = []
+    for name, body in kernels:
+        first_mfma = body.find("v_mfma_f32_16x16x32_bf16")
+        assert first_mfma > 0, name
+        # the outermost loop that holds the first score MFMA is the tile loop
+        heads = [m.end() for m in re.finditer(r"This (?:Inner )?Loop Header: Depth=1", body[:first_mfma])]
+        assert heads, name
+        waits = [int(x) for x in re.findall(r"s_waitcnt vmcnt\((\d+)\)", body[heads[-1]:first_mfma])]
+        assert waits, name
+        if min(waits) < LOADS_PER_TILE:
+            bad.append((name, waits))
+    assert not bad, bad
