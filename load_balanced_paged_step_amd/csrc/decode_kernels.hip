@@ -160,23 +160,39 @@ struct TileSlot {
 };
 
 // Host-planned tile source: walks this worker's entries in the plan words.
+// The worker's first 64 entries (and their sequence lengths) are fetched once
+// into the lanes of a few vector registers, lane i holding entry i, so moving
+// to the next entry is a lane read, not a chain of dependent memory loads;
+// entries beyond those are read from memory.
 struct HostWalker {
     const int32_t* entries;
     const int32_t* seq_lens;
-    int H, e, e_end;
+    int H, e, e0, e_end;
     int b, h, t, tb, L, part;
     bool have, at_entry_start;
+    int c_u, c_t0, c_t1, c_part, c_len;   // lane i: entry e0 + i
 
     __device__ __forceinline__ void load_entry() {
         have = e < e_end;
         if (!have) return;
-        const int u = entries[4 * e + 0];
+        const int i = e - e0;
+        int u, len;
+        if (i < 64) {
+            u = __builtin_amdgcn_readlane(c_u, i);
+            t = __builtin_amdgcn_readlane(c_t0, i);
+            tb = __builtin_amdgcn_readlane(c_t1, i);
+            part = __builtin_amdgcn_readlane(c_part, i);
+            len = __builtin_amdgcn_readlane(c_len, i);
+        } else {
+            u = entries[4 * e + 0];
+            t = entries[4 * e + 1];
+            tb = entries[4 * e + 2];
+            part = entries[4 * e + 3];
+            len = seq_lens[u / H];
+        }
         b = u / H;
         h = u - b * H;
-        t = entries[4 * e + 1];
-        tb = entries[4 * e + 2];
-        part = entries[4 * e + 3];
-        L = seq_lens[b];
+        L = len;
         at_entry_start = true;
         ++e;
     }
@@ -185,8 +201,18 @@ struct HostWalker {
         entries = ent;
         seq_lens = lens;
         H = num_kv_heads;
-        e = worker_ptr[w];
+        e = e0 = worker_ptr[w];
         e_end = worker_ptr[w + 1];
+        const int idx = e0 + static_cast<int>(threadIdx.x & 63);
+        c_u = c_t0 = c_t1 = c_part = c_len = 0;
+        if (idx < e_end) {
+            const int4 ew = *reinterpret_cast<const int4*>(ent + 4 * static_cast<int64_t>(idx));
+            c_u = ew.x;
+            c_t0 = ew.y;
+            c_t1 = ew.z;
+            c_part = ew.w;
+            c_len = lens[ew.x / num_kv_heads];
+        }
         load_entry();
     }
     __device__ __forceinline__ bool next(TileRef& r) {

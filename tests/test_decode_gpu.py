@@ -91,6 +91,8 @@ def test_page_permutation_bitwise(fmt):
     ([500, 30], 16, 1, 6),                      # G = 16 (largest supported)
     ([300, 1000, 7], 12, 3, 11),                # G = 4, three KV heads
     ([4000, 17], 64, 8, 64),                    # full 64q/8kv head set, bf16
+    ([(37 * i) % 300 for i in range(90)], 16, 2, 1),   # one worker holding 180 entries
+    ([64] * 70 + [5000], 8, 1, 2),              # more than 64 entries on the first worker
 ])
 def test_edge_shapes(lens, hq, hkv, W):
     announce(f"edge lens={lens} hq={hq} hkv={hkv} W={W}")
