@@ -115,26 +115,39 @@ struct KvTile<HPC_KV_BF16> {
     }
     __device__ __forceinline__ bf16x8 k_op(int kk) const { return bitcast<bf16x8>(k[kk]); }
     __device__ __forceinline__ u32x4 v_row(int i) const { return v[i]; }
+    // byte offset, in a bf16 Q row, of the 8 dims lane group g supplies in QK step kk
+    // (dims 32kk + 8g .. +8, the same k order as the K operand)
+    static __device__ __forceinline__ uint32_t q_offset(int kk, int g) { return 64 * kk + 16 * g; }
 };
 
 template <>
 struct KvTile<HPC_KV_FP8_E4M3> {
     static constexpr uint32_t kRow = kHeadDim;       // bytes per token row
-    u32x2 k[4];   // K row 16*wave+n, dims 32kk+8g .. +8 (fp8)
+    // K row 16*wave+n, bytes 16g .. +16 (k[0]) and 64 + 16g .. +16 (k[1]): each
+    // load instruction reads whole 64-byte halves of the rows.  The QK steps
+    // take the dims in this order (step kk, group g: dims 64 (kk >> 1) + 16g +
+    // 8 (kk & 1) .. +8); the Q operand is loaded in the same order (q_offset).
+    u32x4 k[2];
     u32x2 v[4];   // V rows 16*wave+4g+i, dims 8n .. 8n+7 (fp8)
     __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
                                          int wave, int n, int g) {
-        const uint32_t ko = (16 * wave + n) * kRow + 8 * g;
+        const uint32_t ko = (16 * wave + n) * kRow + 16 * g;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-            k[kk] = __builtin_amdgcn_raw_buffer_load_b64(rk, ko + 32 * kk, 0, kPolicyStream);
+        for (int j = 0; j < 2; ++j)
+            k[j] = __builtin_amdgcn_raw_buffer_load_b128(rk, ko + 64 * j, 0, kPolicyStream);
         const uint32_t vo = (16 * wave + 4 * g) * kRow + 8 * n;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             v[i] = __builtin_amdgcn_raw_buffer_load_b64(rv, vo + i * kRow, 0, kPolicyStream);
     }
-    __device__ __forceinline__ bf16x8 k_op(int kk) const { return bitcast<bf16x8>(fp8x8_to_bf16x8(k[kk][0], k[kk][1])); }
+    __device__ __forceinline__ bf16x8 k_op(int kk) const {
+        const u32x4& x = k[kk >> 1];
+        return bitcast<bf16x8>((kk & 1) ? fp8x8_to_bf16x8(x[2], x[3]) : fp8x8_to_bf16x8(x[0], x[1]));
+    }
     __device__ __forceinline__ u32x4 v_row(int i) const { return fp8x8_to_bf16x8(v[i][0], v[i][1]); }
+    static __device__ __forceinline__ uint32_t q_offset(int kk, int g) {
+        return 128 * (kk >> 1) + 32 * g + 16 * (kk & 1);
+    }
 };
 
 // Where a tile comes from and where its entry's result goes; all wave-uniform
@@ -144,6 +157,8 @@ struct TileInfo {
     int row;      // b * Hq + h * G: first query head row of the entry
     int part;     // output target of the entry (see TileRef::part)
     int page;     // physical page of the tile (its scalar load may still be in flight)
+    int page2;    // tile pairs: page of the entry's next tile, held in the same slot
+    int valid2;   // tile pairs: valid rows of that tile (0: the slot holds one tile)
     __device__ __forceinline__ int valid() const { return bits & 127; }
     __device__ __forceinline__ bool first() const { return (bits >> 7) & 1; }
     __device__ __forceinline__ bool last() const { return (bits >> 8) & 1; }
@@ -151,10 +166,12 @@ struct TileInfo {
     __device__ __forceinline__ int head() const { return bits >> 10; }
 };
 
-// One slot of the prefetch ring: a tile's K/V rows in flight or arrived.
-template <int KV>
+// One slot of the prefetch ring: the K/V rows of NT consecutive tiles of one
+// entry (NT = 2 for fp8, so a slot holds as many bytes as one bf16 tile), in
+// flight or arrived.
+template <int KV, int NT>
 struct TileSlot {
-    KvTile<KV> kv;
+    KvTile<KV> kv[NT];
     u32x4 q[4];   // Q^T operand of the entry, loaded only for an entry's first tile
     TileInfo info;
 };
@@ -250,7 +267,7 @@ __device__ __forceinline__ void fetch_args(A& a, B& b, C& c, D& d) {
     asm("" : "+s"(a), "+s"(b), "+s"(c), "+s"(d));
 }
 
-template <int KV, int PF, bool DEV, bool AHEAD>
+template <int KV, int PF, int NT, bool DEV, bool AHEAD>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     const __bf16* __restrict__ q, const char* __restrict__ kcache, const char* __restrict__ vcache,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
@@ -320,33 +337,62 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
             last = r.last;
             part = r.part;
         }
+        int page2 = 0, valid2 = 0;
+        if constexpr (NT == 2) {
+            // the entry's next tile shares the slot (same sequence, head and Q)
+            if (ok && !last) {
+                TileRef r2;
+                if constexpr (DEV) dwalk.next(r2);
+                else hwalk.next(r2);
+                const int t2 = uniform(r2.t);
+                page2 = block_table[static_cast<int64_t>(uniform(r2.b)) * a.max_pages_per_seq + t2];
+                const int rem2 = uniform(r2.L) - t2 * kPage;
+                valid2 = rem2 < 0 ? 0 : (rem2 > kPage ? kPage : rem2);
+                last = r2.last;
+            }
+        }
         const int valid = rem < 0 ? 0 : (rem > kPage ? kPage : rem);
         s.bits = uniform(valid | (first ? 1 << 7 : 0) | (last ? 1 << 8 : 0) | (ok ? 1 << 9 : 0) | (h << 10));
         s.page = page;
         s.row = uniform(row);
         s.part = uniform(part);
+        s.page2 = page2;
+        s.valid2 = uniform(valid2);
     };
-    auto load_tile = [&](TileSlot<KV>& s, const TileInfo& info) {
+    auto load_tile = [&](TileSlot<KV, NT>& s, const TileInfo& info) {
         s.info = info;
         int page = uniform(info.page);
         if (static_cast<unsigned>(page) >= static_cast<unsigned>(a.num_pages)) {
             s.info.bits &= ~127;
             page = 0;
         }
-        // Q^T operand of a new entry: head n, dims 32kk + 8g .. +8; heads >= G read
+        // Q^T operand of a new entry: head n, in the K operand's dim order
+        // (KvTile::q_offset); heads >= G read
         // as zero, and so does all of it for a tile that does not start an entry.
         // Issued before the K/V loads, so that it has landed whenever they have.
         const __amdgpu_buffer_rsrc_t rq =
             make_rsrc(q + static_cast<int64_t>(info.row) * kHeadDim, info.first() ? G * kHeadDim * 2 : 0);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
-            s.q[kk] = __builtin_amdgcn_raw_buffer_load_b128(rq, n * kHeadDim * 2 + 64 * kk + 16 * g, 0, 0);
+            s.q[kk] = __builtin_amdgcn_raw_buffer_load_b128(rq, n * kHeadDim * 2 + KvTile<KV>::q_offset(kk, g), 0, 0);
         const uint64_t off = (static_cast<uint64_t>(page) * Hkv + info.head()) * kBlock;
         const uint32_t kv_bytes = static_cast<uint32_t>(s.info.valid()) * kRow;
-        s.kv.load(make_rsrc(kcache + off, kv_bytes), make_rsrc(vcache + off, kv_bytes), wave, n, g);
+        s.kv[0].load(make_rsrc(kcache + off, kv_bytes), make_rsrc(vcache + off, kv_bytes), wave, n, g);
+        if constexpr (NT == 2) {
+            int page2 = uniform(info.page2);
+            int valid2 = info.valid2;
+            if (static_cast<unsigned>(page2) >= static_cast<unsigned>(a.num_pages)) {
+                s.info.valid2 = 0;
+                valid2 = 0;
+                page2 = 0;
+            }
+            const uint64_t off2 = (static_cast<uint64_t>(page2) * Hkv + info.head()) * kBlock;
+            const uint32_t kv_bytes2 = static_cast<uint32_t>(valid2) * kRow;
+            s.kv[1].load(make_rsrc(kcache + off2, kv_bytes2), make_rsrc(vcache + off2, kv_bytes2), wave, n, g);
+        }
     };
 
-    TileSlot<KV> ring[PF];
+    TileSlot<KV, NT> ring[PF];
     TileInfo ahead[PF];   // the tile each slot loads next
 #pragma unroll
     for (int j = 0; j < PF; ++j) plan_tile(ahead[j]);
@@ -457,7 +503,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
         for (int nb = 0; nb < 8; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     };
 
-    auto consume = [&](const TileSlot<KV>& s) {
+    auto consume = [&](const TileSlot<KV, NT>& s) {
         // the slot's Q registers are read on every tile (a select, not a
         // branch): a load whose result went unread could have its register
         // reused while still in flight, which forces a wait for every load
@@ -468,44 +514,57 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
             qop[kk] = bitcast<bf16x8>(u32x4{fq ? s.q[kk][0] : prev[0], fq ? s.q[kk][1] : prev[1],
                                             fq ? s.q[kk][2] : prev[2], fq ? s.q[kk][3] : prev[3]});
         }
-        f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s.kv.k_op(kk), qop[kk], sc, 0, 0, 0);
         const int r0 = 16 * wave + 4 * g;
+        f32x4 sc[NT];
         float mt = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            sc[i] = (r0 + i < s.info.valid()) ? sc[i] * a.qk_scale_log2 : -INFINITY;
-            mt = fmaxf(mt, sc[i]);
+        for (int tt = 0; tt < NT; ++tt) {
+            sc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                sc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s.kv[tt].k_op(kk), qop[kk], sc[tt], 0, 0, 0);
+            const int valid = tt == 0 ? s.info.valid() : s.info.valid2;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                sc[tt][i] = (r0 + i < valid) ? sc[tt][i] * a.qk_scale_log2 : -INFINITY;
+                mt = fmaxf(mt, sc[tt][i]);
+            }
         }
         mt = fmaxf(mt, __shfl_xor(mt, 16));
         mt = fmaxf(mt, __shfl_xor(mt, 32));
         const float m_new = fmaxf(m, mt);
         const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
         const float alpha = __builtin_amdgcn_exp2f(m - m_use);
-        float p[4];
         float psum = 0.f;
+        bf16x4 pop[NT];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            p[i] = __builtin_amdgcn_exp2f(sc[i] - m_use);
-            psum += p[i];
+        for (int tt = 0; tt < NT; ++tt) {
+            float p[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                p[i] = __builtin_amdgcn_exp2f(sc[tt][i] - m_use);
+                psum += p[i];
+            }
+            pop[tt] = bf16x4{static_cast<__bf16>(p[0]), static_cast<__bf16>(p[1]), static_cast<__bf16>(p[2]),
+                             static_cast<__bf16>(p[3])};
         }
         l = l * alpha + psum;
         m = m_new;
-        const bf16x4 pop = bf16x4{static_cast<__bf16>(p[0]), static_cast<__bf16>(p[1]),
-                                  static_cast<__bf16>(p[2]), static_cast<__bf16>(p[3])};
-        u32x4 rows[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) rows[i] = s.kv.v_row(i);
+        for (int nb = 0; nb < 8; ++nb) acc[nb] = acc[nb] * alpha;
 #pragma unroll
-        for (int nb = 0; nb < 8; ++nb) {
-            const int d = nb >> 1;
-            const uint32_t sel = (nb & 1) ? kSelHi : kSelLo;
-            const u32x2 vt = u32x2{__builtin_amdgcn_perm(rows[1][d], rows[0][d], sel),
-                                   __builtin_amdgcn_perm(rows[3][d], rows[2][d], sel)};
-            acc[nb] = acc[nb] * alpha;
-            acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(bitcast<bf16x4>(vt), pop, acc[nb], 0, 0, 0);
+        for (int tt = 0; tt < NT; ++tt) {
+            u32x4 rows[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) rows[i] = s.kv[tt].v_row(i);
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb) {
+                const int d = nb >> 1;
+                const uint32_t sel = (nb & 1) ? kSelHi : kSelLo;
+                const u32x2 vt = u32x2{__builtin_amdgcn_perm(rows[1][d], rows[0][d], sel),
+                                       __builtin_amdgcn_perm(rows[3][d], rows[2][d], sel)};
+                acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(bitcast<bf16x4>(vt), pop[tt], acc[nb], 0, 0, 0);
+            }
         }
         if (s.info.last()) flush(s.info);
     };
@@ -781,6 +840,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_device_kernel(const int32_t
 // Off: with it, or with more than two slots, the compiler's load-counter
 // waits at the loop head drain the whole ring once per turn, which measured
 // slower than a clean two-slot ring.
+// fp8: two tiles of an entry per ring slot (a slot then holds as many bytes as a bf16 tile)
+#ifndef HPC_DECODE_PAIR_FP8
+#define HPC_DECODE_PAIR_FP8 1
+#endif
 #ifndef HPC_DECODE_AHEAD_FP8
 #define HPC_DECODE_AHEAD_FP8 0
 #endif
@@ -792,7 +855,8 @@ void launch_decode_t(const DecodeArgs& a, int n_workers, size_t lds, hipStream_t
     constexpr bool kAhead = KV == HPC_KV_FP8_E4M3 ? HPC_DECODE_AHEAD_FP8 != 0 : false;
     const DecodeScalars sc{a.batch,        a.num_kv_heads,  a.group,   a.max_pages_per_seq, a.num_pages,
                            a.max_partials, a.qk_scale_log2, a.v_scale, n_workers};
-    hipExtLaunchKernelGGL((decode_kernel<KV, PF, DEV, kAhead>), dim3(n_workers), dim3(kDecodeThreads),
+    constexpr int kTilesPerSlot = KV == HPC_KV_FP8_E4M3 ? HPC_DECODE_PAIR_FP8 + 1 : 1;
+    hipExtLaunchKernelGGL((decode_kernel<KV, PF, kTilesPerSlot, DEV, kAhead>), dim3(n_workers), dim3(kDecodeThreads),
                           static_cast<std::uint32_t>(lds), s, e0, e1, 0u,
                           static_cast<const __bf16*>(a.q), static_cast<const char*>(a.k),
                           static_cast<const char*>(a.v), a.block_table, a.seq_lens, a.worker_ptr, a.entries,

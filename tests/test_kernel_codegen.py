@@ -74,8 +74,8 @@ def ring_waits(tmp_path_factory):
 
 
 def _device_scheduled(name: str) -> bool:
-    # decode_kernel<KV, PF, DEV, AHEAD>: the third template argument
-    return re.search(r"decode_kernelILi\dELi\dELb1E", name) is not None
+    # decode_kernel<int..., DEV, AHEAD>: the first bool template argument
+    return re.search(r"decode_kernelI(?:Li\d+E)+Lb1E", name) is not None
 
 
 def test_four_decode_kernels(ring_waits):
