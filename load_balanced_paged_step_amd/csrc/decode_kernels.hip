@@ -280,6 +280,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     __shared__ int32_t s_tmp[2 * kWaves];
     extern __shared__ int32_t s_dyn[];   // device schedule: len[B], tile prefix[B + 1]
 
+    // the host-planned walker reads lengths inside the tile loop: it keeps the
+    // argument itself, whose read-only, unaliased provenance lets those reads
+    // go through the scalar unit (a pointer that came out of the asm below
+    // has lost it, and a vector load there would make the loop wait for
+    // every load in flight)
+    const int32_t* __restrict__ lens_loop = seq_lens;
     fetch_args(seq_lens, a.batch, a.max_pages_per_seq, a.n_workers);
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
@@ -310,7 +316,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
         if (w_begin < w_end) dwalk.init(sched, w, w_begin, w_end, true);
         else dwalk.remaining = 0;                  // an empty worker: only bookkeeping below
     } else {
-        hwalk.init(worker_ptr, entries, seq_lens, Hkv, w);
+        hwalk.init(worker_ptr, entries, lens_loop, Hkv, w);
         if (!hwalk.have) return;
     }
 
@@ -396,8 +402,15 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     TileInfo ahead[PF];   // the tile each slot loads next
 #pragma unroll
     for (int j = 0; j < PF; ++j) plan_tile(ahead[j]);
+    // Slots are issued in ring order, each slot's Q before its K/V: the
+    // loop's first wait (for slot 0) must leave the later slots in flight on
+    // the path that enters the loop too, so the scheduler may not reorder
+    // these loads across slots.
 #pragma unroll
-    for (int j = 0; j < PF; ++j) load_tile(ring[j], ahead[j]);
+    for (int j = 0; j < PF; ++j) {
+        load_tile(ring[j], ahead[j]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
     if constexpr (AHEAD) {
 #pragma unroll
         for (int j = 0; j < PF; ++j) plan_tile(ahead[j]);

@@ -88,9 +88,10 @@ def test_device_scheduled_ring_keeps_a_tile_in_flight(ring_waits):
     assert not bad, bad
 
 
-@pytest.mark.xfail(reason="the host-planned kernel's loop head waits for every load (compiler register "
-                          "copies of in-flight Q registers); it runs about 20% slower than the device-"
-                          "scheduled kernel on the skewed batch", strict=True)
 def test_host_planned_ring_keeps_a_tile_in_flight(ring_waits):
+    # Two things once made this kernel wait for every load at its loop head:
+    # a length read through a pointer that had lost its read-only provenance
+    # (a vector load inside the loop), and the prologue issuing slot 0's Q
+    # loads last (so the loop-entry path needed all loads done).
     bad = [(n, w) for n, w in ring_waits.items() if not _device_scheduled(n) and min(w) < KV_LOADS_PER_TILE]
     assert not bad, bad
