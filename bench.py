@@ -6,8 +6,9 @@ tiles spread evenly over the persistent grid), the decode kernel, and the
 log-sum-exp merge of split sequences.  With --schedule device (default) the
 decode kernel derives the schedule from the lengths on the GPU and writes one
 merge record per (sequence, KV head) for the merge kernel that follows; with
---schedule host the C++ planner runs on the host every step, the plan is
-uploaded, and the decode and merge kernels read it.  Default workload: the skewed batch of one
+--schedule host one native call per step runs the C++ planner on the host,
+queues the plan's upload and launches the decode and merge kernels, which
+read it.  Default workload: the skewed batch of one
 131072-token sequence and 31 sequences of 4096 tokens, 8 query heads over one
 KV head, head dim 128, bf16 KV in 64-token pages, shuffled block table
 ("vLLM x HPC-Ops ...", §Attention Decode under Mixed-Length Batches).
@@ -111,8 +112,8 @@ def cpu_baseline(inp, alg_bytes: int):
 def main() -> int:
     args = parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the decode path has no "
-              "multi-GPU mode in this build", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the decode path runs on a "
+              "single GPU and has no multi-GPU mode", file=sys.stderr)
         return 2
 
     import numpy as np
@@ -171,11 +172,14 @@ def main() -> int:
         def one_step(i: int) -> None:
             launchers[i % copies]()
     else:
-        step = hd.DecodeStep(inp.num_q_heads, inp.num_kv_heads, inp.batch, W, device=dev)
+        ws = torch.empty(hd.hpc_decode_plan_workspace_bound(inp.batch, inp.num_q_heads, inp.num_kv_heads, W),
+                         dtype=torch.uint8, device=dev)
+        planned = [hd.PlannedStepLauncher(q, ks[c], vs[c], bt, sl, out, lse, num_kv_heads=inp.num_kv_heads,
+                                          n_workers=W, workspace=ws, **scales) for c in range(copies)]
+        lens_np = np.ascontiguousarray(lens_host, dtype=np.int32)
 
         def one_step(i: int) -> None:
-            step.plan(lens_host)
-            step.attend(q, ks[i % copies], vs[i % copies], bt, sl, out, lse, **scales)
+            planned[i % copies](lens_np)
 
     log(f"warmup {args.warmup} steps")
     for i in range(args.warmup):

@@ -191,6 +191,43 @@ int hpc_decode_check(const hpc_decode_params* params, const void* q, const void*
                      int64_t workspace_bytes, const void* out, const float* lse);
 
 /*
+ * Workspace, in bytes, that is enough for hpc_decode_attn under any plan of
+ * this batch size and worker count (a plan has at most W + B*H_kv - 1
+ * entries, so at most that many partial slots).  Negative status for
+ * batch < 0, n_workers < 1 or heads that do not group.
+ */
+int64_t hpc_decode_plan_workspace_bound(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t n_workers);
+
+/*
+ * A host-planned decode step in one call, for callers that hold the step's
+ * lengths on the host (the per-step scheduler of §Attention Backend: Dynamic
+ * Load-Balanced Scheduling, then the attention): hpc_decode_plan of
+ * seq_lens_host into plan_host, the host checks of hpc_decode_attn, an
+ * asynchronous copy of the plan's words to plan_dev queued on `stream`, and
+ * the kernels of hpc_decode_attn on the same stream.
+ *
+ * seq_lens_host  host int32 [batch]: the lengths seq_lens (device) holds
+ * plan_host      host buffer of plan_capacity >= hpc_decode_plan_size words.
+ *                Pinned memory (hipHostMalloc) makes the copy asynchronous;
+ *                the caller must not rewrite the buffer until that copy has
+ *                executed on the stream (two buffers used in turn, each
+ *                guarded by an event recorded after the call, suffice)
+ * plan_dev       device buffer of at least as many words; must differ from
+ *                plan_host; valid until the stream work completes
+ * workspace      device, >= hpc_decode_workspace_size of the plan made here
+ *                (hpc_decode_plan_workspace_bound is always enough)
+ * Other arguments as for hpc_decode_attn.  Every check (planner arguments,
+ * plan against params, workspace size) runs before the first HIP call; a
+ * failed copy or launch returns HPC_ERR_HIP.
+ */
+int hpc_decode_plan_attn(const hpc_decode_params* params, const int32_t* seq_lens_host, int32_t batch,
+                         int32_t n_workers, int32_t* plan_host, int64_t plan_capacity, int32_t* plan_dev,
+                         const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                         const int32_t* seq_lens, void* workspace, int64_t workspace_bytes, void* out,
+                         float* lse, void* stream);
+
+/*
  * Device-scheduled decode step (no host plan).  The same per-step schedule
  * as hpc_decode_plan (§Attention Backend: Dynamic Load-Balanced Scheduling)
  * is derived inside the decode kernel from the device copy of the lengths:

@@ -30,6 +30,7 @@ __all__ = [
     "hpc_decode_check", "hpc_decode_attn", "hpc_status_string", "hpc_decode_profile_start",
     "hpc_decode_profile_stop", "hpc_probe_read", "hpc_probe_copy", "hpc_decode_step",
     "hpc_decode_step_check", "hpc_decode_step_workspace_size", "hpc_decode_plan_device", "StepLauncher",
+    "hpc_decode_plan_workspace_bound", "hpc_decode_plan_attn", "PlannedStepLauncher",
     "DecodeStep", "HpcDecodeError",
     "kv_dtype_code", "make_params", "HPC_KV_BF16", "HPC_KV_FP8_E4M3",
 ]
@@ -200,6 +201,100 @@ def hpc_decode_attn(q, k_cache, v_cache, block_table, seq_lens, plan_host, plan_
     args, _ = _attn_args(q, k_cache, v_cache, block_table, seq_lens, plan_host, plan_dev, workspace, out,
                          lse, num_kv_heads, sm_scale, k_scale, v_scale)
     _lib.check(lib().hpc_decode_attn(*args, _stream_handle(stream)), "hpc_decode_attn")
+
+
+# ------------------------------------------------ host-planned step in one call ---
+
+def hpc_decode_plan_workspace_bound(batch: int, num_q_heads: int, num_kv_heads: int, n_workers: int) -> int:
+    return _lib.check(lib().hpc_decode_plan_workspace_bound(batch, num_q_heads, num_kv_heads, n_workers),
+                      "hpc_decode_plan_workspace_bound")
+
+
+def hpc_decode_plan_attn(seq_lens_host, plan_host, plan_dev, q, k_cache, v_cache, block_table, seq_lens,
+                         workspace, out, lse, *, num_kv_heads, n_workers, sm_scale, k_scale=1.0, v_scale=1.0,
+                         stream=None) -> np.ndarray:
+    """Plan the host lengths into ``plan_host`` (a host int32 buffer, pinned
+    for an asynchronous upload), queue its copy to ``plan_dev`` and launch the
+    step, in one native call; returns the plan words (a view of plan_host).
+    The caller keeps plan_host unchanged until the copy has run on the stream."""
+    lens = _host_i32(seq_lens_host).reshape(-1)
+    params, args = _step_args(q, k_cache, v_cache, block_table, seq_lens, workspace, out, lse, num_kv_heads,
+                              n_workers, sm_scale, k_scale, v_scale)
+    if lens.shape[0] != q.shape[0]:
+        raise ValueError("seq_lens_host has the wrong batch size")
+    ph = plan_host.numpy() if isinstance(plan_host, torch.Tensor) else plan_host
+    if not isinstance(ph, np.ndarray) or ph.dtype != np.int32 or not ph.flags.c_contiguous:
+        raise ValueError("plan_host must be a contiguous int32 host buffer")
+    dev = _dev_ptr(plan_dev, "plan_dev", torch.int32)
+    if plan_dev.numel() < ph.shape[0]:
+        raise ValueError("plan_dev is smaller than plan_host")
+    _lib.check(lib().hpc_decode_plan_attn(ctypes.byref(params), lens.ctypes.data, lens.shape[0], n_workers,
+                                          ph.ctypes.data, ph.shape[0], dev, *args[2:], _stream_handle(stream)),
+               "hpc_decode_plan_attn")
+    return ph[:hpc_decode_plan_words(ph)]
+
+
+class PlannedStepLauncher:
+    """A host-planned decode step with its device arguments marshalled once.
+
+    Each call plans the host lengths it is given into one of two pinned plan
+    buffers, queues the plan's upload and launches the kernels, all in one
+    ``hpc_decode_plan_attn`` call on the stream given at construction
+    (default: the current stream then).  An event recorded after each call
+    guards its buffer: the call after next waits for it before rewriting the
+    buffer.  Tensors must stay alive and unchanged in shape for the
+    launcher's lifetime; ``plan_host`` is the last call's plan words.
+    """
+
+    def __init__(self, q, k_cache, v_cache, block_table, seq_lens, out, lse, *, num_kv_heads, n_workers,
+                 sm_scale, k_scale=1.0, v_scale=1.0, workspace=None, stream=None):
+        B = q.shape[0]
+        if workspace is None:
+            need = hpc_decode_plan_workspace_bound(B, q.shape[1], num_kv_heads, n_workers)
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        self.params, args = _step_args(q, k_cache, v_cache, block_table, seq_lens, workspace, out, lse,
+                                       num_kv_heads, n_workers, sm_scale, k_scale, v_scale)
+        self._keep = (q, k_cache, v_cache, block_table, seq_lens, out, lse, workspace)
+        self.workspace = workspace
+        self.batch, self.n_workers = int(B), int(n_workers)
+        self._cap = hpc_decode_plan_size(B, num_kv_heads, n_workers)
+        self._host = [torch.empty(self._cap, dtype=torch.int32, pin_memory=True) for _ in range(2)]
+        self._host_np = [h.numpy() for h in self._host]
+        self.plan_dev = torch.empty(self._cap, dtype=torch.int32, device=q.device)
+        self._stream = stream if stream is not None else torch.cuda.current_stream(q.device)
+        self._events = [torch.cuda.Event(), torch.cuda.Event()]
+        self._pending = [False, False]
+        self._flip = 0
+        self._last = None
+        self._fn = lib().hpc_decode_plan_attn
+        self._pre = (ctypes.byref(self.params),)
+        self._post = (ctypes.c_void_p(self.plan_dev.data_ptr()),) + args[2:] + (_stream_handle(self._stream),)
+
+    def __call__(self, seq_lens_host) -> None:
+        lens = seq_lens_host
+        if not (type(lens) is np.ndarray and lens.dtype == np.int32 and lens.flags.c_contiguous
+                and lens.shape == (self.batch,)):
+            lens = _host_i32(lens).reshape(-1)
+            if lens.shape[0] != self.batch:
+                raise ValueError("seq_lens_host has the wrong batch size")
+        i = self._flip
+        self._flip = i ^ 1
+        if self._pending[i]:
+            self._events[i].synchronize()          # this buffer's last upload has run
+        status = self._fn(*self._pre, lens.ctypes.data, self.batch, self.n_workers,
+                          self._host_np[i].ctypes.data, self._cap, *self._post)
+        if status:
+            _lib.check(status, "hpc_decode_plan_attn")
+        self._events[i].record(self._stream)
+        self._pending[i] = True
+        self._last = i
+
+    @property
+    def plan_host(self) -> np.ndarray:
+        if self._last is None:
+            raise RuntimeError("no step has been launched")
+        h = self._host_np[self._last]
+        return h[:hpc_decode_plan_words(h)]
 
 
 # -------------------------------------------- device-scheduled decode step ---

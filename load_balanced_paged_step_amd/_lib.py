@@ -65,6 +65,11 @@ SIGNATURES = {
                                         _VP, _VP]),
     "hpc_decode_attn": (ctypes.c_int, [_PP, _VP, _VP, _VP, _VP, _VP, _I32P, _VP, _VP, ctypes.c_int64,
                                        _VP, _VP, _VP]),
+    "hpc_decode_plan_workspace_bound": (ctypes.c_int64, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                         ctypes.c_int32]),
+    # host pointers as plain addresses: the per-step launcher passes integers
+    "hpc_decode_plan_attn": (ctypes.c_int, [_PP, _VP, ctypes.c_int32, ctypes.c_int32, _VP, ctypes.c_int64, _VP,
+                                            _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_int64, _VP, _VP, _VP]),
     "hpc_decode_step": (ctypes.c_int, [_PP, ctypes.c_int32, ctypes.c_int32, _VP, _VP, _VP, _VP, _VP, _VP,
                                        ctypes.c_int64, _VP, _VP, _VP]),
     "hpc_decode_step_check": (ctypes.c_int, [_PP, ctypes.c_int32, ctypes.c_int32, _VP, _VP, _VP, _VP, _VP,

@@ -92,14 +92,12 @@ extern "C" int hpc_decode_check(const hpc_decode_params* p, const void* q, const
     return HPC_OK;
 }
 
-extern "C" int hpc_decode_attn(const hpc_decode_params* p, const void* q, const void* k_cache,
-                               const void* v_cache, const int32_t* block_table,
-                               const int32_t* seq_lens, const int32_t* plan_host,
-                               const int32_t* plan_dev, void* workspace, int64_t workspace_bytes,
-                               void* out, float* lse, void* stream) {
-    const int status = hpc_decode_check(p, q, k_cache, v_cache, block_table, seq_lens, plan_host,
-                                        plan_dev, workspace, workspace_bytes, out, lse);
-    if (status != HPC_OK) return status;
+namespace {
+
+// The launches of a host-planned step, after hpc_decode_check has passed.
+int launch_planned(const hpc_decode_params* p, const void* q, const void* k_cache, const void* v_cache,
+                   const int32_t* block_table, const int32_t* seq_lens, const int32_t* plan_host,
+                   const int32_t* plan_dev, void* workspace, void* out, float* lse, void* stream) {
     const int32_t G = p->num_q_heads / p->num_kv_heads;
     const int32_t Hkv = plan_host[2], W = plan_host[3], E = plan_host[5], P = plan_host[6],
                   C = plan_host[7];
@@ -146,6 +144,53 @@ extern "C" int hpc_decode_attn(const hpc_decode_params* p, const void* q, const 
     if (E > 0 && hpcd::launch_decode(da, p->kv_dtype, W, false, stream, ev[0], ev[1]) != 0) return HPC_ERR_HIP;
     if (C > 0 && hpcd::launch_combine(ca, C, false, stream, ev[2], ev[3]) != 0) return HPC_ERR_HIP;
     return HPC_OK;
+}
+
+}  // namespace
+
+extern "C" int hpc_decode_attn(const hpc_decode_params* p, const void* q, const void* k_cache,
+                               const void* v_cache, const int32_t* block_table,
+                               const int32_t* seq_lens, const int32_t* plan_host,
+                               const int32_t* plan_dev, void* workspace, int64_t workspace_bytes,
+                               void* out, float* lse, void* stream) {
+    const int status = hpc_decode_check(p, q, k_cache, v_cache, block_table, seq_lens, plan_host,
+                                        plan_dev, workspace, workspace_bytes, out, lse);
+    if (status != HPC_OK) return status;
+    return launch_planned(p, q, k_cache, v_cache, block_table, seq_lens, plan_host, plan_dev, workspace, out,
+                          lse, stream);
+}
+
+extern "C" int64_t hpc_decode_plan_workspace_bound(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                                   int32_t n_workers) {
+    if (batch < 0 || n_workers < 1 || num_kv_heads < 1 || num_q_heads < num_kv_heads ||
+        num_q_heads % num_kv_heads != 0)
+        return HPC_ERR_INVALID;
+    // every split entry has a slot, and a plan has at most W + U - 1 entries
+    const int64_t partials = static_cast<int64_t>(n_workers) + static_cast<int64_t>(batch) * num_kv_heads;
+    const int64_t G = num_q_heads / num_kv_heads;
+    const int64_t o_bytes = partials * G * HPC_DECODE_HEAD_DIM * 4;
+    return (o_bytes + 255) / 256 * 256 + partials * G * 4;
+}
+
+extern "C" int hpc_decode_plan_attn(const hpc_decode_params* p, const int32_t* seq_lens_host, int32_t batch,
+                                    int32_t n_workers, int32_t* plan_host, int64_t plan_capacity,
+                                    int32_t* plan_dev, const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* block_table, const int32_t* seq_lens, void* workspace,
+                                    int64_t workspace_bytes, void* out, float* lse, void* stream) {
+    if (!p || !plan_host || !plan_dev) return HPC_ERR_NULL;
+    if (static_cast<const void*>(plan_dev) == static_cast<const void*>(plan_host)) return HPC_ERR_INVALID;
+    int status = hpc_decode_plan(seq_lens_host, batch, p->num_kv_heads, n_workers, plan_host, plan_capacity);
+    if (status != HPC_OK) return status;
+    status = hpc_decode_check(p, q, k_cache, v_cache, block_table, seq_lens, plan_host, plan_dev, workspace,
+                              workspace_bytes, out, lse);
+    if (status != HPC_OK) return status;
+    const int64_t words = hpc_decode_plan_words(plan_host);
+    if (words < 0) return static_cast<int>(words);
+    if (hipMemcpyAsync(plan_dev, plan_host, static_cast<size_t>(words) * sizeof(int32_t), hipMemcpyHostToDevice,
+                       static_cast<hipStream_t>(stream)) != hipSuccess)
+        return HPC_ERR_HIP;
+    return launch_planned(p, q, k_cache, v_cache, block_table, seq_lens, plan_host, plan_dev, workspace, out,
+                          lse, stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -264,3 +264,47 @@ def test_plan_device_argument_errors():
     assert lib.hpc_decode_plan_device(ptr, 4, 1, 8, 4, ptr, cap - 1, None) == hd.HPC_ERR_TOO_SMALL
     assert lib.hpc_decode_plan_device(ptr, 4, 1, 0, 4, ptr, cap, None) == hd.HPC_ERR_INVALID
     assert lib.hpc_decode_plan_device(ptr, 4096, 1, 8, 4, ptr, 1 << 30, None) == hd.HPC_ERR_UNSUPPORTED
+
+
+def test_plan_workspace_bound_covers_every_plan():
+    rng = np.random.default_rng(3)
+    for _ in range(40):
+        B = int(rng.integers(1, 40))
+        H = int(rng.choice([1, 2, 8]))
+        W = int(rng.integers(1, 300))
+        lens = rng.integers(0, 5000, size=B).astype(np.int32)
+        plan = _cpp_plan(lens, H, W)
+        bound = hd.hpc_decode_plan_workspace_bound(B, 8 * H, H, W)
+        assert bound >= hd.hpc_decode_workspace_size(plan, 8 * H, H)
+    assert _lib.lib().hpc_decode_plan_workspace_bound(2, 8, 1, 0) == hd.HPC_ERR_INVALID
+    assert _lib.lib().hpc_decode_plan_workspace_bound(2, 12, 8, 4) == hd.HPC_ERR_INVALID
+
+
+def test_plan_attn_errors_before_any_hip_call():
+    """Every failure of hpc_decode_plan_attn here is found on the host before
+    the plan copy or a launch is queued (no device exists in this process)."""
+    lib = _lib.lib()
+    ptr = 0x1000
+    lens = np.asarray([37, 200], dtype=np.int32)
+    H, Hq, W = 1, 8, 4
+    cap = hd.hpc_decode_plan_size(2, H, W)
+    host = np.zeros(cap, dtype=np.int32)
+    params = hd.make_params(Hq, H, 4, 8, hd.HPC_KV_BF16, 1 / np.sqrt(128))
+    need = hd.hpc_decode_workspace_size(_cpp_plan(lens, H, W), Hq, H)
+
+    def call(lens_p=lens.ctypes.data, batch=2, w=W, ph=host.ctypes.data, c=cap, pd=ptr, sl=ptr, wsb=need,
+             p=ctypes.byref(params)):
+        return lib.hpc_decode_plan_attn(p, lens_p, batch, w, ph, c, pd, ptr, ptr, ptr, ptr, sl, ptr, wsb, ptr,
+                                        ptr, None)
+    assert call(p=None) == hd.HPC_ERR_NULL
+    assert call(ph=None) == hd.HPC_ERR_NULL and call(pd=None) == hd.HPC_ERR_NULL
+    assert call(pd=host.ctypes.data) == hd.HPC_ERR_INVALID           # the copy needs a separate device buffer
+    assert call(lens_p=None) == hd.HPC_ERR_NULL                      # from the planner
+    assert call(w=0) == hd.HPC_ERR_INVALID
+    assert call(c=10) == hd.HPC_ERR_TOO_SMALL
+    assert call(sl=None) == hd.HPC_ERR_NULL                          # from the attention checks
+    assert call(wsb=need - 1) == hd.HPC_ERR_TOO_SMALL
+    bad = np.asarray([37, 300], dtype=np.int32)                      # 5 tiles > 4 pages per sequence
+    assert call(lens_p=bad.ctypes.data) == hd.HPC_ERR_INVALID
+    # the planner wrote the plan of the last lengths before the check failed
+    assert np.array_equal(host[:hd.hpc_decode_plan_words(host)], _cpp_plan(bad, H, W))
