@@ -274,7 +274,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     const int32_t* __restrict__ worker_ptr, const int32_t* __restrict__ entries,
     __bf16* __restrict__ out, float* __restrict__ lse, float* __restrict__ o_part,
     float* __restrict__ lse_part, int32_t* __restrict__ merge_records, DecodeScalars a) {
-    __shared__ float s_acc[kWaves][4][8][64];
+    // entry ends: register i of every wave's eight accumulators, as two
+    // 16-byte halves per lane, so each wave stores and loads whole f32x4s
+    __shared__ f32x4 s_acc[4][kWaves][2][64];
     __shared__ float s_m[kWaves][64];
     __shared__ float s_l[kWaves][64];
     __shared__ int32_t s_tmp[2 * kWaves];
@@ -303,6 +305,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     DeviceWalker dwalk;
     HostWalker hwalk;
     int64_t w_begin = 0, w_end = 0;
+    int u_first = 0;
     if constexpr (DEV) {
         build_prefix(seq_lens, a.batch, a.max_pages_per_seq, s_dyn, s_dyn + a.batch);
         sched.len = s_dyn;
@@ -313,8 +316,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
         sched.set_tiles(static_cast<int64_t>(Hkv) * s_dyn[2 * a.batch]);
         w_begin = sched.range_begin(w);
         w_end = sched.range_begin(w + 1);
-        if (w_begin < w_end) dwalk.init(sched, w, w_begin, w_end, true);
-        else dwalk.remaining = 0;                  // an empty worker: only bookkeeping below
+        if (w_begin < w_end) {
+            dwalk.init(sched, w, w_begin, w_end, true);
+            u_first = dwalk.b * Hkv + dwalk.h;    // the unit of the worker's first tile
+        } else {
+            dwalk.remaining = 0;                   // an empty worker: only bookkeeping below
+        }
     } else {
         hwalk.init(worker_ptr, entries, lens_loop, Hkv, w);
         if (!hwalk.have) return;
@@ -418,8 +425,14 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
 
     // Device schedule, while the first tiles are in flight: empty sequences
     // get out = 0, lse = -inf and a merge record saying so, from worker
-    // u mod W (every other unit's record is written by the worker holding
-    // its first tile, so all records are rewritten every step).
+    // u mod W; every other unit's record {S_u, first worker, its slot, P_u,
+    // T} is written by the worker holding the unit's first tile, here
+    // rather than at the entry's end, so no entry end waits for it.  Units
+    // are in tile order, so this worker's are the ones from the unit of its
+    // first tile on whose first tile lies before its range ends; such a
+    // unit is its first entry (slot 2w when split) if it starts the range,
+    // else its last (slot 2w + 1 when split).  All records are rewritten
+    // every step.
     if constexpr (DEV) {
         const int U = a.batch * Hkv;
         for (int u = w + a.n_workers * static_cast<int>(threadIdx.x); u < U;
@@ -433,6 +446,20 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
             merge_records[kRecordWords * u] = 0;
         }
         if (w_begin == w_end) return;
+        for (int u = u_first + static_cast<int>(threadIdx.x); u < U; u += kDecodeThreads) {
+            const int b = u / Hkv;
+            const int h = u - b * Hkv;
+            const int64_t pu = sched.unit_start(b, h);
+            if (pu >= w_end) break;
+            if (pu < w_begin || sched.len[b] == 0) continue;
+            const int S = sched.parts(b, h);
+            int32_t* rec = merge_records + kRecordWords * u;
+            rec[0] = S;
+            rec[1] = w;
+            rec[2] = S >= 2 ? 2 * w + (pu == w_begin ? 0 : 1) : -1;
+            rec[3] = static_cast<int32_t>(pu);
+            rec[4] = static_cast<int32_t>(sched.T);
+        }
     }
 
     float m = -INFINITY;   // running max (log2 domain), uniform over g
@@ -450,9 +477,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
         s_m[wave][lane] = m;
         s_l[wave][lane] = l;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int nb = 0; nb < 8; ++nb) s_acc[wave][i][nb][lane] = acc[nb][i];
+        for (int i = 0; i < 4; ++i) {
+            s_acc[i][wave][0][lane] = f32x4{acc[0][i], acc[1][i], acc[2][i], acc[3][i]};
+            s_acc[i][wave][1][lane] = f32x4{acc[4][i], acc[5][i], acc[6][i], acc[7][i]};
+        }
         __syncthreads();
         float ms[kWaves], M = -INFINITY;
 #pragma unroll
@@ -467,13 +495,16 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
             wt[s] = __builtin_amdgcn_exp2f(ms[s] - M_use);
             wsum += wt[s] * s_l[s][lane];
         }
-        float o[8];
+        float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int nb = 0; nb < 8; ++nb) {
-            float x = 0.f;
+        for (int s = 0; s < kWaves; ++s) {
+            const f32x4 lo = s_acc[wave][s][0][lane];
+            const f32x4 hi = s_acc[wave][s][1][lane];
 #pragma unroll
-            for (int s = 0; s < kWaves; ++s) x += wt[s] * s_acc[s][wave][nb][lane];
-            o[nb] = x;
+            for (int k = 0; k < 4; ++k) {
+                o[k] += wt[s] * lo[k];
+                o[4 + k] += wt[s] * hi[k];
+            }
         }
         const int slot = part;
         if (n < G) {
@@ -491,22 +522,6 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
                 *reinterpret_cast<f32x4*>(dst) = f32x4{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
                 *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv};
                 if (wave == 0 && g == 0) lse_part[static_cast<int64_t>(slot) * G + n] = lse_val;
-            }
-        }
-        if constexpr (DEV) {
-            if (threadIdx.x == 0) {
-                const int u = row / G;
-                const int bu = u / Hkv;
-                const int hu = u - bu * Hkv;
-                const int64_t pu = sched.unit_start(bu, hu);
-                if (pu >= w_begin && pu < w_end) {   // this worker holds the unit's first tile
-                    int32_t* rec = merge_records + kRecordWords * u;
-                    rec[0] = sched.parts(bu, hu);
-                    rec[1] = w;
-                    rec[2] = part;
-                    rec[3] = static_cast<int32_t>(pu);
-                    rec[4] = static_cast<int32_t>(sched.T);
-                }
             }
         }
         __syncthreads();
@@ -579,17 +594,22 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
                 acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(bitcast<bf16x4>(vt), pop[tt], acc[nb], 0, 0, 0);
             }
         }
-        if (s.info.last()) flush(s.info);
     };
 
-    // Leaving the loop the moment a slot is empty keeps every path that
-    // reaches the back edge with all PF slots re-issued, so the compiler's
-    // load-counter waits let the other PF - 1 tiles stay in flight.
+    // One exit, at the end of a full ring turn: every path back to the top
+    // has re-issued all PF slots, so the compiler's load-counter waits let
+    // the other PF - 1 tiles stay in flight.  Slots are filled in tile order,
+    // so once slot 0 comes back empty all slots are; a later slot of the last
+    // turn may be consumed empty, which changes nothing (its scores are all
+    // -inf).  Slot 0 holds a tile on entry (workers without tiles returned
+    // above).  A slot that ends an entry is refilled before the entry is
+    // flushed, so the flush (whose barriers wait for the slowest wave) runs
+    // with every slot's loads in flight.
     for (;;) {
 #pragma unroll
         for (int j = 0; j < PF; ++j) {
-            if (!ring[j].info.real()) goto done;
             consume(ring[j]);
+            const TileInfo ended = ring[j].info;
             if constexpr (AHEAD) {
                 load_tile(ring[j], ahead[j]);
                 plan_tile(ahead[j]);
@@ -597,10 +617,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
                 plan_tile(ahead[j]);
                 load_tile(ring[j], ahead[j]);
             }
+            if (ended.last()) flush(ended);
         }
+        if (!ring[0].info.real()) break;
     }
-done:
-    return;
 }
 
 // Merge of split units: kMergeSplit workgroups per (merge record, query head
