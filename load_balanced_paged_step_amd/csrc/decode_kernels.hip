@@ -623,22 +623,26 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     }
 }
 
-// Merge of split units: kMergeSplit workgroups per (merge record, query head
-// of the group), each merging 32 of the 128 dims, so that a unit shared by
-// many workers is read by several compute units at once.  256 threads = 32
-// partial lanes x 8 dim quads.  Lane pl folds partials i = pl, pl + 32, ...
-// into a running (max, weighted sum, weight) triple, issuing up to eight
-// partials' loads before using any of them; the 32 triples are then merged by
-// log-sum-exp, 8 per wave with lane shuffles and the 4 wave results in LDS.  The records are the host plan's
-// merge list, or, for the device-scheduled step, one record per unit written
-// by the decode kernel.
-constexpr int kMergeSplit = 4;                          // workgroups per (record, head)
-constexpr int kMergeQuads = kHeadDim / 4 / kMergeSplit;  // dim quads per workgroup (8)
-constexpr int kMergeLanes = kCombineThreads / kMergeQuads;
+// Merge of split units: SPLIT workgroups per (merge record, query head of
+// the group), each merging 128 / SPLIT of the dims.  SPLIT = 4 (few records)
+// lets a unit shared by many workers be read by several compute units at
+// once; SPLIT = 1 (many records) keeps the grid small when most records need
+// little or no work.  256 threads = kLanes partial lanes x kQuads dim quads.
+// Lane pl folds partials i = pl, pl + kLanes, ... into a running (max,
+// weighted sum, weight) triple, issuing up to eight partials' loads before
+// using any of them; the triples are then merged by log-sum-exp, within each
+// wave with lane shuffles and the 4 wave results in LDS.  The records are the
+// host plan's merge list, or, for the device-scheduled step, one record per
+// unit written by the decode kernel.
 constexpr int kMergeUnroll = 8;
+constexpr int kMergeGridBudget = 2048;   // largest grid the 4-way split may take
 
-template <bool DEV>
+template <bool DEV, int SPLIT>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a) {
+    constexpr int kMergeSplit = SPLIT;
+    constexpr int kMergeQuads = kHeadDim / 4 / kMergeSplit;   // dim quads per workgroup
+    constexpr int kMergeLanes = kCombineThreads / kMergeQuads;
+    static_assert(kMergeQuads <= 32, "at least two partial lanes per wave");
     __shared__ f32x4 s_acc[kCombineThreads / 64][kMergeQuads];
     __shared__ float s_m[kCombineThreads / 64];
     __shared__ float s_w[kCombineThreads / 64];
@@ -725,8 +729,9 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
         }
         m = mk;
     }
-    // fold the 8 partial lanes of each wave with shuffles (lanes differing in
-    // bits 3..5 hold the same dims), then the 4 waves through LDS
+    // fold the partial lanes of each wave with shuffles (lanes that differ
+    // only in bits at or above log2(kMergeQuads) hold the same dims), then
+    // the 4 waves through LDS
 #pragma unroll
     for (int off = kMergeQuads; off < 64; off <<= 1) {
         const float m2 = __shfl_xor(m, off);
@@ -917,12 +922,15 @@ int launch_combine(const CombineArgs& a, int n_records, bool device_sched, void*
                    void* ev_stop) {
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipEvent_t e0 = static_cast<hipEvent_t>(ev_start), e1 = static_cast<hipEvent_t>(ev_stop);
-    if (device_sched)
-        hipExtLaunchKernelGGL(combine_kernel<true>, dim3(n_records * a.group * kMergeSplit), dim3(kCombineThreads), 0u, s, e0, e1,
-                              0u, a);
-    else
-        hipExtLaunchKernelGGL(combine_kernel<false>, dim3(n_records * a.group * kMergeSplit), dim3(kCombineThreads), 0u, s, e0,
-                              e1, 0u, a);
+    const bool wide = static_cast<int64_t>(n_records) * a.group * 4 <= kMergeGridBudget;
+    const dim3 grid(static_cast<unsigned>(n_records * a.group * (wide ? 4 : 1)));
+    if (device_sched) {
+        if (wide) hipExtLaunchKernelGGL(combine_kernel<true, 4>, grid, dim3(kCombineThreads), 0u, s, e0, e1, 0u, a);
+        else hipExtLaunchKernelGGL(combine_kernel<true, 1>, grid, dim3(kCombineThreads), 0u, s, e0, e1, 0u, a);
+    } else {
+        if (wide) hipExtLaunchKernelGGL(combine_kernel<false, 4>, grid, dim3(kCombineThreads), 0u, s, e0, e1, 0u, a);
+        else hipExtLaunchKernelGGL(combine_kernel<false, 1>, grid, dim3(kCombineThreads), 0u, s, e0, e1, 0u, a);
+    }
     return static_cast<int>(hipGetLastError());
 }
 
