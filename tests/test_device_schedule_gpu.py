@@ -124,6 +124,8 @@ def test_step_equals_host_planned(cfg, W):
     ([0, 0, 0], 8, 1, 4), ([0, 37, 0, 1], 8, 1, 3), ([1] * 9, 8, 1, 4),
     ([63, 64, 65, 127, 128, 129], 8, 1, 5), ([500, 30], 16, 1, 6), ([300, 1000, 7], 12, 3, 11),
     ([4000, 17], 64, 8, 64), ([2] * 700, 8, 1, 256),
+    # 64 sequences (schedule held in registers) and 65 (schedule in LDS), many of them empty
+    ([0, 5, 0, 130] * 16, 8, 1, 40), ([0, 5, 0, 130] * 16 + [64], 8, 1, 40), ([64] * 64, 16, 2, 300),
 ])
 def test_step_edge_shapes(lens, hq, hkv, W):
     inp = make_inputs(lens, hq, hkv, "bf16", seed=len(lens) + hq, poison=True)
