@@ -104,9 +104,23 @@ def cpu_baseline(inp, alg_bytes: int):
         decode_attention(*args, **kw)
         times.append(time.perf_counter() - t0)
     med = statistics.median(times)
-    return {"value": alg_bytes / med / 1e12, "unit": "TB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"whole workload, {len(times)} runs of the float64 oracle, median {med:.3f} s/step",
-            "s_per_step": med}
+    result = {"value": alg_bytes / med / 1e12, "unit": "TB/s", "cores": int(threads), "kind": "oracle",
+              "sample": f"whole workload, {len(times)} runs of the float64 oracle, median {med:.3f} s/step",
+              "s_per_step": med}
+    try:   # the same oracle held to one BLAS thread
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            one = []
+            t_start = time.perf_counter()
+            while len(one) < 3 and (time.perf_counter() - t_start < 20.0 or not one):
+                t0 = time.perf_counter()
+                decode_attention(*args, **kw)
+                one.append(time.perf_counter() - t0)
+        m1 = statistics.median(one)
+        result["single_thread"] = {"value": alg_bytes / m1 / 1e12, "s_per_step": m1, "runs": len(one)}
+    except ImportError:
+        pass
+    return result
 
 
 def main() -> int:
