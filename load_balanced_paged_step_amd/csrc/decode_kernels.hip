@@ -267,7 +267,7 @@ __device__ __forceinline__ void fetch_args(A& a, B& b, C& c, D& d) {
     asm("" : "+s"(a), "+s"(b), "+s"(c), "+s"(d));
 }
 
-template <int KV, int PF, int NT, bool DEV, bool AHEAD>
+template <int KV, int PF, int NT, bool DEV>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     const __bf16* __restrict__ q, const char* __restrict__ kcache, const char* __restrict__ vcache,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
@@ -329,10 +329,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
 
     // Filling a ring slot: `plan_tile` takes the next tile of the worker and
     // starts the scalar load of its page id; `load_tile` issues the K/V (and,
-    // for an entry's first tile, Q) loads.  With AHEAD, every slot's
-    // following tile is planned one full ring turn before it is loaded, so
-    // the page-id load never delays the K/V loads (measured no faster:
-    // off by default).
+    // for an entry's first tile, Q) loads.
     auto plan_tile = [&](TileInfo& s) {
         TileRef r;
         bool ok;
@@ -406,21 +403,17 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     };
 
     TileSlot<KV, NT> ring[PF];
-    TileInfo ahead[PF];   // the tile each slot loads next
+    TileInfo planned[PF];   // the tile each slot loads next
 #pragma unroll
-    for (int j = 0; j < PF; ++j) plan_tile(ahead[j]);
+    for (int j = 0; j < PF; ++j) plan_tile(planned[j]);
     // Slots are issued in ring order, each slot's Q before its K/V: the
     // loop's first wait (for slot 0) must leave the later slots in flight on
     // the path that enters the loop too, so the scheduler may not reorder
     // these loads across slots.
 #pragma unroll
     for (int j = 0; j < PF; ++j) {
-        load_tile(ring[j], ahead[j]);
+        load_tile(ring[j], planned[j]);
         __builtin_amdgcn_sched_barrier(0);
-    }
-    if constexpr (AHEAD) {
-#pragma unroll
-        for (int j = 0; j < PF; ++j) plan_tile(ahead[j]);
     }
 
     // Device schedule, while the first tiles are in flight: empty sequences
@@ -610,13 +603,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
         for (int j = 0; j < PF; ++j) {
             consume(ring[j]);
             const TileInfo ended = ring[j].info;
-            if constexpr (AHEAD) {
-                load_tile(ring[j], ahead[j]);
-                plan_tile(ahead[j]);
-            } else {
-                plan_tile(ahead[j]);
-                load_tile(ring[j], ahead[j]);
-            }
+            plan_tile(planned[j]);
+            load_tile(ring[j], planned[j]);
             if (ended.last()) flush(ended);
         }
         if (!ring[0].info.real()) break;
@@ -874,27 +862,19 @@ __global__ __launch_bounds__(kPlanThreads) void plan_device_kernel(const int32_t
 #ifndef HPC_DECODE_PREFETCH_FP8
 #define HPC_DECODE_PREFETCH_FP8 2
 #endif
-// fp8 tiles: plan every slot's next tile one ring turn ahead (see load_tile).
-// Off: with it, or with more than two slots, the compiler's load-counter
-// waits at the loop head drain the whole ring once per turn, which measured
-// slower than a clean two-slot ring.
 // fp8: two tiles of an entry per ring slot (a slot then holds as many bytes as a bf16 tile)
 #ifndef HPC_DECODE_PAIR_FP8
 #define HPC_DECODE_PAIR_FP8 1
-#endif
-#ifndef HPC_DECODE_AHEAD_FP8
-#define HPC_DECODE_AHEAD_FP8 0
 #endif
 constexpr int kPrefetchBf16 = HPC_DECODE_PREFETCH_BF16;
 constexpr int kPrefetchFp8 = HPC_DECODE_PREFETCH_FP8;
 
 template <int KV, int PF, bool DEV>
 void launch_decode_t(const DecodeArgs& a, int n_workers, size_t lds, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-    constexpr bool kAhead = KV == HPC_KV_FP8_E4M3 ? HPC_DECODE_AHEAD_FP8 != 0 : false;
     const DecodeScalars sc{a.batch,        a.num_kv_heads,  a.group,   a.max_pages_per_seq, a.num_pages,
                            a.max_partials, a.qk_scale_log2, a.v_scale, n_workers};
     constexpr int kTilesPerSlot = KV == HPC_KV_FP8_E4M3 ? HPC_DECODE_PAIR_FP8 + 1 : 1;
-    hipExtLaunchKernelGGL((decode_kernel<KV, PF, kTilesPerSlot, DEV, kAhead>), dim3(n_workers), dim3(kDecodeThreads),
+    hipExtLaunchKernelGGL((decode_kernel<KV, PF, kTilesPerSlot, DEV>), dim3(n_workers), dim3(kDecodeThreads),
                           static_cast<std::uint32_t>(lds), s, e0, e1, 0u,
                           static_cast<const __bf16*>(a.q), static_cast<const char*>(a.k),
                           static_cast<const char*>(a.v), a.block_table, a.seq_lens, a.worker_ptr, a.entries,

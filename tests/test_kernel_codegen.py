@@ -74,7 +74,7 @@ def ring_waits(tmp_path_factory):
 
 
 def _device_scheduled(name: str) -> bool:
-    # decode_kernel<int..., DEV, AHEAD>: the first bool template argument
+    # decode_kernel<int KV, int PF, int NT, bool DEV>
     return re.search(r"decode_kernelI(?:Li\d+E)+Lb1E", name) is not None
 
 
