@@ -86,6 +86,26 @@ def parse_args():
     return ap.parse_args()
 
 
+def native_planner_us(seq_lens, num_kv_heads: int, n_workers: int, calls: int = 200) -> float:
+    """Mean time of one hpc_decode_plan call into a preallocated buffer, as
+    hpc_decode_plan_attn makes it (no Python-side argument conversion)."""
+    import ctypes
+    import numpy as np
+    import load_balanced_paged_step_amd as hd
+    from load_balanced_paged_step_amd import _lib
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    lens = np.ascontiguousarray(seq_lens, dtype=np.int32).reshape(-1)
+    cap = hd.hpc_decode_plan_size(lens.shape[0], num_kv_heads, n_workers)
+    buf = np.empty(cap, dtype=np.int32)
+    fn = _lib.lib().hpc_decode_plan
+    lp, bp, B = lens.ctypes.data_as(i32p), buf.ctypes.data_as(i32p), lens.shape[0]
+    _lib.check(fn(lp, B, num_kv_heads, n_workers, bp, cap), "hpc_decode_plan")
+    t0 = time.perf_counter()
+    for _ in range(calls):
+        fn(lp, B, num_kv_heads, n_workers, bp, cap)
+    return (time.perf_counter() - t0) / calls * 1e6
+
+
 def cpu_baseline(inp, alg_bytes: int):
     """The float64 oracle on the host cores, over the same workload (median of repeated runs)."""
     from oracle import decode_attention
@@ -200,11 +220,10 @@ def main() -> int:
         one_step(i)
     torch.cuda.synchronize()
 
-    # host planner cost alone (part of every step; overlaps the previous step's kernels)
-    t0 = time.perf_counter()
-    for _ in range(200):
-        hd.hpc_decode_plan(lens_host, inp.num_kv_heads, W)
-    plan_us = (time.perf_counter() - t0) / 200 * 1e6
+    # the native host planner alone, called as the one-call host step calls it
+    # (preallocated buffers; part of every --schedule host step, overlapping
+    # the previous step's kernels)
+    plan_us = native_planner_us(lens_host, inp.num_kv_heads, W, calls=200)
 
     # timed region: K whole steps, bracketed by device synchronisation
     log(f"timed region: {args.steps} steps")
