@@ -72,6 +72,8 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=4, help="workload number (1-5); 4 = 1x128K+31x4K")
     ap.add_argument("--n-workers", type=int, default=0, help="persistent workgroups (0: one per CU)")
+    ap.add_argument("--plan-in-place", action="store_true",
+                    help="--schedule host: the kernels read the plan from the pinned host buffer (no upload)")
     ap.add_argument("--copies", type=int, default=0, help="rotating KV copies (0: enough for >= 1 GiB)")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--probe", action="store_true", help="also measure the HBM streaming-read ceiling")
@@ -209,7 +211,8 @@ def main() -> int:
         ws = torch.empty(hd.hpc_decode_plan_workspace_bound(inp.batch, inp.num_q_heads, inp.num_kv_heads, W),
                          dtype=torch.uint8, device=dev)
         planned = [hd.PlannedStepLauncher(q, ks[c], vs[c], bt, sl, out, lse, num_kv_heads=inp.num_kv_heads,
-                                          n_workers=W, workspace=ws, **scales) for c in range(copies)]
+                                          n_workers=W, workspace=ws, in_place=args.plan_in_place, **scales)
+                   for c in range(copies)]
         lens_np = np.ascontiguousarray(lens_host, dtype=np.int32)
 
         def one_step(i: int) -> None:
@@ -273,7 +276,9 @@ def main() -> int:
             "workload": wl.name, "batch": inp.batch, "kv_lens": _lens_summary(lens_host),
             "num_q_heads": inp.num_q_heads, "num_kv_heads": inp.num_kv_heads, "head_dim": 128,
             "page_size": 64, "kv_dtype": inp.kv_dtype, "n_workers": W, "kv_copies": copies,
-            "algorithmic_bytes": alg_bytes, "schedule": args.schedule, "parallelism": "single GPU",
+            "algorithmic_bytes": alg_bytes,
+            "schedule": args.schedule + (", plan in place" if args.schedule == "host" and args.plan_in_place else ""),
+            "parallelism": "single GPU",
         },
         "kernels": {"decode_us": round(decode_us, 3), "merge_us": round(combine_us, 3),
                     "plan_host_us": round(plan_us, 2), "timed_calls": n_calls},

@@ -213,13 +213,18 @@ int64_t hpc_decode_plan_workspace_bound(int32_t batch, int32_t num_q_heads, int3
  *                the caller must not rewrite the buffer until that copy has
  *                executed on the stream (two buffers used in turn, each
  *                guarded by an event recorded after the call, suffice)
- * plan_dev       device buffer of at least as many words; must differ from
- *                plan_host; valid until the stream work completes
+ * plan_dev       device buffer of at least as many words, valid until the
+ *                stream work completes; or plan_host itself, when plan_host
+ *                is pinned memory mapped at the same address on the device
+ *                (hipHostMalloc, torch pin_memory): the kernels then read the
+ *                plan in place, over the host link, no copy is queued, and
+ *                the buffer must stay unchanged until the kernels have run.
+ *                Any other host pointer passed as plan_dev is HPC_ERR_INVALID
  * workspace      device, >= hpc_decode_workspace_size of the plan made here
  *                (hpc_decode_plan_workspace_bound is always enough)
  * Other arguments as for hpc_decode_attn.  Every check (planner arguments,
- * plan against params, workspace size) runs before the first HIP call; a
- * failed copy or launch returns HPC_ERR_HIP.
+ * plan against params, workspace size, the in-place pointer query) runs
+ * before anything is queued; a failed copy or launch returns HPC_ERR_HIP.
  */
 int hpc_decode_plan_attn(const hpc_decode_params* params, const int32_t* seq_lens_host, int32_t batch,
                          int32_t n_workers, int32_t* plan_host, int64_t plan_capacity, int32_t* plan_dev,

@@ -240,14 +240,16 @@ class PlannedStepLauncher:
     Each call plans the host lengths it is given into one of two pinned plan
     buffers, queues the plan's upload and launches the kernels, all in one
     ``hpc_decode_plan_attn`` call on the stream given at construction
-    (default: the current stream then).  An event recorded after each call
-    guards its buffer: the call after next waits for it before rewriting the
-    buffer.  Tensors must stay alive and unchanged in shape for the
-    launcher's lifetime; ``plan_host`` is the last call's plan words.
+    (default: the current stream then).  With ``in_place`` the kernels read
+    the plan from the pinned buffer itself and no upload is queued.  An
+    event recorded after each call guards its buffer: the call after next
+    waits for it before rewriting the buffer.  Tensors must stay alive and
+    unchanged in shape for the launcher's lifetime; ``plan_host`` is the last
+    call's plan words.
     """
 
     def __init__(self, q, k_cache, v_cache, block_table, seq_lens, out, lse, *, num_kv_heads, n_workers,
-                 sm_scale, k_scale=1.0, v_scale=1.0, workspace=None, stream=None):
+                 sm_scale, k_scale=1.0, v_scale=1.0, workspace=None, stream=None, in_place=False):
         B = q.shape[0]
         if workspace is None:
             need = hpc_decode_plan_workspace_bound(B, q.shape[1], num_kv_heads, n_workers)
@@ -268,7 +270,9 @@ class PlannedStepLauncher:
         self._last = None
         self._fn = lib().hpc_decode_plan_attn
         self._pre = (ctypes.byref(self.params),)
-        self._post = (ctypes.c_void_p(self.plan_dev.data_ptr()),) + args[2:] + (_stream_handle(self._stream),)
+        self._post = args[2:] + (_stream_handle(self._stream),)
+        self._host_ptr = [h.ctypes.data for h in self._host_np]
+        self._dev_of = self._host_ptr if in_place else [self.plan_dev.data_ptr()] * 2
 
     def __call__(self, seq_lens_host) -> None:
         lens = seq_lens_host
@@ -282,7 +286,7 @@ class PlannedStepLauncher:
         if self._pending[i]:
             self._events[i].synchronize()          # this buffer's last upload has run
         status = self._fn(*self._pre, lens.ctypes.data, self.batch, self.n_workers,
-                          self._host_np[i].ctypes.data, self._cap, *self._post)
+                          self._host_ptr[i], self._cap, self._dev_of[i], *self._post)
         if status:
             _lib.check(status, "hpc_decode_plan_attn")
         self._events[i].record(self._stream)

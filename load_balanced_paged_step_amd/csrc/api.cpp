@@ -178,7 +178,6 @@ extern "C" int hpc_decode_plan_attn(const hpc_decode_params* p, const int32_t* s
                                     const int32_t* block_table, const int32_t* seq_lens, void* workspace,
                                     int64_t workspace_bytes, void* out, float* lse, void* stream) {
     if (!p || !plan_host || !plan_dev) return HPC_ERR_NULL;
-    if (static_cast<const void*>(plan_dev) == static_cast<const void*>(plan_host)) return HPC_ERR_INVALID;
     int status = hpc_decode_plan(seq_lens_host, batch, p->num_kv_heads, n_workers, plan_host, plan_capacity);
     if (status != HPC_OK) return status;
     status = hpc_decode_check(p, q, k_cache, v_cache, block_table, seq_lens, plan_host, plan_dev, workspace,
@@ -186,9 +185,19 @@ extern "C" int hpc_decode_plan_attn(const hpc_decode_params* p, const int32_t* s
     if (status != HPC_OK) return status;
     const int64_t words = hpc_decode_plan_words(plan_host);
     if (words < 0) return static_cast<int>(words);
-    if (hipMemcpyAsync(plan_dev, plan_host, static_cast<size_t>(words) * sizeof(int32_t), hipMemcpyHostToDevice,
-                       static_cast<hipStream_t>(stream)) != hipSuccess)
+    if (static_cast<const void*>(plan_dev) == static_cast<const void*>(plan_host)) {
+        // in place: the kernels read the plan from the caller's pinned host
+        // buffer, which must be mapped at the same address on the device
+        hipPointerAttribute_t attr{};
+        if (hipPointerGetAttributes(&attr, plan_host) != hipSuccess || attr.type != hipMemoryTypeHost ||
+            attr.devicePointer != static_cast<void*>(plan_host)) {
+            (void)hipGetLastError();
+            return HPC_ERR_INVALID;
+        }
+    } else if (hipMemcpyAsync(plan_dev, plan_host, static_cast<size_t>(words) * sizeof(int32_t),
+                              hipMemcpyHostToDevice, static_cast<hipStream_t>(stream)) != hipSuccess) {
         return HPC_ERR_HIP;
+    }
     return launch_planned(p, q, k_cache, v_cache, block_table, seq_lens, plan_host, plan_dev, workspace, out,
                           lse, stream);
 }

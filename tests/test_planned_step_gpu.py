@@ -1,5 +1,7 @@
 """GPU tests of the one-call host-planned step (hpc_decode_plan_attn): the
 native planner, the queued plan upload and the kernels in one C call."""
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -43,22 +45,24 @@ def test_plan_attn_equals_attn(lens, hq, hkv, W, kv):
     compare(inp, got, run_oracle(inp), "plan_attn")
 
 
-def test_launcher_runs_ahead_over_changing_lengths():
+@pytest.mark.parametrize("in_place", [False, True])
+def test_launcher_runs_ahead_over_changing_lengths(in_place):
     """Steps queued back to back with no host synchronisation, each with other
     lengths: the two pinned plan buffers are reused in turn while earlier
-    uploads may still be queued, and every step still matches the oracle."""
+    uploads (or, in place, earlier kernels reading them) may still be queued,
+    and every step still matches the oracle."""
     base = make_inputs([7000, 300, 65, 4000], 16, 2, "bf16", seed=23, max_pages_per_seq=130)
     dev = to_device(base)
     out = torch.empty_like(dev["q"])
     lse = torch.empty(dev["q"].shape[:2], dtype=torch.float32, device="cuda")
     sl = dev["sl"]
     launch = hd.PlannedStepLauncher(dev["q"], dev["k"], dev["v"], dev["bt"], sl, out, lse, num_kv_heads=2,
-                                    n_workers=64, sm_scale=base.sm_scale)
+                                    n_workers=64, sm_scale=base.sm_scale, in_place=in_place)
     steps = ([7000, 300, 65, 4000], [7001, 0, 66, 4100], [8000, 1, 64, 8300], [100, 200, 300, 400],
              [0, 0, 0, 0], [64, 8320, 1, 5], [7000, 300, 65, 4000])
     lens_dev = [torch.tensor(x, dtype=torch.int32).pin_memory() for x in steps]
     results = []
-    announce(f"planned launcher, {len(steps)} steps queued")
+    announce(f"planned launcher (in place: {in_place}), {len(steps)} steps queued")
     for x, xd in zip(steps, lens_dev):
         sl.copy_(xd, non_blocking=True)
         launch(np.asarray(x, dtype=np.int32))
@@ -84,3 +88,34 @@ def test_launcher_rejects_wrong_batch():
     launch(inp.seq_lens.numpy())
     torch.cuda.synchronize()
     compare(inp, _np(out, lse), run_oracle(inp), "after rejected calls")
+
+
+def test_plan_in_place_equals_copied_plan():
+    """The kernels reading the plan from pinned host memory give bitwise the
+    result of the uploaded plan; a host pointer that is not pinned is refused."""
+    inp = make_inputs([7000, 300, 0, 4000, 129], 16, 2, "bf16", seed=31, poison=True)
+    announce("plan read in place from pinned memory")
+    dev = to_device(inp)
+    cap = hd.hpc_decode_plan_size(inp.batch, 2, 48)
+    ws = torch.empty(hd.hpc_decode_plan_workspace_bound(inp.batch, 16, 2, 48), dtype=torch.uint8, device="cuda")
+    res = []
+    for in_place in (False, True):
+        out = torch.empty_like(dev["q"])
+        lse = torch.empty(dev["q"].shape[:2], dtype=torch.float32, device="cuda")
+        host = torch.zeros(cap, dtype=torch.int32, pin_memory=True)
+        plan_dev = host if in_place else torch.empty(cap, dtype=torch.int32, device="cuda")
+        params, args = hd._step_args(dev["q"], dev["k"], dev["v"], dev["bt"], dev["sl"], ws, out, lse, 2, 48,
+                                     inp.sm_scale, 1.0, 1.0)
+        lens = inp.seq_lens.numpy().astype(np.int32)
+        st = hd.lib().hpc_decode_plan_attn(ctypes.byref(params), lens.ctypes.data, inp.batch, 48,
+                                           host.data_ptr(), cap, plan_dev.data_ptr(), *args[2:],
+                                           hd._stream_handle(None))
+        assert st == 0, hd.hpc_status_string(st)
+        torch.cuda.synchronize()
+        res.append(_np(out, lse))
+    assert np.array_equal(res[0][0], res[1][0]) and np.array_equal(res[0][1], res[1][1])
+    compare(inp, res[1], run_oracle(inp), "plan in place")
+    pageable = np.zeros(cap, dtype=np.int32)
+    st = hd.lib().hpc_decode_plan_attn(ctypes.byref(params), lens.ctypes.data, inp.batch, 48, pageable.ctypes.data,
+                                       cap, pageable.ctypes.data, *args[2:], hd._stream_handle(None))
+    assert st == hd.HPC_ERR_INVALID
