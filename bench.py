@@ -356,7 +356,7 @@ def skew_sweep(dev, W: int, cus: int, steps: int, warmup: int) -> dict:
         scales = dict(sm_scale=inp.sm_scale, k_scale=inp.k_scale, v_scale=inp.v_scale)
 
         def kernel_us(one_step) -> float:
-            for i in range(warmup):
+            for i in range(max(warmup, 20)):   # small batches: let clocks and caches settle
                 one_step(i)
             torch.cuda.synchronize()
             hd.hpc_decode_profile_start(steps)
