@@ -18,9 +18,15 @@
 //  * every wave owns a fixed 16-token slice (rows 16*wave .. +15) of every
 //    64-token tile and keeps its own online-softmax state; at the end of an
 //    entry the four states meet in LDS and one result per entry is written;
-//  * a ring of PF tile slots is kept in flight across entry boundaries: each
-//    slot holds its K/V rows, and for the first tile of an entry also that
-//    entry's Q, so changing sequence never drains the load pipeline;
+//  * a ring of PF = 2 slots is kept in flight across entry boundaries: each
+//    slot holds the K/V rows of one tile (bf16) or of two consecutive tiles
+//    of one entry (fp8, so a slot holds as many bytes either way), and for
+//    an entry's first tile also that entry's Q, so changing sequence never
+//    drains the load pipeline; the loop leaves only at the end of a full
+//    ring turn, and a slot that ends an entry is refilled before the entry
+//    is flushed;
+//  * with the device schedule, each unit's merge record is written in the
+//    prologue by the worker holding the unit's first tile;
 //  * K, V and Q are read with buffer loads whose range is the valid part of
 //    the page (rows past a sequence's end, padding heads and ring slots past
 //    the worker's last tile read as zeros without touching memory); K/V use
@@ -30,9 +36,13 @@
 //    registers by byte permutes (each lane holds 4 token rows x 8 dims);
 //  * fp8 tiles are widened to bf16 exactly (every E4M3FN value is a bf16
 //    value); k_scale folds into the score scale, v_scale into the output.
+// Merge kernel: SPLIT workgroups per (split unit, query head), SPLIT = 4
+// for small grids (a unit shared by many workers is read by several CUs),
+// 1 for many units.
 // Lane layout: lane = n + 16 g (n = lane & 15, g = lane >> 4).
-//   QK:  A = K rows [token n][dims 32kk+8g .. +8], B = Q^T [head n][same dims],
-//        D[token 4g+i][head n] in register i.
+//   QK:  A = K rows [token n][8 dims per k-step, in the order KvTile loads
+//        them], B = Q^T [head n][the same dims], D[token 4g+i][head n] in
+//        register i.
 //   PV:  A = V^T [dim 8n+nb][tokens 4g .. 4g+3], B = P^T [tokens 4g+i][head n],
 //        D[dim 8(4g+i)+nb][head n] in register i of accumulator nb.
 
