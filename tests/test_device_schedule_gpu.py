@@ -168,3 +168,21 @@ def test_repeated_device_steps_with_changing_splits():
         base.seq_lens = torch.tensor(lens, dtype=torch.int32)
         got = (out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64))
         compare(base, got, run_oracle(base), f"step {i}")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
+@pytest.mark.parametrize("G", [1, 2, 3, 5, 7, 16])
+def test_group_sizes_both_schedules(G, kv):
+    """Every GQA group size up to the largest supported, ragged and empty
+    sequences, two KV heads: both schedules against the oracle, and against
+    each other."""
+    lens = [700, 0, 65, 3000, 1]
+    inp = make_inputs(lens, 2 * G, 2, kv, seed=100 + G, poison=True)
+    announce(f"group size G={G} {kv}")
+    dev = to_device(inp)
+    a = run_step(inp, 13, dev)
+    b = run_hip(inp, 13, dev)
+    assert_same_as_host_planned(inp, 13, a, b)
+    ref = run_oracle(inp)
+    compare(inp, a, ref, f"device step G={G} {kv}")
+    compare(inp, b, ref, f"host plan G={G} {kv}")
