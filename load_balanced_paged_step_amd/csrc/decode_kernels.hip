@@ -633,7 +633,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
 // host plan's merge list, or, for the device-scheduled step, one record per
 // unit written by the decode kernel.
 constexpr int kMergeUnroll = 8;
-constexpr int kMergeGridBudget = 2048;   // largest grid the 4-way split may take
+constexpr int kMergeGridBudget = 1024;   // largest grid the 4-way split may take (4 per CU)
 
 template <bool DEV, int SPLIT>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a) {
