@@ -186,3 +186,35 @@ def test_group_sizes_both_schedules(G, kv):
     ref = run_oracle(inp)
     compare(inp, a, ref, f"device step G={G} {kv}")
     compare(inp, b, ref, f"host plan G={G} {kv}")
+
+
+def _random_case(seed):
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 81))
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    G = int(rng.integers(1, 17))
+    kind = rng.random(B)
+    lens = np.where(kind < 0.15, 0,
+                    np.where(kind < 0.3, rng.choice([1, 63, 64, 65, 127, 128, 129], B),
+                             rng.integers(1, 4000, B))).astype(int)
+    if B * hkv * 64 > 6000:           # keep the oracle quick: shorten big batches
+        lens = np.minimum(lens, 600)
+    W = int(rng.choice([1, 3, 17, 64, 256, 333, 600]))
+    kv = "fp8_e4m3" if rng.random() < 0.4 else "bf16"
+    return [int(x) for x in lens], G * hkv, hkv, W, kv
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_batches_both_schedules(seed):
+    """Seeded random batches: sizes, lengths (zeros and page-boundary values
+    included), group sizes, KV head counts, worker counts and KV types."""
+    lens, hq, hkv, W, kv = _random_case(1000 + seed)
+    announce(f"random batch seed={seed} B={len(lens)} hq={hq} hkv={hkv} W={W} {kv} lens[:6]={lens[:6]}")
+    inp = make_inputs(lens, hq, hkv, kv, seed=2000 + seed, poison=True)
+    dev = to_device(inp)
+    a = run_step(inp, W, dev)
+    b = run_hip(inp, W, dev)
+    assert_same_as_host_planned(inp, W, a, b)
+    ref = run_oracle(inp)
+    compare(inp, a, ref, f"random device step seed={seed}")
+    compare(inp, b, ref, f"random host plan seed={seed}")
