@@ -308,7 +308,25 @@ def main() -> int:
             gbps = nbytes * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
             best = max(best, gbps)
             log(f"read probe, {nwg} workgroups: {gbps:.0f} GB/s")
-        result["probe"] = {"read_GBps": round(best, 1), "bytes": nbytes}
+        # the same bytes as one decode step: a plain streaming read of exactly
+        # the algorithmic bytes, rotating over disjoint chunks of the buffer
+        # as the steps rotate over KV copies; each launch timed from its
+        # dispatch to its end, like the decode kernel above
+        n_same = min(alg_bytes, nbytes) // 16 * 16
+        chunks = max(1, nbytes // n_same)
+        same = {}
+        for nwg in (cus, cus * 2, cus * 4):
+            ts = []
+            for i in range(40):
+                c = i % chunks
+                t = hd.hpc_probe_read_timed(buf[c * n_same:(c + 1) * n_same], sink, nwg)
+                if i >= 10:
+                    ts.append(t * 1e3)
+            same[str(nwg)] = round(float(np.median(ts)), 3)
+            log(f"read probe over {n_same} bytes, {nwg} workgroups: {same[str(nwg)]:.2f} us")
+        result["probe"] = {"read_GBps": round(best, 1), "bytes": nbytes,
+                           "same_bytes_us": same, "same_bytes": n_same,
+                           "same_bytes_GBps": round(n_same / (min(same.values()) * 1e-6) / 1e9, 1)}
 
     if args.cpu_baseline == "on":
         log("timing the float64 oracle on the host (cpu_baseline)")

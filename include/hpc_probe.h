@@ -23,6 +23,15 @@ extern "C" {
  * elided).  HPC_ERR_NULL / HPC_ERR_INVALID on bad arguments. */
 int hpc_probe_read(const void* buf, int64_t bytes, float* sink, int32_t n_workgroups, void* stream);
 
+/* As hpc_probe_read, then waits for that launch to finish and stores in *ms
+ * its duration in milliseconds, from the kernel's dispatch to its end (HIP
+ * events stamped by the launch itself, so host launch overhead is excluded).
+ * Synchronous: returns only after the kernel has finished.  HPC_ERR_NULL /
+ * HPC_ERR_INVALID on bad arguments, HPC_ERR_HIP if the launch or an event
+ * call fails. */
+int hpc_probe_read_timed(const void* buf, int64_t bytes, float* sink, int32_t n_workgroups, void* stream,
+                         float* ms);
+
 /* Copy `bytes` (a positive multiple of 16) from device `src` to device `dst`
  * (non-overlapping) with 16-byte accesses.  HPC_ERR_NULL / HPC_ERR_INVALID on
  * bad arguments. */

@@ -28,7 +28,7 @@ __all__ = [
     "hpc_decode_static_splits",
     "hpc_decode_plan_words", "hpc_decode_workspace_size",
     "hpc_decode_check", "hpc_decode_attn", "hpc_status_string", "hpc_decode_profile_start",
-    "hpc_decode_profile_stop", "hpc_probe_read", "hpc_probe_copy", "hpc_decode_step",
+    "hpc_decode_profile_stop", "hpc_probe_read", "hpc_probe_read_timed", "hpc_probe_copy", "hpc_decode_step",
     "hpc_decode_step_check", "hpc_decode_step_workspace_size", "hpc_decode_plan_device", "StepLauncher",
     "hpc_decode_plan_workspace_bound", "hpc_decode_plan_attn", "PlannedStepLauncher",
     "DecodeStep", "HpcDecodeError",
@@ -413,6 +413,17 @@ def hpc_probe_read(buf: torch.Tensor, sink: torch.Tensor, n_workgroups: int, str
         raise ValueError("sink must hold n_workgroups float32 values")
     _lib.check(lib().hpc_probe_read(_dev_ptr(buf, "buf"), nbytes, _dev_ptr(sink, "sink"), n_workgroups,
                                     _stream_handle(stream)), "hpc_probe_read")
+
+
+def hpc_probe_read_timed(buf: torch.Tensor, sink: torch.Tensor, n_workgroups: int, stream=None) -> float:
+    """One read-probe launch over `buf`; returns its dispatch-to-end duration in ms (synchronous)."""
+    nbytes = buf.numel() * buf.element_size()
+    if sink.numel() < n_workgroups or sink.dtype != torch.float32:
+        raise ValueError("sink must hold n_workgroups float32 values")
+    ms = ctypes.c_float()
+    _lib.check(lib().hpc_probe_read_timed(_dev_ptr(buf, "buf"), nbytes, _dev_ptr(sink, "sink"), n_workgroups,
+                                          _stream_handle(stream), ctypes.byref(ms)), "hpc_probe_read_timed")
+    return ms.value
 
 
 def hpc_probe_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:

@@ -82,6 +82,8 @@ SIGNATURES = {
     "hpc_decode_profile_start": (ctypes.c_int, [ctypes.c_int32]),
     "hpc_decode_profile_stop": (ctypes.c_int, [_F64P, _F64P, _I32P]),
     "hpc_probe_read": (ctypes.c_int, [_VP, ctypes.c_int64, _VP, ctypes.c_int32, _VP]),
+    "hpc_probe_read_timed": (ctypes.c_int, [_VP, ctypes.c_int64, _VP, ctypes.c_int32, _VP,
+                                            ctypes.POINTER(ctypes.c_float)]),
     "hpc_probe_copy": (ctypes.c_int, [_VP, _VP, ctypes.c_int64, _VP]),
 }
 

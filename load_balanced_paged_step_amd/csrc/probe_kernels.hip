@@ -2,6 +2,7 @@
 // and a plain 16-byte copy.  Every access is within [0, bytes) of the
 // caller's buffers.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -58,6 +59,28 @@ extern "C" int hpc_probe_read(const void* buf, int64_t bytes, float* sink, int32
     hipLaunchKernelGGL(read_probe_kernel, dim3(n_workgroups), dim3(256), 0, static_cast<hipStream_t>(stream),
                        static_cast<const u32x4*>(buf), bytes / 16, sink);
     return hipGetLastError() == hipSuccess ? HPC_OK : HPC_ERR_HIP;
+}
+
+extern "C" int hpc_probe_read_timed(const void* buf, int64_t bytes, float* sink, int32_t n_workgroups, void* stream,
+                                    float* ms) {
+    if (!buf || !sink || !ms) return HPC_ERR_NULL;
+    if (bytes <= 0 || bytes % 16 != 0 || n_workgroups < 1) return HPC_ERR_INVALID;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (hipEventCreate(&e0) != hipSuccess) return HPC_ERR_HIP;
+    if (hipEventCreate(&e1) != hipSuccess) {
+        (void)hipEventDestroy(e0);
+        return HPC_ERR_HIP;
+    }
+    // the events are stamped when the kernel is dispatched and when it ends,
+    // as for the decode library's own kernel timings
+    hipExtLaunchKernelGGL(read_probe_kernel, dim3(n_workgroups), dim3(256), 0, static_cast<hipStream_t>(stream), e0, e1,
+                          0u, static_cast<const u32x4*>(buf), bytes / 16, sink);
+    int status = hipGetLastError() == hipSuccess ? HPC_OK : HPC_ERR_HIP;
+    if (status == HPC_OK && (hipEventSynchronize(e1) != hipSuccess || hipEventElapsedTime(ms, e0, e1) != hipSuccess))
+        status = HPC_ERR_HIP;
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    return status;
 }
 
 extern "C" int hpc_probe_copy(const void* src, void* dst, int64_t bytes, void* stream) {

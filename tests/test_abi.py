@@ -308,3 +308,21 @@ def test_plan_attn_errors_before_any_hip_call():
     assert call(lens_p=bad.ctypes.data) == hd.HPC_ERR_INVALID
     # the planner wrote the plan of the last lengths before the check failed
     assert np.array_equal(host[:hd.hpc_decode_plan_words(host)], _cpp_plan(bad, H, W))
+
+
+def test_probe_argument_errors_before_any_hip_call():
+    """The measurement probes reject bad arguments on the host, before any launch."""
+    lib = _lib.lib()
+    ptr = 0x1000
+    ms = ctypes.c_float()
+    assert lib.hpc_probe_read(None, 1024, ptr, 4, None) == hd.HPC_ERR_NULL
+    assert lib.hpc_probe_read(ptr, 1024, None, 4, None) == hd.HPC_ERR_NULL
+    assert lib.hpc_probe_read(ptr, 1000, ptr, 4, None) == hd.HPC_ERR_INVALID     # not a multiple of 16
+    assert lib.hpc_probe_read(ptr, 0, ptr, 4, None) == hd.HPC_ERR_INVALID
+    assert lib.hpc_probe_read(ptr, 1024, ptr, 0, None) == hd.HPC_ERR_INVALID
+    assert lib.hpc_probe_read_timed(ptr, 1024, ptr, 4, None, None) == hd.HPC_ERR_NULL
+    assert lib.hpc_probe_read_timed(None, 1024, ptr, 4, None, ctypes.byref(ms)) == hd.HPC_ERR_NULL
+    assert lib.hpc_probe_read_timed(ptr, 1008 + 8, ptr, 4, None, ctypes.byref(ms)) == hd.HPC_ERR_INVALID
+    assert lib.hpc_probe_read_timed(ptr, 1024, ptr, -1, None, ctypes.byref(ms)) == hd.HPC_ERR_INVALID
+    assert lib.hpc_probe_copy(None, ptr, 1024, None) == hd.HPC_ERR_NULL
+    assert lib.hpc_probe_copy(ptr, ptr, -16, None) == hd.HPC_ERR_INVALID
