@@ -5,9 +5,12 @@ against the host planner and the oracle.
   word (every tile covered once, same entries, slots and merge records);
 * a device-scheduled step matches the host-planned step: bitwise for every
   sequence that one worker finishes alone (same schedule, same arithmetic),
-  and to fp32 rounding for split sequences, whose merge runs in the decode
-  kernel (groups of 16 partials folded in order) instead of the separate
-  merge kernel (32 lanes reduced in LDS); both match the float64 oracle.
+  and to fp32 rounding for split sequences, whose partials the merge kernel
+  may fold in another order (its grid, and so the lanes that take each
+  partial, is sized from the number of merge records, which differs between
+  the two schedules); both match the float64 oracle;
+* both hold at the device schedule's limits (2048 sequences, 4096 units,
+  65536 workers).
 """
 import numpy as np
 import pytest
@@ -81,8 +84,9 @@ def test_device_plan_of_fp8_workload():
         assert np.array_equal(_device_plan(lens, 8, W), build_plan(lens, 8, W))
 
 
-def assert_same_as_host_planned(inp, W, a, b):
-    plan = build_plan(inp.seq_lens.numpy(), inp.num_kv_heads, W)
+def assert_same_as_host_planned(inp, W, a, b, plan=None):
+    if plan is None:
+        plan = build_plan(inp.seq_lens.numpy(), inp.num_kv_heads, W)
     hdr_W, E = int(plan[3]), int(plan[5])
     ents = plan[16 + hdr_W + 1:16 + hdr_W + 1 + 4 * E].reshape(E, 4)
     G = inp.num_q_heads // inp.num_kv_heads
@@ -124,7 +128,7 @@ def test_step_equals_host_planned(cfg, W):
     ([0, 0, 0], 8, 1, 4), ([0, 37, 0, 1], 8, 1, 3), ([1] * 9, 8, 1, 4),
     ([63, 64, 65, 127, 128, 129], 8, 1, 5), ([500, 30], 16, 1, 6), ([300, 1000, 7], 12, 3, 11),
     ([4000, 17], 64, 8, 64), ([2] * 700, 8, 1, 256),
-    # 64 sequences (schedule held in registers) and 65 (schedule in LDS), many of them empty
+    # 64 and 65 sequences (one and two 64-lane rounds of the prefix scan), many of them empty
     ([0, 5, 0, 130] * 16, 8, 1, 40), ([0, 5, 0, 130] * 16 + [64], 8, 1, 40), ([64] * 64, 16, 2, 300),
 ])
 def test_step_edge_shapes(lens, hq, hkv, W):
@@ -218,3 +222,34 @@ def test_random_batches_both_schedules(seed):
     ref = run_oracle(inp)
     compare(inp, a, ref, f"random device step seed={seed}")
     compare(inp, b, ref, f"random host plan seed={seed}")
+
+
+def _limit_lengths():
+    rng = np.random.default_rng(2048)
+    lens = rng.integers(0, 300, size=2048)
+    lens[rng.random(2048) < 0.1] = 0
+    return lens
+
+
+def test_device_plan_at_its_limits():
+    """The plan-materialising kernel at its largest batch, units and workers."""
+    lens = _limit_lengths()
+    announce("device plan at the limits: B=2048 H=2 W=2048")
+    assert np.array_equal(_device_plan(lens, 2, 2048), build_plan(lens, 2, 2048))
+
+
+@pytest.mark.parametrize("W", [4099, 65536])
+def test_step_at_the_size_limits(W):
+    """The device-scheduled step at its largest batch (2048 sequences, 4096
+    units) and worker count (65536, far more workers than tiles) against the
+    host-planned step and the oracle.  The host plan here is the C++
+    planner's, which the CPU tests hold equal to the oracle's word for word
+    (the oracle's planner is too slow at 65536 workers)."""
+    lens = _limit_lengths()
+    inp = make_inputs(lens, 8, 2, "bf16", seed=7, poison=True)
+    announce(f"device step at the limits: B=2048 hq=8 hkv=2 W={W}")
+    dev = to_device(inp)
+    a = run_step(inp, W, dev)
+    b = run_hip(inp, W, dev)
+    assert_same_as_host_planned(inp, W, a, b, plan=hd.hpc_decode_plan(inp.seq_lens.numpy(), 2, W))
+    compare(inp, a, run_oracle(inp), f"device step at the limits W={W}")
