@@ -76,7 +76,8 @@ def parse_args():
                     help="--schedule host: the kernels read the plan from the pinned host buffer (no upload)")
     ap.add_argument("--copies", type=int, default=0, help="rotating KV copies (0: enough for >= 1 GiB)")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
-    ap.add_argument("--probe", action="store_true", help="also measure the HBM streaming-read ceiling")
+    ap.add_argument("--probe", choices=["on", "off"], nargs="?", const="on", default="on",
+                    help="also measure the HBM streaming-read ceiling and a plain read of the step's bytes")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run the plain copy kernel over MIB MiB (hardware-counter calibration) and exit")
     ap.add_argument("--skew-sweep", action="store_true",
@@ -289,7 +290,7 @@ def main() -> int:
                      "kernel_us_hip_events": round(decode_us, 3)},
     }
 
-    if args.probe:
+    if args.probe == "on":
         nbytes = 1 << 30
         buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         buf.fill_(1)
