@@ -83,6 +83,11 @@ def parse_args():
     ap.add_argument("--skew-sweep", action="store_true",
                     help="instead of the bench line: time the balanced schedule against static split-KV "
                          "schedules on batches from uniform 64x512 to 1x128K+31x4K, print one JSON line")
+    ap.add_argument("--tile-math", choices=["mfma", "valu"], default="mfma",
+                    help="tile arithmetic: matrix cores (default) or vector ALU dot2 products")
+    ap.add_argument("--tile-math-sweep", action="store_true",
+                    help="time the decode kernel with MFMA and with VALU tile math on workloads 2-5 "
+                         "(device schedule) and print one JSON line")
     ap.add_argument("--schedule", choices=["device", "host"], default="device",
                     help="device: kernels derive the per-step schedule from the lengths on the GPU; "
                          "host: C++ planner on the host + plan upload every step")
@@ -179,6 +184,9 @@ def main() -> int:
     if args.skew_sweep:
         print(json.dumps(skew_sweep(dev, W, cus, args.steps, args.warmup)), flush=True)
         return 0
+    if args.tile_math_sweep:
+        print(json.dumps(tile_math_sweep(dev, W, args.steps, args.warmup)), flush=True)
+        return 0
     wl = WORKLOADS[args.workload]
 
     log(f"building inputs for workload {args.workload} ({wl.name})")
@@ -204,7 +212,8 @@ def main() -> int:
         ws = torch.zeros(hd.hpc_decode_step_workspace_size(inp.batch, inp.num_q_heads, inp.num_kv_heads, W),
                          dtype=torch.uint8, device=dev)
         launchers = [hd.StepLauncher(q, ks[c], vs[c], bt, sl, out, lse, num_kv_heads=inp.num_kv_heads,
-                                     n_workers=W, workspace=ws, **scales) for c in range(copies)]
+                                     n_workers=W, workspace=ws, tile_math=args.tile_math, **scales)
+                     for c in range(copies)]
 
         def one_step(i: int) -> None:
             launchers[i % copies]()
@@ -212,7 +221,8 @@ def main() -> int:
         ws = torch.empty(hd.hpc_decode_plan_workspace_bound(inp.batch, inp.num_q_heads, inp.num_kv_heads, W),
                          dtype=torch.uint8, device=dev)
         planned = [hd.PlannedStepLauncher(q, ks[c], vs[c], bt, sl, out, lse, num_kv_heads=inp.num_kv_heads,
-                                          n_workers=W, workspace=ws, in_place=args.plan_in_place, **scales)
+                                          n_workers=W, workspace=ws, in_place=args.plan_in_place,
+                                          tile_math=args.tile_math, **scales)
                    for c in range(copies)]
         lens_np = np.ascontiguousarray(lens_host, dtype=np.int32)
 
@@ -271,7 +281,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": inp.kv_dtype if inp.kv_dtype == "bf16" else "fp8-e4m3 KV, bf16 MFMA",
+        "dtype": inp.kv_dtype if inp.kv_dtype == "bf16" else f"fp8-e4m3 KV, bf16 {args.tile_math.upper()}",
         "data": "synthetic (seeded N(0,1) Q/K/V, shuffled block table)",
         "config": {
             "workload": wl.name, "batch": inp.batch, "kv_lens": _lens_summary(lens_host),
@@ -279,13 +289,14 @@ def main() -> int:
             "page_size": 64, "kv_dtype": inp.kv_dtype, "n_workers": W, "kv_copies": copies,
             "algorithmic_bytes": alg_bytes,
             "schedule": args.schedule + (", plan in place" if args.schedule == "host" and args.plan_in_place else ""),
-            "parallelism": "single GPU",
+            "parallelism": "single GPU", "tile_math": args.tile_math,
         },
         "kernels": {"decode_us": round(decode_us, 3), "merge_us": round(combine_us, 3),
                     "plan_host_us": round(plan_us, 2), "timed_calls": n_calls},
         "roofline": {"bound": "hbm", "achieved": round(achieved_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic(wl.name, args.schedule, W),
+                     "traffic": (measured_traffic(wl.name, args.schedule, W)
+                                 if args.tile_math == "mfma" else None),
                      "kernel": "decode_kernel", "bytes_per_launch": alg_bytes,
                      "kernel_us_hip_events": round(decode_us, 3)},
     }
@@ -334,6 +345,65 @@ def main() -> int:
         result["cpu_baseline"] = cpu_baseline(inp, alg_bytes)
     print(json.dumps(result), flush=True)
     return 0
+
+
+def tile_math_sweep(dev, W: int, steps: int, warmup: int) -> dict:
+    """Decode-kernel time with the MFMA and with the VALU tile math, same
+    inputs, same device-scheduled step, alternating rounds of the two so
+    that clock or thermal drift hits both alike."""
+    import numpy as np
+    import torch
+
+    import load_balanced_paged_step_amd as hd
+    from workloads import WORKLOADS, workload_inputs
+
+    rows = []
+    for cfg in (2, 3, 4, 5):
+        inp = workload_inputs(cfg)
+        kv_bytes = inp.k_cache.numel() * inp.k_cache.element_size() * 2
+        copies = max(1, min(16, math.ceil((1 << 30) / kv_bytes)))
+        q, bt, sl = inp.q.to(dev), inp.block_table.to(dev), inp.seq_lens.to(dev)
+        k0, v0 = inp.k_cache.to(dev), inp.v_cache.to(dev)
+        ks = [k0] + [k0.clone() for _ in range(copies - 1)]
+        vs = [v0] + [v0.clone() for _ in range(copies - 1)]
+        out = torch.empty_like(q)
+        lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+        ws = torch.zeros(hd.hpc_decode_step_workspace_size(inp.batch, inp.num_q_heads, inp.num_kv_heads, W),
+                         dtype=torch.uint8, device=dev)
+        scales = dict(sm_scale=inp.sm_scale, k_scale=inp.k_scale, v_scale=inp.v_scale)
+        launch = {m: [hd.StepLauncher(q, ks[c], vs[c], bt, sl, out, lse, num_kv_heads=inp.num_kv_heads,
+                                      n_workers=W, workspace=ws, tile_math=m, **scales) for c in range(copies)]
+                  for m in ("mfma", "valu")}
+        alg = inp.algorithmic_bytes()
+        times = {"mfma": [], "valu": []}
+        for rnd in range(3):
+            for m in ("mfma", "valu"):
+                for i in range(warmup):
+                    launch[m][i % copies]()
+                torch.cuda.synchronize()
+                hd.hpc_decode_profile_start(steps)
+                for i in range(steps):
+                    launch[m][i % copies]()
+                torch.cuda.synchronize()
+                d_ms, c_ms, n = hd.hpc_decode_profile_stop()
+                times[m].append((d_ms / max(n, 1) * 1e3, c_ms / max(n, 1) * 1e3))
+        row = {"workload": WORKLOADS[cfg].name, "kv_dtype": inp.kv_dtype,
+               "heads": f"{inp.num_q_heads}q/{inp.num_kv_heads}kv", "algorithmic_bytes": alg}
+        for m in ("mfma", "valu"):
+            d = float(np.median([t[0] for t in times[m]]))
+            c = float(np.median([t[1] for t in times[m]]))
+            row[m] = {"decode_us": round(d, 3), "merge_us": round(c, 3),
+                      "decode_GBps": round(alg / (d * 1e-6) / 1e9, 1),
+                      "rounds_decode_us": [round(t[0], 3) for t in times[m]]}
+        row["valu_over_mfma"] = round(row["valu"]["decode_us"] / row["mfma"]["decode_us"], 3)
+        log(f"{row['workload']}: decode MFMA {row['mfma']['decode_us']:.2f} us, "
+            f"VALU {row['valu']['decode_us']:.2f} us ({row['valu_over_mfma']:.3f}x)")
+        rows.append(row)
+        del launch, ks, vs
+        torch.cuda.empty_cache()
+    return {"mode": "tile-math-sweep", "n_workers": W, "steps": steps, "warmup": warmup,
+            "schedule": "device", "timing": "decode kernel, dispatch-stamped HIP events, median of 3 rounds",
+            "rows": rows}
 
 
 SKEW_BATCHES = (

@@ -56,6 +56,10 @@ extern "C" {
 #define HPC_KV_BF16      0   /* bfloat16                                            */
 #define HPC_KV_FP8_E4M3  1   /* OCP FP8 E4M3FN (torch.float8_e4m3fn), x = code*scale */
 
+/* ---- Tile arithmetic (how a tile's scores and P V are computed) ---------- */
+#define HPC_TILE_MATH_MFMA  0   /* matrix cores: QK^T and P V as 16x16 bf16 MFMA tiles  */
+#define HPC_TILE_MATH_VALU  1   /* vector ALU only: bf16 dot2 products; needs G <= 8    */
+
 #define HPC_DECODE_HEAD_DIM   128
 #define HPC_DECODE_PAGE       64   /* tokens per page = tokens per scheduling tile */
 #define HPC_DECODE_MAX_GROUP  16   /* query heads per KV head supported            */
@@ -74,6 +78,10 @@ typedef struct hpc_decode_params {
     float   sm_scale;           /* softmax scale, normally 1/sqrt(head_dim)          */
     float   k_scale;            /* per-tensor dequantisation scale of K (1 for bf16) */
     float   v_scale;            /* per-tensor dequantisation scale of V (1 for bf16) */
+    int32_t tile_math;          /* HPC_TILE_MATH_MFMA (0, the default) or          */
+                                /* HPC_TILE_MATH_VALU; both compute the same       */
+                                /* attention, the kernel being HBM-bound either    */
+                                /* way; VALU with G > 8 is HPC_ERR_UNSUPPORTED     */
 } hpc_decode_params;
 
 /*

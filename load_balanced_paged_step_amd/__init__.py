@@ -21,7 +21,8 @@ import torch
 from . import _lib
 from ._lib import (HPC_OK, HPC_ERR_NULL, HPC_ERR_INVALID, HPC_ERR_UNSUPPORTED, HPC_ERR_PLAN_MISMATCH,
                    HPC_ERR_TOO_SMALL, HPC_ERR_HIP, HPC_KV_BF16, HPC_KV_FP8_E4M3, HEAD_DIM, PAGE,
-                   MAX_GROUP, PLAN_HEADER_WORDS, HpcDecodeError, hpc_decode_params, lib)
+                   MAX_GROUP, PLAN_HEADER_WORDS, HPC_TILE_MATH_MFMA, HPC_TILE_MATH_VALU, VALU_MAX_GROUP,
+                   HpcDecodeError, hpc_decode_params, lib)
 
 __all__ = [
     "hpc_decode_plan_size", "hpc_decode_plan", "hpc_decode_plan_static_size", "hpc_decode_plan_static",
@@ -32,7 +33,8 @@ __all__ = [
     "hpc_decode_step_check", "hpc_decode_step_workspace_size", "hpc_decode_plan_device", "StepLauncher",
     "hpc_decode_plan_workspace_bound", "hpc_decode_plan_attn", "PlannedStepLauncher",
     "DecodeStep", "HpcDecodeError",
-    "kv_dtype_code", "make_params", "HPC_KV_BF16", "HPC_KV_FP8_E4M3",
+    "kv_dtype_code", "make_params", "tile_math_code", "HPC_KV_BF16", "HPC_KV_FP8_E4M3",
+    "HPC_TILE_MATH_MFMA", "HPC_TILE_MATH_VALU", "VALU_MAX_GROUP",
 ]
 
 _I32P = ctypes.POINTER(ctypes.c_int32)
@@ -82,12 +84,23 @@ def kv_dtype_code(dtype: torch.dtype) -> int:
     raise ValueError(f"unsupported KV-cache dtype {dtype}")
 
 
+def tile_math_code(tile_math) -> int:
+    """HPC_TILE_MATH_* code of ``tile_math`` ("mfma", "valu" or the code itself)."""
+    if isinstance(tile_math, str):
+        codes = {"mfma": HPC_TILE_MATH_MFMA, "valu": HPC_TILE_MATH_VALU}
+        if tile_math not in codes:
+            raise ValueError(f"tile_math must be 'mfma' or 'valu', not {tile_math!r}")
+        return codes[tile_math]
+    return int(tile_math)
+
+
 def make_params(num_q_heads, num_kv_heads, max_pages_per_seq, num_pages, kv_dtype, sm_scale,
-                k_scale=1.0, v_scale=1.0, head_dim=HEAD_DIM, page_size=PAGE) -> hpc_decode_params:
+                k_scale=1.0, v_scale=1.0, head_dim=HEAD_DIM, page_size=PAGE,
+                tile_math="mfma") -> hpc_decode_params:
     code = kv_dtype if isinstance(kv_dtype, int) else kv_dtype_code(kv_dtype)
     return hpc_decode_params(int(num_q_heads), int(num_kv_heads), int(head_dim), int(page_size),
                              int(max_pages_per_seq), int(num_pages), code, float(sm_scale),
-                             float(k_scale), float(v_scale))
+                             float(k_scale), float(v_scale), tile_math_code(tile_math))
 
 
 # ---------------------------------------------------------------- planner ---
@@ -157,13 +170,14 @@ def hpc_status_string(status: int) -> str:
 # ----------------------------------------------------------- decode step ---
 
 def _attn_args(q, k_cache, v_cache, block_table, seq_lens, plan_host, plan_dev, workspace, out, lse,
-               num_kv_heads, sm_scale, k_scale, v_scale):
+               num_kv_heads, sm_scale, k_scale, v_scale, tile_math="mfma"):
     if k_cache.dtype != v_cache.dtype:
         raise ValueError("k_cache and v_cache must have the same dtype")
     if q.dim() != 3 or k_cache.dim() != 4 or block_table.dim() != 2:
         raise ValueError("expected q [B,Hq,128], caches [pages,H_kv,64,128], block_table [B,max_pages]")
     params = make_params(q.shape[1], num_kv_heads, block_table.shape[1], k_cache.shape[0], k_cache.dtype,
-                         sm_scale, k_scale, v_scale, head_dim=q.shape[2], page_size=k_cache.shape[2])
+                         sm_scale, k_scale, v_scale, head_dim=q.shape[2], page_size=k_cache.shape[2],
+                         tile_math=tile_math)
     ph = plan_host if isinstance(plan_host, np.ndarray) else _host_i32(plan_host)
     if int(ph[1]) != q.shape[0] or block_table.shape[0] != q.shape[0] or seq_lens.shape[0] != q.shape[0]:
         raise ValueError("batch sizes of q, block_table, seq_lens and the plan differ")
@@ -188,18 +202,19 @@ def _attn_args(q, k_cache, v_cache, block_table, seq_lens, plan_host, plan_dev, 
 
 
 def hpc_decode_check(q, k_cache, v_cache, block_table, seq_lens, plan_host, plan_dev, workspace, out,
-                     lse, *, num_kv_heads, sm_scale, k_scale=1.0, v_scale=1.0) -> int:
+                     lse, *, num_kv_heads, sm_scale, k_scale=1.0, v_scale=1.0, tile_math="mfma") -> int:
     """Status that hpc_decode_attn would return for these arguments (no launch)."""
     args, _ = _attn_args(q, k_cache, v_cache, block_table, seq_lens, plan_host, plan_dev, workspace, out,
-                         lse, num_kv_heads, sm_scale, k_scale, v_scale)
+                         lse, num_kv_heads, sm_scale, k_scale, v_scale, tile_math)
     return lib().hpc_decode_check(*args)
 
 
 def hpc_decode_attn(q, k_cache, v_cache, block_table, seq_lens, plan_host, plan_dev, workspace, out,
-                    lse, *, num_kv_heads, sm_scale, k_scale=1.0, v_scale=1.0, stream=None) -> None:
+                    lse, *, num_kv_heads, sm_scale, k_scale=1.0, v_scale=1.0, stream=None,
+                    tile_math="mfma") -> None:
     """One decode step on ``stream`` (default: torch's current stream); see hpc_decode.h."""
     args, _ = _attn_args(q, k_cache, v_cache, block_table, seq_lens, plan_host, plan_dev, workspace, out,
-                         lse, num_kv_heads, sm_scale, k_scale, v_scale)
+                         lse, num_kv_heads, sm_scale, k_scale, v_scale, tile_math)
     _lib.check(lib().hpc_decode_attn(*args, _stream_handle(stream)), "hpc_decode_attn")
 
 
@@ -212,14 +227,14 @@ def hpc_decode_plan_workspace_bound(batch: int, num_q_heads: int, num_kv_heads: 
 
 def hpc_decode_plan_attn(seq_lens_host, plan_host, plan_dev, q, k_cache, v_cache, block_table, seq_lens,
                          workspace, out, lse, *, num_kv_heads, n_workers, sm_scale, k_scale=1.0, v_scale=1.0,
-                         stream=None) -> np.ndarray:
+                         stream=None, tile_math="mfma") -> np.ndarray:
     """Plan the host lengths into ``plan_host`` (a host int32 buffer, pinned
     for an asynchronous upload), queue its copy to ``plan_dev`` and launch the
     step, in one native call; returns the plan words (a view of plan_host).
     The caller keeps plan_host unchanged until the copy has run on the stream."""
     lens = _host_i32(seq_lens_host).reshape(-1)
     params, args = _step_args(q, k_cache, v_cache, block_table, seq_lens, workspace, out, lse, num_kv_heads,
-                              n_workers, sm_scale, k_scale, v_scale)
+                              n_workers, sm_scale, k_scale, v_scale, tile_math)
     if lens.shape[0] != q.shape[0]:
         raise ValueError("seq_lens_host has the wrong batch size")
     ph = plan_host.numpy() if isinstance(plan_host, torch.Tensor) else plan_host
@@ -249,13 +264,14 @@ class PlannedStepLauncher:
     """
 
     def __init__(self, q, k_cache, v_cache, block_table, seq_lens, out, lse, *, num_kv_heads, n_workers,
-                 sm_scale, k_scale=1.0, v_scale=1.0, workspace=None, stream=None, in_place=False):
+                 sm_scale, k_scale=1.0, v_scale=1.0, workspace=None, stream=None, in_place=False,
+                 tile_math="mfma"):
         B = q.shape[0]
         if workspace is None:
             need = hpc_decode_plan_workspace_bound(B, q.shape[1], num_kv_heads, n_workers)
             workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
         self.params, args = _step_args(q, k_cache, v_cache, block_table, seq_lens, workspace, out, lse,
-                                       num_kv_heads, n_workers, sm_scale, k_scale, v_scale)
+                                       num_kv_heads, n_workers, sm_scale, k_scale, v_scale, tile_math)
         self._keep = (q, k_cache, v_cache, block_table, seq_lens, out, lse, workspace)
         self.workspace = workspace
         self.batch, self.n_workers = int(B), int(n_workers)
@@ -309,7 +325,7 @@ def hpc_decode_step_workspace_size(batch: int, num_q_heads: int, num_kv_heads: i
 
 
 def _step_args(q, k_cache, v_cache, block_table, seq_lens, workspace, out, lse, num_kv_heads, n_workers,
-               sm_scale, k_scale, v_scale):
+               sm_scale, k_scale, v_scale, tile_math="mfma"):
     if k_cache.dtype != v_cache.dtype or tuple(k_cache.shape) != tuple(v_cache.shape):
         raise ValueError("k_cache and v_cache must have the same dtype and shape")
     if q.dim() != 3 or k_cache.dim() != 4 or block_table.dim() != 2 or k_cache.shape[1] != num_kv_heads:
@@ -320,7 +336,8 @@ def _step_args(q, k_cache, v_cache, block_table, seq_lens, workspace, out, lse, 
     if tuple(out.shape) != tuple(q.shape) or tuple(lse.shape) != tuple(q.shape[:2]):
         raise ValueError("out must match q's shape and lse must be [B, Hq]")
     params = make_params(q.shape[1], num_kv_heads, block_table.shape[1], k_cache.shape[0], k_cache.dtype,
-                         sm_scale, k_scale, v_scale, head_dim=q.shape[2], page_size=k_cache.shape[2])
+                         sm_scale, k_scale, v_scale, head_dim=q.shape[2], page_size=k_cache.shape[2],
+                         tile_math=tile_math)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     return (params,
             (ctypes.c_int32(B), ctypes.c_int32(n_workers),
@@ -336,17 +353,17 @@ def _step_args(q, k_cache, v_cache, block_table, seq_lens, workspace, out, lse, 
 
 
 def hpc_decode_step_check(q, k_cache, v_cache, block_table, seq_lens, workspace, out, lse, *, num_kv_heads,
-                          n_workers, sm_scale, k_scale=1.0, v_scale=1.0) -> int:
+                          n_workers, sm_scale, k_scale=1.0, v_scale=1.0, tile_math="mfma") -> int:
     params, args = _step_args(q, k_cache, v_cache, block_table, seq_lens, workspace, out, lse, num_kv_heads,
-                              n_workers, sm_scale, k_scale, v_scale)
+                              n_workers, sm_scale, k_scale, v_scale, tile_math)
     return lib().hpc_decode_step_check(ctypes.byref(params), *args)
 
 
 def hpc_decode_step(q, k_cache, v_cache, block_table, seq_lens, workspace, out, lse, *, num_kv_heads,
-                    n_workers, sm_scale, k_scale=1.0, v_scale=1.0, stream=None) -> None:
+                    n_workers, sm_scale, k_scale=1.0, v_scale=1.0, stream=None, tile_math="mfma") -> None:
     """One decode step with the schedule derived on the device from ``seq_lens``."""
     params, args = _step_args(q, k_cache, v_cache, block_table, seq_lens, workspace, out, lse, num_kv_heads,
-                              n_workers, sm_scale, k_scale, v_scale)
+                              n_workers, sm_scale, k_scale, v_scale, tile_math)
     _lib.check(lib().hpc_decode_step(ctypes.byref(params), *args, _stream_handle(stream)), "hpc_decode_step")
 
 
@@ -374,13 +391,13 @@ class StepLauncher:
     """
 
     def __init__(self, q, k_cache, v_cache, block_table, seq_lens, out, lse, *, num_kv_heads, n_workers,
-                 sm_scale, k_scale=1.0, v_scale=1.0, workspace=None, stream=None):
+                 sm_scale, k_scale=1.0, v_scale=1.0, workspace=None, stream=None, tile_math="mfma"):
         need = hpc_decode_step_workspace_size(q.shape[0], q.shape[1], num_kv_heads, n_workers)
         if workspace is None:
             workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
         self._keep = (q, k_cache, v_cache, block_table, seq_lens, out, lse, workspace)
         self.params, args = _step_args(q, k_cache, v_cache, block_table, seq_lens, workspace, out, lse,
-                                       num_kv_heads, n_workers, sm_scale, k_scale, v_scale)
+                                       num_kv_heads, n_workers, sm_scale, k_scale, v_scale, tile_math)
         self.workspace = workspace
         self._args = (ctypes.byref(self.params),) + args + (_stream_handle(stream),)
         status = lib().hpc_decode_step_check(*self._args[:-1])
@@ -488,7 +505,7 @@ class DecodeStep:
         return words
 
     def attend(self, q, k_cache, v_cache, block_table, seq_lens_dev, out=None, lse=None, *,
-               sm_scale, k_scale=1.0, v_scale=1.0):
+               sm_scale, k_scale=1.0, v_scale=1.0, tile_math="mfma"):
         if self.plan_host is None:
             raise RuntimeError("call plan() before attend()")
         if out is None:
@@ -498,7 +515,7 @@ class DecodeStep:
         ws = self.workspace if self.workspace.numel() else None
         hpc_decode_attn(q, k_cache, v_cache, block_table, seq_lens_dev, self.plan_host, self.plan_dev, ws,
                         out, lse, num_kv_heads=self.num_kv_heads, sm_scale=sm_scale, k_scale=k_scale,
-                        v_scale=v_scale, stream=self._stream())
+                        v_scale=v_scale, stream=self._stream(), tile_math=tile_math)
         return out, lse
 
     def __call__(self, seq_lens_host, q, k_cache, v_cache, block_table, seq_lens_dev, out=None, lse=None,

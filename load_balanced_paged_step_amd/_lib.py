@@ -25,6 +25,9 @@ HPC_KV_FP8_E4M3 = 1
 HEAD_DIM = 128
 PAGE = 64
 MAX_GROUP = 16
+HPC_TILE_MATH_MFMA = 0
+HPC_TILE_MATH_VALU = 1
+VALU_MAX_GROUP = 8
 PLAN_HEADER_WORDS = 16
 
 
@@ -40,6 +43,7 @@ class hpc_decode_params(ctypes.Structure):
         ("sm_scale", ctypes.c_float),
         ("k_scale", ctypes.c_float),
         ("v_scale", ctypes.c_float),
+        ("tile_math", ctypes.c_int32),
     ]
 
 

@@ -58,6 +58,8 @@ extern "C" int hpc_decode_check(const hpc_decode_params* p, const void* q, const
         return HPC_ERR_INVALID;
     const int32_t G = p->num_q_heads / p->num_kv_heads;
     if (G > HPC_DECODE_MAX_GROUP) return HPC_ERR_UNSUPPORTED;
+    if (p->tile_math != HPC_TILE_MATH_MFMA && p->tile_math != HPC_TILE_MATH_VALU) return HPC_ERR_INVALID;
+    if (p->tile_math == HPC_TILE_MATH_VALU && G > hpcd::kValuMaxGroup) return HPC_ERR_UNSUPPORTED;
     if (p->max_pages_per_seq < 1 || p->num_pages < 1) return HPC_ERR_INVALID;
     if (!std::isfinite(p->sm_scale) || !std::isfinite(p->k_scale) || !std::isfinite(p->v_scale))
         return HPC_ERR_INVALID;
@@ -141,7 +143,7 @@ int launch_planned(const hpc_decode_params* p, const void* q, const void* k_cach
 
     hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
     claim_profile_events(ev, E > 0, C > 0);
-    if (E > 0 && hpcd::launch_decode(da, p->kv_dtype, W, false, stream, ev[0], ev[1]) != 0) return HPC_ERR_HIP;
+    if (E > 0 && hpcd::launch_decode(da, p->kv_dtype, p->tile_math, W, false, stream, ev[0], ev[1]) != 0) return HPC_ERR_HIP;
     if (C > 0 && hpcd::launch_combine(ca, C, false, stream, ev[2], ev[3]) != 0) return HPC_ERR_HIP;
     return HPC_OK;
 }
@@ -251,6 +253,9 @@ extern "C" int hpc_decode_step_check(const hpc_decode_params* p, int32_t batch, 
     if (p->num_kv_heads < 1 || p->num_q_heads < p->num_kv_heads || p->num_q_heads % p->num_kv_heads != 0)
         return HPC_ERR_INVALID;
     if (p->num_q_heads / p->num_kv_heads > HPC_DECODE_MAX_GROUP) return HPC_ERR_UNSUPPORTED;
+    if (p->tile_math != HPC_TILE_MATH_MFMA && p->tile_math != HPC_TILE_MATH_VALU) return HPC_ERR_INVALID;
+    if (p->tile_math == HPC_TILE_MATH_VALU && p->num_q_heads / p->num_kv_heads > hpcd::kValuMaxGroup)
+        return HPC_ERR_UNSUPPORTED;
     if (p->max_pages_per_seq < 1 || p->num_pages < 1) return HPC_ERR_INVALID;
     if (!std::isfinite(p->sm_scale) || !std::isfinite(p->k_scale) || !std::isfinite(p->v_scale))
         return HPC_ERR_INVALID;
@@ -318,7 +323,7 @@ extern "C" int hpc_decode_step(const hpc_decode_params* p, int32_t batch, int32_
     const bool any_split = n_workers > 1;
 
     claim_profile_events(ev, true, any_split);
-    if (hpcd::launch_decode(da, p->kv_dtype, n_workers, true, stream, ev[0], ev[1]) != 0) return HPC_ERR_HIP;
+    if (hpcd::launch_decode(da, p->kv_dtype, p->tile_math, n_workers, true, stream, ev[0], ev[1]) != 0) return HPC_ERR_HIP;
     if (any_split && hpcd::launch_combine(ca, static_cast<int>(units), true, stream, ev[2], ev[3]) != 0)
         return HPC_ERR_HIP;
     return HPC_OK;

@@ -102,6 +102,55 @@ __device__ __forceinline__ u32x4 fp8x8_to_bf16x8(uint32_t lo4, uint32_t hi4) {
                  fp8x2_to_bf16x2<false>(hi4), fp8x2_to_bf16x2<true>(hi4)};
 }
 
+// ---- VALU tile math (the alternative to MFMA, selected per launch) ----
+// Largest query-head group the VALU tile math holds (its accumulators are
+// 8 heads x 8 dims per lane).
+constexpr int kValuHeads = kValuMaxGroup;
+static_assert(kValuHeads == 8, "the VALU accumulators are laid out for 8 heads");
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// two bf16 products summed into an fp32 accumulator (v_dot2c_f32_bf16)
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf16x2>(a), bitcast<bf16x2>(b), c, false);
+}
+
+// a lane of the same 16-lane row, chosen by a DPP control word
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return bitcast<float>(__builtin_amdgcn_update_dpp(0, bitcast<int>(x), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppSwap1 = 0xB1;    // quad_perm [1,0,3,2]: lane ^ 1
+constexpr int kDppSwap2 = 0x4E;    // quad_perm [2,3,0,1]: lane ^ 2
+constexpr int kDppRor4 = 0x124;    // row_ror:4
+constexpr int kDppRor8 = 0x128;    // row_ror:8
+
+// max / sum over the 16 lanes of each row, the result in every lane of it
+__device__ __forceinline__ float row16_max(float x) {
+    x = fmaxf(x, dpp_f<kDppSwap1>(x));
+    x = fmaxf(x, dpp_f<kDppSwap2>(x));
+    x = fmaxf(x, dpp_f<kDppRor4>(x));
+    return fmaxf(x, dpp_f<kDppRor8>(x));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+    x += dpp_f<kDppSwap1>(x);
+    x += dpp_f<kDppSwap2>(x);
+    x += dpp_f<kDppRor4>(x);
+    return x + dpp_f<kDppRor8>(x);
+}
+
+// x summed over the four 16-lane rows (lanes n, n+16, n+32, n+48), in every
+// lane: each swap exchanges half the rows of two copies of x, so the two
+// halves it returns add up to the pairwise sum, the same in both lanes
+__device__ __forceinline__ float rows4_sum(float x) {
+    const uint32_t xb = bitcast<uint32_t>(x);
+    const auto s32 = __builtin_amdgcn_permlane32_swap(xb, xb, false, false);
+    const float y = bitcast<float>(s32[0]) + bitcast<float>(s32[1]);
+    const uint32_t yb = bitcast<uint32_t>(y);
+    const auto s16 = __builtin_amdgcn_permlane16_swap(yb, yb, false, false);
+    return bitcast<float>(s16[0]) + bitcast<float>(s16[1]);
+}
+
 // Per KV element type: what one wave loads from one tile, and how it becomes
 // MFMA operands.  Offsets are relative to the (page, kv head) block.
 template <int KV>
@@ -215,7 +264,11 @@ struct HostWalker {
             t = entries[4 * e + 1];
             tb = entries[4 * e + 2];
             part = entries[4 * e + 3];
-            len = seq_lens[u / H];
+            // through the constant address space: the kernel never writes the
+            // lengths, and such a load always takes the scalar unit (as a
+            // vector load, issued behind the ring's loads, waiting for it
+            // would wait for all of them)
+            len = ((const __attribute__((address_space(4))) int32_t*)(seq_lens))[u / H];
         }
         b = u / H;
         h = u - b * H;
@@ -277,7 +330,7 @@ __device__ __forceinline__ void fetch_args(A& a, B& b, C& c, D& d) {
     asm("" : "+s"(a), "+s"(b), "+s"(c), "+s"(d));
 }
 
-template <int KV, int PF, int NT, bool DEV>
+template <int KV, int PF, int NT, bool DEV, bool VALU>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     const __bf16* __restrict__ q, const char* __restrict__ kcache, const char* __restrict__ vcache,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
@@ -291,6 +344,14 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     __shared__ float s_l[kWaves][64];
     __shared__ int32_t s_tmp[2 * kWaves];
     extern __shared__ int32_t s_dyn[];   // device schedule: len[B], tile prefix[B + 1]
+    // VALU tile math: each wave's copy of its entry's Q ([head][dim group g]
+    // [k-step], in the K operand's dim order), and the entry-end exchange
+    // (per wave and dim group: 8 heads x 128 dims of output sums, and the
+    // wave's running max and sum per head)
+    __shared__ u32x4 s_vq[kWaves][kValuHeads][4][4];
+    __shared__ f32x4 s_vacc[kWaves][4][kValuHeads][kHeadDim / 4];
+    __shared__ float s_vm[kWaves][kValuHeads];
+    __shared__ float s_vl[kWaves][kValuHeads];
 
     // the host-planned walker reads lengths inside the tile loop: it keeps the
     // argument itself, whose read-only, unaliased provenance lets those reads
@@ -599,6 +660,198 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
         }
     };
 
+    // ---- VALU tile math ----
+    // K: lane (n, g) holds token row 16 wave + n, dims of group g (the MFMA
+    // K operand registers).  Scores: dot2 over the lane's 32 dims against
+    // the entry's Q (read from this wave's LDS copy), summed over the four
+    // dim groups, so every lane holds the scores of its row for all heads.
+    // V: lane (n, g) holds rows 16 wave + 4g + i (i < 4), dims 8n .. 8n+7
+    // (the MFMA V registers); P reaches it as bf16 pairs of rows (4g + 2j,
+    // 4g + 2j + 1) gathered from the lanes holding those rows' scores, and
+    // P V is dot2 over those token pairs into vacc[head][dim 8n + e], a
+    // partial sum over the lane's 4 rows.  Running max vm[h] is the same in
+    // every lane of the wave; vl[h] is the lane's row share of the sum.
+    float vm[kValuHeads], vl[kValuHeads], vacc[kValuHeads][8];
+#pragma unroll
+    for (int h = 0; h < kValuHeads; ++h) {
+        vm[h] = -INFINITY;
+        vl[h] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vacc[h][e] = 0.f;
+    }
+
+    auto consume_valu = [&](const TileSlot<KV, NT>& s) {
+        const bool fq = s.info.first();
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const u32x4 prev = bitcast<u32x4>(qop[kk]);
+            qop[kk] = bitcast<bf16x8>(u32x4{fq ? s.q[kk][0] : prev[0], fq ? s.q[kk][1] : prev[1],
+                                            fq ? s.q[kk][2] : prev[2], fq ? s.q[kk][3] : prev[3]});
+        }
+        // a new entry's Q into this wave's copy (lane (n, g) holds head n);
+        // LDS accesses of one wave complete in order, so the reads below see it
+        if (fq && n < kValuHeads) {
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) s_vq[wave][n][g][kk] = bitcast<u32x4>(qop[kk]);
+        }
+        u32x4 kw[NT][4];
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) kw[tt][kk] = bitcast<u32x4>(s.kv[tt].k_op(kk));
+        float sv[NT][kValuHeads];
+#pragma unroll
+        for (int h = 0; h < kValuHeads; ++h) {
+            u32x4 qw[4];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) qw[kk] = s_vq[wave][h][g][kk];
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) {
+                float d = 0.f;
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) d = dot2(kw[tt][kk][j], qw[kk][j], d);
+                sv[tt][h] = rows4_sum(d);
+            }
+        }
+        const int kr = 16 * wave + n;   // this lane's K row in the tile
+        float mt[kValuHeads];
+#pragma unroll
+        for (int h = 0; h < kValuHeads; ++h) mt[h] = -INFINITY;
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+            const int valid = tt == 0 ? s.info.valid() : s.info.valid2;
+#pragma unroll
+            for (int h = 0; h < kValuHeads; ++h) {
+                sv[tt][h] = (kr < valid) ? sv[tt][h] * a.qk_scale_log2 : -INFINITY;
+                mt[h] = fmaxf(mt[h], sv[tt][h]);
+            }
+        }
+        float mu[kValuHeads], alpha[kValuHeads];
+        bool grew = false;
+#pragma unroll
+        for (int h = 0; h < kValuHeads; ++h) {
+            const float m_new = fmaxf(vm[h], row16_max(mt[h]));
+            mu[h] = (m_new == -INFINITY) ? 0.f : m_new;
+            alpha[h] = __builtin_amdgcn_exp2f(vm[h] - mu[h]);
+            grew |= m_new > vm[h];
+            vm[h] = m_new;
+        }
+        float p[NT][kValuHeads];
+#pragma unroll
+        for (int h = 0; h < kValuHeads; ++h) {
+            float ps = 0.f;
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) {
+                p[tt][h] = __builtin_amdgcn_exp2f(sv[tt][h] - mu[h]);
+                ps += p[tt][h];
+            }
+            vl[h] = vl[h] * alpha[h] + ps;
+        }
+        // rescale the output sums only when some running max grew (alpha is
+        // exactly 1 wherever it did not)
+        if (__builtin_amdgcn_ballot_w64(grew) != 0) {
+#pragma unroll
+            for (int h = 0; h < kValuHeads; ++h)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) vacc[h][e] *= alpha[h];
+        }
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+            // bf16 pairs of P over rows (4g + 2j, 4g + 2j + 1): a lane of even
+            // row r packs (p[r], p[r + 1]); lane (n, g) then reads rows 4g, 4g + 2
+            // from its own 16-lane row (every row holds all scores)
+            uint32_t pp[kValuHeads][2];
+#pragma unroll
+            for (int h = 0; h < kValuHeads; ++h) {
+                const float pn = dpp_f<kDppSwap1>(p[tt][h]);
+                const uint32_t pk = bitcast<uint32_t>(bf16x2{static_cast<__bf16>(p[tt][h]), static_cast<__bf16>(pn)});
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    pp[h][j] = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(
+                        4 * ((lane & 48) | (4 * g + 2 * j)), static_cast<int>(pk)));
+            }
+            u32x4 rows[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) rows[i] = s.kv[tt].v_row(i);
+            // V pairs over the same rows, one per dim: (v[4g+2j][d], v[4g+2j+1][d])
+            uint32_t vp[2][8];
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    vp[j][2 * d] = __builtin_amdgcn_perm(rows[2 * j + 1][d], rows[2 * j][d], kSelLo);
+                    vp[j][2 * d + 1] = __builtin_amdgcn_perm(rows[2 * j + 1][d], rows[2 * j][d], kSelHi);
+                }
+#pragma unroll
+            for (int h = 0; h < kValuHeads; ++h)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) vacc[h][e] = dot2(vp[1][e], pp[h][1], dot2(vp[0][e], pp[h][0], vacc[h][e]));
+        }
+    };
+
+    auto flush_valu = [&](const TileInfo& ts) {
+        const int row = ts.row;
+        const int part = ts.part;
+        // every lane's output sums (its 4 rows, dims 8n ..) and the wave's max and sum per head
+#pragma unroll
+        for (int h = 0; h < kValuHeads; ++h) {
+            s_vacc[wave][g][h][2 * n] = f32x4{vacc[h][0], vacc[h][1], vacc[h][2], vacc[h][3]};
+            s_vacc[wave][g][h][2 * n + 1] = f32x4{vacc[h][4], vacc[h][5], vacc[h][6], vacc[h][7]};
+            const float lw = row16_sum(vl[h]);
+            if (lane == 0) {
+                s_vm[wave][h] = vm[h];
+                s_vl[wave][h] = lw;
+            }
+        }
+        __syncthreads();
+        // thread t: head t / 32, dims 4 (t % 32) .. +4, over 4 waves x 4 dim groups
+        const int hh = static_cast<int>(threadIdx.x) >> 5;
+        const int dq = static_cast<int>(threadIdx.x) & 31;
+        float ms[kWaves], M = -INFINITY;
+#pragma unroll
+        for (int s = 0; s < kWaves; ++s) {
+            ms[s] = s_vm[s][hh];
+            M = fmaxf(M, ms[s]);
+        }
+        const float M_use = (M == -INFINITY) ? 0.f : M;
+        float wsum = 0.f;
+        f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < kWaves; ++s) {
+            const float wt = __builtin_amdgcn_exp2f(ms[s] - M_use);
+            wsum += wt * s_vl[s][hh];
+            f32x4 sw = s_vacc[s][0][hh][dq];
+#pragma unroll
+            for (int gg = 1; gg < 4; ++gg) sw += s_vacc[s][gg][hh][dq];
+            o += wt * sw;
+        }
+        if (hh < G) {
+            const float inv = (wsum > 0.f) ? a.v_scale / wsum : 0.f;
+            const float lse_val = (wsum > 0.f) ? (M + __log2f(wsum)) * kLn2 : -INFINITY;
+            const int slot = part;
+            if (slot < 0) {
+                const bf16x4 ov = bf16x4{static_cast<__bf16>(o[0] * inv), static_cast<__bf16>(o[1] * inv),
+                                         static_cast<__bf16>(o[2] * inv), static_cast<__bf16>(o[3] * inv)};
+                *reinterpret_cast<bf16x4*>(out + static_cast<int64_t>(row + hh) * kHeadDim + 4 * dq) = ov;
+                if (dq == 0) lse[row + hh] = lse_val;
+            } else if (slot < a.max_partials) {   // a slot is always in range; the test keeps stray writes out
+                float* dst = o_part + (static_cast<int64_t>(slot) * G + hh) * kHeadDim + 4 * dq;
+                *reinterpret_cast<f32x4*>(dst) = o * inv;
+                if (dq == 0) lse_part[static_cast<int64_t>(slot) * G + hh] = lse_val;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int h = 0; h < kValuHeads; ++h) {
+            vm[h] = -INFINITY;
+            vl[h] = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vacc[h][e] = 0.f;
+        }
+    };
+
     // One exit, at the end of a full ring turn: every path back to the top
     // has re-issued all PF slots, so the compiler's load-counter waits let
     // the other PF - 1 tiles stay in flight.  Slots are filled in tile order,
@@ -611,11 +864,15 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     for (;;) {
 #pragma unroll
         for (int j = 0; j < PF; ++j) {
-            consume(ring[j]);
+            if constexpr (VALU) consume_valu(ring[j]);
+            else consume(ring[j]);
             const TileInfo ended = ring[j].info;
             plan_tile(planned[j]);
             load_tile(ring[j], planned[j]);
-            if (ended.last()) flush(ended);
+            if (ended.last()) {
+                if constexpr (VALU) flush_valu(ended);
+                else flush(ended);
+            }
         }
         if (!ring[0].info.real()) break;
     }
@@ -879,12 +1136,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_device_kernel(const int32_t
 constexpr int kPrefetchBf16 = HPC_DECODE_PREFETCH_BF16;
 constexpr int kPrefetchFp8 = HPC_DECODE_PREFETCH_FP8;
 
-template <int KV, int PF, bool DEV>
+template <int KV, int PF, bool DEV, bool VALU>
 void launch_decode_t(const DecodeArgs& a, int n_workers, size_t lds, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     const DecodeScalars sc{a.batch,        a.num_kv_heads,  a.group,   a.max_pages_per_seq, a.num_pages,
                            a.max_partials, a.qk_scale_log2, a.v_scale, n_workers};
     constexpr int kTilesPerSlot = KV == HPC_KV_FP8_E4M3 ? HPC_DECODE_PAIR_FP8 + 1 : 1;
-    hipExtLaunchKernelGGL((decode_kernel<KV, PF, kTilesPerSlot, DEV>), dim3(n_workers), dim3(kDecodeThreads),
+    hipExtLaunchKernelGGL((decode_kernel<KV, PF, kTilesPerSlot, DEV, VALU>), dim3(n_workers), dim3(kDecodeThreads),
                           static_cast<std::uint32_t>(lds), s, e0, e1, 0u,
                           static_cast<const __bf16*>(a.q), static_cast<const char*>(a.k),
                           static_cast<const char*>(a.v), a.block_table, a.seq_lens, a.worker_ptr, a.entries,
@@ -893,18 +1150,27 @@ void launch_decode_t(const DecodeArgs& a, int n_workers, size_t lds, hipStream_t
 
 }  // namespace
 
-int launch_decode(const DecodeArgs& a, int kv_dtype, int n_workers, bool device_sched, void* stream,
+namespace {
+template <bool VALU>
+void launch_decode_m(const DecodeArgs& a, int kv_dtype, int n_workers, bool device_sched, size_t lds,
+                     hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+    if (kv_dtype == HPC_KV_BF16) {
+        if (device_sched) launch_decode_t<HPC_KV_BF16, kPrefetchBf16, true, VALU>(a, n_workers, lds, s, e0, e1);
+        else launch_decode_t<HPC_KV_BF16, kPrefetchBf16, false, VALU>(a, n_workers, lds, s, e0, e1);
+    } else {
+        if (device_sched) launch_decode_t<HPC_KV_FP8_E4M3, kPrefetchFp8, true, VALU>(a, n_workers, lds, s, e0, e1);
+        else launch_decode_t<HPC_KV_FP8_E4M3, kPrefetchFp8, false, VALU>(a, n_workers, lds, s, e0, e1);
+    }
+}
+}  // namespace
+
+int launch_decode(const DecodeArgs& a, int kv_dtype, int tile_math, int n_workers, bool device_sched, void* stream,
                   void* ev_start, void* ev_stop) {
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipEvent_t e0 = static_cast<hipEvent_t>(ev_start), e1 = static_cast<hipEvent_t>(ev_stop);
     const size_t lds = device_sched ? (2 * static_cast<size_t>(a.batch) + 1) * sizeof(int32_t) : 0;
-    if (kv_dtype == HPC_KV_BF16) {
-        if (device_sched) launch_decode_t<HPC_KV_BF16, kPrefetchBf16, true>(a, n_workers, lds, s, e0, e1);
-        else launch_decode_t<HPC_KV_BF16, kPrefetchBf16, false>(a, n_workers, lds, s, e0, e1);
-    } else {
-        if (device_sched) launch_decode_t<HPC_KV_FP8_E4M3, kPrefetchFp8, true>(a, n_workers, lds, s, e0, e1);
-        else launch_decode_t<HPC_KV_FP8_E4M3, kPrefetchFp8, false>(a, n_workers, lds, s, e0, e1);
-    }
+    if (tile_math == HPC_TILE_MATH_VALU) launch_decode_m<true>(a, kv_dtype, n_workers, device_sched, lds, s, e0, e1);
+    else launch_decode_m<false>(a, kv_dtype, n_workers, device_sched, lds, s, e0, e1);
     return static_cast<int>(hipGetLastError());
 }
 

@@ -12,6 +12,7 @@ constexpr int kWaves = 4;                 // waves per decode workgroup
 constexpr int kDecodeThreads = 64 * kWaves;
 constexpr int kCombineThreads = 256;
 constexpr int kPlanThreads = 1024;
+constexpr int kValuMaxGroup = 8;          // query heads per KV head the VALU tile math holds
 
 // Limits of the device-scheduled path: the lengths, their tile prefix and
 // the per-unit split tables live in LDS of every workgroup.
@@ -63,7 +64,8 @@ struct CombineArgs {
 // and writes one merge record per unit for the merge kernel.
 // ev_start / ev_stop (hipEvent_t or null): events that the launch itself
 // stamps when the kernel starts and ends, i.e. the kernel's own duration.
-int launch_decode(const DecodeArgs& a, int kv_dtype, int n_workers, bool device_sched, void* stream,
+// tile_math: HPC_TILE_MATH_MFMA or HPC_TILE_MATH_VALU (the latter needs group <= 8).
+int launch_decode(const DecodeArgs& a, int kv_dtype, int tile_math, int n_workers, bool device_sched, void* stream,
                   void* ev_start = nullptr, void* ev_stop = nullptr);
 int launch_combine(const CombineArgs& a, int n_records, bool device_sched, void* stream,
                    void* ev_start = nullptr, void* ev_stop = nullptr);

@@ -23,14 +23,14 @@ def to_device(inp, device="cuda"):
                 bt=inp.block_table.to(device), sl=inp.seq_lens.to(device))
 
 
-def run_hip(inp, n_workers: int, dev=None, return_step=False):
+def run_hip(inp, n_workers: int, dev=None, return_step=False, tile_math="mfma"):
     """One decode step through DecodeStep (C++ planner, upload, HIP kernels)."""
     if dev is None:
         dev = to_device(inp)
     step = hd.DecodeStep(inp.num_q_heads, inp.num_kv_heads, inp.batch, n_workers)
     step.plan(inp.seq_lens)
     out, lse = step.attend(dev["q"], dev["k"], dev["v"], dev["bt"], dev["sl"], sm_scale=inp.sm_scale,
-                           k_scale=inp.k_scale, v_scale=inp.v_scale)
+                           k_scale=inp.k_scale, v_scale=inp.v_scale, tile_math=tile_math)
     torch.cuda.synchronize()
     res = (out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64))
     return (res + (step,)) if return_step else res
@@ -66,7 +66,7 @@ def compare(inp, got, ref, what=""):
     return {"max_err": max_err, "tol": tol, "lse_err": lse_err}
 
 
-def run_hip_plan(inp, plan_words, dev=None):
+def run_hip_plan(inp, plan_words, dev=None, tile_math="mfma"):
     """One decode step through hpc_decode_attn with a given host plan (any
     schedule in the plan word layout), uploaded once."""
     if dev is None:
@@ -79,6 +79,22 @@ def run_hip_plan(inp, plan_words, dev=None):
     lse = torch.empty(dev["q"].shape[:2], dtype=torch.float32, device="cuda")
     hd.hpc_decode_attn(dev["q"], dev["k"], dev["v"], dev["bt"], dev["sl"], plan_host, plan_dev, ws, out, lse,
                        num_kv_heads=inp.num_kv_heads, sm_scale=inp.sm_scale, k_scale=inp.k_scale,
-                       v_scale=inp.v_scale)
+                       v_scale=inp.v_scale, tile_math=tile_math)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def run_hip_step(inp, n_workers: int, dev=None, tile_math="mfma"):
+    """One device-scheduled decode step (hpc_decode_step: schedule from the
+    lengths on the GPU, decode and merge kernels)."""
+    if dev is None:
+        dev = to_device(inp)
+    ws_bytes = hd.hpc_decode_step_workspace_size(inp.batch, inp.num_q_heads, inp.num_kv_heads, n_workers)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(dev["q"])
+    lse = torch.empty(dev["q"].shape[:2], dtype=torch.float32, device="cuda")
+    hd.hpc_decode_step(dev["q"], dev["k"], dev["v"], dev["bt"], dev["sl"], ws, out, lse,
+                       num_kv_heads=inp.num_kv_heads, n_workers=n_workers, sm_scale=inp.sm_scale,
+                       k_scale=inp.k_scale, v_scale=inp.v_scale, tile_math=tile_math)
     torch.cuda.synchronize()
     return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)

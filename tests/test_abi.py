@@ -207,6 +207,34 @@ def test_check_group_too_large():
     assert f.check() == hd.HPC_ERR_UNSUPPORTED
 
 
+def test_check_tile_math():
+    f = _Fake(H=2, Hq=16)                      # G = 8: both tile maths
+    for code in (hd.HPC_TILE_MATH_MFMA, hd.HPC_TILE_MATH_VALU):
+        f.params.tile_math = code
+        assert f.check() == hd.HPC_OK
+    for bad in (2, -1):
+        f.params.tile_math = bad
+        assert f.check() == hd.HPC_ERR_INVALID
+    g = _Fake(H=1, Hq=16)                      # G = 16: MFMA only
+    assert g.check() == hd.HPC_OK
+    g.params.tile_math = hd.HPC_TILE_MATH_VALU
+    assert g.check() == hd.HPC_ERR_UNSUPPORTED
+    assert hd.make_params(8, 1, 4, 8, hd.HPC_KV_BF16, 0.1, tile_math="valu").tile_math == hd.HPC_TILE_MATH_VALU
+    assert hd.make_params(8, 1, 4, 8, hd.HPC_KV_BF16, 0.1).tile_math == hd.HPC_TILE_MATH_MFMA
+    with pytest.raises(ValueError):
+        hd.make_params(8, 1, 4, 8, hd.HPC_KV_BF16, 0.1, tile_math="simd")
+
+
+def test_params_struct_matches_header():
+    """The ctypes mirror of hpc_decode_params has the header's fields, in order."""
+    import re
+    hdr = open(os.path.join(ROOT, "include", "hpc_decode.h")).read()
+    body = re.search(r"typedef struct hpc_decode_params \{(.*?)\} hpc_decode_params;", hdr, re.S).group(1)
+    fields = re.findall(r"^\s*(?:int32_t|float)\s+(\w+);", body, re.M)
+    assert fields == [f[0] for f in hd.hpc_decode_params._fields_]
+    assert ctypes.sizeof(hd.hpc_decode_params) == 4 * len(fields)
+
+
 def test_check_plan_mismatches():
     f = _Fake()
     assert f.check(wsb=f.ws - 1) == hd.HPC_ERR_TOO_SMALL

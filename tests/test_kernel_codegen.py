@@ -44,9 +44,11 @@ def _ring_waits(asm: str):
     """(kernel name, every vmcnt wait inside the tile loop) for every decode
     kernel.  The tile loop is the outermost loop that holds the first score
     MFMA: its header and every block the compiler marks as belonging to it
-    (directly or through an inner loop)."""
+    (directly or through an inner loop).  The VALU tile math's loop is found
+    the same way from its first dot2."""
     for name, body in _kernels(asm):
-        first_mfma = body.find("v_mfma_f32_16x16x32_bf16")
+        # the first score instruction: an MFMA, or a dot2 in the VALU tile math
+        first_mfma = body.find("v_dot2c_f32_bf16" if _valu(name) else "v_mfma_f32_16x16x32_bf16")
         assert first_mfma > 0, name
         heads = list(re.finditer(r"^\.(LBB\w+):\s*;\s*=>\s*This (?:Inner )?Loop Header: Depth=1",
                                  body[:first_mfma], re.M))
@@ -74,13 +76,19 @@ def ring_waits(tmp_path_factory):
 
 
 def _device_scheduled(name: str) -> bool:
-    # decode_kernel<int KV, int PF, int NT, bool DEV>
+    # decode_kernel<int KV, int PF, int NT, bool DEV, bool VALU>
     return re.search(r"decode_kernelI(?:Li\d+E)+Lb1E", name) is not None
 
 
-def test_four_decode_kernels(ring_waits):
-    assert len(ring_waits) == 4, list(ring_waits)   # bf16 / fp8 x host plan / device schedule
-    assert sum(_device_scheduled(n) for n in ring_waits) == 2
+def _valu(name: str) -> bool:
+    return re.search(r"decode_kernelI(?:Li\d+E)+Lb[01]ELb1E", name) is not None
+
+
+def test_eight_decode_kernels(ring_waits):
+    # bf16 / fp8 x host plan / device schedule x MFMA / VALU tile math
+    assert len(ring_waits) == 8, list(ring_waits)
+    assert sum(_device_scheduled(n) for n in ring_waits) == 4
+    assert sum(_valu(n) for n in ring_waits) == 4
 
 
 def test_device_scheduled_ring_keeps_a_tile_in_flight(ring_waits):
