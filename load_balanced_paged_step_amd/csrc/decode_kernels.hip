@@ -115,10 +115,12 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf16x2>(a), bitcast<bf16x2>(b), c, false);
 }
 
-// a lane of the same 16-lane row, chosen by a DPP control word
+// a lane of the same 16-lane row, chosen by a DPP control word (every
+// control used here names a valid lane for every lane, so the bound control
+// bit only lets the move fold into the instruction that uses it)
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {
-    return bitcast<float>(__builtin_amdgcn_update_dpp(0, bitcast<int>(x), CTRL, 0xf, 0xf, false));
+    return bitcast<float>(__builtin_amdgcn_update_dpp(0, bitcast<int>(x), CTRL, 0xf, 0xf, true));
 }
 constexpr int kDppSwap1 = 0xB1;    // quad_perm [1,0,3,2]: lane ^ 1
 constexpr int kDppSwap2 = 0x4E;    // quad_perm [2,3,0,1]: lane ^ 2
@@ -137,18 +139,6 @@ __device__ __forceinline__ float row16_sum(float x) {
     x += dpp_f<kDppSwap2>(x);
     x += dpp_f<kDppRor4>(x);
     return x + dpp_f<kDppRor8>(x);
-}
-
-// x summed over the four 16-lane rows (lanes n, n+16, n+32, n+48), in every
-// lane: each swap exchanges half the rows of two copies of x, so the two
-// halves it returns add up to the pairwise sum, the same in both lanes
-__device__ __forceinline__ float rows4_sum(float x) {
-    const uint32_t xb = bitcast<uint32_t>(x);
-    const auto s32 = __builtin_amdgcn_permlane32_swap(xb, xb, false, false);
-    const float y = bitcast<float>(s32[0]) + bitcast<float>(s32[1]);
-    const uint32_t yb = bitcast<uint32_t>(y);
-    const auto s16 = __builtin_amdgcn_permlane16_swap(yb, yb, false, false);
-    return bitcast<float>(s16[0]) + bitcast<float>(s16[1]);
 }
 
 // Per KV element type: what one wave loads from one tile, and how it becomes
@@ -349,6 +339,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     // (per wave and dim group: 8 heads x 128 dims of output sums, and the
     // wave's running max and sum per head)
     __shared__ u32x4 s_vq[kWaves][kValuHeads][4][4];
+    __shared__ u32x4 s_vq_sink[kWaves][4][4];
     __shared__ f32x4 s_vacc[kWaves][4][kValuHeads][kHeadDim / 4];
     __shared__ float s_vm[kWaves][kValuHeads];
     __shared__ float s_vl[kWaves][kValuHeads];
@@ -663,115 +654,154 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     // ---- VALU tile math ----
     // K: lane (n, g) holds token row 16 wave + n, dims of group g (the MFMA
     // K operand registers).  Scores: dot2 over the lane's 32 dims against
-    // the entry's Q (read from this wave's LDS copy), summed over the four
-    // dim groups, so every lane holds the scores of its row for all heads.
-    // V: lane (n, g) holds rows 16 wave + 4g + i (i < 4), dims 8n .. 8n+7
-    // (the MFMA V registers); P reaches it as bf16 pairs of rows (4g + 2j,
-    // 4g + 2j + 1) gathered from the lanes holding those rows' scores, and
-    // P V is dot2 over those token pairs into vacc[head][dim 8n + e], a
-    // partial sum over the lane's 4 rows.  Running max vm[h] is the same in
-    // every lane of the wave; vl[h] is the lane's row share of the sum.
-    float vm[kValuHeads], vl[kValuHeads], vacc[kValuHeads][8];
+    // the entry's Q (read from this wave's LDS copy), then summed over the
+    // four dim groups by a reduce-scatter of half-wave and row swaps that
+    // leaves 4 heads per register, one head per 16-lane row: register R,
+    // row r holds head hid[R] of that row (R = head / 4) for token row n.
+    // The softmax then runs on 2 registers.  V: lane (n, g) holds rows
+    // 16 wave + 4g + i (i < 4), dims 8n .. 8n+7 (the MFMA V registers); P
+    // reaches it as bf16 pairs of rows (4g + 2j, 4g + 2j + 1) gathered from
+    // the row holding the head, and P V is dot2 over those token pairs into
+    // vacc[head][dim 8n + e], a partial sum over the lane's 4 rows.  vm[R]
+    // (running max) is the same in the 16 lanes of a row; vl[R] is the
+    // lane's token share of the running sum.
+    float vm[2], vl[2], vacc[kValuHeads][8];
 #pragma unroll
-    for (int h = 0; h < kValuHeads; ++h) {
-        vm[h] = -INFINITY;
-        vl[h] = 0.f;
+    for (int R = 0; R < 2; ++R) {
+        vm[R] = -INFINITY;
+        vl[R] = 0.f;
+    }
+#pragma unroll
+    for (int h = 0; h < kValuHeads; ++h)
 #pragma unroll
         for (int e = 0; e < 8; ++e) vacc[h][e] = 0.f;
+
+    // Which head each row of a reduced register holds: the same swaps applied
+    // to head numbers (a swap returns, in any one lane, two halves of one
+    // source register, so those lanes' sum belongs to that register's head).
+    int hid[2];
+#pragma unroll
+    for (int R = 0; R < 2; ++R) {
+        const auto x = __builtin_amdgcn_permlane32_swap(4u * R, 4u * R + 1u, false, false);
+        const auto y = __builtin_amdgcn_permlane32_swap(4u * R + 2u, 4u * R + 3u, false, false);
+        hid[R] = static_cast<int>(__builtin_amdgcn_permlane16_swap(x[0], y[0], false, false)[0]);
+    }
+    // and the row of each head (wave-uniform)
+    int row_of[kValuHeads];
+#pragma unroll
+    for (int h = 0; h < kValuHeads; ++h) {
+        const int R = h >> 2;
+        const int i0 = __builtin_amdgcn_readlane(hid[R], 0), i1 = __builtin_amdgcn_readlane(hid[R], 16),
+                  i2 = __builtin_amdgcn_readlane(hid[R], 32);
+        row_of[h] = i0 == h ? 0 : (i1 == h ? 1 : (i2 == h ? 2 : 3));
     }
 
+    // sum of four heads' partial dot products over the four dim groups:
+    // row r of the result holds the head hid[R] says, for token row n
+    auto reduce4 = [](float d0, float d1, float d2, float d3) -> float {
+        const auto a = __builtin_amdgcn_permlane32_swap(bitcast<uint32_t>(d0), bitcast<uint32_t>(d1), false, false);
+        const auto b = __builtin_amdgcn_permlane32_swap(bitcast<uint32_t>(d2), bitcast<uint32_t>(d3), false, false);
+        const float x = bitcast<float>(a[0]) + bitcast<float>(a[1]);
+        const float y = bitcast<float>(b[0]) + bitcast<float>(b[1]);
+        const auto c = __builtin_amdgcn_permlane16_swap(bitcast<uint32_t>(x), bitcast<uint32_t>(y), false, false);
+        return bitcast<float>(c[0]) + bitcast<float>(c[1]);
+    };
+
     auto consume_valu = [&](const TileSlot<KV, NT>& s) {
-        const bool fq = s.info.first();
+        // the slot's Q words go to LDS on every tile (so its load registers
+        // are read on every path, as in the MFMA body): into this wave's copy
+        // for an entry's first tile (lane (n, g) holds head n), else into a
+        // sink.  LDS accesses of one wave complete in order, so the reads
+        // below see them.
+        const bool to_copy = s.info.first() && n < kValuHeads;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-            const u32x4 prev = bitcast<u32x4>(qop[kk]);
-            qop[kk] = bitcast<bf16x8>(u32x4{fq ? s.q[kk][0] : prev[0], fq ? s.q[kk][1] : prev[1],
-                                            fq ? s.q[kk][2] : prev[2], fq ? s.q[kk][3] : prev[3]});
+            u32x4* dst = to_copy ? &s_vq[wave][n & (kValuHeads - 1)][g][kk] : &s_vq_sink[wave][g][kk];
+            *dst = s.q[kk];
         }
-        // a new entry's Q into this wave's copy (lane (n, g) holds head n);
-        // LDS accesses of one wave complete in order, so the reads below see it
-        if (fq && n < kValuHeads) {
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) s_vq[wave][n][g][kk] = bitcast<u32x4>(qop[kk]);
-        }
-        u32x4 kw[NT][4];
+        // partial dot products: k-step outer, so the 8 heads' Q of one step
+        // are read together and the 8 accumulator chains interleave
+        float d[NT][kValuHeads];
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) kw[tt][kk] = bitcast<u32x4>(s.kv[tt].k_op(kk));
-        float sv[NT][kValuHeads];
+            for (int h = 0; h < kValuHeads; ++h) d[tt][h] = 0.f;
 #pragma unroll
-        for (int h = 0; h < kValuHeads; ++h) {
-            u32x4 qw[4];
+        for (int kk = 0; kk < 4; ++kk) {
+            u32x4 qw[kValuHeads];
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) qw[kk] = s_vq[wave][h][g][kk];
+            for (int h = 0; h < kValuHeads; ++h) qw[h] = s_vq[wave][h][g][kk];
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt) {
-                float d = 0.f;
+                const u32x4 kw = bitcast<u32x4>(s.kv[tt].k_op(kk));
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
+                for (int j = 0; j < 4; ++j)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) d = dot2(kw[tt][kk][j], qw[kk][j], d);
-                sv[tt][h] = rows4_sum(d);
+                    for (int h = 0; h < kValuHeads; ++h) d[tt][h] = dot2(kw[j], qw[h][j], d[tt][h]);
             }
         }
         const int kr = 16 * wave + n;   // this lane's K row in the tile
-        float mt[kValuHeads];
-#pragma unroll
-        for (int h = 0; h < kValuHeads; ++h) mt[h] = -INFINITY;
+        float sc[NT][2], mt[2] = {-INFINITY, -INFINITY};
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) {
             const int valid = tt == 0 ? s.info.valid() : s.info.valid2;
 #pragma unroll
-            for (int h = 0; h < kValuHeads; ++h) {
-                sv[tt][h] = (kr < valid) ? sv[tt][h] * a.qk_scale_log2 : -INFINITY;
-                mt[h] = fmaxf(mt[h], sv[tt][h]);
+            for (int R = 0; R < 2; ++R) {
+                const float x = reduce4(d[tt][4 * R], d[tt][4 * R + 1], d[tt][4 * R + 2], d[tt][4 * R + 3]);
+                sc[tt][R] = (kr < valid) ? x * a.qk_scale_log2 : -INFINITY;
+                mt[R] = fmaxf(mt[R], sc[tt][R]);
             }
         }
-        float mu[kValuHeads], alpha[kValuHeads];
+        float mu[2], alpha[2];
         bool grew = false;
 #pragma unroll
-        for (int h = 0; h < kValuHeads; ++h) {
-            const float m_new = fmaxf(vm[h], row16_max(mt[h]));
-            mu[h] = (m_new == -INFINITY) ? 0.f : m_new;
-            alpha[h] = __builtin_amdgcn_exp2f(vm[h] - mu[h]);
-            grew |= m_new > vm[h];
-            vm[h] = m_new;
+        for (int R = 0; R < 2; ++R) {
+            const float m_new = fmaxf(vm[R], row16_max(mt[R]));
+            mu[R] = (m_new == -INFINITY) ? 0.f : m_new;
+            alpha[R] = __builtin_amdgcn_exp2f(vm[R] - mu[R]);
+            grew |= m_new > vm[R];
+            vm[R] = m_new;
         }
-        float p[NT][kValuHeads];
+        float p[NT][2];
 #pragma unroll
-        for (int h = 0; h < kValuHeads; ++h) {
+        for (int R = 0; R < 2; ++R) {
             float ps = 0.f;
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt) {
-                p[tt][h] = __builtin_amdgcn_exp2f(sv[tt][h] - mu[h]);
-                ps += p[tt][h];
+                p[tt][R] = __builtin_amdgcn_exp2f(sc[tt][R] - mu[R]);
+                ps += p[tt][R];
             }
-            vl[h] = vl[h] * alpha[h] + ps;
+            vl[R] = vl[R] * alpha[R] + ps;
         }
         // rescale the output sums only when some running max grew (alpha is
-        // exactly 1 wherever it did not)
+        // exactly 1 wherever it did not); a head's factor is uniform over its row
         if (__builtin_amdgcn_ballot_w64(grew) != 0) {
 #pragma unroll
-            for (int h = 0; h < kValuHeads; ++h)
+            for (int h = 0; h < kValuHeads; ++h) {
+                const float f = bitcast<float>(
+                    __builtin_amdgcn_readlane(bitcast<int>(alpha[h >> 2]), 16 * row_of[h]));
 #pragma unroll
-                for (int e = 0; e < 8; ++e) vacc[h][e] *= alpha[h];
+                for (int e = 0; e < 8; ++e) vacc[h][e] *= f;
+            }
         }
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) {
-            // bf16 pairs of P over rows (4g + 2j, 4g + 2j + 1): a lane of even
-            // row r packs (p[r], p[r + 1]); lane (n, g) then reads rows 4g, 4g + 2
-            // from its own 16-lane row (every row holds all scores)
+            // bf16 pairs of P over rows (t, t + 1): a lane of even token row
+            // packs (p[t], p[t + 1]); lane (n, g) reads token rows 4g and
+            // 4g + 2 from the row holding each head
+            uint32_t pk[2];
+#pragma unroll
+            for (int R = 0; R < 2; ++R) {
+                const float pn = dpp_f<kDppSwap1>(p[tt][R]);
+                pk[R] = bitcast<uint32_t>(bf16x2{static_cast<__bf16>(p[tt][R]), static_cast<__bf16>(pn)});
+            }
             uint32_t pp[kValuHeads][2];
 #pragma unroll
-            for (int h = 0; h < kValuHeads; ++h) {
-                const float pn = dpp_f<kDppSwap1>(p[tt][h]);
-                const uint32_t pk = bitcast<uint32_t>(bf16x2{static_cast<__bf16>(p[tt][h]), static_cast<__bf16>(pn)});
+            for (int h = 0; h < kValuHeads; ++h)
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
                     pp[h][j] = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(
-                        4 * ((lane & 48) | (4 * g + 2 * j)), static_cast<int>(pk)));
-            }
+                        4 * (16 * row_of[h] + 4 * g + 2 * j), static_cast<int>(pk[h >> 2])));
             u32x4 rows[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) rows[i] = s.kv[tt].v_row(i);
@@ -780,9 +810,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    vp[j][2 * d] = __builtin_amdgcn_perm(rows[2 * j + 1][d], rows[2 * j][d], kSelLo);
-                    vp[j][2 * d + 1] = __builtin_amdgcn_perm(rows[2 * j + 1][d], rows[2 * j][d], kSelHi);
+                for (int dd = 0; dd < 4; ++dd) {
+                    vp[j][2 * dd] = __builtin_amdgcn_perm(rows[2 * j + 1][dd], rows[2 * j][dd], kSelLo);
+                    vp[j][2 * dd + 1] = __builtin_amdgcn_perm(rows[2 * j + 1][dd], rows[2 * j][dd], kSelHi);
                 }
 #pragma unroll
             for (int h = 0; h < kValuHeads; ++h)
@@ -794,15 +824,19 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     auto flush_valu = [&](const TileInfo& ts) {
         const int row = ts.row;
         const int part = ts.part;
-        // every lane's output sums (its 4 rows, dims 8n ..) and the wave's max and sum per head
+        // every lane's output sums (its 4 rows, dims 8n ..), and each head's
+        // running max and sum from the first lane of its row
 #pragma unroll
         for (int h = 0; h < kValuHeads; ++h) {
             s_vacc[wave][g][h][2 * n] = f32x4{vacc[h][0], vacc[h][1], vacc[h][2], vacc[h][3]};
             s_vacc[wave][g][h][2 * n + 1] = f32x4{vacc[h][4], vacc[h][5], vacc[h][6], vacc[h][7]};
-            const float lw = row16_sum(vl[h]);
-            if (lane == 0) {
-                s_vm[wave][h] = vm[h];
-                s_vl[wave][h] = lw;
+        }
+#pragma unroll
+        for (int R = 0; R < 2; ++R) {
+            const float lw = row16_sum(vl[R]);
+            if (n == 0) {
+                s_vm[wave][hid[R]] = vm[R];
+                s_vl[wave][hid[R]] = lw;
             }
         }
         __syncthreads();
@@ -811,20 +845,20 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
         const int dq = static_cast<int>(threadIdx.x) & 31;
         float ms[kWaves], M = -INFINITY;
 #pragma unroll
-        for (int s = 0; s < kWaves; ++s) {
-            ms[s] = s_vm[s][hh];
-            M = fmaxf(M, ms[s]);
+        for (int w4 = 0; w4 < kWaves; ++w4) {
+            ms[w4] = s_vm[w4][hh];
+            M = fmaxf(M, ms[w4]);
         }
         const float M_use = (M == -INFINITY) ? 0.f : M;
         float wsum = 0.f;
         f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < kWaves; ++s) {
-            const float wt = __builtin_amdgcn_exp2f(ms[s] - M_use);
-            wsum += wt * s_vl[s][hh];
-            f32x4 sw = s_vacc[s][0][hh][dq];
+        for (int w4 = 0; w4 < kWaves; ++w4) {
+            const float wt = __builtin_amdgcn_exp2f(ms[w4] - M_use);
+            wsum += wt * s_vl[w4][hh];
+            f32x4 sw = s_vacc[w4][0][hh][dq];
 #pragma unroll
-            for (int gg = 1; gg < 4; ++gg) sw += s_vacc[s][gg][hh][dq];
+            for (int gg = 1; gg < 4; ++gg) sw += s_vacc[w4][gg][hh][dq];
             o += wt * sw;
         }
         if (hh < G) {
@@ -844,12 +878,14 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
         }
         __syncthreads();
 #pragma unroll
-        for (int h = 0; h < kValuHeads; ++h) {
-            vm[h] = -INFINITY;
-            vl[h] = 0.f;
+        for (int R = 0; R < 2; ++R) {
+            vm[R] = -INFINITY;
+            vl[R] = 0.f;
+        }
+#pragma unroll
+        for (int h = 0; h < kValuHeads; ++h)
 #pragma unroll
             for (int e = 0; e < 8; ++e) vacc[h][e] = 0.f;
-        }
     };
 
     // One exit, at the end of a full ring turn: every path back to the top
