@@ -332,7 +332,6 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     __shared__ f32x4 s_acc[4][kWaves][2][64];
     __shared__ float s_m[kWaves][64];
     __shared__ float s_l[kWaves][64];
-    __shared__ int32_t s_tmp[2 * kWaves];
     extern __shared__ int32_t s_dyn[];   // device schedule: len[B], tile prefix[B + 1]
     // VALU tile math: each wave's copy of its entry's Q ([head][dim group g]
     // [k-step], in the K operand's dim order), and the entry-end exchange
