@@ -114,6 +114,27 @@ def native_planner_us(seq_lens, num_kv_heads: int, n_workers: int, calls: int = 
     return (time.perf_counter() - t0) / calls * 1e6
 
 
+def plan_upload_us(seq_lens, num_kv_heads: int, n_workers: int, dev, copies: int = 200) -> float:
+    """Mean time, on the stream, of one upload of this step's plan words from
+    pinned host memory to the device: the copy the host-planned step queues
+    before its kernels (hpc_decode_plan_attn without an in-place plan)."""
+    import torch
+    import load_balanced_paged_step_amd as hd
+    words = hd.hpc_decode_plan(seq_lens, num_kv_heads, n_workers)
+    host = torch.from_numpy(words.copy()).pin_memory()
+    dst = torch.empty_like(host, device=dev)
+    for _ in range(10):
+        dst.copy_(host, non_blocking=True)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(copies):
+        dst.copy_(host, non_blocking=True)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / copies * 1e3
+
+
 def cpu_baseline(inp, alg_bytes: int):
     """The float64 oracle on the host cores, over the same workload (median of repeated runs)."""
     from oracle import decode_attention
@@ -238,6 +259,7 @@ def main() -> int:
     # (preallocated buffers; part of every --schedule host step, overlapping
     # the previous step's kernels)
     plan_us = native_planner_us(lens_host, inp.num_kv_heads, W, calls=200)
+    upload_us = plan_upload_us(lens_host, inp.num_kv_heads, W, dev)
 
     # timed region: K whole steps, bracketed by device synchronisation
     log(f"timed region: {args.steps} steps")
@@ -292,7 +314,8 @@ def main() -> int:
             "parallelism": "single GPU", "tile_math": args.tile_math,
         },
         "kernels": {"decode_us": round(decode_us, 3), "merge_us": round(combine_us, 3),
-                    "plan_host_us": round(plan_us, 2), "timed_calls": n_calls},
+                    "plan_host_us": round(plan_us, 2), "plan_upload_us": round(upload_us, 2),
+                    "timed_calls": n_calls},
         "roofline": {"bound": "hbm", "achieved": round(achieved_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": (measured_traffic(wl.name, args.schedule, W)
