@@ -17,7 +17,9 @@
 //    both walk the same tile sequence;
 //  * every wave owns a fixed 16-token slice (rows 16*wave .. +15) of every
 //    64-token tile and keeps its own online-softmax state; at the end of an
-//    entry the four states meet in LDS and one result per entry is written;
+//    entry each wave leaves its state in one of two LDS slots without
+//    waiting, and once both slots are taken (or the range ends) the four
+//    states of each pending entry meet and one result per entry is written;
 //  * a ring of PF = 2 slots is kept in flight across entry boundaries: each
 //    slot holds the K/V rows of one tile (bf16) or of two consecutive tiles
 //    of one entry (fp8, so a slot holds as many bytes either way), and for
@@ -66,6 +68,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
+#ifndef HPC_DECODE_PENDING
+#define HPC_DECODE_PENDING 2
+#endif
+constexpr int kPending = HPC_DECODE_PENDING;   // entry ends merged together (MFMA tile math)
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw (untyped) buffer, gfx9 family
 #ifndef HPC_DECODE_KV_POLICY
@@ -329,9 +335,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     float* __restrict__ lse_part, int32_t* __restrict__ merge_records, DecodeScalars a) {
     // entry ends: register i of every wave's eight accumulators, as two
     // 16-byte halves per lane, so each wave stores and loads whole f32x4s
-    __shared__ f32x4 s_acc[4][kWaves][2][64];
-    __shared__ float s_m[kWaves][64];
-    __shared__ float s_l[kWaves][64];
+    // entry ends (MFMA tile math): up to kPending entries' states wait in
+    // LDS, each wave depositing its own without a barrier, and are merged
+    // together when the slots are full or the worker's range ends
+    __shared__ f32x4 s_acc[kPending][4][kWaves][2][64];
+    __shared__ float s_m[kPending][kWaves][64];
+    __shared__ float s_l[kPending][kWaves][64];
+    __shared__ int32_t s_pend[kPending][2];   // output row and target of each pending entry
     extern __shared__ int32_t s_dyn[];   // device schedule: len[B], tile prefix[B + 1]
     // VALU tile math: each wave's copy of its entry's Q ([head][dim group g]
     // [k-step], in the K operand's dim order), and the entry-end exchange
@@ -523,66 +533,84 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     for (int nb = 0; nb < 8; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     bf16x8 qop[4];
 
-    auto flush = [&](const TileInfo& ts) {
-        const int row = ts.row;
-        const int part = ts.part;
+    // An entry ends: this wave's state goes to pending slot npend (every
+    // wave sees the same entries, so npend is the same in all of them), and
+    // the wave goes on without waiting for the others.
+    int npend = 0;
+    auto deposit = [&](const TileInfo& ts) {
         l += __shfl_xor(l, 16);
         l += __shfl_xor(l, 32);
-        s_m[wave][lane] = m;
-        s_l[wave][lane] = l;
+        const int p = npend;
+        s_m[p][wave][lane] = m;
+        s_l[p][wave][lane] = l;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            s_acc[i][wave][0][lane] = f32x4{acc[0][i], acc[1][i], acc[2][i], acc[3][i]};
-            s_acc[i][wave][1][lane] = f32x4{acc[4][i], acc[5][i], acc[6][i], acc[7][i]};
+            s_acc[p][i][wave][0][lane] = f32x4{acc[0][i], acc[1][i], acc[2][i], acc[3][i]};
+            s_acc[p][i][wave][1][lane] = f32x4{acc[4][i], acc[5][i], acc[6][i], acc[7][i]};
         }
-        __syncthreads();
-        float ms[kWaves], M = -INFINITY;
-#pragma unroll
-        for (int s = 0; s < kWaves; ++s) {
-            ms[s] = s_m[s][lane];
-            M = fmaxf(M, ms[s]);
+        if (threadIdx.x == 0) {
+            s_pend[p][0] = ts.row;
+            s_pend[p][1] = ts.part;
         }
-        const float M_use = (M == -INFINITY) ? 0.f : M;
-        float wt[kWaves], wsum = 0.f;
-#pragma unroll
-        for (int s = 0; s < kWaves; ++s) {
-            wt[s] = __builtin_amdgcn_exp2f(ms[s] - M_use);
-            wsum += wt[s] * s_l[s][lane];
-        }
-        float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < kWaves; ++s) {
-            const f32x4 lo = s_acc[wave][s][0][lane];
-            const f32x4 hi = s_acc[wave][s][1][lane];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                o[k] += wt[s] * lo[k];
-                o[4 + k] += wt[s] * hi[k];
-            }
-        }
-        const int slot = part;
-        if (n < G) {
-            const float inv = (wsum > 0.f) ? a.v_scale / wsum : 0.f;
-            const float lse_val = (wsum > 0.f) ? (M + __log2f(wsum)) * kLn2 : -INFINITY;
-            const int dim0 = 32 * g + 8 * wave;   // this wave merges register i = wave
-            if (slot < 0) {
-                bf16x8 ov;
-#pragma unroll
-                for (int nb = 0; nb < 8; ++nb) ov[nb] = static_cast<__bf16>(o[nb] * inv);
-                *reinterpret_cast<bf16x8*>(out + static_cast<int64_t>(row + n) * kHeadDim + dim0) = ov;
-                if (wave == 0 && g == 0) lse[row + n] = lse_val;
-            } else if (slot < a.max_partials) {   // a slot is always in range; the test keeps stray writes out
-                float* dst = o_part + (static_cast<int64_t>(slot) * G + n) * kHeadDim + dim0;
-                *reinterpret_cast<f32x4*>(dst) = f32x4{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
-                *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv};
-                if (wave == 0 && g == 0) lse_part[static_cast<int64_t>(slot) * G + n] = lse_val;
-            }
-        }
-        __syncthreads();
+        ++npend;
         m = -INFINITY;
         l = 0.f;
 #pragma unroll
         for (int nb = 0; nb < 8; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    };
+    // The pending entries meet: one (o, lse) per head and entry, bf16 out for
+    // a whole unit, an fp32 partial otherwise.  Wave w merges accumulator
+    // register w of all four waves (dims 32g + 8w .. +8 of head n).
+    auto merge_pending = [&]() {
+        __syncthreads();
+        for (int p = 0; p < npend; ++p) {
+            const int row = s_pend[p][0];
+            const int part = s_pend[p][1];
+            float ms[kWaves], M = -INFINITY;
+#pragma unroll
+            for (int s = 0; s < kWaves; ++s) {
+                ms[s] = s_m[p][s][lane];
+                M = fmaxf(M, ms[s]);
+            }
+            const float M_use = (M == -INFINITY) ? 0.f : M;
+            float wt[kWaves], wsum = 0.f;
+#pragma unroll
+            for (int s = 0; s < kWaves; ++s) {
+                wt[s] = __builtin_amdgcn_exp2f(ms[s] - M_use);
+                wsum += wt[s] * s_l[p][s][lane];
+            }
+            float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < kWaves; ++s) {
+                const f32x4 lo = s_acc[p][wave][s][0][lane];
+                const f32x4 hi = s_acc[p][wave][s][1][lane];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    o[k] += wt[s] * lo[k];
+                    o[4 + k] += wt[s] * hi[k];
+                }
+            }
+            const int slot = part;
+            if (n < G) {
+                const float inv = (wsum > 0.f) ? a.v_scale / wsum : 0.f;
+                const float lse_val = (wsum > 0.f) ? (M + __log2f(wsum)) * kLn2 : -INFINITY;
+                const int dim0 = 32 * g + 8 * wave;
+                if (slot < 0) {
+                    bf16x8 ov;
+#pragma unroll
+                    for (int nb = 0; nb < 8; ++nb) ov[nb] = static_cast<__bf16>(o[nb] * inv);
+                    *reinterpret_cast<bf16x8*>(out + static_cast<int64_t>(row + n) * kHeadDim + dim0) = ov;
+                    if (wave == 0 && g == 0) lse[row + n] = lse_val;
+                } else if (slot < a.max_partials) {   // a slot is always in range; the test keeps stray writes out
+                    float* dst = o_part + (static_cast<int64_t>(slot) * G + n) * kHeadDim + dim0;
+                    *reinterpret_cast<f32x4*>(dst) = f32x4{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
+                    *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv};
+                    if (wave == 0 && g == 0) lse_part[static_cast<int64_t>(slot) * G + n] = lse_val;
+                }
+            }
+        }
+        __syncthreads();
+        npend = 0;
     };
 
     auto consume = [&](const TileSlot<KV, NT>& s) {
@@ -893,9 +921,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     // so once slot 0 comes back empty all slots are; a later slot of the last
     // turn may be consumed empty, which changes nothing (its scores are all
     // -inf).  Slot 0 holds a tile on entry (workers without tiles returned
-    // above).  A slot that ends an entry is refilled before the entry is
-    // flushed, so the flush (whose barriers wait for the slowest wave) runs
-    // with every slot's loads in flight.
+    // above).  A slot that ends an entry is refilled before the entry's
+    // state is deposited (or, with the VALU tile math, merged), so the
+    // barriers of a merge, which wait for the slowest wave, run with every
+    // slot's loads in flight.
     for (;;) {
 #pragma unroll
         for (int j = 0; j < PF; ++j) {
@@ -905,11 +934,18 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
             plan_tile(planned[j]);
             load_tile(ring[j], planned[j]);
             if (ended.last()) {
-                if constexpr (VALU) flush_valu(ended);
-                else flush(ended);
+                if constexpr (VALU) {
+                    flush_valu(ended);
+                } else {
+                    deposit(ended);
+                    if (npend == kPending) merge_pending();
+                }
             }
         }
         if (!ring[0].info.real()) break;
+    }
+    if constexpr (!VALU) {
+        if (npend > 0) merge_pending();
     }
 }
 
