@@ -71,7 +71,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 #ifndef HPC_DECODE_PENDING
 #define HPC_DECODE_PENDING 2
 #endif
-constexpr int kPending = HPC_DECODE_PENDING;   // entry ends merged together (MFMA tile math)
+constexpr int kPending = HPC_DECODE_PENDING;   // entry ends merged together
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw (untyped) buffer, gfx9 family
 #ifndef HPC_DECODE_KV_POLICY
@@ -349,9 +349,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     // wave's running max and sum per head)
     __shared__ u32x4 s_vq[kWaves][kValuHeads][4][4];
     __shared__ u32x4 s_vq_sink[kWaves][4][4];
-    __shared__ f32x4 s_vacc[kWaves][4][kValuHeads][kHeadDim / 4];
-    __shared__ float s_vm[kWaves][kValuHeads];
-    __shared__ float s_vl[kWaves][kValuHeads];
+    __shared__ f32x4 s_vacc[kPending][kWaves][4][kValuHeads][kHeadDim / 4];
+    __shared__ float s_vm[kPending][kWaves][kValuHeads];
+    __shared__ float s_vl[kPending][kWaves][kValuHeads];
 
     // the host-planned walker reads lengths inside the tile loop: it keeps the
     // argument itself, whose read-only, unaliased provenance lets those reads
@@ -848,62 +848,32 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
         }
     };
 
-    auto flush_valu = [&](const TileInfo& ts) {
-        const int row = ts.row;
-        const int part = ts.part;
-        // every lane's output sums (its 4 rows, dims 8n ..), and each head's
-        // running max and sum from the first lane of its row
+    // Entry ends of the VALU tile math, as for the MFMA one: each wave
+    // deposits its state in pending slot nvpend without waiting (its output
+    // sums for its 4 rows, dims 8n ..; each head's running max and sum from
+    // the first lane of the head's row), and the pending entries meet when
+    // the slots are full or the range ends.
+    int nvpend = 0;
+    auto deposit_valu = [&](const TileInfo& ts) {
+        const int p = nvpend;
 #pragma unroll
         for (int h = 0; h < kValuHeads; ++h) {
-            s_vacc[wave][g][h][2 * n] = f32x4{vacc[h][0], vacc[h][1], vacc[h][2], vacc[h][3]};
-            s_vacc[wave][g][h][2 * n + 1] = f32x4{vacc[h][4], vacc[h][5], vacc[h][6], vacc[h][7]};
+            s_vacc[p][wave][g][h][2 * n] = f32x4{vacc[h][0], vacc[h][1], vacc[h][2], vacc[h][3]};
+            s_vacc[p][wave][g][h][2 * n + 1] = f32x4{vacc[h][4], vacc[h][5], vacc[h][6], vacc[h][7]};
         }
 #pragma unroll
         for (int R = 0; R < 2; ++R) {
             const float lw = row16_sum(vl[R]);
             if (n == 0) {
-                s_vm[wave][hid[R]] = vm[R];
-                s_vl[wave][hid[R]] = lw;
+                s_vm[p][wave][hid[R]] = vm[R];
+                s_vl[p][wave][hid[R]] = lw;
             }
         }
-        __syncthreads();
-        // thread t: head t / 32, dims 4 (t % 32) .. +4, over 4 waves x 4 dim groups
-        const int hh = static_cast<int>(threadIdx.x) >> 5;
-        const int dq = static_cast<int>(threadIdx.x) & 31;
-        float ms[kWaves], M = -INFINITY;
-#pragma unroll
-        for (int w4 = 0; w4 < kWaves; ++w4) {
-            ms[w4] = s_vm[w4][hh];
-            M = fmaxf(M, ms[w4]);
+        if (threadIdx.x == 0) {
+            s_pend[p][0] = ts.row;
+            s_pend[p][1] = ts.part;
         }
-        const float M_use = (M == -INFINITY) ? 0.f : M;
-        float wsum = 0.f;
-        f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int w4 = 0; w4 < kWaves; ++w4) {
-            const float wt = __builtin_amdgcn_exp2f(ms[w4] - M_use);
-            wsum += wt * s_vl[w4][hh];
-            f32x4 sw = s_vacc[w4][0][hh][dq];
-#pragma unroll
-            for (int gg = 1; gg < 4; ++gg) sw += s_vacc[w4][gg][hh][dq];
-            o += wt * sw;
-        }
-        if (hh < G) {
-            const float inv = (wsum > 0.f) ? a.v_scale / wsum : 0.f;
-            const float lse_val = (wsum > 0.f) ? (M + __log2f(wsum)) * kLn2 : -INFINITY;
-            const int slot = part;
-            if (slot < 0) {
-                const bf16x4 ov = bf16x4{static_cast<__bf16>(o[0] * inv), static_cast<__bf16>(o[1] * inv),
-                                         static_cast<__bf16>(o[2] * inv), static_cast<__bf16>(o[3] * inv)};
-                *reinterpret_cast<bf16x4*>(out + static_cast<int64_t>(row + hh) * kHeadDim + 4 * dq) = ov;
-                if (dq == 0) lse[row + hh] = lse_val;
-            } else if (slot < a.max_partials) {   // a slot is always in range; the test keeps stray writes out
-                float* dst = o_part + (static_cast<int64_t>(slot) * G + hh) * kHeadDim + 4 * dq;
-                *reinterpret_cast<f32x4*>(dst) = o * inv;
-                if (dq == 0) lse_part[static_cast<int64_t>(slot) * G + hh] = lse_val;
-            }
-        }
-        __syncthreads();
+        ++nvpend;
 #pragma unroll
         for (int R = 0; R < 2; ++R) {
             vm[R] = -INFINITY;
@@ -914,6 +884,52 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
 #pragma unroll
             for (int e = 0; e < 8; ++e) vacc[h][e] = 0.f;
     };
+    // thread t: head t / 32, dims 4 (t % 32) .. +4 of each pending entry,
+    // over 4 waves x 4 dim groups
+    auto merge_pending_valu = [&]() {
+        __syncthreads();
+        const int hh = static_cast<int>(threadIdx.x) >> 5;
+        const int dq = static_cast<int>(threadIdx.x) & 31;
+        for (int p = 0; p < nvpend; ++p) {
+            const int row = s_pend[p][0];
+            const int part = s_pend[p][1];
+            float ms[kWaves], M = -INFINITY;
+#pragma unroll
+            for (int w4 = 0; w4 < kWaves; ++w4) {
+                ms[w4] = s_vm[p][w4][hh];
+                M = fmaxf(M, ms[w4]);
+            }
+            const float M_use = (M == -INFINITY) ? 0.f : M;
+            float wsum = 0.f;
+            f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int w4 = 0; w4 < kWaves; ++w4) {
+                const float wt = __builtin_amdgcn_exp2f(ms[w4] - M_use);
+                wsum += wt * s_vl[p][w4][hh];
+                f32x4 sw = s_vacc[p][w4][0][hh][dq];
+#pragma unroll
+                for (int gg = 1; gg < 4; ++gg) sw += s_vacc[p][w4][gg][hh][dq];
+                o += wt * sw;
+            }
+            if (hh < G) {
+                const float inv = (wsum > 0.f) ? a.v_scale / wsum : 0.f;
+                const float lse_val = (wsum > 0.f) ? (M + __log2f(wsum)) * kLn2 : -INFINITY;
+                const int slot = part;
+                if (slot < 0) {
+                    const bf16x4 ov = bf16x4{static_cast<__bf16>(o[0] * inv), static_cast<__bf16>(o[1] * inv),
+                                             static_cast<__bf16>(o[2] * inv), static_cast<__bf16>(o[3] * inv)};
+                    *reinterpret_cast<bf16x4*>(out + static_cast<int64_t>(row + hh) * kHeadDim + 4 * dq) = ov;
+                    if (dq == 0) lse[row + hh] = lse_val;
+                } else if (slot < a.max_partials) {   // a slot is always in range; the test keeps stray writes out
+                    float* dst = o_part + (static_cast<int64_t>(slot) * G + hh) * kHeadDim + 4 * dq;
+                    *reinterpret_cast<f32x4*>(dst) = o * inv;
+                    if (dq == 0) lse_part[static_cast<int64_t>(slot) * G + hh] = lse_val;
+                }
+            }
+        }
+        __syncthreads();
+        nvpend = 0;
+    };
 
     // One exit, at the end of a full ring turn: every path back to the top
     // has re-issued all PF slots, so the compiler's load-counter waits let
@@ -922,9 +938,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     // turn may be consumed empty, which changes nothing (its scores are all
     // -inf).  Slot 0 holds a tile on entry (workers without tiles returned
     // above).  A slot that ends an entry is refilled before the entry's
-    // state is deposited (or, with the VALU tile math, merged), so the
-    // barriers of a merge, which wait for the slowest wave, run with every
-    // slot's loads in flight.
+    // state is deposited, so the barriers of a merge, which wait for the
+    // slowest wave, run with every slot's loads in flight.
     for (;;) {
 #pragma unroll
         for (int j = 0; j < PF; ++j) {
@@ -935,7 +950,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
             load_tile(ring[j], planned[j]);
             if (ended.last()) {
                 if constexpr (VALU) {
-                    flush_valu(ended);
+                    deposit_valu(ended);
+                    if (nvpend == kPending) merge_pending_valu();
                 } else {
                     deposit(ended);
                     if (npend == kPending) merge_pending();
@@ -944,7 +960,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
         }
         if (!ring[0].info.real()) break;
     }
-    if constexpr (!VALU) {
+    if constexpr (VALU) {
+        if (nvpend > 0) merge_pending_valu();
+    } else {
         if (npend > 0) merge_pending();
     }
 }

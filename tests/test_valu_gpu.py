@@ -29,9 +29,7 @@ def _gpu():
 
 
 def _both(inp, W, what, dev=None):
-    """VALU host-planned and device-scheduled steps against the oracle; the
-    two schedules' results for sequences one worker finishes alone agree
-    bitwise (same tiles, same arithmetic, same order)."""
+    """VALU host-planned and device-scheduled steps, each against the oracle."""
     dev = dev or to_device(inp)
     ref = run_oracle(inp)
     a = run_hip(inp, W, dev, tile_math="valu")
@@ -131,6 +129,18 @@ def test_bitwise_deterministic():
     r1 = run_hip_step(inp, 256, dev, tile_math="valu")
     r2 = run_hip_step(inp, 256, dev, tile_math="valu")
     assert np.array_equal(r1[0], r2[0]) and np.array_equal(r1[1], r2[1])
+
+
+def test_device_schedule_size_limit():
+    """2048 sequences (the device schedule's largest batch), where the LDS of
+    the VALU instantiation is fullest (its two pending entry slots plus the
+    lengths and their prefix)."""
+    rng = np.random.default_rng(2048)
+    lens = rng.integers(0, 300, size=2048)
+    lens[rng.random(2048) < 0.1] = 0
+    announce("valu device step at 2048 sequences, 2 kv heads")
+    inp = make_inputs([int(x) for x in lens], 8, 2, "bf16", seed=7, poison=True)
+    compare(inp, run_hip_step(inp, 256, tile_math="valu"), run_oracle(inp), "valu 2048 sequences")
 
 
 def test_group_above_eight_is_refused():
