@@ -85,6 +85,8 @@ def parse_args():
                          "schedules on batches from uniform 64x512 to 1x128K+31x4K, print one JSON line")
     ap.add_argument("--tile-math", choices=["mfma", "valu"], default="mfma",
                     help="tile arithmetic: matrix cores (default) or vector ALU dot2 products")
+    ap.add_argument("--fused-merge", action="store_true",
+                    help="device schedule: the decode kernel merges split sequences itself (no merge kernel)")
     ap.add_argument("--tile-math-sweep", action="store_true",
                     help="time the decode kernel with MFMA and with VALU tile math on workloads 2-5 "
                          "(device schedule) and print one JSON line")
@@ -205,6 +207,9 @@ def main() -> int:
     if args.skew_sweep:
         print(json.dumps(skew_sweep(dev, W, cus, args.steps, args.warmup)), flush=True)
         return 0
+    if args.fused_merge and args.schedule != "device":
+        print("--fused-merge needs the device schedule", file=sys.stderr)
+        return 2
     if args.tile_math_sweep:
         print(json.dumps(tile_math_sweep(dev, W, args.steps, args.warmup)), flush=True)
         return 0
@@ -233,7 +238,8 @@ def main() -> int:
         ws = torch.zeros(hd.hpc_decode_step_workspace_size(inp.batch, inp.num_q_heads, inp.num_kv_heads, W),
                          dtype=torch.uint8, device=dev)
         launchers = [hd.StepLauncher(q, ks[c], vs[c], bt, sl, out, lse, num_kv_heads=inp.num_kv_heads,
-                                     n_workers=W, workspace=ws, tile_math=args.tile_math, **scales)
+                                     n_workers=W, workspace=ws, tile_math=args.tile_math,
+                                     fused_merge=args.fused_merge, **scales)
                      for c in range(copies)]
 
         def one_step(i: int) -> None:
@@ -312,6 +318,7 @@ def main() -> int:
             "algorithmic_bytes": alg_bytes,
             "schedule": args.schedule + (", plan in place" if args.schedule == "host" and args.plan_in_place else ""),
             "parallelism": "single GPU", "tile_math": args.tile_math,
+            "merge": "in the decode kernel" if args.fused_merge else "separate kernel",
         },
         "kernels": {"decode_us": round(decode_us, 3), "merge_us": round(combine_us, 3),
                     "plan_host_us": round(plan_us, 2), "plan_upload_us": round(upload_us, 2),

@@ -82,6 +82,17 @@ typedef struct hpc_decode_params {
                                 /* HPC_TILE_MATH_VALU; both compute the same       */
                                 /* attention, the kernel being HBM-bound either    */
                                 /* way; VALU with G > 8 is HPC_ERR_UNSUPPORTED     */
+    int32_t fused_merge;        /* 0 (default): split sequences are merged by a    */
+                                /* second kernel.  1: hpc_decode_step only; the    */
+                                /* worker that finishes a split unit last merges   */
+                                /* it, and no second kernel runs.  Pays off when   */
+                                /* few workers share a unit (short sequences);     */
+                                /* correct for any batch.  The step's workspace    */
+                                /* must be zero-filled before its first use with   */
+                                /* this mode, and every step leaves it so.  The    */
+                                /* host-planned entry points return                */
+                                /* HPC_ERR_UNSUPPORTED for 1; other values are     */
+                                /* HPC_ERR_INVALID.                                */
 } hpc_decode_params;
 
 /*

@@ -96,11 +96,11 @@ def tile_math_code(tile_math) -> int:
 
 def make_params(num_q_heads, num_kv_heads, max_pages_per_seq, num_pages, kv_dtype, sm_scale,
                 k_scale=1.0, v_scale=1.0, head_dim=HEAD_DIM, page_size=PAGE,
-                tile_math="mfma") -> hpc_decode_params:
+                tile_math="mfma", fused_merge=False) -> hpc_decode_params:
     code = kv_dtype if isinstance(kv_dtype, int) else kv_dtype_code(kv_dtype)
     return hpc_decode_params(int(num_q_heads), int(num_kv_heads), int(head_dim), int(page_size),
                              int(max_pages_per_seq), int(num_pages), code, float(sm_scale),
-                             float(k_scale), float(v_scale), tile_math_code(tile_math))
+                             float(k_scale), float(v_scale), tile_math_code(tile_math), int(fused_merge))
 
 
 # ---------------------------------------------------------------- planner ---
@@ -325,7 +325,7 @@ def hpc_decode_step_workspace_size(batch: int, num_q_heads: int, num_kv_heads: i
 
 
 def _step_args(q, k_cache, v_cache, block_table, seq_lens, workspace, out, lse, num_kv_heads, n_workers,
-               sm_scale, k_scale, v_scale, tile_math="mfma"):
+               sm_scale, k_scale, v_scale, tile_math="mfma", fused_merge=False):
     if k_cache.dtype != v_cache.dtype or tuple(k_cache.shape) != tuple(v_cache.shape):
         raise ValueError("k_cache and v_cache must have the same dtype and shape")
     if q.dim() != 3 or k_cache.dim() != 4 or block_table.dim() != 2 or k_cache.shape[1] != num_kv_heads:
@@ -337,7 +337,7 @@ def _step_args(q, k_cache, v_cache, block_table, seq_lens, workspace, out, lse, 
         raise ValueError("out must match q's shape and lse must be [B, Hq]")
     params = make_params(q.shape[1], num_kv_heads, block_table.shape[1], k_cache.shape[0], k_cache.dtype,
                          sm_scale, k_scale, v_scale, head_dim=q.shape[2], page_size=k_cache.shape[2],
-                         tile_math=tile_math)
+                         tile_math=tile_math, fused_merge=fused_merge)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     return (params,
             (ctypes.c_int32(B), ctypes.c_int32(n_workers),
@@ -353,17 +353,22 @@ def _step_args(q, k_cache, v_cache, block_table, seq_lens, workspace, out, lse, 
 
 
 def hpc_decode_step_check(q, k_cache, v_cache, block_table, seq_lens, workspace, out, lse, *, num_kv_heads,
-                          n_workers, sm_scale, k_scale=1.0, v_scale=1.0, tile_math="mfma") -> int:
+                          n_workers, sm_scale, k_scale=1.0, v_scale=1.0, tile_math="mfma",
+                          fused_merge=False) -> int:
     params, args = _step_args(q, k_cache, v_cache, block_table, seq_lens, workspace, out, lse, num_kv_heads,
-                              n_workers, sm_scale, k_scale, v_scale, tile_math)
+                              n_workers, sm_scale, k_scale, v_scale, tile_math, fused_merge)
     return lib().hpc_decode_step_check(ctypes.byref(params), *args)
 
 
 def hpc_decode_step(q, k_cache, v_cache, block_table, seq_lens, workspace, out, lse, *, num_kv_heads,
-                    n_workers, sm_scale, k_scale=1.0, v_scale=1.0, stream=None, tile_math="mfma") -> None:
-    """One decode step with the schedule derived on the device from ``seq_lens``."""
+                    n_workers, sm_scale, k_scale=1.0, v_scale=1.0, stream=None, tile_math="mfma",
+                    fused_merge=False) -> None:
+    """One decode step with the schedule derived on the device from ``seq_lens``.
+    With ``fused_merge`` the decode kernel merges split sequences itself (no
+    second kernel); the workspace must then be zero-filled before its first
+    use, and every step leaves it so."""
     params, args = _step_args(q, k_cache, v_cache, block_table, seq_lens, workspace, out, lse, num_kv_heads,
-                              n_workers, sm_scale, k_scale, v_scale, tile_math)
+                              n_workers, sm_scale, k_scale, v_scale, tile_math, fused_merge)
     _lib.check(lib().hpc_decode_step(ctypes.byref(params), *args, _stream_handle(stream)), "hpc_decode_step")
 
 
@@ -391,13 +396,15 @@ class StepLauncher:
     """
 
     def __init__(self, q, k_cache, v_cache, block_table, seq_lens, out, lse, *, num_kv_heads, n_workers,
-                 sm_scale, k_scale=1.0, v_scale=1.0, workspace=None, stream=None, tile_math="mfma"):
+                 sm_scale, k_scale=1.0, v_scale=1.0, workspace=None, stream=None, tile_math="mfma",
+                 fused_merge=False):
         need = hpc_decode_step_workspace_size(q.shape[0], q.shape[1], num_kv_heads, n_workers)
-        if workspace is None:
-            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        if workspace is None:   # zero-filled, as the in-kernel merge needs
+            workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=q.device)
         self._keep = (q, k_cache, v_cache, block_table, seq_lens, out, lse, workspace)
         self.params, args = _step_args(q, k_cache, v_cache, block_table, seq_lens, workspace, out, lse,
-                                       num_kv_heads, n_workers, sm_scale, k_scale, v_scale, tile_math)
+                                       num_kv_heads, n_workers, sm_scale, k_scale, v_scale, tile_math,
+                                       fused_merge)
         self.workspace = workspace
         self._args = (ctypes.byref(self.params),) + args + (_stream_handle(stream),)
         status = lib().hpc_decode_step_check(*self._args[:-1])

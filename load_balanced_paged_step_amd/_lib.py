@@ -44,6 +44,7 @@ class hpc_decode_params(ctypes.Structure):
         ("k_scale", ctypes.c_float),
         ("v_scale", ctypes.c_float),
         ("tile_math", ctypes.c_int32),
+        ("fused_merge", ctypes.c_int32),
     ]
 
 

@@ -60,6 +60,8 @@ extern "C" int hpc_decode_check(const hpc_decode_params* p, const void* q, const
     if (G > HPC_DECODE_MAX_GROUP) return HPC_ERR_UNSUPPORTED;
     if (p->tile_math != HPC_TILE_MATH_MFMA && p->tile_math != HPC_TILE_MATH_VALU) return HPC_ERR_INVALID;
     if (p->tile_math == HPC_TILE_MATH_VALU && G > hpcd::kValuMaxGroup) return HPC_ERR_UNSUPPORTED;
+    if (p->fused_merge != 0 && p->fused_merge != 1) return HPC_ERR_INVALID;
+    if (p->fused_merge) return HPC_ERR_UNSUPPORTED;   // the host-planned step has no in-kernel merge
     if (p->max_pages_per_seq < 1 || p->num_pages < 1) return HPC_ERR_INVALID;
     if (!std::isfinite(p->sm_scale) || !std::isfinite(p->k_scale) || !std::isfinite(p->v_scale))
         return HPC_ERR_INVALID;
@@ -256,6 +258,7 @@ extern "C" int hpc_decode_step_check(const hpc_decode_params* p, int32_t batch, 
     if (p->tile_math != HPC_TILE_MATH_MFMA && p->tile_math != HPC_TILE_MATH_VALU) return HPC_ERR_INVALID;
     if (p->tile_math == HPC_TILE_MATH_VALU && p->num_q_heads / p->num_kv_heads > hpcd::kValuMaxGroup)
         return HPC_ERR_UNSUPPORTED;
+    if (p->fused_merge != 0 && p->fused_merge != 1) return HPC_ERR_INVALID;
     if (p->max_pages_per_seq < 1 || p->num_pages < 1) return HPC_ERR_INVALID;
     if (!std::isfinite(p->sm_scale) || !std::isfinite(p->k_scale) || !std::isfinite(p->v_scale))
         return HPC_ERR_INVALID;
@@ -306,6 +309,7 @@ extern "C" int hpc_decode_step(const hpc_decode_params* p, int32_t batch, int32_
     da.num_pages = p->num_pages;
     da.qk_scale_log2 = static_cast<float>(static_cast<double>(p->sm_scale) * p->k_scale * 1.4426950408889634);
     da.v_scale = p->v_scale;
+    da.fused_merge = p->fused_merge;
 
     hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
     hpcd::CombineArgs ca{};
@@ -320,7 +324,7 @@ extern "C" int hpc_decode_step(const hpc_decode_params* p, int32_t batch, int32_
 
     ca.n_workers = n_workers;
     const int64_t units = static_cast<int64_t>(batch) * p->num_kv_heads;
-    const bool any_split = n_workers > 1;
+    const bool any_split = n_workers > 1 && !p->fused_merge;   // fused: the decode kernel merges
 
     claim_profile_events(ev, true, any_split);
     if (hpcd::launch_decode(da, p->kv_dtype, p->tile_math, n_workers, true, stream, ev[0], ev[1]) != 0) return HPC_ERR_HIP;

@@ -72,6 +72,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 #define HPC_DECODE_PENDING 2
 #endif
 constexpr int kPending = HPC_DECODE_PENDING;   // entry ends merged together
+constexpr int kFusedUnroll = 8;                 // partials' loads in flight per lane, in-kernel merge
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw (untyped) buffer, gfx9 family
 #ifndef HPC_DECODE_KV_POLICY
@@ -314,6 +315,7 @@ struct DecodeScalars {
     int32_t max_partials;   // partial slots the workspace holds
     float qk_scale_log2, v_scale;
     int32_t n_workers;      // the grid size (passed so no hidden argument is read)
+    int32_t fused_merge;    // device schedule: split units merged by their last-arriving worker
 };
 
 // Passes kernel arguments through one empty scalar-register asm, so that
@@ -342,6 +344,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     __shared__ float s_m[kPending][kWaves][64];
     __shared__ float s_l[kPending][kWaves][64];
     __shared__ int32_t s_pend[kPending][2];   // output row and target of each pending entry
+    __shared__ int32_t s_last;                 // in-kernel merge: this worker arrived last at the unit
     extern __shared__ int32_t s_dyn[];   // device schedule: len[B], tile prefix[B + 1]
     // VALU tile math: each wave's copy of its entry's Q ([head][dim group g]
     // [k-step], in the K operand's dim order), and the entry-end exchange
@@ -965,6 +968,92 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     } else {
         if (npend > 0) merge_pending();
     }
+
+    // In-kernel merge (device schedule, on request): every partial of this
+    // worker is written.  One agent-scope release makes them visible to the
+    // other dies; then, for each split unit the worker holds a share of
+    // (its first entry, and its last when that is another unit), one
+    // atomic count in the unit's merge record.  The worker that brings the
+    // count to S_u merges the unit and sets the count back to zero, so the
+    // records are ready for the next step.  No worker waits for another.
+    if constexpr (DEV) {
+        if (a.fused_merge) {
+            __syncthreads();   // every wave's partial stores precede the release below
+            const int uA = u_first;
+            int bB, hB, tB;
+            sched.locate_uniform(w_end - 1, bB, hB, tB);
+            const int uB = bB * Hkv + hB;
+#pragma unroll 1
+            for (int k = 0; k < 2; ++k) {
+                const int u = k == 0 ? uA : uB;
+                if (k == 1 && uB == uA) break;
+                const int bu = u / Hkv;
+                const int S = sched.parts(bu, u - bu * Hkv);
+                if (S < 2) continue;
+                int32_t* rec = merge_records + kRecordWords * u;
+                if (threadIdx.x == 0) {
+                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+                    const int before = __hip_atomic_fetch_add(rec + 5, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    const int last = before == S - 1;
+                    if (last) {
+                        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                        __hip_atomic_store(rec + 5, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                    s_last = last;
+                }
+                __syncthreads();
+                if (s_last) {
+                    // the unit's partial slots, from its record (written by its first
+                    // worker, which released it with its own partials)
+                    const int w_first = rec[1], first_slot = rec[2];
+                    const int64_t Pu = rec[3], T = rec[4];
+                    auto slot_of = [&](int kk) -> int {
+                        if (kk == 0) return first_slot;
+                        if (static_cast<int64_t>(a.n_workers) <= T) return 2 * (w_first + kk);
+                        return 2 * small_quot((Pu + kk + 1) * a.n_workers - 1, T);
+                    };
+                    const int64_t row0 = static_cast<int64_t>(bu) * Hq + (u - bu * Hkv) * G;
+                    const int dq = static_cast<int>(threadIdx.x) & 31;
+                    for (int hh = static_cast<int>(threadIdx.x) >> 5; hh < G; hh += kDecodeThreads / 32) {
+                        float mm = -INFINITY, ww = 0.f;
+                        f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+                        for (int i0 = 0; i0 < S; i0 += kFusedUnroll) {
+                            float lv[kFusedUnroll];
+                            f32x4 ov[kFusedUnroll];
+#pragma unroll
+                            for (int j = 0; j < kFusedUnroll; ++j) {
+                                const int i = i0 + j;
+                                const int slot = slot_of(i < S ? i : 0);
+                                const int64_t pidx = (slot < a.max_partials ? static_cast<int64_t>(slot) : 0) * G + hh;
+                                lv[j] = (i < S && slot < a.max_partials) ? lse_part[pidx] * kLog2e : -INFINITY;
+                                ov[j] = *reinterpret_cast<const f32x4*>(o_part + pidx * kHeadDim + 4 * dq);
+                            }
+                            float mk = mm;
+#pragma unroll
+                            for (int j = 0; j < kFusedUnroll; ++j) mk = fmaxf(mk, lv[j]);
+                            const float m_use = (mk == -INFINITY) ? 0.f : mk;
+                            const float f = __builtin_amdgcn_exp2f(mm - m_use);
+                            o *= f;
+                            ww *= f;
+#pragma unroll
+                            for (int j = 0; j < kFusedUnroll; ++j) {
+                                const float e = __builtin_amdgcn_exp2f(lv[j] - m_use);
+                                o += e * ov[j];
+                                ww += e;
+                            }
+                            mm = mk;
+                        }
+                        const float inv = ww > 0.f ? 1.f / ww : 0.f;
+                        const bf16x4 res = bf16x4{static_cast<__bf16>(o[0] * inv), static_cast<__bf16>(o[1] * inv),
+                                                  static_cast<__bf16>(o[2] * inv), static_cast<__bf16>(o[3] * inv)};
+                        *reinterpret_cast<bf16x4*>(out + (row0 + hh) * kHeadDim + 4 * dq) = res;
+                        if (dq == 0) lse[row0 + hh] = ww > 0.f ? (mm + __log2f(ww)) * kLn2 : -INFINITY;
+                    }
+                }
+                __syncthreads();   // s_last is rewritten for the next unit
+            }
+        }
+    }
 }
 
 // Merge of split units: SPLIT workgroups per (merge record, query head of
@@ -1228,7 +1317,7 @@ constexpr int kPrefetchFp8 = HPC_DECODE_PREFETCH_FP8;
 template <int KV, int PF, bool DEV, bool VALU>
 void launch_decode_t(const DecodeArgs& a, int n_workers, size_t lds, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     const DecodeScalars sc{a.batch,        a.num_kv_heads,  a.group,   a.max_pages_per_seq, a.num_pages,
-                           a.max_partials, a.qk_scale_log2, a.v_scale, n_workers};
+                           a.max_partials, a.qk_scale_log2, a.v_scale, n_workers, a.fused_merge};
     constexpr int kTilesPerSlot = KV == HPC_KV_FP8_E4M3 ? HPC_DECODE_PAIR_FP8 + 1 : 1;
     hipExtLaunchKernelGGL((decode_kernel<KV, PF, kTilesPerSlot, DEV, VALU>), dim3(n_workers), dim3(kDecodeThreads),
                           static_cast<std::uint32_t>(lds), s, e0, e1, 0u,

@@ -45,6 +45,7 @@ struct DecodeArgs {
     int32_t max_partials;        // partial slots in the workspace
     float qk_scale_log2;         // sm_scale * k_scale * log2(e)
     float v_scale;
+    int32_t fused_merge;         // device schedule: the decode kernel merges split units itself
 };
 
 struct CombineArgs {

@@ -84,17 +84,18 @@ def run_hip_plan(inp, plan_words, dev=None, tile_math="mfma"):
     return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
 
-def run_hip_step(inp, n_workers: int, dev=None, tile_math="mfma"):
+def run_hip_step(inp, n_workers: int, dev=None, tile_math="mfma", fused_merge=False, workspace=None):
     """One device-scheduled decode step (hpc_decode_step: schedule from the
-    lengths on the GPU, decode and merge kernels)."""
+    lengths on the GPU, decode and merge kernels, or the decode kernel alone
+    with ``fused_merge``).  A given workspace is reused as it is."""
     if dev is None:
         dev = to_device(inp)
     ws_bytes = hd.hpc_decode_step_workspace_size(inp.batch, inp.num_q_heads, inp.num_kv_heads, n_workers)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    ws = workspace if workspace is not None else torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
     out = torch.empty_like(dev["q"])
     lse = torch.empty(dev["q"].shape[:2], dtype=torch.float32, device="cuda")
     hd.hpc_decode_step(dev["q"], dev["k"], dev["v"], dev["bt"], dev["sl"], ws, out, lse,
                        num_kv_heads=inp.num_kv_heads, n_workers=n_workers, sm_scale=inp.sm_scale,
-                       k_scale=inp.k_scale, v_scale=inp.v_scale, tile_math=tile_math)
+                       k_scale=inp.k_scale, v_scale=inp.v_scale, tile_math=tile_math, fused_merge=fused_merge)
     torch.cuda.synchronize()
     return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)

@@ -225,6 +225,22 @@ def test_check_tile_math():
         hd.make_params(8, 1, 4, 8, hd.HPC_KV_BF16, 0.1, tile_math="simd")
 
 
+def test_check_fused_merge():
+    f = _Fake()
+    f.params.fused_merge = 1                   # the host-planned step has no in-kernel merge
+    assert f.check() == hd.HPC_ERR_UNSUPPORTED
+    f.params.fused_merge = 2
+    assert f.check() == hd.HPC_ERR_INVALID
+    lib = _lib.lib()
+    ptr = ctypes.c_void_p(0x1000)
+    need = hd.hpc_decode_step_workspace_size(2, 8, 1, 16)
+    for val, code in ((0, hd.HPC_OK), (1, hd.HPC_OK), (-1, hd.HPC_ERR_INVALID), (3, hd.HPC_ERR_INVALID)):
+        params = hd.make_params(8, 1, 4, 8, hd.HPC_KV_BF16, 1 / np.sqrt(128))
+        params.fused_merge = val
+        assert lib.hpc_decode_step_check(ctypes.byref(params), 2, 16, ptr, ptr, ptr, ptr, ptr, ptr, need,
+                                         ptr, ptr) == code, val
+
+
 def test_params_struct_matches_header():
     """The ctypes mirror of hpc_decode_params has the header's fields, in order."""
     import re
