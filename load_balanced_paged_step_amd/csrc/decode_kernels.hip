@@ -40,7 +40,12 @@
 //    value); k_scale folds into the score scale, v_scale into the output.
 // Merge kernel: SPLIT workgroups per (split unit, query head), SPLIT = 4
 // for small grids (a unit shared by many workers is read by several CUs),
-// 1 for many units.
+// 1 for many units.  On request (device schedule), the decode kernel's
+// last-arriving worker of each split unit merges it instead, counted with
+// one atomic per unit after an agent-scope release; that is correct for
+// any batch but was slower than the merge kernel on every batch measured.
+// The VALU tile math (dot2 products instead of MFMA, G <= 8) shares the
+// ring, schedule and merges.
 // Lane layout: lane = n + 16 g (n = lane & 15, g = lane >> 4).
 //   QK:  A = K rows [token n][8 dims per k-step, in the order KvTile loads
 //        them], B = Q^T [head n][the same dims], D[token 4g+i][head n] in
