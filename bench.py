@@ -320,6 +320,8 @@ def main() -> int:
             "parallelism": "single GPU", "tile_math": args.tile_math,
             "merge": "in the decode kernel" if args.fused_merge else "separate kernel",
         },
+        "step_clocks_us": {"host_clock": round(wall / args.steps * 1e6, 3),
+                           "stream_events": round(ev_ms / args.steps * 1e3, 3)},
         "kernels": {"decode_us": round(decode_us, 3), "merge_us": round(combine_us, 3),
                     "plan_host_us": round(plan_us, 2), "plan_upload_us": round(upload_us, 2),
                     "timed_calls": n_calls},
