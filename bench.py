@@ -256,6 +256,7 @@ def main() -> int:
         def one_step(i: int) -> None:
             planned[i % copies](lens_np)
 
+    clock_warmup(dev, cus)
     log(f"warmup {args.warmup} steps")
     for i in range(args.warmup):
         one_step(i)
@@ -379,6 +380,21 @@ def main() -> int:
     return 0
 
 
+def clock_warmup(dev, cus: int, seconds: float = 0.2) -> None:
+    """About `seconds` of streaming reads, so that nothing is timed while the
+    GPU's clocks are still ramping up (set-up, outside every timed region)."""
+    import torch
+
+    import load_balanced_paged_step_amd as hd
+    buf = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    sink = torch.empty(cus * 4, dtype=torch.float32, device=dev)
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end:
+        hd.hpc_probe_read(buf, sink, cus * 4)
+        torch.cuda.synchronize()
+    del buf, sink
+
+
 def tile_math_sweep(dev, W: int, steps: int, warmup: int) -> dict:
     """Decode-kernel time with the MFMA and with the VALU tile math, same
     inputs, same device-scheduled step, alternating rounds of the two so
@@ -464,15 +480,7 @@ def skew_sweep(dev, W: int, cus: int, steps: int, warmup: int) -> dict:
     from workloads import make_inputs
 
     steps = min(steps, 50)
-    # about 0.2 s of streaming reads first, so the first batch is not timed
-    # while the GPU's clocks are still ramping up
-    buf = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
-    sink = torch.empty(cus * 4, dtype=torch.float32, device=dev)
-    t_end = time.perf_counter() + 0.2
-    while time.perf_counter() < t_end:
-        hd.hpc_probe_read(buf, sink, cus * 4)
-        torch.cuda.synchronize()
-    del buf, sink
+    clock_warmup(dev, cus)   # the first batch is not timed while clocks ramp up
     rows = []
     for name, lens in SKEW_BATCHES:
         inp = make_inputs(lens, 8, 1, "bf16", seed=4)
