@@ -405,6 +405,7 @@ def tile_math_sweep(dev, W: int, steps: int, warmup: int) -> dict:
     import load_balanced_paged_step_amd as hd
     from workloads import WORKLOADS, workload_inputs
 
+    clock_warmup(dev, torch.cuda.get_device_properties(dev).multi_processor_count)
     rows = []
     for cfg in (2, 3, 4, 5):
         inp = workload_inputs(cfg)
