@@ -272,7 +272,11 @@ int hpc_decode_plan_attn(const hpc_decode_params* params, const int32_t* seq_len
  *              [0, max_pages_per_seq * 64] so no read leaves the block table
  * workspace    device, >= hpc_decode_step_workspace_size(batch, Hq, H_kv, W);
  *              calls that may run concurrently (other streams) need
- *              separate workspaces
+ *              separate workspaces.  With params->fused_merge = 1 the merge
+ *              kernel is not launched: the decode kernel's last worker to
+ *              finish a split sequence merges it, counting arrivals in the
+ *              workspace, which must be zero-filled before its first use in
+ *              that mode (every call leaves the counts at zero)
  * Other arguments as for hpc_decode_attn.  Errors as hpc_decode_attn, plus
  * HPC_ERR_UNSUPPORTED beyond those limits and HPC_ERR_INVALID when
  * batch * max_pages_per_seq * H_kv does not fit in int32.
