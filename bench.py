@@ -331,7 +331,12 @@ def main() -> int:
                      "traffic": (measured_traffic(wl.name, args.schedule, W)
                                  if args.tile_math == "mfma" else None),
                      "kernel": "decode_kernel", "bytes_per_launch": alg_bytes,
-                     "kernel_us_hip_events": round(decode_us, 3)},
+                     "kernel_us_hip_events": round(decode_us, 3),
+                     "duration_source": ("decode kernel alone: mean of HIP events stamped by each launch's "
+                                         "dispatch (kernel start to end), on the launch stream, in a pass of "
+                                         "the same steps right after the timed region"),
+                     "step_frac": round(step_tbps * 1e3 / HBM_PEAK_GBPS, 4),
+                     "step_frac_source": "whole step (decode + merge + gaps): algorithmic bytes / us_per_step"},
     }
 
     if args.probe == "on":

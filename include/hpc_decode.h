@@ -99,6 +99,10 @@ typedef struct hpc_decode_params {
  * Upper bound, in int32 words, of the plan for this batch shape:
  * 16 + (W + 1) + 4 (W + U) + 3 U with U = batch * num_kv_heads, W = n_workers
  * (a work list holds at most W + U - 1 entries and at most U merge records).
+ * The plan is the work list of the per-step scheduler of "vLLM x HPC-Ops
+ * ...", §Attention Backend: Dynamic Load-Balanced Scheduling (tiles spread
+ * evenly over a persistent grid); the bound lets a caller size the plan
+ * buffer once per batch shape, before the lengths are known.
  * Returns a negative status for batch < 0, num_kv_heads < 1 or n_workers < 1.
  */
 int64_t hpc_decode_plan_size(int32_t batch, int32_t num_kv_heads, int32_t n_workers);
@@ -169,6 +173,12 @@ int64_t hpc_decode_plan_words(const int32_t* plan);
  * Device workspace, in bytes, that hpc_decode_attn needs for this plan:
  * n_partials * G * 128 fp32 partial outputs followed (256-byte aligned) by
  * n_partials * G fp32 partial log-sum-exps.  0 when no sequence is split.
+ * The partials are those of sequences the scheduler of §Attention Backend:
+ * Dynamic Load-Balanced Scheduling ("vLLM x HPC-Ops ...") spreads over
+ * several workers; the pages do not describe how they are combined, and the
+ * log-sum-exp merge is the reading used here.  plan is host memory (the
+ * words of hpc_decode_plan or hpc_decode_plan_static); a negative status is
+ * returned for a NULL or malformed plan or heads that do not group.
  */
 int64_t hpc_decode_workspace_size(const int32_t* plan, int32_t num_q_heads,
                                   int32_t num_kv_heads);
@@ -176,7 +186,13 @@ int64_t hpc_decode_workspace_size(const int32_t* plan, int32_t num_q_heads,
 /*
  * One decode step on `stream`: the persistent decode kernel (grid = the
  * plan's W workgroups, each walking its entries), then, when the plan has
- * merge records, the log-sum-exp merge kernel.
+ * merge records, the log-sum-exp merge kernel.  This is the attention of
+ * "vLLM x HPC-Ops ...", §Attention Backend: Dynamic Load-Balanced
+ * Scheduling, run over a plan made by hpc_decode_plan: each worker streams
+ * its 64-token tiles of K and V (one page each) and keeps an online softmax;
+ * a sequence held by several workers is merged by log-sum-exp.  The decode
+ * shapes measured on the pages (§Attention Decode under Mixed-Length
+ * Batches) are 64 x 0.5K and 1 x 128K + 31 x 4K tokens.
  *
  * q            device bf16 [batch][Hq][128], contiguous
  * k_cache      device bf16 or fp8 [num_pages][H_kv][64][128], contiguous

@@ -12,6 +12,21 @@ from oracle import decode_attention, cache_bits_to_f64
 OUT_TOL = {"bf16": 1e-2, "fp8_e4m3": 3e-2}
 # absolute log-sum-exp tolerance (natural log)
 LSE_TOL = {"bf16": 1e-3, "fp8_e4m3": 1e-2}
+# Per-unit output bound, for every (sequence, KV head) unit u and its G query
+# heads: max|out_u - ref_u| <= UNIT_TOL * max|ref_u| + UNIT_ABS.  The output
+# is an fp32 result rounded to bf16 (relative error <= 2^-8), and the
+# probabilities are rounded to bf16 before P V (relative error <= 2^-8 each,
+# summing like a random walk over the tokens, about 2^-8/sqrt(3) of |out| at
+# the element that is largest), so the ratio stays near 4e-3 whatever the
+# length; 1e-2 leaves a factor of about 2.5.  The same bound holds for fp8
+# KV, whose codes widen to bf16 exactly.  The global bound above cannot see
+# a long sequence's output at all: its |out| is far below 1e-2 max|V|.
+UNIT_TOL = 1e-2
+UNIT_ABS = 1e-6
+
+# worst per-unit ratio max|out_u - ref_u| / max|ref_u| seen in this session,
+# per KV type (printed in the test summary)
+WORST_UNIT = {}
 
 
 def announce(msg: str) -> None:
@@ -63,7 +78,35 @@ def compare(inp, got, ref, what=""):
     lse_err = float(np.abs(lse[~neg] - ref_lse[~neg]).max()) if (~neg).any() else 0.0
     assert lse_err <= LSE_TOL[inp.kv_dtype], f"{what}: max|lse-ref| = {lse_err:.3e}"
     assert np.all(out[neg.nonzero()] == 0), f"{what}: empty sequences must give zeros"
-    return {"max_err": max_err, "tol": tol, "lse_err": lse_err}
+    ratio, where = unit_check(out, ref_out, inp.num_kv_heads, what)
+    prev = WORST_UNIT.get(inp.kv_dtype)
+    if prev is None or ratio > prev[0]:
+        WORST_UNIT[inp.kv_dtype] = (ratio, f"{what} {where}")
+    return {"max_err": max_err, "tol": tol, "lse_err": lse_err, "worst_unit_ratio": ratio}
+
+
+def unit_check(out, ref_out, num_kv_heads: int, what: str = ""):
+    """Per-unit bound: for every (sequence b, KV head h) the G query heads'
+    outputs satisfy max|out - ref| <= UNIT_TOL max|ref| + UNIT_ABS.  Returns
+    the worst ratio max|out - ref| / max|ref| over non-zero units and where."""
+    B, Hq = out.shape[:2]
+    G = Hq // num_kv_heads
+    o = out.reshape(B, num_kv_heads, G * out.shape[-1])
+    r = ref_out.reshape(B, num_kv_heads, G * out.shape[-1])
+    err = np.abs(o - r).max(axis=-1)
+    mag = np.abs(r).max(axis=-1)
+    bad = err > UNIT_TOL * mag + UNIT_ABS
+    if bad.any():
+        b, h = map(int, np.argwhere(bad)[0])
+        raise AssertionError(f"{what}: unit (seq {b}, kv head {h}): max|out-ref| = {err[b, h]:.3e} > "
+                             f"{UNIT_TOL:g} * max|ref| ({mag[b, h]:.3e}) + {UNIT_ABS:g}; "
+                             f"{int(bad.sum())} units fail")
+    nz = mag > 0
+    if not nz.any():
+        return 0.0, "(all units zero)"
+    ratio = np.where(nz, err / np.where(nz, mag, 1.0), 0.0)
+    b, h = map(int, np.unravel_index(np.argmax(ratio), ratio.shape))
+    return float(ratio[b, h]), f"(seq {b}, kv head {h})"
 
 
 def run_hip_plan(inp, plan_words, dev=None, tile_math="mfma"):

@@ -1,8 +1,10 @@
 """Parity of the HIP decode path (through the C ABI) against the float64 oracle.
 
 Tolerances: max|out - oracle| <= 1e-2 max|V| (bf16 KV) or 3e-2 max|V| (fp8
-KV, oracle on the dequantised cache); |lse - oracle| <= 1e-3 (bf16) or 1e-2
-(fp8).  Plans are compared word for word; determinism and page-permutation
+KV, oracle on the dequantised cache); for every (sequence, KV head) unit,
+max|out_u - oracle_u| <= 1e-2 max|oracle_u| + 1e-6 (both KV types; this is
+the bound that sees long sequences, whose outputs are far below max|V|);
+|lse - oracle| <= 1e-3 (bf16) or 1e-2 (fp8).  Plans are compared word for word; determinism and page-permutation
 invariance are bitwise.
 """
 import numpy as np
@@ -13,7 +15,7 @@ import load_balanced_paged_step_amd as hd
 from oracle import build_plan, split_decode_attention, parse_plan
 from workloads import make_inputs, workload_inputs
 
-from decode_harness import announce, compare, run_hip, run_oracle, to_device
+from decode_harness import UNIT_ABS, UNIT_TOL, announce, compare, run_hip, run_oracle, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -154,7 +156,10 @@ def test_partials_match_oracle_split():
         slot = int(e[3])
         if slot < 0:
             continue
-        assert np.abs(o_part[slot] - o_ref).max() <= 1e-2 * 4.5
+        # per-slot bound, as for a unit's output: the partial is fp32, so
+        # only the bf16 rounding of the probabilities enters it
+        err = np.abs(o_part[slot] - o_ref).max()
+        assert err <= UNIT_TOL * np.abs(o_ref).max() + UNIT_ABS, (slot, err, np.abs(o_ref).max())
         assert np.abs(lse_part[slot] - l_ref).max() <= 1e-3
         checked += 1
     assert checked == P > 0

@@ -3,8 +3,9 @@ decode kernel's last-arriving worker of every split unit merges the unit's
 partials, and no merge kernel runs.
 
 Checked against the float64 oracle like every decode result (max|out -
-oracle| <= 1e-2 max|V| for bf16 KV, 3e-2 for fp8; |lse - oracle| <= 1e-3 /
-1e-2), with exact tile-visit counts (Q = 0: lse = ln L_b, as in
+oracle| <= 1e-2 max|V| for bf16 KV, 3e-2 for fp8; per (sequence, KV head)
+unit max|out_u - oracle_u| <= 1e-2 max|oracle_u| + 1e-6; |lse - oracle| <=
+1e-3 / 1e-2), with exact tile-visit counts (Q = 0: lse = ln L_b, as in
 test_tile_visits_gpu.py), for both tile maths, and over repeated steps that
 reuse one workspace while the lengths change, since each unit's arrival
 count lives in the workspace and every step must leave it at zero.

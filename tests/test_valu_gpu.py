@@ -6,8 +6,9 @@ The VALU path computes the same attention as the MFMA one: scores from bf16
 K and Q with fp32 accumulation, an exp2-domain online softmax, P rounded to
 bf16 for P V with fp32 accumulation.  Tolerances are the same as for every
 decode result: max|out - oracle| <= 1e-2 max|V| (bf16 KV) or 3e-2 max|V|
-(fp8 KV, oracle on the dequantised cache); |lse - oracle| <= 1e-3 (bf16) or
-1e-2 (fp8).
+(fp8 KV, oracle on the dequantised cache); per (sequence, KV head) unit
+max|out_u - oracle_u| <= 1e-2 max|oracle_u| + 1e-6; |lse - oracle| <= 1e-3
+(bf16) or 1e-2 (fp8).
 """
 import numpy as np
 import pytest
