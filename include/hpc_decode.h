@@ -317,6 +317,37 @@ int64_t hpc_decode_step_workspace_size(int32_t batch, int32_t num_q_heads, int32
                                        int32_t n_workers);
 
 /*
+ * hpc_decode_step for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same kernels and results as hpc_decode_step, with the step's scratch
+ * (partial outputs, partial log-sum-exps and merge records, the layout of
+ * hpc_decode_step_workspace_size) held in a fixed device array that the
+ * library owns instead of a workspace argument.  The call allocates nothing
+ * and frees nothing.
+ *
+ * The array holds hpc_decode_step_noalloc_max_bytes() bytes (16 MiB) on every
+ * GPU the library runs on, kept until the process ends.  Shapes whose
+ * hpc_decode_step_workspace_size exceeds it return HPC_ERR_TOO_SMALL before
+ * any HIP call (for example W = 1024 workers with G = 16 heads per KV head);
+ * W = 256 fits up to G = 16, W = 1024 up to G = 8.
+ * Every call on one GPU shares that GPU's array and leaves its contents
+ * behind: calls that can overlap on one GPU (other streams, other host
+ * threads) race and must be ordered by the caller.  Nothing in the array has
+ * to start at zero: every merge record the step reads is written by the same
+ * call.  params->fused_merge must be 0 (the in-kernel merge keeps arrival
+ * counts between calls; 1 returns HPC_ERR_UNSUPPORTED).  The array's device
+ * address is looked up on the first call on each device, with the stream's
+ * device current; a failed lookup returns HPC_ERR_HIP.
+ * Other arguments, limits and errors as hpc_decode_step.
+ */
+int hpc_decode_step_noalloc(const hpc_decode_params* params, int32_t batch, int32_t n_workers, const void* q,
+                            const void* k_cache, const void* v_cache, const int32_t* block_table,
+                            const int32_t* seq_lens, void* out, float* lse, void* stream);
+
+/* Bytes of the fixed scratch array of hpc_decode_step_noalloc (per GPU). */
+int64_t hpc_decode_step_noalloc_max_bytes(void);
+
+/*
  * The device-derived schedule written out on `stream` into device `plan`
  * (int32 words, capacity >= hpc_decode_plan_size) in exactly the layout of
  * hpc_decode_plan, so the two can be compared word for word.  One

@@ -31,6 +31,7 @@ __all__ = [
     "hpc_decode_check", "hpc_decode_attn", "hpc_status_string", "hpc_decode_profile_start",
     "hpc_decode_profile_stop", "hpc_probe_read", "hpc_probe_read_timed", "hpc_probe_copy", "hpc_decode_step",
     "hpc_decode_step_check", "hpc_decode_step_workspace_size", "hpc_decode_plan_device", "StepLauncher",
+    "hpc_decode_step_noalloc", "hpc_decode_step_noalloc_max_bytes",
     "hpc_decode_plan_workspace_bound", "hpc_decode_plan_attn", "PlannedStepLauncher",
     "DecodeStep", "HpcDecodeError",
     "kv_dtype_code", "make_params", "tile_math_code", "HPC_KV_BF16", "HPC_KV_FP8_E4M3",
@@ -370,6 +371,22 @@ def hpc_decode_step(q, k_cache, v_cache, block_table, seq_lens, workspace, out, 
     params, args = _step_args(q, k_cache, v_cache, block_table, seq_lens, workspace, out, lse, num_kv_heads,
                               n_workers, sm_scale, k_scale, v_scale, tile_math, fused_merge)
     _lib.check(lib().hpc_decode_step(ctypes.byref(params), *args, _stream_handle(stream)), "hpc_decode_step")
+
+
+def hpc_decode_step_noalloc_max_bytes() -> int:
+    return int(lib().hpc_decode_step_noalloc_max_bytes())
+
+
+def hpc_decode_step_noalloc(q, k_cache, v_cache, block_table, seq_lens, out, lse, *, num_kv_heads, n_workers,
+                            sm_scale, k_scale=1.0, v_scale=1.0, stream=None, tile_math="mfma") -> None:
+    """hpc_decode_step with its scratch in the library's fixed per-GPU array
+    (no workspace argument, no allocation); calls on one GPU share that array
+    and must not overlap."""
+    params, args = _step_args(q, k_cache, v_cache, block_table, seq_lens, None, out, lse, num_kv_heads,
+                              n_workers, sm_scale, k_scale, v_scale, tile_math, False)
+    args = args[:7] + args[9:]       # no workspace pointer or size
+    _lib.check(lib().hpc_decode_step_noalloc(ctypes.byref(params), *args, _stream_handle(stream)),
+               "hpc_decode_step_noalloc")
 
 
 def hpc_decode_plan_device(seq_lens: torch.Tensor, num_kv_heads: int, n_workers: int, max_pages_per_seq: int,

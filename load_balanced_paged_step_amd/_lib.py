@@ -77,6 +77,9 @@ SIGNATURES = {
                                             _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_int64, _VP, _VP, _VP]),
     "hpc_decode_step": (ctypes.c_int, [_PP, ctypes.c_int32, ctypes.c_int32, _VP, _VP, _VP, _VP, _VP, _VP,
                                        ctypes.c_int64, _VP, _VP, _VP]),
+    "hpc_decode_step_noalloc": (ctypes.c_int, [_PP, ctypes.c_int32, ctypes.c_int32, _VP, _VP, _VP, _VP, _VP,
+                                               _VP, _VP, _VP]),
+    "hpc_decode_step_noalloc_max_bytes": (ctypes.c_int64, []),
     "hpc_decode_step_check": (ctypes.c_int, [_PP, ctypes.c_int32, ctypes.c_int32, _VP, _VP, _VP, _VP, _VP,
                                              _VP, ctypes.c_int64, _VP, _VP]),
     "hpc_decode_step_workspace_size": (ctypes.c_int64, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,

@@ -23,6 +23,7 @@ SOURCES = [
     "csrc/api.cpp",
     "csrc/decode_kernels.hip",
     "csrc/probe_kernels.hip",
+    "csrc/step_noalloc.hip",
 ]
 
 ARCH = "gfx950"

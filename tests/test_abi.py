@@ -370,3 +370,21 @@ def test_probe_argument_errors_before_any_hip_call():
     assert lib.hpc_probe_read_timed(ptr, 1024, ptr, -1, None, ctypes.byref(ms)) == hd.HPC_ERR_INVALID
     assert lib.hpc_probe_copy(None, ptr, 1024, None) == hd.HPC_ERR_NULL
     assert lib.hpc_probe_copy(ptr, ptr, -16, None) == hd.HPC_ERR_INVALID
+
+
+def test_noalloc_step_errors_before_any_hip_call():
+    """The no-allocation step refuses, on the host, shapes whose scratch
+    exceeds its fixed array, the in-kernel merge and missing pointers."""
+    f = hd.lib().hpc_decode_step_noalloc
+    cap = hd.hpc_decode_step_noalloc_max_bytes()
+    assert cap == 16 << 20
+    fake = ctypes.c_void_p(0x1000)
+    args = [fake] * 7
+    ok = hd.make_params(16, 1, 8, 16, hd.HPC_KV_BF16, 0.088)
+    assert hd.hpc_decode_step_workspace_size(2, 16, 1, 1024) > cap
+    assert f(ctypes.byref(ok), 2, 1024, *args, None) == hd.HPC_ERR_TOO_SMALL
+    fused = hd.make_params(16, 1, 8, 16, hd.HPC_KV_BF16, 0.088, fused_merge=True)
+    assert f(ctypes.byref(fused), 2, 256, *args, None) == hd.HPC_ERR_UNSUPPORTED
+    assert f(ctypes.byref(ok), 2, 256, *args[:6], None, None) == hd.HPC_ERR_NULL
+    assert f(ctypes.byref(ok), 0, 256, *args, None) == hd.HPC_ERR_INVALID
+    assert f(None, 2, 256, *args, None) == hd.HPC_ERR_NULL
