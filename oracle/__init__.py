@@ -12,22 +12,28 @@ und Tencent Hunyuan streamen zwei HPC-Backends für NVIDIA-Hopper-GPUs
 upstream" (German retelling).
 
 Contents
-  formats    bf16 and OCP FP8 E4M3FN bit patterns -> float64
+  formats    bf16 and OCP FP8 E4M3FN bit patterns -> float64, and float64 ->
+             codes (nearest, ties to even, rounded once)
   attention  paged decode attention as its plain definition (O1), attention
              over a token range plus the log-sum-exp merge (O2)
   plan       the per-step tile schedule (O3), an integer algorithm
+  prologue   the step before attention: QK-norm, RoPE, paged append of the
+             new token's K/V (fp8 quantised for an fp8 cache)
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 against brute force, closed forms, invariants, or torch's own format casts.
 """
 
-from .formats import bf16_bits_to_f64, e4m3fn_bits_to_f64, cache_bits_to_f64
+from .formats import (bf16_bits_to_f64, e4m3fn_bits_to_f64, cache_bits_to_f64, f64_to_bf16_bits,
+                      f64_to_e4m3fn_bits)
 from .attention import (decode_attention, range_attention, merge_partials,
                         split_decode_attention)
 from .plan import build_plan, parse_plan, plan_size_words
+from .prologue import decode_prologue, rms_norm, rope_angles, rope_rotate
 
 __all__ = [
-    "bf16_bits_to_f64", "e4m3fn_bits_to_f64", "cache_bits_to_f64",
+    "bf16_bits_to_f64", "e4m3fn_bits_to_f64", "cache_bits_to_f64", "f64_to_bf16_bits", "f64_to_e4m3fn_bits",
+    "decode_prologue", "rms_norm", "rope_angles", "rope_rotate",
     "decode_attention", "range_attention", "merge_partials", "split_decode_attention",
     "build_plan", "parse_plan", "plan_size_words",
 ]

@@ -41,3 +41,60 @@ def cache_bits_to_f64(bits: np.ndarray, kv_format: str) -> np.ndarray:
     if kv_format == "fp8_e4m3":
         return e4m3fn_bits_to_f64(bits)
     raise ValueError(f"unknown kv format {kv_format!r}")
+
+
+# ---------------------------------------------------------------- encoders ---
+# Rounding of a float64 value to the two formats, each taken once from the
+# exact value (no intermediate float32), to nearest with ties to the even
+# code, as both formats define it.
+
+def _round_to_grid(a: np.ndarray, min_normal_exp: int, mant_bits: int) -> np.ndarray:
+    """|a| (float64, finite, >= 0) rounded to nearest-even on the grid of a
+    binary format with `mant_bits` stored mantissa bits whose smallest normal
+    exponent is `min_normal_exp` (subnormals below it share that spacing)."""
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, min_normal_exp)
+    # log2 can land one off near powers of two; fix e so that 2^e <= a < 2^(e+1)
+    e = np.where((a >= np.exp2(e + 1)) & (a > 0), e + 1, e)
+    e = np.where((a < np.exp2(e)) & (e > min_normal_exp), e - 1, e)
+    spacing = np.exp2(e - mant_bits)
+    return np.rint(a / spacing) * spacing          # np.rint rounds halves to even
+
+
+def f64_to_bf16_bits(x) -> np.ndarray:
+    """bfloat16 code of each value: nearest, ties to even; beyond the largest
+    finite value (by at least half a step) -> infinity; NaN -> 0x7FC0."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    fin = np.isfinite(a)
+    r = _round_to_grid(np.where(fin, a, 0.0), -126, 7)
+    r = np.where(fin, r, np.inf)
+    r = np.where(r > 3.3895313892515355e38, np.inf, r)     # above the largest finite bf16
+    bits = (r.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    bits = np.where(np.signbit(x), bits | np.uint16(0x8000), bits)
+    return np.where(np.isnan(x), np.uint16(0x7FC0), bits).astype(np.uint16)
+
+
+E4M3_MAX = 448.0
+
+
+def f64_to_e4m3fn_bits(x) -> np.ndarray:
+    """OCP E4M3FN code of each value: nearest, ties to even, saturated to
+    +-448 (the format has no infinity; a quantiser clamps to its largest
+    value); the sign of a value that rounds to zero is kept; NaN -> 0x7F."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    a = np.where(np.isnan(x), 0.0, a)
+    r = _round_to_grid(a, -6, 3)
+    r = np.minimum(r, E4M3_MAX)
+    # code from the value: exponent field and mantissa of r
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(r > 0, r, 1.0)))
+    sub = r < 2.0 ** -6
+    man_sub = np.rint(r / 2.0 ** -9)                              # 0..7 (8 = smallest normal)
+    e = np.maximum(e, -6)
+    man_norm = np.rint(r / np.exp2(e - 3)) - 8                      # 0..7
+    code = np.where(sub, man_sub, (e + 7) * 8 + man_norm).astype(np.int64)
+    code = np.where(np.signbit(x), code | 0x80, code)
+    return np.where(np.isnan(x), 0x7F, code).astype(np.uint8)

@@ -227,3 +227,57 @@ def workload_inputs(cfg: int, seed: int | None = None, poison: bool = False) -> 
                       poison=poison, rng=rng)
     inp.meta["workload"] = w.name
     return inp
+
+
+# ---------------------------------------------------------------- prologue ---
+
+@dataclass
+class PrologueInputs:
+    """One step's new token per sequence, before the fused prologue.
+
+    ``cache`` holds the KV cache with room for the new token: its lengths are
+    the cached lengths + 1, so the page of position ``positions[b]`` exists;
+    the row of that position holds random (or poisoned) values until the
+    prologue writes the new token there.  ``positions[b]`` = tokens cached
+    before the step (the new token's position).
+    """
+    cache: DecodeInputs            # seq_lens = positions + 1 (the decode step after the prologue)
+    positions: torch.Tensor        # int32 [B]
+    q_in: torch.Tensor             # bf16 [B, Hq, 128]: the new token's query projection
+    k_in: torch.Tensor             # bf16 [B, H_kv, 128]
+    v_in: torch.Tensor             # bf16 [B, H_kv, 128]
+    q_norm_w: torch.Tensor         # bf16 [128]
+    k_norm_w: torch.Tensor         # bf16 [128]
+    eps: float = 1e-6
+    theta: float = 10000.0
+    q_scale: float = 1.0 / 56.0    # fp8 query output: code = e4m3(q / q_scale)
+
+    @staticmethod
+    def bits(t: torch.Tensor) -> np.ndarray:
+        return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def make_prologue_inputs(cached_lens, num_q_heads: int, num_kv_heads: int, kv_dtype: str = "bf16",
+                         seed: int = 0, poison: bool = False, in_scale: float = 1.0) -> PrologueInputs:
+    """Draw a prologue step: the cache (as ``make_inputs`` for cached_lens + 1,
+    same rng), then Q, K, V of the new token as N(0, 1) * in_scale cast to
+    bf16, then the two norm weights as N(1, 0.25^2) cast to bf16.  A negative
+    cached length marks a padding slot: position -1, one cached token kept
+    for the cache shape."""
+    rng = np.random.default_rng(seed)
+    lens = np.asarray(cached_lens, dtype=np.int64)
+    cache = make_inputs(np.where(lens < 0, 1, lens + 1), num_q_heads, num_kv_heads, kv_dtype, seed=seed,
+                        poison=poison, rng=rng)
+    B = int(lens.shape[0])
+
+    def draw(shape, mean=0.0, sd=1.0):
+        x = rng.standard_normal(size=shape, dtype=np.float32) * np.float32(sd) + np.float32(mean)
+        return torch.from_numpy(x).to(torch.bfloat16)
+
+    q_in = draw((B, num_q_heads, HEAD_DIM), sd=in_scale)
+    k_in = draw((B, num_kv_heads, HEAD_DIM), sd=in_scale)
+    v_in = draw((B, num_kv_heads, HEAD_DIM), sd=in_scale)
+    q_w = draw((HEAD_DIM,), mean=1.0, sd=0.25)
+    k_w = draw((HEAD_DIM,), mean=1.0, sd=0.25)
+    return PrologueInputs(cache=cache, positions=torch.from_numpy(np.where(lens < 0, -1, lens).astype(np.int32)),
+                          q_in=q_in, k_in=k_in, v_in=v_in, q_norm_w=q_w, k_norm_w=k_w)
