@@ -48,6 +48,23 @@ class hpc_decode_params(ctypes.Structure):
     ]
 
 
+class hpc_prologue_params(ctypes.Structure):
+    _fields_ = [
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("max_pages_per_seq", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
+        ("eps", ctypes.c_float),
+        ("rope_theta", ctypes.c_float),
+        ("k_scale", ctypes.c_float),
+        ("v_scale", ctypes.c_float),
+        ("q_scale", ctypes.c_float),
+    ]
+
+
 _I32P = ctypes.POINTER(ctypes.c_int32)
 _F32P = ctypes.POINTER(ctypes.c_float)
 _F64P = ctypes.POINTER(ctypes.c_double)
@@ -86,6 +103,9 @@ SIGNATURES = {
                                                         ctypes.c_int32]),
     "hpc_decode_plan_device": (ctypes.c_int, [_VP, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                               ctypes.c_int32, _VP, ctypes.c_int64, _VP]),
+    "hpc_decode_prologue": (ctypes.c_int, [ctypes.POINTER(hpc_prologue_params), ctypes.c_int32] + [_VP] * 12),
+    "hpc_decode_prologue_check": (ctypes.c_int, [ctypes.POINTER(hpc_prologue_params), ctypes.c_int32]
+                                  + [_VP] * 11),
     "hpc_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "hpc_decode_profile_start": (ctypes.c_int, [ctypes.c_int32]),
     "hpc_decode_profile_stop": (ctypes.c_int, [_F64P, _F64P, _I32P]),

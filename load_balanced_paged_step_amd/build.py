@@ -24,6 +24,8 @@ SOURCES = [
     "csrc/decode_kernels.hip",
     "csrc/probe_kernels.hip",
     "csrc/step_noalloc.hip",
+    "csrc/prologue_api.cpp",
+    "csrc/prologue_kernels.hip",
 ]
 
 ARCH = "gfx950"

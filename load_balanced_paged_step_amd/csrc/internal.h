@@ -60,6 +60,29 @@ struct CombineArgs {
     int32_t max_partials;        // partial slots in the workspace
 };
 
+struct PrologueArgs {
+    const uint16_t* q_in;        // bf16 [B][Hq][128]
+    const uint16_t* k_in;        // bf16 [B][H_kv][128]
+    const uint16_t* v_in;        // bf16 [B][H_kv][128]
+    const uint16_t* q_norm_w;    // bf16 [128]
+    const uint16_t* k_norm_w;    // bf16 [128]
+    const int32_t* positions;    // [B]
+    const int32_t* block_table;  // [B][max_pages_per_seq]
+    void* k_cache;               // bf16|fp8 [num_pages][H_kv][64][128]
+    void* v_cache;
+    uint16_t* q_out;             // bf16 [B][Hq][128]
+    uint8_t* q_fp8;              // e4m3 [B][Hq][128] or null
+    int32_t batch;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t max_pages_per_seq;
+    int32_t num_pages;
+    int32_t kv_fp8;              // 1: fp8 e4m3 cache, 0: bf16
+    float eps;
+    float k_scale, v_scale, q_scale;
+    double log2_theta_over_64;   // log2(theta) / 64: the angle of dimension i is p * 2^(-i * this)
+};
+
 // All return the hipError_t of the launch as int (0 = success).
 // device_sched: the decode kernel derives the schedule from seq_lens itself
 // and writes one merge record per unit for the merge kernel.
@@ -70,6 +93,7 @@ int launch_decode(const DecodeArgs& a, int kv_dtype, int tile_math, int n_worker
                   void* ev_start = nullptr, void* ev_stop = nullptr);
 int launch_combine(const CombineArgs& a, int n_records, bool device_sched, void* stream,
                    void* ev_start = nullptr, void* ev_stop = nullptr);
+int launch_prologue(const PrologueArgs& a, void* stream);
 int launch_plan_device(const int32_t* seq_lens, int batch, int num_kv_heads, int n_workers,
                        int max_pages_per_seq, int32_t* plan, void* stream);
 
