@@ -17,6 +17,7 @@ Contents
   attention  paged decode attention as its plain definition (O1), attention
              over a token range plus the log-sum-exp merge (O2)
   plan       the per-step tile schedule (O3), an integer algorithm
+  prefill    causal prefill / extend attention over the paged cache
   prologue   the step before attention: QK-norm, RoPE, paged append of the
              new token's K/V (fp8 quantised for an fp8 cache)
 
@@ -30,10 +31,11 @@ from .attention import (decode_attention, range_attention, merge_partials,
                         split_decode_attention)
 from .plan import build_plan, parse_plan, plan_size_words
 from .prologue import decode_prologue, rms_norm, rope_angles, rope_rotate
+from .prefill import prefill_attention
 
 __all__ = [
     "bf16_bits_to_f64", "e4m3fn_bits_to_f64", "cache_bits_to_f64", "f64_to_bf16_bits", "f64_to_e4m3fn_bits",
-    "decode_prologue", "rms_norm", "rope_angles", "rope_rotate",
+    "decode_prologue", "rms_norm", "rope_angles", "rope_rotate", "prefill_attention",
     "decode_attention", "range_attention", "merge_partials", "split_decode_attention",
     "build_plan", "parse_plan", "plan_size_words",
 ]

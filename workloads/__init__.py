@@ -281,3 +281,89 @@ def make_prologue_inputs(cached_lens, num_q_heads: int, num_kv_heads: int, kv_dt
     k_w = draw((HEAD_DIM,), mean=1.0, sd=0.25)
     return PrologueInputs(cache=cache, positions=torch.from_numpy(np.where(lens < 0, -1, lens).astype(np.int32)),
                           q_in=q_in, k_in=k_in, v_in=v_in, q_norm_w=q_w, k_norm_w=k_w)
+
+
+# ----------------------------------------------------------------- prefill ---
+
+@dataclass
+class PrefillInputs:
+    """A prefill / extend step: sequence b has ctx_b tokens cached before the
+    step and n_b new tokens, whose K/V are already in the cache (lengths
+    ctx_b + n_b); its queries are rows [q_start[b], q_start[b+1]) of q."""
+    cache: DecodeInputs            # seq_lens = ctx + n (the cache the queries attend to)
+    q: torch.Tensor                # bf16 [total, Hq, 128]
+    q_start: torch.Tensor          # int32 [B + 1]
+
+    @property
+    def total(self) -> int:
+        return int(self.q.shape[0])
+
+    def q_bits(self) -> np.ndarray:
+        return self.q.view(torch.int16).numpy().view(np.uint16)
+
+    def q_lens(self) -> np.ndarray:
+        s = self.q_start.numpy().astype(np.int64)
+        return s[1:] - s[:-1]
+
+    def flops(self) -> int:
+        """4 * 128 FLOP (q.k and p.v) per (query head, visible token)."""
+        lens = self.cache.seq_lens.numpy().astype(np.int64)
+        n = self.q_lens()
+        vis = sum(int(n_b * (L - n_b) + n_b * (n_b + 1) // 2) for n_b, L in zip(n, lens))
+        return vis * self.cache.num_q_heads * 4 * HEAD_DIM
+
+
+@dataclass(frozen=True)
+class PrefillWorkload:
+    name: str
+    num_q_heads: int
+    num_kv_heads: int
+    kv_dtype: str
+    q_lens: tuple
+    ctx_lens: tuple | None = None          # None -> log-uniform from the seed
+    ctx_loguniform: tuple = (64, 16384)
+    description: str = ""
+
+
+PREFILL_WORKLOADS = {
+    "prefill-q512": PrefillWorkload("prefill-q512", 64, 8, "bf16", (512,), (0,),
+                                    description="one 512-token prompt, causal, 64q/8kv, bf16"),
+    "prefill-q512-8q1kv": PrefillWorkload("prefill-q512-8q1kv", 8, 1, "bf16", (512,), (0,),
+                                          description="one 512-token prompt, causal, 8q/1kv (one GPU of TP8)"),
+    "extend-8x512": PrefillWorkload("extend-8x512", 64, 8, "bf16", (512,) * 8, None,
+                                    description="8 chunks of 512 new tokens after log-uniform [64, 16384] "
+                                                "cached tokens, 64q/8kv, bf16"),
+    "extend-8x256-fp8": PrefillWorkload("extend-8x256-fp8", 64, 8, "fp8_e4m3", (256,) * 8, None,
+                                        description="8 chunks of 256 after log-uniform [64, 16384] cached "
+                                                    "tokens, 64q/8kv, fp8-e4m3 KV"),
+}
+
+
+def make_prefill_inputs(ctx_lens, q_lens, num_q_heads: int, num_kv_heads: int, kv_dtype: str = "bf16",
+                        seed: int = 0, poison: bool = False, rng: np.random.Generator | None = None,
+                        max_pages_per_seq: int | None = None) -> PrefillInputs:
+    """Draw a prefill / extend step: the cache as ``make_inputs`` for
+    ctx + n tokens (same rng), then the packed queries as N(0, 1) cast to
+    bf16."""
+    if rng is None:
+        rng = np.random.default_rng(seed)
+    ctx = np.asarray(ctx_lens, dtype=np.int64)
+    n = np.asarray(q_lens, dtype=np.int64)
+    cache = make_inputs(ctx + n, num_q_heads, num_kv_heads, kv_dtype, seed=seed, poison=poison, rng=rng,
+                        max_pages_per_seq=max_pages_per_seq)
+    q = _normal_bf16(rng, (int(n.sum()), num_q_heads, HEAD_DIM))
+    q_start = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    return PrefillInputs(cache=cache, q=q, q_start=torch.from_numpy(q_start))
+
+
+def prefill_workload_inputs(name: str, seed: int = 7, poison: bool = False) -> PrefillInputs:
+    w = PREFILL_WORKLOADS[name]
+    rng = np.random.default_rng(seed)
+    if w.ctx_lens is None:
+        ctx = draw_loguniform_lengths(rng, len(w.q_lens), *w.ctx_loguniform)
+    else:
+        ctx = np.asarray(w.ctx_lens, dtype=np.int64)
+    inp = make_prefill_inputs(ctx, w.q_lens, w.num_q_heads, w.num_kv_heads, w.kv_dtype, seed=seed,
+                              poison=poison, rng=rng)
+    inp.cache.meta["workload"] = w.name
+    return inp
