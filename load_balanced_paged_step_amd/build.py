@@ -26,6 +26,8 @@ SOURCES = [
     "csrc/step_noalloc.hip",
     "csrc/prologue_api.cpp",
     "csrc/prologue_kernels.hip",
+    "csrc/prefill_api.cpp",
+    "csrc/prefill_kernels.hip",
 ]
 
 ARCH = "gfx950"

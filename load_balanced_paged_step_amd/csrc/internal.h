@@ -83,6 +83,26 @@ struct PrologueArgs {
     double log2_theta_over_64;   // log2(theta) / 64: the angle of dimension i is p * 2^(-i * this)
 };
 
+struct PrefillArgs {
+    const void* q;               // bf16 [total][Hq][128]
+    const int32_t* q_start;      // [B + 1]
+    const void* k;               // bf16|fp8 [num_pages][H_kv][64][128]
+    const void* v;
+    const int32_t* block_table;  // [B][max_pages_per_seq]
+    const int32_t* seq_lens;     // [B]: cached tokens, the chunk's new tokens included
+    const int32_t* work;         // [n_units][4]: (sequence, query block, KV head, cost)
+    void* out;                   // bf16 [total][Hq][128]
+    float* lse;                  // [total][Hq]
+    int32_t batch;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t group;
+    int32_t max_pages_per_seq;
+    int32_t num_pages;
+    float qk_scale_log2;
+    float v_scale;
+};
+
 // All return the hipError_t of the launch as int (0 = success).
 // device_sched: the decode kernel derives the schedule from seq_lens itself
 // and writes one merge record per unit for the merge kernel.
@@ -94,6 +114,7 @@ int launch_decode(const DecodeArgs& a, int kv_dtype, int tile_math, int n_worker
 int launch_combine(const CombineArgs& a, int n_records, bool device_sched, void* stream,
                    void* ev_start = nullptr, void* ev_stop = nullptr);
 int launch_prologue(const PrologueArgs& a, void* stream);
+int launch_prefill(const PrefillArgs& a, int n_units, bool kv_fp8, void* stream);
 int launch_plan_device(const int32_t* seq_lens, int batch, int num_kv_heads, int n_workers,
                        int max_pages_per_seq, int32_t* plan, void* stream);
 

@@ -1,0 +1,319 @@
+// Causal prefill / extend attention over the paged KV cache on gfx950.
+//
+// "vLLM x HPC-Ops ...", §Attention Across Prefill, Extend and Decode Shapes
+// measures the attention backend on prefill ("q512") and extend shapes as
+// well as decode; the pages give no kernel design for them.  What is
+// computed (the plain reading): sequence b holds L_b cached tokens whose last
+// n_b are this step's new tokens; new token j, at position
+// p = L_b - n_b + j, is a query over the cached tokens t <= p.
+//
+// Work: one workgroup (4 waves) per unit (sequence b, KV head h, block of 16
+// consecutive queries), taken from a host-made work list ordered by
+// decreasing cost (the number of 64-token KV tiles the block sees), so the
+// longest units start first and the short ones fill in behind them.
+//  * Each wave owns heads w, w + 4, w + 8, w + 12 (< G) of the KV head's
+//    query group: per head a 16-query row block, whose Q stays in registers.
+//  * Per 64-token tile, K and V (one page of head h) are loaded by all 256
+//    threads with buffer loads whose range ends at the sequence's last token
+//    (rows past it read as zeros: a poisoned tail cannot reach the sums),
+//    written to LDS (fp8 widened to bf16 exactly) with a 16-byte pad per row
+//    so the operand reads of 8 lanes hit distinct banks, and read by all four
+//    waves.  The next tile's loads are in flight while the current tile is
+//    computed.
+//  * S^T = K Q^T on MFMA 16x16x32 bf16 (16 KV tokens x 16 queries), exp2
+//    domain online softmax per query, P V on MFMA 16x16x16 bf16 as
+//    O^T = V^T P^T with P taken straight from the score registers.
+//  * The causal mask is applied on the tiles that reach past the block's
+//    first query position; tokens > p score -inf.
+// Lane layout (lane = n + 16 g): QK: A = K [token n][dims 32 kk + 8 g ..],
+// B = Q^T [query n][same dims], D[token 4 g + i][query n] in register i.
+// PV: A = V^T [dim 8 n + nb][tokens 4 g .. 4 g + 3], B = P^T, D[dim
+// 8 (4 g + i) + nb][query n] in register i of accumulator nb.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <cstdint>
+
+#include "internal.h"
+
+namespace hpcd {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kQBlock = 16;                       // queries per unit
+constexpr int kLdsRow = kHeadDim * 2 + 16;        // bytes per LDS row: 256 + 16 pad
+constexpr uint32_t kRsrcWord3 = 0x00020000u;      // raw (untyped) buffer
+constexpr uint32_t kSelLo = 0x05040100u;          // v_perm: {b.lo, a.lo}
+constexpr uint32_t kSelHi = 0x07060302u;          // v_perm: {b.hi, a.hi}
+constexpr float kLn2 = 0.69314718055994531f;
+
+template <typename To, typename From>
+__device__ __forceinline__ To bitcast(const From& x) {
+    static_assert(sizeof(To) == sizeof(From), "size mismatch");
+    return __builtin_bit_cast(To, x);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kRsrcWord3);
+}
+
+// four E4M3FN codes -> four bf16 (exact: every E4M3FN value is a bf16 value)
+__device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t x) {
+    return u32x2{bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false)),
+                 bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true))};
+}
+
+// two fp32 -> two bf16 (nearest-even) in one word, a in the low half
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    return uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(a))) |
+           (uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(b))) << 16);
+}
+
+// One 64-token tile of K or V in flight: 16 KiB bf16 = 4 x 16 B per thread,
+// 8 KiB fp8 = 2 x 16 B per thread.
+template <bool FP8>
+struct TileRegs {
+    static constexpr int kLoads = FP8 ? 2 : 4;
+    u32x4 k[kLoads], v[kLoads];
+
+    // rows [0, valid) of page `page`, KV head h; everything else reads as 0
+    __device__ __forceinline__ void load(const PrefillArgs& a, int page, int h, int valid, int tid) {
+        const int64_t elem = FP8 ? 1 : 2;
+        const int64_t head_bytes = int64_t(kPage) * kHeadDim * elem;
+        const bool ok = page >= 0 && page < a.num_pages;
+        const int64_t off = ok ? (int64_t(page) * a.num_kv_heads + h) * head_bytes : 0;
+        const uint32_t bytes = ok ? static_cast<uint32_t>(valid * kHeadDim * elem) : 0u;
+        const auto rk = make_rsrc(static_cast<const char*>(a.k) + off, bytes);
+        const auto rv = make_rsrc(static_cast<const char*>(a.v) + off, bytes);
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) {
+            const int c = tid + kThreads * i;          // 16-byte chunk of the tile, row-major
+            k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, c * 16, 0, 0);
+            v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, c * 16, 0, 0);
+        }
+    }
+
+    __device__ __forceinline__ void store(char* lds_k, char* lds_v, int tid) const {
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) {
+            const int c = tid + kThreads * i;
+            if constexpr (FP8) {
+                const int row = c >> 3, col = (c & 7) * 32;      // 16 codes -> 32 bytes of bf16
+                char* pk = lds_k + row * kLdsRow + col;
+                char* pv = lds_v + row * kLdsRow + col;
+                const u32x2 k0 = fp8x4_to_bf16x4(k[i][0]), k1 = fp8x4_to_bf16x4(k[i][1]);
+                const u32x2 k2 = fp8x4_to_bf16x4(k[i][2]), k3 = fp8x4_to_bf16x4(k[i][3]);
+                const u32x2 v0 = fp8x4_to_bf16x4(v[i][0]), v1 = fp8x4_to_bf16x4(v[i][1]);
+                const u32x2 v2 = fp8x4_to_bf16x4(v[i][2]), v3 = fp8x4_to_bf16x4(v[i][3]);
+                *reinterpret_cast<u32x4*>(pk) = u32x4{k0[0], k0[1], k1[0], k1[1]};
+                *reinterpret_cast<u32x4*>(pk + 16) = u32x4{k2[0], k2[1], k3[0], k3[1]};
+                *reinterpret_cast<u32x4*>(pv) = u32x4{v0[0], v0[1], v1[0], v1[1]};
+                *reinterpret_cast<u32x4*>(pv + 16) = u32x4{v2[0], v2[1], v3[0], v3[1]};
+            } else {
+                const int row = c >> 4, col = (c & 15) * 16;
+                *reinterpret_cast<u32x4*>(lds_k + row * kLdsRow + col) = k[i];
+                *reinterpret_cast<u32x4*>(lds_v + row * kLdsRow + col) = v[i];
+            }
+        }
+    }
+};
+
+template <bool FP8, int HPW>
+__global__ void __launch_bounds__(kThreads)
+prefill_kernel(PrefillArgs a) {
+    __shared__ __attribute__((aligned(16))) char lds_k[kPage * kLdsRow];
+    __shared__ __attribute__((aligned(16))) char lds_v[kPage * kLdsRow];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 15;          // query column / K row / V dim group
+    const int g = lane >> 4;          // lane group
+
+    // the unit
+    const int32_t* w = a.work + 4 * static_cast<int64_t>(blockIdx.x);
+    const int b = __builtin_amdgcn_readfirstlane(w[0]);
+    const int qb = __builtin_amdgcn_readfirstlane(w[1]);
+    const int h = __builtin_amdgcn_readfirstlane(w[2]);
+    if (b < 0 || b >= a.batch || h < 0 || h >= a.num_kv_heads || qb < 0) return;
+    const int r0 = a.q_start[b];
+    const int nq_seq = a.q_start[b + 1] - r0;
+    if (qb * kQBlock >= nq_seq) return;
+    int L = a.seq_lens[b];
+    L = L < 0 ? 0 : (L > a.max_pages_per_seq * kPage ? a.max_pages_per_seq * kPage : L);
+    const int q0 = qb * kQBlock;                                  // first query of the block in the chunk
+    const int nq = nq_seq - q0 < kQBlock ? nq_seq - q0 : kQBlock;   // queries in the block
+    const int pos0 = L - nq_seq + q0;                             // position of the block's first query
+    const int last = pos0 + nq - 1;                               // position of its last query
+    const int n_tiles = last < 0 ? 0 : last / kPage + 1;
+    const int G = a.group;
+
+    // Q of this wave's heads: row block r holds head hg = wave + 4 r
+    bf16x8 qop[HPW][4];
+#pragma unroll
+    for (int r = 0; r < HPW; ++r) {
+        const int hg = wave + kWaves * r;
+        const int64_t row_stride = int64_t(a.num_q_heads) * kHeadDim * 2;
+        const char* base = static_cast<const char*>(a.q) + (int64_t(r0 + q0) * a.num_q_heads + h * G + hg) * kHeadDim * 2;
+        const uint32_t bytes = (hg < G && nq > 0) ? static_cast<uint32_t>((nq - 1) * row_stride + kHeadDim * 2) : 0u;
+        const auto rq = make_rsrc(base, bytes);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            qop[r][kk] = bitcast<bf16x8>(__builtin_amdgcn_raw_buffer_load_b128(
+                rq, static_cast<int>(n * row_stride + (32 * kk + 8 * g) * 2), 0, 0));
+    }
+
+    f32x4 acc[HPW][8];
+    float m[HPW], l[HPW];
+#pragma unroll
+    for (int r = 0; r < HPW; ++r) {
+        m[r] = -INFINITY;
+        l[r] = 0.f;
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) acc[r][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    const int32_t* bt = a.block_table + int64_t(b) * a.max_pages_per_seq;
+    TileRegs<FP8> regs;
+    if (n_tiles > 0) regs.load(a, bt[0], h, L < kPage ? L : kPage, tid);
+
+    for (int t = 0; t < n_tiles; ++t) {
+        __syncthreads();                      // every wave is done with the previous tile
+        regs.store(lds_k, lds_v, tid);
+        __syncthreads();                      // the tile is in LDS
+        if (t + 1 < n_tiles) {
+            const int rest = L - (t + 1) * kPage;
+            regs.load(a, bt[t + 1], h, rest < kPage ? rest : kPage, tid);
+        }
+
+        // S^T blocks: 4 x 16 KV tokens against each row block's 16 queries
+        f32x4 sc[HPW][4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+            for (int r = 0; r < HPW; ++r) sc[r][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const bf16x8 kop = *reinterpret_cast<const bf16x8*>(lds_k + (16 * kb + n) * kLdsRow + (32 * kk + 8 * g) * 2);
+#pragma unroll
+                for (int r = 0; r < HPW; ++r)
+                    sc[r][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[r][kk], sc[r][kb], 0, 0, 0);
+            }
+        }
+
+        // online softmax per query column n, exp2 domain
+        const int tok0 = t * kPage;
+        const bool masked_tile = tok0 + kPage - 1 > pos0;      // some token here is past some query
+        const int qpos = pos0 + n;
+        bf16x4 pop[HPW][4];
+#pragma unroll
+        for (int r = 0; r < HPW; ++r) {
+            float mt = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int tok = tok0 + 16 * kb + 4 * g + i;
+                    const bool vis = !masked_tile || tok <= qpos;
+                    sc[r][kb][i] = vis ? sc[r][kb][i] * a.qk_scale_log2 : -INFINITY;
+                    mt = fmaxf(mt, sc[r][kb][i]);
+                }
+            }
+            mt = fmaxf(mt, __shfl_xor(mt, 16));
+            mt = fmaxf(mt, __shfl_xor(mt, 32));
+            const float m_new = fmaxf(m[r], mt);
+            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+            const float alpha = __builtin_amdgcn_exp2f(m[r] - m_use);
+            m[r] = m_new;
+            float psum = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                float p[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    p[i] = __builtin_amdgcn_exp2f(sc[r][kb][i] - m_use);
+                    psum += p[i];
+                }
+                pop[r][kb] = bf16x4{static_cast<__bf16>(p[0]), static_cast<__bf16>(p[1]),
+                                    static_cast<__bf16>(p[2]), static_cast<__bf16>(p[3])};
+            }
+            l[r] = l[r] * alpha + psum;
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb) acc[r][nb] = acc[r][nb] * alpha;
+        }
+
+        // O^T += V^T P^T
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            u32x4 rows[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                rows[i] = *reinterpret_cast<const u32x4*>(lds_v + (16 * kb + 4 * g + i) * kLdsRow + 16 * n);
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb) {
+                const int d = nb >> 1;
+                const uint32_t sel = (nb & 1) ? kSelHi : kSelLo;
+                const u32x2 vt = u32x2{__builtin_amdgcn_perm(rows[1][d], rows[0][d], sel),
+                                       __builtin_amdgcn_perm(rows[3][d], rows[2][d], sel)};
+#pragma unroll
+                for (int r = 0; r < HPW; ++r)
+                    acc[r][nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(bitcast<bf16x4>(vt), pop[r][kb],
+                                                                           acc[r][nb], 0, 0, 0);
+            }
+        }
+    }
+
+    // epilogue: out = acc / l, lse = (m + log2 l) ln 2; a query with no
+    // visible token gets 0 and -inf
+#pragma unroll
+    for (int r = 0; r < HPW; ++r) {
+        const int hg = wave + kWaves * r;
+        if (hg >= G) break;
+        float lt = l[r];
+        lt += __shfl_xor(lt, 16);
+        lt += __shfl_xor(lt, 32);
+        if (n >= nq) continue;
+        const float inv = lt > 0.f ? a.v_scale / lt : 0.f;
+        const int64_t row = int64_t(r0 + q0 + n) * a.num_q_heads + h * G + hg;
+        char* o = static_cast<char*>(a.out) + row * kHeadDim * 2;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const u32x4 pk = u32x4{pack_bf16x2(acc[r][0][i] * inv, acc[r][1][i] * inv),
+                                   pack_bf16x2(acc[r][2][i] * inv, acc[r][3][i] * inv),
+                                   pack_bf16x2(acc[r][4][i] * inv, acc[r][5][i] * inv),
+                                   pack_bf16x2(acc[r][6][i] * inv, acc[r][7][i] * inv)};
+            *reinterpret_cast<u32x4*>(o + (32 * g + 8 * i) * 2) = pk;
+        }
+        if (g == 0) a.lse[row] = lt > 0.f ? (m[r] + __log2f(lt)) * kLn2 : -INFINITY;
+    }
+}
+
+template <bool FP8>
+int launch_fp8(const PrefillArgs& a, int n_units, void* stream) {
+    const dim3 grid(n_units), block(kThreads);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (a.group <= 4)
+        hipLaunchKernelGGL((prefill_kernel<FP8, 1>), grid, block, 0, s, a);
+    else if (a.group <= 8)
+        hipLaunchKernelGGL((prefill_kernel<FP8, 2>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((prefill_kernel<FP8, 4>), grid, block, 0, s, a);
+    return static_cast<int>(hipGetLastError());
+}
+
+}  // namespace
+
+int launch_prefill(const PrefillArgs& a, int n_units, bool kv_fp8, void* stream) {
+    if (n_units == 0) return 0;
+    return kv_fp8 ? launch_fp8<true>(a, n_units, stream) : launch_fp8<false>(a, n_units, stream);
+}
+
+}  // namespace hpcd
