@@ -90,6 +90,12 @@ def parse_args():
     ap.add_argument("--tile-math-sweep", action="store_true",
                     help="time the decode kernel with MFMA and with VALU tile math on workloads 2-5 "
                          "(device schedule) and print one JSON line")
+    ap.add_argument("--prefill", nargs="?", const="all", default=None, metavar="WORKLOAD",
+                    help="instead of the bench line: time causal prefill/extend attention on the prefill "
+                         "workloads (all, or one by name) and print one JSON line")
+    ap.add_argument("--prologue", action="store_true",
+                    help="instead of the bench line: time the fused prologue (QK-norm, RoPE, paged append) "
+                         "alone and before the decode step on workloads 4 and 5, print one JSON line")
     ap.add_argument("--schedule", choices=["device", "host"], default="device",
                     help="device: kernels derive the per-step schedule from the lengths on the GPU; "
                          "host: C++ planner on the host + plan upload every step")
@@ -212,6 +218,12 @@ def main() -> int:
         return 2
     if args.tile_math_sweep:
         print(json.dumps(tile_math_sweep(dev, W, args.steps, args.warmup)), flush=True)
+        return 0
+    if args.prefill:
+        print(json.dumps(prefill_bench(dev, cus, args.prefill, args.steps, args.warmup)), flush=True)
+        return 0
+    if args.prologue:
+        print(json.dumps(prologue_bench(dev, cus, W, args.steps, args.warmup)), flush=True)
         return 0
     wl = WORKLOADS[args.workload]
 
@@ -457,6 +469,131 @@ def tile_math_sweep(dev, W: int, steps: int, warmup: int) -> dict:
         torch.cuda.empty_cache()
     return {"mode": "tile-math-sweep", "n_workers": W, "steps": steps, "warmup": warmup,
             "schedule": "device", "timing": "decode kernel, dispatch-stamped HIP events, median of 3 rounds",
+            "rows": rows}
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def _events_us(fn, steps: int, warmup: int) -> float:
+    """Mean time per call of `fn` over `steps` back-to-back calls on the
+    current stream, bracketed by events (after `warmup` calls)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps * 1e3
+
+
+def prefill_bench(dev, cus: int, which: str, steps: int, warmup: int) -> dict:
+    """Causal prefill / extend attention: mean kernel time over back-to-back
+    launches (events on the launch stream; the work list is planned and
+    uploaded once, outside the timing), algorithmic FLOPs (4 * 128 per query
+    head and visible token) against the bf16 MFMA peak."""
+    import torch
+
+    from load_balanced_paged_step_amd.prefill import PrefillStep
+    from workloads import PREFILL_WORKLOADS, prefill_workload_inputs
+
+    clock_warmup(dev, cus)
+    names = list(PREFILL_WORKLOADS) if which == "all" else [which]
+    rows = []
+    for name in names:
+        pi = prefill_workload_inputs(name)
+        c = pi.cache
+        q, qs = pi.q.to(dev), pi.q_start.to(dev)
+        k, v = c.k_cache.to(dev), c.v_cache.to(dev)
+        bt, sl = c.block_table.to(dev), c.seq_lens.to(dev)
+        out = torch.empty_like(q)
+        lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+        t0 = time.perf_counter()
+        step = PrefillStep(pi.q_start, c.seq_lens, c.num_kv_heads, c.max_pages_per_seq, device=dev)
+        plan_us = (time.perf_counter() - t0) * 1e6
+
+        one = step.bind(q, qs, k, v, bt, sl, out, lse, sm_scale=c.sm_scale, k_scale=c.k_scale, v_scale=c.v_scale)
+        us = _events_us(one, max(steps, 20), max(warmup, 5))
+        flops = pi.flops()
+        tflops = flops / (us * 1e-6) / 1e12
+        row = {"workload": name, "heads": f"{c.num_q_heads}q/{c.num_kv_heads}kv", "kv_dtype": c.kv_dtype,
+               "queries": pi.total, "kv_lens": _lens_summary(c.seq_lens.numpy()), "units": step.n_units,
+               "us": round(us, 3), "flops": flops, "TFLOPs": round(tflops, 1),
+               "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                            "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)},
+               "plan_and_upload_us": round(plan_us, 1)}
+        log(f"prefill {name}: {us:.2f} us, {tflops:.1f} TFLOP/s ({row['roofline']['frac']:.3f} of bf16 MFMA peak), "
+            f"{step.n_units} units")
+        rows.append(row)
+        del q, k, v, out, lse
+        torch.cuda.empty_cache()
+    return {"mode": "prefill", "timing": "mean of back-to-back launches, HIP events on the launch stream",
+            "peak_note": "fp8 KV widens to bf16 in LDS; all products run on bf16 MFMA", "rows": rows}
+
+
+def prologue_bench(dev, cus: int, W: int, steps: int, warmup: int) -> dict:
+    """The fused prologue (QK-norm, RoPE, paged append of the new token) on
+    the decode workloads' shapes: its mean time over back-to-back launches,
+    its algorithmic bytes (new q/k/v read, q written, the new K/V rows
+    written, norm weights), and the whole decode step with it in front
+    (prologue + decode + merge, device schedule) against the step without."""
+    import numpy as np
+    import torch
+
+    import load_balanced_paged_step_amd as hd
+    from load_balanced_paged_step_amd.prologue import PrologueLauncher
+    from workloads import WORKLOADS, make_prologue_inputs, workload_inputs
+
+    clock_warmup(dev, cus)
+    rows = []
+    for cfg in (4, 5):
+        base = workload_inputs(cfg)
+        lens = base.seq_lens.numpy().astype(np.int64)
+        pi = make_prologue_inputs(lens - 1, base.num_q_heads, base.num_kv_heads, base.kv_dtype, seed=cfg)
+        c = pi.cache
+        q_in, k_in, v_in = pi.q_in.to(dev), pi.k_in.to(dev), pi.v_in.to(dev)
+        wq, wk = pi.q_norm_w.to(dev), pi.k_norm_w.to(dev)
+        pos, bt, sl = pi.positions.to(dev), c.block_table.to(dev), c.seq_lens.to(dev)
+        k, v = c.k_cache.to(dev), c.v_cache.to(dev)
+        q_out = torch.empty_like(q_in)
+        q_fp8 = torch.empty(q_in.shape, dtype=torch.float8_e4m3fn, device=dev) if c.kv_dtype != "bf16" else None
+
+        pro = PrologueLauncher(q_in, k_in, v_in, wq, wk, pos, bt, k, v, q_out, q_fp8, eps=pi.eps, theta=pi.theta,
+                               k_scale=c.k_scale, v_scale=c.v_scale, q_scale=pi.q_scale)
+        ws = torch.zeros(hd.hpc_decode_step_workspace_size(c.batch, c.num_q_heads, c.num_kv_heads, W),
+                         dtype=torch.uint8, device=dev)
+        out = torch.empty_like(q_out)
+        lse = torch.empty(q_out.shape[:2], dtype=torch.float32, device=dev)
+        decode = hd.StepLauncher(q_out, k, v, bt, sl, out, lse, num_kv_heads=c.num_kv_heads, n_workers=W,
+                                 workspace=ws, sm_scale=c.sm_scale, k_scale=c.k_scale, v_scale=c.v_scale)
+
+        def both():
+            pro()
+            decode()
+        B, Hq, Hkv = c.batch, c.num_q_heads, c.num_kv_heads
+        kv_elem = 1 if c.kv_dtype != "bf16" else 2
+        nbytes = (B * (Hq + 2 * Hkv) * 128 * 2 + 2 * 128 * 2 + B * 4 * 2 + B * Hq * 128 * 2
+                  + (B * Hq * 128 if q_fp8 is not None else 0) + 2 * B * Hkv * 128 * kv_elem)
+        n = max(steps, 50)
+        pro_us = _events_us(pro, n, max(warmup, 10))
+        dec_us = _events_us(decode, n, max(warmup, 10))
+        both_us = _events_us(both, n, max(warmup, 10))
+        row = {"workload": WORKLOADS[cfg].name, "heads": f"{Hq}q/{Hkv}kv", "kv_dtype": c.kv_dtype,
+               "fp8_query": q_fp8 is not None, "prologue_us": round(pro_us, 3), "prologue_bytes": nbytes,
+               "prologue_GBps": round(nbytes / (pro_us * 1e-6) / 1e9, 1),
+               "roofline": {"bound": "latency", "achieved": round(nbytes / (pro_us * 1e-6) / 1e9, 1),
+                            "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                            "frac": round(nbytes / (pro_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 5)},
+               "decode_step_us": round(dec_us, 3), "prologue_plus_decode_step_us": round(both_us, 3)}
+        log(f"prologue {row['workload']}: {pro_us:.2f} us ({nbytes} B); decode step {dec_us:.2f} us, "
+            f"with prologue {both_us:.2f} us")
+        rows.append(row)
+    return {"mode": "prologue", "n_workers": W,
+            "timing": "mean of back-to-back launches, HIP events on the launch stream (KV resident, one copy)",
             "rows": rows}
 
 

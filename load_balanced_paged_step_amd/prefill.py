@@ -97,6 +97,25 @@ class PrefillStep:
         self.work_dev = torch.from_numpy(self.work_host.copy()).to(device) if self.n_units else None
         self.num_kv_heads = num_kv_heads
 
+    def bind(self, q, q_start, k_cache, v_cache, block_table, seq_lens, out, lse, *, sm_scale, k_scale=1.0,
+             v_scale=1.0, stream=None):
+        """A callable that issues this step's launch with its arguments
+        marshalled once (the tensors must stay alive and unchanged in shape)."""
+        from . import _stream_handle
+        params, args = _attn_args(q, q_start, k_cache, v_cache, block_table, seq_lens, self.work_dev, self.n_units,
+                                  out, lse, self.num_kv_heads, sm_scale, k_scale, v_scale)
+        full = (ctypes.byref(params), *args, _stream_handle(stream))
+        _lib.check(lib().hpc_prefill_check(*full[:-1]), "PrefillStep.bind")
+        fn = lib().hpc_prefill_attn
+        keep = (params, q, q_start, k_cache, v_cache, block_table, seq_lens, out, lse, self.work_dev)
+
+        def launch() -> None:
+            status = fn(*full)
+            if status:
+                _lib.check(status, "hpc_prefill_attn")
+        launch.keep = keep
+        return launch
+
     def __call__(self, q, q_start, k_cache, v_cache, block_table, seq_lens, out, lse, *, sm_scale, k_scale=1.0,
                  v_scale=1.0, stream=None) -> None:
         hpc_prefill_attn(q, q_start, k_cache, v_cache, block_table, seq_lens, self.work_dev, self.n_units, out, lse,

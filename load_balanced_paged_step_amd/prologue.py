@@ -16,7 +16,7 @@ import torch
 from . import _lib
 from ._lib import HEAD_DIM, PAGE, hpc_prologue_params, lib
 
-__all__ = ["hpc_decode_prologue", "hpc_decode_prologue_check", "make_prologue_params"]
+__all__ = ["hpc_decode_prologue", "hpc_decode_prologue_check", "make_prologue_params", "PrologueLauncher"]
 
 
 def _ptr(t, name, dtype, allow_none=False):
@@ -81,3 +81,25 @@ def hpc_decode_prologue(q_in, k_in, v_in, q_norm_w, k_norm_w, positions, block_t
     params, args = _args(q_in, k_in, v_in, q_norm_w, k_norm_w, positions, block_table, k_cache, v_cache, q_out,
                          q_fp8, eps, theta, k_scale, v_scale, q_scale)
     _lib.check(lib().hpc_decode_prologue(ctypes.byref(params), *args, _stream_handle(stream)), "hpc_decode_prologue")
+
+
+class PrologueLauncher:
+    """hpc_decode_prologue with its arguments marshalled once: each call
+    issues exactly one launch on the stream given at construction (default:
+    the current stream then).  The tensors must stay alive and unchanged in
+    shape; positions and caches are read on the device at every call."""
+
+    def __init__(self, q_in, k_in, v_in, q_norm_w, k_norm_w, positions, block_table, k_cache, v_cache, q_out,
+                 q_fp8=None, *, eps, theta, k_scale=1.0, v_scale=1.0, q_scale=1.0, stream=None):
+        from . import _stream_handle
+        self._keep = (q_in, k_in, v_in, q_norm_w, k_norm_w, positions, block_table, k_cache, v_cache, q_out, q_fp8)
+        self.params, args = _args(q_in, k_in, v_in, q_norm_w, k_norm_w, positions, block_table, k_cache, v_cache,
+                                  q_out, q_fp8, eps, theta, k_scale, v_scale, q_scale)
+        self._args = (ctypes.byref(self.params), *args, _stream_handle(stream))
+        _lib.check(lib().hpc_decode_prologue_check(*self._args[:-1]), "PrologueLauncher")
+        self._fn = lib().hpc_decode_prologue
+
+    def __call__(self) -> None:
+        status = self._fn(*self._args)
+        if status:
+            _lib.check(status, "hpc_decode_prologue")
