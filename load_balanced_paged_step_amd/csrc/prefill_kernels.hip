@@ -126,8 +126,10 @@ struct TileRegs {
     }
 };
 
-template <bool FP8, int HPW>
-__global__ void __launch_bounds__(kThreads)
+// With one tile in flight, two workgroups per CU are the point (they hide
+// each other's load latency), so the register budget is held to 2 waves per SIMD.
+template <bool FP8, int HPW, int PD>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PD == 1 && HPW <= 2 ? 2 : 1, 4)))
 prefill_kernel(PrefillArgs a) {
     __shared__ __attribute__((aligned(16))) char lds_k[kPage * kLdsRow];
     __shared__ __attribute__((aligned(16))) char lds_v[kPage * kLdsRow];
@@ -182,18 +184,10 @@ prefill_kernel(PrefillArgs a) {
     }
 
     const int32_t* bt = a.block_table + int64_t(b) * a.max_pages_per_seq;
-    TileRegs<FP8> regs;
-    if (n_tiles > 0) regs.load(a, bt[0], h, L < kPage ? L : kPage, tid);
+    auto rows_in = [&](int t) { const int r = L - t * kPage; return r < kPage ? r : kPage; };
 
-    for (int t = 0; t < n_tiles; ++t) {
-        __syncthreads();                      // every wave is done with the previous tile
-        regs.store(lds_k, lds_v, tid);
-        __syncthreads();                      // the tile is in LDS
-        if (t + 1 < n_tiles) {
-            const int rest = L - (t + 1) * kPage;
-            regs.load(a, bt[t + 1], h, rest < kPage ? rest : kPage, tid);
-        }
-
+    // one tile, already in LDS: scores, online softmax, P V
+    auto compute = [&](int t) {
         // S^T blocks: 4 x 16 KV tokens against each row block's 16 queries
         f32x4 sc[HPW][4];
 #pragma unroll
@@ -213,7 +207,9 @@ prefill_kernel(PrefillArgs a) {
         const int tok0 = t * kPage;
         const bool masked_tile = tok0 + kPage - 1 > pos0;      // some token here is past some query
         const int qpos = pos0 + n;
-        bf16x4 pop[HPW][4];
+        // P^T operands of 32-token chunks: lane group g's 8 k-slots are tokens
+        // 4g .. 4g+3 of 16-token block 2c and of block 2c + 1
+        bf16x8 pop[HPW][2];
 #pragma unroll
         for (int r = 0; r < HPW; ++r) {
             float mt = -INFINITY;
@@ -234,41 +230,77 @@ prefill_kernel(PrefillArgs a) {
             const float alpha = __builtin_amdgcn_exp2f(m[r] - m_use);
             m[r] = m_new;
             float psum = 0.f;
+            float p[4][4];
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
-                float p[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    p[i] = __builtin_amdgcn_exp2f(sc[r][kb][i] - m_use);
-                    psum += p[i];
+                    p[kb][i] = __builtin_amdgcn_exp2f(sc[r][kb][i] - m_use);
+                    psum += p[kb][i];
                 }
-                pop[r][kb] = bf16x4{static_cast<__bf16>(p[0]), static_cast<__bf16>(p[1]),
-                                    static_cast<__bf16>(p[2]), static_cast<__bf16>(p[3])};
             }
-            l[r] = l[r] * alpha + psum;
 #pragma unroll
-            for (int nb = 0; nb < 8; ++nb) acc[r][nb] = acc[r][nb] * alpha;
+            for (int c = 0; c < 2; ++c)
+                pop[r][c] = bf16x8{static_cast<__bf16>(p[2 * c][0]), static_cast<__bf16>(p[2 * c][1]),
+                                   static_cast<__bf16>(p[2 * c][2]), static_cast<__bf16>(p[2 * c][3]),
+                                   static_cast<__bf16>(p[2 * c + 1][0]), static_cast<__bf16>(p[2 * c + 1][1]),
+                                   static_cast<__bf16>(p[2 * c + 1][2]), static_cast<__bf16>(p[2 * c + 1][3])};
+            l[r] = l[r] * alpha + psum;
+            // the accumulators change only where a running max grew; skip the
+            // rescale when it grew nowhere in the wave
+            if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+                for (int nb = 0; nb < 8; ++nb) acc[r][nb] = acc[r][nb] * alpha;
+            }
         }
 
-        // O^T += V^T P^T
+        // O^T += V^T P^T on 32-token chunks (MFMA 16x16x32): the V^T operand of
+        // lane (n, g) holds dim 8n + nb of the same 8 tokens as its P slots
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            u32x4 rows[4];
+        for (int c = 0; c < 2; ++c) {
+            u32x4 rows[8];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                rows[i] = *reinterpret_cast<const u32x4*>(lds_v + (16 * kb + 4 * g + i) * kLdsRow + 16 * n);
+            for (int i = 0; i < 4; ++i) {
+                rows[i] = *reinterpret_cast<const u32x4*>(lds_v + (32 * c + 4 * g + i) * kLdsRow + 16 * n);
+                rows[4 + i] = *reinterpret_cast<const u32x4*>(lds_v + (32 * c + 16 + 4 * g + i) * kLdsRow + 16 * n);
+            }
 #pragma unroll
             for (int nb = 0; nb < 8; ++nb) {
                 const int d = nb >> 1;
                 const uint32_t sel = (nb & 1) ? kSelHi : kSelLo;
-                const u32x2 vt = u32x2{__builtin_amdgcn_perm(rows[1][d], rows[0][d], sel),
-                                       __builtin_amdgcn_perm(rows[3][d], rows[2][d], sel)};
+                const u32x4 vt = u32x4{__builtin_amdgcn_perm(rows[1][d], rows[0][d], sel),
+                                       __builtin_amdgcn_perm(rows[3][d], rows[2][d], sel),
+                                       __builtin_amdgcn_perm(rows[5][d], rows[4][d], sel),
+                                       __builtin_amdgcn_perm(rows[7][d], rows[6][d], sel)};
 #pragma unroll
                 for (int r = 0; r < HPW; ++r)
-                    acc[r][nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(bitcast<bf16x4>(vt), pop[r][kb],
-                                                                           acc[r][nb], 0, 0, 0);
+                    acc[r][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(vt), pop[r][c], acc[r][nb],
+                                                                         0, 0, 0);
             }
         }
+    };
+
+    // tile t goes global -> registers -> LDS; with PD = 2 two tiles are in
+    // flight (two register sets used in turn), with PD = 1 one
+    auto step = [&](TileRegs<FP8>& rg, int t) {
+        __syncthreads();                      // every wave is done with the previous tile
+        rg.store(lds_k, lds_v, tid);
+        __syncthreads();                      // the tile is in LDS
+        if (t + PD < n_tiles) rg.load(a, bt[t + PD], h, rows_in(t + PD), tid);
+        compute(t);
+    };
+    if constexpr (PD == 2) {
+        TileRegs<FP8> ra, rb;
+        if (n_tiles > 0) ra.load(a, bt[0], h, rows_in(0), tid);
+        if (n_tiles > 1) rb.load(a, bt[1], h, rows_in(1), tid);
+        for (int t = 0; t < n_tiles; t += 2) {
+            step(ra, t);
+            if (t + 1 < n_tiles) step(rb, t + 1);
+        }
+    } else {
+        TileRegs<FP8> ra;
+        if (n_tiles > 0) ra.load(a, bt[0], h, rows_in(0), tid);
+        for (int t = 0; t < n_tiles; ++t) step(ra, t);
     }
 
     // epilogue: out = acc / l, lse = (m + log2 l) ln 2; a query with no
@@ -296,16 +328,41 @@ prefill_kernel(PrefillArgs a) {
     }
 }
 
+// Compute units of the current device (looked up once per device).
+int device_cus() {
+    static int cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cached[dev]) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+        cached[dev] = cus;
+    }
+    return cached[dev];
+}
+
+// Prefetch depth: with fewer than two units per compute unit the grid cannot
+// hide load latency behind other workgroups, so two tiles go in flight (one
+// workgroup per CU fits); with more, one tile in flight keeps two workgroups
+// per CU (HPW <= 2).  HPW = 4 holds one tile in flight either way.
+template <bool FP8, int HPW>
+void launch_hpw(const PrefillArgs& a, int n_units, hipStream_t s) {
+    const dim3 grid(n_units), block(kThreads);
+    if (n_units < 2 * device_cus())
+        hipLaunchKernelGGL((prefill_kernel<FP8, HPW, 2>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((prefill_kernel<FP8, HPW, 1>), grid, block, 0, s, a);
+}
+
 template <bool FP8>
 int launch_fp8(const PrefillArgs& a, int n_units, void* stream) {
-    const dim3 grid(n_units), block(kThreads);
     const hipStream_t s = static_cast<hipStream_t>(stream);
     if (a.group <= 4)
-        hipLaunchKernelGGL((prefill_kernel<FP8, 1>), grid, block, 0, s, a);
+        launch_hpw<FP8, 1>(a, n_units, s);
     else if (a.group <= 8)
-        hipLaunchKernelGGL((prefill_kernel<FP8, 2>), grid, block, 0, s, a);
+        launch_hpw<FP8, 2>(a, n_units, s);
     else
-        hipLaunchKernelGGL((prefill_kernel<FP8, 4>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((prefill_kernel<FP8, 4, 1>), dim3(n_units), dim3(kThreads), 0, s, a);
     return static_cast<int>(hipGetLastError());
 }
 
