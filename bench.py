@@ -616,7 +616,8 @@ def skew_sweep(dev, W: int, cus: int, steps: int, warmup: int) -> dict:
     bf16).  Times are the summed decode + merge kernel durations per step
     (dispatch-stamped events), KV rotated over >= 1 GiB of copies; host plans
     are built and uploaded once, outside the timing; ratio = static /
-    balanced (device-scheduled)."""
+    balanced (device-scheduled), and static / balanced host plan (the same
+    host-planned kernel as the static plans)."""
     import torch
 
     import load_balanced_paged_step_amd as hd
@@ -672,11 +673,14 @@ def skew_sweep(dev, W: int, cus: int, steps: int, warmup: int) -> dict:
         row = {"batch": name, "balanced_us": round(balanced, 2), "balanced_host_plan_us": round(balanced_host, 2),
                "static_us": {str(S): round(t, 2) for S, t in static.items()},
                "rule_splits": rule_S, "ratio_rule": round(static[rule_S] / balanced, 3),
-               "best_splits": best_S, "ratio_best": round(static[best_S] / balanced, 3)}
+               "best_splits": best_S, "ratio_best": round(static[best_S] / balanced, 3),
+               # the balanced plan through the same host-planned kernel the static plans run through
+               "ratio_rule_host_plan": round(static[rule_S] / balanced_host, 3),
+               "ratio_best_host_plan": round(static[best_S] / balanced_host, 3)}
         log(f"skew sweep {name}: balanced {balanced:.1f} us (host-planned {balanced_host:.1f}); "
             f"static S={rule_S} (rule) "
             f"{static[rule_S]:.1f} us = {row['ratio_rule']}x; best static S={best_S} {static[best_S]:.1f} us "
-            f"= {row['ratio_best']}x")
+            f"= {row['ratio_best']}x; host-planned balanced vs best static {row['ratio_best_host_plan']}x")
         rows.append(row)
         del ks, vs, launchers
         torch.cuda.empty_cache()

@@ -288,7 +288,11 @@ struct HostWalker {
         const int idx = e0 + static_cast<int>(threadIdx.x & 63);
         c_u = c_t0 = c_t1 = c_part = c_len = 0;
         if (idx < e_end) {
-            const int4 ew = *reinterpret_cast<const int4*>(ent + 4 * static_cast<int64_t>(idx));
+            // an entry's four words start at a 4-byte boundary only (the plan's
+            // header and worker_ptr come first), so they are copied, not read
+            // through an int4 pointer
+            int4 ew;
+            __builtin_memcpy(&ew, ent + 4 * static_cast<int64_t>(idx), sizeof(ew));
             c_u = ew.x;
             c_t0 = ew.y;
             c_t1 = ew.z;
