@@ -126,19 +126,27 @@ struct TileRegs {
     }
 };
 
-// With one tile in flight, two workgroups per CU are the point (they hide
-// each other's load latency), so the register budget is held to 2 waves per SIMD.
-template <bool FP8, int HPW, int PD>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PD == 1 && HPW <= 2 ? 2 : 1, 4)))
+// NG groups of 4 waves share a unit: group gg takes tiles gg, gg + NG, ...
+// with its own LDS tile, and at the end the groups' softmax states are
+// merged in LDS.  Two waves per SIMD are the point either way (two
+// workgroups per CU with NG = 1, two groups with NG = 2), so the register
+// budget is held to 2 waves per SIMD where the accumulators allow (HPW <= 2).
+template <bool FP8, int HPW, int NG>
+__global__ void __launch_bounds__(kThreads * NG) __attribute__((amdgpu_waves_per_eu(HPW <= 2 ? 2 : 1, 4)))
 prefill_kernel(PrefillArgs a) {
-    __shared__ __attribute__((aligned(16))) char lds_k[kPage * kLdsRow];
-    __shared__ __attribute__((aligned(16))) char lds_v[kPage * kLdsRow];
+    static_assert(NG == 1 || (NG == 2 && HPW <= 2), "a group merge needs the tile buffers' 68 KB");
+    __shared__ __attribute__((aligned(16))) char lds[NG * 2 * kPage * kLdsRow];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int gg = wave_all >> 2;     // group of this wave
+    const int wave = wave_all & 3;    // wave within the group: owns heads wave + 4 r
+    const int tid_g = tid & (kThreads - 1);
     const int n = lane & 15;          // query column / K row / V dim group
     const int g = lane >> 4;          // lane group
+    char* lds_k = lds + gg * 2 * kPage * kLdsRow;
+    char* lds_v = lds_k + kPage * kLdsRow;
 
     // the unit
     const int32_t* w = a.work + 4 * static_cast<int64_t>(blockIdx.x);
@@ -280,27 +288,58 @@ prefill_kernel(PrefillArgs a) {
         }
     };
 
-    // tile t goes global -> registers -> LDS; with PD = 2 two tiles are in
-    // flight (two register sets used in turn), with PD = 1 one
-    auto step = [&](TileRegs<FP8>& rg, int t) {
-        __syncthreads();                      // every wave is done with the previous tile
-        rg.store(lds_k, lds_v, tid);
-        __syncthreads();                      // the tile is in LDS
-        if (t + PD < n_tiles) rg.load(a, bt[t + PD], h, rows_in(t + PD), tid);
-        compute(t);
-    };
-    if constexpr (PD == 2) {
-        TileRegs<FP8> ra, rb;
-        if (n_tiles > 0) ra.load(a, bt[0], h, rows_in(0), tid);
-        if (n_tiles > 1) rb.load(a, bt[1], h, rows_in(1), tid);
-        for (int t = 0; t < n_tiles; t += 2) {
-            step(ra, t);
-            if (t + 1 < n_tiles) step(rb, t + 1);
+    // tile t goes global -> registers -> LDS; one tile in flight per group
+    // while the group computes the one before.  Every wave meets every
+    // barrier; a group past the unit's last tile only waits.
+    {
+        TileRegs<FP8> rg;
+        if (gg < n_tiles) rg.load(a, bt[gg], h, rows_in(gg), tid_g);
+        const int rounds = (n_tiles + NG - 1) / NG;
+        for (int i = 0; i < rounds; ++i) {
+            const int t = NG * i + gg;
+            const bool have = NG == 1 || t < n_tiles;   // a single group always has its tile
+            __syncthreads();                  // every wave is done with the previous tile
+            if (have) rg.store(lds_k, lds_v, tid_g);
+            __syncthreads();                  // the tile is in LDS
+            if (t + NG < n_tiles) rg.load(a, bt[t + NG], h, rows_in(t + NG), tid_g);
+            if (have) compute(t);
         }
-    } else {
-        TileRegs<FP8> ra;
-        if (n_tiles > 0) ra.load(a, bt[0], h, rows_in(0), tid);
-        for (int t = 0; t < n_tiles; ++t) step(ra, t);
+    }
+    if constexpr (NG == 2) {
+        // group 1 leaves its state in LDS (over the tile buffers, exactly
+        // HPW * 34 values per lane), group 0 merges it by log-sum-exp
+        float* st = reinterpret_cast<float*>(lds);
+        const int slot = wave * 64 + lane;
+        __syncthreads();
+        if (gg == 1) {
+#pragma unroll
+            for (int r = 0; r < HPW; ++r) {
+#pragma unroll
+                for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) st[((r * 8 + nb) * 4 + i) * kThreads + slot] = acc[r][nb][i];
+                st[(HPW * 32 + r) * kThreads + slot] = m[r];
+                st[(HPW * 33 + r) * kThreads + slot] = l[r];
+            }
+        }
+        __syncthreads();
+        if (gg == 1) return;
+#pragma unroll
+        for (int r = 0; r < HPW; ++r) {
+            const float m1 = st[(HPW * 32 + r) * kThreads + slot];
+            const float l1 = st[(HPW * 33 + r) * kThreads + slot];
+            const float mx = fmaxf(m[r], m1);
+            const float mu = (mx == -INFINITY) ? 0.f : mx;
+            const float f0 = __builtin_amdgcn_exp2f(m[r] - mu);
+            const float f1 = __builtin_amdgcn_exp2f(m1 - mu);
+            m[r] = mx;
+            l[r] = l[r] * f0 + l1 * f1;
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc[r][nb][i] = acc[r][nb][i] * f0 + st[((r * 8 + nb) * 4 + i) * kThreads + slot] * f1;
+        }
     }
 
     // epilogue: out = acc / l, lse = (m + log2 l) ln 2; a query with no
@@ -341,17 +380,17 @@ int device_cus() {
     return cached[dev];
 }
 
-// Prefetch depth: with fewer than two units per compute unit the grid cannot
-// hide load latency behind other workgroups, so two tiles go in flight (one
-// workgroup per CU fits); with more, one tile in flight keeps two workgroups
-// per CU (HPW <= 2).  HPW = 4 holds one tile in flight either way.
+// With fewer than two units per compute unit the grid cannot hide one
+// unit's tile chain behind other workgroups, so two groups of 4 waves split
+// each unit's tiles (NG = 2, G <= 8); with more, a unit is one group of 4
+// waves and two workgroups share a CU.  G > 8 (4 heads per wave) keeps
+// NG = 1: its group state does not fit the tile buffers.
 template <bool FP8, int HPW>
 void launch_hpw(const PrefillArgs& a, int n_units, hipStream_t s) {
-    const dim3 grid(n_units), block(kThreads);
     if (n_units < 2 * device_cus())
-        hipLaunchKernelGGL((prefill_kernel<FP8, HPW, 2>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((prefill_kernel<FP8, HPW, 2>), dim3(n_units), dim3(2 * kThreads), 0, s, a);
     else
-        hipLaunchKernelGGL((prefill_kernel<FP8, HPW, 1>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((prefill_kernel<FP8, HPW, 1>), dim3(n_units), dim3(kThreads), 0, s, a);
 }
 
 template <bool FP8>
