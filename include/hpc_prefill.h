@@ -63,7 +63,8 @@ int64_t hpc_prefill_plan(const int32_t* q_start, const int32_t* seq_lens, int32_
  * entries).
  *
  * params       heads, page geometry, kv dtype and scales as for decode
- *              (tile_math and fused_merge must be 0)
+ *              (tile_math and fused_merge must be 0; sm_scale * k_scale must
+ *              be positive)
  * total_q      rows of q / out / lse (= q_start[batch])
  * q            device bf16 [total_q][Hq][128]
  * q_start      device int32 [batch + 1]; must hold the values the plan was made from

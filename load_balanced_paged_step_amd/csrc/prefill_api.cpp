@@ -83,6 +83,8 @@ extern "C" int hpc_prefill_check(const hpc_decode_params* p, int32_t batch, int3
     if (p->max_pages_per_seq < 1 || p->num_pages < 1) return HPC_ERR_INVALID;
     if (!std::isfinite(p->sm_scale) || !std::isfinite(p->k_scale) || !std::isfinite(p->v_scale))
         return HPC_ERR_INVALID;
+    // the kernel keeps its running max on raw scores, which needs a positive score scale
+    if (!(static_cast<double>(p->sm_scale) * p->k_scale > 0.0)) return HPC_ERR_INVALID;
     if (batch < 1 || total_q < 0 || n_units < 0) return HPC_ERR_INVALID;
     // q row offsets (16 rows of one block, all heads) and tile indices must fit the kernels' int32 math
     if (int64_t(total_q) * p->num_q_heads * HPC_DECODE_HEAD_DIM * 2 >= INT32_MAX * int64_t(64)) return HPC_ERR_INVALID;

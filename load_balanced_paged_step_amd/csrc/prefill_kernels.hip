@@ -49,7 +49,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kQBlock = 16;                       // queries per unit
-constexpr int kLdsRow = kHeadDim * 2 + 16;        // bytes per LDS row: 256 + 16 pad
+constexpr int kLdsRow = kHeadDim * 2 + 32;        // bytes per LDS row: 256 + 32 pad (half the bank
+                                                  // conflicts of a 16-byte pad, measured)
 constexpr uint32_t kRsrcWord3 = 0x00020000u;      // raw (untyped) buffer
 constexpr uint32_t kSelLo = 0x05040100u;          // v_perm: {b.lo, a.lo}
 constexpr uint32_t kSelHi = 0x07060302u;          // v_perm: {b.hi, a.hi}
@@ -211,10 +212,23 @@ prefill_kernel(PrefillArgs a) {
             }
         }
 
-        // online softmax per query column n, exp2 domain
+        // online softmax per query column n, exp2 domain.  The running max m
+        // is kept on raw scores (c = qk_scale_log2 > 0 keeps their order), and
+        // p = 2^(s c - m c) is one FMA per score.  Only tiles that reach past
+        // the block's first query carry masked tokens.
         const int tok0 = t * kPage;
-        const bool masked_tile = tok0 + kPage - 1 > pos0;      // some token here is past some query
+        const bool masked_tile = tok0 + kPage - 1 > pos0;
         const int qpos = pos0 + n;
+        const float c = a.qk_scale_log2;
+        if (masked_tile) {
+#pragma unroll
+            for (int r = 0; r < HPW; ++r)
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (tok0 + 16 * kb + 4 * g + i > qpos) sc[r][kb][i] = -INFINITY;
+        }
         // P^T operands of 32-token chunks: lane group g's 8 k-slots are tokens
         // 4g .. 4g+3 of 16-token block 2c and of block 2c + 1
         bf16x8 pop[HPW][2];
@@ -222,20 +236,14 @@ prefill_kernel(PrefillArgs a) {
         for (int r = 0; r < HPW; ++r) {
             float mt = -INFINITY;
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
+            for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int tok = tok0 + 16 * kb + 4 * g + i;
-                    const bool vis = !masked_tile || tok <= qpos;
-                    sc[r][kb][i] = vis ? sc[r][kb][i] * a.qk_scale_log2 : -INFINITY;
-                    mt = fmaxf(mt, sc[r][kb][i]);
-                }
-            }
+                for (int i = 0; i < 4; ++i) mt = fmaxf(mt, sc[r][kb][i]);
             mt = fmaxf(mt, __shfl_xor(mt, 16));
             mt = fmaxf(mt, __shfl_xor(mt, 32));
             const float m_new = fmaxf(m[r], mt);
-            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m[r] - m_use);
+            const float mc = (m_new == -INFINITY) ? 0.f : m_new * c;   // the new max, scaled
+            const float alpha = __builtin_amdgcn_exp2f(m[r] * c - mc);
             m[r] = m_new;
             float psum = 0.f;
             float p[4][4];
@@ -243,16 +251,16 @@ prefill_kernel(PrefillArgs a) {
             for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    p[kb][i] = __builtin_amdgcn_exp2f(sc[r][kb][i] - m_use);
+                    p[kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r][kb][i], c, -mc));
                     psum += p[kb][i];
                 }
             }
 #pragma unroll
-            for (int c = 0; c < 2; ++c)
-                pop[r][c] = bf16x8{static_cast<__bf16>(p[2 * c][0]), static_cast<__bf16>(p[2 * c][1]),
-                                   static_cast<__bf16>(p[2 * c][2]), static_cast<__bf16>(p[2 * c][3]),
-                                   static_cast<__bf16>(p[2 * c + 1][0]), static_cast<__bf16>(p[2 * c + 1][1]),
-                                   static_cast<__bf16>(p[2 * c + 1][2]), static_cast<__bf16>(p[2 * c + 1][3])};
+            for (int cc = 0; cc < 2; ++cc)
+                pop[r][cc] = bf16x8{static_cast<__bf16>(p[2 * cc][0]), static_cast<__bf16>(p[2 * cc][1]),
+                                    static_cast<__bf16>(p[2 * cc][2]), static_cast<__bf16>(p[2 * cc][3]),
+                                    static_cast<__bf16>(p[2 * cc + 1][0]), static_cast<__bf16>(p[2 * cc + 1][1]),
+                                    static_cast<__bf16>(p[2 * cc + 1][2]), static_cast<__bf16>(p[2 * cc + 1][3])};
             l[r] = l[r] * alpha + psum;
             // the accumulators change only where a running max grew; skip the
             // rescale when it grew nowhere in the wave
@@ -265,12 +273,12 @@ prefill_kernel(PrefillArgs a) {
         // O^T += V^T P^T on 32-token chunks (MFMA 16x16x32): the V^T operand of
         // lane (n, g) holds dim 8n + nb of the same 8 tokens as its P slots
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
+        for (int cc = 0; cc < 2; ++cc) {
             u32x4 rows[8];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                rows[i] = *reinterpret_cast<const u32x4*>(lds_v + (32 * c + 4 * g + i) * kLdsRow + 16 * n);
-                rows[4 + i] = *reinterpret_cast<const u32x4*>(lds_v + (32 * c + 16 + 4 * g + i) * kLdsRow + 16 * n);
+                rows[i] = *reinterpret_cast<const u32x4*>(lds_v + (32 * cc + 4 * g + i) * kLdsRow + 16 * n);
+                rows[4 + i] = *reinterpret_cast<const u32x4*>(lds_v + (32 * cc + 16 + 4 * g + i) * kLdsRow + 16 * n);
             }
 #pragma unroll
             for (int nb = 0; nb < 8; ++nb) {
@@ -282,7 +290,7 @@ prefill_kernel(PrefillArgs a) {
                                        __builtin_amdgcn_perm(rows[7][d], rows[6][d], sel)};
 #pragma unroll
                 for (int r = 0; r < HPW; ++r)
-                    acc[r][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(vt), pop[r][c], acc[r][nb],
+                    acc[r][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(vt), pop[r][cc], acc[r][nb],
                                                                          0, 0, 0);
             }
         }
@@ -328,10 +336,10 @@ prefill_kernel(PrefillArgs a) {
         for (int r = 0; r < HPW; ++r) {
             const float m1 = st[(HPW * 32 + r) * kThreads + slot];
             const float l1 = st[(HPW * 33 + r) * kThreads + slot];
-            const float mx = fmaxf(m[r], m1);
-            const float mu = (mx == -INFINITY) ? 0.f : mx;
-            const float f0 = __builtin_amdgcn_exp2f(m[r] - mu);
-            const float f1 = __builtin_amdgcn_exp2f(m1 - mu);
+            const float mx = fmaxf(m[r], m1);                       // raw scores, as in the tile loop
+            const float mu = (mx == -INFINITY) ? 0.f : mx * a.qk_scale_log2;
+            const float f0 = __builtin_amdgcn_exp2f(m[r] * a.qk_scale_log2 - mu);
+            const float f1 = __builtin_amdgcn_exp2f(m1 * a.qk_scale_log2 - mu);
             m[r] = mx;
             l[r] = l[r] * f0 + l1 * f1;
 #pragma unroll
@@ -363,7 +371,7 @@ prefill_kernel(PrefillArgs a) {
                                    pack_bf16x2(acc[r][6][i] * inv, acc[r][7][i] * inv)};
             *reinterpret_cast<u32x4*>(o + (32 * g + 8 * i) * 2) = pk;
         }
-        if (g == 0) a.lse[row] = lt > 0.f ? (m[r] + __log2f(lt)) * kLn2 : -INFINITY;
+        if (g == 0) a.lse[row] = lt > 0.f ? (m[r] * a.qk_scale_log2 + __log2f(lt)) * kLn2 : -INFINITY;
     }
 }
 

@@ -83,3 +83,15 @@ def test_check_errors():
     assert call(hd.make_params(64, 2, 8, 32, hd.HPC_KV_BF16, 0.088)) == hd.HPC_ERR_UNSUPPORTED     # G = 32
     assert call(hd.make_params(15, 2, 8, 32, hd.HPC_KV_BF16, 0.088)) == hd.HPC_ERR_INVALID
     assert call(hd.make_params(16, 2, 8, 32, hd.HPC_KV_BF16, float("nan"))) == hd.HPC_ERR_INVALID
+
+
+def test_check_refuses_a_non_positive_score_scale():
+    """The kernel keeps its running max on raw scores, so the score scale
+    sm_scale * k_scale must be positive."""
+    lib = hd.lib()
+    fake = ctypes.c_void_p(0x1000)
+    for sm, ks, code in ((0.088, 1.0, hd.HPC_OK), (-0.088, 1.0, hd.HPC_ERR_INVALID), (0.0, 1.0, hd.HPC_ERR_INVALID),
+                         (0.088, -2.0, hd.HPC_ERR_INVALID)):
+        p = hd.make_params(16, 2, 8, 32, hd.HPC_KV_BF16, sm, k_scale=ks)
+        assert lib.hpc_prefill_check(ctypes.byref(p), 2, 40, fake, fake, fake, fake, fake, fake, fake, 4, fake,
+                                     fake) == code
