@@ -499,6 +499,51 @@ def _events_us(fn, steps: int, warmup: int) -> float:
     return e0.elapsed_time(e1) / steps * 1e3
 
 
+def _blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:
+        return len(os.sched_getaffinity(0))
+
+
+def prefill_oracle_baseline(pi) -> dict:
+    """The float64 prefill oracle on the host, on a bounded sample: the whole
+    step when it holds one sequence, else its first sequence alone (queries
+    and cache as they are); the rate is that sample's FLOPs / time."""
+    import numpy as np
+    from oracle import prefill_attention
+    from workloads import PrefillInputs
+    c = pi.cache
+    qs = pi.q_start.numpy()
+    if c.batch == 1:
+        sample, desc = pi, "the whole step"
+    else:
+        sub = make_sub_prefill(pi, 0)
+        sample, desc = sub, f"sequence 0 alone ({int(qs[1] - qs[0])} queries over {int(c.seq_lens[0])} tokens)"
+    sc = sample.cache
+    t0 = time.perf_counter()
+    prefill_attention(sample.q_bits(), sc.k_bits(), sc.v_bits(), sc.block_table.numpy(), sc.seq_lens.numpy(),
+                      sample.q_start.numpy(), num_q_heads=sc.num_q_heads, num_kv_heads=sc.num_kv_heads,
+                      kv_format=sc.kv_dtype, sm_scale=sc.sm_scale, k_scale=sc.k_scale, v_scale=sc.v_scale)
+    dt = time.perf_counter() - t0
+    return {"value": sample.flops() / dt / 1e12, "unit": "TFLOP/s", "cores": _blas_threads(), "kind": "oracle",
+            "sample": f"{desc}, one run of the float64 oracle, {dt:.2f} s"}
+
+
+def make_sub_prefill(pi, b: int):
+    """Sequence b of a prefill step as a one-sequence step (same cache tensors)."""
+    import numpy as np
+    import torch
+    from dataclasses import replace
+    from workloads import PrefillInputs
+    c = pi.cache
+    qs = pi.q_start.numpy()
+    r0, r1 = int(qs[b]), int(qs[b + 1])
+    sub_cache = replace(c, q=c.q[b:b + 1], block_table=c.block_table[b:b + 1], seq_lens=c.seq_lens[b:b + 1])
+    return PrefillInputs(cache=sub_cache, q=pi.q[r0:r1], q_start=torch.tensor([0, r1 - r0], dtype=torch.int32))
+
+
 def prefill_bench(dev, cus: int, which: str, steps: int, warmup: int) -> dict:
     """Causal prefill / extend attention: mean kernel time over back-to-back
     launches (events on the launch stream; the work list is planned and
@@ -534,8 +579,9 @@ def prefill_bench(dev, cus: int, which: str, steps: int, warmup: int) -> dict:
                "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                             "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)},
                "plan_and_upload_us": round(plan_us, 1)}
+        row["cpu_baseline"] = prefill_oracle_baseline(pi)
         log(f"prefill {name}: {us:.2f} us, {tflops:.1f} TFLOP/s ({row['roofline']['frac']:.3f} of bf16 MFMA peak), "
-            f"{step.n_units} units")
+            f"{step.n_units} units; oracle {row['cpu_baseline']['value']:.4f} TFLOP/s")
         rows.append(row)
         del q, k, v, out, lse
         torch.cuda.empty_cache()
@@ -597,8 +643,18 @@ def prologue_bench(dev, cus: int, W: int, steps: int, warmup: int) -> dict:
                             "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                             "frac": round(nbytes / (pro_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 5)},
                "decode_step_us": round(dec_us, 3), "prologue_plus_decode_step_us": round(both_us, 3)}
+        from oracle import decode_prologue
+        t0 = time.perf_counter()
+        decode_prologue(pi.bits(pi.q_in), pi.bits(pi.k_in), pi.bits(pi.v_in), pi.bits(pi.q_norm_w),
+                        pi.bits(pi.k_norm_w), pi.positions.numpy(), c.block_table.numpy(), c.k_bits(), c.v_bits(),
+                        kv_format=c.kv_dtype, eps=pi.eps, theta=pi.theta, k_scale=c.k_scale, v_scale=c.v_scale,
+                        q_scale=pi.q_scale if q_fp8 is not None else None)
+        dt = time.perf_counter() - t0
+        row["cpu_baseline"] = {"value": round(dt * 1e6, 1), "unit": "us per step", "cores": _blas_threads(),
+                               "kind": "oracle", "sample": "the whole batch, one run of the float64 oracle (it "
+                               "copies both caches, which dominates its time)"}
         log(f"prologue {row['workload']}: {pro_us:.2f} us ({nbytes} B); decode step {dec_us:.2f} us, "
-            f"with prologue {both_us:.2f} us")
+            f"with prologue {both_us:.2f} us; oracle {dt * 1e3:.1f} ms")
         rows.append(row)
     return {"mode": "prologue", "n_workers": W,
             "timing": "mean of back-to-back launches, HIP events on the launch stream (KV resident, one copy)",
