@@ -548,7 +548,10 @@ def prefill_bench(dev, cus: int, which: str, steps: int, warmup: int) -> dict:
     """Causal prefill / extend attention: mean kernel time over back-to-back
     launches (events on the launch stream; the work list is planned and
     uploaded once, outside the timing), algorithmic FLOPs (4 * 128 per query
-    head and visible token) against the bf16 MFMA peak."""
+    head and visible token) against the bf16 MFMA peak.  Each workload runs
+    with whole units (n_workers = 0) and with balanced plans over 1, 2 and 4
+    workers per CU; the roofline object is that of the balanced plan at 2
+    workers per CU (two workgroups of one group fit a CU)."""
     import torch
 
     from load_balanced_paged_step_amd.prefill import PrefillStep
@@ -557,6 +560,7 @@ def prefill_bench(dev, cus: int, which: str, steps: int, warmup: int) -> dict:
     clock_warmup(dev, cus)
     names = list(PREFILL_WORKLOADS) if which == "all" else [which]
     rows = []
+    W_default = 2 * cus
     for name in names:
         pi = prefill_workload_inputs(name)
         c = pi.cache
@@ -565,23 +569,36 @@ def prefill_bench(dev, cus: int, which: str, steps: int, warmup: int) -> dict:
         bt, sl = c.block_table.to(dev), c.seq_lens.to(dev)
         out = torch.empty_like(q)
         lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
-        t0 = time.perf_counter()
-        step = PrefillStep(pi.q_start, c.seq_lens, c.num_kv_heads, c.max_pages_per_seq, device=dev)
-        plan_us = (time.perf_counter() - t0) * 1e6
-
-        one = step.bind(q, qs, k, v, bt, sl, out, lse, sm_scale=c.sm_scale, k_scale=c.k_scale, v_scale=c.v_scale)
-        us = _events_us(one, max(steps, 20), max(warmup, 5))
         flops = pi.flops()
-        tflops = flops / (us * 1e-6) / 1e12
+        plans = {}
+        for W in (0, cus, W_default, 4 * cus):
+            t0 = time.perf_counter()
+            step = PrefillStep(pi.q_start, c.seq_lens, c.num_q_heads, c.num_kv_heads, c.max_pages_per_seq,
+                               n_workers=W, device=dev)
+            plan_us = (time.perf_counter() - t0) * 1e6
+            one = step.bind(q, qs, k, v, bt, sl, out, lse, sm_scale=c.sm_scale, k_scale=c.k_scale,
+                            v_scale=c.v_scale)
+            us = _events_us(one, max(steps, 20), max(warmup, 5))
+            plans[W] = {"n_workers": W, "entries": step.n_entries, "cut_units": step.n_merge,
+                        "longest_entry_tiles": int(step.entries[:, 3].max()) if step.n_entries else 0,
+                        "us": round(us, 3), "TFLOPs": round(flops / (us * 1e-6) / 1e12, 1),
+                        "plan_and_upload_us": round(plan_us, 1)}
+            del one, step
+        main = plans[W_default]
+        tflops = main["TFLOPs"]
         row = {"workload": name, "heads": f"{c.num_q_heads}q/{c.num_kv_heads}kv", "kv_dtype": c.kv_dtype,
-               "queries": pi.total, "kv_lens": _lens_summary(c.seq_lens.numpy()), "units": step.n_units,
-               "us": round(us, 3), "flops": flops, "TFLOPs": round(tflops, 1),
-               "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+               "queries": pi.total, "kv_lens": _lens_summary(c.seq_lens.numpy()),
+               "units": plans[0]["entries"], "flops": flops, "n_workers": W_default, "us": main["us"],
+               "TFLOPs": tflops, "whole_units_us": plans[0]["us"],
+               "balanced_speedup": round(plans[0]["us"] / main["us"], 3),
+               "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
                             "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)},
-               "plan_and_upload_us": round(plan_us, 1)}
+               "plans": list(plans.values())}
         row["cpu_baseline"] = prefill_oracle_baseline(pi)
-        log(f"prefill {name}: {us:.2f} us, {tflops:.1f} TFLOP/s ({row['roofline']['frac']:.3f} of bf16 MFMA peak), "
-            f"{step.n_units} units; oracle {row['cpu_baseline']['value']:.4f} TFLOP/s")
+        log(f"prefill {name}: " + ", ".join(f"W={p['n_workers']} {p['us']:.2f} us ({p['entries']} entries)"
+                                            for p in plans.values())
+            + f"; {tflops:.1f} TFLOP/s at W={W_default} ({row['roofline']['frac']:.3f} of bf16 MFMA peak); "
+            f"oracle {row['cpu_baseline']['value']:.4f} TFLOP/s")
         rows.append(row)
         del q, k, v, out, lse
         torch.cuda.empty_cache()

@@ -107,12 +107,16 @@ SIGNATURES = {
     "hpc_decode_prologue_check": (ctypes.c_int, [ctypes.POINTER(hpc_prologue_params), ctypes.c_int32]
                                   + [_VP] * 11),
     "hpc_prefill_units": (ctypes.c_int64, [_I32P, ctypes.c_int32, ctypes.c_int32]),
-    "hpc_prefill_plan": (ctypes.c_int64, [_I32P, _I32P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _I32P,
-                                          ctypes.c_int64]),
+    "hpc_prefill_plan_size": (ctypes.c_int64, [_I32P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]),
+    "hpc_prefill_plan": (ctypes.c_int, [_I32P, _I32P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_int32, _I32P, ctypes.c_int64, _I32P]),
+    "hpc_prefill_workspace_size": (ctypes.c_int64, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]),
     "hpc_prefill_attn": (ctypes.c_int, [_PP, ctypes.c_int32, ctypes.c_int32, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
-                                        ctypes.c_int32, _VP, _VP, _VP]),
+                                        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _VP, ctypes.c_int64, _VP, _VP,
+                                        _VP]),
     "hpc_prefill_check": (ctypes.c_int, [_PP, ctypes.c_int32, ctypes.c_int32, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
-                                         ctypes.c_int32, _VP, _VP]),
+                                         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _VP, ctypes.c_int64, _VP,
+                                         _VP]),
     "hpc_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "hpc_decode_profile_start": (ctypes.c_int, [ctypes.c_int32]),
     "hpc_decode_profile_stop": (ctypes.c_int, [_F64P, _F64P, _I32P]),

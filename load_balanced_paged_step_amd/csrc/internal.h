@@ -90,9 +90,13 @@ struct PrefillArgs {
     const void* v;
     const int32_t* block_table;  // [B][max_pages_per_seq]
     const int32_t* seq_lens;     // [B]: cached tokens, the chunk's new tokens included
-    const int32_t* work;         // [n_units][4]: (sequence, query block, KV head, cost)
+    const int32_t* work;         // [n_entries][8]: (sequence, query block, KV head, cost, t0, t1, slot, 0)
+    const int32_t* merge;        // [n_merge][8]: (sequence, query block, KV head, shares, first slot, 0...)
     void* out;                   // bf16 [total][Hq][128]
     float* lse;                  // [total][Hq]
+    float* o_part;               // [n_partials][16][G][128]: partial outputs of split units
+    float* lse_part;             // [n_partials][16][G]
+    int32_t n_partials;
     int32_t batch;
     int32_t num_q_heads;
     int32_t num_kv_heads;
@@ -114,7 +118,7 @@ int launch_decode(const DecodeArgs& a, int kv_dtype, int tile_math, int n_worker
 int launch_combine(const CombineArgs& a, int n_records, bool device_sched, void* stream,
                    void* ev_start = nullptr, void* ev_stop = nullptr);
 int launch_prologue(const PrologueArgs& a, void* stream);
-int launch_prefill(const PrefillArgs& a, int n_units, bool kv_fp8, void* stream);
+int launch_prefill(const PrefillArgs& a, int n_entries, int n_merge, bool kv_fp8, void* stream);
 int launch_plan_device(const int32_t* seq_lens, int batch, int num_kv_heads, int n_workers,
                        int max_pages_per_seq, int32_t* plan, void* stream);
 

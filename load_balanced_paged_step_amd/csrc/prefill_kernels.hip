@@ -149,11 +149,14 @@ prefill_kernel(PrefillArgs a) {
     char* lds_k = lds + gg * 2 * kPage * kLdsRow;
     char* lds_v = lds_k + kPage * kLdsRow;
 
-    // the unit
-    const int32_t* w = a.work + 4 * static_cast<int64_t>(blockIdx.x);
+    // the entry: tiles [t0, t1) of unit (b, qb, h), written to partial slot `slot` (-1: out / lse)
+    const int32_t* w = a.work + 8 * static_cast<int64_t>(blockIdx.x);
     const int b = __builtin_amdgcn_readfirstlane(w[0]);
     const int qb = __builtin_amdgcn_readfirstlane(w[1]);
     const int h = __builtin_amdgcn_readfirstlane(w[2]);
+    const int e_t0 = __builtin_amdgcn_readfirstlane(w[4]);
+    const int e_t1 = __builtin_amdgcn_readfirstlane(w[5]);
+    const int slot = __builtin_amdgcn_readfirstlane(w[6]);
     if (b < 0 || b >= a.batch || h < 0 || h >= a.num_kv_heads || qb < 0) return;
     const int r0 = a.q_start[b];
     const int nq_seq = a.q_start[b + 1] - r0;
@@ -164,8 +167,11 @@ prefill_kernel(PrefillArgs a) {
     const int nq = nq_seq - q0 < kQBlock ? nq_seq - q0 : kQBlock;   // queries in the block
     const int pos0 = L - nq_seq + q0;                             // position of the block's first query
     const int last = pos0 + nq - 1;                               // position of its last query
-    const int n_tiles = last < 0 ? 0 : last / kPage + 1;
+    const int unit_tiles = last < 0 ? 0 : last / kPage + 1;   // tiles the block's last query sees
+    const int t_lo = e_t0 < 0 ? 0 : (e_t0 > unit_tiles ? unit_tiles : e_t0);
+    const int t_hi = e_t1 < t_lo ? t_lo : (e_t1 > unit_tiles ? unit_tiles : e_t1);
     const int G = a.group;
+    if (slot >= a.n_partials) return;       // not a slot of this plan: write nothing
 
     // Q of this wave's heads: row block r holds head hg = wave + 4 r
     bf16x8 qop[HPW][4];
@@ -301,15 +307,15 @@ prefill_kernel(PrefillArgs a) {
     // barrier; a group past the unit's last tile only waits.
     {
         TileRegs<FP8> rg;
-        if (gg < n_tiles) rg.load(a, bt[gg], h, rows_in(gg), tid_g);
-        const int rounds = (n_tiles + NG - 1) / NG;
+        if (t_lo + gg < t_hi) rg.load(a, bt[t_lo + gg], h, rows_in(t_lo + gg), tid_g);
+        const int rounds = (t_hi - t_lo + NG - 1) / NG;
         for (int i = 0; i < rounds; ++i) {
-            const int t = NG * i + gg;
-            const bool have = NG == 1 || t < n_tiles;   // a single group always has its tile
+            const int t = t_lo + NG * i + gg;
+            const bool have = NG == 1 || t < t_hi;      // a single group always has its tile
             __syncthreads();                  // every wave is done with the previous tile
             if (have) rg.store(lds_k, lds_v, tid_g);
             __syncthreads();                  // the tile is in LDS
-            if (t + NG < n_tiles) rg.load(a, bt[t + NG], h, rows_in(t + NG), tid_g);
+            if (t + NG < t_hi) rg.load(a, bt[t + NG], h, rows_in(t + NG), tid_g);
             if (have) compute(t);
         }
     }
@@ -317,7 +323,7 @@ prefill_kernel(PrefillArgs a) {
         // group 1 leaves its state in LDS (over the tile buffers, exactly
         // HPW * 34 values per lane), group 0 merges it by log-sum-exp
         float* st = reinterpret_cast<float*>(lds);
-        const int slot = wave * 64 + lane;
+        const int sl = wave * 64 + lane;   // this lane's column of the state
         __syncthreads();
         if (gg == 1) {
 #pragma unroll
@@ -325,17 +331,17 @@ prefill_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) st[((r * 8 + nb) * 4 + i) * kThreads + slot] = acc[r][nb][i];
-                st[(HPW * 32 + r) * kThreads + slot] = m[r];
-                st[(HPW * 33 + r) * kThreads + slot] = l[r];
+                    for (int i = 0; i < 4; ++i) st[((r * 8 + nb) * 4 + i) * kThreads + sl] = acc[r][nb][i];
+                st[(HPW * 32 + r) * kThreads + sl] = m[r];
+                st[(HPW * 33 + r) * kThreads + sl] = l[r];
             }
         }
         __syncthreads();
         if (gg == 1) return;
 #pragma unroll
         for (int r = 0; r < HPW; ++r) {
-            const float m1 = st[(HPW * 32 + r) * kThreads + slot];
-            const float l1 = st[(HPW * 33 + r) * kThreads + slot];
+            const float m1 = st[(HPW * 32 + r) * kThreads + sl];
+            const float l1 = st[(HPW * 33 + r) * kThreads + sl];
             const float mx = fmaxf(m[r], m1);                       // raw scores, as in the tile loop
             const float mu = (mx == -INFINITY) ? 0.f : mx * a.qk_scale_log2;
             const float f0 = __builtin_amdgcn_exp2f(m[r] * a.qk_scale_log2 - mu);
@@ -346,7 +352,7 @@ prefill_kernel(PrefillArgs a) {
             for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    acc[r][nb][i] = acc[r][nb][i] * f0 + st[((r * 8 + nb) * 4 + i) * kThreads + slot] * f1;
+                    acc[r][nb][i] = acc[r][nb][i] * f0 + st[((r * 8 + nb) * 4 + i) * kThreads + sl] * f1;
         }
     }
 
@@ -361,6 +367,21 @@ prefill_kernel(PrefillArgs a) {
         lt += __shfl_xor(lt, 32);
         if (n >= nq) continue;
         const float inv = lt > 0.f ? a.v_scale / lt : 0.f;
+        const float lse_v = lt > 0.f ? (m[r] * a.qk_scale_log2 + __log2f(lt)) * kLn2 : -INFINITY;
+        if (slot >= 0) {
+            // a share of a cut unit: its normalised fp32 output and log-sum-exp
+            const int64_t prow = (int64_t(slot) * kQBlock + n) * G + hg;
+            float* po = a.o_part + prow * kHeadDim;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                *reinterpret_cast<f32x4*>(po + 32 * g + 8 * i) =
+                    f32x4{acc[r][0][i] * inv, acc[r][1][i] * inv, acc[r][2][i] * inv, acc[r][3][i] * inv};
+                *reinterpret_cast<f32x4*>(po + 32 * g + 8 * i + 4) =
+                    f32x4{acc[r][4][i] * inv, acc[r][5][i] * inv, acc[r][6][i] * inv, acc[r][7][i] * inv};
+            }
+            if (g == 0) a.lse_part[prow] = lse_v;
+            continue;
+        }
         const int64_t row = int64_t(r0 + q0 + n) * a.num_q_heads + h * G + hg;
         char* o = static_cast<char*>(a.out) + row * kHeadDim * 2;
 #pragma unroll
@@ -371,7 +392,7 @@ prefill_kernel(PrefillArgs a) {
                                    pack_bf16x2(acc[r][6][i] * inv, acc[r][7][i] * inv)};
             *reinterpret_cast<u32x4*>(o + (32 * g + 8 * i) * 2) = pk;
         }
-        if (g == 0) a.lse[row] = lt > 0.f ? (m[r] * a.qk_scale_log2 + __log2f(lt)) * kLn2 : -INFINITY;
+        if (g == 0) a.lse[row] = lse_v;
     }
 }
 
@@ -386,6 +407,54 @@ int device_cus() {
         cached[dev] = cus;
     }
     return cached[dev];
+}
+
+// Log-sum-exp merge of the shares of each cut unit: one workgroup per
+// (merge record, query head of the group); thread (row, part) folds dims
+// 8 part .. +8 of query row `row` over the unit's S partial slots.  The
+// share loops are unrolled so that their loads are in flight together (a
+// unit can have tens of shares).
+__global__ void __launch_bounds__(256) prefill_merge_kernel(PrefillArgs a) {
+    const int G = a.group;
+    const int rec_i = static_cast<int>(blockIdx.x) / G;
+    const int hg = static_cast<int>(blockIdx.x) - rec_i * G;
+    const int32_t* rec = a.merge + 8 * static_cast<int64_t>(rec_i);
+    const int b = rec[0], qb = rec[1], h = rec[2], S = rec[3], base = rec[4];
+    if (b < 0 || b >= a.batch || h < 0 || h >= a.num_kv_heads || qb < 0 || S < 1 || base < 0 ||
+        base > a.n_partials - S)
+        return;
+    const int r0 = a.q_start[b];
+    const int q0 = qb * kQBlock;
+    const int nq_seq = a.q_start[b + 1] - r0;
+    const int nq = nq_seq - q0 < kQBlock ? nq_seq - q0 : kQBlock;
+    const int row = threadIdx.x >> 4, part = threadIdx.x & 15;
+    if (row >= nq) return;
+    constexpr float kLog2e = 1.4426950408889634f;
+    const int64_t stride = int64_t(kQBlock) * G;                     // one share's rows
+    const int64_t prow0 = (int64_t(base) * kQBlock + row) * G + hg;  // this row in the first share
+    const float* lp = a.lse_part + prow0;
+    float M = -INFINITY;
+#pragma unroll 8
+    for (int s = 0; s < S; ++s) M = fmaxf(M, lp[s * stride]);
+    f32x4 o0 = f32x4{0.f, 0.f, 0.f, 0.f}, o1 = o0;
+    float wsum = 0.f;
+    if (M != -INFINITY) {
+        const float* op = a.o_part + prow0 * kHeadDim + 8 * part;
+#pragma unroll 4
+        for (int s = 0; s < S; ++s) {
+            const float wt = __builtin_amdgcn_exp2f((lp[s * stride] - M) * kLog2e);
+            const f32x4* po = reinterpret_cast<const f32x4*>(op + s * stride * kHeadDim);
+            o0 += wt * po[0];
+            o1 += wt * po[1];
+            wsum += wt;
+        }
+    }
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    const int64_t orow = int64_t(r0 + q0 + row) * a.num_q_heads + h * G + hg;
+    *reinterpret_cast<u32x4*>(static_cast<char*>(a.out) + (orow * kHeadDim + 8 * part) * 2) =
+        u32x4{pack_bf16x2(o0[0] * inv, o0[1] * inv), pack_bf16x2(o0[2] * inv, o0[3] * inv),
+              pack_bf16x2(o1[0] * inv, o1[1] * inv), pack_bf16x2(o1[2] * inv, o1[3] * inv)};
+    if (part == 0) a.lse[orow] = wsum > 0.f ? M + __logf(wsum) : -INFINITY;
 }
 
 // With fewer than two units per compute unit the grid cannot hide one
@@ -415,9 +484,17 @@ int launch_fp8(const PrefillArgs& a, int n_units, void* stream) {
 
 }  // namespace
 
-int launch_prefill(const PrefillArgs& a, int n_units, bool kv_fp8, void* stream) {
-    if (n_units == 0) return 0;
-    return kv_fp8 ? launch_fp8<true>(a, n_units, stream) : launch_fp8<false>(a, n_units, stream);
+int launch_prefill(const PrefillArgs& a, int n_entries, int n_merge, bool kv_fp8, void* stream) {
+    if (n_entries > 0) {
+        const int e = kv_fp8 ? launch_fp8<true>(a, n_entries, stream) : launch_fp8<false>(a, n_entries, stream);
+        if (e) return e;
+    }
+    if (n_merge > 0) {
+        hipLaunchKernelGGL(prefill_merge_kernel, dim3(n_merge * a.group), dim3(256), 0,
+                           static_cast<hipStream_t>(stream), a);
+        return static_cast<int>(hipGetLastError());
+    }
+    return 0;
 }
 
 }  // namespace hpcd

@@ -30,14 +30,18 @@ def _gpu():
     hd.lib()
 
 
-def run_gpu(pi, dev=None):
+def run_gpu(pi, n_workers=0, min_share_tiles=1):
+    """Small cases cut with no floor on the share length (min_share_tiles =
+    1), so that their few tiles are still spread over several shares."""
     c = pi.cache
-    d = dev or {}
-    q = d.get("q", pi.q.cuda())
-    k = d.get("k", c.k_cache.cuda())
-    v = d.get("v", c.v_cache.cuda())
+    q, k, v = pi.q.cuda(), c.k_cache.cuda(), c.v_cache.cuda()
     bt, sl, qs = c.block_table.cuda(), c.seq_lens.cuda(), pi.q_start.cuda()
-    step = PrefillStep(pi.q_start, c.seq_lens, c.num_kv_heads, c.max_pages_per_seq)
+    step = PrefillStep(pi.q_start, c.seq_lens, c.num_q_heads, c.num_kv_heads, c.max_pages_per_seq, n_workers,
+                       min_share_tiles)
+    if n_workers:
+        assert step.n_merge > 0, "the balanced case must cut at least one unit"
+    if step.workspace is not None:
+        step.workspace.fill_(0xFF)          # NaN partials unless the kernel writes every slot it merges
     out = torch.full_like(q, float("nan"))
     lse = torch.full(q.shape[:2], float("nan"), dtype=torch.float32, device="cuda")
     step(q, qs, k, v, bt, sl, out, lse, sm_scale=c.sm_scale, k_scale=c.k_scale, v_scale=c.v_scale)
@@ -92,6 +96,36 @@ def test_prefill_parity(case):
     compare_rows(pi, run_gpu(pi), run_oracle(pi), case)
 
 
+# balanced plans: long units cut into shares merged by log-sum-exp
+BALANCED = {
+    "prompt 200 on 64 workers, 8q/1kv": ([0], [200], 8, 1, "bf16", 64),
+    "extend after 3000, 16q/2kv, 40 workers": ([3000, 0, 10], [40, 17, 1], 16, 2, "bf16", 40),
+    "extends G=16 (4 heads per wave), 30 workers": ([700, 0], [45, 130], 32, 2, "bf16", 30),
+    "extend G=5, one tile a share": ([300], [20], 5, 1, "bf16", 10000),
+    "fp8 extends 64q/8kv, 512 workers": ([2000, 64, 0], [256, 100, 65], 64, 8, "fp8_e4m3", 512),
+    "decode rows after 5000, 8q/1kv, 30 workers": ([5000, 37, 900], [1, 1, 1], 8, 1, "bf16", 30),
+}
+
+
+@pytest.mark.parametrize("case", sorted(BALANCED))
+def test_balanced_prefill_parity(case):
+    ctx, n, hq, hkv, kv, W = BALANCED[case]
+    announce(f"balanced prefill parity, {case}")
+    pi = make_prefill_inputs(ctx, n, hq, hkv, kv, seed=sum(ctx) + sum(n) + hq + 1, poison=True)
+    compare_rows(pi, run_gpu(pi, W), run_oracle(pi), f"balanced {case}")
+
+
+def test_balanced_and_whole_units_agree():
+    """Cut and uncut plans of the same extend: the shares' merge changes
+    only rounding (partials merged in fp32, one bf16 rounding of out)."""
+    pi = make_prefill_inputs([2500, 100], [64, 33], 16, 2, "bf16", seed=12)
+    announce("balanced vs whole units")
+    a, b = run_gpu(pi), run_gpu(pi, 64)
+    tol = OUT_TOL["bf16"] * max_abs_v(pi.cache)
+    assert float(np.abs(a[0] - b[0]).max()) <= tol
+    assert float(np.abs(a[1] - b[1]).max()) <= LSE_TOL["bf16"]
+
+
 @pytest.mark.parametrize("name", ["prefill-q512", "prefill-q512-8q1kv"])
 def test_prompt_workloads_full(name):
     announce(f"prefill workload {name}, every row")
@@ -99,14 +133,16 @@ def test_prompt_workloads_full(name):
     compare_rows(pi, run_gpu(pi), run_oracle(pi), name)
 
 
-@pytest.mark.parametrize("name", ["extend-8x512", "extend-8x256-fp8"])
-def test_extend_workloads_sampled(name):
-    """Full-size extend batches: 96 sampled rows, each against the decode
-    oracle over that row's visible prefix."""
-    announce(f"prefill workload {name}, sampled rows")
+@pytest.mark.parametrize("name,n_workers", [("extend-8x512", 0), ("extend-8x256-fp8", 0), ("extend-8x256-fp8", 1024),
+                                            ("extend-32k+512-8q1kv", 512), ("extend-128k+7x4k-8q1kv", 512)])
+def test_extend_workloads_sampled(name, n_workers):
+    """Full-size extend batches, whole units or balanced (cut units in each):
+    96 sampled rows, each against the decode oracle over that row's visible
+    prefix."""
+    announce(f"prefill workload {name}, n_workers {n_workers}, sampled rows")
     pi = prefill_workload_inputs(name, poison=True)
     c = pi.cache
-    got = run_gpu(pi)
+    got = run_gpu(pi, n_workers, PrefillStep.MIN_SHARE_TILES)
     rng = np.random.default_rng(11)
     qs = pi.q_start.numpy()
     rows = np.sort(rng.choice(pi.total, size=96, replace=False))
@@ -122,14 +158,15 @@ def test_extend_workloads_sampled(name):
                                 np.array([p + 1]), num_q_heads=c.num_q_heads, num_kv_heads=c.num_kv_heads,
                                 kv_format=c.kv_dtype, sm_scale=c.sm_scale, k_scale=c.k_scale, v_scale=c.v_scale)
         ref_out[i], ref_lse[i] = o[0], l[0]
-    compare_rows(pi, got, (ref_out, ref_lse), name, rows=rows)
+    compare_rows(pi, got, (ref_out, ref_lse), f"{name} W={n_workers}", rows=rows)
 
 
-def test_bitwise_deterministic_and_page_permutation():
+@pytest.mark.parametrize("n_workers", [0, 48])
+def test_bitwise_deterministic_and_page_permutation(n_workers):
     pi = make_prefill_inputs([700, 65], [130, 64], 16, 2, "bf16", seed=5)
-    announce("prefill determinism and page permutation")
-    a = run_gpu(pi)
-    b = run_gpu(pi)
+    announce(f"prefill determinism and page permutation, n_workers {n_workers}")
+    a = run_gpu(pi, n_workers)
+    b = run_gpu(pi, n_workers)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
     c = pi.cache
     perm = np.random.default_rng(3).permutation(c.num_pages)
@@ -138,7 +175,7 @@ def test_bitwise_deterministic_and_page_permutation():
     v[torch.from_numpy(perm)] = c.v_cache
     c.k_cache, c.v_cache = k, v
     c.block_table = torch.from_numpy(perm[c.block_table.numpy()].astype(np.int32))
-    p = run_gpu(pi)
+    p = run_gpu(pi, n_workers)
     assert np.array_equal(a[0], p[0]) and np.array_equal(a[1], p[1])
 
 

@@ -336,6 +336,14 @@ PREFILL_WORKLOADS = {
     "extend-8x256-fp8": PrefillWorkload("extend-8x256-fp8", 64, 8, "fp8_e4m3", (256,) * 8, None,
                                         description="8 chunks of 256 after log-uniform [64, 16384] cached "
                                                     "tokens, 64q/8kv, fp8-e4m3 KV"),
+    "extend-32k+512-8q1kv": PrefillWorkload("extend-32k+512-8q1kv", 8, 1, "bf16", (512,), (32768,),
+                                            description="one chunk of 512 new tokens after 32768 cached, 8q/1kv "
+                                                        "(32 units of ~520 tiles each)"),
+    "extend-128k+7x4k-8q1kv": PrefillWorkload("extend-128k+7x4k-8q1kv", 8, 1, "bf16", (512,) * 8,
+                                              (131072,) + (4096,) * 7,
+                                              description="8 chunks of 512, one after 131072 cached tokens and "
+                                                          "seven after 4096, 8q/1kv (the skewed decode batch's "
+                                                          "extend analogue)"),
 }
 
 
