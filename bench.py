@@ -93,6 +93,8 @@ def parse_args():
     ap.add_argument("--prefill", nargs="?", const="all", default=None, metavar="WORKLOAD",
                     help="instead of the bench line: time causal prefill/extend attention on the prefill "
                          "workloads (all, or one by name) and print one JSON line")
+    ap.add_argument("--prefill-workers", type=int, default=None, metavar="W",
+                    help="with --prefill: time only the plan balanced over W workers (0: whole units)")
     ap.add_argument("--prologue", action="store_true",
                     help="instead of the bench line: time the fused prologue (QK-norm, RoPE, paged append) "
                          "alone and before the decode step on workloads 4 and 5, print one JSON line")
@@ -220,7 +222,8 @@ def main() -> int:
         print(json.dumps(tile_math_sweep(dev, W, args.steps, args.warmup)), flush=True)
         return 0
     if args.prefill:
-        print(json.dumps(prefill_bench(dev, cus, args.prefill, args.steps, args.warmup)), flush=True)
+        print(json.dumps(prefill_bench(dev, cus, args.prefill, args.steps, args.warmup, args.prefill_workers)),
+              flush=True)
         return 0
     if args.prologue:
         print(json.dumps(prologue_bench(dev, cus, W, args.steps, args.warmup)), flush=True)
@@ -544,23 +547,25 @@ def make_sub_prefill(pi, b: int):
     return PrefillInputs(cache=sub_cache, q=pi.q[r0:r1], q_start=torch.tensor([0, r1 - r0], dtype=torch.int32))
 
 
-def prefill_bench(dev, cus: int, which: str, steps: int, warmup: int) -> dict:
+def prefill_bench(dev, cus: int, which: str, steps: int, warmup: int, only_workers: int | None = None) -> dict:
     """Causal prefill / extend attention: mean kernel time over back-to-back
     launches (events on the launch stream; the work list is planned and
     uploaded once, outside the timing), algorithmic FLOPs (4 * 128 per query
     head and visible token) against the bf16 MFMA peak.  Each workload runs
     with whole units (n_workers = 0) and with balanced plans over 1, 2 and 4
     workers per CU; the roofline object is that of the balanced plan at 2
-    workers per CU (two workgroups of one group fit a CU)."""
+    workers per CU (two workgroups of one group fit a CU).  only_workers
+    times that one plan alone (for profiler runs)."""
     import torch
 
-    from load_balanced_paged_step_amd.prefill import PrefillStep
+    from load_balanced_paged_step_amd.prefill import PrefillStep, hpc_prefill_units
     from workloads import PREFILL_WORKLOADS, prefill_workload_inputs
 
     clock_warmup(dev, cus)
     names = list(PREFILL_WORKLOADS) if which == "all" else [which]
     rows = []
-    W_default = 2 * cus
+    W_default = 2 * cus if only_workers is None else only_workers
+    sweep = (0, cus, 2 * cus, 4 * cus) if only_workers is None else (only_workers,)
     for name in names:
         pi = prefill_workload_inputs(name)
         c = pi.cache
@@ -571,7 +576,7 @@ def prefill_bench(dev, cus: int, which: str, steps: int, warmup: int) -> dict:
         lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
         flops = pi.flops()
         plans = {}
-        for W in (0, cus, W_default, 4 * cus):
+        for W in sweep:
             t0 = time.perf_counter()
             step = PrefillStep(pi.q_start, c.seq_lens, c.num_q_heads, c.num_kv_heads, c.max_pages_per_seq,
                                n_workers=W, device=dev)
@@ -588,9 +593,10 @@ def prefill_bench(dev, cus: int, which: str, steps: int, warmup: int) -> dict:
         tflops = main["TFLOPs"]
         row = {"workload": name, "heads": f"{c.num_q_heads}q/{c.num_kv_heads}kv", "kv_dtype": c.kv_dtype,
                "queries": pi.total, "kv_lens": _lens_summary(c.seq_lens.numpy()),
-               "units": plans[0]["entries"], "flops": flops, "n_workers": W_default, "us": main["us"],
-               "TFLOPs": tflops, "whole_units_us": plans[0]["us"],
-               "balanced_speedup": round(plans[0]["us"] / main["us"], 3),
+               "units": hpc_prefill_units(pi.q_start, c.num_kv_heads), "flops": flops, "n_workers": W_default,
+               "us": main["us"], "TFLOPs": tflops,
+               "whole_units_us": plans[0]["us"] if 0 in plans else None,
+               "balanced_speedup": round(plans[0]["us"] / main["us"], 3) if 0 in plans else None,
                "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
                             "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)},
                "plans": list(plans.values())}

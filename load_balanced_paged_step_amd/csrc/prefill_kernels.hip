@@ -411,9 +411,12 @@ int device_cus() {
 
 // Log-sum-exp merge of the shares of each cut unit: one workgroup per
 // (merge record, query head of the group); thread (row, part) folds dims
-// 8 part .. +8 of query row `row` over the unit's S partial slots.  The
-// share loops are unrolled so that their loads are in flight together (a
-// unit can have tens of shares).
+// 8 part .. +8 of query row `row` over the unit's S partial slots.  Shares
+// are read in chunks of kMergeChunk whose loads are all issued before any is
+// used (one memory round trip per chunk), and chunks are folded with a
+// running max.
+constexpr int kMergeChunk = 16;
+
 __global__ void __launch_bounds__(256) prefill_merge_kernel(PrefillArgs a) {
     const int G = a.group;
     const int rec_i = static_cast<int>(blockIdx.x) / G;
@@ -433,21 +436,40 @@ __global__ void __launch_bounds__(256) prefill_merge_kernel(PrefillArgs a) {
     const int64_t stride = int64_t(kQBlock) * G;                     // one share's rows
     const int64_t prow0 = (int64_t(base) * kQBlock + row) * G + hg;  // this row in the first share
     const float* lp = a.lse_part + prow0;
-    float M = -INFINITY;
-#pragma unroll 8
-    for (int s = 0; s < S; ++s) M = fmaxf(M, lp[s * stride]);
+    const float* op = a.o_part + prow0 * kHeadDim + 8 * part;
+    float M = -INFINITY, wsum = 0.f;
     f32x4 o0 = f32x4{0.f, 0.f, 0.f, 0.f}, o1 = o0;
-    float wsum = 0.f;
-    if (M != -INFINITY) {
-        const float* op = a.o_part + prow0 * kHeadDim + 8 * part;
-#pragma unroll 4
-        for (int s = 0; s < S; ++s) {
-            const float wt = __builtin_amdgcn_exp2f((lp[s * stride] - M) * kLog2e);
-            const f32x4* po = reinterpret_cast<const f32x4*>(op + s * stride * kHeadDim);
-            o0 += wt * po[0];
-            o1 += wt * po[1];
+    for (int s0 = 0; s0 < S; s0 += kMergeChunk) {
+        float l[kMergeChunk];
+        f32x4 p0[kMergeChunk], p1[kMergeChunk];
+#pragma unroll
+        for (int i = 0; i < kMergeChunk; ++i) {
+            if (s0 + i < S) {
+                const f32x4* po = reinterpret_cast<const f32x4*>(op + (s0 + i) * stride * kHeadDim);
+                l[i] = lp[(s0 + i) * stride];
+                p0[i] = po[0];
+                p1[i] = po[1];
+            } else {
+                l[i] = -INFINITY;
+                p0[i] = p1[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+        float mc = M;
+#pragma unroll
+        for (int i = 0; i < kMergeChunk; ++i) mc = fmaxf(mc, l[i]);
+        if (mc == -INFINITY) continue;                      // no share of this chunk sees a token yet
+        const float alpha = __builtin_amdgcn_exp2f((M - mc) * kLog2e);   // 0 while M = -inf
+        o0 *= alpha;
+        o1 *= alpha;
+        wsum *= alpha;
+#pragma unroll
+        for (int i = 0; i < kMergeChunk; ++i) {
+            const float wt = __builtin_amdgcn_exp2f((l[i] - mc) * kLog2e);
+            o0 += wt * p0[i];
+            o1 += wt * p1[i];
             wsum += wt;
         }
+        M = mc;
     }
     const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
     const int64_t orow = int64_t(r0 + q0 + row) * a.num_q_heads + h * G + hg;
