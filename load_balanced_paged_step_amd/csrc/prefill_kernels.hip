@@ -16,12 +16,13 @@
 //  * Per 64-token tile, K and V (one page of head h) are loaded by all 256
 //    threads with buffer loads whose range ends at the sequence's last token
 //    (rows past it read as zeros: a poisoned tail cannot reach the sums),
-//    written to LDS (fp8 widened to bf16 exactly) with a 16-byte pad per row
-//    so the operand reads of 8 lanes hit distinct banks, and read by all four
-//    waves.  The next tile's loads are in flight while the current tile is
-//    computed.
+//    written to LDS (fp8 widened to bf16 exactly) and read by all four
+//    waves: K row-major with rows padded by 32 bytes, V transposed (each
+//    thread transposes a 4-token x 8-dim block on the way in) in the order
+//    the P V operand reads it.  The next tile's loads are in flight while
+//    the current tile is computed.
 //  * S^T = K Q^T on MFMA 16x16x32 bf16 (16 KV tokens x 16 queries), exp2
-//    domain online softmax per query, P V on MFMA 16x16x16 bf16 as
+//    domain online softmax per query, P V on MFMA 16x16x32 bf16 as
 //    O^T = V^T P^T with P taken straight from the score registers.
 //  * The causal mask is applied on the tiles that reach past the block's
 //    first query position; tokens > p score -inf.
@@ -34,6 +35,7 @@
 #include <stdint.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "internal.h"
 
@@ -78,12 +80,31 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
            (uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(b))) << 16);
 }
 
-// One 64-token tile of K or V in flight: 16 KiB bf16 = 4 x 16 B per thread,
-// 8 KiB fp8 = 2 x 16 B per thread.
+// V^T in LDS: dim d's 64 tokens take 128 bytes, two dims per 256-byte line
+// (line d >> 1, half d & 1).  Within each 32-token chunk cc the tokens are
+// kept in the order the P V operand takes them: for g = 0..3, tokens
+// 4g .. 4g+3 of 16-token block 2cc, then the same of block 2cc + 1, so that
+// lane (n, g) reads its operand for dim 8n + nb as one 16-byte run at byte
+// 64 cc + 16 g of the dim.  The sixteen 16-byte chunks of a line are XOR-
+// swizzled by (line >> 2) & 15: the 16 lanes of one read (n = 0..15, lines
+// 4n + (nb >> 1)) then hit 16 distinct chunk positions, i.e. distinct banks.
+__device__ __forceinline__ int vt_offset(int d, int byte) {   // byte of the dim's 128, 8-aligned
+    const int line = d >> 1;
+    const int q = ((d & 1) << 3) | (byte >> 4);
+    return line * 256 + ((q ^ ((line >> 2) & 15)) << 4) + (byte & 15);
+}
+
+// One 64-token tile of K and V in flight.  K: 16-byte chunks of the
+// row-major tile (16 KiB bf16 = 4 per thread, 8 KiB fp8 = 2 per thread).
+// V: thread (j, m) = (tid >> 4, tid & 15) holds tokens 4j .. 4j+3, dims
+// 8m .. 8m+7 (16 bytes per token in bf16, 8 in fp8), which it transposes into
+// V^T on the way to LDS.
 template <bool FP8>
 struct TileRegs {
-    static constexpr int kLoads = FP8 ? 2 : 4;
-    u32x4 k[kLoads], v[kLoads];
+    static constexpr int kKLoads = FP8 ? 2 : 4;
+    typedef typename std::conditional<FP8, u32x2, u32x4>::type VRow;
+    u32x4 k[kKLoads];
+    VRow v[4];
 
     // rows [0, valid) of page `page`, KV head h; everything else reads as 0
     __device__ __forceinline__ void load(const PrefillArgs& a, int page, int h, int valid, int tid) {
@@ -95,34 +116,58 @@ struct TileRegs {
         const auto rk = make_rsrc(static_cast<const char*>(a.k) + off, bytes);
         const auto rv = make_rsrc(static_cast<const char*>(a.v) + off, bytes);
 #pragma unroll
-        for (int i = 0; i < kLoads; ++i) {
+        for (int i = 0; i < kKLoads; ++i) {
             const int c = tid + kThreads * i;          // 16-byte chunk of the tile, row-major
             k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, c * 16, 0, 0);
-            v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, c * 16, 0, 0);
+        }
+        const int j = tid >> 4, m = tid & 15;
+        constexpr int row = kHeadDim * (FP8 ? 1 : 2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (FP8)
+                v[i] = __builtin_amdgcn_raw_buffer_load_b64(rv, (4 * j + i) * row + 8 * m, 0, 0);
+            else
+                v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, (4 * j + i) * row + 16 * m, 0, 0);
         }
     }
 
     __device__ __forceinline__ void store(char* lds_k, char* lds_v, int tid) const {
 #pragma unroll
-        for (int i = 0; i < kLoads; ++i) {
+        for (int i = 0; i < kKLoads; ++i) {
             const int c = tid + kThreads * i;
             if constexpr (FP8) {
                 const int row = c >> 3, col = (c & 7) * 32;      // 16 codes -> 32 bytes of bf16
                 char* pk = lds_k + row * kLdsRow + col;
-                char* pv = lds_v + row * kLdsRow + col;
                 const u32x2 k0 = fp8x4_to_bf16x4(k[i][0]), k1 = fp8x4_to_bf16x4(k[i][1]);
                 const u32x2 k2 = fp8x4_to_bf16x4(k[i][2]), k3 = fp8x4_to_bf16x4(k[i][3]);
-                const u32x2 v0 = fp8x4_to_bf16x4(v[i][0]), v1 = fp8x4_to_bf16x4(v[i][1]);
-                const u32x2 v2 = fp8x4_to_bf16x4(v[i][2]), v3 = fp8x4_to_bf16x4(v[i][3]);
                 *reinterpret_cast<u32x4*>(pk) = u32x4{k0[0], k0[1], k1[0], k1[1]};
                 *reinterpret_cast<u32x4*>(pk + 16) = u32x4{k2[0], k2[1], k3[0], k3[1]};
-                *reinterpret_cast<u32x4*>(pv) = u32x4{v0[0], v0[1], v1[0], v1[1]};
-                *reinterpret_cast<u32x4*>(pv + 16) = u32x4{v2[0], v2[1], v3[0], v3[1]};
             } else {
                 const int row = c >> 4, col = (c & 15) * 16;
                 *reinterpret_cast<u32x4*>(lds_k + row * kLdsRow + col) = k[i];
-                *reinterpret_cast<u32x4*>(lds_v + row * kLdsRow + col) = v[i];
             }
+        }
+        // V: token rows of 8 dims (bf16 pairs per word) -> for each dim, its 4 tokens
+        u32x4 vb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (FP8) {
+                const u32x2 lo = fp8x4_to_bf16x4(v[i][0]), hi = fp8x4_to_bf16x4(v[i][1]);
+                vb[i] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+            } else {
+                vb[i] = v[i];
+            }
+        }
+        const int j = tid >> 4, m = tid & 15;
+        const int tb = (j >> 3) * 64 + (j & 3) * 16 + ((j >> 2) & 1) * 8;   // byte of token 4j in a dim's 128
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const u32x2 lo = u32x2{__builtin_amdgcn_perm(vb[1][p], vb[0][p], kSelLo),
+                                   __builtin_amdgcn_perm(vb[3][p], vb[2][p], kSelLo)};
+            const u32x2 hi = u32x2{__builtin_amdgcn_perm(vb[1][p], vb[0][p], kSelHi),
+                                   __builtin_amdgcn_perm(vb[3][p], vb[2][p], kSelHi)};
+            *reinterpret_cast<u32x2*>(lds_v + vt_offset(8 * m + 2 * p, tb)) = lo;
+            *reinterpret_cast<u32x2*>(lds_v + vt_offset(8 * m + 2 * p + 1, tb)) = hi;
         }
     }
 };
@@ -277,23 +322,13 @@ prefill_kernel(PrefillArgs a) {
         }
 
         // O^T += V^T P^T on 32-token chunks (MFMA 16x16x32): the V^T operand of
-        // lane (n, g) holds dim 8n + nb of the same 8 tokens as its P slots
+        // lane (n, g) is dim 8n + nb over the same 8 tokens as its P slots,
+        // one 16-byte read of the transposed tile
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
-            u32x4 rows[8];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                rows[i] = *reinterpret_cast<const u32x4*>(lds_v + (32 * cc + 4 * g + i) * kLdsRow + 16 * n);
-                rows[4 + i] = *reinterpret_cast<const u32x4*>(lds_v + (32 * cc + 16 + 4 * g + i) * kLdsRow + 16 * n);
-            }
 #pragma unroll
             for (int nb = 0; nb < 8; ++nb) {
-                const int d = nb >> 1;
-                const uint32_t sel = (nb & 1) ? kSelHi : kSelLo;
-                const u32x4 vt = u32x4{__builtin_amdgcn_perm(rows[1][d], rows[0][d], sel),
-                                       __builtin_amdgcn_perm(rows[3][d], rows[2][d], sel),
-                                       __builtin_amdgcn_perm(rows[5][d], rows[4][d], sel),
-                                       __builtin_amdgcn_perm(rows[7][d], rows[6][d], sel)};
+                const u32x4 vt = *reinterpret_cast<const u32x4*>(lds_v + vt_offset(8 * n + nb, 64 * cc + 16 * g));
 #pragma unroll
                 for (int r = 0; r < HPW; ++r)
                     acc[r][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(vt), pop[r][cc], acc[r][nb],
