@@ -71,7 +71,9 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=4, help="workload number (1-5); 4 = 1x128K+31x4K")
-    ap.add_argument("--n-workers", type=int, default=0, help="persistent workgroups (0: one per CU)")
+    ap.add_argument("--n-workers", type=int, default=0,
+                    help="persistent workgroups (0: the library's worker-count rule over [CUs/2, CUs] for the "
+                         "step; one per CU for the sweeps)")
     ap.add_argument("--plan-in-place", action="store_true",
                     help="--schedule host: the kernels read the plan from the pinned host buffer (no upload)")
     ap.add_argument("--copies", type=int, default=0, help="rotating KV copies (0: enough for >= 1 GiB)")
@@ -235,7 +237,15 @@ def main() -> int:
     kv_bytes_total = inp.k_cache.numel() * inp.k_cache.element_size() * 2
     copies = args.copies or max(1, min(16, math.ceil((1 << 30) / kv_bytes_total)))
     alg_bytes = inp.algorithmic_bytes()
-    log(f"device {props.name}, {cus} CUs; W={W}; KV {kv_bytes_total / 1e6:.1f} MB x {copies} copies; "
+    if args.n_workers:
+        w_rule = "given (--n-workers)"
+    else:
+        # the library's worker-count rule over [CUs / 2, CUs]: tiles plus an
+        # entry price per worker, ties to the larger count
+        W = hd.hpc_decode_choose_workers(inp.seq_lens, inp.num_kv_heads, max(1, cus // 2), cus)
+        w_rule = (f"hpc_decode_choose_workers over [{max(1, cus // 2)}, {cus}], entry cost "
+                  f"{hd.ENTRY_COST_TILES} tile")
+    log(f"device {props.name}, {cus} CUs; W={W} ({w_rule}); KV {kv_bytes_total / 1e6:.1f} MB x {copies} copies; "
         f"algorithmic bytes/step {alg_bytes}")
 
     q = inp.q.to(dev)
@@ -331,7 +341,8 @@ def main() -> int:
         "config": {
             "workload": wl.name, "batch": inp.batch, "kv_lens": _lens_summary(lens_host),
             "num_q_heads": inp.num_q_heads, "num_kv_heads": inp.num_kv_heads, "head_dim": 128,
-            "page_size": 64, "kv_dtype": inp.kv_dtype, "n_workers": W, "kv_copies": copies,
+            "page_size": 64, "kv_dtype": inp.kv_dtype, "n_workers": W, "n_workers_from": w_rule,
+            "kv_copies": copies,
             "algorithmic_bytes": alg_bytes,
             "schedule": args.schedule + (", plan in place" if args.schedule == "host" and args.plan_in_place else ""),
             "parallelism": "single GPU", "tile_math": args.tile_math,

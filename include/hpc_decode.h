@@ -156,6 +156,26 @@ int64_t hpc_decode_plan_static_size(int32_t batch, int32_t num_kv_heads, int32_t
 int hpc_decode_plan_static(const int32_t* seq_lens, int32_t batch, int32_t num_kv_heads,
                            int32_t splits, int32_t* plan, int64_t plan_capacity);
 
+/* Worker count for a step, pure host code.  The balanced partition gives
+ * every worker floor((w+1)T/W) - floor(wT/W) tiles (§Attention Backend:
+ * Dynamic Load-Balanced Scheduling, "vLLM x HPC-Ops: High-Performance
+ * Attention and MoE Backends from Tencent Hunyuan": tiles spread by actual
+ * work over a grid that keeps every compute unit busy), but a worker also
+ * pays for each entry (unit) its range touches: the entry's end and, when
+ * the unit is split, its partial.  This returns the W in [min_workers,
+ * max_workers] whose costliest worker, priced as its tiles plus entry_cost
+ * tiles per entry, is cheapest; ties go to the larger W.  With the lengths
+ * of a batch whose sequence boundaries fall on worker boundaries at some W
+ * just below the compute-unit count, that W wins (one entry per worker).
+ * The pages price tiles only; entry_cost is this library's extension
+ * (about 0.5 measured on MI355X: ~0.6 us per entry end against ~1.25 us
+ * per 32 KiB tile).  Returns W (>= 1), or HPC_ERR_NULL (NULL lengths with
+ * batch > 0), HPC_ERR_INVALID (batch < 0, num_kv_heads < 1, min_workers < 1,
+ * max_workers < min_workers, entry_cost negative or not finite, a negative
+ * length, 2^31 - 1 tiles or more).  An all-empty batch returns max_workers. */
+int32_t hpc_decode_choose_workers(const int32_t* seq_lens, int32_t batch, int32_t num_kv_heads,
+                                  int32_t min_workers, int32_t max_workers, float entry_cost);
+
 /* Split count of the static split-KV baseline for a batch: the smallest
  * power of two S with batch * num_kv_heads * S >= n_cus (one share per
  * compute unit at least), capped at max_splits and at the largest unit's

@@ -26,7 +26,7 @@ from ._lib import (HPC_OK, HPC_ERR_NULL, HPC_ERR_INVALID, HPC_ERR_UNSUPPORTED, H
 
 __all__ = [
     "hpc_decode_plan_size", "hpc_decode_plan", "hpc_decode_plan_static_size", "hpc_decode_plan_static",
-    "hpc_decode_static_splits",
+    "hpc_decode_static_splits", "hpc_decode_choose_workers", "ENTRY_COST_TILES",
     "hpc_decode_plan_words", "hpc_decode_workspace_size",
     "hpc_decode_check", "hpc_decode_attn", "hpc_status_string", "hpc_decode_profile_start",
     "hpc_decode_profile_stop", "hpc_probe_read", "hpc_probe_read_timed", "hpc_probe_copy", "hpc_decode_step",
@@ -151,6 +151,20 @@ def hpc_decode_static_splits(seq_lens, num_kv_heads: int, n_cus: int, max_splits
     lens = _host_i32(seq_lens).reshape(-1)
     return _lib.check(lib().hpc_decode_static_splits(_i32p(lens), lens.shape[0], num_kv_heads, n_cus, max_splits),
                       "hpc_decode_static_splits")
+
+
+#: entry price (in tiles) of the worker-count rule: an entry end costs about
+#: 0.6 us on MI355X against about 1.25 us per 32 KiB tile
+ENTRY_COST_TILES = 0.5
+
+
+def hpc_decode_choose_workers(seq_lens, num_kv_heads: int, min_workers: int, max_workers: int,
+                              entry_cost: float = ENTRY_COST_TILES) -> int:
+    """The worker count in [min_workers, max_workers] whose costliest worker
+    (tiles + entry_cost per entry) is cheapest, ties to the larger count."""
+    lens = _host_i32(seq_lens).reshape(-1)
+    return _lib.check(lib().hpc_decode_choose_workers(_i32p(lens), lens.shape[0], num_kv_heads, min_workers,
+                                                      max_workers, float(entry_cost)), "hpc_decode_choose_workers")
 
 
 def hpc_decode_plan_words(plan) -> int:

@@ -79,6 +79,8 @@ SIGNATURES = {
     "hpc_decode_plan_static_size": (ctypes.c_int64, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]),
     "hpc_decode_plan_static": (ctypes.c_int, [_I32P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _I32P,
                                               ctypes.c_int64]),
+    "hpc_decode_choose_workers": (ctypes.c_int32, [_I32P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                   ctypes.c_int32, ctypes.c_float]),
     "hpc_decode_static_splits": (ctypes.c_int32, [_I32P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                   ctypes.c_int32]),
     "hpc_decode_plan_words": (ctypes.c_int64, [_I32P]),

@@ -214,6 +214,50 @@ extern "C" int32_t hpc_decode_static_splits(const int32_t* seq_lens, int32_t bat
     return static_cast<int32_t>(S);
 }
 
+extern "C" int32_t hpc_decode_choose_workers(const int32_t* seq_lens, int32_t batch, int32_t num_kv_heads,
+                                             int32_t min_workers, int32_t max_workers, float entry_cost) {
+    if (batch > 0 && seq_lens == nullptr) return HPC_ERR_NULL;
+    if (batch < 0 || num_kv_heads < 1 || min_workers < 1 || max_workers < min_workers || !(entry_cost >= 0.f) ||
+        !(entry_cost < 1e30f))
+        return HPC_ERR_INVALID;
+    // [start, end) tile ranges of the units that have tiles, in unit order
+    std::vector<int64_t> s0, s1;
+    int64_t T = 0;
+    for (int32_t b = 0; b < batch; ++b) {
+        if (seq_lens[b] < 0) return HPC_ERR_INVALID;
+        const int64_t n = (static_cast<int64_t>(seq_lens[b]) + kPage - 1) / kPage;
+        for (int32_t h = 0; h < num_kv_heads && n > 0; ++h) {
+            s0.push_back(T);
+            T += n;
+            s1.push_back(T);
+        }
+    }
+    if (T > INT32_MAX - 1) return HPC_ERR_INVALID;
+    if (T == 0) return max_workers;
+    const std::size_t U = s0.size();
+    int32_t best = max_workers;
+    double best_cost = 0.0;
+    for (int32_t W = max_workers; W >= min_workers; --W) {
+        // the costliest worker: its tiles plus entry_cost per unit it touches
+        double worst = 0.0;
+        std::size_t u = 0;
+        for (int64_t w = 0; w < W; ++w) {
+            const int64_t a = w * T / W, e = (w + 1) * T / W;
+            if (a == e) continue;
+            while (u < U && s1[u] <= a) ++u;
+            int64_t entries = 0;
+            for (std::size_t v = u; v < U && s0[v] < e; ++v) ++entries;
+            const double c = static_cast<double>(e - a) + entry_cost * static_cast<double>(entries);
+            if (c > worst) worst = c;
+        }
+        if (W == max_workers || worst < best_cost - 1e-9) {
+            best = W;
+            best_cost = worst;
+        }
+    }
+    return best;
+}
+
 extern "C" int64_t hpc_decode_plan_words(const int32_t* plan) {
     if (plan == nullptr) return HPC_ERR_NULL;
     if (plan[0] != HPC_PLAN_VERSION || plan[8] != HPC_DECODE_PAGE) return HPC_ERR_PLAN_MISMATCH;

@@ -1,0 +1,95 @@
+"""The worker-count rule (hpc_decode_choose_workers), host only.
+
+Its definition, written out here: worker w of W holds global tiles
+[floor(w T / W), floor((w + 1) T / W)) of the unit-major tile list; it costs
+its tile count plus entry_cost for every unit with tiles that its range
+touches; the rule returns the W in [lo, hi] whose costliest worker is
+cheapest, ties to the larger W.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+import load_balanced_paged_step_amd as hd
+from workloads import workload_inputs
+
+
+def _brute(lens, H, lo, hi, ce):
+    units = []
+    start = 0
+    for L in lens:
+        n = -(-int(L) // 64)
+        for _ in range(H):
+            if n:
+                units.append((start, start + n))
+                start += n
+    T = start
+    if T == 0:
+        return hi
+    best, best_cost = None, None
+    for W in range(hi, lo - 1, -1):
+        worst = 0.0
+        for w in range(W):
+            a, b = w * T // W, (w + 1) * T // W
+            if a == b:
+                continue
+            worst = max(worst, (b - a) + ce * sum(1 for s, e in units if s < b and e > a))
+        if best is None or worst < best_cost - 1e-9:
+            best, best_cost = W, worst
+    return best
+
+
+def test_skewed_batch_takes_the_aligned_worker_count():
+    """1 x 128K + 31 x 4K, one KV head: T = 4032 = 16 x 252, so at W = 252
+    every sequence boundary is a worker boundary and each worker holds one
+    entry (16 tiles + 0.5), against 16 tiles and two entries for some of the
+    256 workers."""
+    lens = workload_inputs(4).seq_lens.numpy()
+    assert hd.hpc_decode_choose_workers(lens, 1, 128, 256) == 252
+    assert hd.hpc_decode_choose_workers(lens, 1, 253, 256) == 256      # 252 outside the window
+    assert _brute(lens, 1, 240, 256, 0.5) == 252
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3])
+def test_batches_without_a_better_count_keep_every_worker(cfg):
+    wi = workload_inputs(cfg)
+    assert hd.hpc_decode_choose_workers(wi.seq_lens.numpy(), wi.num_kv_heads, 128, 256) == 256
+
+
+def test_without_an_entry_price_the_largest_count_wins():
+    """Tiles alone: the costliest worker holds ceil(T / W) tiles, which never
+    grows with W, and ties go to the larger W."""
+    rng = np.random.default_rng(3)
+    for _ in range(20):
+        lens = rng.integers(0, 5000, size=rng.integers(1, 12))
+        assert hd.hpc_decode_choose_workers(lens, 2, 10, 90, 0.0) == 90
+
+
+@settings(max_examples=60, deadline=None)
+@given(lens=st.lists(st.integers(0, 3000), min_size=1, max_size=9), H=st.integers(1, 3),
+       lo=st.integers(1, 40), span=st.integers(0, 40), ce=st.sampled_from([0.0, 0.25, 0.5, 1.0, 3.0]))
+def test_matches_the_definition(lens, H, lo, span, ce):
+    assert hd.hpc_decode_choose_workers(np.array(lens), H, lo, lo + span, ce) == _brute(lens, H, lo, lo + span, ce)
+
+
+def test_errors():
+    lib = hd.lib()
+    lens = np.array([100, 200], dtype=np.int32)
+    p = lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    assert lib.hpc_decode_choose_workers(p, 2, 1, 1, 8, 0.5) >= 1
+    assert lib.hpc_decode_choose_workers(None, 2, 1, 1, 8, 0.5) == hd.HPC_ERR_NULL
+    assert lib.hpc_decode_choose_workers(None, 0, 1, 1, 8, 0.5) == 8                    # empty batch
+    assert lib.hpc_decode_choose_workers(p, -1, 1, 1, 8, 0.5) == hd.HPC_ERR_INVALID
+    assert lib.hpc_decode_choose_workers(p, 2, 0, 1, 8, 0.5) == hd.HPC_ERR_INVALID
+    assert lib.hpc_decode_choose_workers(p, 2, 1, 0, 8, 0.5) == hd.HPC_ERR_INVALID
+    assert lib.hpc_decode_choose_workers(p, 2, 1, 9, 8, 0.5) == hd.HPC_ERR_INVALID
+    assert lib.hpc_decode_choose_workers(p, 2, 1, 1, 8, -0.1) == hd.HPC_ERR_INVALID
+    assert lib.hpc_decode_choose_workers(p, 2, 1, 1, 8, float("nan")) == hd.HPC_ERR_INVALID
+    assert lib.hpc_decode_choose_workers(p, 2, 1, 1, 8, float("inf")) == hd.HPC_ERR_INVALID
+    bad = np.array([100, -1], dtype=np.int32)
+    assert lib.hpc_decode_choose_workers(bad.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), 2, 1, 1, 8,
+                                         0.5) == hd.HPC_ERR_INVALID
+    assert lib.hpc_decode_choose_workers(np.zeros(3, np.int32).ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), 3,
+                                         2, 4, 8, 0.5) == 8                             # no tiles

@@ -34,7 +34,7 @@ def test_tiny_workload_worker_sweep(W):
     compare(inp, run_hip(inp, W), run_oracle(inp), f"tiny W={W}")
 
 
-@pytest.mark.parametrize("cfg,W", [(2, 256), (2, 1024), (3, 256), (3, 7), (4, 256), (4, 1024), (4, 512)])
+@pytest.mark.parametrize("cfg,W", [(2, 256), (2, 1024), (3, 256), (3, 7), (4, 256), (4, 1024), (4, 512), (4, 252)])
 def test_bf16_workloads(cfg, W):
     announce(f"workload {cfg}, poisoned, W={W}")
     inp = workload_inputs(cfg, poison=True)
