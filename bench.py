@@ -715,7 +715,8 @@ def skew_sweep(dev, W: int, cus: int, steps: int, warmup: int) -> dict:
     (dispatch-stamped events), KV rotated over >= 1 GiB of copies; host plans
     are built and uploaded once, outside the timing; ratio = static /
     balanced (device-scheduled), and static / balanced host plan (the same
-    host-planned kernel as the static plans)."""
+    host-planned kernel as the static plans).  The device-scheduled step is
+    also timed at the worker-count rule's W where that differs from W."""
     import torch
 
     import load_balanced_paged_step_amd as hd
@@ -751,6 +752,17 @@ def skew_sweep(dev, W: int, cus: int, steps: int, warmup: int) -> dict:
                                      workspace=ws, **scales) for c in range(copies)]
         balanced = kernel_us(lambda i: launchers[i % copies]())
         lens_np = inp.seq_lens.numpy()
+        # the device-scheduled step at the worker-count rule's W (when it differs)
+        w_rule = hd.hpc_decode_choose_workers(lens_np, 1, max(1, cus // 2), cus)
+        if w_rule == W:
+            balanced_rule = balanced
+        else:
+            ws_r = torch.zeros(hd.hpc_decode_step_workspace_size(inp.batch, 8, 1, w_rule), dtype=torch.uint8,
+                               device=dev)
+            launchers_r = [hd.StepLauncher(q, ks[c], vs[c], bt, sl, out, lse, num_kv_heads=1, n_workers=w_rule,
+                                           workspace=ws_r, **scales) for c in range(copies)]
+            balanced_rule = kernel_us(lambda i: launchers_r[i % copies]())
+            del launchers_r
 
         def planned_us(plan) -> float:
             """kernel time of a prebuilt host plan (uploaded once) through hpc_decode_attn"""
@@ -774,11 +786,14 @@ def skew_sweep(dev, W: int, cus: int, steps: int, warmup: int) -> dict:
                "best_splits": best_S, "ratio_best": round(static[best_S] / balanced, 3),
                # the balanced plan through the same host-planned kernel the static plans run through
                "ratio_rule_host_plan": round(static[rule_S] / balanced_host, 3),
-               "ratio_best_host_plan": round(static[best_S] / balanced_host, 3)}
+               "ratio_best_host_plan": round(static[best_S] / balanced_host, 3),
+               "rule_workers": w_rule, "balanced_rule_workers_us": round(balanced_rule, 2),
+               "ratio_best_rule_workers": round(static[best_S] / balanced_rule, 3)}
         log(f"skew sweep {name}: balanced {balanced:.1f} us (host-planned {balanced_host:.1f}); "
             f"static S={rule_S} (rule) "
             f"{static[rule_S]:.1f} us = {row['ratio_rule']}x; best static S={best_S} {static[best_S]:.1f} us "
-            f"= {row['ratio_best']}x; host-planned balanced vs best static {row['ratio_best_host_plan']}x")
+            f"= {row['ratio_best']}x; host-planned balanced vs best static {row['ratio_best_host_plan']}x; "
+            f"device-scheduled at the rule's W={w_rule} {balanced_rule:.1f} us = {row['ratio_best_rule_workers']}x")
         rows.append(row)
         del ks, vs, launchers
         torch.cuda.empty_cache()

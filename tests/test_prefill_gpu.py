@@ -104,6 +104,8 @@ BALANCED = {
     "extend G=5, one tile a share": ([300], [20], 5, 1, "bf16", 10000),
     "fp8 extends 64q/8kv, 512 workers": ([2000, 64, 0], [256, 100, 65], 64, 8, "fp8_e4m3", 512),
     "decode rows after 5000, 8q/1kv, 30 workers": ([5000, 37, 900], [1, 1, 1], 8, 1, "bf16", 30),
+    "empty chunks and an empty sequence, G = 2 (one head per wave)": ([900, 5, 0, 40], [20, 0, 0, 33], 8, 4,
+                                                                     "bf16", 100),
     # 33 one-tile shares: three merge chunks, the last holding only tile 32,
     # which rows 0..7 (positions 2040..2047) do not see
     "33 one-tile shares, a chunk with no visible token": ([2040], [16], 8, 1, "bf16", 10000),
