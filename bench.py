@@ -72,8 +72,8 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=4, help="workload number (1-5); 4 = 1x128K+31x4K")
     ap.add_argument("--n-workers", type=int, default=0,
-                    help="persistent workgroups (0: the library's worker-count rule over [CUs/2, CUs] for the "
-                         "step; one per CU for the sweeps)")
+                    help="persistent workgroups (0: the library's worker-count rule, hpc_decode_pick_workers, for "
+                         "the step; one per CU for the sweeps)")
     ap.add_argument("--plan-in-place", action="store_true",
                     help="--schedule host: the kernels read the plan from the pinned host buffer (no upload)")
     ap.add_argument("--copies", type=int, default=0, help="rotating KV copies (0: enough for >= 1 GiB)")
@@ -240,11 +240,12 @@ def main() -> int:
     if args.n_workers:
         w_rule = "given (--n-workers)"
     else:
-        # the library's worker-count rule over [CUs / 2, CUs]: tiles plus an
-        # entry price per worker, ties to the larger count
-        W = hd.hpc_decode_choose_workers(inp.seq_lens, inp.num_kv_heads, max(1, cus // 2), cus)
-        w_rule = (f"hpc_decode_choose_workers over [{max(1, cus // 2)}, {cus}], entry cost "
-                  f"{hd.ENTRY_COST_TILES} tile")
+        # the library's worker-count rule: the count over [CUs / 2, CUs] whose
+        # costliest worker (tiles plus an entry price) is cheapest, or two per
+        # CU for an fp8 cache with dense entries
+        W = hd.hpc_decode_pick_workers(inp.seq_lens, inp.num_kv_heads, inp.kv_dtype, cus)
+        w_rule = (f"hpc_decode_pick_workers ({cus} CUs; hpc_decode_choose_workers over [{cus // 2}, {cus}], "
+                  f"entry cost {hd.ENTRY_COST_TILES} tile, or {2 * cus} for fp8 with >= 1.5 entries per worker)")
     log(f"device {props.name}, {cus} CUs; W={W} ({w_rule}); KV {kv_bytes_total / 1e6:.1f} MB x {copies} copies; "
         f"algorithmic bytes/step {alg_bytes}")
 

@@ -176,6 +176,26 @@ int hpc_decode_plan_static(const int32_t* seq_lens, int32_t batch, int32_t num_k
 int32_t hpc_decode_choose_workers(const int32_t* seq_lens, int32_t batch, int32_t num_kv_heads,
                                   int32_t min_workers, int32_t max_workers, float entry_cost);
 
+/* The entry price of the worker-count rules, in tiles (about 0.6 us per
+ * entry end against about 1.25 us per 32 KiB tile, measured on MI355X). */
+#define HPC_DECODE_ENTRY_COST 0.5f
+
+/* Worker count for a device-scheduled step on a GPU with n_cus compute
+ * units (>= 2), pure host code.  W1 = hpc_decode_choose_workers over
+ * [n_cus / 2, n_cus] with HPC_DECODE_ENTRY_COST.  On an fp8 cache whose
+ * W1-worker partition has 1.5 entries per worker or more, it returns
+ * 2 n_cus instead: two co-resident workgroups per compute unit then hide
+ * entry ends and fp8's narrower loads better than one (measured on MI355X:
+ * 32 sequences of 64q/8kv fp8, lengths log-uniform in [128, 65536], 154.7 ->
+ * 145.5 us; on bf16 caches and on fp8 batches with about one entry per
+ * worker, one workgroup per CU was as fast or faster).  The count is a
+ * multiple of n_cus in that case: with W between n_cus and 2 n_cus some
+ * compute units carry two workers and others one.  Errors as
+ * hpc_decode_choose_workers, plus HPC_ERR_INVALID for n_cus < 2 or above
+ * 2^20 and HPC_ERR_UNSUPPORTED for an unknown kv_dtype. */
+int32_t hpc_decode_pick_workers(const int32_t* seq_lens, int32_t batch, int32_t num_kv_heads, int32_t kv_dtype,
+                                int32_t n_cus);
+
 /* Split count of the static split-KV baseline for a batch: the smallest
  * power of two S with batch * num_kv_heads * S >= n_cus (one share per
  * compute unit at least), capped at max_splits and at the largest unit's

@@ -26,7 +26,7 @@ from ._lib import (HPC_OK, HPC_ERR_NULL, HPC_ERR_INVALID, HPC_ERR_UNSUPPORTED, H
 
 __all__ = [
     "hpc_decode_plan_size", "hpc_decode_plan", "hpc_decode_plan_static_size", "hpc_decode_plan_static",
-    "hpc_decode_static_splits", "hpc_decode_choose_workers", "ENTRY_COST_TILES",
+    "hpc_decode_static_splits", "hpc_decode_choose_workers", "hpc_decode_pick_workers", "ENTRY_COST_TILES",
     "hpc_decode_plan_words", "hpc_decode_workspace_size",
     "hpc_decode_check", "hpc_decode_attn", "hpc_status_string", "hpc_decode_profile_start",
     "hpc_decode_profile_stop", "hpc_probe_read", "hpc_probe_read_timed", "hpc_probe_copy", "hpc_decode_step",
@@ -153,8 +153,8 @@ def hpc_decode_static_splits(seq_lens, num_kv_heads: int, n_cus: int, max_splits
                       "hpc_decode_static_splits")
 
 
-#: entry price (in tiles) of the worker-count rule: an entry end costs about
-#: 0.6 us on MI355X against about 1.25 us per 32 KiB tile
+#: entry price (in tiles) of the worker-count rule (HPC_DECODE_ENTRY_COST): an
+#: entry end costs about 0.6 us on MI355X against about 1.25 us per 32 KiB tile
 ENTRY_COST_TILES = 0.5
 
 
@@ -165,6 +165,21 @@ def hpc_decode_choose_workers(seq_lens, num_kv_heads: int, min_workers: int, max
     lens = _host_i32(seq_lens).reshape(-1)
     return _lib.check(lib().hpc_decode_choose_workers(_i32p(lens), lens.shape[0], num_kv_heads, min_workers,
                                                       max_workers, float(entry_cost)), "hpc_decode_choose_workers")
+
+
+def hpc_decode_pick_workers(seq_lens, num_kv_heads: int, kv_dtype, n_cus: int) -> int:
+    """The worker count for a device-scheduled step on n_cus compute units:
+    the worker-count rule over [n_cus / 2, n_cus], or 2 n_cus for an fp8
+    cache whose partition then holds 1.5 entries per worker or more."""
+    lens = _host_i32(seq_lens).reshape(-1)
+    if isinstance(kv_dtype, str):
+        code = {"bf16": HPC_KV_BF16, "fp8_e4m3": HPC_KV_FP8_E4M3}[kv_dtype]
+    elif isinstance(kv_dtype, torch.dtype):
+        code = kv_dtype_code(kv_dtype)
+    else:
+        code = int(kv_dtype)
+    return _lib.check(lib().hpc_decode_pick_workers(_i32p(lens), lens.shape[0], num_kv_heads, code, n_cus),
+                      "hpc_decode_pick_workers")
 
 
 def hpc_decode_plan_words(plan) -> int:

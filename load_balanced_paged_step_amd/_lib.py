@@ -81,6 +81,8 @@ SIGNATURES = {
                                               ctypes.c_int64]),
     "hpc_decode_choose_workers": (ctypes.c_int32, [_I32P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                    ctypes.c_int32, ctypes.c_float]),
+    "hpc_decode_pick_workers": (ctypes.c_int32, [_I32P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                 ctypes.c_int32]),
     "hpc_decode_static_splits": (ctypes.c_int32, [_I32P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                   ctypes.c_int32]),
     "hpc_decode_plan_words": (ctypes.c_int64, [_I32P]),

@@ -214,17 +214,15 @@ extern "C" int32_t hpc_decode_static_splits(const int32_t* seq_lens, int32_t bat
     return static_cast<int32_t>(S);
 }
 
-extern "C" int32_t hpc_decode_choose_workers(const int32_t* seq_lens, int32_t batch, int32_t num_kv_heads,
-                                             int32_t min_workers, int32_t max_workers, float entry_cost) {
-    if (batch > 0 && seq_lens == nullptr) return HPC_ERR_NULL;
-    if (batch < 0 || num_kv_heads < 1 || min_workers < 1 || max_workers < min_workers || !(entry_cost >= 0.f) ||
-        !(entry_cost < 1e30f))
-        return HPC_ERR_INVALID;
-    // [start, end) tile ranges of the units that have tiles, in unit order
-    std::vector<int64_t> s0, s1;
-    int64_t T = 0;
+namespace {
+
+// [start, end) tile ranges of the units that have tiles, in unit order, and
+// the total T; false for a negative length or 2^31 - 1 tiles or more
+bool unit_ranges(const int32_t* seq_lens, int32_t batch, int32_t num_kv_heads, std::vector<int64_t>& s0,
+                 std::vector<int64_t>& s1, int64_t& T) {
+    T = 0;
     for (int32_t b = 0; b < batch; ++b) {
-        if (seq_lens[b] < 0) return HPC_ERR_INVALID;
+        if (seq_lens[b] < 0) return false;
         const int64_t n = (static_cast<int64_t>(seq_lens[b]) + kPage - 1) / kPage;
         for (int32_t h = 0; h < num_kv_heads && n > 0; ++h) {
             s0.push_back(T);
@@ -232,30 +230,73 @@ extern "C" int32_t hpc_decode_choose_workers(const int32_t* seq_lens, int32_t ba
             s1.push_back(T);
         }
     }
-    if (T > INT32_MAX - 1) return HPC_ERR_INVALID;
-    if (T == 0) return max_workers;
+    return T <= INT32_MAX - 1;
+}
+
+// over the W workers of the balanced partition: the costliest worker (its
+// tiles plus entry_cost per unit its range touches) and the entry count
+void worker_costs(const std::vector<int64_t>& s0, const std::vector<int64_t>& s1, int64_t T, int64_t W,
+                  double entry_cost, double& worst, int64_t& entries_total) {
+    worst = 0.0;
+    entries_total = 0;
     const std::size_t U = s0.size();
+    std::size_t u = 0;
+    for (int64_t w = 0; w < W; ++w) {
+        const int64_t a = w * T / W, e = (w + 1) * T / W;
+        if (a == e) continue;
+        while (u < U && s1[u] <= a) ++u;
+        int64_t entries = 0;
+        for (std::size_t v = u; v < U && s0[v] < e; ++v) ++entries;
+        entries_total += entries;
+        const double c = static_cast<double>(e - a) + entry_cost * static_cast<double>(entries);
+        if (c > worst) worst = c;
+    }
+}
+
+}  // namespace
+
+extern "C" int32_t hpc_decode_choose_workers(const int32_t* seq_lens, int32_t batch, int32_t num_kv_heads,
+                                             int32_t min_workers, int32_t max_workers, float entry_cost) {
+    if (batch > 0 && seq_lens == nullptr) return HPC_ERR_NULL;
+    if (batch < 0 || num_kv_heads < 1 || min_workers < 1 || max_workers < min_workers || !(entry_cost >= 0.f) ||
+        !(entry_cost < 1e30f))
+        return HPC_ERR_INVALID;
+    std::vector<int64_t> s0, s1;
+    int64_t T = 0;
+    if (!unit_ranges(seq_lens, batch, num_kv_heads, s0, s1, T)) return HPC_ERR_INVALID;
+    if (T == 0) return max_workers;
     int32_t best = max_workers;
     double best_cost = 0.0;
     for (int32_t W = max_workers; W >= min_workers; --W) {
-        // the costliest worker: its tiles plus entry_cost per unit it touches
-        double worst = 0.0;
-        std::size_t u = 0;
-        for (int64_t w = 0; w < W; ++w) {
-            const int64_t a = w * T / W, e = (w + 1) * T / W;
-            if (a == e) continue;
-            while (u < U && s1[u] <= a) ++u;
-            int64_t entries = 0;
-            for (std::size_t v = u; v < U && s0[v] < e; ++v) ++entries;
-            const double c = static_cast<double>(e - a) + entry_cost * static_cast<double>(entries);
-            if (c > worst) worst = c;
-        }
+        double worst;
+        int64_t entries;
+        worker_costs(s0, s1, T, W, entry_cost, worst, entries);
         if (W == max_workers || worst < best_cost - 1e-9) {
             best = W;
             best_cost = worst;
         }
     }
     return best;
+}
+
+extern "C" int32_t hpc_decode_pick_workers(const int32_t* seq_lens, int32_t batch, int32_t num_kv_heads,
+                                           int32_t kv_dtype, int32_t n_cus) {
+    if (batch > 0 && seq_lens == nullptr) return HPC_ERR_NULL;
+    if (n_cus < 2 || n_cus > (1 << 20)) return HPC_ERR_INVALID;
+    if (kv_dtype != HPC_KV_BF16 && kv_dtype != HPC_KV_FP8_E4M3) return HPC_ERR_UNSUPPORTED;
+    const int32_t w1 = hpc_decode_choose_workers(seq_lens, batch, num_kv_heads, n_cus / 2, n_cus,
+                                                 HPC_DECODE_ENTRY_COST);
+    if (w1 < 0 || kv_dtype != HPC_KV_FP8_E4M3) return w1;
+    std::vector<int64_t> s0, s1;
+    int64_t T = 0;
+    unit_ranges(seq_lens, batch, num_kv_heads, s0, s1, T);   // valid: checked above
+    if (T == 0) return w1;
+    double worst;
+    int64_t entries;
+    worker_costs(s0, s1, T, w1, HPC_DECODE_ENTRY_COST, worst, entries);
+    // dense entries (1.5 or more per worker) on an fp8 cache: two workers
+    // per compute unit
+    return 2 * entries >= 3 * static_cast<int64_t>(w1) ? 2 * n_cus : w1;
 }
 
 extern "C" int64_t hpc_decode_plan_words(const int32_t* plan) {

@@ -93,3 +93,37 @@ def test_errors():
                                          0.5) == hd.HPC_ERR_INVALID
     assert lib.hpc_decode_choose_workers(np.zeros(3, np.int32).ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), 3,
                                          2, 4, 8, 0.5) == 8                             # no tiles
+
+
+@pytest.mark.parametrize("cfg,expected", [(1, 256), (2, 256), (3, 256), (4, 252), (5, 512)])
+def test_pick_workers_on_the_decode_workloads(cfg, expected):
+    """One worker per CU at the rule's count, except the fp8 batch (64q/8kv,
+    2 entries per worker at W = 255): two per CU."""
+    wi = workload_inputs(cfg)
+    assert hd.hpc_decode_pick_workers(wi.seq_lens.numpy(), wi.num_kv_heads, wi.kv_dtype, 256) == expected
+
+
+def test_pick_workers_rule():
+    lens5 = workload_inputs(5).seq_lens.numpy()
+    # the same lengths on a bf16 cache: one per CU at the rule's count
+    assert hd.hpc_decode_pick_workers(lens5, 8, "bf16", 256) == hd.hpc_decode_choose_workers(lens5, 8, 128, 256)
+    # fp8 with one entry per worker (16 x 32K, 8 KV heads: 128 units of 512 tiles, half a unit per worker)
+    assert hd.hpc_decode_pick_workers(np.full(16, 32768), 8, "fp8_e4m3", 256) == 256
+    # fp8 with exactly two whole units per worker (64 x 4K, 8 KV heads) goes to two per CU
+    assert hd.hpc_decode_pick_workers(np.full(64, 4096), 8, "fp8_e4m3", 256) == 512
+    # the threshold is 1.5 entries per worker: 3 units over 2 workers -> 2 entries each when split in the middle
+    assert hd.hpc_decode_pick_workers(np.full(3, 64 * 4), 1, "fp8_e4m3", 2) == 4
+    assert hd.hpc_decode_pick_workers(np.full(2, 64 * 4), 1, "fp8_e4m3", 2) == 2
+    assert hd.hpc_decode_pick_workers(np.zeros(4, np.int32), 1, "fp8_e4m3", 64) == 64      # no tiles
+
+
+def test_pick_workers_errors():
+    lib = hd.lib()
+    lens = np.array([100, 200], dtype=np.int32)
+    p = lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    assert lib.hpc_decode_pick_workers(p, 2, 1, hd.HPC_KV_BF16, 256) >= 1
+    assert lib.hpc_decode_pick_workers(None, 2, 1, hd.HPC_KV_BF16, 256) == hd.HPC_ERR_NULL
+    assert lib.hpc_decode_pick_workers(p, 2, 1, hd.HPC_KV_BF16, 1) == hd.HPC_ERR_INVALID
+    assert lib.hpc_decode_pick_workers(p, 2, 1, 7, 256) == hd.HPC_ERR_UNSUPPORTED
+    assert lib.hpc_decode_pick_workers(p, -1, 1, hd.HPC_KV_BF16, 256) == hd.HPC_ERR_INVALID
+    assert lib.hpc_decode_pick_workers(p, 2, 0, hd.HPC_KV_FP8_E4M3, 256) == hd.HPC_ERR_INVALID

@@ -41,7 +41,7 @@ def test_bf16_workloads(cfg, W):
     compare(inp, run_hip(inp, W), run_oracle(inp), f"workload {cfg} W={W}")
 
 
-@pytest.mark.parametrize("W", [256, 1024])
+@pytest.mark.parametrize("W", [256, 512, 1024])
 def test_fp8_full_head_workload(W):
     announce(f"fp8 workload 5, W={W}")
     inp = workload_inputs(5, poison=True)

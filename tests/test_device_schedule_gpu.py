@@ -113,7 +113,7 @@ def run_step(inp, W, dev=None):
     return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
 
-@pytest.mark.parametrize("cfg,W", [(1, 3), (1, 256), (2, 256), (3, 256), (4, 256), (4, 1024), (5, 256), (4, 252), (5, 255)])
+@pytest.mark.parametrize("cfg,W", [(1, 3), (1, 256), (2, 256), (3, 256), (4, 256), (4, 1024), (5, 256), (4, 252), (5, 255), (5, 512)])
 def test_step_equals_host_planned(cfg, W):
     inp = workload_inputs(cfg, poison=True)
     dev = to_device(inp)
