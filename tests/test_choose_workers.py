@@ -13,7 +13,7 @@ import pytest
 from hypothesis import given, settings, strategies as st
 
 import load_balanced_paged_step_amd as hd
-from workloads import workload_inputs
+from workloads import WORKLOADS, workload_inputs, workload_lengths
 
 
 def _brute(lens, H, lo, hi, ce):
@@ -46,7 +46,7 @@ def test_skewed_batch_takes_the_aligned_worker_count():
     every sequence boundary is a worker boundary and each worker holds one
     entry (16 tiles + 0.5), against 16 tiles and two entries for some of the
     256 workers."""
-    lens = workload_inputs(4).seq_lens.numpy()
+    lens = workload_lengths(4)
     assert hd.hpc_decode_choose_workers(lens, 1, 128, 256) == 252
     assert hd.hpc_decode_choose_workers(lens, 1, 253, 256) == 256      # 252 outside the window
     assert _brute(lens, 1, 240, 256, 0.5) == 252
@@ -54,8 +54,7 @@ def test_skewed_batch_takes_the_aligned_worker_count():
 
 @pytest.mark.parametrize("cfg", [1, 2, 3])
 def test_batches_without_a_better_count_keep_every_worker(cfg):
-    wi = workload_inputs(cfg)
-    assert hd.hpc_decode_choose_workers(wi.seq_lens.numpy(), wi.num_kv_heads, 128, 256) == 256
+    assert hd.hpc_decode_choose_workers(workload_lengths(cfg), WORKLOADS[cfg].num_kv_heads, 128, 256) == 256
 
 
 def test_without_an_entry_price_the_largest_count_wins():
@@ -99,12 +98,12 @@ def test_errors():
 def test_pick_workers_on_the_decode_workloads(cfg, expected):
     """One worker per CU at the rule's count, except the fp8 batch (64q/8kv,
     2 entries per worker at W = 255): two per CU."""
-    wi = workload_inputs(cfg)
-    assert hd.hpc_decode_pick_workers(wi.seq_lens.numpy(), wi.num_kv_heads, wi.kv_dtype, 256) == expected
+    w = WORKLOADS[cfg]
+    assert hd.hpc_decode_pick_workers(workload_lengths(cfg), w.num_kv_heads, w.kv_dtype, 256) == expected
 
 
 def test_pick_workers_rule():
-    lens5 = workload_inputs(5).seq_lens.numpy()
+    lens5 = workload_lengths(5)
     # the same lengths on a bf16 cache: one per CU at the rule's count
     assert hd.hpc_decode_pick_workers(lens5, 8, "bf16", 256) == hd.hpc_decode_choose_workers(lens5, 8, 128, 256)
     # fp8 with one entry per worker (16 x 32K, 8 KV heads: 128 units of 512 tiles, half a unit per worker)
@@ -127,3 +126,8 @@ def test_pick_workers_errors():
     assert lib.hpc_decode_pick_workers(p, 2, 1, 7, 256) == hd.HPC_ERR_UNSUPPORTED
     assert lib.hpc_decode_pick_workers(p, -1, 1, hd.HPC_KV_BF16, 256) == hd.HPC_ERR_INVALID
     assert lib.hpc_decode_pick_workers(p, 2, 0, hd.HPC_KV_FP8_E4M3, 256) == hd.HPC_ERR_INVALID
+
+
+@pytest.mark.parametrize("cfg", [1, 4, 5])
+def test_workload_lengths_match_the_inputs(cfg):
+    assert np.array_equal(workload_lengths(cfg), workload_inputs(cfg).seq_lens.numpy())

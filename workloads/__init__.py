@@ -214,6 +214,16 @@ def _poison(cache: torch.Tensor, bt: np.ndarray, lens: np.ndarray, poison_page: 
             raw[last, :, L % PAGE:, :].fill_(int(nan))
 
 
+def workload_lengths(cfg: int, seed: int | None = None) -> np.ndarray:
+    """The sequence lengths of a named workload alone (the first draw of its
+    generator, so they equal workload_inputs(cfg, seed).seq_lens)."""
+    w = WORKLOADS[cfg]
+    seed = cfg if seed is None else seed
+    if w.seq_lens is None:
+        return draw_loguniform_lengths(np.random.default_rng(seed), w.batch, *w.loguniform)
+    return np.asarray(w.seq_lens, dtype=np.int64)
+
+
 def workload_inputs(cfg: int, seed: int | None = None, poison: bool = False) -> DecodeInputs:
     """Inputs for one of the five named workloads (seed defaults to the workload number)."""
     w = WORKLOADS[cfg]
