@@ -97,6 +97,9 @@ def parse_args():
                          "workloads (all, or one by name) and print one JSON line")
     ap.add_argument("--prefill-workers", type=int, default=None, metavar="W",
                     help="with --prefill: time only the plan balanced over W workers (0: whole units)")
+    ap.add_argument("--workers-sweep", action="store_true",
+                    help="instead of the bench line: time the device-scheduled step at one and two workers per CU "
+                         "and at hpc_decode_pick_workers' choice on batches of both KV dtypes, print one JSON line")
     ap.add_argument("--prologue", action="store_true",
                     help="instead of the bench line: time the fused prologue (QK-norm, RoPE, paged append) "
                          "alone and before the decode step on workloads 4 and 5, print one JSON line")
@@ -220,6 +223,9 @@ def main() -> int:
     if args.fused_merge and args.schedule != "device":
         print("--fused-merge needs the device schedule", file=sys.stderr)
         return 2
+    if args.workers_sweep:
+        print(json.dumps(workers_sweep(dev, cus, args.steps, args.warmup)), flush=True)
+        return 0
     if args.tile_math_sweep:
         print(json.dumps(tile_math_sweep(dev, W, args.steps, args.warmup)), flush=True)
         return 0
@@ -802,6 +808,77 @@ def skew_sweep(dev, W: int, cus: int, steps: int, warmup: int) -> dict:
             "unit": "ratio", "higher_is_better": True, "n_workers": W, "steps": steps, "warmup": warmup,
             "heads": "8 q / 1 kv, head dim 128, bf16 KV, page 64",
             "static_rule": "smallest power of two S with units x S >= CUs, S <= 128 and <= the longest unit's tiles",
+            "rows": rows}
+
+
+WORKER_SWEEP_BATCHES = (
+    # (name, lengths or ("loguniform", seed, batch), Hq, Hkv, kv dtype)
+    ("fp8 64q/8kv 32 x log-uniform [128, 65536] (seed 5)", ("loguniform", 5, 32), 64, 8, "fp8_e4m3"),
+    ("bf16 64q/8kv 32 x log-uniform [128, 65536] (seed 5)", ("loguniform", 5, 32), 64, 8, "bf16"),
+    ("fp8 64q/8kv 16 x 32K", [32768] * 16, 64, 8, "fp8_e4m3"),
+    ("bf16 64q/8kv 16 x 32K", [32768] * 16, 64, 8, "bf16"),
+    ("fp8 64q/8kv 64 x 4K", [4096] * 64, 64, 8, "fp8_e4m3"),
+    ("bf16 8q/1kv 64 x log-uniform [128, 65536] (seed 1)", ("loguniform", 1, 64), 8, 1, "bf16"),
+    ("fp8 8q/1kv 1 x 128K + 31 x 4K", [131072] + [4096] * 31, 8, 1, "fp8_e4m3"),
+    ("bf16 8q/1kv 1 x 128K + 31 x 4K", [131072] + [4096] * 31, 8, 1, "bf16"),
+)
+
+
+def workers_sweep(dev, cus: int, steps: int, warmup: int) -> dict:
+    """The device-scheduled step at one and at two workers per CU and at
+    hpc_decode_pick_workers' choice, on batches that differ in KV dtype and
+    in entries per worker: decode + merge kernel time per step
+    (dispatch-stamped events), KV rotated over >= 1 GiB of copies, two
+    rounds per count."""
+    import numpy as np
+    import torch
+
+    import load_balanced_paged_step_amd as hd
+    from workloads import draw_loguniform_lengths, make_inputs
+
+    clock_warmup(dev, cus)
+    steps = max(steps, 50)
+    rows = []
+    for name, lens, hq, hkv, kv in WORKER_SWEEP_BATCHES:
+        if isinstance(lens, tuple):
+            lens = list(draw_loguniform_lengths(np.random.default_rng(lens[1]), lens[2], 128, 65536))
+        inp = make_inputs(lens, hq, hkv, kv, seed=4)
+        kv_bytes = inp.k_cache.numel() * inp.k_cache.element_size() * 2
+        copies = max(1, min(16, math.ceil((1 << 30) / kv_bytes)))
+        q, bt, sl = inp.q.to(dev), inp.block_table.to(dev), inp.seq_lens.to(dev)
+        ks = [inp.k_cache.to(dev) for _ in range(copies)]
+        vs = [inp.v_cache.to(dev) for _ in range(copies)]
+        out = torch.empty_like(q)
+        lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+        scales = dict(sm_scale=inp.sm_scale, k_scale=inp.k_scale, v_scale=inp.v_scale)
+        picked = hd.hpc_decode_pick_workers(inp.seq_lens, hkv, kv, cus)
+        words = hd.hpc_decode_plan(inp.seq_lens.numpy(), hkv, cus)
+        times = {}
+        for W in sorted({cus, 2 * cus, picked}):
+            ws = torch.zeros(hd.hpc_decode_step_workspace_size(inp.batch, hq, hkv, W), dtype=torch.uint8, device=dev)
+            launchers = [hd.StepLauncher(q, ks[c], vs[c], bt, sl, out, lse, num_kv_heads=hkv, n_workers=W,
+                                         workspace=ws, **scales) for c in range(copies)]
+            rounds = []
+            for _ in range(2):
+                for i in range(max(warmup, 20)):
+                    launchers[i % copies]()
+                torch.cuda.synchronize()
+                hd.hpc_decode_profile_start(steps)
+                for i in range(steps):
+                    launchers[i % copies]()
+                torch.cuda.synchronize()
+                d_ms, c_ms, n = hd.hpc_decode_profile_stop()
+                rounds.append(round((d_ms + c_ms) / max(n, 1) * 1e3, 2))
+            times[W] = rounds
+            del launchers, ws
+        row = {"batch": name, "entries_per_worker_at_cus": round(int(words[5]) / cus, 3), "picked_workers": picked,
+               "kernel_us": {str(W): t for W, t in times.items()}}
+        log(f"workers sweep {name}: " + ", ".join(f"W={W} {t} us" for W, t in times.items()) + f"; picked W={picked}")
+        rows.append(row)
+        del ks, vs
+        torch.cuda.empty_cache()
+    return {"mode": "workers-sweep", "cus": cus, "steps": steps,
+            "timing": "decode + merge kernel time per step, dispatch-stamped HIP events, two rounds per count",
             "rows": rows}
 
 

@@ -164,7 +164,9 @@ int hpc_decode_plan_static(const int32_t* seq_lens, int32_t batch, int32_t num_k
  * pays for each entry (unit) its range touches: the entry's end and, when
  * the unit is split, its partial.  This returns the W in [min_workers,
  * max_workers] whose costliest worker, priced as its tiles plus entry_cost
- * tiles per entry, is cheapest; ties go to the larger W.  With the lengths
+ * tiles per entry, is cheapest: scanning down from max_workers, a smaller W
+ * replaces the best so far only when it prices at least HPC_DECODE_MIN_GAIN
+ * (1%) below it, so near-ties keep the larger W.  With the lengths
  * of a batch whose sequence boundaries fall on worker boundaries at some W
  * just below the compute-unit count, that W wins (one entry per worker).
  * The pages price tiles only; entry_cost is this library's extension
@@ -177,8 +179,12 @@ int32_t hpc_decode_choose_workers(const int32_t* seq_lens, int32_t batch, int32_
                                   int32_t min_workers, int32_t max_workers, float entry_cost);
 
 /* The entry price of the worker-count rules, in tiles (about 0.6 us per
- * entry end against about 1.25 us per 32 KiB tile, measured on MI355X). */
+ * entry end against about 1.25 us per 32 KiB tile, measured on MI355X), and
+ * the least relative gain for which the rule leaves more compute units idle
+ * (a bf16 64q/8kv batch priced 0.25% cheaper at 255 workers measured 0.5%
+ * slower than at 256). */
 #define HPC_DECODE_ENTRY_COST 0.5f
+#define HPC_DECODE_MIN_GAIN 0.01
 
 /* Worker count for a device-scheduled step on a GPU with n_cus compute
  * units (>= 2), pure host code.  W1 = hpc_decode_choose_workers over

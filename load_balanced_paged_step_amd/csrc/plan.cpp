@@ -271,7 +271,7 @@ extern "C" int32_t hpc_decode_choose_workers(const int32_t* seq_lens, int32_t ba
         double worst;
         int64_t entries;
         worker_costs(s0, s1, T, W, entry_cost, worst, entries);
-        if (W == max_workers || worst < best_cost - 1e-9) {
+        if (W == max_workers || worst < best_cost * (1.0 - HPC_DECODE_MIN_GAIN) - 1e-9) {
             best = W;
             best_cost = worst;
         }
