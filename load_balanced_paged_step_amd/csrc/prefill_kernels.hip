@@ -7,10 +7,12 @@
 // n_b are this step's new tokens; new token j, at position
 // p = L_b - n_b + j, is a query over the cached tokens t <= p.
 //
-// Work: one workgroup (4 waves) per unit (sequence b, KV head h, block of 16
-// consecutive queries), taken from a host-made work list ordered by
-// decreasing cost (the number of 64-token KV tiles the block sees), so the
-// longest units start first and the short ones fill in behind them.
+// Work: one workgroup (4 waves, or two groups of 4 on small grids) per work
+// entry of a host-made list: a unit (sequence b, KV head h, block of 16
+// consecutive queries) whole, or a contiguous share of a long unit's KV
+// tiles, which writes a normalised fp32 partial and log-sum-exp that
+// prefill_merge_kernel folds afterwards.  Entries run longest first (cost =
+// the 64-token KV tiles they cover), so short ones fill in behind.
 //  * Each wave owns heads w, w + 4, w + 8, w + 12 (< G) of the KV head's
 //    query group: per head a 16-query row block, whose Q stays in registers.
 //  * Per 64-token tile, K and V (one page of head h) are loaded by all 256
@@ -28,8 +30,9 @@
 //    first query position; tokens > p score -inf.
 // Lane layout (lane = n + 16 g): QK: A = K [token n][dims 32 kk + 8 g ..],
 // B = Q^T [query n][same dims], D[token 4 g + i][query n] in register i.
-// PV: A = V^T [dim 8 n + nb][tokens 4 g .. 4 g + 3], B = P^T, D[dim
-// 8 (4 g + i) + nb][query n] in register i of accumulator nb.
+// PV (32-token chunk c): A = V^T [dim 8 n + nb][tokens 4 g .. 4 g + 3 of
+// 16-token blocks 2c and 2c + 1], B = P^T, D[dim 8 (4 g + i) + nb][query n]
+// in register i of accumulator nb.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -546,28 +549,28 @@ __global__ void __launch_bounds__(256) prefill_merge_kernel(PrefillArgs a) {
     if (part == 0) a.lse[orow] = wsum > 0.f ? M + __logf(wsum) : -INFINITY;
 }
 
-// With fewer than two units per compute unit the grid cannot hide one
-// unit's tile chain behind other workgroups, so two groups of 4 waves split
-// each unit's tiles (NG = 2, G <= 8); with more, a unit is one group of 4
-// waves and two workgroups share a CU.  G > 8 (4 heads per wave) keeps
+// With fewer than two work entries per compute unit the grid cannot hide
+// one entry's tile chain behind other workgroups, so two groups of 4 waves
+// split each entry's tiles (NG = 2, G <= 8); with more, an entry is one group
+// of 4 waves and two workgroups share a CU.  G > 8 (4 heads per wave) keeps
 // NG = 1: its group state does not fit the tile buffers.
 template <bool FP8, int HPW>
-void launch_hpw(const PrefillArgs& a, int n_units, hipStream_t s) {
-    if (n_units < 2 * device_cus())
-        hipLaunchKernelGGL((prefill_kernel<FP8, HPW, 2>), dim3(n_units), dim3(2 * kThreads), 0, s, a);
+void launch_hpw(const PrefillArgs& a, int n_entries, hipStream_t s) {
+    if (n_entries < 2 * device_cus())
+        hipLaunchKernelGGL((prefill_kernel<FP8, HPW, 2>), dim3(n_entries), dim3(2 * kThreads), 0, s, a);
     else
-        hipLaunchKernelGGL((prefill_kernel<FP8, HPW, 1>), dim3(n_units), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((prefill_kernel<FP8, HPW, 1>), dim3(n_entries), dim3(kThreads), 0, s, a);
 }
 
 template <bool FP8>
-int launch_fp8(const PrefillArgs& a, int n_units, void* stream) {
+int launch_fp8(const PrefillArgs& a, int n_entries, void* stream) {
     const hipStream_t s = static_cast<hipStream_t>(stream);
     if (a.group <= 4)
-        launch_hpw<FP8, 1>(a, n_units, s);
+        launch_hpw<FP8, 1>(a, n_entries, s);
     else if (a.group <= 8)
-        launch_hpw<FP8, 2>(a, n_units, s);
+        launch_hpw<FP8, 2>(a, n_entries, s);
     else
-        hipLaunchKernelGGL((prefill_kernel<FP8, 4, 1>), dim3(n_units), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((prefill_kernel<FP8, 4, 1>), dim3(n_entries), dim3(kThreads), 0, s, a);
     return static_cast<int>(hipGetLastError());
 }
 
