@@ -97,6 +97,9 @@ def parse_args():
                          "workloads (all, or one by name) and print one JSON line")
     ap.add_argument("--prefill-workers", type=int, default=None, metavar="W",
                     help="with --prefill: time only the plan balanced over W workers (0: whole units)")
+    ap.add_argument("--phase-trace", action="store_true",
+                    help="instead of the bench line: per-worker phase durations of the decode kernel on --workload "
+                         "from the tracing window's stamps, print one JSON line")
     ap.add_argument("--workers-sweep", action="store_true",
                     help="instead of the bench line: time the device-scheduled step at one and two workers per CU "
                          "and at hpc_decode_pick_workers' choice on batches of both KV dtypes, print one JSON line")
@@ -223,6 +226,10 @@ def main() -> int:
     if args.fused_merge and args.schedule != "device":
         print("--fused-merge needs the device schedule", file=sys.stderr)
         return 2
+    if args.phase_trace:
+        print(json.dumps(phase_trace(dev, cus, args.workload, args.n_workers, min(args.steps, 200), args.warmup)),
+              flush=True)
+        return 0
     if args.workers_sweep:
         print(json.dumps(workers_sweep(dev, cus, args.steps, args.warmup)), flush=True)
         return 0
@@ -809,6 +816,74 @@ def skew_sweep(dev, W: int, cus: int, steps: int, warmup: int) -> dict:
             "heads": "8 q / 1 kv, head dim 128, bf16 KV, page 64",
             "static_rule": "smallest power of two S with units x S >= CUs, S <= 128 and <= the longest unit's tiles",
             "rows": rows}
+
+
+def phase_trace(dev, cus: int, cfg: int, n_workers: int, steps: int, warmup: int) -> dict:
+    """Per-worker phases of the device-scheduled decode kernel from the
+    tracing window's wall-clock stamps (100 MHz), over `steps` traced steps
+    (KV rotated over >= 1 GiB of copies): entry -> first loads issued
+    (schedule), entry -> first tile consumed (first data), first -> last tile
+    consumed (steady state, per tile), last tile -> end (entry merges), entry
+    -> end.  Medians and maxima over the workers of each step, then the
+    median over steps; the traced launches' kernel time by events beside."""
+    import numpy as np
+    import torch
+
+    import load_balanced_paged_step_amd as hd
+    from workloads import WORKLOADS, workload_inputs
+
+    inp = workload_inputs(cfg)
+    W = n_workers or hd.hpc_decode_pick_workers(inp.seq_lens, inp.num_kv_heads, inp.kv_dtype, cus)
+    kv_bytes = inp.k_cache.numel() * inp.k_cache.element_size() * 2
+    copies = max(1, min(16, math.ceil((1 << 30) / kv_bytes)))
+    q, bt, sl = inp.q.to(dev), inp.block_table.to(dev), inp.seq_lens.to(dev)
+    ks = [inp.k_cache.to(dev) for _ in range(copies)]
+    vs = [inp.v_cache.to(dev) for _ in range(copies)]
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+    ws = torch.zeros(hd.hpc_decode_step_workspace_size(inp.batch, inp.num_q_heads, inp.num_kv_heads, W),
+                     dtype=torch.uint8, device=dev)
+    launchers = [hd.StepLauncher(q, ks[c], vs[c], bt, sl, out, lse, num_kv_heads=inp.num_kv_heads, n_workers=W,
+                                 workspace=ws, sm_scale=inp.sm_scale, k_scale=inp.k_scale, v_scale=inp.v_scale)
+                 for c in range(copies)]
+    clock_warmup(dev, cus, inputs=ks + vs)
+    for i in range(max(warmup, 20)):
+        launchers[i % copies]()
+    torch.cuda.synchronize()
+    rate_hz = hd.hpc_decode_wall_clock_hz()
+    buf = torch.zeros(8 * W, dtype=torch.int64, device=dev)
+    names = ("schedule_us", "first_tile_us", "steady_us_per_tile", "entry_merges_us", "worker_us")
+    per_step = {n: {"median": [], "max": []} for n in names}
+    hd.hpc_decode_profile_start(steps)
+    hd.hpc_decode_trace_start(buf)
+    try:
+        for i in range(steps):
+            buf.zero_()
+            launchers[i % copies]()
+            st = buf.cpu().numpy().view(np.uint64).reshape(W, 8).astype(np.int64)
+            busy = st[:, 5] > 0
+            t = st[busy, :5] * (1e6 / rate_hz)
+            tiles = st[busy, 5]
+            vals = {"schedule_us": t[:, 1] - t[:, 0], "first_tile_us": t[:, 2] - t[:, 0],
+                    "steady_us_per_tile": (t[:, 3] - t[:, 2]) / np.maximum(tiles - 1, 1),
+                    "entry_merges_us": t[:, 4] - t[:, 3], "worker_us": t[:, 4] - t[:, 0]}
+            for n in names:
+                per_step[n]["median"].append(float(np.median(vals[n])))
+                per_step[n]["max"].append(float(np.max(vals[n])))
+    finally:
+        hd.hpc_decode_trace_stop()
+    d_ms, c_ms, n = hd.hpc_decode_profile_stop()
+    summary = {n: {"median_over_workers": round(float(np.median(per_step[n]["median"])), 3),
+                   "max_over_workers": round(float(np.median(per_step[n]["max"])), 3)} for n in names}
+    log(f"phase trace {WORKLOADS[cfg].name}, W={W}: " + "; ".join(
+        f"{n} {v['median_over_workers']} (max {v['max_over_workers']})" for n, v in summary.items())
+        + f"; traced decode kernel {d_ms / max(n, 1) * 1e3:.2f} us by events")
+    return {"mode": "phase-trace", "workload": WORKLOADS[cfg].name, "n_workers": W, "steps": steps,
+            "clock_hz": rate_hz, "phases": summary,
+            "traced_decode_kernel_us": round(d_ms / max(n, 1) * 1e3, 3),
+            "traced_merge_kernel_us": round(c_ms / max(n, 1) * 1e3, 3),
+            "note": "stamps are taken by wave 0 of each worker; workers on different XCDs have offset clocks, so "
+                    "only durations within a worker are used"}
 
 
 WORKER_SWEEP_BATCHES = (

@@ -420,6 +420,30 @@ const char* hpc_status_string(int status);
 int hpc_decode_profile_start(int32_t capacity);
 int hpc_decode_profile_stop(double* decode_ms, double* combine_ms, int32_t* n_calls);
 
+/*
+ * Tracing window (measurement only).  While it is on, every decode-kernel
+ * launch with W workers, W * 64 <= bytes, records for each worker w eight
+ * uint64 words at device_buffer + 8 w: stamps of the device's constant
+ * wall clock (hipDeviceAttributeWallClockRate, 100 MHz on MI355X) at kernel
+ * entry, once the first ring slots' loads are issued, after the first tile
+ * is consumed, after the last, and at the end (entry merges and any
+ * in-kernel merge done); then the worker's tile count (device schedule; 0
+ * with a host plan), its entry count, and 0.  Workers without tiles leave
+ * their words untouched.  Each launch overwrites the buffer (device memory,
+ * caller-owned, valid while the window is on); a launch with more workers
+ * than it holds records nothing.  Stamps of workers on different XCDs are
+ * not comparable (their clocks differ by up to about 2 us); durations
+ * within one worker are.  Outside the window the kernel only tests a null
+ * pointer at each phase boundary.  Errors: HPC_ERR_NULL, HPC_ERR_INVALID
+ * (bytes < 64).  No HIP call.
+ */
+int hpc_decode_trace_start(void* device_buffer, int64_t bytes);
+int hpc_decode_trace_stop(void);
+
+/* Rate of the clock the tracing stamps count, in Hz, for the current device
+ * (hipDeviceAttributeWallClockRate); HPC_ERR_HIP if HIP cannot report it. */
+int64_t hpc_decode_wall_clock_hz(void);
+
 #ifdef __cplusplus
 }
 #endif

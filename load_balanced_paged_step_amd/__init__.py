@@ -29,7 +29,8 @@ __all__ = [
     "hpc_decode_static_splits", "hpc_decode_choose_workers", "hpc_decode_pick_workers", "ENTRY_COST_TILES",
     "hpc_decode_plan_words", "hpc_decode_workspace_size",
     "hpc_decode_check", "hpc_decode_attn", "hpc_status_string", "hpc_decode_profile_start",
-    "hpc_decode_profile_stop", "hpc_probe_read", "hpc_probe_read_timed", "hpc_probe_copy", "hpc_decode_step",
+    "hpc_decode_profile_stop", "hpc_decode_trace_start", "hpc_decode_trace_stop",
+    "hpc_decode_wall_clock_hz", "hpc_probe_read", "hpc_probe_read_timed", "hpc_probe_copy", "hpc_decode_step",
     "hpc_decode_step_check", "hpc_decode_step_workspace_size", "hpc_decode_plan_device", "StepLauncher",
     "hpc_decode_step_noalloc", "hpc_decode_step_noalloc_max_bytes",
     "hpc_decode_plan_workspace_bound", "hpc_decode_plan_attn", "PlannedStepLauncher",
@@ -475,6 +476,22 @@ def hpc_decode_profile_stop():
     _lib.check(lib().hpc_decode_profile_stop(ctypes.byref(d), ctypes.byref(c), ctypes.byref(n)),
                "hpc_decode_profile_stop")
     return d.value, c.value, n.value
+
+
+def hpc_decode_trace_start(buffer: torch.Tensor) -> None:
+    """Tracing window on: decode launches record 8 uint64 words per worker
+    into ``buffer`` (device memory, >= 64 bytes per worker)."""
+    _lib.check(lib().hpc_decode_trace_start(_dev_ptr(buffer, "buffer"), buffer.numel() * buffer.element_size()),
+               "hpc_decode_trace_start")
+
+
+def hpc_decode_trace_stop() -> None:
+    _lib.check(lib().hpc_decode_trace_stop(), "hpc_decode_trace_stop")
+
+
+def hpc_decode_wall_clock_hz() -> int:
+    """Rate of the tracing stamps' clock (Hz) on the current device."""
+    return _lib.check(lib().hpc_decode_wall_clock_hz(), "hpc_decode_wall_clock_hz")
 
 
 def hpc_probe_read(buf: torch.Tensor, sink: torch.Tensor, n_workgroups: int, stream=None) -> None:

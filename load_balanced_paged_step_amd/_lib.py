@@ -122,6 +122,9 @@ SIGNATURES = {
                                          ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _VP, ctypes.c_int64, _VP,
                                          _VP]),
     "hpc_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "hpc_decode_trace_start": (ctypes.c_int, [_VP, ctypes.c_int64]),
+    "hpc_decode_trace_stop": (ctypes.c_int, []),
+    "hpc_decode_wall_clock_hz": (ctypes.c_int64, []),
     "hpc_decode_profile_start": (ctypes.c_int, [ctypes.c_int32]),
     "hpc_decode_profile_stop": (ctypes.c_int, [_F64P, _F64P, _I32P]),
     "hpc_probe_read": (ctypes.c_int, [_VP, ctypes.c_int64, _VP, ctypes.c_int32, _VP]),

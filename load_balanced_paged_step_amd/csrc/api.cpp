@@ -5,6 +5,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <mutex>
@@ -12,6 +13,23 @@
 
 #include "hpc_decode.h"
 #include "internal.h"
+
+namespace hpcd {
+
+namespace {
+// tracing window: the caller's device buffer and its size, read by every
+// decode launch (lock-free; set and cleared by the host calls below)
+std::atomic<unsigned long long*> g_trace_buf{nullptr};
+std::atomic<int64_t> g_trace_bytes{0};
+}  // namespace
+
+unsigned long long* trace_buffer(int n_workers) {
+    unsigned long long* b = g_trace_buf.load(std::memory_order_acquire);
+    if (b == nullptr || g_trace_bytes.load(std::memory_order_acquire) < int64_t(64) * n_workers) return nullptr;
+    return b;
+}
+
+}  // namespace hpcd
 
 namespace {
 
@@ -346,6 +364,29 @@ extern "C" int hpc_decode_plan_device(const int32_t* seq_lens, int32_t batch, in
     return hpcd::launch_plan_device(seq_lens, batch, num_kv_heads, n_workers, max_pages_per_seq, plan, stream) == 0
                ? HPC_OK
                : HPC_ERR_HIP;
+}
+
+extern "C" int hpc_decode_trace_start(void* device_buffer, int64_t bytes) {
+    if (device_buffer == nullptr) return HPC_ERR_NULL;
+    if (bytes < 64) return HPC_ERR_INVALID;
+    hpcd::g_trace_buf.store(nullptr, std::memory_order_release);
+    hpcd::g_trace_bytes.store(bytes, std::memory_order_release);
+    hpcd::g_trace_buf.store(static_cast<unsigned long long*>(device_buffer), std::memory_order_release);
+    return HPC_OK;
+}
+
+extern "C" int64_t hpc_decode_wall_clock_hz(void) {
+    int dev = 0, khz = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess ||
+        khz <= 0)
+        return HPC_ERR_HIP;
+    return int64_t(khz) * 1000;
+}
+
+extern "C" int hpc_decode_trace_stop(void) {
+    hpcd::g_trace_buf.store(nullptr, std::memory_order_release);
+    hpcd::g_trace_bytes.store(0, std::memory_order_release);
+    return HPC_OK;
 }
 
 extern "C" int hpc_decode_profile_start(int32_t capacity) {

@@ -337,13 +337,14 @@ __device__ __forceinline__ void fetch_args(A& a, B& b, C& c, D& d) {
     asm("" : "+s"(a), "+s"(b), "+s"(c), "+s"(d));
 }
 
-template <int KV, int PF, int NT, bool DEV, bool VALU>
+template <int KV, int PF, int NT, bool DEV, bool VALU, bool TRACE>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     const __bf16* __restrict__ q, const char* __restrict__ kcache, const char* __restrict__ vcache,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ worker_ptr, const int32_t* __restrict__ entries,
     __bf16* __restrict__ out, float* __restrict__ lse, float* __restrict__ o_part,
-    float* __restrict__ lse_part, int32_t* __restrict__ merge_records, DecodeScalars a) {
+    float* __restrict__ lse_part, int32_t* __restrict__ merge_records, unsigned long long* __restrict__ stamps,
+    DecodeScalars a) {
     // entry ends: register i of every wave's eight accumulators, as two
     // 16-byte halves per lane, so each wave stores and loads whole f32x4s
     // entry ends (MFMA tile math): up to kPending entries' states wait in
@@ -372,6 +373,14 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     // every load in flight)
     const int32_t* __restrict__ lens_loop = seq_lens;
     fetch_args(seq_lens, a.batch, a.max_pages_per_seq, a.n_workers);
+    // tracing window (the TRACE instantiation, launched only while a window
+    // is on): wall-clock stamps of this worker's phases, each stored by
+    // thread 0 when taken
+    int n_consumed = 0, n_ended = 0;
+    auto stamp = [&](int i) {
+        if (threadIdx.x == 0) stamps[8 * static_cast<int64_t>(blockIdx.x) + i] = wall_clock64();
+    };
+    if constexpr (TRACE) stamp(0);
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int n = lane & 15;
@@ -498,6 +507,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
         load_tile(ring[j], planned[j]);
         __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (TRACE) stamp(1);
 
     // Device schedule, while the first tiles are in flight: empty sequences
     // get out = 0, lse = -inf and a merge record saying so, from worker
@@ -957,10 +967,14 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
         for (int j = 0; j < PF; ++j) {
             if constexpr (VALU) consume_valu(ring[j]);
             else consume(ring[j]);
+            if constexpr (TRACE) {
+                if (n_consumed++ == 0) stamp(2);
+            }
             const TileInfo ended = ring[j].info;
             plan_tile(planned[j]);
             load_tile(ring[j], planned[j]);
             if (ended.last()) {
+                if constexpr (TRACE) ++n_ended;
                 if constexpr (VALU) {
                     deposit_valu(ended);
                     if (nvpend == kPending) merge_pending_valu();
@@ -972,6 +986,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
         }
         if (!ring[0].info.real()) break;
     }
+    if constexpr (TRACE) stamp(3);
     if constexpr (VALU) {
         if (nvpend > 0) merge_pending_valu();
     } else {
@@ -1061,6 +1076,15 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
                 }
                 __syncthreads();   // s_last is rewritten for the next unit
             }
+        }
+    }
+    if constexpr (TRACE) {
+        stamp(4);
+        if (threadIdx.x == 0) {
+            unsigned long long* st = stamps + 8 * static_cast<int64_t>(w);
+            st[5] = DEV ? static_cast<unsigned long long>(w_end - w_begin) : 0ull;
+            st[6] = static_cast<unsigned long long>(n_ended);
+            st[7] = 0;
         }
     }
 }
@@ -1328,11 +1352,21 @@ void launch_decode_t(const DecodeArgs& a, int n_workers, size_t lds, hipStream_t
     const DecodeScalars sc{a.batch,        a.num_kv_heads,  a.group,   a.max_pages_per_seq, a.num_pages,
                            a.max_partials, a.qk_scale_log2, a.v_scale, n_workers, a.fused_merge};
     constexpr int kTilesPerSlot = KV == HPC_KV_FP8_E4M3 ? HPC_DECODE_PAIR_FP8 + 1 : 1;
-    hipExtLaunchKernelGGL((decode_kernel<KV, PF, kTilesPerSlot, DEV, VALU>), dim3(n_workers), dim3(kDecodeThreads),
-                          static_cast<std::uint32_t>(lds), s, e0, e1, 0u,
-                          static_cast<const __bf16*>(a.q), static_cast<const char*>(a.k),
-                          static_cast<const char*>(a.v), a.block_table, a.seq_lens, a.worker_ptr, a.entries,
-                          static_cast<__bf16*>(a.out), a.lse, a.o_part, a.lse_part, a.merge_records, sc);
+    unsigned long long* const stamps = trace_buffer(n_workers);
+    const auto q = static_cast<const __bf16*>(a.q);
+    const auto k = static_cast<const char*>(a.k);
+    const auto v = static_cast<const char*>(a.v);
+    const auto out = static_cast<__bf16*>(a.out);
+    if (stamps)
+        hipExtLaunchKernelGGL((decode_kernel<KV, PF, kTilesPerSlot, DEV, VALU, true>), dim3(n_workers),
+                              dim3(kDecodeThreads), static_cast<std::uint32_t>(lds), s, e0, e1, 0u, q, k, v,
+                              a.block_table, a.seq_lens, a.worker_ptr, a.entries, out, a.lse, a.o_part, a.lse_part,
+                              a.merge_records, stamps, sc);
+    else
+        hipExtLaunchKernelGGL((decode_kernel<KV, PF, kTilesPerSlot, DEV, VALU, false>), dim3(n_workers),
+                              dim3(kDecodeThreads), static_cast<std::uint32_t>(lds), s, e0, e1, 0u, q, k, v,
+                              a.block_table, a.seq_lens, a.worker_ptr, a.entries, out, a.lse, a.o_part, a.lse_part,
+                              a.merge_records, stamps, sc);
 }
 
 }  // namespace

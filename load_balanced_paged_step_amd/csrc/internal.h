@@ -118,6 +118,9 @@ int launch_decode(const DecodeArgs& a, int kv_dtype, int tile_math, int n_worker
 int launch_combine(const CombineArgs& a, int n_records, bool device_sched, void* stream,
                    void* ev_start = nullptr, void* ev_stop = nullptr);
 int launch_prologue(const PrologueArgs& a, void* stream);
+// The tracing window's device buffer when it is on and holds n_workers
+// workers' stamps (8 words each), else null (api.cpp).
+unsigned long long* trace_buffer(int n_workers);
 int launch_prefill(const PrefillArgs& a, int n_entries, int n_merge, bool kv_fp8, void* stream);
 int launch_plan_device(const int32_t* seq_lens, int batch, int num_kv_heads, int n_workers,
                        int max_pages_per_seq, int32_t* plan, void* stream);

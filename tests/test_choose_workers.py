@@ -142,3 +142,12 @@ def test_near_ties_keep_the_larger_count():
     lens5 = workload_lengths(5)
     assert hd.hpc_decode_choose_workers(lens5, 8, 128, 256) == 256
     assert _brute(lens5, 8, 250, 256, 0.5) == 256
+
+
+def test_trace_window_errors():
+    """The tracing window's host calls check their arguments and call no HIP."""
+    lib = hd.lib()
+    assert lib.hpc_decode_trace_start(None, 4096) == hd.HPC_ERR_NULL
+    assert lib.hpc_decode_trace_start(ctypes.c_void_p(0x1000), 63) == hd.HPC_ERR_INVALID
+    assert lib.hpc_decode_trace_start(ctypes.c_void_p(0x1000), 64) == hd.HPC_OK
+    assert lib.hpc_decode_trace_stop() == hd.HPC_OK
