@@ -115,8 +115,10 @@ class PrefillStep:
     """Plans a prefill / extend step on the host (lengths known there), keeps
     the work list and the partials' workspace on the device, and launches
     the attention (and the merge of cut units).  n_workers = 0 cuts nothing;
-    n_workers > 0 cuts every unit longer than q = max(ceil(T / n_workers),
-    min_share_tiles) tiles into shares of q."""
+    n_workers > 0 cuts every unit longer than 2 q, q = max(ceil(T /
+    n_workers), min_share_tiles), into shares of q tiles; None (the default)
+    takes two workers per compute unit of the device, the count measured
+    best on MI355X (two workgroups of one group fit a CU)."""
 
     #: shares shorter than this many tiles cost more in partial writes and the
     #: merge than they save (measured on the q512 prompts, whose units are
@@ -124,9 +126,11 @@ class PrefillStep:
     MIN_SHARE_TILES = 16
 
     def __init__(self, q_start_host, seq_lens_host, num_q_heads: int, num_kv_heads: int, max_pages_per_seq: int,
-                 n_workers: int = 0, min_share_tiles: int | None = None, device="cuda"):
+                 n_workers: int | None = None, min_share_tiles: int | None = None, device="cuda"):
         if min_share_tiles is None:
             min_share_tiles = self.MIN_SHARE_TILES
+        if n_workers is None:
+            n_workers = 2 * torch.cuda.get_device_properties(torch.device(device)).multi_processor_count
         self.words, self.counts = hpc_prefill_plan(q_start_host, seq_lens_host, num_kv_heads, max_pages_per_seq,
                                                    n_workers, min_share_tiles)
         self.n_entries, self.n_merge, self.n_partials = self.counts
