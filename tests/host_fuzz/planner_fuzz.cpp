@@ -1,4 +1,4 @@
-// Host-only fuzz of the library's planners and host checks, built with
+// Host-only fuzz of the library's planners, built with
 // AddressSanitizer and UBSan by tests/test_host_sanitizers.py (no GPU, no
 // HIP runtime).  Every plan is written into a buffer of exactly the size its
 // size query returned, so a write past the bound is caught; coverage
