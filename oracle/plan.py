@@ -24,8 +24,21 @@ The reading used here (and, independently, by the C++ planner):
      of u in entry order gets slot base_u + k.  Units with S_u != 1 are
      listed for the merge as (u, S_u, base_u), base_u = 0 when S_u = 0.
 
+Priced partition (this build's extension; the pages price tiles only).  A
+worker also pays for each unit it touches, an entry end and possibly a
+partial.  With entry_cost_q = c > 0 (in quarter tiles), step 3 becomes:
+
+  3'. tile j costs 4, plus c when j is the first tile of a unit;
+      A(j) = the cost of tiles 0 .. j-1, C = A(T);
+      s_w = the largest j in [0, T] with A(j) <= floor(w * C / W).
+
+With c = 0 this is s_w = floor(w T / W) again.  c is applied only when
+W <= T and C >= (4 + c + 1) W, so that every worker's share of the cost
+exceeds one tile's and no worker is left without tiles, and C < 2^31.
+Otherwise the plan is the plain one.
+
 Serialised as int32 words:
-  header[16] = {1, B, H_kv, W, T, E, n_partials, n_combine, 64, 0, ..., 0}
+  header[16] = {1, B, H_kv, W, T, E, n_partials, n_combine, 64, c applied, 0, ..., 0}
   worker_ptr[W + 1], entries[E][4] = (u, t0, t1, slot), combine[n_combine][3].
 
 Pinned by ``tests/test_oracle_plan.py``: an independent quota-filling
@@ -49,10 +62,40 @@ def plan_size_words(batch: int, num_kv_heads: int, n_workers: int) -> int:
     return HEADER_WORDS + (n_workers + 1) + 4 * (n_workers + U) + 3 * U
 
 
-def build_plan(seq_lens, num_kv_heads: int, n_workers: int) -> np.ndarray:
+TILE_COST_Q = 4    # one tile, in quarter tiles
+
+
+def priced_boundaries(n_tiles_per_unit, n_workers: int, entry_cost_q: int):
+    """(worker boundaries s[0..W], the entry cost applied) of the priced
+    partition 3' for units of the given tile counts."""
+    n, W, c = list(n_tiles_per_unit), int(n_workers), int(entry_cost_q)
+    T = sum(n)
+    first = set()
+    start = 0
+    for k in n:
+        if k > 0:
+            first.add(start)
+        start += k
+    C = TILE_COST_Q * T + c * len(first)
+    if c <= 0 or W > T or C < (TILE_COST_Q + c + 1) * W or C >= 2**31:
+        return [(w * T) // W for w in range(W + 1)], 0
+    A = [0]                          # A[j] = cost of tiles 0 .. j-1
+    for j in range(T):
+        A.append(A[-1] + TILE_COST_Q + (c if j in first else 0))
+    s = []
+    for w in range(W + 1):
+        tau = (w * C) // W
+        j = T
+        while A[j] > tau:            # the largest j with A(j) <= tau
+            j -= 1
+        s.append(j)
+    return s, c
+
+
+def build_plan(seq_lens, num_kv_heads: int, n_workers: int, entry_cost_q: int = 0) -> np.ndarray:
     lens = [int(x) for x in seq_lens]
     B, H, W = len(lens), int(num_kv_heads), int(n_workers)
-    if W < 1 or H < 1 or any(L < 0 for L in lens):
+    if W < 1 or H < 1 or any(L < 0 for L in lens) or entry_cost_q < 0:
         raise ValueError("invalid plan arguments")
     U = B * H
     n = [(lens[u // H] + PAGE - 1) // PAGE for u in range(U)]
@@ -60,7 +103,7 @@ def build_plan(seq_lens, num_kv_heads: int, n_workers: int) -> np.ndarray:
     for u in range(U):
         P.append(P[-1] + n[u])
     T = P[U]
-    s = [(w * T) // W for w in range(W + 1)]
+    s, c_applied = priced_boundaries(n, W, entry_cost_q)
 
     entries = []          # [u, t0, t1]
     worker_ptr = [0]
@@ -95,7 +138,7 @@ def build_plan(seq_lens, num_kv_heads: int, n_workers: int) -> np.ndarray:
 
     combine = [[u, S[u], base[u]] for u in range(U) if S[u] != 1]
 
-    header = [PLAN_VERSION, B, H, W, T, len(entries), n_partials, len(combine), PAGE]
+    header = [PLAN_VERSION, B, H, W, T, len(entries), n_partials, len(combine), PAGE, c_applied]
     header += [0] * (HEADER_WORDS - len(header))
     words = list(header) + worker_ptr
     for e, slot in zip(entries, slots):
@@ -119,7 +162,8 @@ def parse_plan(words) -> dict:
     return {
         "version": int(hdr[0]), "batch": int(hdr[1]), "num_kv_heads": int(hdr[2]),
         "n_workers": W, "n_tiles": int(hdr[4]), "n_entries": E, "n_partials": int(hdr[6]),
-        "n_combine": C, "tile": int(hdr[8]), "worker_ptr": worker_ptr, "entries": entries,
+        "n_combine": C, "tile": int(hdr[8]), "entry_cost_q": int(hdr[9]), "worker_ptr": worker_ptr,
+        "entries": entries,
         "combine": combine, "n_words": o,
     }
 

@@ -21,7 +21,7 @@ def _golden():
 
 @pytest.mark.parametrize("case", _golden(), ids=lambda c: c["name"])
 def test_hand_worked_schedules(case):
-    words = build_plan(case["seq_lens"], case["num_kv_heads"], case["n_workers"])
+    words = build_plan(case["seq_lens"], case["num_kv_heads"], case["n_workers"], case.get("entry_cost_q", 0))
     assert words.tolist() == case["words"]
 
 
@@ -47,8 +47,36 @@ def quota_walk(lens, H, W):
     return per_worker
 
 
-def check_plan(lens, H, W):
-    words = build_plan(lens, H, W)
+def priced_walk(lens, H, W, c):
+    """Independent construction of the priced partition: tile by tile, with
+    the running cost a = A(j + 1) after tile j, the tile goes to the worker
+    w whose cost window (floor(w C / W), floor((w + 1) C / W)] holds a.
+    Also checks the closed form owner(j) = floor((a W - 1) / C).  Returns
+    per-worker entry lists, or None when the price does not apply."""
+    tiles = [(b * H + h, j) for b in range(len(lens)) for h in range(H)
+             for j in range((lens[b] + PAGE - 1) // PAGE)]
+    T = len(tiles)
+    cost = [4 + (c if j == 0 else 0) for (_, j) in tiles]
+    C = sum(cost)
+    if c == 0 or W > T or C < (4 + c + 1) * W or C >= 2**31:
+        return None
+    per_worker = [[] for _ in range(W)]
+    w, a = 0, 0
+    for (u, j), cj in zip(tiles, cost):
+        a += cj
+        while a > ((w + 1) * C) // W:
+            w += 1
+        assert w == (a * W - 1) // C
+        run = per_worker[w]
+        if run and run[-1][0] == u and run[-1][2] == j:
+            run[-1][2] = j + 1
+        else:
+            run.append([u, j, j + 1])
+    return per_worker
+
+
+def check_plan(lens, H, W, c=0):
+    words = build_plan(lens, H, W, c)
     p = parse_plan(words)
     U = len(lens) * H
     n = [(lens[u // H] + PAGE - 1) // PAGE for u in range(U)]
@@ -60,8 +88,10 @@ def check_plan(lens, H, W):
     wp = p["worker_ptr"]
     assert wp[0] == 0 and wp[-1] == p["n_entries"] and np.all(np.diff(wp) >= 0)
 
-    # same schedule as the independent walk
-    walk = quota_walk(lens, H, W)
+    # same schedule as the independent walk (the priced one when the price applies)
+    priced = priced_walk(lens, H, W, c) if c else None
+    assert p["entry_cost_q"] == (c if priced is not None else 0)
+    walk = priced if priced is not None else quota_walk(lens, H, W)
     for w in range(W):
         got = [list(map(int, e[:3])) for e in ents[wp[w]:wp[w + 1]]]
         assert got == walk[w], (w, got, walk[w])
@@ -73,9 +103,19 @@ def check_plan(lens, H, W):
         seen[int(u)][t0:t1] += 1
     assert all(np.all(v == 1) for v in seen.values())
 
-    # balance: every worker holds floor(T/W) or ceil(T/W) tiles
     loads = [int(sum(e[2] - e[1] for e in ents[wp[w]:wp[w + 1]])) for w in range(W)]
-    assert set(loads) <= {T // W, -(-T // W)} and sum(loads) == T
+    assert sum(loads) == T
+    if priced is None:
+        # balance: every worker holds floor(T/W) or ceil(T/W) tiles
+        assert set(loads) <= {T // W, -(-T // W)}
+    else:
+        # every worker holds tiles, and its cost (4 per tile, c per entry
+        # that starts a unit) is within one priced tile of its share C / W
+        starts = [sum(1 for e in ents[wp[w]:wp[w + 1]] if e[1] == 0) for w in range(W)]
+        costs = [4 * t + c * k for t, k in zip(loads, starts)]
+        C = sum(costs)
+        assert min(loads) >= 1
+        assert all(C // W - (4 + c) < x < -(-C // W) + (4 + c) for x in costs), (costs, C)
     assert p["n_entries"] <= (W + U - 1 if T else 0)
 
     # slots: -1 exactly for single-entry units; otherwise a bijection onto [0, n_partials)
@@ -128,6 +168,42 @@ def test_random_batches(lens, H, W):
     check_plan(lens, H, W)
 
 
+PRICES = (1, 2, 4, 8, 16)
+
+
+def test_priced_exhaustive_small():
+    vals = [0, 1, 64, 65, 128, 200, 640]
+    for a, b in itertools.product(vals, vals):
+        for H in (1, 2):
+            for W in range(1, 9):
+                for c in PRICES:
+                    check_plan([a, b, 64], H, W, c)
+
+
+@settings(max_examples=300, deadline=None)
+@given(lens=st.lists(st.integers(0, 5000), min_size=1, max_size=40),
+       H=st.integers(1, 8), W=st.integers(1, 400), c=st.sampled_from(PRICES))
+def test_priced_random_batches(lens, H, W, c):
+    check_plan(lens, H, W, c)
+
+
+def test_priced_reduces_to_plain():
+    # a zero price, and a price the rule declines, give the plain plan word for word
+    for lens, H, W in (([131072] + [4096] * 31, 1, 252), ([37, 64, 130, 200], 2, 5), ([64] * 9, 1, 9)):
+        plain = build_plan(lens, H, W)
+        assert np.array_equal(build_plan(lens, H, W, 0), plain)
+    assert np.array_equal(build_plan([64] * 9, 1, 9, 8), build_plan([64] * 9, 1, 9))   # C = 108 < 13 * 9
+
+
+def test_priced_workload_sizes():
+    # skewed batch at W = 256: the price moves cuts but never empties a worker
+    p = check_plan([131072] + [4096] * 31, 1, 256, 8)
+    assert p["entry_cost_q"] == 8
+    # 64 equal sequences of 8 tiles at W = 64: every share is one unit, priced or not
+    p = check_plan([512] * 64, 1, 64, 8)
+    assert p["n_partials"] == 0 and p["n_entries"] == 64
+
+
 def test_workload_sizes():
     p = check_plan([131072] + [4096] * 31, 1, 256)
     assert p["n_tiles"] == 4032
@@ -142,3 +218,5 @@ def test_rejects_bad_arguments():
         build_plan([1, 2], 1, 0)
     with pytest.raises(ValueError):
         build_plan([1, -2], 1, 4)
+    with pytest.raises(ValueError):
+        build_plan([1, 2], 1, 4, -1)
