@@ -47,7 +47,7 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(workload_name: str, schedule: str, n_workers: int):
+def measured_traffic(workload_name: str, schedule: str, n_workers: int, entry_price: int = 0):
     """HBM bytes per decode launch from the committed counter summary, or None
     when it was taken for another configuration or an older kernel."""
     try:
@@ -56,7 +56,8 @@ def measured_traffic(workload_name: str, schedule: str, n_workers: int):
     except (OSError, ValueError):
         return None
     if (t.get("kernel_source_sha256") != kernel_source_hash() or t.get("workload") != workload_name
-            or t.get("schedule") != schedule or t.get("n_workers") != n_workers):
+            or t.get("schedule") != schedule or t.get("n_workers") != n_workers
+            or t.get("entry_price", 0) != entry_price):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -74,6 +75,9 @@ def parse_args():
     ap.add_argument("--n-workers", type=int, default=0,
                     help="persistent workgroups (0: the library's worker-count rule, hpc_decode_pick_workers, for "
                          "the step; one per CU for the sweeps)")
+    ap.add_argument("--entry-price", type=int, default=-1,
+                    help="the partition's price of a unit start in quarter tiles (-1: the library's rule, "
+                         "hpc_decode_pick_entry_price, for the step's worker count)")
     ap.add_argument("--plan-in-place", action="store_true",
                     help="--schedule host: the kernels read the plan from the pinned host buffer (no upload)")
     ap.add_argument("--copies", type=int, default=0, help="rotating KV copies (0: enough for >= 1 GiB)")
@@ -103,6 +107,9 @@ def parse_args():
     ap.add_argument("--workers-sweep", action="store_true",
                     help="instead of the bench line: time the device-scheduled step at one and two workers per CU "
                          "and at hpc_decode_pick_workers' choice on batches of both KV dtypes, print one JSON line")
+    ap.add_argument("--price-sweep", action="store_true",
+                    help="instead of the bench line: time the device-scheduled step at entry prices 0, 2, 4, 8, 16 "
+                         "at hpc_decode_pick_workers' count on the sweep batches, print one JSON line")
     ap.add_argument("--prologue", action="store_true",
                     help="instead of the bench line: time the fused prologue (QK-norm, RoPE, paged append) "
                          "alone and before the decode step on workloads 4 and 5, print one JSON line")
@@ -112,9 +119,10 @@ def parse_args():
     return ap.parse_args()
 
 
-def native_planner_us(seq_lens, num_kv_heads: int, n_workers: int, calls: int = 200) -> float:
-    """Mean time of one hpc_decode_plan call into a preallocated buffer, as
-    hpc_decode_plan_attn makes it (no Python-side argument conversion)."""
+def native_planner_us(seq_lens, num_kv_heads: int, n_workers: int, calls: int = 200, entry_price: int = 0) -> float:
+    """Mean time of one hpc_decode_plan_priced call into a preallocated
+    buffer, as hpc_decode_plan_attn makes it (no Python-side argument
+    conversion)."""
     import ctypes
     import numpy as np
     import load_balanced_paged_step_amd as hd
@@ -123,12 +131,12 @@ def native_planner_us(seq_lens, num_kv_heads: int, n_workers: int, calls: int = 
     lens = np.ascontiguousarray(seq_lens, dtype=np.int32).reshape(-1)
     cap = hd.hpc_decode_plan_size(lens.shape[0], num_kv_heads, n_workers)
     buf = np.empty(cap, dtype=np.int32)
-    fn = _lib.lib().hpc_decode_plan
+    fn = _lib.lib().hpc_decode_plan_priced
     lp, bp, B = lens.ctypes.data_as(i32p), buf.ctypes.data_as(i32p), lens.shape[0]
-    _lib.check(fn(lp, B, num_kv_heads, n_workers, bp, cap), "hpc_decode_plan")
+    _lib.check(fn(lp, B, num_kv_heads, n_workers, entry_price, bp, cap), "hpc_decode_plan_priced")
     t0 = time.perf_counter()
     for _ in range(calls):
-        fn(lp, B, num_kv_heads, n_workers, bp, cap)
+        fn(lp, B, num_kv_heads, n_workers, entry_price, bp, cap)
     return (time.perf_counter() - t0) / calls * 1e6
 
 
@@ -227,8 +235,11 @@ def main() -> int:
         print("--fused-merge needs the device schedule", file=sys.stderr)
         return 2
     if args.phase_trace:
-        print(json.dumps(phase_trace(dev, cus, args.workload, args.n_workers, min(args.steps, 200), args.warmup)),
-              flush=True)
+        print(json.dumps(phase_trace(dev, cus, args.workload, args.n_workers, min(args.steps, 200), args.warmup,
+                                     args.entry_price)), flush=True)
+        return 0
+    if args.price_sweep:
+        print(json.dumps(price_sweep(dev, cus, args.steps, args.warmup)), flush=True)
         return 0
     if args.workers_sweep:
         print(json.dumps(workers_sweep(dev, cus, args.steps, args.warmup)), flush=True)
@@ -259,8 +270,16 @@ def main() -> int:
         W = hd.hpc_decode_pick_workers(inp.seq_lens, inp.num_kv_heads, inp.kv_dtype, cus)
         w_rule = (f"hpc_decode_pick_workers ({cus} CUs; hpc_decode_choose_workers over [{cus // 2}, {cus}], "
                   f"entry cost {hd.ENTRY_COST_TILES} tile, or {2 * cus} for fp8 with >= 1.5 entries per worker)")
-    log(f"device {props.name}, {cus} CUs; W={W} ({w_rule}); KV {kv_bytes_total / 1e6:.1f} MB x {copies} copies; "
-        f"algorithmic bytes/step {alg_bytes}")
+    if args.entry_price >= 0:
+        price, price_rule = args.entry_price, "given (--entry-price)"
+    else:
+        # the library's price rule for this W: the partition price (quarter
+        # tiles per unit start) whose costliest worker prices lowest
+        price = hd.hpc_decode_pick_entry_price(inp.seq_lens, inp.num_kv_heads, inp.kv_dtype, W)
+        price_rule = (f"hpc_decode_pick_entry_price (prices 0, 2, 4, 8, 16; entry cost "
+                      f"{0.5 if inp.kv_dtype == 'bf16' else 2.0} tiles on {inp.kv_dtype})")
+    log(f"device {props.name}, {cus} CUs; W={W} ({w_rule}); entry price {price} ({price_rule}); "
+        f"KV {kv_bytes_total / 1e6:.1f} MB x {copies} copies; algorithmic bytes/step {alg_bytes}")
 
     q = inp.q.to(dev)
     bt = inp.block_table.to(dev)
@@ -278,7 +297,7 @@ def main() -> int:
                          dtype=torch.uint8, device=dev)
         launchers = [hd.StepLauncher(q, ks[c], vs[c], bt, sl, out, lse, num_kv_heads=inp.num_kv_heads,
                                      n_workers=W, workspace=ws, tile_math=args.tile_math,
-                                     fused_merge=args.fused_merge, **scales)
+                                     fused_merge=args.fused_merge, entry_price=price, **scales)
                      for c in range(copies)]
 
         def one_step(i: int) -> None:
@@ -288,7 +307,7 @@ def main() -> int:
                          dtype=torch.uint8, device=dev)
         planned = [hd.PlannedStepLauncher(q, ks[c], vs[c], bt, sl, out, lse, num_kv_heads=inp.num_kv_heads,
                                           n_workers=W, workspace=ws, in_place=args.plan_in_place,
-                                          tile_math=args.tile_math, **scales)
+                                          tile_math=args.tile_math, entry_price=price, **scales)
                    for c in range(copies)]
         lens_np = np.ascontiguousarray(lens_host, dtype=np.int32)
 
@@ -332,7 +351,7 @@ def main() -> int:
     # (preallocated buffers; part of every --schedule host step, overlapping
     # the previous step's kernels), and one upload of its plan; taken after the
     # timed steps, so the GPU does not idle between the warm-up and the timing
-    plan_us = native_planner_us(lens_host, inp.num_kv_heads, W, calls=200)
+    plan_us = native_planner_us(lens_host, inp.num_kv_heads, W, calls=200, entry_price=price)
     upload_us = plan_upload_us(lens_host, inp.num_kv_heads, W, dev)
     log(f"decode kernel {decode_us:.2f} us, merge kernel {combine_us:.2f} us (HIP events, {n_calls} calls)")
 
@@ -356,6 +375,7 @@ def main() -> int:
             "workload": wl.name, "batch": inp.batch, "kv_lens": _lens_summary(lens_host),
             "num_q_heads": inp.num_q_heads, "num_kv_heads": inp.num_kv_heads, "head_dim": 128,
             "page_size": 64, "kv_dtype": inp.kv_dtype, "n_workers": W, "n_workers_from": w_rule,
+            "entry_price": price, "entry_price_from": price_rule,
             "kv_copies": copies,
             "algorithmic_bytes": alg_bytes,
             "schedule": args.schedule + (", plan in place" if args.schedule == "host" and args.plan_in_place else ""),
@@ -369,7 +389,7 @@ def main() -> int:
                     "timed_calls": n_calls},
         "roofline": {"bound": "hbm", "achieved": round(achieved_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": (measured_traffic(wl.name, args.schedule, W)
+                     "traffic": (measured_traffic(wl.name, args.schedule, W, price)
                                  if args.tile_math == "mfma" else None),
                      "kernel": "decode_kernel", "bytes_per_launch": alg_bytes,
                      "kernel_us_hip_events": round(decode_us, 3),
@@ -818,7 +838,7 @@ def skew_sweep(dev, W: int, cus: int, steps: int, warmup: int) -> dict:
             "rows": rows}
 
 
-def phase_trace(dev, cus: int, cfg: int, n_workers: int, steps: int, warmup: int) -> dict:
+def phase_trace(dev, cus: int, cfg: int, n_workers: int, steps: int, warmup: int, entry_price: int = -1) -> dict:
     """Per-worker phases of the device-scheduled decode kernel from the
     tracing window's wall-clock stamps (100 MHz), over `steps` traced steps
     (KV rotated over >= 1 GiB of copies): entry -> first loads issued
@@ -834,6 +854,8 @@ def phase_trace(dev, cus: int, cfg: int, n_workers: int, steps: int, warmup: int
 
     inp = workload_inputs(cfg)
     W = n_workers or hd.hpc_decode_pick_workers(inp.seq_lens, inp.num_kv_heads, inp.kv_dtype, cus)
+    price = (entry_price if entry_price >= 0
+             else hd.hpc_decode_pick_entry_price(inp.seq_lens, inp.num_kv_heads, inp.kv_dtype, W))
     kv_bytes = inp.k_cache.numel() * inp.k_cache.element_size() * 2
     copies = max(1, min(16, math.ceil((1 << 30) / kv_bytes)))
     q, bt, sl = inp.q.to(dev), inp.block_table.to(dev), inp.seq_lens.to(dev)
@@ -844,7 +866,8 @@ def phase_trace(dev, cus: int, cfg: int, n_workers: int, steps: int, warmup: int
     ws = torch.zeros(hd.hpc_decode_step_workspace_size(inp.batch, inp.num_q_heads, inp.num_kv_heads, W),
                      dtype=torch.uint8, device=dev)
     launchers = [hd.StepLauncher(q, ks[c], vs[c], bt, sl, out, lse, num_kv_heads=inp.num_kv_heads, n_workers=W,
-                                 workspace=ws, sm_scale=inp.sm_scale, k_scale=inp.k_scale, v_scale=inp.v_scale)
+                                 workspace=ws, sm_scale=inp.sm_scale, k_scale=inp.k_scale, v_scale=inp.v_scale,
+                                 entry_price=price)
                  for c in range(copies)]
     clock_warmup(dev, cus, inputs=ks + vs)
     for i in range(max(warmup, 20)):
@@ -875,10 +898,11 @@ def phase_trace(dev, cus: int, cfg: int, n_workers: int, steps: int, warmup: int
     d_ms, c_ms, n = hd.hpc_decode_profile_stop()
     summary = {n: {"median_over_workers": round(float(np.median(per_step[n]["median"])), 3),
                    "max_over_workers": round(float(np.median(per_step[n]["max"])), 3)} for n in names}
-    log(f"phase trace {WORKLOADS[cfg].name}, W={W}: " + "; ".join(
+    log(f"phase trace {WORKLOADS[cfg].name}, W={W}, entry price {price}: " + "; ".join(
         f"{n} {v['median_over_workers']} (max {v['max_over_workers']})" for n, v in summary.items())
         + f"; traced decode kernel {d_ms / max(n, 1) * 1e3:.2f} us by events")
-    return {"mode": "phase-trace", "workload": WORKLOADS[cfg].name, "n_workers": W, "steps": steps,
+    return {"mode": "phase-trace", "workload": WORKLOADS[cfg].name, "n_workers": W, "entry_price": price,
+            "steps": steps,
             "clock_hz": rate_hz, "phases": summary,
             "traced_decode_kernel_us": round(d_ms / max(n, 1) * 1e3, 3),
             "traced_merge_kernel_us": round(c_ms / max(n, 1) * 1e3, 3),
@@ -954,6 +978,74 @@ def workers_sweep(dev, cus: int, steps: int, warmup: int) -> dict:
         torch.cuda.empty_cache()
     return {"mode": "workers-sweep", "cus": cus, "steps": steps,
             "timing": "decode + merge kernel time per step, dispatch-stamped HIP events, two rounds per count",
+            "rows": rows}
+
+
+PRICE_SWEEP_PRICES = (0, 2, 4, 8, 16)
+
+
+def price_sweep(dev, cus: int, steps: int, warmup: int) -> dict:
+    """The device-scheduled step at entry prices 0, 2, 4, 8 and 16 quarter
+    tiles, at hpc_decode_pick_workers' count, on the worker-sweep batches:
+    decode + merge kernel time per step (dispatch-stamped events), KV
+    rotated over >= 1 GiB of copies, prices taken in turn for three rounds
+    so that drift hits all alike."""
+    import numpy as np
+    import torch
+
+    import load_balanced_paged_step_amd as hd
+    from workloads import draw_loguniform_lengths, make_inputs
+
+    clock_warmup(dev, cus)
+    steps = max(steps, 50)
+    rows = []
+    for name, lens, hq, hkv, kv in WORKER_SWEEP_BATCHES:
+        if isinstance(lens, tuple):
+            lens = list(draw_loguniform_lengths(np.random.default_rng(lens[1]), lens[2], 128, 65536))
+        inp = make_inputs(lens, hq, hkv, kv, seed=4)
+        kv_bytes = inp.k_cache.numel() * inp.k_cache.element_size() * 2
+        copies = max(1, min(16, math.ceil((1 << 30) / kv_bytes)))
+        q, bt, sl = inp.q.to(dev), inp.block_table.to(dev), inp.seq_lens.to(dev)
+        ks = [inp.k_cache.to(dev) for _ in range(copies)]
+        vs = [inp.v_cache.to(dev) for _ in range(copies)]
+        out = torch.empty_like(q)
+        lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+        scales = dict(sm_scale=inp.sm_scale, k_scale=inp.k_scale, v_scale=inp.v_scale)
+        W = hd.hpc_decode_pick_workers(inp.seq_lens, hkv, kv, cus)
+        picked = hd.hpc_decode_pick_entry_price(inp.seq_lens, hkv, kv, W)
+        lens_np = inp.seq_lens.numpy()
+        ws = torch.zeros(hd.hpc_decode_step_workspace_size(inp.batch, hq, hkv, W), dtype=torch.uint8, device=dev)
+        launchers = {c: [hd.StepLauncher(q, ks[i], vs[i], bt, sl, out, lse, num_kv_heads=hkv, n_workers=W,
+                                         workspace=ws, entry_price=c, **scales) for i in range(copies)]
+                     for c in PRICE_SWEEP_PRICES}
+        applied = {c: int(hd.hpc_decode_plan(lens_np, hkv, W, entry_price=c)[9]) for c in PRICE_SWEEP_PRICES}
+        entries = {c: int(hd.hpc_decode_plan(lens_np, hkv, W, entry_price=c)[5]) for c in PRICE_SWEEP_PRICES}
+        times = {c: [] for c in PRICE_SWEEP_PRICES}
+        for _ in range(3):
+            for c in PRICE_SWEEP_PRICES:
+                for i in range(max(warmup, 20)):
+                    launchers[c][i % copies]()
+                torch.cuda.synchronize()
+                hd.hpc_decode_profile_start(steps)
+                for i in range(steps):
+                    launchers[c][i % copies]()
+                torch.cuda.synchronize()
+                d_ms, c_ms, n = hd.hpc_decode_profile_stop()
+                times[c].append(round((d_ms + c_ms) / max(n, 1) * 1e3, 2))
+        med = {c: float(np.median(t)) for c, t in times.items()}
+        best = min(med, key=med.get)
+        row = {"batch": name, "kv_dtype": kv, "n_workers": W, "picked_price": picked,
+               "applied": {str(c): applied[c] for c in PRICE_SWEEP_PRICES},
+               "entries": {str(c): entries[c] for c in PRICE_SWEEP_PRICES},
+               "kernel_us": {str(c): t for c, t in times.items()},
+               "picked_over_best": round(med[picked] / med[best], 4)}
+        log(f"price sweep {name} (W={W}): " + ", ".join(f"c={c} {med[c]:.2f} us" for c in PRICE_SWEEP_PRICES)
+            + f"; picked {picked} ({row['picked_over_best']}x the best)")
+        rows.append(row)
+        del launchers, ks, vs, ws
+        torch.cuda.empty_cache()
+    return {"mode": "price-sweep", "cus": cus, "steps": steps,
+            "timing": "decode + merge kernel time per step, dispatch-stamped HIP events, median of three rounds",
             "rows": rows}
 
 

@@ -93,7 +93,17 @@ typedef struct hpc_decode_params {
                                 /* host-planned entry points return                */
                                 /* HPC_ERR_UNSUPPORTED for 1; other values are     */
                                 /* HPC_ERR_INVALID.                                */
+    int32_t entry_price;        /* the partition's price of a unit start, in       */
+                                /* quarter tiles, 0 .. HPC_DECODE_MAX_ENTRY_PRICE  */
+                                /* (else HPC_ERR_INVALID): 0 (default) gives equal */
+                                /* tile shares, > 0 the priced partition of        */
+                                /* hpc_decode_plan_priced.  Used where the library */
+                                /* partitions: hpc_decode_step (on the device) and */
+                                /* hpc_decode_plan_attn; hpc_decode_attn follows   */
+                                /* the plan it is given.                           */
 } hpc_decode_params;
+
+#define HPC_DECODE_MAX_ENTRY_PRICE 64   /* quarter tiles: 16 tiles per unit start */
 
 /*
  * Upper bound, in int32 words, of the plan for this batch shape:
@@ -134,6 +144,23 @@ int64_t hpc_decode_plan_size(int32_t batch, int32_t num_kv_heads, int32_t n_work
  */
 int hpc_decode_plan(const int32_t* seq_lens, int32_t batch, int32_t num_kv_heads,
                     int32_t n_workers, int32_t* plan, int64_t plan_capacity);
+
+/*
+ * The scheduler above with the partition priced (this library's extension;
+ * the pages spread tiles only).  A worker pays for every unit it starts as
+ * well as for its tiles: the entry's end, the Q reload and, for a split
+ * unit, a partial.  Tile j costs 4 (quarter tiles), plus entry_price when it
+ * is the first tile of its unit; with A(j) the cost of tiles 0 .. j-1 and
+ * C = A(T), worker w starts at the largest j with A(j) <= floor(w C / W).
+ * entry_price = 0 is hpc_decode_plan word for word.  The price applies only
+ * when W <= T, C >= (4 + entry_price + 1) W (no worker is left without
+ * tiles) and C < 2^31; otherwise the plan is the plain one.  Header word 9
+ * holds the price applied (0 when declined).  Errors as hpc_decode_plan,
+ * plus HPC_ERR_INVALID for entry_price outside 0 .. HPC_DECODE_MAX_ENTRY_PRICE.
+ */
+int hpc_decode_plan_priced(const int32_t* seq_lens, int32_t batch, int32_t num_kv_heads,
+                           int32_t n_workers, int32_t entry_price, int32_t* plan,
+                           int64_t plan_capacity);
 
 /*
  * Static split-KV schedule in the same word layout, for comparison with the
@@ -186,6 +213,12 @@ int32_t hpc_decode_choose_workers(const int32_t* seq_lens, int32_t batch, int32_
 #define HPC_DECODE_ENTRY_COST 0.5f
 #define HPC_DECODE_MIN_GAIN 0.01
 
+/* The entry cost, in tiles, of hpc_decode_pick_entry_price on an fp8 cache:
+ * a 16 KiB fp8 tile streams in about half a bf16 tile's time while an entry
+ * end costs the same, so an entry weighs four times as many tiles (fitted on
+ * MI355X: 32 sequences of 64q/8kv fp8, lengths log-uniform in [128, 65536],
+ * fastest at 8 quarter tiles per unit start, at W = 256 and at W = 512). */
+#define HPC_DECODE_ENTRY_COST_FP8 2.0f
 /* Worker count for a device-scheduled step on a GPU with n_cus compute
  * units (>= 2), pure host code.  W1 = hpc_decode_choose_workers over
  * [n_cus / 2, n_cus] with HPC_DECODE_ENTRY_COST.  On an fp8 cache whose
@@ -201,6 +234,21 @@ int32_t hpc_decode_choose_workers(const int32_t* seq_lens, int32_t batch, int32_
  * 2^20 and HPC_ERR_UNSUPPORTED for an unknown kv_dtype. */
 int32_t hpc_decode_pick_workers(const int32_t* seq_lens, int32_t batch, int32_t num_kv_heads, int32_t kv_dtype,
                                 int32_t n_cus);
+
+/* Entry price for a step of n_workers workers (the params field
+ * entry_price), pure host code.  Among the prices 0, 2, 4, 8 and 16 quarter
+ * tiles, each partition (hpc_decode_plan_priced) is priced by its costliest
+ * worker, as its tiles plus an entry cost per unit its range touches
+ * (HPC_DECODE_ENTRY_COST on a bf16 cache, HPC_DECODE_ENTRY_COST_FP8 on fp8).
+ * Scanning up from 0, a price replaces the best so far only when its
+ * partition prices at least HPC_DECODE_MIN_GAIN below it, and a price the
+ * partition declines is skipped, so a batch whose plain partition already
+ * fits unit boundaries keeps price 0.  Returns the price (>= 0), or
+ * HPC_ERR_NULL, HPC_ERR_INVALID (batch < 0, num_kv_heads < 1, n_workers < 1,
+ * a negative length, 2^31 - 1 tiles or more) or HPC_ERR_UNSUPPORTED (an
+ * unknown kv_dtype). */
+int32_t hpc_decode_pick_entry_price(const int32_t* seq_lens, int32_t batch, int32_t num_kv_heads,
+                                    int32_t kv_dtype, int32_t n_workers);
 
 /* Split count of the static split-KV baseline for a batch: the smallest
  * power of two S with batch * num_kv_heads * S >= n_cus (one share per
@@ -396,13 +444,14 @@ int64_t hpc_decode_step_noalloc_max_bytes(void);
 /*
  * The device-derived schedule written out on `stream` into device `plan`
  * (int32 words, capacity >= hpc_decode_plan_size) in exactly the layout of
- * hpc_decode_plan, so the two can be compared word for word.  One
+ * hpc_decode_plan_priced with the same entry_price, so the two can be
+ * compared word for word.  One
  * workgroup; limits: batch <= 2048, n_workers <= 2048, batch * H_kv <= 4096
  * (else HPC_ERR_UNSUPPORTED).  Lengths are clamped as in hpc_decode_step.
  */
 int hpc_decode_plan_device(const int32_t* seq_lens, int32_t batch, int32_t num_kv_heads,
-                           int32_t n_workers, int32_t max_pages_per_seq, int32_t* plan,
-                           int64_t plan_capacity, void* stream);
+                           int32_t n_workers, int32_t entry_price, int32_t max_pages_per_seq,
+                           int32_t* plan, int64_t plan_capacity, void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* hpc_status_string(int status);
@@ -428,7 +477,9 @@ int hpc_decode_profile_stop(double* decode_ms, double* combine_ms, int32_t* n_ca
  * entry, once the first ring slots' loads are issued, after the first tile
  * is consumed, after the last, and at the end (entry merges and any
  * in-kernel merge done); then the worker's tile count (device schedule; 0
- * with a host plan), its entry count, and 0.  Workers without tiles leave
+ * with a host plan), its entry count, and where it ran: the XCC_ID hardware
+ * register in the high 32 bits, HW_ID (CU, shader array and engine ids) in
+ * the low 32.  Workers without tiles leave
  * their words untouched.  Each launch overwrites the buffer (device memory,
  * caller-owned, valid while the window is on); a launch with more workers
  * than it holds records nothing.  Stamps of workers on different XCDs are

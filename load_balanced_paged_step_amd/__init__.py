@@ -27,6 +27,7 @@ from ._lib import (HPC_OK, HPC_ERR_NULL, HPC_ERR_INVALID, HPC_ERR_UNSUPPORTED, H
 __all__ = [
     "hpc_decode_plan_size", "hpc_decode_plan", "hpc_decode_plan_static_size", "hpc_decode_plan_static",
     "hpc_decode_static_splits", "hpc_decode_choose_workers", "hpc_decode_pick_workers", "ENTRY_COST_TILES",
+    "hpc_decode_pick_entry_price", "MAX_ENTRY_PRICE",
     "hpc_decode_plan_words", "hpc_decode_workspace_size",
     "hpc_decode_check", "hpc_decode_attn", "hpc_status_string", "hpc_decode_profile_start",
     "hpc_decode_profile_stop", "hpc_decode_trace_start", "hpc_decode_trace_stop",
@@ -98,11 +99,12 @@ def tile_math_code(tile_math) -> int:
 
 def make_params(num_q_heads, num_kv_heads, max_pages_per_seq, num_pages, kv_dtype, sm_scale,
                 k_scale=1.0, v_scale=1.0, head_dim=HEAD_DIM, page_size=PAGE,
-                tile_math="mfma", fused_merge=False) -> hpc_decode_params:
+                tile_math="mfma", fused_merge=False, entry_price=0) -> hpc_decode_params:
     code = kv_dtype if isinstance(kv_dtype, int) else kv_dtype_code(kv_dtype)
     return hpc_decode_params(int(num_q_heads), int(num_kv_heads), int(head_dim), int(page_size),
                              int(max_pages_per_seq), int(num_pages), code, float(sm_scale),
-                             float(k_scale), float(v_scale), tile_math_code(tile_math), int(fused_merge))
+                             float(k_scale), float(v_scale), tile_math_code(tile_math), int(fused_merge),
+                             int(entry_price))
 
 
 # ---------------------------------------------------------------- planner ---
@@ -111,12 +113,13 @@ def hpc_decode_plan_size(batch: int, num_kv_heads: int, n_workers: int) -> int:
     return _lib.check(lib().hpc_decode_plan_size(batch, num_kv_heads, n_workers), "hpc_decode_plan_size")
 
 
-def hpc_decode_plan(seq_lens, num_kv_heads: int, n_workers: int, out=None) -> np.ndarray:
+def hpc_decode_plan(seq_lens, num_kv_heads: int, n_workers: int, out=None, entry_price: int = 0) -> np.ndarray:
     """Per-step schedule of host lengths ``seq_lens``; returns the used int32 words.
 
     ``out`` may be a preallocated host int32 buffer (numpy array or a pinned
     CPU tensor) of at least ``hpc_decode_plan_size`` words; the result is
-    then a view of it.
+    then a view of it.  ``entry_price`` > 0 gives the priced partition
+    (``hpc_decode_plan_priced``: a unit start costs that many quarter tiles).
     """
     lens = _host_i32(seq_lens).reshape(-1)
     cap = hpc_decode_plan_size(lens.shape[0], num_kv_heads, n_workers)
@@ -126,8 +129,8 @@ def hpc_decode_plan(seq_lens, num_kv_heads: int, n_workers: int, out=None) -> np
         buf = out.numpy() if isinstance(out, torch.Tensor) else out
         if buf.dtype != np.int32 or not buf.flags.c_contiguous:
             raise ValueError("plan buffer must be a contiguous int32 host buffer")
-    _lib.check(lib().hpc_decode_plan(_i32p(lens), lens.shape[0], num_kv_heads, n_workers, _i32p(buf),
-                                     buf.shape[0]), "hpc_decode_plan")
+    _lib.check(lib().hpc_decode_plan_priced(_i32p(lens), lens.shape[0], num_kv_heads, n_workers, int(entry_price),
+                                            _i32p(buf), buf.shape[0]), "hpc_decode_plan_priced")
     return buf[:hpc_decode_plan_words(buf)]
 
 
@@ -168,19 +171,35 @@ def hpc_decode_choose_workers(seq_lens, num_kv_heads: int, min_workers: int, max
                                                       max_workers, float(entry_cost)), "hpc_decode_choose_workers")
 
 
+def _kv_code(kv_dtype) -> int:
+    if isinstance(kv_dtype, str):
+        return {"bf16": HPC_KV_BF16, "fp8_e4m3": HPC_KV_FP8_E4M3}[kv_dtype]
+    if isinstance(kv_dtype, torch.dtype):
+        return kv_dtype_code(kv_dtype)
+    return int(kv_dtype)
+
+
 def hpc_decode_pick_workers(seq_lens, num_kv_heads: int, kv_dtype, n_cus: int) -> int:
     """The worker count for a device-scheduled step on n_cus compute units:
     the worker-count rule over [n_cus / 2, n_cus], or 2 n_cus for an fp8
     cache whose partition then holds 1.5 entries per worker or more."""
     lens = _host_i32(seq_lens).reshape(-1)
-    if isinstance(kv_dtype, str):
-        code = {"bf16": HPC_KV_BF16, "fp8_e4m3": HPC_KV_FP8_E4M3}[kv_dtype]
-    elif isinstance(kv_dtype, torch.dtype):
-        code = kv_dtype_code(kv_dtype)
-    else:
-        code = int(kv_dtype)
-    return _lib.check(lib().hpc_decode_pick_workers(_i32p(lens), lens.shape[0], num_kv_heads, code, n_cus),
-                      "hpc_decode_pick_workers")
+    return _lib.check(lib().hpc_decode_pick_workers(_i32p(lens), lens.shape[0], num_kv_heads, _kv_code(kv_dtype),
+                                                    n_cus), "hpc_decode_pick_workers")
+
+
+#: largest entry price accepted (HPC_DECODE_MAX_ENTRY_PRICE), in quarter tiles
+MAX_ENTRY_PRICE = 64
+
+
+def hpc_decode_pick_entry_price(seq_lens, num_kv_heads: int, kv_dtype, n_workers: int) -> int:
+    """The partition's entry price (quarter tiles per unit start) for a step of
+    n_workers workers: among 0, 2, 4, 8 and 16, the one whose costliest
+    worker prices lowest (by at least 1%), 0 when none does."""
+    lens = _host_i32(seq_lens).reshape(-1)
+    return _lib.check(lib().hpc_decode_pick_entry_price(_i32p(lens), lens.shape[0], num_kv_heads,
+                                                        _kv_code(kv_dtype), n_workers),
+                      "hpc_decode_pick_entry_price")
 
 
 def hpc_decode_plan_words(plan) -> int:
@@ -258,14 +277,14 @@ def hpc_decode_plan_workspace_bound(batch: int, num_q_heads: int, num_kv_heads: 
 
 def hpc_decode_plan_attn(seq_lens_host, plan_host, plan_dev, q, k_cache, v_cache, block_table, seq_lens,
                          workspace, out, lse, *, num_kv_heads, n_workers, sm_scale, k_scale=1.0, v_scale=1.0,
-                         stream=None, tile_math="mfma") -> np.ndarray:
+                         stream=None, tile_math="mfma", entry_price=0) -> np.ndarray:
     """Plan the host lengths into ``plan_host`` (a host int32 buffer, pinned
     for an asynchronous upload), queue its copy to ``plan_dev`` and launch the
     step, in one native call; returns the plan words (a view of plan_host).
     The caller keeps plan_host unchanged until the copy has run on the stream."""
     lens = _host_i32(seq_lens_host).reshape(-1)
     params, args = _step_args(q, k_cache, v_cache, block_table, seq_lens, workspace, out, lse, num_kv_heads,
-                              n_workers, sm_scale, k_scale, v_scale, tile_math)
+                              n_workers, sm_scale, k_scale, v_scale, tile_math, entry_price=entry_price)
     if lens.shape[0] != q.shape[0]:
         raise ValueError("seq_lens_host has the wrong batch size")
     ph = plan_host.numpy() if isinstance(plan_host, torch.Tensor) else plan_host
@@ -296,13 +315,14 @@ class PlannedStepLauncher:
 
     def __init__(self, q, k_cache, v_cache, block_table, seq_lens, out, lse, *, num_kv_heads, n_workers,
                  sm_scale, k_scale=1.0, v_scale=1.0, workspace=None, stream=None, in_place=False,
-                 tile_math="mfma"):
+                 tile_math="mfma", entry_price=0):
         B = q.shape[0]
         if workspace is None:
             need = hpc_decode_plan_workspace_bound(B, q.shape[1], num_kv_heads, n_workers)
             workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
         self.params, args = _step_args(q, k_cache, v_cache, block_table, seq_lens, workspace, out, lse,
-                                       num_kv_heads, n_workers, sm_scale, k_scale, v_scale, tile_math)
+                                       num_kv_heads, n_workers, sm_scale, k_scale, v_scale, tile_math,
+                                       entry_price=entry_price)
         self._keep = (q, k_cache, v_cache, block_table, seq_lens, out, lse, workspace)
         self.workspace = workspace
         self.batch, self.n_workers = int(B), int(n_workers)
@@ -356,7 +376,7 @@ def hpc_decode_step_workspace_size(batch: int, num_q_heads: int, num_kv_heads: i
 
 
 def _step_args(q, k_cache, v_cache, block_table, seq_lens, workspace, out, lse, num_kv_heads, n_workers,
-               sm_scale, k_scale, v_scale, tile_math="mfma", fused_merge=False):
+               sm_scale, k_scale, v_scale, tile_math="mfma", fused_merge=False, entry_price=0):
     if k_cache.dtype != v_cache.dtype or tuple(k_cache.shape) != tuple(v_cache.shape):
         raise ValueError("k_cache and v_cache must have the same dtype and shape")
     if q.dim() != 3 or k_cache.dim() != 4 or block_table.dim() != 2 or k_cache.shape[1] != num_kv_heads:
@@ -368,7 +388,7 @@ def _step_args(q, k_cache, v_cache, block_table, seq_lens, workspace, out, lse, 
         raise ValueError("out must match q's shape and lse must be [B, Hq]")
     params = make_params(q.shape[1], num_kv_heads, block_table.shape[1], k_cache.shape[0], k_cache.dtype,
                          sm_scale, k_scale, v_scale, head_dim=q.shape[2], page_size=k_cache.shape[2],
-                         tile_math=tile_math, fused_merge=fused_merge)
+                         tile_math=tile_math, fused_merge=fused_merge, entry_price=entry_price)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     return (params,
             (ctypes.c_int32(B), ctypes.c_int32(n_workers),
@@ -385,21 +405,22 @@ def _step_args(q, k_cache, v_cache, block_table, seq_lens, workspace, out, lse, 
 
 def hpc_decode_step_check(q, k_cache, v_cache, block_table, seq_lens, workspace, out, lse, *, num_kv_heads,
                           n_workers, sm_scale, k_scale=1.0, v_scale=1.0, tile_math="mfma",
-                          fused_merge=False) -> int:
+                          fused_merge=False, entry_price=0) -> int:
     params, args = _step_args(q, k_cache, v_cache, block_table, seq_lens, workspace, out, lse, num_kv_heads,
-                              n_workers, sm_scale, k_scale, v_scale, tile_math, fused_merge)
+                              n_workers, sm_scale, k_scale, v_scale, tile_math, fused_merge, entry_price)
     return lib().hpc_decode_step_check(ctypes.byref(params), *args)
 
 
 def hpc_decode_step(q, k_cache, v_cache, block_table, seq_lens, workspace, out, lse, *, num_kv_heads,
                     n_workers, sm_scale, k_scale=1.0, v_scale=1.0, stream=None, tile_math="mfma",
-                    fused_merge=False) -> None:
+                    fused_merge=False, entry_price=0) -> None:
     """One decode step with the schedule derived on the device from ``seq_lens``.
     With ``fused_merge`` the decode kernel merges split sequences itself (no
     second kernel); the workspace must then be zero-filled before its first
-    use, and every step leaves it so."""
+    use, and every step leaves it so.  ``entry_price`` > 0 selects the
+    priced partition (quarter tiles per unit start)."""
     params, args = _step_args(q, k_cache, v_cache, block_table, seq_lens, workspace, out, lse, num_kv_heads,
-                              n_workers, sm_scale, k_scale, v_scale, tile_math, fused_merge)
+                              n_workers, sm_scale, k_scale, v_scale, tile_math, fused_merge, entry_price)
     _lib.check(lib().hpc_decode_step(ctypes.byref(params), *args, _stream_handle(stream)), "hpc_decode_step")
 
 
@@ -408,26 +429,28 @@ def hpc_decode_step_noalloc_max_bytes() -> int:
 
 
 def hpc_decode_step_noalloc(q, k_cache, v_cache, block_table, seq_lens, out, lse, *, num_kv_heads, n_workers,
-                            sm_scale, k_scale=1.0, v_scale=1.0, stream=None, tile_math="mfma") -> None:
+                            sm_scale, k_scale=1.0, v_scale=1.0, stream=None, tile_math="mfma",
+                            entry_price=0) -> None:
     """hpc_decode_step with its scratch in the library's fixed per-GPU array
     (no workspace argument, no allocation); calls on one GPU share that array
     and must not overlap."""
     params, args = _step_args(q, k_cache, v_cache, block_table, seq_lens, None, out, lse, num_kv_heads,
-                              n_workers, sm_scale, k_scale, v_scale, tile_math, False)
+                              n_workers, sm_scale, k_scale, v_scale, tile_math, False, entry_price)
     args = args[:7] + args[9:]       # no workspace pointer or size
     _lib.check(lib().hpc_decode_step_noalloc(ctypes.byref(params), *args, _stream_handle(stream)),
                "hpc_decode_step_noalloc")
 
 
 def hpc_decode_plan_device(seq_lens: torch.Tensor, num_kv_heads: int, n_workers: int, max_pages_per_seq: int,
-                           plan: torch.Tensor = None, stream=None) -> torch.Tensor:
+                           plan: torch.Tensor = None, stream=None, entry_price: int = 0) -> torch.Tensor:
     """The device-derived schedule as plan words (device int32 tensor, host-plan layout)."""
     B = int(seq_lens.shape[0])
     cap = hpc_decode_plan_size(B, num_kv_heads, n_workers)
     if plan is None:
         plan = torch.zeros(cap, dtype=torch.int32, device=seq_lens.device)
     _lib.check(lib().hpc_decode_plan_device(_dev_ptr(seq_lens, "seq_lens", torch.int32), B, num_kv_heads,
-                                            n_workers, max_pages_per_seq, _dev_ptr(plan, "plan", torch.int32),
+                                            n_workers, int(entry_price), max_pages_per_seq,
+                                            _dev_ptr(plan, "plan", torch.int32),
                                             plan.numel(), _stream_handle(stream)), "hpc_decode_plan_device")
     return plan
 
@@ -444,14 +467,14 @@ class StepLauncher:
 
     def __init__(self, q, k_cache, v_cache, block_table, seq_lens, out, lse, *, num_kv_heads, n_workers,
                  sm_scale, k_scale=1.0, v_scale=1.0, workspace=None, stream=None, tile_math="mfma",
-                 fused_merge=False):
+                 fused_merge=False, entry_price=0):
         need = hpc_decode_step_workspace_size(q.shape[0], q.shape[1], num_kv_heads, n_workers)
         if workspace is None:   # zero-filled, as the in-kernel merge needs
             workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=q.device)
         self._keep = (q, k_cache, v_cache, block_table, seq_lens, out, lse, workspace)
         self.params, args = _step_args(q, k_cache, v_cache, block_table, seq_lens, workspace, out, lse,
                                        num_kv_heads, n_workers, sm_scale, k_scale, v_scale, tile_math,
-                                       fused_merge)
+                                       fused_merge, entry_price)
         self.workspace = workspace
         self._args = (ctypes.byref(self.params),) + args + (_stream_handle(stream),)
         status = lib().hpc_decode_step_check(*self._args[:-1])
@@ -533,9 +556,10 @@ class DecodeStep:
     """
 
     def __init__(self, num_q_heads: int, num_kv_heads: int, max_batch: int, n_workers: int,
-                 device="cuda", stream=None):
+                 device="cuda", stream=None, entry_price: int = 0):
         self.num_q_heads, self.num_kv_heads = int(num_q_heads), int(num_kv_heads)
         self.n_workers = int(n_workers)
+        self.entry_price = int(entry_price)
         self.device = torch.device(device)
         self.stream = stream
         cap = hpc_decode_plan_size(max_batch, num_kv_heads, n_workers)
@@ -559,7 +583,8 @@ class DecodeStep:
         self._flip ^= 1
         if self._host_ready[i] is not None:
             self._host_ready[i].synchronize()     # its previous upload has left the buffer
-        words = hpc_decode_plan(lens, self.num_kv_heads, self.n_workers, out=self._host[i])
+        words = hpc_decode_plan(lens, self.num_kv_heads, self.n_workers, out=self._host[i],
+                                entry_price=self.entry_price)
         n = words.shape[0]
         s = self._stream()
         with torch.cuda.stream(s):

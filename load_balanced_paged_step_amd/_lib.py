@@ -45,6 +45,7 @@ class hpc_decode_params(ctypes.Structure):
         ("v_scale", ctypes.c_float),
         ("tile_math", ctypes.c_int32),
         ("fused_merge", ctypes.c_int32),
+        ("entry_price", ctypes.c_int32),
     ]
 
 
@@ -76,6 +77,8 @@ SIGNATURES = {
     "hpc_decode_plan_size": (ctypes.c_int64, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]),
     "hpc_decode_plan": (ctypes.c_int, [_I32P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _I32P,
                                        ctypes.c_int64]),
+    "hpc_decode_plan_priced": (ctypes.c_int, [_I32P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                              _I32P, ctypes.c_int64]),
     "hpc_decode_plan_static_size": (ctypes.c_int64, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]),
     "hpc_decode_plan_static": (ctypes.c_int, [_I32P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _I32P,
                                               ctypes.c_int64]),
@@ -83,6 +86,8 @@ SIGNATURES = {
                                                    ctypes.c_int32, ctypes.c_float]),
     "hpc_decode_pick_workers": (ctypes.c_int32, [_I32P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                  ctypes.c_int32]),
+    "hpc_decode_pick_entry_price": (ctypes.c_int32, [_I32P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                     ctypes.c_int32]),
     "hpc_decode_static_splits": (ctypes.c_int32, [_I32P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                   ctypes.c_int32]),
     "hpc_decode_plan_words": (ctypes.c_int64, [_I32P]),
@@ -106,7 +111,7 @@ SIGNATURES = {
     "hpc_decode_step_workspace_size": (ctypes.c_int64, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                         ctypes.c_int32]),
     "hpc_decode_plan_device": (ctypes.c_int, [_VP, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-                                              ctypes.c_int32, _VP, ctypes.c_int64, _VP]),
+                                              ctypes.c_int32, ctypes.c_int32, _VP, ctypes.c_int64, _VP]),
     "hpc_decode_prologue": (ctypes.c_int, [ctypes.POINTER(hpc_prologue_params), ctypes.c_int32] + [_VP] * 12),
     "hpc_decode_prologue_check": (ctypes.c_int, [ctypes.POINTER(hpc_prologue_params), ctypes.c_int32]
                                   + [_VP] * 11),

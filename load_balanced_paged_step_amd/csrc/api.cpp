@@ -80,6 +80,7 @@ extern "C" int hpc_decode_check(const hpc_decode_params* p, const void* q, const
     if (p->tile_math == HPC_TILE_MATH_VALU && G > hpcd::kValuMaxGroup) return HPC_ERR_UNSUPPORTED;
     if (p->fused_merge != 0 && p->fused_merge != 1) return HPC_ERR_INVALID;
     if (p->fused_merge) return HPC_ERR_UNSUPPORTED;   // the host-planned step has no in-kernel merge
+    if (p->entry_price < 0 || p->entry_price > HPC_DECODE_MAX_ENTRY_PRICE) return HPC_ERR_INVALID;
     if (p->max_pages_per_seq < 1 || p->num_pages < 1) return HPC_ERR_INVALID;
     if (!std::isfinite(p->sm_scale) || !std::isfinite(p->k_scale) || !std::isfinite(p->v_scale))
         return HPC_ERR_INVALID;
@@ -200,7 +201,9 @@ extern "C" int hpc_decode_plan_attn(const hpc_decode_params* p, const int32_t* s
                                     const int32_t* block_table, const int32_t* seq_lens, void* workspace,
                                     int64_t workspace_bytes, void* out, float* lse, void* stream) {
     if (!p || !plan_host || !plan_dev) return HPC_ERR_NULL;
-    int status = hpc_decode_plan(seq_lens_host, batch, p->num_kv_heads, n_workers, plan_host, plan_capacity);
+    if (p->entry_price < 0 || p->entry_price > HPC_DECODE_MAX_ENTRY_PRICE) return HPC_ERR_INVALID;
+    int status = hpc_decode_plan_priced(seq_lens_host, batch, p->num_kv_heads, n_workers, p->entry_price, plan_host,
+                                        plan_capacity);
     if (status != HPC_OK) return status;
     status = hpc_decode_check(p, q, k_cache, v_cache, block_table, seq_lens, plan_host, plan_dev, workspace,
                               workspace_bytes, out, lse);
@@ -277,6 +280,7 @@ extern "C" int hpc_decode_step_check(const hpc_decode_params* p, int32_t batch, 
     if (p->tile_math == HPC_TILE_MATH_VALU && p->num_q_heads / p->num_kv_heads > hpcd::kValuMaxGroup)
         return HPC_ERR_UNSUPPORTED;
     if (p->fused_merge != 0 && p->fused_merge != 1) return HPC_ERR_INVALID;
+    if (p->entry_price < 0 || p->entry_price > HPC_DECODE_MAX_ENTRY_PRICE) return HPC_ERR_INVALID;
     if (p->max_pages_per_seq < 1 || p->num_pages < 1) return HPC_ERR_INVALID;
     if (!std::isfinite(p->sm_scale) || !std::isfinite(p->k_scale) || !std::isfinite(p->v_scale))
         return HPC_ERR_INVALID;
@@ -328,6 +332,7 @@ extern "C" int hpc_decode_step(const hpc_decode_params* p, int32_t batch, int32_
     da.qk_scale_log2 = static_cast<float>(static_cast<double>(p->sm_scale) * p->k_scale * 1.4426950408889634);
     da.v_scale = p->v_scale;
     da.fused_merge = p->fused_merge;
+    da.entry_price = p->entry_price;
 
     hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
     hpcd::CombineArgs ca{};
@@ -352,16 +357,19 @@ extern "C" int hpc_decode_step(const hpc_decode_params* p, int32_t batch, int32_
 }
 
 extern "C" int hpc_decode_plan_device(const int32_t* seq_lens, int32_t batch, int32_t num_kv_heads,
-                                      int32_t n_workers, int32_t max_pages_per_seq, int32_t* plan,
-                                      int64_t plan_capacity, void* stream) {
+                                      int32_t n_workers, int32_t entry_price, int32_t max_pages_per_seq,
+                                      int32_t* plan, int64_t plan_capacity, void* stream) {
     if (!seq_lens || !plan) return HPC_ERR_NULL;
-    if (batch < 1 || num_kv_heads < 1 || n_workers < 1 || max_pages_per_seq < 1) return HPC_ERR_INVALID;
+    if (batch < 1 || num_kv_heads < 1 || n_workers < 1 || max_pages_per_seq < 1 || entry_price < 0 ||
+        entry_price > HPC_DECODE_MAX_ENTRY_PRICE)
+        return HPC_ERR_INVALID;
     if (batch > hpcd::kPlanDeviceMaxBatch || n_workers > hpcd::kPlanDeviceMaxWorkers ||
         static_cast<int64_t>(batch) * num_kv_heads > hpcd::kPlanDeviceMaxUnits)
         return HPC_ERR_UNSUPPORTED;
     if (static_cast<int64_t>(batch) * max_pages_per_seq * num_kv_heads >= INT32_MAX) return HPC_ERR_INVALID;
     if (plan_capacity < hpc_decode_plan_size(batch, num_kv_heads, n_workers)) return HPC_ERR_TOO_SMALL;
-    return hpcd::launch_plan_device(seq_lens, batch, num_kv_heads, n_workers, max_pages_per_seq, plan, stream) == 0
+    return hpcd::launch_plan_device(seq_lens, batch, num_kv_heads, n_workers, entry_price, max_pages_per_seq, plan,
+                                    stream) == 0
                ? HPC_OK
                : HPC_ERR_HIP;
 }

@@ -325,6 +325,7 @@ struct DecodeScalars {
     float qk_scale_log2, v_scale;
     int32_t n_workers;      // the grid size (passed so no hidden argument is read)
     int32_t fused_merge;    // device schedule: split units merged by their last-arriving worker
+    int32_t entry_price;    // device schedule: the partition's price of a unit start (quarter tiles)
 };
 
 // Passes kernel arguments through one empty scalar-register asm, so that
@@ -355,7 +356,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     __shared__ float s_l[kPending][kWaves][64];
     __shared__ int32_t s_pend[kPending][2];   // output row and target of each pending entry
     __shared__ int32_t s_last;                 // in-kernel merge: this worker arrived last at the unit
-    extern __shared__ int32_t s_dyn[];   // device schedule: len[B], tile prefix[B + 1]
+    extern __shared__ int32_t s_dyn[];   // device schedule: len[B], tile prefix[B + 1] (, NE prefix[B + 1])
     // VALU tile math: each wave's copy of its entry's Q ([head][dim group g]
     // [k-step], in the K operand's dim order), and the entry-end exchange
     // (per wave and dim group: 8 heads x 128 dims of output sums, and the
@@ -398,19 +399,41 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     HostWalker hwalk;
     int64_t w_begin = 0, w_end = 0;
     int u_first = 0;
+    // in-kernel merge: the units of the worker's first and last tiles and
+    // the workers sharing each, taken here so that the schedule need not
+    // stay live through the tile loop
+    int fm_u[2] = {0, 0}, fm_S[2] = {0, 0};
     if constexpr (DEV) {
-        build_prefix(seq_lens, a.batch, a.max_pages_per_seq, s_dyn, s_dyn + a.batch);
+        int32_t* const s_ne = s_dyn + 2 * a.batch + 1;   // allocated when entry_price > 0
+        build_prefix(seq_lens, a.batch, a.max_pages_per_seq, s_dyn, s_dyn + a.batch,
+                     a.entry_price > 0 ? s_ne : nullptr);
         sched.len = s_dyn;
         sched.pb = s_dyn + a.batch;
+        sched.ne = s_ne;
         sched.B = a.batch;
         sched.H = Hkv;
         sched.W = a.n_workers;
         sched.set_tiles(static_cast<int64_t>(Hkv) * s_dyn[2 * a.batch]);
-        w_begin = sched.range_begin(w);
-        w_end = sched.range_begin(w + 1);
+        sched.set_price(a.entry_price);
+        int b0 = 0, h0 = 0, t0 = 0;
+        if (sched.c != 0) {
+            sched.priced_range_uniform(w, w_begin, w_end, b0, h0, t0);
+        } else {
+            w_begin = sched.range_begin(w);
+            w_end = sched.range_begin(w + 1);
+            if (w_begin < w_end) sched.locate_uniform(w_begin, b0, h0, t0);
+        }
         if (w_begin < w_end) {
-            dwalk.init(sched, w, w_begin, w_end, true);
+            dwalk.init_at(sched, w, w_begin, w_end, b0, h0, t0);
             u_first = dwalk.b * Hkv + dwalk.h;    // the unit of the worker's first tile
+            if (a.fused_merge) {
+                int bB, hB, tB;
+                sched.locate_uniform(w_end - 1, bB, hB, tB);
+                fm_u[0] = u_first;
+                fm_u[1] = bB * Hkv + hB;
+                fm_S[0] = sched.parts(dwalk.b, dwalk.h);
+                fm_S[1] = fm_u[1] == u_first ? 0 : sched.parts(bB, hB);
+            }
         } else {
             dwalk.remaining = 0;                   // an empty worker: only bookkeeping below
         }
@@ -1003,16 +1026,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     if constexpr (DEV) {
         if (a.fused_merge) {
             __syncthreads();   // every wave's partial stores precede the release below
-            const int uA = u_first;
-            int bB, hB, tB;
-            sched.locate_uniform(w_end - 1, bB, hB, tB);
-            const int uB = bB * Hkv + hB;
 #pragma unroll 1
             for (int k = 0; k < 2; ++k) {
-                const int u = k == 0 ? uA : uB;
-                if (k == 1 && uB == uA) break;
+                const int u = fm_u[k];
                 const int bu = u / Hkv;
-                const int S = sched.parts(bu, u - bu * Hkv);
+                const int S = fm_S[k];   // 0 for a second unit that is the first
                 if (S < 2) continue;
                 int32_t* rec = merge_records + kRecordWords * u;
                 if (threadIdx.x == 0) {
@@ -1084,7 +1102,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
             unsigned long long* st = stamps + 8 * static_cast<int64_t>(w);
             st[5] = DEV ? static_cast<unsigned long long>(w_end - w_begin) : 0ull;
             st[6] = static_cast<unsigned long long>(n_ended);
-            st[7] = 0;
+            // where the worker ran: XCC_ID register (high word), HW_ID (low: CU, SH, SE, ...)
+            const unsigned hw_id = __builtin_amdgcn_s_getreg((4) | (0 << 6) | (31 << 11));
+            const unsigned xcc_id = __builtin_amdgcn_s_getreg((20) | (0 << 6) | (31 << 11));
+            st[7] = (static_cast<unsigned long long>(xcc_id) << 32) | hw_id;
         }
     }
 }
@@ -1246,24 +1267,27 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
 // The device schedule written out in the host plan's word layout, by one
 // workgroup, so it can be compared word for word with the host planner.
 __global__ __launch_bounds__(kPlanThreads) void plan_device_kernel(const int32_t* __restrict__ seq_lens, int B,
-                                                                   int H, int W, int max_pages,
+                                                                   int H, int W, int entry_price, int max_pages,
                                                                    int32_t* __restrict__ plan) {
     extern __shared__ int32_t s_dyn[];
     __shared__ int32_t s_tmp[kPlanThreads / 64];
     const int U = B * H;
     int32_t* s_len = s_dyn;               // [B]
     int32_t* s_pb = s_len + B;            // [B + 1]
-    int32_t* s_cnt = s_pb + B + 1;        // [W]   entries per worker -> worker_ptr
+    int32_t* s_ne = s_pb + B + 1;         // [B + 1] sequences with tiles before b
+    int32_t* s_cnt = s_ne + B + 1;        // [W]   entries per worker -> worker_ptr
     int32_t* s_base = s_cnt + W;          // [U]   split slots per unit -> base
     int32_t* s_cidx = s_base + U;         // [U]   merge record flag -> record index
-    build_prefix(seq_lens, B, max_pages, s_len, s_pb);
+    build_prefix(seq_lens, B, max_pages, s_len, s_pb, s_ne);
     Sched sched;
     sched.len = s_len;
     sched.pb = s_pb;
+    sched.ne = s_ne;
     sched.B = B;
     sched.H = H;
     sched.W = W;
     sched.set_tiles(static_cast<int64_t>(H) * s_pb[B]);
+    sched.set_price(entry_price);
     const int t = threadIdx.x;
 
     for (int w = t; w < W; w += kPlanThreads) {
@@ -1289,8 +1313,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_device_kernel(const int32_t
     int32_t* ent = wp + W + 1;
     int32_t* comb = ent + 4 * E;
     if (t < HPC_PLAN_HEADER_WORDS) {
-        const int32_t hdr[9] = {HPC_PLAN_VERSION, B, H, W, static_cast<int32_t>(sched.T), E, P, C, HPC_DECODE_PAGE};
-        plan[t] = t < 9 ? hdr[t] : 0;
+        const int32_t hdr[10] = {HPC_PLAN_VERSION, B, H, W, static_cast<int32_t>(sched.T), E, P, C, HPC_DECODE_PAGE,
+                                 sched.c};
+        plan[t] = t < 10 ? hdr[t] : 0;
     }
     if (t == 0) wp[W] = E;
     for (int w = t; w < W; w += kPlanThreads) {
@@ -1350,7 +1375,8 @@ constexpr int kPrefetchFp8 = HPC_DECODE_PREFETCH_FP8;
 template <int KV, int PF, bool DEV, bool VALU>
 void launch_decode_t(const DecodeArgs& a, int n_workers, size_t lds, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     const DecodeScalars sc{a.batch,        a.num_kv_heads,  a.group,   a.max_pages_per_seq, a.num_pages,
-                           a.max_partials, a.qk_scale_log2, a.v_scale, n_workers, a.fused_merge};
+                           a.max_partials, a.qk_scale_log2, a.v_scale, n_workers, a.fused_merge,
+                           a.entry_price};
     constexpr int kTilesPerSlot = KV == HPC_KV_FP8_E4M3 ? HPC_DECODE_PAIR_FP8 + 1 : 1;
     unsigned long long* const stamps = trace_buffer(n_workers);
     const auto q = static_cast<const __bf16*>(a.q);
@@ -1389,7 +1415,11 @@ int launch_decode(const DecodeArgs& a, int kv_dtype, int tile_math, int n_worker
                   void* ev_start, void* ev_stop) {
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipEvent_t e0 = static_cast<hipEvent_t>(ev_start), e1 = static_cast<hipEvent_t>(ev_stop);
-    const size_t lds = device_sched ? (2 * static_cast<size_t>(a.batch) + 1) * sizeof(int32_t) : 0;
+    // device schedule: lengths and tile prefix, and the NE prefix when priced
+    const size_t lds =
+        device_sched ? ((a.entry_price > 0 ? 3 : 2) * static_cast<size_t>(a.batch) + (a.entry_price > 0 ? 2 : 1)) *
+                           sizeof(int32_t)
+                     : 0;
     if (tile_math == HPC_TILE_MATH_VALU) launch_decode_m<true>(a, kv_dtype, n_workers, device_sched, lds, s, e0, e1);
     else launch_decode_m<false>(a, kv_dtype, n_workers, device_sched, lds, s, e0, e1);
     return static_cast<int>(hipGetLastError());
@@ -1411,12 +1441,12 @@ int launch_combine(const CombineArgs& a, int n_records, bool device_sched, void*
     return static_cast<int>(hipGetLastError());
 }
 
-int launch_plan_device(const int32_t* seq_lens, int batch, int num_kv_heads, int n_workers, int max_pages_per_seq,
-                       int32_t* plan, void* stream) {
+int launch_plan_device(const int32_t* seq_lens, int batch, int num_kv_heads, int n_workers, int entry_price,
+                       int max_pages_per_seq, int32_t* plan, void* stream) {
     const int U = batch * num_kv_heads;
-    const size_t lds = (static_cast<size_t>(2 * batch + 1) + n_workers + 2 * static_cast<size_t>(U)) * sizeof(int32_t);
+    const size_t lds = (static_cast<size_t>(3 * batch + 2) + n_workers + 2 * static_cast<size_t>(U)) * sizeof(int32_t);
     hipLaunchKernelGGL(plan_device_kernel, dim3(1), dim3(kPlanThreads), lds, static_cast<hipStream_t>(stream),
-                       seq_lens, batch, num_kv_heads, n_workers, max_pages_per_seq, plan);
+                       seq_lens, batch, num_kv_heads, n_workers, entry_price, max_pages_per_seq, plan);
     return static_cast<int>(hipGetLastError());
 }
 

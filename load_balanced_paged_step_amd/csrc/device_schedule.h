@@ -3,7 +3,8 @@
 //
 // It is the same schedule the host planner writes (plan.cpp): sequences cut
 // into 64-token tiles, units u = b * H + h in batch-major order, worker w
-// owning global tiles [floor(w T / W), floor((w + 1) T / W)); the split
+// owning global tiles [floor(w T / W), floor((w + 1) T / W)) (or the priced
+// partition below); the split
 // partials of a unit take consecutive slots after those of every earlier
 // split unit.  Here each workgroup derives what it needs from the device
 // copy of the lengths, using closed forms instead of the host's sweep:
@@ -13,6 +14,15 @@
 //   base_u    = sum over u' < u with S_u' >= 2 of S_u'
 // (§Attention Backend: Dynamic Load-Balanced Scheduling, "vLLM x HPC-Ops:
 // High-Performance Attention and MoE Backends from Tencent Hunyuan").
+//
+// Priced partition (this library's extension, hpc_decode_plan_priced): a
+// tile costs 4, a unit's first tile c more; with A(j) the cost of tiles
+// before j and C = A(T), worker w starts at the largest j with
+// A(j) <= floor(w C / W), and the worker of tile j is the one whose cost
+// window (floor(w C / W), floor((w + 1) C / W)] holds A(j + 1):
+//   owner(j)  = floor((A(j + 1) W - 1) / C)
+// With NE_b the sequences with tiles before b, unit (b, h) starts at cost
+// H (4 P_b + c NE_b) + h (4 n_b + c), P_b being the tile prefix per head.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -50,15 +60,16 @@ __device__ __forceinline__ int wave_inclusive_sum(int x) {
 __device__ __forceinline__ int wave_sum(int x) { return __ockl_wfred_add_i32(x); }
 
 // Lengths (clamped to [0, max_pages * 64]) into s_len[B] and the exclusive
-// prefix of tile counts into s_pb[B + 1], built by the first wave alone
-// (wave-wide scans, 64 sequences at a time); every thread of the block calls
-// it and it ends with the block's only barrier.
+// prefix of tile counts into s_pb[B + 1], and, when s_ne is not null, the
+// exclusive count of sequences with tiles into s_ne[B + 1]; built by the
+// first wave alone (wave-wide scans, 64 sequences at a time).  Every thread
+// of the block calls it and it ends with the block's only barrier.
 __device__ void build_prefix(const int32_t* __restrict__ seq_lens, int B, int max_pages, int32_t* s_len,
-                             int32_t* s_pb) {
+                             int32_t* s_pb, int32_t* s_ne = nullptr) {
     if (threadIdx.x < 64) {
         const int lane = threadIdx.x;
         const int cap = max_pages * 64;
-        int carry = 0;
+        int carry = 0, carry_ne = 0;
         for (int b0 = 0; b0 < B; b0 += 64) {
             const int b = b0 + lane;
             int L = b < B ? seq_lens[b] : 0;
@@ -70,8 +81,16 @@ __device__ void build_prefix(const int32_t* __restrict__ seq_lens, int B, int ma
                 s_pb[b] = carry + incl - n;
             }
             carry += __shfl(incl, 63);
+            if (s_ne != nullptr) {
+                const unsigned long long have = __ballot(n > 0);
+                if (b < B) s_ne[b] = carry_ne + __popcll(have & ((1ull << lane) - 1ull));
+                carry_ne += __popcll(have);
+            }
         }
-        if (lane == 0) s_pb[B] = carry;
+        if (lane == 0) {
+            s_pb[B] = carry;
+            if (s_ne != nullptr) s_ne[B] = carry_ne;
+        }
     }
     __syncthreads();
 }
@@ -79,24 +98,108 @@ __device__ void build_prefix(const int32_t* __restrict__ seq_lens, int B, int ma
 struct Sched {
     const int32_t* len;   // LDS [B]
     const int32_t* pb;    // LDS [B + 1]
+    const int32_t* ne;    // LDS [B + 1], sequences with tiles before b (priced partition only)
     int B, H, W;          // W <= 65536
     int64_t T;            // < 2^31
     int64_t qT, rT;       // T = qT W + rT
+    int c;                // entry price applied (0: equal tile shares)
+    int32_t C, qC, rC;    // priced: total cost C < 2^31, C = qC W + rC
 
     __device__ __forceinline__ void set_tiles(int64_t tiles) {
         T = tiles;
         const uint32_t t32 = static_cast<uint32_t>(tiles);
         qT = t32 / static_cast<uint32_t>(W);
         rT = tiles - qT * W;
+        c = 0;
     }
+    // after set_tiles, with ne filled: applies the price where the rule
+    // allows it (W <= T, C >= (4 + c + 1) W, C < 2^31), as the host does
+    __device__ __forceinline__ void set_price(int price) {
+        if (price <= 0 || static_cast<int64_t>(W) > T) return;
+        const int64_t cost = 4 * T + static_cast<int64_t>(price) * H * ne[B];
+        if (cost < static_cast<int64_t>(4 + price + 1) * W || cost >= (int64_t(1) << 31)) return;
+        c = price;
+        C = static_cast<int32_t>(cost);
+        qC = static_cast<int32_t>(static_cast<uint32_t>(cost) / static_cast<uint32_t>(W));
+        rC = C - qC * W;
+    }
+    // priced: cost of the tiles before sequence b, per kv head (H times it is A(P_b))
+    __device__ __forceinline__ int64_t seq_cost(int b) const {
+        return 4 * static_cast<int64_t>(pb[b]) + static_cast<int64_t>(c) * ne[b];
+    }
+    // priced: A at the start of unit (b, h)
+    __device__ __forceinline__ int64_t unit_cost_start(int b, int h) const {
+        return static_cast<int64_t>(H) * seq_cost(b) + static_cast<int64_t>(h) * (4 * tiles(b) + c);
+    }
+    // priced: the worker whose cost window holds a = A(j + 1), 1 <= a <= C
+    __device__ __forceinline__ int owner_at_cost(int64_t a) const { return small_quot(a * W - 1, C); }
 
     __device__ __forceinline__ int tiles(int b) const { return tiles_of(len[b]); }
     __device__ __forceinline__ int64_t unit_start(int b, int h) const {
         return static_cast<int64_t>(H) * pb[b] + static_cast<int64_t>(h) * tiles(b);
     }
-    // floor(w T / W) = w qT + floor(w rT / W), with w rT < W^2
+    // priced: floor(w C / W) = w qC + floor(w rC / W), for w < W (then < C)
+    __device__ __forceinline__ int64_t tau(int w) const {
+        return static_cast<int64_t>(w) * qC + small_quot(static_cast<int64_t>(w) * rC, W);
+    }
+    // priced: the largest j with A(j) <= tau < C, given the last sequence b
+    // whose cost prefix is <= tau (a sequence with tiles, as tau < C).  j
+    // lies in the unit h of b whose cost span holds tau, at the tiles t of
+    // that unit that fit: A(start + t) = start + c + 4 t for t >= 1, and
+    // t < n as tau is below the next unit's start.
+    __device__ __forceinline__ int64_t cut_in(int b, int64_t tau_w, int& h, int& t) const {
+        const int n = tiles(b);
+        const int unit = 4 * n + c;
+        const int r = static_cast<int>(tau_w - static_cast<int64_t>(H) * seq_cost(b));   // < H * unit < 2^31
+        h = r / unit;
+        const int rem = r - h * unit - c;
+        t = rem < 4 ? 0 : min(n - 1, rem >> 2);
+        return static_cast<int64_t>(H) * pb[b] + static_cast<int64_t>(h) * n + t;
+    }
+    // floor(w T / W) = w qT + floor(w rT / W), with w rT < W^2; priced: the
+    // largest j with A(j) <= floor(w C / W), the last sequence whose cost
+    // prefix is at most that found by binary search (per-thread form)
     __device__ __forceinline__ int64_t range_begin(int w) const {
-        return static_cast<int64_t>(w) * qT + small_quot(static_cast<int64_t>(w) * rT, W);
+        if (c == 0) return static_cast<int64_t>(w) * qT + small_quot(static_cast<int64_t>(w) * rT, W);
+        if (w >= W) return T;
+        const int64_t tw = tau(w);
+        int lo = 0, hi = B;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (static_cast<int64_t>(H) * seq_cost(mid) <= tw) lo = mid;
+            else hi = mid;
+        }
+        int h, t;
+        return cut_in(lo, tw, h, t);
+    }
+    // priced, wave-uniform w < W, whole wave active: both ends of worker w's
+    // range from one pass of the lanes over the sequences (64 at a time,
+    // each lane testing one sequence's cost prefix against both bounds),
+    // and the sequence, head and tile of its first tile when the range is
+    // not empty
+    __device__ __forceinline__ void priced_range_uniform(int w, int64_t& begin, int64_t& end, int& b, int& h,
+                                                         int& t) const {
+        const int64_t t0 = tau(w);
+        const bool last = w + 1 >= W;
+        const int64_t t1 = last ? t0 : tau(w + 1);
+        int n0 = 0, n1 = 0;
+        for (int b0 = 0; b0 < B; b0 += 64) {
+            const int bb = b0 + (threadIdx.x & 63);
+            const int64_t sc = bb < B ? static_cast<int64_t>(H) * seq_cost(bb) : INT64_MAX;
+            const int k0 = __popcll(__ballot(sc <= t0));
+            const int k1 = __popcll(__ballot(sc <= t1));
+            n0 += k0;
+            n1 += k1;
+            if (k1 < 64) break;   // the prefix only grows: no later sequence is within either bound
+        }
+        b = __builtin_amdgcn_readfirstlane(n0 - 1);
+        begin = cut_in(b, t0, h, t);
+        if (last) {
+            end = T;
+        } else {
+            int h1, tt1;
+            end = cut_in(__builtin_amdgcn_readfirstlane(n1 - 1), t1, h1, tt1);
+        }
     }
     __device__ __forceinline__ int owner(int64_t j) const {    // valid for W <= T (quotient < W)
         return small_quot((j + 1) * W - 1, T);
@@ -106,6 +209,10 @@ struct Sched {
         const int n = tiles(b);
         if (n == 0) return 0;
         if (static_cast<int64_t>(W) > T) return n;
+        if (c != 0) {
+            const int64_t a = unit_cost_start(b, h);
+            return owner_at_cost(a + 4 * n + c) - owner_at_cost(a + 4 + c) + 1;
+        }
         const int64_t a = unit_start(b, h);
         return owner(a + n - 1) - owner(a) + 1;
     }
@@ -145,6 +252,7 @@ struct Sched {
     // (b, h)) is the k-th worker of that unit
     __device__ __forceinline__ int rank_in_unit(int w, int b, int h, int t_first) const {
         if (static_cast<int64_t>(W) > T) return t_first;
+        if (c != 0) return w - owner_at_cost(unit_cost_start(b, h) + 4 + c);
         return w - owner(unit_start(b, h));
     }
 };
@@ -206,13 +314,24 @@ struct DeviceWalker {
     // wave_uniform: begin is the same in every lane and the whole wave is active
     __device__ __forceinline__ void init(const Sched& sched, int worker, int64_t begin, int64_t end,
                                          bool wave_uniform) {
+        int b0 = 0, h0 = 0, t0 = 0;
+        if (end > begin) {
+            if (wave_uniform) sched.locate_uniform(begin, b0, h0, t0);
+            else sched.locate(begin, b0, h0, t0);
+        }
+        init_at(sched, worker, begin, end, b0, h0, t0);
+    }
+    // the same, with the first tile's sequence, head and tile already known
+    __device__ __forceinline__ void init_at(const Sched& sched, int worker, int64_t begin, int64_t end, int b0,
+                                            int h0, int t0) {
         s = &sched;
         w = worker;
         remaining = end - begin;
         at_start = true;
         if (remaining > 0) {
-            if (wave_uniform) sched.locate_uniform(begin, b, h, t);
-            else sched.locate(begin, b, h, t);
+            b = b0;
+            h = h0;
+            t = t0;
             L = sched.len[b];
             n = tiles_of(L);
             start_entry(true);

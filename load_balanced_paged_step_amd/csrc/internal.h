@@ -46,6 +46,7 @@ struct DecodeArgs {
     float qk_scale_log2;         // sm_scale * k_scale * log2(e)
     float v_scale;
     int32_t fused_merge;         // device schedule: the decode kernel merges split units itself
+    int32_t entry_price;         // device schedule: the partition's price of a unit start, quarter tiles
 };
 
 struct CombineArgs {
@@ -122,7 +123,7 @@ int launch_prologue(const PrologueArgs& a, void* stream);
 // workers' stamps (8 words each), else null (api.cpp).
 unsigned long long* trace_buffer(int n_workers);
 int launch_prefill(const PrefillArgs& a, int n_entries, int n_merge, bool kv_fp8, void* stream);
-int launch_plan_device(const int32_t* seq_lens, int batch, int num_kv_heads, int n_workers,
+int launch_plan_device(const int32_t* seq_lens, int batch, int num_kv_heads, int n_workers, int entry_price,
                        int max_pages_per_seq, int32_t* plan, void* stream);
 
 }  // namespace hpcd

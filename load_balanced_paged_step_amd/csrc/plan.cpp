@@ -5,7 +5,9 @@
 // every KV sequence is cut into uniform 64-token tiles and tiles are given to
 // the persistent grid's workers by actual work, recomputed each decode step.
 // The partition used is contiguous equal shares floor(w*T/W) of the
-// unit-major tile list; the word layout is documented in hpc_decode.h.
+// unit-major tile list; the word layout is documented in hpc_decode.h.  The
+// priced partition (this library's extension) evens out cost instead of
+// tiles, a unit's first tile costing an entry price more than the others.
 //
 // Implementation: one forward sweep.  Worker ranges are increasing and
 // contiguous, so a single cursor over the units (advanced past units that end
@@ -14,6 +16,7 @@
 
 #include "hpc_decode.h"
 
+#include <algorithm>
 #include <cstddef>
 #include <cstdint>
 #include <vector>
@@ -26,6 +29,74 @@ struct Entry {
     int32_t unit, t0, t1, slot;
 };
 
+// [start, end) tile ranges of the units that have tiles, in unit order, and
+// the total T; false for a negative length or 2^31 - 1 tiles or more
+bool unit_ranges(const int32_t* seq_lens, int32_t batch, int32_t num_kv_heads, std::vector<int64_t>& s0,
+                 std::vector<int64_t>& s1, int64_t& T) {
+    T = 0;
+    for (int32_t b = 0; b < batch; ++b) {
+        if (seq_lens[b] < 0) return false;
+        const int64_t n = (static_cast<int64_t>(seq_lens[b]) + kPage - 1) / kPage;
+        for (int32_t h = 0; h < num_kv_heads && n > 0; ++h) {
+            s0.push_back(T);
+            T += n;
+            s1.push_back(T);
+            if (T > INT32_MAX - 1) return false;
+        }
+    }
+    return true;
+}
+
+// Worker boundaries s[0..W] of the tile list.  Plain: s_w = floor(w T / W).
+// Priced by c quarter tiles: a tile costs 4 and a unit's first tile c more,
+// A(j) is the cost of the tiles before j and C = A(T), and s_w is the
+// largest j with A(j) <= floor(w C / W).  The price applies only when
+// W <= T, C >= (4 + c + 1) W (each worker's share then exceeds the costliest
+// tile, so no worker is left without one) and C < 2^31; the return value is
+// the price applied (0: plain).
+int32_t boundaries(const std::vector<int64_t>& s0, const std::vector<int64_t>& s1, int64_t T, int64_t W,
+                   int32_t price, std::vector<int64_t>& s) {
+    s.assign(static_cast<std::size_t>(W) + 1, 0);
+    const int64_t K = static_cast<int64_t>(s0.size());
+    const int64_t c = price;
+    const int64_t C = 4 * T + c * K;
+    if (c <= 0 || W > T || C < (4 + c + 1) * W || C >= (int64_t(1) << 31)) {
+        for (int64_t w = 0; w <= W; ++w) s[w] = w * T / W;
+        return 0;
+    }
+    int64_t k = 0;   // the last unit whose first tile's cost prefix is <= tau
+    for (int64_t w = 0; w <= W; ++w) {
+        const int64_t tau = w * C / W;
+        while (k + 1 < K && 4 * s0[k + 1] + c * (k + 1) <= tau) ++k;
+        // A(s0[k] + t) = 4 s0[k] + c k for t = 0, 4 (s0[k] + t) + c (k + 1) after
+        const int64_t rem = tau - (4 * s0[k] + c * k) - c;
+        const int64_t n = s1[k] - s0[k];
+        s[w] = s0[k] + (rem < 4 ? 0 : std::min(n, rem / 4));
+    }
+    return price;
+}
+
+// over the W workers of a partition: the costliest worker (its tiles plus
+// entry_cost per unit its range touches) and the entry count
+void worker_costs(const std::vector<int64_t>& s0, const std::vector<int64_t>& s1, const std::vector<int64_t>& s,
+                  double entry_cost, double& worst, int64_t& entries_total) {
+    worst = 0.0;
+    entries_total = 0;
+    const int64_t W = static_cast<int64_t>(s.size()) - 1;
+    const std::size_t U = s0.size();
+    std::size_t u = 0;
+    for (int64_t w = 0; w < W; ++w) {
+        const int64_t a = s[w], e = s[w + 1];
+        if (a == e) continue;
+        while (u < U && s1[u] <= a) ++u;
+        int64_t entries = 0;
+        for (std::size_t v = u; v < U && s0[v] < e; ++v) ++entries;
+        entries_total += entries;
+        const double cost = static_cast<double>(e - a) + entry_cost * static_cast<double>(entries);
+        if (cost > worst) worst = cost;
+    }
+}
+
 }  // namespace
 
 extern "C" int64_t hpc_decode_plan_size(int32_t batch, int32_t num_kv_heads, int32_t n_workers) {
@@ -37,8 +108,16 @@ extern "C" int64_t hpc_decode_plan_size(int32_t batch, int32_t num_kv_heads, int
 
 extern "C" int hpc_decode_plan(const int32_t* seq_lens, int32_t batch, int32_t num_kv_heads,
                                int32_t n_workers, int32_t* plan, int64_t plan_capacity) {
+    return hpc_decode_plan_priced(seq_lens, batch, num_kv_heads, n_workers, 0, plan, plan_capacity);
+}
+
+extern "C" int hpc_decode_plan_priced(const int32_t* seq_lens, int32_t batch, int32_t num_kv_heads,
+                                      int32_t n_workers, int32_t entry_price, int32_t* plan,
+                                      int64_t plan_capacity) {
     if (plan == nullptr || (batch > 0 && seq_lens == nullptr)) return HPC_ERR_NULL;
-    if (batch < 0 || num_kv_heads < 1 || n_workers < 1) return HPC_ERR_INVALID;
+    if (batch < 0 || num_kv_heads < 1 || n_workers < 1 || entry_price < 0 ||
+        entry_price > HPC_DECODE_MAX_ENTRY_PRICE)
+        return HPC_ERR_INVALID;
 
     const int64_t H = num_kv_heads;
     const int64_t U = static_cast<int64_t>(batch) * H;
@@ -58,6 +137,10 @@ extern "C" int hpc_decode_plan(const int32_t* seq_lens, int32_t batch, int32_t n
     }
     const int64_t T = start[U];
     if (T > INT32_MAX - 1) return HPC_ERR_INVALID;
+    std::vector<int64_t> s0, s1, bound;
+    int64_t T_ne = 0;
+    unit_ranges(seq_lens, batch, num_kv_heads, s0, s1, T_ne);   // valid: checked above
+    const int32_t price = boundaries(s0, s1, T, W, entry_price, bound);
 
     std::vector<Entry> entries;
     entries.reserve(static_cast<std::size_t>(W + U));
@@ -65,8 +148,8 @@ extern "C" int hpc_decode_plan(const int32_t* seq_lens, int32_t batch, int32_t n
     int64_t cursor = 0;  // first unit that may still own tiles
     for (int64_t w = 0; w < W; ++w) {
         worker_ptr[w] = static_cast<int32_t>(entries.size());
-        int64_t lo = (w * T) / W;
-        const int64_t hi = ((w + 1) * T) / W;
+        int64_t lo = bound[w];
+        const int64_t hi = bound[w + 1];
         while (lo < hi) {
             while (start[cursor + 1] <= lo) ++cursor;
             const int64_t end = hi < start[cursor + 1] ? hi : start[cursor + 1];
@@ -102,7 +185,7 @@ extern "C" int hpc_decode_plan(const int32_t* seq_lens, int32_t batch, int32_t n
     const int32_t header[HPC_PLAN_HEADER_WORDS] = {
         HPC_PLAN_VERSION, batch, num_kv_heads, n_workers, static_cast<int32_t>(T),
         static_cast<int32_t>(E), static_cast<int32_t>(n_partials), static_cast<int32_t>(n_combine),
-        HPC_DECODE_PAGE, 0, 0, 0, 0, 0, 0, 0};
+        HPC_DECODE_PAGE, price, 0, 0, 0, 0, 0, 0};
     for (int i = 0; i < HPC_PLAN_HEADER_WORDS; ++i) *p++ = header[i];
     for (int64_t w = 0; w <= W; ++w) *p++ = worker_ptr[w];
     for (const Entry& e : entries) {
@@ -214,47 +297,6 @@ extern "C" int32_t hpc_decode_static_splits(const int32_t* seq_lens, int32_t bat
     return static_cast<int32_t>(S);
 }
 
-namespace {
-
-// [start, end) tile ranges of the units that have tiles, in unit order, and
-// the total T; false for a negative length or 2^31 - 1 tiles or more
-bool unit_ranges(const int32_t* seq_lens, int32_t batch, int32_t num_kv_heads, std::vector<int64_t>& s0,
-                 std::vector<int64_t>& s1, int64_t& T) {
-    T = 0;
-    for (int32_t b = 0; b < batch; ++b) {
-        if (seq_lens[b] < 0) return false;
-        const int64_t n = (static_cast<int64_t>(seq_lens[b]) + kPage - 1) / kPage;
-        for (int32_t h = 0; h < num_kv_heads && n > 0; ++h) {
-            s0.push_back(T);
-            T += n;
-            s1.push_back(T);
-        }
-    }
-    return T <= INT32_MAX - 1;
-}
-
-// over the W workers of the balanced partition: the costliest worker (its
-// tiles plus entry_cost per unit its range touches) and the entry count
-void worker_costs(const std::vector<int64_t>& s0, const std::vector<int64_t>& s1, int64_t T, int64_t W,
-                  double entry_cost, double& worst, int64_t& entries_total) {
-    worst = 0.0;
-    entries_total = 0;
-    const std::size_t U = s0.size();
-    std::size_t u = 0;
-    for (int64_t w = 0; w < W; ++w) {
-        const int64_t a = w * T / W, e = (w + 1) * T / W;
-        if (a == e) continue;
-        while (u < U && s1[u] <= a) ++u;
-        int64_t entries = 0;
-        for (std::size_t v = u; v < U && s0[v] < e; ++v) ++entries;
-        entries_total += entries;
-        const double c = static_cast<double>(e - a) + entry_cost * static_cast<double>(entries);
-        if (c > worst) worst = c;
-    }
-}
-
-}  // namespace
-
 extern "C" int32_t hpc_decode_choose_workers(const int32_t* seq_lens, int32_t batch, int32_t num_kv_heads,
                                              int32_t min_workers, int32_t max_workers, float entry_cost) {
     if (batch > 0 && seq_lens == nullptr) return HPC_ERR_NULL;
@@ -267,10 +309,12 @@ extern "C" int32_t hpc_decode_choose_workers(const int32_t* seq_lens, int32_t ba
     if (T == 0) return max_workers;
     int32_t best = max_workers;
     double best_cost = 0.0;
+    std::vector<int64_t> bound;
     for (int32_t W = max_workers; W >= min_workers; --W) {
         double worst;
         int64_t entries;
-        worker_costs(s0, s1, T, W, entry_cost, worst, entries);
+        boundaries(s0, s1, T, W, 0, bound);
+        worker_costs(s0, s1, bound, entry_cost, worst, entries);
         if (W == max_workers || worst < best_cost * (1.0 - HPC_DECODE_MIN_GAIN) - 1e-9) {
             best = W;
             best_cost = worst;
@@ -293,10 +337,39 @@ extern "C" int32_t hpc_decode_pick_workers(const int32_t* seq_lens, int32_t batc
     if (T == 0) return w1;
     double worst;
     int64_t entries;
-    worker_costs(s0, s1, T, w1, HPC_DECODE_ENTRY_COST, worst, entries);
+    std::vector<int64_t> bound;
+    boundaries(s0, s1, T, w1, 0, bound);
+    worker_costs(s0, s1, bound, HPC_DECODE_ENTRY_COST, worst, entries);
     // dense entries (1.5 or more per worker) on an fp8 cache: two workers
     // per compute unit
     return 2 * entries >= 3 * static_cast<int64_t>(w1) ? 2 * n_cus : w1;
+}
+
+extern "C" int32_t hpc_decode_pick_entry_price(const int32_t* seq_lens, int32_t batch, int32_t num_kv_heads,
+                                               int32_t kv_dtype, int32_t n_workers) {
+    if (batch > 0 && seq_lens == nullptr) return HPC_ERR_NULL;
+    if (batch < 0 || num_kv_heads < 1 || n_workers < 1) return HPC_ERR_INVALID;
+    if (kv_dtype != HPC_KV_BF16 && kv_dtype != HPC_KV_FP8_E4M3) return HPC_ERR_UNSUPPORTED;
+    std::vector<int64_t> s0, s1;
+    int64_t T = 0;
+    if (!unit_ranges(seq_lens, batch, num_kv_heads, s0, s1, T)) return HPC_ERR_INVALID;
+    if (T == 0) return 0;
+    const double entry_cost = kv_dtype == HPC_KV_FP8_E4M3 ? HPC_DECODE_ENTRY_COST_FP8 : HPC_DECODE_ENTRY_COST;
+    std::vector<int64_t> bound;
+    double best_cost, worst;
+    int64_t entries;
+    boundaries(s0, s1, T, n_workers, 0, bound);
+    worker_costs(s0, s1, bound, entry_cost, best_cost, entries);
+    int32_t best = 0;
+    for (int32_t price : {2, 4, 8, 16}) {
+        if (boundaries(s0, s1, T, n_workers, price, bound) == 0) continue;
+        worker_costs(s0, s1, bound, entry_cost, worst, entries);
+        if (worst < best_cost * (1.0 - HPC_DECODE_MIN_GAIN) - 1e-9) {
+            best = price;
+            best_cost = worst;
+        }
+    }
+    return best;
 }
 
 extern "C" int64_t hpc_decode_plan_words(const int32_t* plan) {

@@ -127,7 +127,8 @@ def run_hip_plan(inp, plan_words, dev=None, tile_math="mfma"):
     return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
 
-def run_hip_step(inp, n_workers: int, dev=None, tile_math="mfma", fused_merge=False, workspace=None):
+def run_hip_step(inp, n_workers: int, dev=None, tile_math="mfma", fused_merge=False, workspace=None,
+                 entry_price=0):
     """One device-scheduled decode step (hpc_decode_step: schedule from the
     lengths on the GPU, decode and merge kernels, or the decode kernel alone
     with ``fused_merge``).  A given workspace is reused as it is."""
@@ -139,6 +140,7 @@ def run_hip_step(inp, n_workers: int, dev=None, tile_math="mfma", fused_merge=Fa
     lse = torch.empty(dev["q"].shape[:2], dtype=torch.float32, device="cuda")
     hd.hpc_decode_step(dev["q"], dev["k"], dev["v"], dev["bt"], dev["sl"], ws, out, lse,
                        num_kv_heads=inp.num_kv_heads, n_workers=n_workers, sm_scale=inp.sm_scale,
-                       k_scale=inp.k_scale, v_scale=inp.v_scale, tile_math=tile_math, fused_merge=fused_merge)
+                       k_scale=inp.k_scale, v_scale=inp.v_scale, tile_math=tile_math, fused_merge=fused_merge,
+                       entry_price=entry_price)
     torch.cuda.synchronize()
     return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)

@@ -59,6 +59,25 @@ int main() {
         }
         CHECK(covered == T);
         ++plans;
+        // the priced partition: same buffer bound, every tile once, no empty worker when applied
+        const int32_t price = static_cast<int32_t>(uni(0, HPC_DECODE_MAX_ENTRY_PRICE));
+        std::vector<int32_t> pplan(static_cast<std::size_t>(cap));
+        CHECK(hpc_decode_plan_priced(B ? lens.data() : nullptr, B, H, W, price, pplan.data(), cap) == HPC_OK);
+        CHECK(hpc_decode_plan_words(pplan.data()) <= cap);
+        CHECK(pplan[9] == 0 || pplan[9] == price);
+        covered = 0;
+        for (int32_t e = 0; e < pplan[5]; ++e) {
+            const int32_t* en = pplan.data() + HPC_PLAN_HEADER_WORDS + (W + 1) + 4 * e;
+            CHECK(en[1] < en[2]);
+            covered += en[2] - en[1];
+        }
+        CHECK(covered == T);
+        if (pplan[9] != 0)
+            for (int32_t w = 0; w < W; ++w) CHECK(pplan[HPC_PLAN_HEADER_WORDS + w + 1] > pplan[HPC_PLAN_HEADER_WORDS + w]);
+        const int32_t pick = hpc_decode_pick_entry_price(B ? lens.data() : nullptr, B, H,
+                                                         uni(0, 1) ? HPC_KV_BF16 : HPC_KV_FP8_E4M3, W);
+        CHECK(pick == 0 || pick == 2 || pick == 4 || pick == 8 || pick == 16);
+        ++plans;
         // the static split-KV planner
         const int32_t S = static_cast<int32_t>(uni(1, 64));
         const int64_t scap = hpc_decode_plan_static_size(B, H, S);

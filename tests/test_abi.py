@@ -77,6 +77,56 @@ def test_cpp_plan_random(lens, H, W):
     assert np.array_equal(_cpp_plan(lens, H, W), build_plan(lens, H, W))
 
 
+PRICES = (1, 2, 4, 8, 16, 64)
+
+
+@pytest.mark.parametrize("c", PRICES)
+@pytest.mark.parametrize("lens,H,W", [
+    ([37, 64, 130, 200], 1, 4), ([0, 100, 10], 2, 4), ([64, 64, 64, 640], 1, 2), ([64, 0, 192], 2, 2),
+    ([131072] + [4096] * 31, 1, 252), ([131072] + [4096] * 31, 1, 256), ([512] * 64, 1, 256),
+    ([0, 0, 0], 8, 7), ([5000] * 3, 8, 700),
+])
+def test_cpp_priced_plan_equals_oracle(lens, H, W, c):
+    got = hd.hpc_decode_plan(np.asarray(lens, dtype=np.int32), H, W, entry_price=c)
+    assert np.array_equal(got, build_plan(lens, H, W, c))
+
+
+def test_cpp_priced_plan_cost_limit():
+    """16 units of 2^25 - 1 tiles: C = 4 T + 16 c = 2^31 - 64 + 16 c, priced
+    only while below 2^31 (c <= 3).  Each worker's share then starts where
+    the cost prefix says (units of equal cost: worker w of 64 at unit w / 4)."""
+    lens = np.array([64 * (2 ** 25 - 1)], dtype=np.int32)
+    for c, applied in ((2, 2), (3, 3), (4, 0), (16, 0)):
+        words = hd.hpc_decode_plan(lens, 16, 64, entry_price=c)
+        assert int(words[9]) == applied
+        wp = words[16:16 + 65]
+        ents = words[16 + 65:16 + 65 + 4 * int(words[5])].reshape(-1, 4)
+        starts = [tuple(ents[wp[w]][:2]) for w in range(0, 64, 4)]
+        assert starts == [(w // 4, 0) for w in range(0, 64, 4)]
+
+
+@settings(max_examples=300, deadline=None)
+@given(lens=st.lists(st.integers(0, 70000), min_size=0, max_size=48), H=st.integers(1, 8),
+       W=st.integers(1, 1500), c=st.sampled_from(PRICES))
+def test_cpp_priced_plan_random(lens, H, W, c):
+    got = hd.hpc_decode_plan(np.asarray(lens, dtype=np.int32), H, W, entry_price=c)
+    assert np.array_equal(got, build_plan(lens, H, W, c))
+
+
+def test_priced_plan_errors():
+    lib = _lib.lib()
+    lens = np.array([100, 200], dtype=np.int32)
+    p = lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    buf = np.zeros(hd.hpc_decode_plan_size(2, 1, 4), dtype=np.int32)
+    q = buf.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    assert lib.hpc_decode_plan_priced(p, 2, 1, 4, 0, q, buf.size) == hd.HPC_OK
+    assert lib.hpc_decode_plan_priced(p, 2, 1, 4, hd.MAX_ENTRY_PRICE, q, buf.size) == hd.HPC_OK
+    assert lib.hpc_decode_plan_priced(p, 2, 1, 4, -1, q, buf.size) == hd.HPC_ERR_INVALID
+    assert lib.hpc_decode_plan_priced(p, 2, 1, 4, hd.MAX_ENTRY_PRICE + 1, q, buf.size) == hd.HPC_ERR_INVALID
+    assert lib.hpc_decode_plan_priced(None, 2, 1, 4, 4, q, buf.size) == hd.HPC_ERR_NULL
+    assert lib.hpc_decode_plan_priced(p, 2, 1, 4, 4, q, 3) == hd.HPC_ERR_TOO_SMALL
+
+
 @pytest.mark.parametrize("lens,H,S", [
     ([37, 64, 130, 200], 1, 2), ([0, 320], 2, 3), ([130], 1, 4), ([0, 0], 1, 8), ([1, 0, 128], 1, 1),
     ([131072] + [4096] * 31, 1, 8), ([131072] + [4096] * 31, 1, 128), ([512] * 64, 1, 4), ([5000] * 3, 8, 7),
@@ -189,6 +239,7 @@ def test_check_null_workspace_only_when_needed():
     ("num_q_heads", 0, hd.HPC_ERR_INVALID), ("num_kv_heads", 0, hd.HPC_ERR_INVALID),
     ("max_pages_per_seq", 0, hd.HPC_ERR_INVALID), ("num_pages", 0, hd.HPC_ERR_INVALID),
     ("sm_scale", float("nan"), hd.HPC_ERR_INVALID), ("v_scale", float("inf"), hd.HPC_ERR_INVALID),
+    ("entry_price", -1, hd.HPC_ERR_INVALID), ("entry_price", hd.MAX_ENTRY_PRICE + 1, hd.HPC_ERR_INVALID),
 ])
 def test_check_bad_params(field, value, code):
     f = _Fake()
@@ -293,6 +344,11 @@ def test_step_check_errors():
     assert chk(batch=0) == hd.HPC_ERR_INVALID and chk(W=0) == hd.HPC_ERR_INVALID
     assert chk(batch=5000, wsb=1 << 40) == hd.HPC_ERR_UNSUPPORTED
     assert chk(W=65537, wsb=1 << 40) == hd.HPC_ERR_UNSUPPORTED
+    for price, code in ((hd.MAX_ENTRY_PRICE, hd.HPC_OK), (hd.MAX_ENTRY_PRICE + 1, hd.HPC_ERR_INVALID),
+                        (-1, hd.HPC_ERR_INVALID)):
+        params.entry_price = price
+        assert chk() == code
+    params.entry_price = 0
     params.max_pages_per_seq = 1 << 20
     assert chk(batch=2048, wsb=1 << 40) == hd.HPC_ERR_INVALID       # tile indices beyond int32
     params.max_pages_per_seq = 4
@@ -304,10 +360,12 @@ def test_plan_device_argument_errors():
     lib = _lib.lib()
     ptr = ctypes.c_void_p(0x1000)
     cap = hd.hpc_decode_plan_size(4, 1, 8)
-    assert lib.hpc_decode_plan_device(None, 4, 1, 8, 4, ptr, cap, None) == hd.HPC_ERR_NULL
-    assert lib.hpc_decode_plan_device(ptr, 4, 1, 8, 4, ptr, cap - 1, None) == hd.HPC_ERR_TOO_SMALL
-    assert lib.hpc_decode_plan_device(ptr, 4, 1, 0, 4, ptr, cap, None) == hd.HPC_ERR_INVALID
-    assert lib.hpc_decode_plan_device(ptr, 4096, 1, 8, 4, ptr, 1 << 30, None) == hd.HPC_ERR_UNSUPPORTED
+    assert lib.hpc_decode_plan_device(None, 4, 1, 8, 0, 4, ptr, cap, None) == hd.HPC_ERR_NULL
+    assert lib.hpc_decode_plan_device(ptr, 4, 1, 8, 0, 4, ptr, cap - 1, None) == hd.HPC_ERR_TOO_SMALL
+    assert lib.hpc_decode_plan_device(ptr, 4, 1, 0, 0, 4, ptr, cap, None) == hd.HPC_ERR_INVALID
+    assert lib.hpc_decode_plan_device(ptr, 4, 1, 8, -1, 4, ptr, cap, None) == hd.HPC_ERR_INVALID
+    assert lib.hpc_decode_plan_device(ptr, 4, 1, 8, hd.MAX_ENTRY_PRICE + 1, 4, ptr, cap, None) == hd.HPC_ERR_INVALID
+    assert lib.hpc_decode_plan_device(ptr, 4096, 1, 8, 0, 4, ptr, 1 << 30, None) == hd.HPC_ERR_UNSUPPORTED
 
 
 def test_plan_workspace_bound_covers_every_plan():

@@ -13,6 +13,7 @@ import pytest
 from hypothesis import given, settings, strategies as st
 
 import load_balanced_paged_step_amd as hd
+from oracle.plan import priced_boundaries
 from workloads import WORKLOADS, workload_inputs, workload_lengths
 
 
@@ -151,3 +152,71 @@ def test_trace_window_errors():
     assert lib.hpc_decode_trace_start(ctypes.c_void_p(0x1000), 63) == hd.HPC_ERR_INVALID
     assert lib.hpc_decode_trace_start(ctypes.c_void_p(0x1000), 64) == hd.HPC_OK
     assert lib.hpc_decode_trace_stop() == hd.HPC_OK
+
+
+# ------------------------------------------------ entry price of the partition ---
+
+ENTRY_COST = {"bf16": 0.5, "fp8_e4m3": 2.0}
+
+
+def _brute_price(lens, H, W, kv):
+    """The price rule written out: each candidate price's partition (the
+    oracle's priced boundaries) costs its costliest worker's tiles plus
+    ENTRY_COST per unit its range touches; scanning 0, 2, 4, 8, 16, a price
+    replaces the best only when 1% cheaper, and a declined price is skipped."""
+    n = [-(-int(L) // 64) for L in lens for _ in range(H)]
+    units, start = [], 0
+    for k in n:
+        if k:
+            units.append((start, start + k))
+        start += k
+    if start == 0:
+        return 0
+    ce = ENTRY_COST[kv]
+    best, best_cost = None, None
+    for c in (0, 2, 4, 8, 16):
+        s, applied = priced_boundaries(n, W, c)
+        if c and not applied:
+            continue
+        worst = 0.0
+        for w in range(W):
+            a, b = s[w], s[w + 1]
+            if a < b:
+                worst = max(worst, (b - a) + ce * sum(1 for u0, u1 in units if u0 < b and u1 > a))
+        if best is None or worst < best_cost * (1 - MIN_GAIN) - 1e-9:
+            best, best_cost = c, worst
+    return best
+
+
+@pytest.mark.parametrize("cfg,W,expected", [(4, 252, 0), (4, 256, 4), (5, 512, 8), (5, 256, 8)])
+def test_pick_entry_price_on_the_decode_workloads(cfg, W, expected):
+    """The skewed batch at 252 workers fits unit boundaries exactly (price 0);
+    at 256 a small price removes second entries; the fp8 batch, with about
+    two entries per worker, takes 8 quarter tiles at either worker count."""
+    w = WORKLOADS[cfg]
+    lens = workload_lengths(cfg)
+    got = hd.hpc_decode_pick_entry_price(lens, w.num_kv_heads, w.kv_dtype, W)
+    assert got == expected == _brute_price(lens, w.num_kv_heads, W, w.kv_dtype)
+
+
+@settings(max_examples=80, deadline=None)
+@given(lens=st.lists(st.integers(0, 6000), min_size=1, max_size=12), H=st.integers(1, 4),
+       W=st.integers(1, 60), kv=st.sampled_from(["bf16", "fp8_e4m3"]))
+def test_pick_entry_price_matches_the_definition(lens, H, W, kv):
+    assert hd.hpc_decode_pick_entry_price(np.array(lens), H, kv, W) == _brute_price(lens, H, W, kv)
+
+
+def test_pick_entry_price_errors():
+    lib = hd.lib()
+    lens = np.array([100, 200], dtype=np.int32)
+    p = lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    assert lib.hpc_decode_pick_entry_price(p, 2, 1, hd.HPC_KV_BF16, 4) >= 0
+    assert lib.hpc_decode_pick_entry_price(None, 2, 1, hd.HPC_KV_BF16, 4) == hd.HPC_ERR_NULL
+    assert lib.hpc_decode_pick_entry_price(None, 0, 1, hd.HPC_KV_BF16, 4) == 0           # empty batch
+    assert lib.hpc_decode_pick_entry_price(p, -1, 1, hd.HPC_KV_BF16, 4) == hd.HPC_ERR_INVALID
+    assert lib.hpc_decode_pick_entry_price(p, 2, 0, hd.HPC_KV_BF16, 4) == hd.HPC_ERR_INVALID
+    assert lib.hpc_decode_pick_entry_price(p, 2, 1, hd.HPC_KV_BF16, 0) == hd.HPC_ERR_INVALID
+    assert lib.hpc_decode_pick_entry_price(p, 2, 1, 7, 4) == hd.HPC_ERR_UNSUPPORTED
+    bad = np.array([100, -1], dtype=np.int32)
+    assert lib.hpc_decode_pick_entry_price(bad.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), 2, 1,
+                                           hd.HPC_KV_BF16, 4) == hd.HPC_ERR_INVALID

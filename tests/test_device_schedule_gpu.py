@@ -20,7 +20,7 @@ import load_balanced_paged_step_amd as hd
 from oracle import build_plan
 from workloads import make_inputs, workload_inputs
 
-from decode_harness import announce, compare, run_hip, run_oracle, to_device
+from decode_harness import announce, compare, run_hip, run_hip_plan, run_hip_step, run_oracle, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -32,11 +32,11 @@ def _gpu():
     hd.lib()
 
 
-def _device_plan(lens, H, W, max_pages=None):
+def _device_plan(lens, H, W, max_pages=None, entry_price=0):
     lens = np.asarray(lens, dtype=np.int32)
     mp = max_pages or max(1, int((lens.max() + 63) // 64) if lens.size else 1)
     sl = torch.from_numpy(lens).cuda()
-    plan = hd.hpc_decode_plan_device(sl, H, W, mp)
+    plan = hd.hpc_decode_plan_device(sl, H, W, mp, entry_price=entry_price)
     torch.cuda.synchronize()
     words = plan.cpu().numpy()
     return words[:hd.hpc_decode_plan_words(words)]
@@ -100,14 +100,14 @@ def assert_same_as_host_planned(inp, W, a, b, plan=None):
     np.testing.assert_allclose(a[1][fin], b[1][fin], rtol=0, atol=4e-6)
 
 
-def run_step(inp, W, dev=None):
+def run_step(inp, W, dev=None, entry_price=0):
     if dev is None:
         dev = to_device(inp)
     out = torch.empty_like(dev["q"])
     lse = torch.empty(dev["q"].shape[:2], dtype=torch.float32, device="cuda")
     launch = hd.StepLauncher(dev["q"], dev["k"], dev["v"], dev["bt"], dev["sl"], out, lse,
                              num_kv_heads=inp.num_kv_heads, n_workers=W, sm_scale=inp.sm_scale,
-                             k_scale=inp.k_scale, v_scale=inp.v_scale)
+                             k_scale=inp.k_scale, v_scale=inp.v_scale, entry_price=entry_price)
     launch()
     torch.cuda.synchronize()
     return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
@@ -253,3 +253,97 @@ def test_step_at_the_size_limits(W):
     b = run_hip(inp, W, dev)
     assert_same_as_host_planned(inp, W, a, b, plan=hd.hpc_decode_plan(inp.seq_lens.numpy(), 2, W))
     compare(inp, a, run_oracle(inp), f"device step at the limits W={W}")
+
+
+# ------------------------------------------------------ priced partition ---
+
+PRICED_PLAN_CASES = [
+    ([37, 64, 130, 200], 1, 4), ([0, 100, 10], 2, 4), ([64, 64, 64, 640], 1, 2), ([64, 0, 192], 2, 2),
+    ([131072] + [4096] * 31, 1, 252), ([131072] + [4096] * 31, 1, 256), ([512] * 64, 1, 256),
+    ([5000] * 3, 8, 700), ([1] * 300, 2, 37), ([0, 5, 0, 130] * 16 + [64], 8, 40), ([0, 0, 0], 8, 7),
+]
+
+
+@pytest.mark.parametrize("c", [2, 8, 16])
+@pytest.mark.parametrize("lens,H,W", PRICED_PLAN_CASES)
+def test_device_priced_plan_equals_oracle(lens, H, W, c):
+    announce(f"device priced plan lens[:4]={lens[:4]} B={len(lens)} H={H} W={W} c={c}")
+    assert np.array_equal(_device_plan(lens, H, W, entry_price=c), build_plan(lens, H, W, c))
+
+
+def test_device_priced_plan_random_batches():
+    rng = np.random.default_rng(321)
+    for i in range(40):
+        B = int(rng.integers(1, 70))
+        H = int(rng.integers(1, 9))
+        W = int(rng.integers(1, 1200))
+        c = int(rng.choice([1, 2, 4, 8, 16, 64]))
+        lens = rng.integers(0, 20000, size=B)
+        lens[rng.random(B) < 0.2] = 0
+        announce(f"device priced plan random #{i} B={B} H={H} W={W} c={c}")
+        assert np.array_equal(_device_plan(lens, H, W, entry_price=c), build_plan(lens, H, W, c)), \
+            (lens.tolist(), H, W, c)
+
+
+@pytest.mark.parametrize("lens,H,W,c", [
+    ([64 * (2 ** 25 - 1)], 16, 64, 3),                      # C = 2^31 - 16: the largest priced cost
+    ([64 * (2 ** 25 - 1)], 16, 64, 4),                      # C = 2^31: declined
+    ([2 ** 28 - 1, 5, 2 ** 27 + 13, 0] * 4, 8, 2047, 16),   # C near 2^29.6, large quotients
+    ([64 * 2047 - 1, 1, 1, 1], 1, 2048, 8),                 # W just above T: declined
+])
+def test_device_priced_plan_extremes(lens, H, W, c):
+    """Too many tiles for the float64 oracle's walk: the device plan against the
+    host planner, which equals the oracle on every smaller case."""
+    announce(f"device priced plan extreme B={len(lens)} H={H} W={W} c={c}")
+    host = hd.hpc_decode_plan(np.asarray(lens, dtype=np.int32), H, W, entry_price=c)
+    assert np.array_equal(_device_plan(lens, H, W, entry_price=c), host)
+
+
+@pytest.mark.parametrize("cfg,W,c", [(5, 512, 8), (5, 256, 8), (4, 256, 4), (4, 252, 8), (2, 256, 16),
+                                     (3, 256, 8), (1, 3, 4)])
+def test_priced_step_equals_host_planned(cfg, W, c):
+    """The device-scheduled step with an entry price against the host-planned
+    step of the oracle's priced plan (bitwise on unsplit units) and against
+    the float64 oracle."""
+    inp = workload_inputs(cfg, poison=True)
+    dev = to_device(inp)
+    announce(f"priced device step vs host plan, workload {cfg}, W={W}, c={c}")
+    plan = build_plan(inp.seq_lens.numpy(), inp.num_kv_heads, W, c)
+    a = run_step(inp, W, dev, entry_price=c)
+    b = run_hip_plan(inp, plan, dev)
+    assert_same_as_host_planned(inp, W, a, b, plan=plan)
+    compare(inp, a, run_oracle(inp), f"priced device step workload {cfg} W={W} c={c}")
+
+
+@pytest.mark.parametrize("lens,hq,hkv,W", [
+    ([0, 37, 0, 1], 8, 1, 3), ([63, 64, 65, 127, 128, 129], 8, 1, 5), ([300, 1000, 7], 12, 3, 11),
+    ([4000, 17], 64, 8, 64), ([0, 5, 0, 130] * 16 + [64], 8, 1, 40), ([64] * 64, 16, 2, 300),
+])
+@pytest.mark.parametrize("fused", [False, True])
+def test_priced_step_edge_shapes(lens, hq, hkv, W, fused):
+    inp = make_inputs(lens, hq, hkv, "bf16", seed=len(lens) + hq + 1, poison=True)
+    announce(f"priced device step edge lens[:4]={lens[:4]} B={len(lens)} hq={hq} hkv={hkv} W={W} fused={fused}")
+    dev = to_device(inp)
+    a = run_hip_step(inp, W, dev, fused_merge=fused, entry_price=16)
+    plan = build_plan(inp.seq_lens.numpy(), hkv, W, 16)
+    b = run_hip_plan(inp, plan, dev)
+    if not fused:
+        assert_same_as_host_planned(inp, W, a, b, plan=plan)
+    compare(inp, a, run_oracle(inp), "priced device step edge")
+
+
+def test_priced_repeated_steps_with_changing_splits():
+    """One workspace reused across priced steps whose lengths change which
+    units are split, with the in-kernel merge (its counters must return to
+    zero every step)."""
+    base = make_inputs([7000, 300, 65, 4000], 16, 2, "fp8_e4m3", seed=19, max_pages_per_seq=130)
+    dev = to_device(base)
+    ws = torch.zeros(hd.hpc_decode_step_workspace_size(4, 16, 2, 64), dtype=torch.uint8, device="cuda")
+    for i, lens in enumerate(([7000, 300, 65, 4000], [7001, 0, 66, 4100], [8000, 1, 64, 8300],
+                              [100, 200, 300, 400], [0, 0, 0, 0], [7000, 300, 65, 4000])):
+        for fused in (True, False):
+            announce(f"priced repeated step {i} fused={fused} lens={lens}")
+            dev["sl"].copy_(torch.tensor(lens, dtype=torch.int32))
+            base.seq_lens = torch.tensor(lens, dtype=torch.int32)
+            got = run_hip_step(base, 64, dev, fused_merge=fused, workspace=ws, entry_price=8)
+            compare(base, got, run_oracle(base), f"priced step {i} fused={fused}")
