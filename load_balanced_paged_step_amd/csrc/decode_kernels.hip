@@ -84,6 +84,10 @@ constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw (untyped) buffer, gfx9 fam
 #define HPC_DECODE_KV_POLICY 2
 #endif
 constexpr int kPolicyStream = HPC_DECODE_KV_POLICY;   // K/V buffer-load cache policy (2: nontemporal)
+// buffer cache policy sc1: the access is coherent at agent scope, across
+// every XCD's L2 (a store writes through, a load reads the coherent copy);
+// the in-kernel merge passes partials and records between workers with it
+constexpr int kPolicyAgent = 16;
 constexpr uint32_t kSelLo = 0x05040100u;       // v_perm: low halves of (a, b) -> {a.lo, b.lo}
 constexpr uint32_t kSelHi = 0x07060302u;       // v_perm: high halves -> {a.hi, b.hi}
 // device-scheduled merge record of a unit: {workers sharing it (0: empty),
@@ -102,6 +106,14 @@ __device__ __forceinline__ To bitcast(const From& x) {
 }
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// one int32 word written / read coherently at agent scope (a relaxed atomic)
+__device__ __forceinline__ void store_agent(int32_t* p, int32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t load_agent(const int32_t* p) {
+    return __hip_atomic_load(const_cast<int32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // two E4M3FN codes (16-bit half HI of x) -> two bf16, exact
 template <bool HI>
@@ -552,7 +564,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
             for (int i = 0; i < G * 16; ++i)
                 *reinterpret_cast<u32x4*>(out + (row + (i >> 4)) * kHeadDim + 8 * (i & 15)) = u32x4{0u, 0u, 0u, 0u};
             for (int i = 0; i < G; ++i) lse[row + i] = -INFINITY;
-            merge_records[kRecordWords * u] = 0;
+            if (a.fused_merge) store_agent(merge_records + kRecordWords * u, 0);
+            else merge_records[kRecordWords * u] = 0;
         }
         if (w_begin == w_end) return;
         for (int u = u_first + static_cast<int>(threadIdx.x); u < U; u += kDecodeThreads) {
@@ -563,11 +576,17 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
             if (pu < w_begin || sched.len[b] == 0) continue;
             const int S = sched.parts(b, h);
             int32_t* rec = merge_records + kRecordWords * u;
-            rec[0] = S;
-            rec[1] = w;
-            rec[2] = S >= 2 ? 2 * w + (pu == w_begin ? 0 : 1) : -1;
-            rec[3] = static_cast<int32_t>(pu);
-            rec[4] = static_cast<int32_t>(sched.T);
+            const int32_t words[5] = {S, w, S >= 2 ? 2 * w + (pu == w_begin ? 0 : 1) : -1, static_cast<int32_t>(pu),
+                                      static_cast<int32_t>(sched.T)};
+            if (a.fused_merge) {
+                // the in-kernel merge reads them from other XCDs within this
+                // launch: stored coherently at agent scope
+#pragma unroll
+                for (int i = 0; i < 5; ++i) store_agent(rec + i, words[i]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 5; ++i) rec[i] = words[i];
+            }
         }
     }
 
@@ -647,10 +666,24 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
                     *reinterpret_cast<bf16x8*>(out + static_cast<int64_t>(row + n) * kHeadDim + dim0) = ov;
                     if (wave == 0 && g == 0) lse[row + n] = lse_val;
                 } else if (slot < a.max_partials) {   // a slot is always in range; the test keeps stray writes out
-                    float* dst = o_part + (static_cast<int64_t>(slot) * G + n) * kHeadDim + dim0;
-                    *reinterpret_cast<f32x4*>(dst) = f32x4{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
-                    *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv};
-                    if (wave == 0 && g == 0) lse_part[static_cast<int64_t>(slot) * G + n] = lse_val;
+                    const int64_t pidx = static_cast<int64_t>(slot) * G + n;
+                    const f32x4 lo4 = f32x4{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
+                    const f32x4 hi4 = f32x4{o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv};
+                    if (DEV && a.fused_merge) {
+                        // read by another worker of this launch: written through to agent scope
+                        const __amdgpu_buffer_rsrc_t ro = make_rsrc(o_part, 0xFFFFFFFFu);
+                        const uint32_t off = static_cast<uint32_t>((pidx * kHeadDim + dim0) * 4);
+                        __builtin_amdgcn_raw_buffer_store_b128(bitcast<u32x4>(lo4), ro, off, 0, kPolicyAgent);
+                        __builtin_amdgcn_raw_buffer_store_b128(bitcast<u32x4>(hi4), ro, off + 16, 0, kPolicyAgent);
+                        if (wave == 0 && g == 0)
+                            __builtin_amdgcn_raw_buffer_store_b32(bitcast<uint32_t>(lse_val), make_rsrc(lse_part, 0xFFFFFFFFu),
+                                                                  static_cast<uint32_t>(pidx * 4), 0, kPolicyAgent);
+                    } else {
+                        float* dst = o_part + pidx * kHeadDim + dim0;
+                        *reinterpret_cast<f32x4*>(dst) = lo4;
+                        *reinterpret_cast<f32x4*>(dst + 4) = hi4;
+                        if (wave == 0 && g == 0) lse_part[pidx] = lse_val;
+                    }
                 }
             }
         }
@@ -966,9 +999,19 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
                     *reinterpret_cast<bf16x4*>(out + static_cast<int64_t>(row + hh) * kHeadDim + 4 * dq) = ov;
                     if (dq == 0) lse[row + hh] = lse_val;
                 } else if (slot < a.max_partials) {   // a slot is always in range; the test keeps stray writes out
-                    float* dst = o_part + (static_cast<int64_t>(slot) * G + hh) * kHeadDim + 4 * dq;
-                    *reinterpret_cast<f32x4*>(dst) = o * inv;
-                    if (dq == 0) lse_part[static_cast<int64_t>(slot) * G + hh] = lse_val;
+                    const int64_t pidx = static_cast<int64_t>(slot) * G + hh;
+                    if (DEV && a.fused_merge) {
+                        // read by another worker of this launch: written through to agent scope
+                        __builtin_amdgcn_raw_buffer_store_b128(bitcast<u32x4>(o * inv), make_rsrc(o_part, 0xFFFFFFFFu),
+                                                               static_cast<uint32_t>((pidx * kHeadDim + 4 * dq) * 4), 0,
+                                                               kPolicyAgent);
+                        if (dq == 0)
+                            __builtin_amdgcn_raw_buffer_store_b32(bitcast<uint32_t>(lse_val), make_rsrc(lse_part, 0xFFFFFFFFu),
+                                                                  static_cast<uint32_t>(pidx * 4), 0, kPolicyAgent);
+                    } else {
+                        *reinterpret_cast<f32x4*>(o_part + pidx * kHeadDim + 4 * dq) = o * inv;
+                        if (dq == 0) lse_part[pidx] = lse_val;
+                    }
                 }
             }
         }
@@ -1017,15 +1060,20 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     }
 
     // In-kernel merge (device schedule, on request): every partial of this
-    // worker is written.  One agent-scope release makes them visible to the
-    // other dies; then, for each split unit the worker holds a share of
-    // (its first entry, and its last when that is another unit), one
-    // atomic count in the unit's merge record.  The worker that brings the
-    // count to S_u merges the unit and sets the count back to zero, so the
-    // records are ready for the next step.  No worker waits for another.
+    // worker is written.  Partials and merge records cross XCDs only through
+    // agent-coherent (sc1) stores and loads, so no L2 write-back or
+    // invalidate is needed: each wave waits until its stores have completed,
+    // and after the barrier one atomic count per split unit the worker holds
+    // a share of (its first entry, and its last when that is another unit)
+    // goes to the unit's merge record.  The worker that brings the count to
+    // S_u merges the unit and sets the count back to zero, so the records
+    // are ready for the next step.  No worker waits for another.
     if constexpr (DEV) {
         if (a.fused_merge) {
-            __syncthreads();   // every wave's partial stores precede the release below
+            // this wave's partial and record stores (agent-coherent) have completed
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
 #pragma unroll 1
             for (int k = 0; k < 2; ++k) {
                 const int u = fm_u[k];
@@ -1034,21 +1082,19 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
                 if (S < 2) continue;
                 int32_t* rec = merge_records + kRecordWords * u;
                 if (threadIdx.x == 0) {
-                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
                     const int before = __hip_atomic_fetch_add(rec + 5, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     const int last = before == S - 1;
-                    if (last) {
-                        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-                        __hip_atomic_store(rec + 5, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    }
+                    if (last) store_agent(rec + 5, 0);
                     s_last = last;
                 }
                 __syncthreads();
                 if (s_last) {
-                    // the unit's partial slots, from its record (written by its first
-                    // worker, which released it with its own partials)
-                    const int w_first = rec[1], first_slot = rec[2];
-                    const int64_t Pu = rec[3], T = rec[4];
+                    // the unit's partial slots, from its record (stored by its first
+                    // worker before that worker's count, agent-coherently)
+                    const int w_first = load_agent(rec + 1), first_slot = load_agent(rec + 2);
+                    const int64_t Pu = load_agent(rec + 3), T = load_agent(rec + 4);
+                    const __amdgpu_buffer_rsrc_t ro = make_rsrc(o_part, 0xFFFFFFFFu);
+                    const __amdgpu_buffer_rsrc_t rl = make_rsrc(lse_part, 0xFFFFFFFFu);
                     auto slot_of = [&](int kk) -> int {
                         if (kk == 0) return first_slot;
                         if (static_cast<int64_t>(a.n_workers) <= T) return 2 * (w_first + kk);
@@ -1067,8 +1113,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
                                 const int i = i0 + j;
                                 const int slot = slot_of(i < S ? i : 0);
                                 const int64_t pidx = (slot < a.max_partials ? static_cast<int64_t>(slot) : 0) * G + hh;
-                                lv[j] = (i < S && slot < a.max_partials) ? lse_part[pidx] * kLog2e : -INFINITY;
-                                ov[j] = *reinterpret_cast<const f32x4*>(o_part + pidx * kHeadDim + 4 * dq);
+                                const float lp = bitcast<float>(__builtin_amdgcn_raw_buffer_load_b32(
+                                    rl, static_cast<uint32_t>(pidx * 4), 0, kPolicyAgent));
+                                lv[j] = (i < S && slot < a.max_partials) ? lp * kLog2e : -INFINITY;
+                                ov[j] = bitcast<f32x4>(__builtin_amdgcn_raw_buffer_load_b128(
+                                    ro, static_cast<uint32_t>((pidx * kHeadDim + 4 * dq) * 4), 0, kPolicyAgent));
                             }
                             float mk = mm;
 #pragma unroll
