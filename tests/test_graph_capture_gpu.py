@@ -20,7 +20,7 @@ def _np(out, lse):
     return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
 
-@pytest.mark.parametrize("mode", ["mfma", "mfma+fused_merge", "valu", "valu+fused_merge"])
+@pytest.mark.parametrize("mode", ["mfma", "mfma+fused_merge", "valu", "valu+fused_merge", "mfma+price"])
 @pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
 def test_graph_replays_match_eager_over_changing_lengths(kv, mode):
     """Also with the VALU tile math and with the in-kernel merge, whose
@@ -29,6 +29,7 @@ def test_graph_replays_match_eager_over_changing_lengths(kv, mode):
     same order, so replays stay bitwise equal to eager steps)."""
     tile_math = "valu" if mode.startswith("valu") else "mfma"
     fused = mode.endswith("fused_merge")
+    price = 8 if mode.endswith("price") else 0
     hq, hkv, W = (16, 2, 64) if kv == "bf16" else (64, 8, 48)
     base = make_inputs([7000, 300, 65, 4000], hq, hkv, kv, seed=29, max_pages_per_seq=130)
     dev = to_device(base)
@@ -38,7 +39,7 @@ def test_graph_replays_match_eager_over_changing_lengths(kv, mode):
     s = torch.cuda.Stream()
     launch = hd.StepLauncher(dev["q"], dev["k"], dev["v"], dev["bt"], sl, out, lse, num_kv_heads=hkv, n_workers=W,
                              sm_scale=base.sm_scale, k_scale=base.k_scale, v_scale=base.v_scale, stream=s,
-                             tile_math=tile_math, fused_merge=fused)
+                             tile_math=tile_math, fused_merge=fused, entry_price=price)
     with torch.cuda.stream(s):
         launch()                                  # warm-up outside the capture
     torch.cuda.synchronize()

@@ -45,6 +45,36 @@ def test_plan_attn_equals_attn(lens, hq, hkv, W, kv):
     compare(inp, got, run_oracle(inp), "plan_attn")
 
 
+@pytest.mark.parametrize("lens,hq,hkv,W,kv,c", [
+    ([7000, 300, 0, 4000], 16, 2, 64, "bf16", 8), ([3000, 65, 129, 5000], 64, 8, 40, "fp8_e4m3", 16),
+])
+def test_plan_attn_with_entry_price(lens, hq, hkv, W, kv, c):
+    """The one-call step plans with params.entry_price: its plan words are
+    the priced planner's (the price applied, header word 9), and the result
+    is bitwise that of hpc_decode_attn with the oracle's priced plan."""
+    from oracle import build_plan
+    from decode_harness import run_hip_plan
+    inp = make_inputs(lens, hq, hkv, kv, seed=len(lens) + W + c, poison=True)
+    announce(f"plan_attn priced lens={lens} hq={hq} hkv={hkv} W={W} {kv} c={c}")
+    dev = to_device(inp)
+    out = torch.empty_like(dev["q"])
+    lse = torch.empty(dev["q"].shape[:2], dtype=torch.float32, device="cuda")
+    cap = hd.hpc_decode_plan_size(len(lens), hkv, W)
+    host = torch.empty(cap, dtype=torch.int32, pin_memory=True)
+    plan_dev = torch.empty(cap, dtype=torch.int32, device="cuda")
+    ws = torch.empty(hd.hpc_decode_plan_workspace_bound(len(lens), hq, hkv, W), dtype=torch.uint8, device="cuda")
+    words = hd.hpc_decode_plan_attn(inp.seq_lens, host, plan_dev, dev["q"], dev["k"], dev["v"], dev["bt"],
+                                    dev["sl"], ws, out, lse, num_kv_heads=hkv, n_workers=W,
+                                    sm_scale=inp.sm_scale, k_scale=inp.k_scale, v_scale=inp.v_scale, entry_price=c)
+    torch.cuda.synchronize()
+    got = _np(out, lse)
+    plan = build_plan(inp.seq_lens.numpy(), hkv, W, c)
+    assert int(plan[9]) == c and np.array_equal(words, plan)
+    ref = run_hip_plan(inp, plan, dev)
+    assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1])
+    compare(inp, got, run_oracle(inp), "plan_attn priced")
+
+
 @pytest.mark.parametrize("in_place", [False, True])
 def test_launcher_runs_ahead_over_changing_lengths(in_place):
     """Steps queued back to back with no host synchronisation, each with other

@@ -26,11 +26,11 @@ def _gpu():
     hd.lib()
 
 
-def _step(inp, dev, W, noalloc, tile_math="mfma"):
+def _step(inp, dev, W, noalloc, tile_math="mfma", entry_price=0):
     out = torch.empty_like(dev["q"])
     lse = torch.empty(dev["q"].shape[:2], dtype=torch.float32, device="cuda")
     kw = dict(num_kv_heads=inp.num_kv_heads, n_workers=W, sm_scale=inp.sm_scale, k_scale=inp.k_scale,
-              v_scale=inp.v_scale, tile_math=tile_math)
+              v_scale=inp.v_scale, tile_math=tile_math, entry_price=entry_price)
     if noalloc:
         hd.hpc_decode_step_noalloc(dev["q"], dev["k"], dev["v"], dev["bt"], dev["sl"], out, lse, **kw)
     else:
@@ -60,6 +60,18 @@ def test_two_calls_second_smaller(first, second, W):
         ref = _step(inp, dev, W, noalloc=False)
         _same(got, ref, f"workload {cfg} W={W}")
         compare(inp, got, run_oracle(inp), f"no-alloc workload {cfg} W={W}")
+
+
+def test_two_priced_calls_second_smaller():
+    """With the partition's entry price (the fp8 batch's rule price, 8), the
+    no-allocation step equals hpc_decode_step bitwise, twice in a row."""
+    for cfg in (5, 2):
+        inp = workload_inputs(cfg, poison=True)
+        dev = to_device(inp)
+        announce(f"no-alloc priced step, workload {cfg}, W=512")
+        got = _step(inp, dev, 512, noalloc=True, entry_price=8)
+        _same(got, _step(inp, dev, 512, noalloc=False, entry_price=8), f"priced workload {cfg}")
+        compare(inp, got, run_oracle(inp), f"no-alloc priced workload {cfg}")
 
 
 def test_shrinking_edge_batches_and_valu():
