@@ -151,7 +151,7 @@ struct Sched {
         const int n = tiles(b);
         const int unit = 4 * n + c;
         const int r = static_cast<int>(tau_w - static_cast<int64_t>(H) * seq_cost(b));   // < H * unit < 2^31
-        h = r / unit;
+        h = small_quot(r, unit);   // < H
         const int rem = r - h * unit - c;
         t = rem < 4 ? 0 : min(n - 1, rem >> 2);
         return static_cast<int64_t>(H) * pb[b] + static_cast<int64_t>(h) * n + t;
