@@ -146,8 +146,10 @@ int hpc_decode_plan(const int32_t* seq_lens, int32_t batch, int32_t num_kv_heads
                     int32_t n_workers, int32_t* plan, int64_t plan_capacity);
 
 /*
- * The scheduler above with the partition priced (this library's extension;
- * the pages spread tiles only).  A worker pays for every unit it starts as
+ * The scheduler above with the partition priced.  It extends the rule of
+ * §Attention Backend: Dynamic Load-Balanced Scheduling ("vLLM x HPC-Ops:
+ * High-Performance Attention and MoE Backends from Tencent Hunyuan"), which
+ * spreads tiles by actual work; the pages price tiles only.  A worker pays for every unit it starts as
  * well as for its tiles: the entry's end, the Q reload and, for a split
  * unit, a partial.  Tile j costs 4 (quarter tiles), plus entry_price when it
  * is the first tile of its unit; with A(j) the cost of tiles 0 .. j-1 and
@@ -220,7 +222,10 @@ int32_t hpc_decode_choose_workers(const int32_t* seq_lens, int32_t batch, int32_
  * fastest at 8 quarter tiles per unit start, at W = 256 and at W = 512). */
 #define HPC_DECODE_ENTRY_COST_FP8 2.0f
 /* Worker count for a device-scheduled step on a GPU with n_cus compute
- * units (>= 2), pure host code.  W1 = hpc_decode_choose_workers over
+ * units (>= 2), pure host code: the size of the persistent grid that keeps
+ * every compute unit busy (§Attention Backend: Dynamic Load-Balanced
+ * Scheduling, "vLLM x HPC-Ops: High-Performance Attention and MoE Backends
+ * from Tencent Hunyuan").  W1 = hpc_decode_choose_workers over
  * [n_cus / 2, n_cus] with HPC_DECODE_ENTRY_COST.  On an fp8 cache whose
  * W1-worker partition has 1.5 entries per worker or more, it returns
  * 2 n_cus instead: two co-resident workgroups per compute unit then hide
@@ -236,7 +241,9 @@ int32_t hpc_decode_pick_workers(const int32_t* seq_lens, int32_t batch, int32_t 
                                 int32_t n_cus);
 
 /* Entry price for a step of n_workers workers (the params field
- * entry_price), pure host code.  Among the prices 0, 2, 4, 8 and 16 quarter
+ * entry_price), pure host code; the price extends the work-based tile
+ * spreading of §Attention Backend: Dynamic Load-Balanced Scheduling ("vLLM
+ * x HPC-Ops ...").  Among the prices 0, 2, 4, 8 and 16 quarter
  * tiles, each partition (hpc_decode_plan_priced) is priced by its costliest
  * worker, as its tiles plus an entry cost per unit its range touches
  * (HPC_DECODE_ENTRY_COST on a bf16 cache, HPC_DECODE_ENTRY_COST_FP8 on fp8).
@@ -259,8 +266,10 @@ int32_t hpc_decode_pick_entry_price(const int32_t* seq_lens, int32_t batch, int3
 int32_t hpc_decode_static_splits(const int32_t* seq_lens, int32_t batch, int32_t num_kv_heads, int32_t n_cus,
                                  int32_t max_splits);
 
-/* Words actually used by a plan written by hpc_decode_plan (from its header),
- * or a negative status for a NULL pointer or a malformed header. */
+/* Words actually used by a plan written by hpc_decode_plan (the work list
+ * of §Attention Backend: Dynamic Load-Balanced Scheduling, "vLLM x HPC-Ops
+ * ..."; from its header), or a negative status for a NULL pointer or a
+ * malformed header. */
 int64_t hpc_decode_plan_words(const int32_t* plan);
 
 /*
@@ -310,7 +319,9 @@ int hpc_decode_attn(const hpc_decode_params* params, const void* q, const void* 
                     int64_t workspace_bytes, void* out, float* lse, void* stream);
 
 /*
- * The host-side checks of hpc_decode_attn alone, with the same arguments
+ * The host-side checks of hpc_decode_attn (the decode step of §Attention
+ * Backend: Dynamic Load-Balanced Scheduling, "vLLM x HPC-Ops ...") alone,
+ * with the same arguments
  * (no stream): returns the status hpc_decode_attn would return before
  * launching anything.  Never calls HIP and never dereferences device pointers.
  */
@@ -320,7 +331,9 @@ int hpc_decode_check(const hpc_decode_params* params, const void* q, const void*
                      int64_t workspace_bytes, const void* out, const float* lse);
 
 /*
- * Workspace, in bytes, that is enough for hpc_decode_attn under any plan of
+ * Workspace, in bytes, that is enough for hpc_decode_attn (the split-KV
+ * partials of §Attention Decode under Mixed-Length Batches, "vLLM x HPC-Ops
+ * ...") under any plan of
  * this batch size and worker count (a plan has at most W + B*H_kv - 1
  * entries, so at most that many partial slots).  Negative status for
  * batch < 0, n_workers < 1 or heads that do not group.
@@ -396,13 +409,16 @@ int hpc_decode_step(const hpc_decode_params* params, int32_t batch, int32_t n_wo
                     const int32_t* seq_lens, void* workspace, int64_t workspace_bytes, void* out,
                     float* lse, void* stream);
 
-/* The host-side checks of hpc_decode_step alone (never calls HIP). */
+/* The host-side checks of hpc_decode_step (§Attention Backend: Dynamic
+ * Load-Balanced Scheduling, "vLLM x HPC-Ops ...") alone (never calls HIP). */
 int hpc_decode_step_check(const hpc_decode_params* params, int32_t batch, int32_t n_workers,
                           const void* q, const void* k_cache, const void* v_cache,
                           const int32_t* block_table, const int32_t* seq_lens, const void* workspace,
                           int64_t workspace_bytes, const void* out, const float* lse);
 
-/* Workspace bytes hpc_decode_step needs for any lengths: P = 2 W partial
+/* Workspace bytes hpc_decode_step needs for any lengths (the partials of
+ * sequences split over workers, which the pages' split-KV decode merges:
+ * §Attention Decode under Mixed-Length Batches, "vLLM x HPC-Ops ..."): P = 2 W partial
  * slots (a worker's first and last entries are the only ones that can be
  * split, and they use slots 2w and 2w + 1): fp32 outputs [P][G][128], then
  * (256-byte aligned) fp32 lse [P][G], then (aligned) int32 merge records
@@ -442,7 +458,8 @@ int hpc_decode_step_noalloc(const hpc_decode_params* params, int32_t batch, int3
 int64_t hpc_decode_step_noalloc_max_bytes(void);
 
 /*
- * The device-derived schedule written out on `stream` into device `plan`
+ * The device-derived schedule (§Attention Backend: Dynamic Load-Balanced
+ * Scheduling, "vLLM x HPC-Ops ...") written out on `stream` into device `plan`
  * (int32 words, capacity >= hpc_decode_plan_size) in exactly the layout of
  * hpc_decode_plan_priced with the same entry_price, so the two can be
  * compared word for word.  One
@@ -479,14 +496,15 @@ int hpc_decode_profile_stop(double* decode_ms, double* combine_ms, int32_t* n_ca
  * in-kernel merge done); then the worker's tile count (device schedule; 0
  * with a host plan), its entry count, and where it ran: the XCC_ID hardware
  * register in the high 32 bits, HW_ID (CU, shader array and engine ids) in
- * the low 32.  Workers without tiles leave
- * their words untouched.  Each launch overwrites the buffer (device memory,
- * caller-owned, valid while the window is on); a launch with more workers
- * than it holds records nothing.  Stamps of workers on different XCDs are
- * not comparable (their clocks differ by up to about 2 us); durations
- * within one worker are.  Outside the window the kernel only tests a null
- * pointer at each phase boundary.  Errors: HPC_ERR_NULL, HPC_ERR_INVALID
- * (bytes < 64).  No HIP call.
+ * the low 32.  Workers without tiles leave their words untouched.  Each
+ * launch overwrites the buffer (device memory, caller-owned, valid while
+ * the window is on); a launch with more workers than it holds records
+ * nothing.  Stamps of workers on different XCDs are not comparable (their
+ * clocks differ by up to about 2 us); durations within one worker are.
+ * Inside the window the launches use a separate instantiation of the decode
+ * kernel that takes the stamps; outside it the untraced kernel runs, with
+ * no trace code at all.  Errors: HPC_ERR_NULL, HPC_ERR_INVALID (bytes <
+ * 64).  No HIP call.
  */
 int hpc_decode_trace_start(void* device_buffer, int64_t bytes);
 int hpc_decode_trace_stop(void);
