@@ -67,6 +67,18 @@ __device__ __forceinline__ To bitcast(const From& x) {
     return __builtin_bit_cast(To, x);
 }
 
+// max of x over lanes l and l ^ 16 (l ^ 32): the lane-swap instructions put
+// each lane's value and its partner's in the two results, in VALU, where a
+// shuffle would take a round trip through the LDS unit
+__device__ __forceinline__ float max_xor16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(bitcast<uint32_t>(x), bitcast<uint32_t>(x), false, false);
+    return fmaxf(bitcast<float>(r[0]), bitcast<float>(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(bitcast<uint32_t>(x), bitcast<uint32_t>(x), false, false);
+    return fmaxf(bitcast<float>(r[0]), bitcast<float>(r[1]));
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kRsrcWord3);
 }
@@ -301,8 +313,7 @@ prefill_kernel(PrefillArgs a) {
             for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) mt = fmaxf(mt, sc[r][kb][i]);
-            mt = fmaxf(mt, __shfl_xor(mt, 16));
-            mt = fmaxf(mt, __shfl_xor(mt, 32));
+            mt = max_xor32(max_xor16(mt));
             const float m_new = fmaxf(m[r], mt);
             const float mc = (m_new == -INFINITY) ? 0.f : m_new * c;   // the new max, scaled
             const float alpha = __builtin_amdgcn_exp2f(m[r] * c - mc);
