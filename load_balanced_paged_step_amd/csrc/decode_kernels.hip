@@ -84,10 +84,6 @@ constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw (untyped) buffer, gfx9 fam
 #define HPC_DECODE_KV_POLICY 2
 #endif
 constexpr int kPolicyStream = HPC_DECODE_KV_POLICY;   // K/V buffer-load cache policy (2: nontemporal)
-// buffer cache policy sc1: the access is coherent at agent scope, across
-// every XCD's L2 (a store writes through, a load reads the coherent copy);
-// the in-kernel merge passes partials and records between workers with it
-constexpr int kPolicyAgent = 16;
 constexpr uint32_t kSelLo = 0x05040100u;       // v_perm: low halves of (a, b) -> {a.lo, b.lo}
 constexpr uint32_t kSelHi = 0x07060302u;       // v_perm: high halves -> {a.hi, b.hi}
 // device-scheduled merge record of a unit: {workers sharing it (0: empty),
@@ -107,12 +103,47 @@ __device__ __forceinline__ To bitcast(const From& x) {
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-// one int32 word written / read coherently at agent scope (a relaxed atomic)
-__device__ __forceinline__ void store_agent(int32_t* p, int32_t v) {
+// x over lanes l and l ^ 16 (l ^ 32), combined: the lane-swap instructions
+// put each lane's value and its partner's in the two results, in VALU,
+// where a shuffle would take a round trip through the LDS unit
+__device__ __forceinline__ uint2 swap_xor16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(bitcast<uint32_t>(x), bitcast<uint32_t>(x), false, false);
+    return uint2{r[0], r[1]};
+}
+__device__ __forceinline__ uint2 swap_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(bitcast<uint32_t>(x), bitcast<uint32_t>(x), false, false);
+    return uint2{r[0], r[1]};
+}
+__device__ __forceinline__ float max_xor16(float x) {
+    const uint2 r = swap_xor16(x);
+    return fmaxf(bitcast<float>(r.x), bitcast<float>(r.y));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+    const uint2 r = swap_xor32(x);
+    return fmaxf(bitcast<float>(r.x), bitcast<float>(r.y));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+    const uint2 r = swap_xor16(x);
+    return bitcast<float>(r.x) + bitcast<float>(r.y);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+    const uint2 r = swap_xor32(x);
+    return bitcast<float>(r.x) + bitcast<float>(r.y);
+}
+
+// buffer cache policy sc1: the access is coherent at agent scope, across
+// every XCD's L2 (a store writes through, a load reads the coherent copy)
+constexpr int kPolicyAgent = 16;
+
+// one word written / read coherently at agent scope (a relaxed atomic: a
+// global store or load with sc1)
+template <typename T>
+__device__ __forceinline__ void store_agent(T* p, T v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ int32_t load_agent(const int32_t* p) {
-    return __hip_atomic_load(const_cast<int32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+template <typename T>
+__device__ __forceinline__ T load_agent(const T* p) {
+    return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // two E4M3FN codes (16-bit half HI of x) -> two bf16, exact
@@ -336,7 +367,6 @@ struct DecodeScalars {
     int32_t max_partials;   // partial slots the workspace holds
     float qk_scale_log2, v_scale;
     int32_t n_workers;      // the grid size (passed so no hidden argument is read)
-    int32_t fused_merge;    // device schedule: split units merged by their last-arriving worker
     int32_t entry_price;    // device schedule: the partition's price of a unit start (quarter tiles)
 };
 
@@ -350,7 +380,10 @@ __device__ __forceinline__ void fetch_args(A& a, B& b, C& c, D& d) {
     asm("" : "+s"(a), "+s"(b), "+s"(c), "+s"(d));
 }
 
-template <int KV, int PF, int NT, bool DEV, bool VALU, bool TRACE>
+// FUSED (device schedule only): the in-kernel merge of split units, as its
+// own instantiation, so that the default kernels carry none of its code or
+// register pressure
+template <int KV, int PF, int NT, bool DEV, bool VALU, bool TRACE, bool FUSED>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     const __bf16* __restrict__ q, const char* __restrict__ kcache, const char* __restrict__ vcache,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
@@ -358,6 +391,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     __bf16* __restrict__ out, float* __restrict__ lse, float* __restrict__ o_part,
     float* __restrict__ lse_part, int32_t* __restrict__ merge_records, unsigned long long* __restrict__ stamps,
     DecodeScalars a) {
+    static_assert(DEV || !FUSED, "the in-kernel merge needs the device schedule");
     // entry ends: register i of every wave's eight accumulators, as two
     // 16-byte halves per lane, so each wave stores and loads whole f32x4s
     // entry ends (MFMA tile math): up to kPending entries' states wait in
@@ -438,7 +472,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
         if (w_begin < w_end) {
             dwalk.init_at(sched, w, w_begin, w_end, b0, h0, t0);
             u_first = dwalk.b * Hkv + dwalk.h;    // the unit of the worker's first tile
-            if (a.fused_merge) {
+            if constexpr (FUSED) {
                 int bB, hB, tB;
                 sched.locate_uniform(w_end - 1, bB, hB, tB);
                 fm_u[0] = u_first;
@@ -564,7 +598,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
             for (int i = 0; i < G * 16; ++i)
                 *reinterpret_cast<u32x4*>(out + (row + (i >> 4)) * kHeadDim + 8 * (i & 15)) = u32x4{0u, 0u, 0u, 0u};
             for (int i = 0; i < G; ++i) lse[row + i] = -INFINITY;
-            if (a.fused_merge) store_agent(merge_records + kRecordWords * u, 0);
+            if constexpr (FUSED) store_agent(merge_records + kRecordWords * u, 0);
             else merge_records[kRecordWords * u] = 0;
         }
         if (w_begin == w_end) return;
@@ -578,7 +612,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
             int32_t* rec = merge_records + kRecordWords * u;
             const int32_t words[5] = {S, w, S >= 2 ? 2 * w + (pu == w_begin ? 0 : 1) : -1, static_cast<int32_t>(pu),
                                       static_cast<int32_t>(sched.T)};
-            if (a.fused_merge) {
+            if constexpr (FUSED) {
                 // the in-kernel merge reads them from other XCDs within this
                 // launch: stored coherently at agent scope
 #pragma unroll
@@ -602,8 +636,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     // the wave goes on without waiting for the others.
     int npend = 0;
     auto deposit = [&](const TileInfo& ts) {
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
+        l = sum_xor32(sum_xor16(l));
         const int p = npend;
         s_m[p][wave][lane] = m;
         s_l[p][wave][lane] = l;
@@ -669,7 +702,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
                     const int64_t pidx = static_cast<int64_t>(slot) * G + n;
                     const f32x4 lo4 = f32x4{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
                     const f32x4 hi4 = f32x4{o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv};
-                    if (DEV && a.fused_merge) {
+                    if constexpr (FUSED) {
                         // read by another worker of this launch: written through to agent scope
                         const __amdgpu_buffer_rsrc_t ro = make_rsrc(o_part, 0xFFFFFFFFu);
                         const uint32_t off = static_cast<uint32_t>((pidx * kHeadDim + dim0) * 4);
@@ -718,8 +751,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
                 mt = fmaxf(mt, sc[tt][i]);
             }
         }
-        mt = fmaxf(mt, __shfl_xor(mt, 16));
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        mt = max_xor32(max_xor16(mt));
         const float m_new = fmaxf(m, mt);
         const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
         const float alpha = __builtin_amdgcn_exp2f(m - m_use);
@@ -1000,7 +1032,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
                     if (dq == 0) lse[row + hh] = lse_val;
                 } else if (slot < a.max_partials) {   // a slot is always in range; the test keeps stray writes out
                     const int64_t pidx = static_cast<int64_t>(slot) * G + hh;
-                    if (DEV && a.fused_merge) {
+                    if constexpr (FUSED) {
                         // read by another worker of this launch: written through to agent scope
                         __builtin_amdgcn_raw_buffer_store_b128(bitcast<u32x4>(o * inv), make_rsrc(o_part, 0xFFFFFFFFu),
                                                                static_cast<uint32_t>((pidx * kHeadDim + 4 * dq) * 4), 0,
@@ -1059,7 +1091,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
         if (npend > 0) merge_pending();
     }
 
-    // In-kernel merge (device schedule, on request): every partial of this
+    // In-kernel merge (the FUSED instantiation): every partial of this
     // worker is written.  Partials and merge records cross XCDs only through
     // agent-coherent (sc1) stores and loads, so no L2 write-back or
     // invalidate is needed: each wave waits until its stores have completed,
@@ -1068,8 +1100,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     // goes to the unit's merge record.  The worker that brings the count to
     // S_u merges the unit and sets the count back to zero, so the records
     // are ready for the next step.  No worker waits for another.
-    if constexpr (DEV) {
-        if (a.fused_merge) {
+    if constexpr (FUSED) {
+        {
             // this wave's partial and record stores (agent-coherent) have completed
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
             __builtin_amdgcn_s_waitcnt(0);
@@ -1090,7 +1122,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
                 __syncthreads();
                 if (s_last) {
                     // the unit's partial slots, from its record (stored by its first
-                    // worker before that worker's count, agent-coherently)
+                    // worker, agent-coherently, before that worker's count), and
+                    // the partials, read coherently too: no L2 invalidate
                     const int w_first = load_agent(rec + 1), first_slot = load_agent(rec + 2);
                     const int64_t Pu = load_agent(rec + 3), T = load_agent(rec + 4);
                     const __amdgpu_buffer_rsrc_t ro = make_rsrc(o_part, 0xFFFFFFFFu);
@@ -1421,11 +1454,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_device_kernel(const int32_t
 constexpr int kPrefetchBf16 = HPC_DECODE_PREFETCH_BF16;
 constexpr int kPrefetchFp8 = HPC_DECODE_PREFETCH_FP8;
 
-template <int KV, int PF, bool DEV, bool VALU>
-void launch_decode_t(const DecodeArgs& a, int n_workers, size_t lds, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+template <int KV, int PF, bool DEV, bool VALU, bool FUSED>
+void launch_decode_f(const DecodeArgs& a, int n_workers, size_t lds, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     const DecodeScalars sc{a.batch,        a.num_kv_heads,  a.group,   a.max_pages_per_seq, a.num_pages,
-                           a.max_partials, a.qk_scale_log2, a.v_scale, n_workers, a.fused_merge,
-                           a.entry_price};
+                           a.max_partials, a.qk_scale_log2, a.v_scale, n_workers, a.entry_price};
     constexpr int kTilesPerSlot = KV == HPC_KV_FP8_E4M3 ? HPC_DECODE_PAIR_FP8 + 1 : 1;
     unsigned long long* const stamps = trace_buffer(n_workers);
     const auto q = static_cast<const __bf16*>(a.q);
@@ -1433,15 +1465,26 @@ void launch_decode_t(const DecodeArgs& a, int n_workers, size_t lds, hipStream_t
     const auto v = static_cast<const char*>(a.v);
     const auto out = static_cast<__bf16*>(a.out);
     if (stamps)
-        hipExtLaunchKernelGGL((decode_kernel<KV, PF, kTilesPerSlot, DEV, VALU, true>), dim3(n_workers),
+        hipExtLaunchKernelGGL((decode_kernel<KV, PF, kTilesPerSlot, DEV, VALU, true, FUSED>), dim3(n_workers),
                               dim3(kDecodeThreads), static_cast<std::uint32_t>(lds), s, e0, e1, 0u, q, k, v,
                               a.block_table, a.seq_lens, a.worker_ptr, a.entries, out, a.lse, a.o_part, a.lse_part,
                               a.merge_records, stamps, sc);
     else
-        hipExtLaunchKernelGGL((decode_kernel<KV, PF, kTilesPerSlot, DEV, VALU, false>), dim3(n_workers),
+        hipExtLaunchKernelGGL((decode_kernel<KV, PF, kTilesPerSlot, DEV, VALU, false, FUSED>), dim3(n_workers),
                               dim3(kDecodeThreads), static_cast<std::uint32_t>(lds), s, e0, e1, 0u, q, k, v,
                               a.block_table, a.seq_lens, a.worker_ptr, a.entries, out, a.lse, a.o_part, a.lse_part,
                               a.merge_records, stamps, sc);
+}
+
+template <int KV, int PF, bool DEV, bool VALU>
+void launch_decode_t(const DecodeArgs& a, int n_workers, size_t lds, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+    if constexpr (DEV) {
+        if (a.fused_merge) {
+            launch_decode_f<KV, PF, true, VALU, true>(a, n_workers, lds, s, e0, e1);
+            return;
+        }
+    }
+    launch_decode_f<KV, PF, DEV, VALU, false>(a, n_workers, lds, s, e0, e1);
 }
 
 }  // namespace

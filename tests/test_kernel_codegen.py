@@ -76,7 +76,7 @@ def ring_waits(tmp_path_factory):
 
 
 def _device_scheduled(name: str) -> bool:
-    # decode_kernel<int KV, int PF, int NT, bool DEV, bool VALU, bool TRACE>
+    # decode_kernel<int KV, int PF, int NT, bool DEV, bool VALU, bool TRACE, bool FUSED>
     return re.search(r"decode_kernelI(?:Li\d+E)+Lb1E", name) is not None
 
 
@@ -88,13 +88,19 @@ def _traced(name: str) -> bool:
     return re.search(r"decode_kernelI(?:Li\d+E)+Lb[01]ELb[01]ELb1E", name) is not None
 
 
-def test_eight_decode_kernels_and_their_traced_twins(ring_waits):
-    # bf16 / fp8 x host plan / device schedule x MFMA / VALU tile math, each
-    # also as the tracing-window instantiation
+def _fused(name: str) -> bool:
+    return re.search(r"decode_kernelI(?:Li\d+E)+Lb[01]ELb[01]ELb[01]ELb1E", name) is not None
+
+
+def test_decode_kernels_and_their_traced_twins(ring_waits):
+    # bf16 / fp8 x host plan / device schedule x MFMA / VALU tile math, plus
+    # the device-scheduled in-kernel-merge variants, each also as the
+    # tracing-window instantiation
     plain = [n for n in ring_waits if not _traced(n)]
-    assert len(plain) == 8 and len(ring_waits) == 16, list(ring_waits)
-    assert sum(_device_scheduled(n) for n in plain) == 4
-    assert sum(_valu(n) for n in plain) == 4
+    assert len(plain) == 12 and len(ring_waits) == 24, list(ring_waits)
+    assert sum(_device_scheduled(n) for n in plain) == 8
+    assert sum(_valu(n) for n in plain) == 6
+    assert sum(_fused(n) for n in plain) == 4 and all(_device_scheduled(n) for n in plain if _fused(n))
 
 
 def test_device_scheduled_ring_keeps_a_tile_in_flight(ring_waits):
