@@ -318,16 +318,15 @@ prefill_kernel(PrefillArgs a) {
             const float mc = (m_new == -INFINITY) ? 0.f : m_new * c;   // the new max, scaled
             const float alpha = __builtin_amdgcn_exp2f(m[r] * c - mc);
             m[r] = m_new;
-            float psum = 0.f;
-            float p[4][4];
+            float p[4][4], ps[4];
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    p[kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r][kb][i], c, -mc));
-                    psum += p[kb][i];
-                }
+                for (int i = 0; i < 4; ++i) p[kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r][kb][i], c, -mc));
+                ps[kb] = (p[kb][0] + p[kb][1]) + (p[kb][2] + p[kb][3]);
             }
+            // a pairwise sum: depth 4 where a running sum would chain 16 adds
+            const float psum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
 #pragma unroll
             for (int cc = 0; cc < 2; ++cc)
                 pop[r][cc] = bf16x8{static_cast<__bf16>(p[2 * cc][0]), static_cast<__bf16>(p[2 * cc][1]),
