@@ -91,8 +91,14 @@ def parse_args():
                          "schedules on batches from uniform 64x512 to 1x128K+31x4K, print one JSON line")
     ap.add_argument("--tile-math", choices=["mfma", "valu"], default="mfma",
                     help="tile arithmetic: matrix cores (default) or vector ALU dot2 products")
-    ap.add_argument("--fused-merge", action="store_true",
-                    help="device schedule: the decode kernel merges split sequences itself (no merge kernel)")
+    ap.add_argument("--merge", choices=["rule", "kernel", "in-kernel"], default="rule",
+                    help="device schedule: how split sequences are merged -- the library's rule "
+                         "(hpc_decode_pick_merge), a separate merge kernel, or in the decode kernel by the worker "
+                         "that finishes a split sequence last; the host schedule always uses the merge kernel")
+    ap.add_argument("--fused-merge", action="store_true", help="the same as --merge in-kernel")
+    ap.add_argument("--merge-sweep", action="store_true",
+                    help="instead of the bench line: time the device-scheduled step with the merge kernel and "
+                         "with the in-kernel merge on batches of 2 to 128 workers per unit, print one JSON line")
     ap.add_argument("--tile-math-sweep", action="store_true",
                     help="time the decode kernel with MFMA and with VALU tile math on workloads 2-5 "
                          "(device schedule) and print one JSON line")
@@ -231,8 +237,10 @@ def main() -> int:
     if args.skew_sweep:
         print(json.dumps(skew_sweep(dev, W, cus, args.steps, args.warmup)), flush=True)
         return 0
-    if args.fused_merge and args.schedule != "device":
-        print("--fused-merge needs the device schedule", file=sys.stderr)
+    if args.fused_merge:
+        args.merge = "in-kernel"
+    if args.merge == "in-kernel" and args.schedule != "device":
+        print("--merge in-kernel needs the device schedule", file=sys.stderr)
         return 2
     if args.phase_trace:
         print(json.dumps(phase_trace(dev, cus, args.workload, args.n_workers, min(args.steps, 200), args.warmup,
@@ -240,6 +248,9 @@ def main() -> int:
         return 0
     if args.price_sweep:
         print(json.dumps(price_sweep(dev, cus, args.steps, args.warmup)), flush=True)
+        return 0
+    if args.merge_sweep:
+        print(json.dumps(merge_sweep(dev, cus, args.steps, args.warmup)), flush=True)
         return 0
     if args.workers_sweep:
         print(json.dumps(workers_sweep(dev, cus, args.steps, args.warmup)), flush=True)
@@ -278,7 +289,18 @@ def main() -> int:
         price = hd.hpc_decode_pick_entry_price(inp.seq_lens, inp.num_kv_heads, inp.kv_dtype, W)
         price_rule = (f"hpc_decode_pick_entry_price (prices 0, 2, 4, 8, 16; entry cost "
                       f"{0.5 if inp.kv_dtype == 'bf16' else 2.0} tiles on {inp.kv_dtype})")
+    if args.schedule != "device":
+        fused, merge_rule = False, "the host schedule merges in the merge kernel"
+    elif args.merge == "rule":
+        # the library's merge rule: in the decode kernel when no sequence-head
+        # unit of this partition is shared by more than FUSED_MAX_SHARES workers
+        fused = hd.hpc_decode_pick_merge(inp.seq_lens, inp.num_kv_heads, W, price)
+        merge_rule = (f"hpc_decode_pick_merge (in the decode kernel when no unit is shared by more than "
+                      f"{hd.FUSED_MAX_SHARES} workers)")
+    else:
+        fused, merge_rule = args.merge == "in-kernel", "given (--merge)"
     log(f"device {props.name}, {cus} CUs; W={W} ({w_rule}); entry price {price} ({price_rule}); "
+        f"merge {'in the decode kernel' if fused else 'kernel'} ({merge_rule}); "
         f"KV {kv_bytes_total / 1e6:.1f} MB x {copies} copies; algorithmic bytes/step {alg_bytes}")
 
     q = inp.q.to(dev)
@@ -297,7 +319,7 @@ def main() -> int:
                          dtype=torch.uint8, device=dev)
         launchers = [hd.StepLauncher(q, ks[c], vs[c], bt, sl, out, lse, num_kv_heads=inp.num_kv_heads,
                                      n_workers=W, workspace=ws, tile_math=args.tile_math,
-                                     fused_merge=args.fused_merge, entry_price=price, **scales)
+                                     fused_merge=fused, entry_price=price, **scales)
                      for c in range(copies)]
 
         def one_step(i: int) -> None:
@@ -380,7 +402,7 @@ def main() -> int:
             "algorithmic_bytes": alg_bytes,
             "schedule": args.schedule + (", plan in place" if args.schedule == "host" and args.plan_in_place else ""),
             "parallelism": "single GPU", "tile_math": args.tile_math,
-            "merge": "in the decode kernel" if args.fused_merge else "separate kernel",
+            "merge": "in the decode kernel" if fused else "separate kernel", "merge_from": merge_rule,
         },
         "step_clocks_us": {"host_clock": round(wall / args.steps * 1e6, 3),
                            "stream_events": round(ev_ms / args.steps * 1e3, 3)},
@@ -390,7 +412,7 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": round(achieved_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": (measured_traffic(wl.name, args.schedule, W, price)
-                                 if args.tile_math == "mfma" else None),
+                                 if args.tile_math == "mfma" and not fused else None),
                      "kernel": "decode_kernel", "bytes_per_launch": alg_bytes,
                      "kernel_us_hip_events": round(decode_us, 3),
                      "duration_source": ("decode kernel alone: mean of HIP events stamped by each launch's "
@@ -488,6 +510,8 @@ def tile_math_sweep(dev, W: int, steps: int, warmup: int) -> dict:
         k0, v0 = inp.k_cache.to(dev), inp.v_cache.to(dev)
         ks = [k0] + [k0.clone() for _ in range(copies - 1)]
         vs = [v0] + [v0.clone() for _ in range(copies - 1)]
+        # every copy read once before timing (a copy's first step runs slower)
+        clock_warmup(dev, torch.cuda.get_device_properties(dev).multi_processor_count, inputs=ks + vs)
         out = torch.empty_like(q)
         lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
         ws = torch.zeros(hd.hpc_decode_step_workspace_size(inp.batch, inp.num_q_heads, inp.num_kv_heads, W),
@@ -750,7 +774,9 @@ def skew_sweep(dev, W: int, cus: int, steps: int, warmup: int) -> dict:
     are built and uploaded once, outside the timing; ratio = static /
     balanced (device-scheduled), and static / balanced host plan (the same
     host-planned kernel as the static plans).  The device-scheduled step is
-    also timed at the worker-count rule's W where that differs from W."""
+    also timed as the library's rules set it up (hpc_decode_pick_workers,
+    hpc_decode_pick_entry_price, hpc_decode_pick_merge) where that differs.
+    Every KV copy of a batch is read once before its first timing."""
     import torch
 
     import load_balanced_paged_step_amd as hd
@@ -766,6 +792,7 @@ def skew_sweep(dev, W: int, cus: int, steps: int, warmup: int) -> dict:
         q, bt, sl = inp.q.to(dev), inp.block_table.to(dev), inp.seq_lens.to(dev)
         ks = [inp.k_cache.to(dev) for _ in range(copies)]
         vs = [inp.v_cache.to(dev) for _ in range(copies)]
+        clock_warmup(dev, cus, inputs=ks + vs)   # every copy read once before timing
         out = torch.empty_like(q)
         lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
         scales = dict(sm_scale=inp.sm_scale, k_scale=inp.k_scale, v_scale=inp.v_scale)
@@ -786,15 +813,19 @@ def skew_sweep(dev, W: int, cus: int, steps: int, warmup: int) -> dict:
                                      workspace=ws, **scales) for c in range(copies)]
         balanced = kernel_us(lambda i: launchers[i % copies]())
         lens_np = inp.seq_lens.numpy()
-        # the device-scheduled step at the worker-count rule's W (when it differs)
-        w_rule = hd.hpc_decode_choose_workers(lens_np, 1, max(1, cus // 2), cus)
-        if w_rule == W:
+        # the device-scheduled step as the library's rules set it up: worker
+        # count, entry price and merge mode (when that differs from the above)
+        w_rule = hd.hpc_decode_pick_workers(lens_np, 1, "bf16", cus)
+        price_rule = hd.hpc_decode_pick_entry_price(lens_np, 1, "bf16", w_rule)
+        fused_rule = hd.hpc_decode_pick_merge(lens_np, 1, w_rule, price_rule)
+        if w_rule == W and price_rule == 0 and not fused_rule:
             balanced_rule = balanced
         else:
             ws_r = torch.zeros(hd.hpc_decode_step_workspace_size(inp.batch, 8, 1, w_rule), dtype=torch.uint8,
                                device=dev)
             launchers_r = [hd.StepLauncher(q, ks[c], vs[c], bt, sl, out, lse, num_kv_heads=1, n_workers=w_rule,
-                                           workspace=ws_r, **scales) for c in range(copies)]
+                                           workspace=ws_r, entry_price=price_rule, fused_merge=fused_rule,
+                                           **scales) for c in range(copies)]
             balanced_rule = kernel_us(lambda i: launchers_r[i % copies]())
             del launchers_r
 
@@ -821,13 +852,17 @@ def skew_sweep(dev, W: int, cus: int, steps: int, warmup: int) -> dict:
                # the balanced plan through the same host-planned kernel the static plans run through
                "ratio_rule_host_plan": round(static[rule_S] / balanced_host, 3),
                "ratio_best_host_plan": round(static[best_S] / balanced_host, 3),
-               "rule_workers": w_rule, "balanced_rule_workers_us": round(balanced_rule, 2),
-               "ratio_best_rule_workers": round(static[best_S] / balanced_rule, 3)}
+               "rules": {"n_workers": w_rule, "entry_price": price_rule,
+                         "merge": "in the decode kernel" if fused_rule else "merge kernel"},
+               "balanced_rules_us": round(balanced_rule, 2),
+               "ratio_best_rules": round(static[best_S] / balanced_rule, 3)}
         log(f"skew sweep {name}: balanced {balanced:.1f} us (host-planned {balanced_host:.1f}); "
             f"static S={rule_S} (rule) "
             f"{static[rule_S]:.1f} us = {row['ratio_rule']}x; best static S={best_S} {static[best_S]:.1f} us "
             f"= {row['ratio_best']}x; host-planned balanced vs best static {row['ratio_best_host_plan']}x; "
-            f"device-scheduled at the rule's W={w_rule} {balanced_rule:.1f} us = {row['ratio_best_rule_workers']}x")
+            f"device-scheduled by the rules (W={w_rule}, price {price_rule}, "
+            f"{'in-kernel merge' if fused_rule else 'merge kernel'}) {balanced_rule:.1f} us = "
+            f"{row['ratio_best_rules']}x")
         rows.append(row)
         del ks, vs, launchers
         torch.cuda.empty_cache()
@@ -947,6 +982,7 @@ def workers_sweep(dev, cus: int, steps: int, warmup: int) -> dict:
         q, bt, sl = inp.q.to(dev), inp.block_table.to(dev), inp.seq_lens.to(dev)
         ks = [inp.k_cache.to(dev) for _ in range(copies)]
         vs = [inp.v_cache.to(dev) for _ in range(copies)]
+        clock_warmup(dev, cus, inputs=ks + vs)   # every copy read once before timing
         out = torch.empty_like(q)
         lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
         scales = dict(sm_scale=inp.sm_scale, k_scale=inp.k_scale, v_scale=inp.v_scale)
@@ -1008,6 +1044,7 @@ def price_sweep(dev, cus: int, steps: int, warmup: int) -> dict:
         q, bt, sl = inp.q.to(dev), inp.block_table.to(dev), inp.seq_lens.to(dev)
         ks = [inp.k_cache.to(dev) for _ in range(copies)]
         vs = [inp.v_cache.to(dev) for _ in range(copies)]
+        clock_warmup(dev, cus, inputs=ks + vs)   # every copy read once before timing
         out = torch.empty_like(q)
         lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
         scales = dict(sm_scale=inp.sm_scale, k_scale=inp.k_scale, v_scale=inp.v_scale)
@@ -1055,6 +1092,99 @@ def _lens_summary(lens) -> str:
     if len(c) > 6:
         return f"{len(lens)} seqs, {int(min(lens))}..{int(max(lens))} (sum {int(sum(lens))})"
     return " + ".join(f"{n}x{L}" for L, n in sorted(c.items(), key=lambda kv: -kv[0]))
+
+
+MERGE_SWEEP_BATCHES = (
+    # (name, lengths, q heads, kv heads, kv dtype): 2 to 32 workers per unit at one worker per CU
+    ("bf16 8q/1kv 128x256", [256] * 128, 8, 1, "bf16"),
+    ("bf16 8q/1kv 64x512", [512] * 64, 8, 1, "bf16"),
+    ("bf16 8q/1kv 32x1K", [1024] * 32, 8, 1, "bf16"),
+    ("bf16 8q/1kv 16x2K", [2048] * 16, 8, 1, "bf16"),
+    ("bf16 8q/1kv 8x4K", [4096] * 8, 8, 1, "bf16"),
+    ("bf16 8q/1kv 64x1K", [1024] * 64, 8, 1, "bf16"),
+    ("bf16 8q/1kv 32x2K", [2048] * 32, 8, 1, "bf16"),
+    ("bf16 64q/8kv 8x1K", [1024] * 8, 64, 8, "bf16"),
+    ("bf16 64q/8kv 4x2K", [2048] * 4, 64, 8, "bf16"),
+    ("fp8 64q/8kv 16x512", [512] * 16, 64, 8, "fp8_e4m3"),
+    ("fp8 64q/8kv 8x1K", [1024] * 8, 64, 8, "fp8_e4m3"),
+    ("fp8 64q/8kv 4x2K", [2048] * 4, 64, 8, "fp8_e4m3"),
+    ("fp8 64q/8kv 2x4K", [4096] * 2, 64, 8, "fp8_e4m3"),
+    ("bf16 8q/1kv 4 short (37-200)", [37, 80, 150, 200], 8, 1, "bf16"),
+    ("bf16 8q/1kv 1x8K+31x4K", [8192] + [4096] * 31, 8, 1, "bf16"),
+    ("bf16 8q/1kv 1x16K+31x4K", [16384] + [4096] * 31, 8, 1, "bf16"),
+    ("bf16 8q/1kv 1x128K+31x4K", [131072] + [4096] * 31, 8, 1, "bf16"),
+)
+
+
+def plan_max_shares(words) -> int:
+    """Most workers sharing one unit in a host plan (its merge records hold
+    each split unit's worker count; header of 16 words, then W + 1 worker
+    pointers, 4 words per entry, 3 per merge record)."""
+    W, E, C = int(words[3]), int(words[5]), int(words[7])
+    o = 16 + W + 1 + 4 * E
+    return max([1] + [int(words[o + 3 * i + 1]) for i in range(C)])
+
+
+def merge_sweep(dev, cus: int, steps: int, warmup: int) -> dict:
+    """The device-scheduled step with the merge kernel and with the in-kernel
+    merge, at the rules' worker count and entry price, on batches whose
+    units are shared by 2 to 128 workers: decode + merge kernel time per
+    step (dispatch-stamped events), KV rotated over >= 1 GiB of copies, the
+    two modes taken in turn for three rounds, medians."""
+    import numpy as np
+    import torch
+
+    import load_balanced_paged_step_amd as hd
+    from workloads import make_inputs
+
+    clock_warmup(dev, cus)
+    steps = max(steps, 50)
+    rows = []
+    for name, lens, hq, hkv, kv in MERGE_SWEEP_BATCHES:
+        inp = make_inputs(lens, hq, hkv, kv, seed=4)
+        kv_bytes = inp.k_cache.numel() * inp.k_cache.element_size() * 2
+        copies = max(1, min(16, math.ceil((1 << 30) / kv_bytes)))
+        q, bt, sl = inp.q.to(dev), inp.block_table.to(dev), inp.seq_lens.to(dev)
+        ks = [inp.k_cache.to(dev) for _ in range(copies)]
+        vs = [inp.v_cache.to(dev) for _ in range(copies)]
+        clock_warmup(dev, cus, inputs=ks + vs)   # every copy read once before timing
+        out = torch.empty_like(q)
+        lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+        scales = dict(sm_scale=inp.sm_scale, k_scale=inp.k_scale, v_scale=inp.v_scale)
+        lens_np = inp.seq_lens.numpy()
+        W = hd.hpc_decode_pick_workers(lens_np, hkv, kv, cus)
+        price = hd.hpc_decode_pick_entry_price(lens_np, hkv, kv, W)
+        picked = hd.hpc_decode_pick_merge(lens_np, hkv, W, price)
+        shares = plan_max_shares(hd.hpc_decode_plan(lens_np, hkv, W, entry_price=price))
+        ws = torch.zeros(hd.hpc_decode_step_workspace_size(inp.batch, hq, hkv, W), dtype=torch.uint8, device=dev)
+        launchers = {f: [hd.StepLauncher(q, ks[i], vs[i], bt, sl, out, lse, num_kv_heads=hkv, n_workers=W,
+                                         workspace=ws, entry_price=price, fused_merge=f, **scales)
+                         for i in range(copies)] for f in (False, True)}
+        times = {f: [] for f in (False, True)}
+        for _ in range(3):
+            for f in (False, True):
+                for i in range(max(warmup, 20)):
+                    launchers[f][i % copies]()
+                torch.cuda.synchronize()
+                hd.hpc_decode_profile_start(steps)
+                for i in range(steps):
+                    launchers[f][i % copies]()
+                torch.cuda.synchronize()
+                d_ms, c_ms, n = hd.hpc_decode_profile_stop()
+                times[f].append(round((d_ms + c_ms) / max(n, 1) * 1e3, 2))
+        med = {f: float(np.median(t)) for f, t in times.items()}
+        row = {"batch": name, "n_workers": W, "entry_price": price, "max_shares": shares,
+               "merge_kernel_us": times[False], "in_kernel_us": times[True],
+               "picked": "in the decode kernel" if picked else "merge kernel",
+               "picked_over_best": round(med[picked] / min(med.values()), 4)}
+        log(f"merge sweep {name} (W={W}, price {price}, up to {shares} workers per unit): merge kernel "
+            f"{med[False]:.2f} us, in-kernel {med[True]:.2f} us; picked {row['picked']}")
+        rows.append(row)
+        del launchers, ks, vs, ws
+        torch.cuda.empty_cache()
+    return {"mode": "merge-sweep", "cus": cus, "steps": steps,
+            "timing": "decode + merge kernel time per step, dispatch-stamped HIP events, three rounds",
+            "rows": rows}
 
 
 if __name__ == "__main__":

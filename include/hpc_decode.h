@@ -257,6 +257,34 @@ int32_t hpc_decode_pick_workers(const int32_t* seq_lens, int32_t batch, int32_t 
 int32_t hpc_decode_pick_entry_price(const int32_t* seq_lens, int32_t batch, int32_t num_kv_heads,
                                     int32_t kv_dtype, int32_t n_workers);
 
+/* The most workers that may share one sequence-head unit for
+ * hpc_decode_pick_merge to keep the merge in the decode kernel.  Measured on
+ * MI355X (device-scheduled steps, W = 256 and the worker-count rule's W):
+ * with 2, 4 and 8 workers per unit the in-kernel merge ran 0.3-1.3 us faster
+ * than the merge kernel (uniform bf16 8q/1kv and 64q/8kv and fp8 64q/8kv
+ * batches, and 4 short sequences); with 16 it tied on uniform batches and
+ * lost 2.1 us on 1 x 8K + 31 x 4K, and with 30 or more it lost 2.5 us or
+ * more, since the last worker folds all of a unit's partials alone. */
+#define HPC_DECODE_FUSED_MAX_SHARES 8
+
+/* Merge mode for a device-scheduled step (the params field fused_merge),
+ * pure host code.  Split-KV decode merges a sequence split over several
+ * workers from their partial results (§Attention Backend: Dynamic
+ * Load-Balanced Scheduling, "vLLM x HPC-Ops: High-Performance Attention and
+ * MoE Backends from Tencent Hunyuan"; the log-sum-exp merge is the reading
+ * used here).  Over the partition the step will use (n_workers workers,
+ * entry_price applied as hpc_decode_plan_priced applies it), it counts the
+ * workers whose tile range meets each (sequence, KV head) unit.  Returns 1
+ * (merge in the decode kernel) when no unit has more than
+ * HPC_DECODE_FUSED_MAX_SHARES, which includes a batch with no split unit or
+ * no tiles (the merge kernel's launch is then saved), else 0 (merge kernel).
+ * Negative status: HPC_ERR_NULL for NULL lengths with batch > 0,
+ * HPC_ERR_INVALID for batch < 0, num_kv_heads < 1, n_workers < 1,
+ * entry_price outside 0 .. HPC_DECODE_MAX_ENTRY_PRICE, a negative length or
+ * 2^31 - 1 tiles or more. */
+int32_t hpc_decode_pick_merge(const int32_t* seq_lens, int32_t batch, int32_t num_kv_heads, int32_t n_workers,
+                              int32_t entry_price);
+
 /* Split count of the static split-KV baseline for a batch: the smallest
  * power of two S with batch * num_kv_heads * S >= n_cus (one share per
  * compute unit at least), capped at max_splits and at the largest unit's

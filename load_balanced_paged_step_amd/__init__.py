@@ -27,7 +27,7 @@ from ._lib import (HPC_OK, HPC_ERR_NULL, HPC_ERR_INVALID, HPC_ERR_UNSUPPORTED, H
 __all__ = [
     "hpc_decode_plan_size", "hpc_decode_plan", "hpc_decode_plan_static_size", "hpc_decode_plan_static",
     "hpc_decode_static_splits", "hpc_decode_choose_workers", "hpc_decode_pick_workers", "ENTRY_COST_TILES",
-    "hpc_decode_pick_entry_price", "MAX_ENTRY_PRICE",
+    "hpc_decode_pick_entry_price", "MAX_ENTRY_PRICE", "hpc_decode_pick_merge", "FUSED_MAX_SHARES",
     "hpc_decode_plan_words", "hpc_decode_workspace_size",
     "hpc_decode_check", "hpc_decode_attn", "hpc_status_string", "hpc_decode_profile_start",
     "hpc_decode_profile_stop", "hpc_decode_trace_start", "hpc_decode_trace_stop",
@@ -200,6 +200,21 @@ def hpc_decode_pick_entry_price(seq_lens, num_kv_heads: int, kv_dtype, n_workers
     return _lib.check(lib().hpc_decode_pick_entry_price(_i32p(lens), lens.shape[0], num_kv_heads,
                                                         _kv_code(kv_dtype), n_workers),
                       "hpc_decode_pick_entry_price")
+
+
+#: most workers per unit for which hpc_decode_pick_merge keeps the merge in the
+#: decode kernel (HPC_DECODE_FUSED_MAX_SHARES)
+FUSED_MAX_SHARES = 8
+
+
+def hpc_decode_pick_merge(seq_lens, num_kv_heads: int, n_workers: int, entry_price: int = 0) -> bool:
+    """The merge mode of a device-scheduled step (``fused_merge``): True
+    (merge in the decode kernel) when no (sequence, KV head) unit of the
+    step's partition is shared by more than FUSED_MAX_SHARES workers, False
+    (merge kernel) otherwise."""
+    lens = _host_i32(seq_lens).reshape(-1)
+    return bool(_lib.check(lib().hpc_decode_pick_merge(_i32p(lens), lens.shape[0], num_kv_heads, n_workers,
+                                                       entry_price), "hpc_decode_pick_merge"))
 
 
 def hpc_decode_plan_words(plan) -> int:

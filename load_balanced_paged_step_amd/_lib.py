@@ -88,6 +88,8 @@ SIGNATURES = {
                                                  ctypes.c_int32]),
     "hpc_decode_pick_entry_price": (ctypes.c_int32, [_I32P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                      ctypes.c_int32]),
+    "hpc_decode_pick_merge": (ctypes.c_int32, [_I32P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                               ctypes.c_int32]),
     "hpc_decode_static_splits": (ctypes.c_int32, [_I32P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                   ctypes.c_int32]),
     "hpc_decode_plan_words": (ctypes.c_int64, [_I32P]),

@@ -372,6 +372,33 @@ extern "C" int32_t hpc_decode_pick_entry_price(const int32_t* seq_lens, int32_t 
     return best;
 }
 
+extern "C" int32_t hpc_decode_pick_merge(const int32_t* seq_lens, int32_t batch, int32_t num_kv_heads,
+                                         int32_t n_workers, int32_t entry_price) {
+    if (batch > 0 && seq_lens == nullptr) return HPC_ERR_NULL;
+    if (batch < 0 || num_kv_heads < 1 || n_workers < 1 || entry_price < 0 ||
+        entry_price > HPC_DECODE_MAX_ENTRY_PRICE)
+        return HPC_ERR_INVALID;
+    std::vector<int64_t> s0, s1;
+    int64_t T = 0;
+    if (!unit_ranges(seq_lens, batch, num_kv_heads, s0, s1, T)) return HPC_ERR_INVALID;
+    if (T == 0) return 1;
+    std::vector<int64_t> bound;
+    boundaries(s0, s1, T, n_workers, entry_price, bound);
+    // workers per unit: each non-empty range [a, e) adds one to every unit it meets
+    const std::size_t U = s0.size();
+    std::vector<int32_t> shares(U, 0);
+    std::size_t u = 0;
+    for (int64_t w = 0; w < n_workers; ++w) {
+        const int64_t a = bound[w], e = bound[w + 1];
+        if (a == e) continue;
+        while (u < U && s1[u] <= a) ++u;
+        for (std::size_t v = u; v < U && s0[v] < e; ++v) ++shares[v];
+    }
+    for (std::size_t v = 0; v < U; ++v)
+        if (shares[v] > HPC_DECODE_FUSED_MAX_SHARES) return 0;
+    return 1;
+}
+
 extern "C" int64_t hpc_decode_plan_words(const int32_t* plan) {
     if (plan == nullptr) return HPC_ERR_NULL;
     if (plan[0] != HPC_PLAN_VERSION || plan[8] != HPC_DECODE_PAGE) return HPC_ERR_PLAN_MISMATCH;

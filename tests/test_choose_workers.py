@@ -13,7 +13,7 @@ import pytest
 from hypothesis import given, settings, strategies as st
 
 import load_balanced_paged_step_amd as hd
-from oracle.plan import priced_boundaries
+from oracle.plan import build_plan, parse_plan, priced_boundaries
 from workloads import WORKLOADS, workload_inputs, workload_lengths
 
 
@@ -220,3 +220,66 @@ def test_pick_entry_price_errors():
     bad = np.array([100, -1], dtype=np.int32)
     assert lib.hpc_decode_pick_entry_price(bad.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), 2, 1,
                                            hd.HPC_KV_BF16, 4) == hd.HPC_ERR_INVALID
+
+
+# ------------------------------------------------------ merge mode of the step ---
+
+def _oracle_max_shares(lens, H, W, price):
+    """Most workers sharing one unit, read off the oracle plan's merge records
+    (each record holds a split unit's worker count)."""
+    plan = parse_plan(build_plan(np.asarray(lens, dtype=np.int64), H, W, entry_cost_q=price))
+    return max([1] + [int(r[1]) for r in plan["combine"]])
+
+
+@pytest.mark.parametrize("lens,H,W,expected", [
+    ([512] * 64, 1, 256, True),                  # 4 workers per sequence
+    ([1024] * 32, 1, 256, True),                 # 8
+    ([2048] * 16, 1, 256, False),                # 16
+    ([131072] + [4096] * 31, 1, 252, False),     # the long sequence over 128 workers
+    ([37, 80, 150, 200], 1, 256, True),          # fewer tiles than workers: one per tile
+    ([4096] * 64, 1, 64, True),                  # no unit split: no merge kernel to launch
+    ([0, 0, 0], 2, 16, True),                    # no tiles at all
+])
+def test_pick_merge_cases(lens, H, W, expected):
+    assert hd.hpc_decode_pick_merge(np.array(lens), H, W) is expected
+    assert (_oracle_max_shares(lens, H, W, 0) <= hd.FUSED_MAX_SHARES) is expected
+
+
+def test_pick_merge_on_the_decode_workloads():
+    """At the rules' worker count and price: the in-kernel merge for the tiny
+    and the uniform batch, the merge kernel where a sequence spreads over more
+    than 8 workers (8 x 1K at 256 workers, the 128K sequence, the fp8 batch's
+    long sequences)."""
+    got = {}
+    for cfg, w in WORKLOADS.items():
+        lens = workload_lengths(cfg)
+        W = hd.hpc_decode_pick_workers(lens, w.num_kv_heads, w.kv_dtype, 256)
+        price = hd.hpc_decode_pick_entry_price(lens, w.num_kv_heads, w.kv_dtype, W)
+        got[cfg] = hd.hpc_decode_pick_merge(lens, w.num_kv_heads, W, price)
+        assert got[cfg] is (_oracle_max_shares(lens, w.num_kv_heads, W, price) <= hd.FUSED_MAX_SHARES)
+    assert got == {1: True, 2: True, 3: False, 4: False, 5: False}
+
+
+@settings(max_examples=80, deadline=None)
+@given(lens=st.lists(st.integers(0, 6000), min_size=1, max_size=12), H=st.integers(1, 4),
+       W=st.integers(1, 60), price=st.sampled_from([0, 2, 4, 8, 16, 64]))
+def test_pick_merge_matches_the_oracle_plan(lens, H, W, price):
+    want = _oracle_max_shares(lens, H, W, price) <= hd.FUSED_MAX_SHARES
+    assert hd.hpc_decode_pick_merge(np.array(lens), H, W, price) is want
+
+
+def test_pick_merge_errors():
+    lib = hd.lib()
+    lens = np.array([100, 200], dtype=np.int32)
+    p = lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    assert lib.hpc_decode_pick_merge(p, 2, 1, 4, 0) == 1
+    assert lib.hpc_decode_pick_merge(None, 2, 1, 4, 0) == hd.HPC_ERR_NULL
+    assert lib.hpc_decode_pick_merge(None, 0, 1, 4, 0) == 1                  # empty batch
+    assert lib.hpc_decode_pick_merge(p, -1, 1, 4, 0) == hd.HPC_ERR_INVALID
+    assert lib.hpc_decode_pick_merge(p, 2, 0, 4, 0) == hd.HPC_ERR_INVALID
+    assert lib.hpc_decode_pick_merge(p, 2, 1, 0, 0) == hd.HPC_ERR_INVALID
+    assert lib.hpc_decode_pick_merge(p, 2, 1, 4, -1) == hd.HPC_ERR_INVALID
+    assert lib.hpc_decode_pick_merge(p, 2, 1, 4, hd.MAX_ENTRY_PRICE + 1) == hd.HPC_ERR_INVALID
+    bad = np.array([100, -1], dtype=np.int32)
+    assert lib.hpc_decode_pick_merge(bad.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), 2, 1, 4, 0) == \
+        hd.HPC_ERR_INVALID

@@ -89,6 +89,26 @@ def test_random_batches(seed):
         _fused(inp, W, f"random seed={seed}", dev, m, ref)
 
 
+@pytest.mark.parametrize("lens,hq,hkv,kv", [
+    ([256] * 128, 8, 1, "bf16"),           # 2 workers per sequence
+    ([1024] * 32, 8, 1, "bf16"),           # 8: the most the merge rule keeps in the kernel
+    ([2048] * 4, 64, 8, "fp8_e4m3"),       # 8 per (sequence, KV head)
+    ([37, 80, 150, 200], 8, 1, "bf16"),    # one worker per tile
+])
+def test_batches_the_merge_rule_keeps_in_the_kernel(lens, hq, hkv, kv):
+    """The step as the library's rules set it up (worker count, entry price,
+    merge mode) on batches whose units are shared by 2 to 8 workers, for
+    which hpc_decode_pick_merge picks the in-kernel merge."""
+    W = hd.hpc_decode_pick_workers(np.array(lens), hkv, kv, 256)
+    price = hd.hpc_decode_pick_entry_price(np.array(lens), hkv, kv, W)
+    assert hd.hpc_decode_pick_merge(np.array(lens), hkv, W, price)
+    announce(f"merge rule batch {len(lens)}x{lens[0]} {hq}q/{hkv}kv {kv} W={W} price={price}")
+    inp = make_inputs(lens, hq, hkv, kv, seed=77, poison=True)
+    dev = to_device(inp)
+    got = run_hip_step(inp, W, dev, fused_merge=True, entry_price=price)
+    compare(inp, got, run_oracle(inp), f"merge rule batch {len(lens)}x{lens[0]}")
+
+
 def test_repeated_steps_reuse_the_workspace():
     """Twelve steps on one zero-filled workspace, with the lengths (and so
     every unit's number of sharing workers) changing from step to step and
