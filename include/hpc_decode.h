@@ -278,6 +278,7 @@ int32_t hpc_decode_pick_entry_price(const int32_t* seq_lens, int32_t batch, int3
  * (merge in the decode kernel) when no unit has more than
  * HPC_DECODE_FUSED_MAX_SHARES, which includes a batch with no split unit or
  * no tiles (the merge kernel's launch is then saved), else 0 (merge kernel).
+ * For hpc_decode_step; hpc_decode_step_noalloc takes fused_merge = 0 only.
  * Negative status: HPC_ERR_NULL for NULL lengths with batch > 0,
  * HPC_ERR_INVALID for batch < 0, num_kv_heads < 1, n_workers < 1,
  * entry_price outside 0 .. HPC_DECODE_MAX_ENTRY_PRICE, a negative length or

@@ -241,11 +241,14 @@ prefill_kernel(PrefillArgs a) {
     const int G = a.group;
     if (slot >= a.n_partials) return;       // not a slot of this plan: write nothing
 
-    // Q of this wave's heads: row block r holds head hg = wave + 4 r
+    // this workgroup's heads of the query group: hbase .. hbase + 4 HPW - 1
+    // (grid y splits a larger group over several workgroups)
+    const int hbase = static_cast<int>(blockIdx.y) * (kWaves * HPW);
+    // Q of this wave's heads: row block r holds head hg = hbase + wave + 4 r
     bf16x8 qop[HPW][4];
 #pragma unroll
     for (int r = 0; r < HPW; ++r) {
-        const int hg = wave + kWaves * r;
+        const int hg = hbase + wave + kWaves * r;
         const int64_t row_stride = int64_t(a.num_q_heads) * kHeadDim * 2;
         const char* base = static_cast<const char*>(a.q) + (int64_t(r0 + q0) * a.num_q_heads + h * G + hg) * kHeadDim * 2;
         const uint32_t bytes = (hg < G && nq > 0) ? static_cast<uint32_t>((nq - 1) * row_stride + kHeadDim * 2) : 0u;
@@ -440,7 +443,7 @@ prefill_kernel(PrefillArgs a) {
     // visible token gets 0 and -inf
 #pragma unroll
     for (int r = 0; r < HPW; ++r) {
-        const int hg = wave + kWaves * r;
+        const int hg = hbase + wave + kWaves * r;
         if (hg >= G) break;
         float lt = l[r];
         lt += __shfl_xor(lt, 16);
@@ -559,17 +562,21 @@ __global__ void __launch_bounds__(256) prefill_merge_kernel(PrefillArgs a) {
     if (part == 0) a.lse[orow] = wsum > 0.f ? M + __logf(wsum) : -INFINITY;
 }
 
-// With fewer than two work entries per compute unit the grid cannot hide
-// one entry's tile chain behind other workgroups, so two groups of 4 waves
-// split each entry's tiles (NG = 2, G <= 8); with more, an entry is one group
-// of 4 waves and two workgroups share a CU.  G > 8 (4 heads per wave) keeps
-// NG = 1: its group state does not fit the tile buffers.
+// A workgroup takes 4 HPW heads of an entry's query group; a larger group
+// (G > 8) is split over grid y, so every wave keeps two heads and two waves
+// share a SIMD (measured on extends: 4 heads per wave at one wave per SIMD
+// ran at 650 TFLOP/s where two heads per wave ran at 930).  With fewer than
+// two workgroups per compute unit the grid cannot hide one entry's tile
+// chain behind other workgroups, so two groups of 4 waves split each
+// entry's tiles (NG = 2); with more, a workgroup is one group of 4 waves and
+// two workgroups share a CU.
 template <bool FP8, int HPW>
 void launch_hpw(const PrefillArgs& a, int n_entries, hipStream_t s) {
-    if (n_entries < 2 * device_cus())
-        hipLaunchKernelGGL((prefill_kernel<FP8, HPW, 2>), dim3(n_entries), dim3(2 * kThreads), 0, s, a);
+    const int ny = (a.group + kWaves * HPW - 1) / (kWaves * HPW);
+    if (static_cast<int64_t>(n_entries) * ny < 2 * device_cus())
+        hipLaunchKernelGGL((prefill_kernel<FP8, HPW, 2>), dim3(n_entries, ny), dim3(2 * kThreads), 0, s, a);
     else
-        hipLaunchKernelGGL((prefill_kernel<FP8, HPW, 1>), dim3(n_entries), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((prefill_kernel<FP8, HPW, 1>), dim3(n_entries, ny), dim3(kThreads), 0, s, a);
 }
 
 template <bool FP8>
@@ -577,10 +584,8 @@ int launch_fp8(const PrefillArgs& a, int n_entries, void* stream) {
     const hipStream_t s = static_cast<hipStream_t>(stream);
     if (a.group <= 4)
         launch_hpw<FP8, 1>(a, n_entries, s);
-    else if (a.group <= 8)
-        launch_hpw<FP8, 2>(a, n_entries, s);
     else
-        hipLaunchKernelGGL((prefill_kernel<FP8, 4, 1>), dim3(n_entries), dim3(kThreads), 0, s, a);
+        launch_hpw<FP8, 2>(a, n_entries, s);
     return static_cast<int>(hipGetLastError());
 }
 

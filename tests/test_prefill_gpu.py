@@ -80,7 +80,8 @@ CASES = {
     "ragged extends, 16q/2kv": ([100, 0, 63, 1000, 5, 64], [1, 15, 17, 33, 64, 0], 16, 2, "bf16"),
     "extends G=1": ([300, 20], [40, 70], 4, 4, "bf16"),
     "extends G=2": ([128, 7], [50, 9], 8, 4, "bf16"),
-    "extends G=16 (4 heads per wave)": ([70, 0], [45, 130], 32, 2, "bf16"),
+    "extends G=16 (two workgroups of 8 heads)": ([70, 0], [45, 130], 32, 2, "bf16"),
+    "extends G=12 (the second workgroup's heads part-filled)": ([50, 200], [70, 33], 24, 2, "bf16"),
     "extends G=5": ([90], [77], 5, 1, "bf16"),
     "fp8 extends 64q/8kv": ([2000, 64, 0], [256, 100, 65], 64, 8, "fp8_e4m3"),
     "fp8 prompt G=16": ([0], [300], 16, 1, "fp8_e4m3"),
@@ -100,7 +101,7 @@ def test_prefill_parity(case):
 BALANCED = {
     "prompt 200 on 64 workers, 8q/1kv": ([0], [200], 8, 1, "bf16", 64),
     "extend after 3000, 16q/2kv, 40 workers": ([3000, 0, 10], [40, 17, 1], 16, 2, "bf16", 40),
-    "extends G=16 (4 heads per wave), 30 workers": ([700, 0], [45, 130], 32, 2, "bf16", 30),
+    "extends G=16 (two workgroups of 8 heads), 30 workers": ([700, 0], [45, 130], 32, 2, "bf16", 30),
     "extend G=5, one tile a share": ([300], [20], 5, 1, "bf16", 10000),
     "fp8 extends 64q/8kv, 512 workers": ([2000, 64, 0], [256, 100, 65], 64, 8, "fp8_e4m3", 512),
     "decode rows after 5000, 8q/1kv, 30 workers": ([5000, 37, 900], [1, 1, 1], 8, 1, "bf16", 30),

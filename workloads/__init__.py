@@ -343,6 +343,9 @@ PREFILL_WORKLOADS = {
     "extend-8x512": PrefillWorkload("extend-8x512", 64, 8, "bf16", (512,) * 8, None,
                                     description="8 chunks of 512 new tokens after log-uniform [64, 16384] "
                                                 "cached tokens, 64q/8kv, bf16"),
+    "extend-8x512-128q8kv": PrefillWorkload("extend-8x512-128q8kv", 128, 8, "bf16", (512,) * 8, None,
+                                            description="extend-8x512 with 16 query heads per KV head, the "
+                                                        "largest group the library takes (128q/8kv, bf16)"),
     "extend-8x256-fp8": PrefillWorkload("extend-8x256-fp8", 64, 8, "fp8_e4m3", (256,) * 8, None,
                                         description="8 chunks of 256 after log-uniform [64, 16384] cached "
                                                     "tokens, 64q/8kv, fp8-e4m3 KV"),
