@@ -555,20 +555,25 @@ def tile_math_sweep(dev, W: int, steps: int, warmup: int) -> dict:
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
-def _events_us(fn, steps: int, warmup: int) -> float:
-    """Mean time per call of `fn` over `steps` back-to-back calls on the
-    current stream, bracketed by events (after `warmup` calls)."""
+def _events_us(fn, steps: int, warmup: int, reps: int = 3) -> float:
+    """Time per call of `fn`: the mean over `steps` back-to-back calls on the
+    current stream, bracketed by events (after `warmup` calls), taken `reps`
+    times; the median of those means (a single pass of a launch this short
+    was seen to double now and then)."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        fn()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps * 1e3
+    means = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        means.append(e0.elapsed_time(e1) / steps * 1e3)
+    return sorted(means)[len(means) // 2]
 
 
 def _blas_threads() -> int:
@@ -677,7 +682,7 @@ def prefill_bench(dev, cus: int, which: str, steps: int, warmup: int, only_worke
         rows.append(row)
         del q, k, v, out, lse
         torch.cuda.empty_cache()
-    return {"mode": "prefill", "timing": "mean of back-to-back launches, HIP events on the launch stream",
+    return {"mode": "prefill", "timing": "mean of back-to-back launches, HIP events on the launch stream; median of three passes",
             "peak_note": "fp8 KV widens to bf16 in LDS; all products run on bf16 MFMA", "rows": rows}
 
 
@@ -749,7 +754,7 @@ def prologue_bench(dev, cus: int, W: int, steps: int, warmup: int) -> dict:
             f"with prologue {both_us:.2f} us; oracle {dt * 1e3:.1f} ms")
         rows.append(row)
     return {"mode": "prologue", "n_workers": W,
-            "timing": "mean of back-to-back launches, HIP events on the launch stream (KV resident, one copy)",
+            "timing": "mean of back-to-back launches, HIP events on the launch stream (KV resident, one copy); median of three passes",
             "rows": rows}
 
 
