@@ -105,6 +105,9 @@ def parse_args():
     ap.add_argument("--prefill", nargs="?", const="all", default=None, metavar="WORKLOAD",
                     help="instead of the bench line: time causal prefill/extend attention on the prefill "
                          "workloads (all, or one by name) and print one JSON line")
+    ap.add_argument("--prefill-group-sweep", action="store_true",
+                    help="instead of the bench line: time causal extend attention at 1-16 query heads per KV head "
+                         "on extend-8x512's contexts, print one JSON line")
     ap.add_argument("--prefill-workers", type=int, default=None, metavar="W",
                     help="with --prefill: time only the plan balanced over W workers (0: whole units)")
     ap.add_argument("--phase-trace", action="store_true",
@@ -248,6 +251,9 @@ def main() -> int:
         return 0
     if args.price_sweep:
         print(json.dumps(price_sweep(dev, cus, args.steps, args.warmup)), flush=True)
+        return 0
+    if args.prefill_group_sweep:
+        print(json.dumps(prefill_group_sweep(dev, cus, args.steps, args.warmup)), flush=True)
         return 0
     if args.merge_sweep:
         print(json.dumps(merge_sweep(dev, cus, args.steps, args.warmup)), flush=True)
@@ -1097,6 +1103,52 @@ def _lens_summary(lens) -> str:
     if len(c) > 6:
         return f"{len(lens)} seqs, {int(min(lens))}..{int(max(lens))} (sum {int(sum(lens))})"
     return " + ".join(f"{n}x{L}" for L, n in sorted(c.items(), key=lambda kv: -kv[0]))
+
+
+def prefill_group_sweep(dev, cus: int, steps: int, warmup: int) -> dict:
+    """Causal extend attention at 1, 2, 4, 8 and 16 query heads per KV head
+    (8 KV heads, bf16): the contexts and chunks of extend-8x512 (8 chunks of
+    512 new tokens after log-uniform [64, 16384] cached, seed 7), whole units
+    (W = 0) and the balanced plan at 2 workers per CU; launch time by events,
+    median of three passes."""
+    import numpy as np
+    import torch
+
+    from load_balanced_paged_step_amd.prefill import PrefillStep
+    from workloads import PREFILL_WORKLOADS, draw_loguniform_lengths, make_prefill_inputs
+
+    w = PREFILL_WORKLOADS["extend-8x512"]
+    clock_warmup(dev, cus)
+    rng = np.random.default_rng(7)
+    ctx = draw_loguniform_lengths(rng, len(w.q_lens), *w.ctx_loguniform)
+    qn = np.asarray(w.q_lens, dtype=np.int64)
+    rows = []
+    for hq in (8, 16, 32, 64, 128):
+        pi = make_prefill_inputs(ctx, qn, hq, 8, "bf16", seed=7)
+        c = pi.cache
+        q, qs = pi.q.to(dev), pi.q_start.to(dev)
+        k, v = c.k_cache.to(dev), c.v_cache.to(dev)
+        bt, sl = c.block_table.to(dev), c.seq_lens.to(dev)
+        out = torch.empty_like(q)
+        lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+        flops = pi.flops()
+        row = {"heads": f"{hq}q/8kv", "group": hq // 8, "flops": flops}
+        for W in (0, 2 * cus):
+            step = PrefillStep(pi.q_start, c.seq_lens, c.num_q_heads, c.num_kv_heads, c.max_pages_per_seq,
+                               n_workers=W, device=dev)
+            one = step.bind(q, qs, k, v, bt, sl, out, lse, sm_scale=c.sm_scale, k_scale=c.k_scale,
+                            v_scale=c.v_scale)
+            us = _events_us(one, max(steps, 20), max(warmup, 5))
+            row[f"W={W}"] = {"us": round(us, 2), "TFLOPs": round(flops / (us * 1e-6) / 1e12, 1)}
+            del one, step
+        log(f"prefill group sweep {hq}q/8kv (G={hq // 8}): " + ", ".join(
+            f"{k} {v['us']:.1f} us ({v['TFLOPs']:.0f} TFLOP/s)" for k, v in row.items() if k.startswith("W=")))
+        rows.append(row)
+        del q, k, v, out, lse
+        torch.cuda.empty_cache()
+    return {"mode": "prefill-group-sweep", "contexts": "extend-8x512's (seed 7)",
+            "timing": "mean of back-to-back launches, HIP events on the launch stream; median of three passes",
+            "rows": rows}
 
 
 MERGE_SWEEP_BATCHES = (

@@ -51,8 +51,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
 constexpr int kQBlock = 16;                       // queries per unit
 constexpr int kLdsRow = kHeadDim * 2 + 32;        // bytes per LDS row: 256 + 32 pad (half the bank
                                                   // conflicts of a 16-byte pad, measured)
@@ -109,17 +107,20 @@ __device__ __forceinline__ int vt_offset(int d, int byte) {   // byte of the dim
     return line * 256 + ((q ^ ((line >> 2) & 15)) << 4) + (byte & 15);
 }
 
-// One 64-token tile of K and V in flight.  K: 16-byte chunks of the
-// row-major tile (16 KiB bf16 = 4 per thread, 8 KiB fp8 = 2 per thread).
-// V: thread (j, m) = (tid >> 4, tid & 15) holds tokens 4j .. 4j+3, dims
-// 8m .. 8m+7 (16 bytes per token in bf16, 8 in fp8), which it transposes into
-// V^T on the way to LDS.
-template <bool FP8>
+// One 64-token tile of K and V in flight, staged by the 64 NW threads of a
+// group.  K: 16-byte chunks of the row-major tile (16 KiB bf16 = 16 per 4
+// threads, 8 KiB fp8 = 8).  V: thread (j, m) = (tid >> 4 + 4 NW p, tid & 15)
+// holds tokens 4j .. 4j+3, dims 8m .. 8m+7 (16 bytes per token in bf16, 8 in
+// fp8), for each of its 4 / NW passes p, which it transposes into V^T on the
+// way to LDS.
+template <bool FP8, int NW>
 struct TileRegs {
-    static constexpr int kKLoads = FP8 ? 2 : 4;
+    static constexpr int kThr = 64 * NW;
+    static constexpr int kRep = 4 / NW;
+    static constexpr int kKLoads = (FP8 ? 2 : 4) * kRep;
     typedef typename std::conditional<FP8, u32x2, u32x4>::type VRow;
     u32x4 k[kKLoads];
-    VRow v[4];
+    VRow v[4 * kRep];
 
     // rows [0, valid) of page `page`, KV head h; everything else reads as 0
     __device__ __forceinline__ void load(const PrefillArgs& a, int page, int h, int valid, int tid) {
@@ -132,24 +133,28 @@ struct TileRegs {
         const auto rv = make_rsrc(static_cast<const char*>(a.v) + off, bytes);
 #pragma unroll
         for (int i = 0; i < kKLoads; ++i) {
-            const int c = tid + kThreads * i;          // 16-byte chunk of the tile, row-major
+            const int c = tid + kThr * i;              // 16-byte chunk of the tile, row-major
             k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, c * 16, 0, 0);
         }
-        const int j = tid >> 4, m = tid & 15;
+        const int m = tid & 15;
         constexpr int row = kHeadDim * (FP8 ? 1 : 2);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if constexpr (FP8)
-                v[i] = __builtin_amdgcn_raw_buffer_load_b64(rv, (4 * j + i) * row + 8 * m, 0, 0);
-            else
-                v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, (4 * j + i) * row + 16 * m, 0, 0);
+        for (int pp = 0; pp < kRep; ++pp) {
+            const int j = (tid >> 4) + (kThr >> 4) * pp;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if constexpr (FP8)
+                    v[4 * pp + i] = __builtin_amdgcn_raw_buffer_load_b64(rv, (4 * j + i) * row + 8 * m, 0, 0);
+                else
+                    v[4 * pp + i] = __builtin_amdgcn_raw_buffer_load_b128(rv, (4 * j + i) * row + 16 * m, 0, 0);
+            }
         }
     }
 
     __device__ __forceinline__ void store(char* lds_k, char* lds_v, int tid) const {
 #pragma unroll
         for (int i = 0; i < kKLoads; ++i) {
-            const int c = tid + kThreads * i;
+            const int c = tid + kThr * i;
             if constexpr (FP8) {
                 const int row = c >> 3, col = (c & 7) * 32;      // 16 codes -> 32 bytes of bf16
                 char* pk = lds_k + row * kLdsRow + col;
@@ -163,26 +168,30 @@ struct TileRegs {
             }
         }
         // V: token rows of 8 dims (bf16 pairs per word) -> for each dim, its 4 tokens
-        u32x4 vb[4];
+        const int m = tid & 15;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if constexpr (FP8) {
-                const u32x2 lo = fp8x4_to_bf16x4(v[i][0]), hi = fp8x4_to_bf16x4(v[i][1]);
-                vb[i] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-            } else {
-                vb[i] = v[i];
+        for (int pp = 0; pp < kRep; ++pp) {
+            u32x4 vb[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if constexpr (FP8) {
+                    const u32x2 lo = fp8x4_to_bf16x4(v[4 * pp + i][0]), hi = fp8x4_to_bf16x4(v[4 * pp + i][1]);
+                    vb[i] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+                } else {
+                    vb[i] = v[4 * pp + i];
+                }
             }
-        }
-        const int j = tid >> 4, m = tid & 15;
-        const int tb = (j >> 3) * 64 + (j & 3) * 16 + ((j >> 2) & 1) * 8;   // byte of token 4j in a dim's 128
+            const int j = (tid >> 4) + (kThr >> 4) * pp;
+            const int tb = (j >> 3) * 64 + (j & 3) * 16 + ((j >> 2) & 1) * 8;   // byte of token 4j in a dim's 128
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const u32x2 lo = u32x2{__builtin_amdgcn_perm(vb[1][p], vb[0][p], kSelLo),
-                                   __builtin_amdgcn_perm(vb[3][p], vb[2][p], kSelLo)};
-            const u32x2 hi = u32x2{__builtin_amdgcn_perm(vb[1][p], vb[0][p], kSelHi),
-                                   __builtin_amdgcn_perm(vb[3][p], vb[2][p], kSelHi)};
-            *reinterpret_cast<u32x2*>(lds_v + vt_offset(8 * m + 2 * p, tb)) = lo;
-            *reinterpret_cast<u32x2*>(lds_v + vt_offset(8 * m + 2 * p + 1, tb)) = hi;
+            for (int p = 0; p < 4; ++p) {
+                const u32x2 lo = u32x2{__builtin_amdgcn_perm(vb[1][p], vb[0][p], kSelLo),
+                                       __builtin_amdgcn_perm(vb[3][p], vb[2][p], kSelLo)};
+                const u32x2 hi = u32x2{__builtin_amdgcn_perm(vb[1][p], vb[0][p], kSelHi),
+                                       __builtin_amdgcn_perm(vb[3][p], vb[2][p], kSelHi)};
+                *reinterpret_cast<u32x2*>(lds_v + vt_offset(8 * m + 2 * p, tb)) = lo;
+                *reinterpret_cast<u32x2*>(lds_v + vt_offset(8 * m + 2 * p + 1, tb)) = hi;
+            }
         }
     }
 };
@@ -192,10 +201,11 @@ struct TileRegs {
 // merged in LDS.  Two waves per SIMD are the point either way (two
 // workgroups per CU with NG = 1, two groups with NG = 2), so the register
 // budget is held to 2 waves per SIMD where the accumulators allow (HPW <= 2).
-template <bool FP8, int HPW, int NG>
-__global__ void __launch_bounds__(kThreads * NG) __attribute__((amdgpu_waves_per_eu(HPW <= 2 ? 2 : 1, 4)))
+template <bool FP8, int HPW, int NG, int NW>
+__global__ void __launch_bounds__(64 * NW * NG) __attribute__((amdgpu_waves_per_eu(2, 4)))
 prefill_kernel(PrefillArgs a) {
-    static_assert(NG == 1 || (NG == 2 && HPW <= 2), "a group merge needs HPW * 34 KB of the tile buffers");
+    static_assert(HPW <= 2 && (NW == 2 || NW == 4), "two waves per SIMD: at most two heads per wave");
+    constexpr int kThreads = 64 * NW;   // threads of one group
     // per group one tile buffer (K rows, then V^T), or with two groups two
     // buffers used by alternate rounds (measured: one barrier per round pays
     // there; with one group per workgroup, two barriers around a single
@@ -208,8 +218,8 @@ prefill_kernel(PrefillArgs a) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int gg = wave_all >> 2;     // group of this wave
-    const int wave = wave_all & 3;    // wave within the group: owns heads wave + 4 r
+    const int gg = wave_all / NW;     // group of this wave
+    const int wave = wave_all % NW;   // wave within the group: owns heads hbase + wave + NW r
     const int tid_g = tid & (kThreads - 1);
     const int n = lane & 15;          // query column / K row / V dim group
     const int g = lane >> 4;          // lane group
@@ -241,14 +251,14 @@ prefill_kernel(PrefillArgs a) {
     const int G = a.group;
     if (slot >= a.n_partials) return;       // not a slot of this plan: write nothing
 
-    // this workgroup's heads of the query group: hbase .. hbase + 4 HPW - 1
+    // this workgroup's heads of the query group: hbase .. hbase + NW HPW - 1
     // (grid y splits a larger group over several workgroups)
-    const int hbase = static_cast<int>(blockIdx.y) * (kWaves * HPW);
-    // Q of this wave's heads: row block r holds head hg = hbase + wave + 4 r
+    const int hbase = static_cast<int>(blockIdx.y) * (NW * HPW);
+    // Q of this wave's heads: row block r holds head hg = hbase + wave + NW r
     bf16x8 qop[HPW][4];
 #pragma unroll
     for (int r = 0; r < HPW; ++r) {
-        const int hg = hbase + wave + kWaves * r;
+        const int hg = hbase + wave + NW * r;
         const int64_t row_stride = int64_t(a.num_q_heads) * kHeadDim * 2;
         const char* base = static_cast<const char*>(a.q) + (int64_t(r0 + q0) * a.num_q_heads + h * G + hg) * kHeadDim * 2;
         const uint32_t bytes = (hg < G && nq > 0) ? static_cast<uint32_t>((nq - 1) * row_stride + kHeadDim * 2) : 0u;
@@ -365,7 +375,7 @@ prefill_kernel(PrefillArgs a) {
     // per group while the group computes the one before.  Every wave meets
     // every barrier; a group past the unit's last tile only waits.
     {
-        TileRegs<FP8> rg;
+        TileRegs<FP8, NW> rg;
         const int rounds = (t_hi - t_lo + NG - 1) / NG;
         if constexpr (kBufs == 1) {
             if (t_lo + gg < t_hi) rg.load(a, bt[t_lo + gg], h, rows_in(t_lo + gg), tid_g);
@@ -443,7 +453,7 @@ prefill_kernel(PrefillArgs a) {
     // visible token gets 0 and -inf
 #pragma unroll
     for (int r = 0; r < HPW; ++r) {
-        const int hg = hbase + wave + kWaves * r;
+        const int hg = hbase + wave + NW * r;
         if (hg >= G) break;
         float lt = l[r];
         lt += __shfl_xor(lt, 16);
@@ -562,30 +572,33 @@ __global__ void __launch_bounds__(256) prefill_merge_kernel(PrefillArgs a) {
     if (part == 0) a.lse[orow] = wsum > 0.f ? M + __logf(wsum) : -INFINITY;
 }
 
-// A workgroup takes 4 HPW heads of an entry's query group; a larger group
-// (G > 8) is split over grid y, so every wave keeps two heads and two waves
-// share a SIMD (measured on extends: 4 heads per wave at one wave per SIMD
-// ran at 650 TFLOP/s where two heads per wave ran at 930).  With fewer than
-// two workgroups per compute unit the grid cannot hide one entry's tile
-// chain behind other workgroups, so two groups of 4 waves split each
-// entry's tiles (NG = 2); with more, a workgroup is one group of 4 waves and
-// two workgroups share a CU.
-template <bool FP8, int HPW>
-void launch_hpw(const PrefillArgs& a, int n_entries, hipStream_t s) {
-    const int ny = (a.group + kWaves * HPW - 1) / (kWaves * HPW);
-    if (static_cast<int64_t>(n_entries) * ny < 2 * device_cus())
-        hipLaunchKernelGGL((prefill_kernel<FP8, HPW, 2>), dim3(n_entries, ny), dim3(2 * kThreads), 0, s, a);
+// A workgroup takes NW HPW heads of an entry's query group (NW waves of HPW
+// heads); a larger group is split over grid y, so every wave keeps at most
+// two heads and two waves share a SIMD (measured on extends: 4 heads per wave
+// at one wave per SIMD ran at 650 TFLOP/s where two heads per wave ran at
+// 930).  Groups of at most 4 heads take 2 waves per workgroup, so no wave
+// idles and four workgroups share a CU.  With fewer than two waves per SIMD
+// the grid cannot hide one entry's tile chain behind other workgroups, so two
+// groups of NW waves split each entry's tiles (NG = 2); otherwise a
+// workgroup is one group.
+template <bool FP8, int HPW, int NW>
+void launch_cfg(const PrefillArgs& a, int n_entries, hipStream_t s) {
+    const int ny = (a.group + NW * HPW - 1) / (NW * HPW);
+    if (static_cast<int64_t>(n_entries) * ny * NW < 8 * static_cast<int64_t>(device_cus()))
+        hipLaunchKernelGGL((prefill_kernel<FP8, HPW, 2, NW>), dim3(n_entries, ny), dim3(2 * 64 * NW), 0, s, a);
     else
-        hipLaunchKernelGGL((prefill_kernel<FP8, HPW, 1>), dim3(n_entries, ny), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((prefill_kernel<FP8, HPW, 1, NW>), dim3(n_entries, ny), dim3(64 * NW), 0, s, a);
 }
 
 template <bool FP8>
 int launch_fp8(const PrefillArgs& a, int n_entries, void* stream) {
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    if (a.group <= 4)
-        launch_hpw<FP8, 1>(a, n_entries, s);
+    if (a.group <= 2)
+        launch_cfg<FP8, 1, 2>(a, n_entries, s);
+    else if (a.group <= 4)
+        launch_cfg<FP8, 2, 2>(a, n_entries, s);
     else
-        launch_hpw<FP8, 2>(a, n_entries, s);
+        launch_cfg<FP8, 2, 4>(a, n_entries, s);
     return static_cast<int>(hipGetLastError());
 }
 
