@@ -4,6 +4,7 @@ from __future__ import annotations
 
 import numpy as np
 import torch
+import xxhash
 
 import load_balanced_paged_step_amd as hd
 from oracle import decode_attention, cache_bits_to_f64
@@ -51,15 +52,42 @@ def run_hip(inp, n_workers: int, dev=None, return_step=False, tile_math="mfma"):
     return (res + (step,)) if return_step else res
 
 
+# oracle results by a digest of everything they depend on: several tests run
+# the oracle on the same seeded workload, and on the largest one it takes
+# tens of seconds
+_ORACLE_CACHE: dict = {}
+
+
+def _inputs_digest(inp) -> tuple:
+    h = xxhash.xxh3_128()
+    for a in (inp.q_bits(), inp.k_bits(), inp.v_bits(), inp.block_table.numpy(), inp.seq_lens.numpy()):
+        a = np.ascontiguousarray(a)
+        h.update(str((a.dtype.str, a.shape)).encode())
+        h.update(a.data)
+    return (h.hexdigest(), inp.num_q_heads, inp.num_kv_heads, inp.kv_dtype, float(inp.sm_scale),
+            float(inp.k_scale), float(inp.v_scale))
+
+
 def run_oracle(inp):
-    return decode_attention(inp.q_bits(), inp.k_bits(), inp.v_bits(), inp.block_table.numpy(),
-                            inp.seq_lens.numpy(), num_q_heads=inp.num_q_heads,
-                            num_kv_heads=inp.num_kv_heads, kv_format=inp.kv_dtype,
-                            sm_scale=inp.sm_scale, k_scale=inp.k_scale, v_scale=inp.v_scale)
+    key = _inputs_digest(inp)
+    hit = _ORACLE_CACHE.get(key)
+    if hit is None:
+        hit = decode_attention(inp.q_bits(), inp.k_bits(), inp.v_bits(), inp.block_table.numpy(),
+                               inp.seq_lens.numpy(), num_q_heads=inp.num_q_heads,
+                               num_kv_heads=inp.num_kv_heads, kv_format=inp.kv_dtype,
+                               sm_scale=inp.sm_scale, k_scale=inp.k_scale, v_scale=inp.v_scale)
+        if len(_ORACLE_CACHE) >= 16:
+            _ORACLE_CACHE.pop(next(iter(_ORACLE_CACHE)))
+        _ORACLE_CACHE[key] = hit
+    return tuple(np.copy(x) for x in hit)
 
 
 def max_abs_v(inp) -> float:
-    v = cache_bits_to_f64(inp.v_bits(), inp.kv_dtype) * inp.v_scale
+    """max |V| over the cache, dequantised: the maximum over the distinct
+    codes the cache holds (one decode per distinct code, not per element)."""
+    bits = np.ascontiguousarray(inp.v_bits()).reshape(-1)
+    codes = np.flatnonzero(np.bincount(bits.view(np.uint8 if bits.itemsize == 1 else np.uint16)))
+    v = cache_bits_to_f64(codes.astype(bits.dtype), inp.kv_dtype) * inp.v_scale
     v = v[np.isfinite(v)]
     return float(np.abs(v).max()) if v.size else 1.0
 
