@@ -83,6 +83,9 @@ CASES = {
     "extends G=16 (two workgroups of 8 heads)": ([70, 0], [45, 130], 32, 2, "bf16"),
     "extends G=12 (the second workgroup's heads part-filled)": ([50, 200], [70, 33], 24, 2, "bf16"),
     "extends G=5": ([90], [77], 5, 1, "bf16"),
+    "extends G=3 (two heads per wave, two-wave groups)": ([150, 0], [50, 64], 6, 2, "bf16"),
+    "extends G=4 (two heads per wave, two-wave groups)": ([300, 20, 0], [40, 70, 33], 16, 4, "bf16"),
+    "fp8 extends G=4": ([500, 30], [64, 17], 32, 8, "fp8_e4m3"),
     "fp8 extends 64q/8kv": ([2000, 64, 0], [256, 100, 65], 64, 8, "fp8_e4m3"),
     "fp8 prompt G=16": ([0], [300], 16, 1, "fp8_e4m3"),
     "one-token chunks (decode)": ([37, 64, 3000], [1, 1, 1], 8, 1, "bf16"),
@@ -103,6 +106,7 @@ BALANCED = {
     "extend after 3000, 16q/2kv, 40 workers": ([3000, 0, 10], [40, 17, 1], 16, 2, "bf16", 40),
     "extends G=16 (two workgroups of 8 heads), 30 workers": ([700, 0], [45, 130], 32, 2, "bf16", 30),
     "extend G=5, one tile a share": ([300], [20], 5, 1, "bf16", 10000),
+    "extends G=4 after 2000, 40 workers": ([2000, 10], [33, 20], 8, 2, "bf16", 40),
     "fp8 extends 64q/8kv, 512 workers": ([2000, 64, 0], [256, 100, 65], 64, 8, "fp8_e4m3", 512),
     "decode rows after 5000, 8q/1kv, 30 workers": ([5000, 37, 900], [1, 1, 1], 8, 1, "bf16", 30),
     "empty chunks and an empty sequence, G = 2 (one head per wave)": ([900, 5, 0, 40], [20, 0, 0, 33], 8, 4,
@@ -146,7 +150,24 @@ def test_extend_workloads_sampled(name, n_workers):
     96 sampled rows, each against the decode oracle over that row's visible
     prefix."""
     announce(f"prefill workload {name}, n_workers {n_workers}, sampled rows")
-    pi = prefill_workload_inputs(name, poison=True)
+    _check_sampled(prefill_workload_inputs(name, poison=True), n_workers, f"{name} W={n_workers}")
+
+
+@pytest.mark.parametrize("hq", [8, 16, 32])
+def test_small_groups_on_a_full_grid(hq):
+    """extend-8x512's contexts and chunks with 8 KV heads and 1, 2 or 4 query
+    heads each: 2048 units, enough two-wave workgroups for one group each
+    (the small cases above run two groups per workgroup); sampled rows."""
+    from workloads import PREFILL_WORKLOADS, draw_loguniform_lengths
+    w = PREFILL_WORKLOADS["extend-8x512"]
+    rng = np.random.default_rng(7)
+    ctx = draw_loguniform_lengths(rng, len(w.q_lens), *w.ctx_loguniform)
+    announce(f"prefill extend-8x512 contexts, {hq}q/8kv, sampled rows")
+    pi = make_prefill_inputs(ctx, w.q_lens, hq, 8, "bf16", seed=7, poison=True)
+    _check_sampled(pi, 0, f"extend-8x512 contexts {hq}q/8kv")
+
+
+def _check_sampled(pi, n_workers, what):
     c = pi.cache
     got = run_gpu(pi, n_workers, PrefillStep.MIN_SHARE_TILES)
     rng = np.random.default_rng(11)
@@ -164,7 +185,7 @@ def test_extend_workloads_sampled(name, n_workers):
                                 np.array([p + 1]), num_q_heads=c.num_q_heads, num_kv_heads=c.num_kv_heads,
                                 kv_format=c.kv_dtype, sm_scale=c.sm_scale, k_scale=c.k_scale, v_scale=c.v_scale)
         ref_out[i], ref_lse[i] = o[0], l[0]
-    compare_rows(pi, got, (ref_out, ref_lse), f"{name} W={n_workers}", rows=rows)
+    compare_rows(pi, got, (ref_out, ref_lse), what, rows=rows)
 
 
 @pytest.mark.parametrize("n_workers", [0, 48])
