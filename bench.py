@@ -582,6 +582,28 @@ def _events_us(fn, steps: int, warmup: int, reps: int = 3) -> float:
     return sorted(means)[len(means) // 2]
 
 
+def _step_us(one_step, steps: int, warmup: int, reps: int = 3) -> float:
+    """Time per step of `one_step(i)` (all of a step's launches): the mean
+    over `steps` back-to-back steps between two events on the current stream,
+    after `warmup` steps, taken `reps` times; the median.  No per-kernel
+    events: bracketing every launch with events lengthens each kernel, so a
+    step of two kernels would pay that twice and a step of one kernel once."""
+    import torch
+    for i in range(warmup):
+        one_step(i)
+    torch.cuda.synchronize()
+    means = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            one_step(i)
+        e1.record()
+        torch.cuda.synchronize()
+        means.append(e0.elapsed_time(e1) / steps * 1e3)
+    return sorted(means)[len(means) // 2]
+
+
 def _blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
@@ -780,8 +802,9 @@ def skew_sweep(dev, W: int, cus: int, steps: int, warmup: int) -> dict:
     """Balanced step (device-scheduled, and from a prebuilt host plan) against
     static split-KV plans with S splits per sequence, on batches from uniform
     to one long sequence among short ones (8 query heads over one KV head,
-    bf16).  Times are the summed decode + merge kernel durations per step
-    (dispatch-stamped events), KV rotated over >= 1 GiB of copies; host plans
+    bf16).  Times are whole steps (all of a step's launches, gaps between
+    kernels included), the mean over back-to-back steps between two events,
+    median of three passes, KV rotated over >= 1 GiB of copies; host plans
     are built and uploaded once, outside the timing; ratio = static /
     balanced (device-scheduled), and static / balanced host plan (the same
     host-planned kernel as the static plans).  The device-scheduled step is
@@ -809,15 +832,8 @@ def skew_sweep(dev, W: int, cus: int, steps: int, warmup: int) -> dict:
         scales = dict(sm_scale=inp.sm_scale, k_scale=inp.k_scale, v_scale=inp.v_scale)
 
         def kernel_us(one_step) -> float:
-            for i in range(max(warmup, 20)):   # small batches: let clocks and caches settle
-                one_step(i)
-            torch.cuda.synchronize()
-            hd.hpc_decode_profile_start(steps)
-            for i in range(steps):
-                one_step(i)
-            torch.cuda.synchronize()
-            d_ms, c_ms, n = hd.hpc_decode_profile_stop()
-            return (d_ms + c_ms) / max(n, 1) * 1e3
+            # small batches: let clocks and caches settle first
+            return _step_us(one_step, steps, max(warmup, 20))
 
         ws = torch.zeros(hd.hpc_decode_step_workspace_size(inp.batch, 8, 1, W), dtype=torch.uint8, device=dev)
         launchers = [hd.StepLauncher(q, ks[c], vs[c], bt, sl, out, lse, num_kv_heads=1, n_workers=W,
@@ -841,15 +857,14 @@ def skew_sweep(dev, W: int, cus: int, steps: int, warmup: int) -> dict:
             del launchers_r
 
         def planned_us(plan) -> float:
-            """kernel time of a prebuilt host plan (uploaded once) through hpc_decode_attn"""
+            """step time of a prebuilt host plan (uploaded once) through hpc_decode_attn, its arguments
+            marshalled once per KV copy (AttnLauncher), as the device step's are (StepLauncher)"""
             plan_dev = torch.from_numpy(plan.copy()).to(dev)
             nb = hd.hpc_decode_workspace_size(plan, 8, 1)
             sws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev) if nb > 0 else None
-
-            def one(i):
-                hd.hpc_decode_attn(q, ks[i % copies], vs[i % copies], bt, sl, plan, plan_dev, sws, out, lse,
-                                   num_kv_heads=1, **scales)
-            return kernel_us(one)
+            ls = [hd.AttnLauncher(q, ks[c], vs[c], bt, sl, plan, plan_dev, sws, out, lse, num_kv_heads=1, **scales)
+                  for c in range(copies)]
+            return kernel_us(lambda i: ls[i % copies]())
 
         balanced_host = planned_us(hd.hpc_decode_plan(lens_np, 1, W))
         rule_S = hd.hpc_decode_static_splits(lens_np, 1, cus)
@@ -877,7 +892,7 @@ def skew_sweep(dev, W: int, cus: int, steps: int, warmup: int) -> dict:
         rows.append(row)
         del ks, vs, launchers
         torch.cuda.empty_cache()
-    return {"metric": "static split-KV / balanced schedule kernel time, uniform -> skewed batches",
+    return {"metric": "static split-KV / balanced schedule step time, uniform -> skewed batches",
             "unit": "ratio", "higher_is_better": True, "n_workers": W, "steps": steps, "warmup": warmup,
             "heads": "8 q / 1 kv, head dim 128, bf16 KV, page 64",
             "static_rule": "smallest power of two S with units x S >= CUs, S <= 128 and <= the longest unit's tiles",
@@ -1167,6 +1182,13 @@ MERGE_SWEEP_BATCHES = (
     ("fp8 64q/8kv 4x2K", [2048] * 4, 64, 8, "fp8_e4m3"),
     ("fp8 64q/8kv 2x4K", [4096] * 2, 64, 8, "fp8_e4m3"),
     ("bf16 8q/1kv 4 short (37-200)", [37, 80, 150, 200], 8, 1, "bf16"),
+    # fewer tiles than workers: every worker holds at most one tile
+    ("bf16 8q/1kv 8x128", [128] * 8, 8, 1, "bf16"),
+    ("bf16 8q/1kv 16x256", [256] * 16, 8, 1, "bf16"),
+    ("bf16 8q/1kv 8x512", [512] * 8, 8, 1, "bf16"),
+    ("bf16 8q/1kv 32x256", [256] * 32, 8, 1, "bf16"),
+    ("bf16 8q/1kv 8x1K", [1024] * 8, 8, 1, "bf16"),
+    ("fp8 64q/8kv 2x512", [512] * 2, 64, 8, "fp8_e4m3"),
     ("bf16 8q/1kv 1x8K+31x4K", [8192] + [4096] * 31, 8, 1, "bf16"),
     ("bf16 8q/1kv 1x16K+31x4K", [16384] + [4096] * 31, 8, 1, "bf16"),
     ("bf16 8q/1kv 1x128K+31x4K", [131072] + [4096] * 31, 8, 1, "bf16"),
@@ -1185,9 +1207,10 @@ def plan_max_shares(words) -> int:
 def merge_sweep(dev, cus: int, steps: int, warmup: int) -> dict:
     """The device-scheduled step with the merge kernel and with the in-kernel
     merge, at the rules' worker count and entry price, on batches whose
-    units are shared by 2 to 128 workers: decode + merge kernel time per
-    step (dispatch-stamped events), KV rotated over >= 1 GiB of copies, the
-    two modes taken in turn for three rounds, medians."""
+    units are shared by 2 to 128 workers: whole-step time (the mean over
+    back-to-back steps between two events, gaps between kernels included),
+    KV rotated over >= 1 GiB of copies, the two modes taken in turn for three
+    rounds, medians."""
     import numpy as np
     import torch
 
@@ -1220,15 +1243,8 @@ def merge_sweep(dev, cus: int, steps: int, warmup: int) -> dict:
         times = {f: [] for f in (False, True)}
         for _ in range(3):
             for f in (False, True):
-                for i in range(max(warmup, 20)):
-                    launchers[f][i % copies]()
-                torch.cuda.synchronize()
-                hd.hpc_decode_profile_start(steps)
-                for i in range(steps):
-                    launchers[f][i % copies]()
-                torch.cuda.synchronize()
-                d_ms, c_ms, n = hd.hpc_decode_profile_stop()
-                times[f].append(round((d_ms + c_ms) / max(n, 1) * 1e3, 2))
+                times[f].append(round(_step_us(lambda i: launchers[f][i % copies](), steps, max(warmup, 20),
+                                               reps=1), 2))
         med = {f: float(np.median(t)) for f, t in times.items()}
         row = {"batch": name, "n_workers": W, "entry_price": price, "max_shares": shares,
                "merge_kernel_us": times[False], "in_kernel_us": times[True],
@@ -1240,7 +1256,7 @@ def merge_sweep(dev, cus: int, steps: int, warmup: int) -> dict:
         del launchers, ks, vs, ws
         torch.cuda.empty_cache()
     return {"mode": "merge-sweep", "cus": cus, "steps": steps,
-            "timing": "decode + merge kernel time per step, dispatch-stamped HIP events, three rounds",
+            "timing": "whole step, the mean over back-to-back steps between two events, three rounds",
             "rows": rows}
 
 

@@ -258,13 +258,7 @@ int32_t hpc_decode_pick_entry_price(const int32_t* seq_lens, int32_t batch, int3
                                     int32_t kv_dtype, int32_t n_workers);
 
 /* The most workers that may share one sequence-head unit for
- * hpc_decode_pick_merge to keep the merge in the decode kernel.  Measured on
- * MI355X (device-scheduled steps, W = 256 and the worker-count rule's W):
- * with 2, 4 and 8 workers per unit the in-kernel merge ran 0.3-1.3 us faster
- * than the merge kernel (uniform bf16 8q/1kv and 64q/8kv and fp8 64q/8kv
- * batches, and 4 short sequences); with 16 it tied on uniform batches and
- * lost 2.1 us on 1 x 8K + 31 x 4K, and with 30 or more it lost 2.5 us or
- * more, since the last worker folds all of a unit's partials alone. */
+ * hpc_decode_pick_merge to keep the merge in the decode kernel. */
 #define HPC_DECODE_FUSED_MAX_SHARES 8
 
 /* Merge mode for a device-scheduled step (the params field fused_merge),
@@ -275,9 +269,15 @@ int32_t hpc_decode_pick_entry_price(const int32_t* seq_lens, int32_t batch, int3
  * used here).  Over the partition the step will use (n_workers workers,
  * entry_price applied as hpc_decode_plan_priced applies it), it counts the
  * workers whose tile range meets each (sequence, KV head) unit.  Returns 1
- * (merge in the decode kernel) when no unit has more than
- * HPC_DECODE_FUSED_MAX_SHARES, which includes a batch with no split unit or
- * no tiles (the merge kernel's launch is then saved), else 0 (merge kernel).
+ * (merge in the decode kernel) when no unit is split, or when the batch has
+ * no more tiles than workers (each worker holds at most one) and no unit is
+ * shared by more than HPC_DECODE_FUSED_MAX_SHARES workers; else 0 (merge
+ * kernel).  Measured on MI355X as whole steps (W = 256 and the worker-count
+ * rule's W): batches of 10 to 128 tiles with 2 to 8 workers per unit ran
+ * 0.2-0.8 us faster with the in-kernel merge; batches with more tiles than
+ * workers ran as fast or up to 0.4 us faster with the merge kernel, and
+ * units shared by 16 or more workers up to 14 us faster, since the last
+ * worker folds all of a unit's partials alone.
  * For hpc_decode_step; hpc_decode_step_noalloc takes fused_merge = 0 only.
  * Negative status: HPC_ERR_NULL for NULL lengths with batch > 0,
  * HPC_ERR_INVALID for batch < 0, num_kv_heads < 1, n_workers < 1,

@@ -33,6 +33,7 @@ __all__ = [
     "hpc_decode_profile_stop", "hpc_decode_trace_start", "hpc_decode_trace_stop",
     "hpc_decode_wall_clock_hz", "hpc_probe_read", "hpc_probe_read_timed", "hpc_probe_copy", "hpc_decode_step",
     "hpc_decode_step_check", "hpc_decode_step_workspace_size", "hpc_decode_plan_device", "StepLauncher",
+    "AttnLauncher",
     "hpc_decode_step_noalloc", "hpc_decode_step_noalloc_max_bytes",
     "hpc_decode_plan_workspace_bound", "hpc_decode_plan_attn", "PlannedStepLauncher",
     "DecodeStep", "HpcDecodeError",
@@ -210,8 +211,9 @@ FUSED_MAX_SHARES = 8
 def hpc_decode_pick_merge(seq_lens, num_kv_heads: int, n_workers: int, entry_price: int = 0) -> bool:
     """The merge mode of a device-scheduled step (``fused_merge``): True
     (merge in the decode kernel) when no (sequence, KV head) unit of the
-    step's partition is shared by more than FUSED_MAX_SHARES workers, False
-    (merge kernel) otherwise."""
+    step's partition is split, or when the batch has no more tiles than
+    workers and no unit is shared by more than FUSED_MAX_SHARES workers;
+    False (merge kernel) otherwise."""
     lens = _host_i32(seq_lens).reshape(-1)
     return bool(_lib.check(lib().hpc_decode_pick_merge(_i32p(lens), lens.shape[0], num_kv_heads, n_workers,
                                                        entry_price), "hpc_decode_pick_merge"))
@@ -281,6 +283,31 @@ def hpc_decode_attn(q, k_cache, v_cache, block_table, seq_lens, plan_host, plan_
     args, _ = _attn_args(q, k_cache, v_cache, block_table, seq_lens, plan_host, plan_dev, workspace, out,
                          lse, num_kv_heads, sm_scale, k_scale, v_scale, tile_math)
     _lib.check(lib().hpc_decode_attn(*args, _stream_handle(stream)), "hpc_decode_attn")
+
+
+class AttnLauncher:
+    """A host-planned decode step for one prebuilt plan (``hpc_decode_attn``),
+    with its arguments marshalled once.
+
+    Calling it issues exactly one ``hpc_decode_attn`` on the stream given at
+    construction (default: the current stream then).  The plan must already
+    be on the device in ``plan_dev``; the plan words, the tensors and the
+    workspace must stay alive and unchanged for the launcher's lifetime.
+    """
+
+    def __init__(self, q, k_cache, v_cache, block_table, seq_lens, plan_host, plan_dev, workspace, out, lse, *,
+                 num_kv_heads, sm_scale, k_scale=1.0, v_scale=1.0, stream=None, tile_math="mfma"):
+        args, ph = _attn_args(q, k_cache, v_cache, block_table, seq_lens, plan_host, plan_dev, workspace, out,
+                              lse, num_kv_heads, sm_scale, k_scale, v_scale, tile_math)
+        self._keep = (q, k_cache, v_cache, block_table, seq_lens, ph, plan_dev, workspace, out, lse)
+        _lib.check(lib().hpc_decode_check(*args), "AttnLauncher")
+        self._args = args + (_stream_handle(stream),)
+        self._fn = lib().hpc_decode_attn
+
+    def __call__(self) -> None:
+        status = self._fn(*self._args)
+        if status:
+            _lib.check(status, "hpc_decode_attn")
 
 
 # ------------------------------------------------ host-planned step in one call ---

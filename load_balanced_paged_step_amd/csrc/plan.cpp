@@ -394,9 +394,10 @@ extern "C" int32_t hpc_decode_pick_merge(const int32_t* seq_lens, int32_t batch,
         while (u < U && s1[u] <= a) ++u;
         for (std::size_t v = u; v < U && s0[v] < e; ++v) ++shares[v];
     }
-    for (std::size_t v = 0; v < U; ++v)
-        if (shares[v] > HPC_DECODE_FUSED_MAX_SHARES) return 0;
-    return 1;
+    int32_t most = 1;
+    for (std::size_t v = 0; v < U; ++v) most = shares[v] > most ? shares[v] : most;
+    if (most == 1) return 1;   // nothing to merge: the merge kernel's launch is saved
+    return (T <= n_workers && most <= HPC_DECODE_FUSED_MAX_SHARES) ? 1 : 0;
 }
 
 extern "C" int64_t hpc_decode_plan_words(const int32_t* plan) {

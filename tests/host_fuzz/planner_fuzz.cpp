@@ -77,12 +77,13 @@ int main() {
         const int32_t pick = hpc_decode_pick_entry_price(B ? lens.data() : nullptr, B, H,
                                                          uni(0, 1) ? HPC_KV_BF16 : HPC_KV_FP8_E4M3, W);
         CHECK(pick == 0 || pick == 2 || pick == 4 || pick == 8 || pick == 16);
-        // the merge mode: in-kernel exactly when no merge record counts more than the limit
+        // the merge mode: in-kernel when nothing is split, or with no more tiles than workers
+        // and no merge record counting more than the limit
         int32_t most = 1;
         const int32_t* rec = pplan.data() + HPC_PLAN_HEADER_WORDS + (W + 1) + 4 * pplan[5];
         for (int32_t c = 0; c < pplan[7]; ++c) most = rec[3 * c + 1] > most ? rec[3 * c + 1] : most;
         CHECK(hpc_decode_pick_merge(B ? lens.data() : nullptr, B, H, W, price) ==
-              (most <= HPC_DECODE_FUSED_MAX_SHARES ? 1 : 0));
+              ((most == 1 || (T <= W && most <= HPC_DECODE_FUSED_MAX_SHARES)) ? 1 : 0));
         ++plans;
         // the static split-KV planner
         const int32_t S = static_cast<int32_t>(uni(1, 64));

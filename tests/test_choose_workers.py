@@ -226,53 +226,61 @@ def test_pick_entry_price_errors():
 
 def _oracle_max_shares(lens, H, W, price):
     """Most workers sharing one unit, read off the oracle plan's merge records
-    (each record holds a split unit's worker count)."""
+    (each record holds a split unit's worker count), and the plan's tile count."""
     plan = parse_plan(build_plan(np.asarray(lens, dtype=np.int64), H, W, entry_cost_q=price))
-    return max([1] + [int(r[1]) for r in plan["combine"]])
+    return max([1] + [int(r[1]) for r in plan["combine"]]), plan["n_tiles"]
+
+
+def _rule(lens, H, W, price):
+    """The merge rule written out: in the kernel when nothing is split, or
+    when there are no more tiles than workers and no unit has more than
+    FUSED_MAX_SHARES workers."""
+    most, T = _oracle_max_shares(lens, H, W, price)
+    return most == 1 or (T <= W and most <= hd.FUSED_MAX_SHARES)
 
 
 @pytest.mark.parametrize("lens,H,W,expected", [
-    ([512] * 64, 1, 256, True),                  # 4 workers per sequence
-    ([1024] * 32, 1, 256, True),                 # 8
-    ([2048] * 16, 1, 256, False),                # 16
+    ([37, 80, 150, 200], 1, 256, True),          # 10 tiles, up to 4 workers a unit
+    ([512] * 8, 1, 256, True),                   # 64 tiles, 8 workers a unit
+    ([1024] * 8, 1, 256, False),                 # 128 tiles, 16 workers a unit
+    ([512] * 64, 1, 256, False),                 # more tiles than workers
     ([131072] + [4096] * 31, 1, 252, False),     # the long sequence over 128 workers
-    ([37, 80, 150, 200], 1, 256, True),          # fewer tiles than workers: one per tile
     ([4096] * 64, 1, 64, True),                  # no unit split: no merge kernel to launch
     ([0, 0, 0], 2, 16, True),                    # no tiles at all
 ])
 def test_pick_merge_cases(lens, H, W, expected):
     assert hd.hpc_decode_pick_merge(np.array(lens), H, W) is expected
-    assert (_oracle_max_shares(lens, H, W, 0) <= hd.FUSED_MAX_SHARES) is expected
+    assert _rule(lens, H, W, 0) is expected
 
 
 def test_pick_merge_on_the_decode_workloads():
     """At the rules' worker count and price: the in-kernel merge for the tiny
-    and the uniform batch, the merge kernel where a sequence spreads over more
-    than 8 workers (8 x 1K at 256 workers, the 128K sequence, the fp8 batch's
-    long sequences)."""
+    batch only (10 tiles); the uniform batch has more tiles than workers, and
+    8 x 1K, the 128K sequence and the fp8 batch's long sequences spread over
+    more than 8 workers."""
     got = {}
     for cfg, w in WORKLOADS.items():
         lens = workload_lengths(cfg)
         W = hd.hpc_decode_pick_workers(lens, w.num_kv_heads, w.kv_dtype, 256)
         price = hd.hpc_decode_pick_entry_price(lens, w.num_kv_heads, w.kv_dtype, W)
         got[cfg] = hd.hpc_decode_pick_merge(lens, w.num_kv_heads, W, price)
-        assert got[cfg] is (_oracle_max_shares(lens, w.num_kv_heads, W, price) <= hd.FUSED_MAX_SHARES)
-    assert got == {1: True, 2: True, 3: False, 4: False, 5: False}
+        assert got[cfg] is _rule(lens, w.num_kv_heads, W, price)
+    assert got == {1: True, 2: False, 3: False, 4: False, 5: False}
 
 
 @settings(max_examples=80, deadline=None)
 @given(lens=st.lists(st.integers(0, 6000), min_size=1, max_size=12), H=st.integers(1, 4),
-       W=st.integers(1, 60), price=st.sampled_from([0, 2, 4, 8, 16, 64]))
+       W=st.integers(1, 600), price=st.sampled_from([0, 2, 4, 8, 16, 64]))
 def test_pick_merge_matches_the_oracle_plan(lens, H, W, price):
-    want = _oracle_max_shares(lens, H, W, price) <= hd.FUSED_MAX_SHARES
-    assert hd.hpc_decode_pick_merge(np.array(lens), H, W, price) is want
+    assert hd.hpc_decode_pick_merge(np.array(lens), H, W, price) is _rule(lens, H, W, price)
 
 
 def test_pick_merge_errors():
     lib = hd.lib()
     lens = np.array([100, 200], dtype=np.int32)
     p = lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
-    assert lib.hpc_decode_pick_merge(p, 2, 1, 4, 0) == 1
+    assert lib.hpc_decode_pick_merge(p, 2, 1, 8, 0) == 1     # 6 tiles over 8 workers
+    assert lib.hpc_decode_pick_merge(p, 2, 1, 4, 0) == 0     # more tiles than workers
     assert lib.hpc_decode_pick_merge(None, 2, 1, 4, 0) == hd.HPC_ERR_NULL
     assert lib.hpc_decode_pick_merge(None, 0, 1, 4, 0) == 1                  # empty batch
     assert lib.hpc_decode_pick_merge(p, -1, 1, 4, 0) == hd.HPC_ERR_INVALID

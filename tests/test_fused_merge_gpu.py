@@ -90,15 +90,15 @@ def test_random_batches(seed):
 
 
 @pytest.mark.parametrize("lens,hq,hkv,kv", [
-    ([256] * 128, 8, 1, "bf16"),           # 2 workers per sequence
-    ([1024] * 32, 8, 1, "bf16"),           # 8: the most the merge rule keeps in the kernel
-    ([2048] * 4, 64, 8, "fp8_e4m3"),       # 8 per (sequence, KV head)
+    ([128] * 8, 8, 1, "bf16"),             # 16 tiles, 2 workers per sequence
+    ([512] * 8, 8, 1, "bf16"),             # 64 tiles, 8: the most the merge rule keeps in the kernel
+    ([512] * 2, 64, 8, "fp8_e4m3"),        # 128 tiles, 8 per (sequence, KV head)
     ([37, 80, 150, 200], 8, 1, "bf16"),    # one worker per tile
 ])
 def test_batches_the_merge_rule_keeps_in_the_kernel(lens, hq, hkv, kv):
     """The step as the library's rules set it up (worker count, entry price,
-    merge mode) on batches whose units are shared by 2 to 8 workers, for
-    which hpc_decode_pick_merge picks the in-kernel merge."""
+    merge mode) on batches with no more tiles than workers and 2 to 8 workers
+    per unit, for which hpc_decode_pick_merge picks the in-kernel merge."""
     W = hd.hpc_decode_pick_workers(np.array(lens), hkv, kv, 256)
     price = hd.hpc_decode_pick_entry_price(np.array(lens), hkv, kv, W)
     assert hd.hpc_decode_pick_merge(np.array(lens), hkv, W, price)
