@@ -461,16 +461,16 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
         sched.W = a.n_workers;
         sched.set_tiles(static_cast<int64_t>(Hkv) * s_dyn[2 * a.batch]);
         sched.set_price(a.entry_price);
-        int b0 = 0, h0 = 0, t0 = 0;
+        int b0 = 0, h0 = 0, t0 = 0, L0 = -1;
         if (sched.c != 0) {
             sched.priced_range_uniform(w, w_begin, w_end, b0, h0, t0);
         } else {
-            w_begin = sched.range_begin(w);
-            w_end = sched.range_begin(w + 1);
-            if (w_begin < w_end) sched.locate_uniform(w_begin, b0, h0, t0);
+            w_begin = uniform(static_cast<int>(sched.equal_begin(w)));   // T < 2^31
+            w_end = uniform(static_cast<int>(sched.equal_begin(w + 1)));
+            if (w_begin < w_end) sched.locate_uniform_len(w_begin, b0, h0, t0, L0);
         }
         if (w_begin < w_end) {
-            dwalk.init_at(sched, w, w_begin, w_end, b0, h0, t0);
+            dwalk.init_at(sched, w, w_begin, w_end, b0, h0, t0, L0);
             u_first = dwalk.b * Hkv + dwalk.h;    // the unit of the worker's first tile
             if constexpr (FUSED) {
                 int bB, hB, tB;

@@ -47,6 +47,18 @@ __device__ __forceinline__ int small_quot(int64_t x, int64_t y) {
     return q;
 }
 
+// floor(x / y) when the quotient is at most qmax < 2^16 and qmax * y < 2^32:
+// the single-precision estimate is off by at most one (as above), clamping it
+// to qmax keeps the 32-bit products below from wrapping, and one step fixes it.
+__device__ __forceinline__ uint32_t quot_u32(uint32_t x, uint32_t y, uint32_t qmax) {
+    uint32_t q = static_cast<uint32_t>(static_cast<float>(x) * __builtin_amdgcn_rcpf(static_cast<float>(y)));
+    q = min(q, qmax);
+    const uint32_t p = q * y;
+    if (p > x) --q;
+    else if (x - p >= y) ++q;
+    return q;
+}
+
 __device__ __forceinline__ int wave_inclusive_sum(int x) {
     const int lane = threadIdx.x & 63;
 #pragma unroll
@@ -156,11 +168,20 @@ struct Sched {
         t = rem < 4 ? 0 : min(n - 1, rem >> 2);
         return static_cast<int64_t>(H) * pb[b] + static_cast<int64_t>(h) * n + t;
     }
+    // equal shares: floor(w T / W) = w qT + floor(w rT / W) for 0 <= w <= W,
+    // all in 32 bits: w qT <= T < 2^31, w rT < W^2 <= 2^32, and the quotient
+    // is below W <= 2^16 (at most W - 1, with (W - 1) W < 2^32)
+    __device__ __forceinline__ int64_t equal_begin(int w) const {
+        const uint32_t uw = static_cast<uint32_t>(w);
+        const uint32_t uW = static_cast<uint32_t>(W);
+        return static_cast<int64_t>(uw * static_cast<uint32_t>(qT) +
+                                    quot_u32(uw * static_cast<uint32_t>(rT), uW, uW - 1));
+    }
     // floor(w T / W) = w qT + floor(w rT / W), with w rT < W^2; priced: the
     // largest j with A(j) <= floor(w C / W), the last sequence whose cost
     // prefix is at most that found by binary search (per-thread form)
     __device__ __forceinline__ int64_t range_begin(int w) const {
-        if (c == 0) return static_cast<int64_t>(w) * qT + small_quot(static_cast<int64_t>(w) * rT, W);
+        if (c == 0) return equal_begin(w);
         if (w >= W) return T;
         const int64_t tw = tau(w);
         int lo = 0, hi = B;
@@ -248,6 +269,40 @@ struct Sched {
         }
         split_tile(j, __builtin_amdgcn_readfirstlane(count - 1), b, h, t);
     }
+    // locate_uniform for 0 <= j < T, also giving the sequence's length L; the
+    // prefix and length of the sequence found come from the lane that read
+    // them, not from a second LDS read, and the arithmetic is 32-bit (H P_b
+    // <= T < 2^31; the head index is below H <= 4096, with H n <= T).
+    // Prefixes are non-decreasing, so the lanes at or before j are the first
+    // `cnt` of each chunk, and a chunk with none ends the search in the
+    // previous chunk's last lane.
+    __device__ __forceinline__ void locate_uniform_len(int64_t j, int& b, int& h, int& t, int& L) const {
+        const int lane = threadIdx.x & 63;
+        const uint32_t uj = static_cast<uint32_t>(j);
+        int at = 0, p = 0, l = 0;
+        for (int b0 = 0; b0 < B; b0 += 64) {
+            const int bb = b0 + lane;
+            int pc = INT32_MAX, lc = 0;
+            if (bb < B) {
+                pc = H * pb[bb];
+                lc = len[bb];
+            }
+            const int cnt = __popcll(__ballot(static_cast<uint32_t>(pc) <= uj));
+            if (cnt > 0) {
+                at = b0 + cnt - 1;
+                p = __builtin_amdgcn_readlane(pc, cnt - 1);
+                l = __builtin_amdgcn_readlane(lc, cnt - 1);
+            }
+            if (cnt < 64) break;
+        }
+        b = at;
+        L = l;
+        const uint32_t n = static_cast<uint32_t>(tiles_of(l));
+        const uint32_t r = uj - static_cast<uint32_t>(p);   // < H n
+        const uint32_t hh = __builtin_amdgcn_readfirstlane(quot_u32(r, n, static_cast<uint32_t>(H - 1)));
+        h = static_cast<int>(hh);
+        t = static_cast<int>(r - hh * n);
+    }
     // k such that worker w (whose range starts at tile `t_first` of unit
     // (b, h)) is the k-th worker of that unit
     __device__ __forceinline__ int rank_in_unit(int w, int b, int h, int t_first) const {
@@ -322,8 +377,9 @@ struct DeviceWalker {
         init_at(sched, worker, begin, end, b0, h0, t0);
     }
     // the same, with the first tile's sequence, head and tile already known
+    // (L0 >= 0: the length of sequence b0, already read)
     __device__ __forceinline__ void init_at(const Sched& sched, int worker, int64_t begin, int64_t end, int b0,
-                                            int h0, int t0) {
+                                            int h0, int t0, int L0 = -1) {
         s = &sched;
         w = worker;
         remaining = end - begin;
@@ -332,7 +388,7 @@ struct DeviceWalker {
             b = b0;
             h = h0;
             t = t0;
-            L = sched.len[b];
+            L = L0 >= 0 ? L0 : sched.len[b];
             n = tiles_of(L);
             start_entry(true);
         } else {
