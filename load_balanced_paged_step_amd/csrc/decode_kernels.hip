@@ -473,8 +473,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
             dwalk.init_at(sched, w, w_begin, w_end, b0, h0, t0, L0);
             u_first = dwalk.b * Hkv + dwalk.h;    // the unit of the worker's first tile
             if constexpr (FUSED) {
-                int bB, hB, tB;
-                sched.locate_uniform(w_end - 1, bB, hB, tB);
+                int bB, hB, tB, LB;
+                sched.locate_uniform_len(w_end - 1, bB, hB, tB, LB);
                 fm_u[0] = u_first;
                 fm_u[1] = bB * Hkv + hB;
                 fm_S[0] = sched.parts(dwalk.b, dwalk.h);

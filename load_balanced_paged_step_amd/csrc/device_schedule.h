@@ -150,20 +150,26 @@ struct Sched {
     __device__ __forceinline__ int64_t unit_start(int b, int h) const {
         return static_cast<int64_t>(H) * pb[b] + static_cast<int64_t>(h) * tiles(b);
     }
-    // priced: floor(w C / W) = w qC + floor(w rC / W), for w < W (then < C)
+    // priced: floor(w C / W) = w qC + floor(w rC / W), for w < W (then < C);
+    // 32-bit as equal_begin, with C < 2^31 in place of T
     __device__ __forceinline__ int64_t tau(int w) const {
-        return static_cast<int64_t>(w) * qC + small_quot(static_cast<int64_t>(w) * rC, W);
+        const uint32_t uw = static_cast<uint32_t>(w);
+        const uint32_t uW = static_cast<uint32_t>(W);
+        return static_cast<int64_t>(uw * static_cast<uint32_t>(qC) +
+                                    quot_u32(uw * static_cast<uint32_t>(rC), uW, uW - 1));
     }
     // priced: the largest j with A(j) <= tau < C, given the last sequence b
     // whose cost prefix is <= tau (a sequence with tiles, as tau < C).  j
     // lies in the unit h of b whose cost span holds tau, at the tiles t of
     // that unit that fit: A(start + t) = start + c + 4 t for t >= 1, and
-    // t < n as tau is below the next unit's start.
+    // t < n as tau is below the next unit's start.  32-bit: H unit <= C < 2^31
+    // and H <= 4096, within quot_u32's bounds.
     __device__ __forceinline__ int64_t cut_in(int b, int64_t tau_w, int& h, int& t) const {
         const int n = tiles(b);
         const int unit = 4 * n + c;
         const int r = static_cast<int>(tau_w - static_cast<int64_t>(H) * seq_cost(b));   // < H * unit < 2^31
-        h = small_quot(r, unit);   // < H
+        h = static_cast<int>(quot_u32(static_cast<uint32_t>(r), static_cast<uint32_t>(unit),
+                                      static_cast<uint32_t>(H - 1)));   // < H
         const int rem = r - h * unit - c;
         t = rem < 4 ? 0 : min(n - 1, rem >> 2);
         return static_cast<int64_t>(H) * pb[b] + static_cast<int64_t>(h) * n + t;
@@ -203,23 +209,28 @@ struct Sched {
         const int64_t t0 = tau(w);
         const bool last = w + 1 >= W;
         const int64_t t1 = last ? t0 : tau(w + 1);
+        // every cost prefix H (4 P_b + c NE_b) and bound is at most C < 2^31
+        const int u0 = static_cast<int>(t0), u1 = static_cast<int>(t1);
         int n0 = 0, n1 = 0;
         for (int b0 = 0; b0 < B; b0 += 64) {
             const int bb = b0 + (threadIdx.x & 63);
-            const int64_t sc = bb < B ? static_cast<int64_t>(H) * seq_cost(bb) : INT64_MAX;
-            const int k0 = __popcll(__ballot(sc <= t0));
-            const int k1 = __popcll(__ballot(sc <= t1));
+            const int sc = bb < B ? H * (4 * pb[bb] + c * ne[bb]) : INT32_MAX;
+            const int k0 = __popcll(__ballot(sc <= u0));
+            const int k1 = __popcll(__ballot(sc <= u1));
             n0 += k0;
             n1 += k1;
             if (k1 < 64) break;   // the prefix only grows: no later sequence is within either bound
         }
         b = __builtin_amdgcn_readfirstlane(n0 - 1);
-        begin = cut_in(b, t0, h, t);
+        begin = __builtin_amdgcn_readfirstlane(static_cast<int>(cut_in(b, t0, h, t)));   // < T < 2^31
+        h = __builtin_amdgcn_readfirstlane(h);
+        t = __builtin_amdgcn_readfirstlane(t);
         if (last) {
             end = T;
         } else {
             int h1, tt1;
-            end = cut_in(__builtin_amdgcn_readfirstlane(n1 - 1), t1, h1, tt1);
+            end = __builtin_amdgcn_readfirstlane(
+                static_cast<int>(cut_in(__builtin_amdgcn_readfirstlane(n1 - 1), t1, h1, tt1)));
         }
     }
     __device__ __forceinline__ int owner(int64_t j) const {    // valid for W <= T (quotient < W)
